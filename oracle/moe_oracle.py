@@ -1,0 +1,283 @@
+"""Plain CPU oracle for the local Mixture-of-Experts FFN forward.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import or call
+this module: only the tests, the smoke check and the benchmark's CPU-baseline
+leg use it. It shares no code with the HIP library.
+
+What it computes (ruDNN user guide, "3. MoE workflow"): logits -> fp32 softmax
+over all experts -> top-k -> compact dispatch -> bias-free SwiGLU experts ->
+weighted combine in token order; plus the fused combine + residual Add +
+RMSNorm epilogue of the CANN page aclnnMoeDistributeCombineAddRmsNormV2
+("function description", formula).
+
+Precision policy:
+  * softmax: computed exactly (fp64) from the fp32-widened logits and rounded
+    once to fp32, which is the most accurate result an fp32 softmax can give;
+    top-k selection compares these fp32 probabilities (routing contract: the
+    softmax over all experts is fp32 and precedes the top-k);
+  * expert GEMMs, SiLU, combine and RMSNorm: fp64, with one round-to-nearest-
+    even into the model dtype at each tensor the API returns (h inside the
+    experts, expert_out, out, x_out, y) and fp32 for rstd;
+  * bf16 values travel as uint16 bit patterns; fp16 as numpy float16.
+
+Every function is a direct statement of the definition, vectorised with numpy
+where that keeps it readable. Library primitives used: exp, sum, matmul,
+lexsort.
+
+Parity pins for every function live in tests/test_oracle_pins.py; no function
+here is "parity unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F32, F16, BF16 = "f32", "f16", "bf16"
+
+
+# --------------------------------------------------------------------------
+# storage dtypes
+# --------------------------------------------------------------------------
+def decode(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Stored values -> exact fp64 values."""
+    if dtype == F32:
+        return np.asarray(a, dtype=np.float32).astype(np.float64)
+    if dtype == F16:
+        return np.asarray(a, dtype=np.float16).astype(np.float64)
+    if dtype == BF16:
+        bits = np.asarray(a, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+        return bits.view(np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+def _round_bf16(x: np.ndarray) -> np.ndarray:
+    """fp64 -> bf16 bits, round to nearest, ties to even, in one step.
+
+    bf16 keeps 8 significant bits and fp32's exponent range. For |x| in
+    [2^(e-1), 2^e) the spacing of bf16 values is 2^(e-8); below 2^-126
+    (subnormal) it is fixed at 2^-133. Dividing by a power of two is exact,
+    so np.round (half to even) of x / spacing is the RNE integer multiple."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    fin = np.isfinite(x)
+    xf = x[fin]
+    _, e = np.frexp(xf)
+    e = np.maximum(e, -125)
+    q = np.ldexp(1.0, e - 8)
+    r = np.round(xf / q) * q
+    with np.errstate(over="ignore"):
+        r32 = r.astype(np.float32)  # exact, or +-inf past the largest bf16
+    out[fin] = (r32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    nan = np.isnan(x)
+    out[nan] = 0x7FC0
+    out[np.isposinf(x)] = 0x7F80
+    out[np.isneginf(x)] = 0xFF80
+    return out
+
+
+def round_to(x: np.ndarray, dtype: str) -> np.ndarray:
+    """fp64 -> storage dtype, one rounding to nearest even."""
+    x = np.asarray(x, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        if dtype == F32:
+            return x.astype(np.float32)
+        if dtype == F16:
+            return x.astype(np.float16)
+    if dtype == BF16:
+        return _round_bf16(x)
+    raise ValueError(dtype)
+
+
+# --------------------------------------------------------------------------
+# routing  (ruDNN user guide, "4. Routing contract")
+# --------------------------------------------------------------------------
+def invalid_rows(z: np.ndarray) -> np.ndarray:
+    """Rows that contain NaN, contain +inf, or are entirely -inf. The routing
+    contract keeps NaN weights for these rows instead of a uniform fallback."""
+    return np.isnan(z).any(axis=1) | np.isposinf(z).any(axis=1) | np.isneginf(z).all(axis=1)
+
+
+def softmax_fp32(logits: np.ndarray, logits_dtype: str) -> np.ndarray:
+    """p[t, e] = exp(z[t, e]) / sum_j exp(z[t, j]) over all E experts, delivered
+    in fp32. Computed as exp(z - max) in fp64 and rounded once."""
+    z = decode(logits, logits_dtype)
+    T, E = z.shape
+    p = np.full((T, E), np.nan, dtype=np.float32)
+    ok = ~invalid_rows(z)
+    if ok.any():
+        zo = z[ok]
+        a = np.exp(zo - zo.max(axis=1, keepdims=True))
+        p[ok] = (a / a.sum(axis=1, keepdims=True)).astype(np.float32)
+    return p
+
+
+def route(logits: np.ndarray, logits_dtype: str, top_k: int, renormalize: bool):
+    """Routing plan: (indices uint32 [T, k], weights [T, k] in logits dtype).
+
+    Selection: the k largest fp32 probabilities, largest first; equal
+    probabilities favour the lower expert id. Rows that are invalid (see
+    invalid_rows) have all probabilities NaN; NaNs tie with each other, so the
+    tie rule selects ids 0..k-1, and every weight is NaN.
+    With renormalize the selected probabilities are divided by their sum, then
+    cast to the logits dtype; without it they are cast as they are."""
+    z = decode(logits, logits_dtype)
+    T, E = z.shape
+    if not (1 <= top_k <= E):
+        raise ValueError("top_k must satisfy 1 <= top_k <= E")
+    p = softmax_fp32(logits, logits_dtype)
+    bad = invalid_rows(z)
+    ids = np.broadcast_to(np.arange(E), (T, E))
+    order = np.lexsort((ids, -p.astype(np.float64)), axis=-1)  # key 1: -p, key 2: id
+    order[bad] = np.arange(E)
+    idx = order[:, :top_k]
+    psel = np.take_along_axis(p, idx, axis=1).astype(np.float64)
+    if renormalize:
+        w = psel / psel.sum(axis=1, keepdims=True)
+    else:
+        w = psel
+    w[bad] = np.nan
+    return idx.astype(np.uint32), round_to(w, logits_dtype)
+
+
+# --------------------------------------------------------------------------
+# dispatch  (ruDNN user guide, "5. Expert weights and dispatch")
+# --------------------------------------------------------------------------
+def dispatch(indices: np.ndarray, E: int, x: np.ndarray | None = None):
+    """Compact grouping of the T*k (token, slot) pairs by expert, no capacity
+    drop. Within an expert, pairs keep (token, slot) order (the pages leave
+    this order free; this build fixes it). Returns
+      offsets     int32 [E+1]  rows of expert e are offsets[e]:offsets[e+1]
+      slot_of_row int32 [R]    flat slot t*k+j held by dispatched row r
+      row_of_slot int32 [T*k]  inverse map; -1 for an out-of-range expert id
+      x_disp      [R, H]       x_disp[r] = x[slot_of_row[r] // k]   (if x given)
+    where R = number of in-range pairs."""
+    T, k = indices.shape
+    flat = indices.reshape(-1).astype(np.int64)
+    slots_by_expert = [np.nonzero(flat == e)[0] for e in range(E)]
+    counts = np.array([len(s) for s in slots_by_expert], dtype=np.int64)
+    offsets = np.zeros(E + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(counts)
+    slot_of_row = (np.concatenate(slots_by_expert) if E else np.zeros(0, np.int64)).astype(np.int32)
+    row_of_slot = np.full(T * k, -1, dtype=np.int32)
+    row_of_slot[slot_of_row] = np.arange(len(slot_of_row), dtype=np.int32)
+    out = dict(offsets=offsets, slot_of_row=slot_of_row, row_of_slot=row_of_slot)
+    if x is not None:
+        out["x_disp"] = x[slot_of_row // k]
+    return out
+
+
+# --------------------------------------------------------------------------
+# experts  (ruDNN user guide, "3. MoE workflow" and "5. Expert weights")
+# --------------------------------------------------------------------------
+def silu(g: np.ndarray) -> np.ndarray:
+    """SiLU(g) = g * sigmoid(g) = g / (1 + exp(-g))."""
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
+def swiglu_expert(x_rows: np.ndarray, w_gate_e: np.ndarray, w_up_e: np.ndarray,
+                  w_down_e: np.ndarray, dtype: str) -> np.ndarray:
+    """One bias-free SwiGLU expert on its rows.
+    x_rows [n, H]; gate/up [I, H]; down [H, I] (all stored in dtype).
+      g = x W_gate^T, u = x W_up^T            (fp64)
+      h = round(SiLU(g) * u)                  (stored in the model dtype)
+      y = round(h W_down^T)                   [n, H]"""
+    x = decode(x_rows, dtype)
+    g = x @ decode(w_gate_e, dtype).T
+    u = x @ decode(w_up_e, dtype).T
+    h = decode(round_to(silu(g) * u, dtype), dtype)
+    return round_to(h @ decode(w_down_e, dtype).T, dtype)
+
+
+def experts_forward_dispatched(x_disp: np.ndarray, offsets: np.ndarray, weights_of, dtype: str):
+    """Expert outputs for every dispatched row, in dispatched order.
+    weights_of(e) -> (gate [I,H], up [I,H], down [H,I]) for expert e."""
+    R = int(offsets[-1])
+    E = len(offsets) - 1
+    out = None
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if a == b:
+            continue
+        y = swiglu_expert(x_disp[a:b], *weights_of(e), dtype)
+        if out is None:
+            out = np.empty((R, y.shape[1]), dtype=y.dtype)
+        out[a:b] = y
+    return out
+
+
+# --------------------------------------------------------------------------
+# combine  (ruDNN user guide, "6. Calling MoE": combine restores token order
+# with the saved map and merges expert outputs using the routing weights)
+# --------------------------------------------------------------------------
+def combine_fp64(expert_out, row_of_slot, weights, w_dtype, T, k, dtype):
+    """c[t] = sum_{j<k} w[t,j] * expert_out[row_of_slot[t*k+j]] in fp64; a token
+    with an unassigned slot (row -1) gets a NaN row."""
+    rows = row_of_slot.reshape(T, k).astype(np.int64)
+    w = decode(weights, w_dtype).reshape(T, k)
+    H = expert_out.shape[1] if expert_out is not None and expert_out.ndim == 2 else 0
+    c = np.zeros((T, H), dtype=np.float64)
+    y = decode(expert_out, dtype) if H else None
+    for j in range(k):
+        rj = rows[:, j]
+        good = rj >= 0
+        contrib = np.full((T, H), np.nan)
+        contrib[good] = w[good, j][:, None] * y[rj[good]]
+        c += contrib
+    return c
+
+
+def combine(expert_out, row_of_slot, weights, w_dtype, T, k, dtype):
+    """out [T, H] in the model dtype."""
+    return round_to(combine_fp64(expert_out, row_of_slot, weights, w_dtype, T, k, dtype), dtype)
+
+
+def combine_add_rmsnorm(expert_out, row_of_slot, weights, w_dtype, shared, residual,
+                        gamma, eps, T, k, dtype):
+    """aclnnMoeDistributeCombineAddRmsNormV2, formula (local part):
+      combineOut = sum_j (w_j * y_j + w_j * s)      s = shared-expert row (0 if absent)
+      x          = combineOut + residual
+      rstd       = 1 / sqrt(mean_H(x^2) + eps)
+      y          = x * rstd * gamma
+    Returns (y, x_out) in the model dtype and rstd fp32 [T]. Statistics use the
+    unrounded x; gamma is fp32 (ruDNN user guide, "7. LayerNorm, RMSNorm and
+    Softmax": affine parameters stay F32)."""
+    c = combine_fp64(expert_out, row_of_slot, weights, w_dtype, T, k, dtype)
+    if shared is not None:
+        wsum = decode(weights, w_dtype).reshape(T, k).sum(axis=1)
+        c = c + wsum[:, None] * decode(shared, dtype)
+    x = c + decode(residual, dtype)
+    rstd = 1.0 / np.sqrt((x * x).mean(axis=1) + float(eps))
+    y = x * rstd[:, None] * np.asarray(gamma, dtype=np.float32).astype(np.float64)[None, :]
+    return round_to(y, dtype), round_to(x, dtype), rstd.astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# whole local forward  (ruDNN user guide, "6. Calling MoE": forward(input,
+# logits, options) = route -> dispatch -> forward_dispatched -> combine)
+# --------------------------------------------------------------------------
+def forward(x, logits, logits_dtype, top_k, renormalize, weights_of, E, dtype):
+    idx, w = route(logits, logits_dtype, top_k, renormalize)
+    d = dispatch(idx, E, x)
+    T = x.shape[0]
+    y = experts_forward_dispatched(d["x_disp"], d["offsets"], weights_of, dtype)
+    if y is None:
+        return idx, w, d, None, round_to(np.zeros((T, x.shape[1])), dtype)
+    return idx, w, d, y, combine(y, d["row_of_slot"], w, logits_dtype, T, top_k, dtype)
+
+
+def expert_out_rows(x, indices, tokens, weights_of, dtype):
+    """Expert outputs for the (token, slot) pairs of the given tokens only:
+    returns {(t, j): y row} computed one by one, for sampled checks at sizes
+    where the full forward is too slow. x [T, H]; indices [T, k]."""
+    need = {}
+    for t in tokens:
+        for j, e in enumerate(indices[t]):
+            need.setdefault(int(e), []).append((int(t), j))
+    out = {}
+    for e, pairs in sorted(need.items()):
+        wg, wu, wd = weights_of(e)
+        rows = np.stack([x[t] for t, _ in pairs])
+        y = swiglu_expert(rows, wg, wu, wd, dtype)
+        for (t, j), yr in zip(pairs, y):
+            out[(t, j)] = yr
+    return out

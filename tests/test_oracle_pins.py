@@ -1,0 +1,407 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: closed forms
+(tests/golden), brute force on tiny inputs, special cases that reduce to a
+library routine (torch softmax, torch rms_norm, torch bf16 cast, stable
+argsort, bincount), and invariants. The cases are chosen so that a dropped
+term, a wrong sign or index, or a transposed operand fails at least one.
+"""
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _num(s):
+    if s.startswith("ln"):
+        return math.log(int(s[2:]))
+    return float(s)
+
+
+def _frac(s):
+    if s == "nan":
+        return float("nan")
+    return float(Fraction(s))
+
+
+def rng(seed=0):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------- rounding --
+def test_bf16_round_matches_torch_on_fp32_inputs():
+    x = torch.randn(200000, dtype=torch.float32) * torch.exp(torch.randn(200000) * 20)
+    ref = x.to(torch.bfloat16).view(torch.int16).numpy().astype(np.uint16)
+    got = O.round_to(x.numpy().astype(np.float64), "bf16")
+    assert (ref == got).all()
+
+
+def test_bf16_round_ties_and_specials():
+    # 1 + 2^-8 is exactly between 1 and 1+2^-7: ties to even -> 1.0 (0x3F80)
+    # 1 + 3*2^-8 is between 1+2^-7 and 1+2^-6: ties to even -> 1+2^-6 (0x3F82)
+    cases = [(1.0 + 2**-8, 0x3F80), (1.0 + 3 * 2**-8, 0x3F82),
+             # just above the tie, in fp64 only (fp32 would round to the tie first)
+             (1.0 + 2**-8 + 2**-40, 0x3F81),
+             (-2.0, 0xC000), (0.0, 0x0000), (-0.0, 0x8000),
+             (float("inf"), 0x7F80), (float("-inf"), 0xFF80),
+             (3.4e38, 0x7F80),  # past the largest finite bf16 once rounded
+             (2.0**-133, 0x0001),  # smallest bf16 subnormal
+             (2.0**-134, 0x0000),  # tie between 0 and 2^-133 -> even (0)
+             (3 * 2.0**-134, 0x0002)]
+    for v, bits in cases:
+        assert int(O.round_to(np.array([v]), "bf16")[0]) == bits, v
+    assert np.isnan(O.decode(O.round_to(np.array([np.nan]), "bf16"), "bf16")[0])
+
+
+def test_decode_bf16_exact():
+    bits = np.array([0x3F80, 0xC000, 0x7F80, 0x0001, 0x4049], dtype=np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    assert (O.decode(bits, "bf16") == ref).all()
+
+
+# ----------------------------------------------------------------- routing --
+def test_routing_golden_closed_forms():
+    spec = json.load(open(os.path.join(GOLDEN, "routing_closed_form.json")))
+    for case in spec["cases"]:
+        z = np.array([[_num(s) for s in case["logits"]]], dtype=np.float32)
+        idx, w = O.route(z, "f32", case["top_k"], case["renormalize"])
+        assert idx[0].tolist() == case["indices"], case["name"]
+        exp = np.array([_frac(s) for s in case["weights"]])
+        got = w[0].astype(np.float64)
+        assert (np.isnan(got) == np.isnan(exp)).all(), case["name"]
+        ok = ~np.isnan(exp)
+        # fp32 softmax, one renormalisation and one cast: a few fp32 ulps
+        assert np.allclose(got[ok], exp[ok], rtol=4e-7, atol=0), (case["name"], got, exp)
+
+
+def test_softmax_matches_torch():
+    z = rng(1).standard_normal((300, 37)).astype(np.float32) * 4
+    ref = torch.softmax(torch.from_numpy(z).double(), dim=-1).float().numpy()
+    got = O.softmax_fp32(z, "f32")
+    assert np.array_equal(got, ref) or np.abs(got - ref).max() <= 1e-7 * ref.max()
+    assert np.allclose(got.sum(axis=1), 1.0, atol=1e-6)
+
+
+def test_topk_equals_E_is_sorted_softmax():
+    z = rng(2).standard_normal((64, 16)).astype(np.float32)
+    idx, w = O.route(z, "f32", 16, False)
+    p = torch.softmax(torch.from_numpy(z).double(), dim=-1).float()
+    vals, order = torch.sort(p, dim=-1, descending=True, stable=True)
+    assert (idx.astype(np.int64) == order.numpy()).all()
+    assert np.array_equal(w, vals.numpy())
+
+
+def _brute_topk(p, k):
+    """Exhaustive: the k-subset with the largest probabilities in
+    (p desc, id asc) order is the one whose sorted key list is
+    lexicographically best; listed best first."""
+    E = len(p)
+    best = None
+    for sub in itertools.combinations(range(E), k):
+        key = sorted(((-p[i], i) for i in sub))
+        if best is None or key < best:
+            best = key
+    return [i for _, i in best]
+
+
+@pytest.mark.parametrize("E", [1, 2, 3, 5, 6])
+def test_topk_brute_force_tiny(E):
+    g = rng(10 + E)
+    for trial in range(40):
+        # quantised logits force many exact ties
+        z = (g.integers(-3, 4, size=(1, E)) * 0.5).astype(np.float32)
+        p = O.softmax_fp32(z, "f32")[0]
+        for k in range(1, E + 1):
+            idx, _ = O.route(z, "f32", k, False)
+            assert idx[0].tolist() == _brute_topk(p.tolist(), k)
+
+
+def test_renormalize_invariants():
+    z = rng(3).standard_normal((500, 64)).astype(np.float32)
+    for k in (1, 2, 8, 64):
+        idx, w = O.route(z, "f32", k, True)
+        assert np.abs(w.astype(np.float64).sum(axis=1) - 1).max() <= k * 2.0**-23
+        assert (np.diff(w.astype(np.float64), axis=1) <= 0).all()
+        idx2, w2 = O.route(z, "f32", k, False)
+        assert (idx == idx2).all()
+        assert (w2.astype(np.float64).sum(axis=1) <= 1 + 64 * 2.0**-24).all()
+        # renormalised = plain / sum(plain)
+        ratio = w2.astype(np.float64) / w2.astype(np.float64).sum(axis=1, keepdims=True)
+        assert np.allclose(w, ratio, rtol=3e-7, atol=0)
+
+
+def test_k1_renormalized_weight_is_exactly_one():
+    z = rng(4).standard_normal((200, 9)).astype(np.float32)
+    idx, w = O.route(z, "f32", 1, True)
+    assert (w == 1.0).all()
+    assert (idx[:, 0] == z.argmax(axis=1)).all()
+
+
+def test_nan_contract_rows_isolated():
+    z = rng(5).standard_normal((6, 10)).astype(np.float32)
+    idx0, w0 = O.route(z, "f32", 3, True)
+    z2 = z.copy()
+    z2[1, 4] = np.nan
+    z2[3, 0] = np.inf
+    z2[5, :] = -np.inf
+    idx, w = O.route(z2, "f32", 3, True)
+    for r in (1, 3, 5):
+        assert idx[r].tolist() == [0, 1, 2]
+        assert np.isnan(w[r]).all()
+    for r in (0, 2, 4):
+        assert (idx[r] == idx0[r]).all() and np.array_equal(w[r], w0[r])
+
+
+def test_weights_take_logits_dtype():
+    z32 = rng(6).standard_normal((50, 8)).astype(np.float32)
+    zb = O.round_to(z32.astype(np.float64), "bf16")
+    idx, w = O.route(zb, "bf16", 2, True)
+    assert w.dtype == np.uint16
+    zf = O.decode(zb, "bf16").astype(np.float32)
+    idx_f, w_f = O.route(zf, "f32", 2, True)
+    assert (idx == idx_f).all()
+    # one rounding into bf16: within half a bf16 ulp, i.e. 2^-8 relative (plus fp32 rounding)
+    wd = O.decode(w, "bf16")
+    assert (np.abs(wd - w_f) <= (2.0**-8 + 2.0**-23) * np.abs(w_f)).all()
+    z16 = z32.astype(np.float16)
+    idx16, w16 = O.route(z16, "f16", 2, False)
+    assert w16.dtype == np.float16
+
+
+def test_route_rejects_bad_top_k():
+    z = np.zeros((2, 4), np.float32)
+    for k in (0, 5):
+        with pytest.raises(ValueError):
+            O.route(z, "f32", k, True)
+
+
+# ---------------------------------------------------------------- dispatch --
+def test_dispatch_invariants():
+    g = rng(7)
+    T, k, E, H = 97, 3, 11, 5
+    idx = np.stack([g.permutation(E)[:k] for _ in range(T)]).astype(np.uint32)
+    x = g.standard_normal((T, H)).astype(np.float32)
+    d = O.dispatch(idx, E, x)
+    counts = np.bincount(idx.ravel().astype(np.int64), minlength=E)
+    assert (np.diff(d["offsets"]) == counts).all() and d["offsets"][0] == 0
+    assert d["offsets"][-1] == T * k
+    order = np.argsort(idx.ravel(), kind="stable")
+    assert (d["slot_of_row"] == order).all()
+    assert (d["row_of_slot"][d["slot_of_row"]] == np.arange(T * k)).all()
+    assert np.array_equal(d["x_disp"], x[order // k])
+    # every row of expert e holds a slot routed to e
+    for e in range(E):
+        sl = d["slot_of_row"][d["offsets"][e]:d["offsets"][e + 1]]
+        assert (idx.ravel()[sl] == e).all()
+
+
+def test_dispatch_out_of_range_ids_are_dropped():
+    idx = np.array([[0, 5], [2, 1], [9, 0]], dtype=np.uint32)
+    d = O.dispatch(idx, 3)
+    assert d["offsets"].tolist() == [0, 2, 3, 4]
+    assert d["row_of_slot"].tolist() == [0, -1, 3, 2, -1, 1]
+    assert d["slot_of_row"].tolist() == [0, 5, 3, 2]
+
+
+# ----------------------------------------------------------------- experts --
+def _torch_swiglu(x, wg, wu, wd):
+    x, wg, wu, wd = (torch.from_numpy(np.asarray(a, np.float64)) for a in (x, wg, wu, wd))
+    return (torch.nn.functional.silu(x @ wg.T) * (x @ wu.T)) @ wd.T
+
+
+def test_swiglu_expert_fp32_matches_dense_torch():
+    g = rng(8)
+    n, H, I = 7, 12, 20  # H != I so a transposed operand cannot pass
+    x = g.standard_normal((n, H)).astype(np.float32)
+    wg = g.standard_normal((I, H)).astype(np.float32) / np.sqrt(H)
+    wu = g.standard_normal((I, H)).astype(np.float32) / np.sqrt(H)
+    wd = g.standard_normal((H, I)).astype(np.float32) / np.sqrt(I)
+    got = O.swiglu_expert(x, wg, wu, wd, "f32").astype(np.float64)
+    ref = _torch_swiglu(x, wg, wu, wd).numpy()
+    # the oracle rounds h to fp32 once; that bounds the difference
+    assert np.allclose(got, ref, rtol=1e-6, atol=1e-6)
+    # swapping gate and up changes the result (SiLU applies to the gate)
+    swapped = O.swiglu_expert(x, wu, wg, wd, "f32").astype(np.float64)
+    assert not np.allclose(swapped, ref, rtol=1e-3, atol=1e-3)
+
+
+def test_swiglu_expert_bf16_rounding_points():
+    g = rng(9)
+    n, H, I = 5, 16, 24
+    b = lambda a: O.round_to(a, "bf16")  # noqa: E731
+    x, wg, wu = b(g.standard_normal((n, H))), b(g.standard_normal((I, H)) / 4), b(g.standard_normal((I, H)) / 4)
+    wd = b(g.standard_normal((H, I)) / 5)
+    got = O.swiglu_expert(x, wg, wu, wd, "bf16")
+    xt, wgt, wut, wdt = (torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).double() for a in (x, wg, wu, wd))
+    h = (torch.nn.functional.silu(xt @ wgt.T) * (xt @ wut.T)).to(torch.bfloat16).double()
+    ref = (h @ wdt.T).numpy()
+    gotd = O.decode(got, "bf16")
+    # torch's double->bf16 cast passes through fp32; allow one bf16 ulp
+    assert np.allclose(gotd, ref, rtol=2.0**-7, atol=1e-30)
+
+
+def test_power_of_two_linearity_of_down_projection():
+    g = rng(10)
+    n, H, I = 6, 8, 12
+    b = lambda a: O.round_to(a, "bf16")  # noqa: E731
+    x, wg, wu, wd = b(g.standard_normal((n, H))), b(g.standard_normal((I, H))), b(g.standard_normal((I, H))), b(g.standard_normal((H, I)))
+    y1 = O.decode(O.swiglu_expert(x, wg, wu, wd, "bf16"), "bf16")
+    wd2 = O.round_to(2 * O.decode(wd, "bf16"), "bf16")
+    y2 = O.decode(O.swiglu_expert(x, wg, wu, wd2, "bf16"), "bf16")
+    assert np.array_equal(2 * y1, y2)
+
+
+def _weights(g, E, H, I):
+    wg = g.standard_normal((E, I, H)).astype(np.float32) / np.sqrt(H)
+    wu = g.standard_normal((E, I, H)).astype(np.float32) / np.sqrt(H)
+    wd = g.standard_normal((E, H, I)).astype(np.float32) / np.sqrt(I)
+    return wg, wu, wd
+
+
+def test_forward_one_hot_equals_dense_swiglu_of_argmax_expert():
+    g = rng(11)
+    T, H, I, E = 33, 10, 14, 5
+    x = g.standard_normal((T, H)).astype(np.float32)
+    z = g.standard_normal((T, E)).astype(np.float32)
+    wg, wu, wd = _weights(g, E, H, I)
+    idx, w, d, y, out = O.forward(x, z, "f32", 1, True, lambda e: (wg[e], wu[e], wd[e]), E, "f32")
+    assert (w == 1.0).all()
+    am = z.argmax(axis=1)
+    ref = np.stack([_torch_swiglu(x[t:t + 1], wg[am[t]], wu[am[t]], wd[am[t]]).numpy()[0] for t in range(T)])
+    assert np.allclose(out, ref, rtol=1e-6, atol=1e-6)
+
+
+def test_single_expert_reduces_to_dense_swiglu():
+    g = rng(12)
+    T, H, I = 9, 6, 10
+    x = g.standard_normal((T, H)).astype(np.float32)
+    z = g.standard_normal((T, 1)).astype(np.float32)
+    wg, wu, wd = _weights(g, 1, H, I)
+    _, _, _, _, out = O.forward(x, z, "f32", 1, False, lambda e: (wg[e], wu[e], wd[e]), 1, "f32")
+    ref = _torch_swiglu(x, wg[0], wu[0], wd[0]).numpy()
+    assert np.allclose(out, ref, rtol=1e-6, atol=1e-6)
+
+
+def test_forward_top2_matches_weighted_dense_mixture():
+    """Dense reference: every expert on every token, weighted by the routing
+    weights of the selected experts (zero elsewhere)."""
+    g = rng(13)
+    T, H, I, E, k = 21, 8, 12, 6, 2
+    x = g.standard_normal((T, H)).astype(np.float32)
+    z = g.standard_normal((T, E)).astype(np.float32)
+    wg, wu, wd = _weights(g, E, H, I)
+    idx, w, d, y, out = O.forward(x, z, "f32", k, True, lambda e: (wg[e], wu[e], wd[e]), E, "f32")
+    dense = np.stack([_torch_swiglu(x, wg[e], wu[e], wd[e]).numpy() for e in range(E)], 1)  # [T,E,H]
+    gate = np.zeros((T, E))
+    p = torch.softmax(torch.from_numpy(z).double(), -1).numpy()
+    top = np.argsort(-p, axis=1, kind="stable")[:, :k]
+    for t in range(T):
+        gate[t, top[t]] = p[t, top[t]] / p[t, top[t]].sum()
+    ref = np.einsum("te,teh->th", gate, dense)
+    assert np.allclose(out, ref, rtol=1e-5, atol=1e-6)
+
+
+def test_expert_out_rows_matches_full_forward():
+    g = rng(14)
+    T, H, I, E, k = 40, 8, 12, 5, 2
+    x = g.standard_normal((T, H)).astype(np.float32)
+    z = g.standard_normal((T, E)).astype(np.float32)
+    wg, wu, wd = _weights(g, E, H, I)
+    wo = lambda e: (wg[e], wu[e], wd[e])  # noqa: E731
+    idx, w, d, y, out = O.forward(x, z, "f32", k, True, wo, E, "f32")
+    rows = O.expert_out_rows(x, idx, [0, 7, 39], wo, "f32")
+    for (t, j), yr in rows.items():
+        assert np.array_equal(yr, y[d["row_of_slot"][t * k + j]])
+
+
+# ----------------------------------------------------------------- combine --
+def test_combine_k1_unit_weight_is_exact_gather():
+    g = rng(15)
+    T, H = 12, 9
+    y = O.round_to(g.standard_normal((T, H)), "bf16")
+    perm = g.permutation(T).astype(np.int32)
+    w = np.ones((T, 1), np.float32)
+    out = O.combine(y, perm, w, "f32", T, 1, "bf16")
+    assert np.array_equal(out, y[perm])
+
+
+def test_combine_weighted_sum_matches_torch():
+    g = rng(16)
+    T, k, H = 10, 3, 7
+    y = g.standard_normal((T * k, H)).astype(np.float32)
+    ros = g.permutation(T * k).astype(np.int32)
+    w = g.random((T, k)).astype(np.float32)
+    out = O.combine(y, ros, w, "f32", T, k, "f32")
+    ref = torch.einsum("tj,tjh->th", torch.from_numpy(w).double(),
+                       torch.from_numpy(y).double()[torch.from_numpy(ros).long()].reshape(T, k, H))
+    assert np.allclose(out, ref.numpy(), rtol=1e-7, atol=1e-7)
+
+
+def test_combine_unassigned_slot_gives_nan_row():
+    y = np.ones((3, 4), np.float32)
+    out = O.combine(y, np.array([0, -1, 1, 2], np.int32), np.ones((2, 2), np.float32), "f32", 2, 2, "f32")
+    assert np.isnan(out[0]).all() and (out[1] == 2).all()
+
+
+def test_rmsnorm_matches_torch_rms_norm():
+    g = rng(17)
+    T, k, H = 6, 2, 32
+    y = g.standard_normal((T * k, H)).astype(np.float32)
+    ros = np.arange(T * k, dtype=np.int32)
+    w = np.full((T, k), 0.5, np.float32)
+    res = g.standard_normal((T, H)).astype(np.float32)
+    gamma = g.uniform(0.5, 1.5, H).astype(np.float32)
+    yo, xo, rstd = O.combine_add_rmsnorm(y, ros, w, "f32", None, res, gamma, 1e-6, T, k, "f32")
+    x = torch.from_numpy(y).double().reshape(T, k, H).mul(0.5).sum(1) + torch.from_numpy(res).double()
+    ref = torch.nn.functional.rms_norm(x, (H,), torch.from_numpy(gamma).double(), 1e-6)
+    assert np.allclose(yo, ref.numpy(), rtol=1e-6, atol=1e-6)
+    assert np.allclose(xo, x.numpy(), rtol=1e-7, atol=1e-7)
+    assert np.allclose(rstd, torch.rsqrt(x.pow(2).mean(-1) + 1e-6).numpy(), rtol=1e-7)
+
+
+def test_rmsnorm_constant_rows_closed_form():
+    T, H, c, eps = 3, 16, 0.75, 1e-6
+    y = np.zeros((T, H), np.float32)
+    res = np.full((T, H), c, np.float32)
+    gamma = np.full(H, 2.0, np.float32)
+    yo, xo, rstd = O.combine_add_rmsnorm(y, np.arange(T, dtype=np.int32), np.ones((T, 1), np.float32),
+                                         "f32", None, res, gamma, eps, T, 1, "f32")
+    r = 1 / math.sqrt(c * c + eps)
+    assert np.allclose(rstd, r, rtol=1e-7)
+    assert np.allclose(yo, 2 * c * r, rtol=1e-7)
+    assert (xo == c).all()
+
+
+def test_shared_term_reading_equals_sum_plus_shared_when_renormalized():
+    g = rng(18)
+    T, k, H = 8, 3, 10
+    y = g.standard_normal((T * k, H)).astype(np.float32)
+    ros = np.arange(T * k, dtype=np.int32)
+    z = g.standard_normal((T, 6)).astype(np.float32)
+    _, w = O.route(z, "f32", k, True)
+    s = g.standard_normal((T, H)).astype(np.float32)
+    r = g.standard_normal((T, H)).astype(np.float32)
+    gamma = np.ones(H, np.float32)
+    _, xo, _ = O.combine_add_rmsnorm(y, ros, w, "f32", s, r, gamma, 1e-6, T, k, "f32")
+    ref = np.einsum("tj,tjh->th", w.astype(np.float64), y.reshape(T, k, H).astype(np.float64)) + s + r
+    assert np.allclose(xo, ref, rtol=1e-6, atol=1e-6)
+
+
+def test_rmsnorm_nan_weights_propagate_to_row_only():
+    T, k, H = 3, 2, 8
+    y = np.ones((T * k, H), np.float32)
+    w = np.full((T, k), 0.5, np.float32)
+    w[1] = np.nan
+    yo, xo, rstd = O.combine_add_rmsnorm(y, np.arange(T * k, dtype=np.int32), w, "f32", None,
+                                         np.zeros((T, H), np.float32), np.ones(H, np.float32), 1e-6, T, k, "f32")
+    assert np.isnan(yo[1]).all() and np.isnan(rstd[1])
+    assert np.isfinite(yo[[0, 2]]).all()
