@@ -1,0 +1,203 @@
+"""Benchmark of the local MoE FFN forward on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+route -> dispatch (maps) -> experts gate/up (+SiLU*up) -> experts down ->
+combine, each through the C ABI on the current stream, inputs resident in
+HBM. Default workload: the Mixtral-shaped bf16 batch (T=4096, H=4096,
+I=14336, E=8, top_k=2, renormalize). Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+The dominant kernel (the gate/up grouped GEMM) is bracketed by HIP events on
+the stream it runs on, every timed step; its average duration gives the
+roofline figure. The CPU baseline times the oracle on the first tokens of the
+same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE fwd tokens/s; expert GEMM TFLOP/s (% MFMA peak); combine GB/s (% HBM)"
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral_8x_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=2048,
+                    help="tokens of the workload the CPU oracle runs on")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no "
+              "multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from mixture_experts_ffn_top_amd import inputs as I
+    from mixture_experts_ffn_top_amd import moe
+
+    w = I.workload(args.workload)
+    T, H, I_, E, k = w.T, w.H, w.I, w.E, w.top_k
+    R = T * k
+    td = {"bf16": torch.bfloat16, "f32": torch.float32}[w.dtype]
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    moe.lib()
+
+    def to_dev(a, dtype=w.dtype):
+        if dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+    # ---- inputs (host generation, then resident in HBM) --------------------
+    t0 = time.time()
+    z = I.logits_for(w)
+    x = I.tokens_for(w)
+    n_cpu = min(args.cpu_tokens, T)
+    keep = set()
+    if not args.no_cpu_baseline:
+        from oracle import moe_oracle as O
+        idx_s, _ = O.route(z[:n_cpu], "f32", k, w.renormalize)
+        keep = set(int(e) for e in idx_s.ravel())
+    wt = {}
+    kept = {e: {} for e in keep}
+    for name in ("w_gate", "w_up", "w_down"):
+        shape = (E, I_, H) if name != "w_down" else (E, H, I_)
+        t = torch.empty(shape, dtype=td, device=dev)
+        for e0 in range(0, E, 16):
+            ex = list(range(e0, min(E, e0 + 16)))
+            a = I.expert_weights(w, name, ex)
+            t[ex[0]:ex[-1] + 1].copy_(torch.from_numpy(a.view(np.int16) if w.dtype == "bf16" else a).view(td))
+            for i, e in enumerate(ex):
+                if e in kept:
+                    kept[e][name] = a[i].copy()
+            del a
+        wt[name] = t
+    xd, zd = to_dev(x), to_dev(z, "f32")
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.time() - t0:.1f}s: {args.workload} T={T} H={H} I={I_} E={E} k={k}")
+
+    # ---- buffers ----------------------------------------------------------
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    wts = torch.empty((T, k), dtype=torch.float32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    sor = torch.empty(R, dtype=torch.int32, device=dev)
+    ros = torch.empty(R, dtype=torch.int32, device=dev)
+    h = torch.empty((R, I_), dtype=td, device=dev)
+    y = torch.empty((R, H), dtype=td, device=dev)
+    out = torch.empty((T, H), dtype=td, device=dev)
+    ws_d = torch.empty(max(moe.moe_dispatch_workspace_size(T, k, E), 1), dtype=torch.uint8, device=dev)
+    ws_g = torch.empty(max(moe.moe_experts_gemm_workspace_size(R, E, td), 1), dtype=torch.uint8, device=dev)
+    ws_g2 = torch.empty_like(ws_g)
+
+    stages = ["route", "dispatch", "gate_up", "down", "combine"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        moe.moe_route(zd, k, w.renormalize, indices=idx, weights=wts)
+        mark(1)
+        moe.moe_dispatch(idx, E, ws=ws_d, offsets=offsets, slot_of_row=sor, row_of_slot=ros)
+        mark(2)
+        moe.moe_experts_gate_up(xd, offsets, wt["w_gate"], wt["w_up"], row_map=sor, map_div=k,
+                                rows=R, h=h, ws=ws_g)
+        mark(3)
+        moe.moe_experts_down(h, offsets, wt["w_down"], expert_out=y, ws=ws_g2)
+        mark(4)
+        moe.moe_combine(y, ros, wts, out=out)
+        mark(5)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    elapsed = t_end - t_start
+    log(f"timed {args.steps} steps in {elapsed:.3f}s")
+
+    stage_ms = {name: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
+                for i, name in enumerate(stages)}
+    ms_step = elapsed / args.steps * 1e3
+    tokens_per_s = T * args.steps / elapsed
+
+    # ---- roofline of the dominant kernel (gate/up grouped GEMM) -----------
+    flops_gate_up = 4.0 * R * H * I_  # two [R,H]x[H,I] products per launch
+    flops_down = 2.0 * R * H * I_
+    gu_s = stage_ms["gate_up"] / 1e3
+    achieved = flops_gate_up / gu_s / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    counts = np.diff(offsets.cpu().numpy())
+    touched = int((counts > 0).sum())
+    es = 2 if w.dtype == "bf16" else 4
+    combine_bytes = R * H * es + R * 4 + R * 4 + T * H * es
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": None,
+                "kernel": "mfma_gemm_kernel<bf16, gate/up+SiLU>" if w.dtype == "bf16" else "gate/up GEMM",
+                "flops_per_launch": flops_gate_up}
+    expert_tflops = (flops_gate_up + flops_down) / ((stage_ms["gate_up"] + stage_ms["down"]) / 1e3) / 1e12
+    extra = {
+        "stages_ms": {k_: round(v, 4) for k_, v in stage_ms.items()},
+        "expert_gemm_tflops": round(expert_tflops, 1),
+        "expert_gemm_frac_peak": round(expert_tflops / peak, 4),
+        "combine_gbs": round(combine_bytes / (stage_ms["combine"] / 1e3) / 1e9, 1),
+        "combine_frac_hbm": round(combine_bytes / (stage_ms["combine"] / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+        "experts_touched": touched,
+    }
+
+    # ---- CPU baseline: the oracle on the first tokens of the workload -----
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import moe_oracle as O
+        cores = len(os.sched_getaffinity(0))
+        wo = lambda e: (kept[e]["w_gate"], kept[e]["w_up"], kept[e]["w_down"])  # noqa: E731
+        log(f"cpu baseline: oracle on {n_cpu} tokens")
+        c0 = time.perf_counter()
+        O.forward(x[:n_cpu], z[:n_cpu], "f32", k, w.renormalize, wo, E, w.dtype)
+        c_el = time.perf_counter() - c0
+        cpu = {"value": round(n_cpu / c_el, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+               "sample": f"first {n_cpu} of {T} tokens of {args.workload}; route, dispatch, "
+                         f"fp64 SwiGLU experts, combine; {c_el:.1f}s wall"}
+
+    res = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "T": T, "H": H, "I": I_, "E": E, "top_k": k,
+                   "renormalize": w.renormalize, "logits_dtype": "f32"},
+        "roofline": roofline, "cpu_baseline": cpu,
+    }
+    res.update(extra)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,220 @@
+/*
+ * moe_ffn.h - C ABI of the local Mixture-of-Experts FFN forward for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The computation (ruDNN user guide, "3. MoE workflow"):
+ *   logits -> fp32 softmax over all experts -> top-k -> compact dispatch ->
+ *   bias-free SwiGLU experts -> weighted combine restoring token order,
+ * plus the fused combine + residual Add + RMSNorm epilogue of the CANN
+ * operator aclnnMoeDistributeCombineAddRmsNormV2 ("function description",
+ * formula), restricted to one device.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Tensors are dense, row-major, caller-owned DEVICE memory on the device
+ *    of `stream` (e.g. allocated by PyTorch). The library allocates nothing
+ *    and keeps no state between calls.
+ *  - Scratch memory is caller-provided: each call that needs it takes
+ *    (`ws`, `ws_bytes`) and has a `*_workspace_size` query returning the
+ *    bytes it needs (the two-phase "get workspace size, then execute on a
+ *    stream" convention of the CANN operator pages). `ws` must be 256-byte
+ *    aligned. Concurrent calls need distinct workspaces.
+ *  - Every call validates its arguments on the host before enqueueing
+ *    anything; on error nothing is enqueued and a status is returned
+ *    (ruDNN user guide, "3. MoE workflow": invalid shapes, dtypes or other
+ *    arguments are errors; "6. Calling MoE": shape, dtype or device
+ *    mismatches are errors). On success the work is enqueued on `stream`
+ *    and the call returns without synchronising the host.
+ *  - T = 0 is a successful no-op. NaN / +inf / -inf logits are data, not
+ *    errors (routing contract, below).
+ *  - Sizes are int64_t; T*top_k must fit in int32; E <= 1024.
+ *  - Row lengths H and I must be multiples of 8 elements (16 bytes of
+ *    bf16/f16; fp32 tensors are also read in 8-element steps).
+ */
+#ifndef MOE_FFN_H
+#define MOE_FFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_dtype {
+  MOE_F32 = 0,
+  MOE_F16 = 1,
+  MOE_BF16 = 2
+} moe_dtype;
+
+typedef enum moe_status {
+  MOE_SUCCESS = 0,
+  MOE_ERROR_NULL_POINTER = 1, /* a required pointer is NULL */
+  MOE_ERROR_SHAPE = 2,        /* negative or inconsistent sizes */
+  MOE_ERROR_DTYPE = 3,        /* unknown dtype, or x/weights dtypes differ */
+  MOE_ERROR_ARGUMENT = 4,     /* top_k outside [1, E]; eps not finite or <= 0;
+                                 an output overlaps an input or another output */
+  MOE_ERROR_DEVICE = 5,       /* a pointer is not device memory of the stream's device */
+  MOE_ERROR_WORKSPACE = 6,    /* workspace NULL, misaligned or too small */
+  MOE_ERROR_UNSUPPORTED = 7,  /* E > 1024, T*top_k > INT32_MAX, H or I not a multiple of 8 */
+  MOE_ERROR_HIP = 8           /* a HIP launch or query failed */
+} moe_status;
+
+/* Human-readable name of a status (static string, never NULL). */
+const char* moe_status_string(moe_status s);
+
+/*
+ * moe_route - routing plan from logits.
+ * Passage: ruDNN user guide, "4. Routing contract".
+ *   logits   [T, E], dtype logits_dt (F32, F16 or BF16), read only.
+ *   For each token: p = softmax over all E experts, computed in fp32; the
+ *   top_k experts by p are selected, largest first, equal p favouring the
+ *   lower expert id. With renormalize != 0 the selected p are divided by
+ *   their sum. Weights are then converted to logits_dt.
+ *   A row that contains a NaN, contains +inf, or is entirely -inf keeps NaN
+ *   weights (no uniform fallback); its indices are 0..top_k-1 (NaNs tie, and
+ *   ties favour the lower id).
+ *   indices  [T, top_k] uint32, written.
+ *   weights  [T, top_k] logits_dt, written.
+ * Errors: ARGUMENT if top_k not in [1, E]; UNSUPPORTED if E > 1024.
+ */
+moe_status moe_route(const void* logits, moe_dtype logits_dt, int64_t T, int64_t E,
+                     int64_t top_k, int renormalize, uint32_t* indices, void* weights,
+                     hipStream_t stream);
+
+/*
+ * moe_dispatch - compact grouping of tokens by expert, no capacity drop.
+ * Passage: ruDNN user guide, "5. Expert weights and dispatch" (no token is
+ * dropped to enforce a capacity; a saved map restores token order).
+ *   indices        [T, top_k] uint32 expert ids (e.g. from moe_route), read.
+ *   x              [T, H] dtype dt, read; may be NULL only if x_disp is NULL.
+ *   x_disp         [T*top_k, H] dtype dt, written: rows grouped by expert;
+ *                  may be NULL (maps only).
+ *   expert_offsets [E+1] int32, written: rows of expert e are
+ *                  expert_offsets[e] .. expert_offsets[e+1]-1.
+ *   slot_of_row    [T*top_k] int32, written: flat slot t*top_k+j held by
+ *                  dispatched row r (only the first expert_offsets[E] rows).
+ *   row_of_slot    [T*top_k] int32, written: the inverse map (-1 for a slot
+ *                  whose expert id is >= E; such slots are not dispatched).
+ *   Order inside an expert: increasing flat slot (deterministic; the pages
+ *   leave this order free).
+ *   ws / ws_bytes  scratch, at least moe_dispatch_workspace_size(T, top_k, E).
+ */
+moe_status moe_dispatch(const uint32_t* indices, int64_t T, int64_t top_k, int64_t E,
+                        const void* x, moe_dtype dt, int64_t H, void* x_disp,
+                        int32_t* expert_offsets, int32_t* slot_of_row, int32_t* row_of_slot,
+                        void* ws, size_t ws_bytes, hipStream_t stream);
+size_t moe_dispatch_workspace_size(int64_t T, int64_t top_k, int64_t E);
+
+/*
+ * moe_experts_forward_dispatched - bias-free SwiGLU experts on dispatched rows.
+ * Passages: ruDNN user guide, "3. MoE workflow" (SwiGluExperts::new builds
+ * bias-free expert weights; forward_dispatched computes the dispatched
+ * tokens) and "5. Expert weights and dispatch" (layouts).
+ *   x_disp         [rows, H] dtype dt, read (rows grouped by expert).
+ *   expert_offsets [E+1] int32 device array from moe_dispatch, read on the
+ *                  device (counts never return to the host).
+ *   rows           host upper bound of expert_offsets[E] (normally T*top_k).
+ *   w_gate, w_up   [E, I, H] dtype dt;  w_down [E, H, I] dtype dt.
+ *   For every dispatched row r of expert e:
+ *     h = SiLU(W_gate[e] x_r) * (W_up[e] x_r)    (length I, stored in dt)
+ *     expert_out[r] = W_down[e] h                (length H, stored in dt)
+ *   with SiLU(g) = g / (1 + exp(-g)) and fp32 accumulation.
+ *   expert_out     [rows, H] dtype dt, written for rows < expert_offsets[E].
+ *   ws / ws_bytes  scratch, at least moe_experts_workspace_size(...).
+ * dt: BF16 and F16 run on the matrix cores; F32 on the vector ALUs.
+ */
+moe_status moe_experts_forward_dispatched(const void* x_disp, const int32_t* expert_offsets,
+                                          int64_t rows, int64_t E, int64_t H, int64_t I,
+                                          const void* w_gate, const void* w_up,
+                                          const void* w_down, moe_dtype dt, void* expert_out,
+                                          void* ws, size_t ws_bytes, hipStream_t stream);
+size_t moe_experts_workspace_size(int64_t rows, int64_t E, int64_t H, int64_t I, moe_dtype dt);
+
+/*
+ * moe_experts_gate_up / moe_experts_down - the two halves of
+ * moe_experts_forward_dispatched, for callers that want h or time the GEMMs
+ * separately. Same passages and arithmetic.
+ *   moe_experts_gate_up:  h[r] = SiLU(W_gate[e] a_r) * (W_up[e] a_r), h [rows, I] dt.
+ *     With row_map == NULL, a_r is row r of x (x = x_disp, [rows, H]).
+ *     With row_map != NULL, a_r is row row_map[r] / map_div of x (x = the
+ *     token matrix [ceil(rows/map_div), H]); pass slot_of_row from
+ *     moe_dispatch and map_div = top_k to read tokens without materialising
+ *     x_disp. Map entries are clamped to the rows of x.
+ *   moe_experts_down:  expert_out[r] = W_down[e] h[r], expert_out [rows, H] dt.
+ *   ws / ws_bytes: at least moe_experts_gemm_workspace_size(rows, E, dt)
+ *   (the device-built tile list); one workspace per in-flight call.
+ * Errors: ARGUMENT if row_map is given and map_div is not in [1, rows].
+ */
+moe_status moe_experts_gate_up(const void* x, const int32_t* row_map, int64_t map_div,
+                               const int32_t* expert_offsets, int64_t rows, int64_t E, int64_t H,
+                               int64_t I, const void* w_gate, const void* w_up, moe_dtype dt,
+                               void* h, void* ws, size_t ws_bytes, hipStream_t stream);
+moe_status moe_experts_down(const void* h, const int32_t* expert_offsets, int64_t rows, int64_t E,
+                            int64_t H, int64_t I, const void* w_down, moe_dtype dt,
+                            void* expert_out, void* ws, size_t ws_bytes, hipStream_t stream);
+size_t moe_experts_gemm_workspace_size(int64_t rows, int64_t E, moe_dtype dt);
+
+/*
+ * moe_combine - restore token order and merge expert outputs.
+ * Passage: ruDNN user guide, "6. Calling MoE" (combine uses the dispatch map
+ * to restore token order and merges expert outputs with the routing weights).
+ *   out[t] = sum_{j<top_k} weights[t,j] * expert_out[row_of_slot[t*top_k+j]]
+ *   accumulated in fp32 in j order, stored in dt. A token with a slot whose
+ *   row is -1 gets a NaN row.
+ *   expert_out [rows, H] dt; row_of_slot [T*top_k] int32; weights [T, top_k]
+ *   w_dt; out [T, H] dt (written).
+ */
+moe_status moe_combine(const void* expert_out, const int32_t* row_of_slot, const void* weights,
+                       moe_dtype w_dt, int64_t T, int64_t top_k, int64_t H, moe_dtype dt,
+                       void* out, hipStream_t stream);
+
+/*
+ * moe_forward - the whole local forward: route -> dispatch -> experts ->
+ * combine, on one stream, no host synchronisation.
+ * Passage: ruDNN user guide, "6. Calling MoE" (forward(input, logits,
+ * options) takes precomputed logits; it does not run the model's gate
+ * projection or load weight files).
+ *   x [T, H] dt; logits [T, E] logits_dt; weights as in
+ *   moe_experts_forward_dispatched; out [T, H] dt (written).
+ *   indices_out [T, top_k] uint32 and weights_out [T, top_k] logits_dt are
+ *   optional copies of the routing plan (NULL to skip).
+ *   ws / ws_bytes scratch, at least moe_forward_workspace_size(...).
+ */
+moe_status moe_forward(const void* x, const void* logits, moe_dtype logits_dt, int64_t T,
+                       int64_t H, int64_t I, int64_t E, int64_t top_k, int renormalize,
+                       const void* w_gate, const void* w_up, const void* w_down, moe_dtype dt,
+                       void* out, uint32_t* indices_out, void* weights_out,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+size_t moe_forward_workspace_size(int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k,
+                                  moe_dtype dt, moe_dtype logits_dt);
+
+/*
+ * moe_combine_add_rmsnorm - combine fused with the shared-expert term, the
+ * residual Add and RMSNorm.
+ * Passages: aclnnMoeDistributeCombineAddRmsNormV2, "function description"
+ * (formula) and parameter list (yOut, rstdOut, xOut); ruDNN user guide,
+ * "7. LayerNorm, RMSNorm and Softmax" (fp32 statistics and affine math,
+ * F32 gamma, output in the input dtype, eps finite and > 0).
+ *   c[t]    = sum_j weights[t,j] * (expert_out[row_of_slot[t*k+j]] + shared[t])
+ *             (shared may be NULL: term omitted)
+ *   x[t]    = c[t] + residual[t]
+ *   rstd[t] = 1 / sqrt(mean_H(x[t]^2) + eps)
+ *   y[t]    = x[t] * rstd[t] * gamma
+ *   all in fp32; x_out = x and y stored in dt, rstd in fp32.
+ *   expert_out [rows, H] dt; shared, residual [T, H] dt; gamma [H] fp32;
+ *   y, x_out [T, H] dt (written); rstd [T] fp32 (written).
+ * Errors: ARGUMENT if eps is not finite or <= 0; UNSUPPORTED if H > 32768.
+ */
+moe_status moe_combine_add_rmsnorm(const void* expert_out, const int32_t* row_of_slot,
+                                   const void* weights, moe_dtype w_dt, const void* shared,
+                                   const void* residual, const float* gamma, float eps,
+                                   int64_t T, int64_t top_k, int64_t H, moe_dtype dt,
+                                   void* y, void* x_out, float* rstd, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FFN_H */

@@ -1,0 +1,364 @@
+// C ABI of libmoe_ffn: host-side validation, workspace carving and launches.
+// Every check runs before anything is enqueued; on error nothing is enqueued.
+#include <math.h>
+#include <stdint.h>
+
+#include "kernels.h"
+#include "moe_ffn.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int64_t kMaxE = 1024;
+constexpr int64_t kMaxNormH = 32768;
+
+size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+
+struct Span {
+  const void* p;
+  size_t n;
+};
+
+bool overlaps(Span a, Span b) {
+  if (!a.p || !b.p || !a.n || !b.n) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+  return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+// Each output must be disjoint from every input and every other output.
+bool any_overlap(const Span* outs, int n_out, const Span* ins, int n_in) {
+  for (int i = 0; i < n_out; ++i) {
+    for (int j = 0; j < n_in; ++j)
+      if (overlaps(outs[i], ins[j])) return true;
+    for (int j = i + 1; j < n_out; ++j)
+      if (overlaps(outs[i], outs[j])) return true;
+  }
+  return false;
+}
+
+bool valid_dt(int dt) { return dt == MOE_F32 || dt == MOE_F16 || dt == MOE_BF16; }
+
+moe_status stream_device(hipStream_t s, int* dev) {
+  if (s == nullptr) return hipGetDevice(dev) == hipSuccess ? MOE_SUCCESS : MOE_ERROR_HIP;
+  if (hipStreamGetDevice(s, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return MOE_ERROR_HIP;
+  }
+  return MOE_SUCCESS;
+}
+
+// Pointers must be device (or managed) memory of the stream's device.
+moe_status check_device(const void* const* ptrs, int n, hipStream_t s) {
+  int dev = 0;
+  moe_status st = stream_device(s, &dev);
+  if (st != MOE_SUCCESS) return st;
+  for (int i = 0; i < n; ++i) {
+    if (!ptrs[i]) continue;
+    hipPointerAttribute_t at;
+    if (hipPointerGetAttributes(&at, ptrs[i]) != hipSuccess) {
+      (void)hipGetLastError();
+      return MOE_ERROR_DEVICE;
+    }
+    if (at.type != hipMemoryTypeDevice && at.type != hipMemoryTypeManaged) return MOE_ERROR_DEVICE;
+    if (at.device != dev) return MOE_ERROR_DEVICE;
+  }
+  return MOE_SUCCESS;
+}
+
+moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_SUCCESS : MOE_ERROR_HIP; }
+
+moe_status check_route_args(int64_t T, int64_t E, int64_t top_k, moe_dtype logits_dt) {
+  if (T < 0 || E < 1) return MOE_ERROR_SHAPE;
+  if (!valid_dt(logits_dt)) return MOE_ERROR_DTYPE;
+  if (top_k < 1 || top_k > E) return MOE_ERROR_ARGUMENT;
+  if (E > kMaxE || T * top_k > INT32_MAX) return MOE_ERROR_UNSUPPORTED;
+  return MOE_SUCCESS;
+}
+
+bool row_len_ok(int64_t n) { return n > 0 && n % 8 == 0; }
+
+// Layout of the moe_forward workspace; every piece 256-byte aligned.
+struct ForwardLayout {
+  size_t indices, weights, offsets, slot_of_row, row_of_slot, dispatch, expert_out, experts, total;
+};
+
+ForwardLayout forward_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int dt,
+                             int logits_dt) {
+  ForwardLayout L;
+  const size_t slots = (size_t)(T * k);
+  size_t o = 0;
+  L.indices = o;     o += align256(slots * 4);
+  L.weights = o;     o += align256(slots * dtype_size(logits_dt));
+  L.offsets = o;     o += align256((size_t)(E + 1) * 4);
+  L.slot_of_row = o; o += align256(slots * 4);
+  L.row_of_slot = o; o += align256(slots * 4);
+  L.dispatch = o;    o += align256(dispatch_scratch_bytes((int64_t)slots, E));
+  L.expert_out = o;  o += align256(slots * (size_t)H * dtype_size(dt));
+  L.experts = o;     o += align256(experts_scratch_bytes((int64_t)slots, E, I, dt));
+  L.total = o;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_SUCCESS: return "MOE_SUCCESS";
+    case MOE_ERROR_NULL_POINTER: return "MOE_ERROR_NULL_POINTER";
+    case MOE_ERROR_SHAPE: return "MOE_ERROR_SHAPE";
+    case MOE_ERROR_DTYPE: return "MOE_ERROR_DTYPE";
+    case MOE_ERROR_ARGUMENT: return "MOE_ERROR_ARGUMENT";
+    case MOE_ERROR_DEVICE: return "MOE_ERROR_DEVICE";
+    case MOE_ERROR_WORKSPACE: return "MOE_ERROR_WORKSPACE";
+    case MOE_ERROR_UNSUPPORTED: return "MOE_ERROR_UNSUPPORTED";
+    case MOE_ERROR_HIP: return "MOE_ERROR_HIP";
+  }
+  return "MOE_ERROR_UNKNOWN";
+}
+
+moe_status moe_route(const void* logits, moe_dtype logits_dt, int64_t T, int64_t E, int64_t top_k,
+                     int renormalize, uint32_t* indices, void* weights, hipStream_t stream) {
+  moe_status st = check_route_args(T, E, top_k, logits_dt);
+  if (st != MOE_SUCCESS) return st;
+  if (T == 0) return MOE_SUCCESS;
+  if (!logits || !indices || !weights) return MOE_ERROR_NULL_POINTER;
+  const size_t ls = dtype_size(logits_dt);
+  const Span outs[] = {{indices, (size_t)(T * top_k) * 4}, {weights, (size_t)(T * top_k) * ls}};
+  const Span ins[] = {{logits, (size_t)(T * E) * ls}};
+  if (any_overlap(outs, 2, ins, 1)) return MOE_ERROR_ARGUMENT;
+  const void* ptrs[] = {logits, indices, weights};
+  if ((st = check_device(ptrs, 3, stream)) != MOE_SUCCESS) return st;
+  return from_hip(launch_route(logits, logits_dt, (int)T, (int)E, (int)top_k, renormalize ? 1 : 0,
+                               indices, weights, stream));
+}
+
+size_t moe_dispatch_workspace_size(int64_t T, int64_t top_k, int64_t E) {
+  if (T < 0 || top_k < 1 || E < 1 || E > kMaxE || T * top_k > INT32_MAX) return 0;
+  return align256(dispatch_scratch_bytes(T * top_k, E));
+}
+
+moe_status moe_dispatch(const uint32_t* indices, int64_t T, int64_t top_k, int64_t E,
+                        const void* x, moe_dtype dt, int64_t H, void* x_disp,
+                        int32_t* expert_offsets, int32_t* slot_of_row, int32_t* row_of_slot,
+                        void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (T < 0 || E < 1 || H < 0) return MOE_ERROR_SHAPE;
+  if (!valid_dt(dt)) return MOE_ERROR_DTYPE;
+  if (top_k < 1 || top_k > E) return MOE_ERROR_ARGUMENT;
+  if (E > kMaxE || T * top_k > INT32_MAX) return MOE_ERROR_UNSUPPORTED;
+  if (x_disp && !row_len_ok(H)) return MOE_ERROR_UNSUPPORTED;
+  if (!expert_offsets) return MOE_ERROR_NULL_POINTER;
+  if (T > 0 && (!indices || !slot_of_row || !row_of_slot)) return MOE_ERROR_NULL_POINTER;
+  if (x_disp && !x) return MOE_ERROR_NULL_POINTER;
+  const size_t need = moe_dispatch_workspace_size(T, top_k, E);
+  if (!ws || ((uintptr_t)ws & 255) || ws_bytes < need) return MOE_ERROR_WORKSPACE;
+  const size_t slots = (size_t)(T * top_k), ds = dtype_size(dt);
+  const Span outs[] = {{x_disp, x_disp ? slots * (size_t)H * ds : 0},
+                       {expert_offsets, (size_t)(E + 1) * 4},
+                       {slot_of_row, slots * 4},
+                       {row_of_slot, slots * 4},
+                       {ws, need}};
+  const Span ins[] = {{indices, slots * 4}, {x, x ? (size_t)T * (size_t)H * ds : 0}};
+  if (any_overlap(outs, 5, ins, 2)) return MOE_ERROR_ARGUMENT;
+  const void* ptrs[] = {indices, x, x_disp, expert_offsets, slot_of_row, row_of_slot, ws};
+  moe_status st = check_device(ptrs, 7, stream);
+  if (st != MOE_SUCCESS) return st;
+  hipError_t e = launch_dispatch_maps(indices, (int)slots, (int)E, expert_offsets, slot_of_row,
+                                      row_of_slot, static_cast<int32_t*>(ws), stream);
+  if (e == hipSuccess && x_disp && slots)
+    e = launch_gather_rows(x, dt, (int)H, (int)top_k, slot_of_row, expert_offsets + E, (int)slots,
+                           x_disp, stream);
+  return from_hip(e);
+}
+
+size_t moe_experts_workspace_size(int64_t rows, int64_t E, int64_t H, int64_t I, moe_dtype dt) {
+  if (rows < 0 || E < 1 || E > kMaxE || rows > INT32_MAX || H < 1 || I < 1 || !valid_dt(dt))
+    return 0;
+  return align256(experts_scratch_bytes(rows, E, I, dt));
+}
+
+moe_status moe_experts_forward_dispatched(const void* x_disp, const int32_t* expert_offsets,
+                                          int64_t rows, int64_t E, int64_t H, int64_t I,
+                                          const void* w_gate, const void* w_up,
+                                          const void* w_down, moe_dtype dt, void* expert_out,
+                                          void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (rows < 0 || E < 1 || H < 1 || I < 1) return MOE_ERROR_SHAPE;
+  if (!valid_dt(dt)) return MOE_ERROR_DTYPE;
+  if (E > kMaxE || rows > INT32_MAX || !row_len_ok(H) || !row_len_ok(I))
+    return MOE_ERROR_UNSUPPORTED;
+  if (rows == 0) return MOE_SUCCESS;
+  if (!x_disp || !expert_offsets || !w_gate || !w_up || !w_down || !expert_out)
+    return MOE_ERROR_NULL_POINTER;
+  const size_t need = moe_experts_workspace_size(rows, E, H, I, dt);
+  if (!ws || ((uintptr_t)ws & 255) || ws_bytes < need) return MOE_ERROR_WORKSPACE;
+  const size_t ds = dtype_size(dt), wbytes = (size_t)E * (size_t)I * (size_t)H * ds;
+  const Span outs[] = {{expert_out, (size_t)rows * (size_t)H * ds}, {ws, need}};
+  const Span ins[] = {{x_disp, (size_t)rows * (size_t)H * ds},
+                      {expert_offsets, (size_t)(E + 1) * 4},
+                      {w_gate, wbytes}, {w_up, wbytes}, {w_down, wbytes}};
+  if (any_overlap(outs, 2, ins, 5)) return MOE_ERROR_ARGUMENT;
+  const void* ptrs[] = {x_disp, expert_offsets, w_gate, w_up, w_down, expert_out, ws};
+  moe_status st = check_device(ptrs, 7, stream);
+  if (st != MOE_SUCCESS) return st;
+  return from_hip(launch_experts(x_disp, nullptr, 1, expert_offsets, (int)rows, (int)E, (int)H,
+                                 (int)I, w_gate, w_up, w_down, dt, expert_out, ws, stream));
+}
+
+size_t moe_experts_gemm_workspace_size(int64_t rows, int64_t E, moe_dtype dt) {
+  if (rows < 0 || E < 1 || E > kMaxE || rows > INT32_MAX || !valid_dt(dt)) return 0;
+  return align256(tile_scratch_bytes(rows, E, dt));
+}
+
+moe_status moe_experts_gate_up(const void* x, const int32_t* row_map, int64_t map_div,
+                               const int32_t* expert_offsets, int64_t rows, int64_t E, int64_t H,
+                               int64_t I, const void* w_gate, const void* w_up, moe_dtype dt,
+                               void* h, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (rows < 0 || E < 1 || H < 1 || I < 1) return MOE_ERROR_SHAPE;
+  if (!valid_dt(dt)) return MOE_ERROR_DTYPE;
+  if (row_map && (map_div < 1 || map_div > rows)) return MOE_ERROR_ARGUMENT;
+  if (E > kMaxE || rows > INT32_MAX || !row_len_ok(H) || !row_len_ok(I))
+    return MOE_ERROR_UNSUPPORTED;
+  if (rows == 0) return MOE_SUCCESS;
+  if (!x || !expert_offsets || !w_gate || !w_up || !h) return MOE_ERROR_NULL_POINTER;
+  const size_t need = moe_experts_gemm_workspace_size(rows, E, dt);
+  if (!ws || ((uintptr_t)ws & 255) || ws_bytes < need) return MOE_ERROR_WORKSPACE;
+  const size_t ds = dtype_size(dt), wbytes = (size_t)E * (size_t)I * (size_t)H * ds;
+  const size_t x_rows = row_map ? (size_t)((rows + map_div - 1) / map_div) : (size_t)rows;
+  const Span outs[] = {{h, (size_t)rows * (size_t)I * ds}, {ws, need}};
+  const Span ins[] = {{x, x_rows * (size_t)H * ds}, {row_map, row_map ? (size_t)rows * 4 : 0},
+                      {expert_offsets, (size_t)(E + 1) * 4}, {w_gate, wbytes}, {w_up, wbytes}};
+  if (any_overlap(outs, 2, ins, 5)) return MOE_ERROR_ARGUMENT;
+  const void* ptrs[] = {x, row_map, expert_offsets, w_gate, w_up, h, ws};
+  moe_status st = check_device(ptrs, 7, stream);
+  if (st != MOE_SUCCESS) return st;
+  return from_hip(launch_gate_up(x, row_map, row_map ? (int)map_div : 1, expert_offsets, (int)rows,
+                                 (int)E, (int)H, (int)I, w_gate, w_up, dt, h, ws, stream));
+}
+
+moe_status moe_experts_down(const void* h, const int32_t* expert_offsets, int64_t rows, int64_t E,
+                            int64_t H, int64_t I, const void* w_down, moe_dtype dt,
+                            void* expert_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (rows < 0 || E < 1 || H < 1 || I < 1) return MOE_ERROR_SHAPE;
+  if (!valid_dt(dt)) return MOE_ERROR_DTYPE;
+  if (E > kMaxE || rows > INT32_MAX || !row_len_ok(H) || !row_len_ok(I))
+    return MOE_ERROR_UNSUPPORTED;
+  if (rows == 0) return MOE_SUCCESS;
+  if (!h || !expert_offsets || !w_down || !expert_out) return MOE_ERROR_NULL_POINTER;
+  const size_t need = moe_experts_gemm_workspace_size(rows, E, dt);
+  if (!ws || ((uintptr_t)ws & 255) || ws_bytes < need) return MOE_ERROR_WORKSPACE;
+  const size_t ds = dtype_size(dt), wbytes = (size_t)E * (size_t)I * (size_t)H * ds;
+  const Span outs[] = {{expert_out, (size_t)rows * (size_t)H * ds}, {ws, need}};
+  const Span ins[] = {{h, (size_t)rows * (size_t)I * ds}, {expert_offsets, (size_t)(E + 1) * 4},
+                      {w_down, wbytes}};
+  if (any_overlap(outs, 2, ins, 3)) return MOE_ERROR_ARGUMENT;
+  const void* ptrs[] = {h, expert_offsets, w_down, expert_out, ws};
+  moe_status st = check_device(ptrs, 5, stream);
+  if (st != MOE_SUCCESS) return st;
+  return from_hip(launch_down(h, expert_offsets, (int)rows, (int)E, (int)H, (int)I, w_down, dt,
+                              expert_out, ws, stream));
+}
+
+moe_status moe_combine(const void* expert_out, const int32_t* row_of_slot, const void* weights,
+                       moe_dtype w_dt, int64_t T, int64_t top_k, int64_t H, moe_dtype dt,
+                       void* out, hipStream_t stream) {
+  if (T < 0 || top_k < 1 || H < 1) return MOE_ERROR_SHAPE;
+  if (!valid_dt(dt) || !valid_dt(w_dt)) return MOE_ERROR_DTYPE;
+  if (T * top_k > INT32_MAX || !row_len_ok(H)) return MOE_ERROR_UNSUPPORTED;
+  if (T == 0) return MOE_SUCCESS;
+  if (!expert_out || !row_of_slot || !weights || !out) return MOE_ERROR_NULL_POINTER;
+  const size_t ds = dtype_size(dt), slots = (size_t)(T * top_k);
+  // expert_out holds at most T*top_k rows (one per dispatched slot).
+  const Span outs[] = {{out, (size_t)T * (size_t)H * ds}};
+  const Span ins[] = {{expert_out, slots * (size_t)H * ds}, {row_of_slot, slots * 4},
+                      {weights, slots * dtype_size(w_dt)}};
+  if (any_overlap(outs, 1, ins, 3)) return MOE_ERROR_ARGUMENT;
+  const void* ptrs[] = {expert_out, row_of_slot, weights, out};
+  moe_status st = check_device(ptrs, 4, stream);
+  if (st != MOE_SUCCESS) return st;
+  return from_hip(launch_combine(expert_out, row_of_slot, weights, w_dt, (int)T, (int)top_k,
+                                 (int)H, dt, out, stream));
+}
+
+moe_status moe_combine_add_rmsnorm(const void* expert_out, const int32_t* row_of_slot,
+                                   const void* weights, moe_dtype w_dt, const void* shared,
+                                   const void* residual, const float* gamma, float eps,
+                                   int64_t T, int64_t top_k, int64_t H, moe_dtype dt, void* y,
+                                   void* x_out, float* rstd, hipStream_t stream) {
+  if (T < 0 || top_k < 1 || H < 1) return MOE_ERROR_SHAPE;
+  if (!valid_dt(dt) || !valid_dt(w_dt)) return MOE_ERROR_DTYPE;
+  if (!isfinite(eps) || eps <= 0.f) return MOE_ERROR_ARGUMENT;
+  if (T * top_k > INT32_MAX || !row_len_ok(H) || H > kMaxNormH) return MOE_ERROR_UNSUPPORTED;
+  if (T == 0) return MOE_SUCCESS;
+  if (!expert_out || !row_of_slot || !weights || !residual || !gamma || !y || !x_out || !rstd)
+    return MOE_ERROR_NULL_POINTER;
+  const size_t ds = dtype_size(dt), slots = (size_t)(T * top_k), th = (size_t)T * (size_t)H * ds;
+  const Span outs[] = {{y, th}, {x_out, th}, {rstd, (size_t)T * 4}};
+  const Span ins[] = {{expert_out, slots * (size_t)H * ds}, {row_of_slot, slots * 4},
+                      {weights, slots * dtype_size(w_dt)}, {shared, shared ? th : 0},
+                      {residual, th}, {gamma, (size_t)H * 4}};
+  if (any_overlap(outs, 3, ins, 6)) return MOE_ERROR_ARGUMENT;
+  const void* ptrs[] = {expert_out, row_of_slot, weights, shared, residual, gamma, y, x_out, rstd};
+  moe_status st = check_device(ptrs, 9, stream);
+  if (st != MOE_SUCCESS) return st;
+  return from_hip(launch_combine_add_rmsnorm(expert_out, row_of_slot, weights, w_dt, shared,
+                                             residual, gamma, eps, (int)T, (int)top_k, (int)H, dt,
+                                             y, x_out, rstd, stream));
+}
+
+size_t moe_forward_workspace_size(int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k,
+                                  moe_dtype dt, moe_dtype logits_dt) {
+  if (check_route_args(T, E, top_k, logits_dt) != MOE_SUCCESS) return 0;
+  if (H < 1 || I < 1 || !valid_dt(dt)) return 0;
+  return forward_layout(T, H, I, E, top_k, dt, logits_dt).total;
+}
+
+moe_status moe_forward(const void* x, const void* logits, moe_dtype logits_dt, int64_t T,
+                       int64_t H, int64_t I, int64_t E, int64_t top_k, int renormalize,
+                       const void* w_gate, const void* w_up, const void* w_down, moe_dtype dt,
+                       void* out, uint32_t* indices_out, void* weights_out, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
+  if (H < 1 || I < 1) return MOE_ERROR_SHAPE;
+  moe_status st = check_route_args(T, E, top_k, logits_dt);
+  if (st != MOE_SUCCESS) return st;
+  if (!valid_dt(dt)) return MOE_ERROR_DTYPE;
+  if (!row_len_ok(H) || !row_len_ok(I)) return MOE_ERROR_UNSUPPORTED;
+  if (T == 0) return MOE_SUCCESS;
+  if (!x || !logits || !w_gate || !w_up || !w_down || !out) return MOE_ERROR_NULL_POINTER;
+  const ForwardLayout L = forward_layout(T, H, I, E, top_k, dt, logits_dt);
+  if (!ws || ((uintptr_t)ws & 255) || ws_bytes < L.total) return MOE_ERROR_WORKSPACE;
+  const size_t ds = dtype_size(dt), ls = dtype_size(logits_dt), slots = (size_t)(T * top_k);
+  const size_t wbytes = (size_t)E * (size_t)I * (size_t)H * ds;
+  const Span outs[] = {{out, (size_t)T * (size_t)H * ds}, {indices_out, indices_out ? slots * 4 : 0},
+                       {weights_out, weights_out ? slots * ls : 0}, {ws, L.total}};
+  const Span ins[] = {{x, (size_t)T * (size_t)H * ds}, {logits, (size_t)(T * E) * ls},
+                      {w_gate, wbytes}, {w_up, wbytes}, {w_down, wbytes}};
+  if (any_overlap(outs, 4, ins, 5)) return MOE_ERROR_ARGUMENT;
+  const void* ptrs[] = {x, logits, w_gate, w_up, w_down, out, indices_out, weights_out, ws};
+  if ((st = check_device(ptrs, 9, stream)) != MOE_SUCCESS) return st;
+
+  char* base = static_cast<char*>(ws);
+  uint32_t* idx = indices_out ? indices_out : reinterpret_cast<uint32_t*>(base + L.indices);
+  void* w = weights_out ? weights_out : static_cast<void*>(base + L.weights);
+  int32_t* offsets = reinterpret_cast<int32_t*>(base + L.offsets);
+  int32_t* sor = reinterpret_cast<int32_t*>(base + L.slot_of_row);
+  int32_t* ros = reinterpret_cast<int32_t*>(base + L.row_of_slot);
+  void* y = base + L.expert_out;
+
+  hipError_t e = launch_route(logits, logits_dt, (int)T, (int)E, (int)top_k,
+                              renormalize ? 1 : 0, idx, w, stream);
+  if (e == hipSuccess)
+    e = launch_dispatch_maps(idx, (int)slots, (int)E, offsets, sor, ros,
+                             reinterpret_cast<int32_t*>(base + L.dispatch), stream);
+  // The expert GEMM gathers token rows through slot_of_row; x_disp is never
+  // materialised on this path.
+  if (e == hipSuccess)
+    e = launch_experts(x, sor, (int)top_k, offsets, (int)slots, (int)E, (int)H, (int)I, w_gate,
+                       w_up, w_down, dt, y, base + L.experts, stream);
+  if (e == hipSuccess)
+    e = launch_combine(y, ros, w, logits_dt, (int)T, (int)top_k, (int)H, dt, out, stream);
+  return from_hip(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,212 @@
+// Combine: restore token order and merge expert outputs with the routing
+// weights (ruDNN user guide, "6. Calling MoE"), and the fused variant with
+// the shared-expert term, residual Add and RMSNorm
+// (aclnnMoeDistributeCombineAddRmsNormV2, "function description", formula;
+// ruDNN user guide, "7. LayerNorm, RMSNorm and Softmax" for fp32 statistics
+// and F32 gamma).
+//
+// Both kernels read expert rows through row_of_slot with 16-byte loads; all
+// arithmetic is fp32, summed over the k slots in slot order; there are no
+// atomics, so results are bitwise reproducible.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+// Grid T * ceil(H/8/256) (token-major); each thread produces 8 consecutive
+// outputs.
+template <typename T, typename WT>
+__global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y,
+                                                       const int32_t* __restrict__ row_of_slot,
+                                                       const WT* __restrict__ w, int k, int H,
+                                                       int blocks_per_token,
+                                                       T* __restrict__ out) {
+  const int t = blockIdx.x / blocks_per_token;
+  const int v = (blockIdx.x % blocks_per_token) * blockDim.x + threadIdx.x;
+  if (v * 8 >= H) return;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  bool lost = false;
+  for (int j = 0; j < k; ++j) {
+    const int r = row_of_slot[(int64_t)t * k + j];
+    const float wj = to_f32(w[(int64_t)t * k + j]);
+    if (r < 0) { lost = true; continue; }
+    Vec8<T> d;
+    d.load(y + (int64_t)r * H + v * 8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, d.get(i), acc[i]);
+  }
+  Vec8<T> o;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o.set(i, lost ? NAN : acc[i]);
+  o.store(out + (int64_t)t * H + v * 8);
+}
+
+constexpr int kNormThreads = 256;
+
+// One workgroup per token; thread owns VPT groups of 8 columns, strided by
+// the workgroup, and keeps x in registers between the two passes.
+template <typename T, typename WT, int VPT>
+__global__ __launch_bounds__(kNormThreads) void combine_norm_kernel(
+    const T* __restrict__ y, const int32_t* __restrict__ row_of_slot, const WT* __restrict__ w,
+    const T* __restrict__ shared, const T* __restrict__ residual, const float* __restrict__ gamma,
+    float eps, int k, int H, T* __restrict__ y_out, T* __restrict__ x_out,
+    float* __restrict__ rstd_out) {
+  __shared__ float red[kNormThreads / kWave];
+  const int t = blockIdx.x;
+  const int nvec = H / 8;
+  float x[VPT][8];
+#pragma unroll
+  for (int q = 0; q < VPT; ++q)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[q][i] = 0.f;
+
+  float wsum = 0.f;
+  bool lost = false;
+  for (int j = 0; j < k; ++j) {
+    const int r = row_of_slot[(int64_t)t * k + j];
+    const float wj = to_f32(w[(int64_t)t * k + j]);
+    wsum += wj;
+    if (r < 0) { lost = true; continue; }
+#pragma unroll
+    for (int q = 0; q < VPT; ++q) {
+      const int v = threadIdx.x + q * kNormThreads;
+      if (v < nvec) {
+        Vec8<T> d;
+        d.load(y + (int64_t)r * H + v * 8);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[q][i] = fmaf(wj, d.get(i), x[q][i]);
+      }
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int q = 0; q < VPT; ++q) {
+    const int v = threadIdx.x + q * kNormThreads;
+    if (v < nvec) {
+      Vec8<T> rs;
+      rs.load(residual + (int64_t)t * H + v * 8);
+      Vec8<T> sh;
+      if (shared) sh.load(shared + (int64_t)t * H + v * 8);
+      Vec8<T> xo;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        // sum_j w_j * (y_j + s) = sum_j w_j y_j + (sum_j w_j) s
+        float xv = x[q][i];
+        if (shared) xv = fmaf(wsum, sh.get(i), xv);
+        xv = lost ? NAN : xv + rs.get(i);
+        x[q][i] = xv;
+        ss = fmaf(xv, xv, ss);
+        xo.set(i, xv);
+      }
+      xo.store(x_out + (int64_t)t * H + v * 8);
+    }
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) ss += __shfl_xor(ss, d, kWave);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int i = 0; i < kNormThreads / kWave; ++i) tot += red[i];
+  const float rstd = 1.0f / sqrtf(tot / (float)H + eps);
+  if (threadIdx.x == 0) rstd_out[t] = rstd;
+#pragma unroll
+  for (int q = 0; q < VPT; ++q) {
+    const int v = threadIdx.x + q * kNormThreads;
+    if (v < nvec) {
+      const float4 g0 = *reinterpret_cast<const float4*>(gamma + v * 8);
+      const float4 g1 = *reinterpret_cast<const float4*>(gamma + v * 8 + 4);
+      const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+      Vec8<T> yo;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) yo.set(i, x[q][i] * rstd * g[i]);
+      yo.store(y_out + (int64_t)t * H + v * 8);
+    }
+  }
+}
+
+template <typename T, typename WT>
+hipError_t combine_t(const void* y, const int32_t* ros, const void* w, int T_, int k, int H,
+                     void* out, hipStream_t s) {
+  const int bpt = (H / 8 + 255) / 256;
+  hipLaunchKernelGGL((combine_kernel<T, WT>), dim3((int64_t)T_ * bpt), dim3(256), 0, s,
+                     static_cast<const T*>(y), ros, static_cast<const WT*>(w), k, H, bpt,
+                     static_cast<T*>(out));
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t combine_w(const void* y, const int32_t* ros, const void* w, int w_dt, int T_, int k,
+                     int H, void* out, hipStream_t s) {
+  switch (w_dt) {
+    case kF32: return combine_t<T, float>(y, ros, w, T_, k, H, out, s);
+    case kF16: return combine_t<T, f16>(y, ros, w, T_, k, H, out, s);
+    default: return combine_t<T, bf16>(y, ros, w, T_, k, H, out, s);
+  }
+}
+
+template <typename T, typename WT, int VPT>
+hipError_t norm_launch(const void* y, const int32_t* ros, const void* w, const void* sh,
+                       const void* res, const float* gamma, float eps, int T_, int k, int H,
+                       void* yo, void* xo, float* rstd, hipStream_t s) {
+  hipLaunchKernelGGL((combine_norm_kernel<T, WT, VPT>), dim3(T_), dim3(kNormThreads), 0, s,
+                     static_cast<const T*>(y), ros, static_cast<const WT*>(w),
+                     static_cast<const T*>(sh), static_cast<const T*>(res), gamma, eps, k, H,
+                     static_cast<T*>(yo), static_cast<T*>(xo), rstd);
+  return hipGetLastError();
+}
+
+template <typename T, typename WT>
+hipError_t norm_vpt(const void* y, const int32_t* ros, const void* w, const void* sh,
+                    const void* res, const float* gamma, float eps, int T_, int k, int H,
+                    void* yo, void* xo, float* rstd, hipStream_t s) {
+  const int per = (H / 8 + kNormThreads - 1) / kNormThreads;
+  if (per <= 1) return norm_launch<T, WT, 1>(y, ros, w, sh, res, gamma, eps, T_, k, H, yo, xo, rstd, s);
+  if (per <= 2) return norm_launch<T, WT, 2>(y, ros, w, sh, res, gamma, eps, T_, k, H, yo, xo, rstd, s);
+  if (per <= 4) return norm_launch<T, WT, 4>(y, ros, w, sh, res, gamma, eps, T_, k, H, yo, xo, rstd, s);
+  if (per <= 8) return norm_launch<T, WT, 8>(y, ros, w, sh, res, gamma, eps, T_, k, H, yo, xo, rstd, s);
+  return norm_launch<T, WT, 16>(y, ros, w, sh, res, gamma, eps, T_, k, H, yo, xo, rstd, s);
+}
+
+template <typename T>
+hipError_t norm_w(const void* y, const int32_t* ros, const void* w, int w_dt, const void* sh,
+                  const void* res, const float* gamma, float eps, int T_, int k, int H, void* yo,
+                  void* xo, float* rstd, hipStream_t s) {
+  switch (w_dt) {
+    case kF32: return norm_vpt<T, float>(y, ros, w, sh, res, gamma, eps, T_, k, H, yo, xo, rstd, s);
+    case kF16: return norm_vpt<T, f16>(y, ros, w, sh, res, gamma, eps, T_, k, H, yo, xo, rstd, s);
+    default: return norm_vpt<T, bf16>(y, ros, w, sh, res, gamma, eps, T_, k, H, yo, xo, rstd, s);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const void* expert_out, const int32_t* row_of_slot, const void* weights,
+                          int w_dt, int T, int k, int H, int dt, void* out, hipStream_t s) {
+  switch (dt) {
+    case kF32: return combine_w<float>(expert_out, row_of_slot, weights, w_dt, T, k, H, out, s);
+    case kF16: return combine_w<f16>(expert_out, row_of_slot, weights, w_dt, T, k, H, out, s);
+    default: return combine_w<bf16>(expert_out, row_of_slot, weights, w_dt, T, k, H, out, s);
+  }
+}
+
+hipError_t launch_combine_add_rmsnorm(const void* expert_out, const int32_t* row_of_slot,
+                                      const void* weights, int w_dt, const void* shared,
+                                      const void* residual, const float* gamma, float eps, int T,
+                                      int k, int H, int dt, void* y, void* x_out, float* rstd,
+                                      hipStream_t s) {
+  switch (dt) {
+    case kF32:
+      return norm_w<float>(expert_out, row_of_slot, weights, w_dt, shared, residual, gamma, eps, T,
+                           k, H, y, x_out, rstd, s);
+    case kF16:
+      return norm_w<f16>(expert_out, row_of_slot, weights, w_dt, shared, residual, gamma, eps, T,
+                         k, H, y, x_out, rstd, s);
+    default:
+      return norm_w<bf16>(expert_out, row_of_slot, weights, w_dt, shared, residual, gamma, eps, T,
+                          k, H, y, x_out, rstd, s);
+  }
+}
+
+}  // namespace moe

@@ -1,0 +1,226 @@
+"""Thin Python binding of libmoe_ffn (the C ABI in include/moe_ffn.h).
+
+Argument marshalling only: every function passes device pointers, sizes and
+the current HIP stream to the C call of the same name and raises MoeError on a
+non-success status. All computation happens in the library's HIP kernels;
+there is no fallback. PyTorch provides device memory (outputs and workspaces
+are allocated with torch.empty when the caller does not pass them) and the
+stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_ffn.so")
+_lib = None
+
+F32, F16, BF16 = 0, 1, 2
+_DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+_TORCH = {v: k for k, v in _DT.items()}
+
+STATUS = ["MOE_SUCCESS", "MOE_ERROR_NULL_POINTER", "MOE_ERROR_SHAPE", "MOE_ERROR_DTYPE",
+          "MOE_ERROR_ARGUMENT", "MOE_ERROR_DEVICE", "MOE_ERROR_WORKSPACE",
+          "MOE_ERROR_UNSUPPORTED", "MOE_ERROR_HIP"]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        name = STATUS[status] if 0 <= status < len(STATUS) else f"status {status}"
+        super().__init__(f"{call}: {name}")
+
+
+P, I64, SZ, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+_SIGS = {
+    "moe_status_string": ([I32], ctypes.c_char_p),
+    "moe_route": ([P, I32, I64, I64, I64, I32, P, P, P], I32),
+    "moe_dispatch": ([P, I64, I64, I64, P, I32, I64, P, P, P, P, P, SZ, P], I32),
+    "moe_dispatch_workspace_size": ([I64, I64, I64], SZ),
+    "moe_experts_forward_dispatched": ([P, P, I64, I64, I64, I64, P, P, P, I32, P, P, SZ, P], I32),
+    "moe_experts_workspace_size": ([I64, I64, I64, I64, I32], SZ),
+    "moe_experts_gate_up": ([P, P, I64, P, I64, I64, I64, I64, P, P, I32, P, P, SZ, P], I32),
+    "moe_experts_down": ([P, P, I64, I64, I64, I64, P, I32, P, P, SZ, P], I32),
+    "moe_experts_gemm_workspace_size": ([I64, I64, I32], SZ),
+    "moe_combine": ([P, P, P, I32, I64, I64, I64, I32, P, P], I32),
+    "moe_forward": ([P, P, I32, I64, I64, I64, I64, I64, I32, P, P, P, I32, P, P, P, P, SZ, P], I32),
+    "moe_forward_workspace_size": ([I64, I64, I64, I64, I64, I32, I32], SZ),
+    "moe_combine_add_rmsnorm": ([P, P, P, I32, P, P, P, ctypes.c_float, I64, I64, I64, I32, P, P,
+                                 P, P], I32),
+}
+
+
+def lib():
+    """Load libmoe_ffn.so (built in-tree). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                               "`python -m mixture_experts_ffn_top_amd.build`")
+        handle = ctypes.CDLL(_LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.argtypes, fn.restype = args, res
+        _lib = handle
+    return _lib
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(status, call):
+    if status != 0:
+        raise MoeError(status, call)
+
+
+def dtype_code(dt: torch.dtype) -> int:
+    if dt not in _DT:
+        raise MoeError(3, "dtype")
+    return _DT[dt]
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    # torch's caching allocator returns 512-byte aligned blocks
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def moe_route(logits, top_k: int, renormalize: bool, indices=None, weights=None):
+    """Returns (indices uint32 [T,k] as int32 storage, weights [T,k] logits dtype)."""
+    T, E = logits.shape
+    if indices is None:
+        indices = torch.empty((T, top_k), dtype=torch.int32, device=logits.device)
+    if weights is None:
+        weights = torch.empty((T, top_k), dtype=logits.dtype, device=logits.device)
+    _check(lib().moe_route(_ptr(logits), dtype_code(logits.dtype), T, E, top_k, int(renormalize),
+                           _ptr(indices), _ptr(weights), _stream()), "moe_route")
+    return indices, weights
+
+
+def moe_dispatch_workspace_size(T: int, top_k: int, E: int) -> int:
+    return lib().moe_dispatch_workspace_size(T, top_k, E)
+
+
+def moe_dispatch(indices, E: int, x=None, with_x_disp: bool = True, ws=None, offsets=None,
+                 slot_of_row=None, row_of_slot=None, x_disp=None):
+    """Returns dict(offsets [E+1], slot_of_row [T*k], row_of_slot [T*k], x_disp [T*k, H] or None)."""
+    T, k = indices.shape
+    dev = indices.device
+    H = x.shape[1] if x is not None else 0
+    dt = dtype_code(x.dtype) if x is not None else BF16
+    if x_disp is None and x is not None and with_x_disp:
+        x_disp = torch.empty((T * k, H), dtype=x.dtype, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev) if offsets is None else offsets
+    sor = torch.empty(T * k, dtype=torch.int32, device=dev) if slot_of_row is None else slot_of_row
+    ros = torch.empty(T * k, dtype=torch.int32, device=dev) if row_of_slot is None else row_of_slot
+    if ws is None:
+        ws = _workspace(moe_dispatch_workspace_size(T, k, E), dev)
+    _check(lib().moe_dispatch(_ptr(indices), T, k, E, _ptr(x), dt, H, _ptr(x_disp), _ptr(offsets),
+                              _ptr(sor), _ptr(ros), _ptr(ws), ws.numel(), _stream()), "moe_dispatch")
+    return dict(offsets=offsets, slot_of_row=sor, row_of_slot=ros, x_disp=x_disp)
+
+
+def moe_experts_workspace_size(rows: int, E: int, H: int, I: int, dt: torch.dtype) -> int:
+    return lib().moe_experts_workspace_size(rows, E, H, I, dtype_code(dt))
+
+
+def moe_experts_forward_dispatched(x_disp, expert_offsets, w_gate, w_up, w_down,
+                                   expert_out=None, ws=None):
+    rows, H = x_disp.shape
+    E, I, _ = w_gate.shape
+    if expert_out is None:
+        expert_out = torch.empty((rows, H), dtype=x_disp.dtype, device=x_disp.device)
+    if ws is None:
+        ws = _workspace(moe_experts_workspace_size(rows, E, H, I, x_disp.dtype), x_disp.device)
+    _check(lib().moe_experts_forward_dispatched(
+        _ptr(x_disp), _ptr(expert_offsets), rows, E, H, I, _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+        dtype_code(x_disp.dtype), _ptr(expert_out), _ptr(ws), ws.numel(), _stream()),
+        "moe_experts_forward_dispatched")
+    return expert_out
+
+
+def moe_experts_gemm_workspace_size(rows: int, E: int, dt: torch.dtype) -> int:
+    return lib().moe_experts_gemm_workspace_size(rows, E, dtype_code(dt))
+
+
+def moe_experts_gate_up(x, expert_offsets, w_gate, w_up, row_map=None, map_div: int = 1, rows=None,
+                        h=None, ws=None):
+    """h = SiLU(x W_gate^T) * (x W_up^T) per expert; rows default to x's rows
+    (or to len(row_map) when x is read through the dispatch map)."""
+    H = x.shape[1]
+    E, I, _ = w_gate.shape
+    if rows is None:
+        rows = row_map.numel() if row_map is not None else x.shape[0]
+    if h is None:
+        h = torch.empty((rows, I), dtype=x.dtype, device=x.device)
+    if ws is None:
+        ws = _workspace(moe_experts_gemm_workspace_size(rows, E, x.dtype), x.device)
+    _check(lib().moe_experts_gate_up(_ptr(x), _ptr(row_map), map_div, _ptr(expert_offsets), rows, E, H,
+                                     I, _ptr(w_gate), _ptr(w_up), dtype_code(x.dtype), _ptr(h),
+                                     _ptr(ws), ws.numel(), _stream()), "moe_experts_gate_up")
+    return h
+
+
+def moe_experts_down(h, expert_offsets, w_down, expert_out=None, ws=None):
+    rows, I = h.shape
+    E, H, _ = w_down.shape
+    if expert_out is None:
+        expert_out = torch.empty((rows, H), dtype=h.dtype, device=h.device)
+    if ws is None:
+        ws = _workspace(moe_experts_gemm_workspace_size(rows, E, h.dtype), h.device)
+    _check(lib().moe_experts_down(_ptr(h), _ptr(expert_offsets), rows, E, H, I, _ptr(w_down),
+                                  dtype_code(h.dtype), _ptr(expert_out), _ptr(ws), ws.numel(),
+                                  _stream()), "moe_experts_down")
+    return expert_out
+
+
+def moe_combine(expert_out, row_of_slot, weights, out=None):
+    T, k = weights.shape
+    H = expert_out.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=expert_out.dtype, device=expert_out.device)
+    _check(lib().moe_combine(_ptr(expert_out), _ptr(row_of_slot), _ptr(weights),
+                             dtype_code(weights.dtype), T, k, H, dtype_code(expert_out.dtype),
+                             _ptr(out), _stream()), "moe_combine")
+    return out
+
+
+def moe_forward_workspace_size(T, H, I, E, top_k, dt, logits_dt) -> int:
+    return lib().moe_forward_workspace_size(T, H, I, E, top_k, dtype_code(dt), dtype_code(logits_dt))
+
+
+def moe_forward(x, logits, top_k: int, renormalize: bool, w_gate, w_up, w_down, out=None,
+                indices_out=None, weights_out=None, ws=None):
+    T, H = x.shape
+    E = logits.shape[1]
+    I = w_gate.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=x.dtype, device=x.device)
+    if ws is None:
+        ws = _workspace(moe_forward_workspace_size(T, H, I, E, top_k, x.dtype, logits.dtype), x.device)
+    _check(lib().moe_forward(_ptr(x), _ptr(logits), dtype_code(logits.dtype), T, H, I, E, top_k,
+                             int(renormalize), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+                             dtype_code(x.dtype), _ptr(out), _ptr(indices_out), _ptr(weights_out),
+                             _ptr(ws), ws.numel(), _stream()), "moe_forward")
+    return out
+
+
+def moe_combine_add_rmsnorm(expert_out, row_of_slot, weights, residual, gamma, eps: float,
+                            shared=None, y=None, x_out=None, rstd=None):
+    T, k = weights.shape
+    H = expert_out.shape[1]
+    dev, dt = expert_out.device, expert_out.dtype
+    y = torch.empty((T, H), dtype=dt, device=dev) if y is None else y
+    x_out = torch.empty((T, H), dtype=dt, device=dev) if x_out is None else x_out
+    rstd = torch.empty(T, dtype=torch.float32, device=dev) if rstd is None else rstd
+    _check(lib().moe_combine_add_rmsnorm(
+        _ptr(expert_out), _ptr(row_of_slot), _ptr(weights), dtype_code(weights.dtype), _ptr(shared),
+        _ptr(residual), _ptr(gamma), float(eps), T, k, H, dtype_code(dt), _ptr(y), _ptr(x_out),
+        _ptr(rstd), _stream()), "moe_combine_add_rmsnorm")
+    return y, x_out, rstd

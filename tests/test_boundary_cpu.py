@@ -1,0 +1,159 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every
+function include/moe_ffn.h declares, and rejects bad arguments on the host
+before touching the device (no compute calls are made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_experts_ffn_top_amd import moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_ffn.h")
+
+S = {n: i for i, n in enumerate(moe.STATUS)}
+FAKE = 0x7F0000000000  # never dereferenced: every case below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) == 13, names
+    lib = moe.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(moe._SIGS) == set(names)
+
+
+def test_status_strings():
+    lib = moe.lib()
+    for i, n in enumerate(moe.STATUS):
+        assert lib.moe_status_string(i).decode() == n
+    assert lib.moe_status_string(99).decode() == "MOE_ERROR_UNKNOWN"
+
+
+def test_route_validation():
+    f = moe.lib().moe_route
+    assert f(FAKE, 0, 4, 8, 0, 1, FAKE, FAKE + 4096, None) == S["MOE_ERROR_ARGUMENT"]
+    assert f(FAKE, 0, 4, 8, 9, 1, FAKE, FAKE + 4096, None) == S["MOE_ERROR_ARGUMENT"]
+    assert f(FAKE, 0, -1, 8, 2, 1, FAKE, FAKE + 4096, None) == S["MOE_ERROR_SHAPE"]
+    assert f(FAKE, 0, 4, 0, 1, 1, FAKE, FAKE + 4096, None) == S["MOE_ERROR_SHAPE"]
+    assert f(FAKE, 7, 4, 8, 2, 1, FAKE, FAKE + 4096, None) == S["MOE_ERROR_DTYPE"]
+    assert f(FAKE, 0, 4, 1025, 2, 1, FAKE, FAKE + 4096, None) == S["MOE_ERROR_UNSUPPORTED"]
+    assert f(FAKE, 0, 2**31, 8, 2, 1, FAKE, FAKE + 4096, None) == S["MOE_ERROR_UNSUPPORTED"]
+    assert f(None, 0, 4, 8, 2, 1, FAKE, FAKE + 4096, None) == S["MOE_ERROR_NULL_POINTER"]
+    # T = 0 is a no-op, even with NULL pointers
+    assert f(None, 0, 0, 8, 2, 1, None, None, None) == S["MOE_SUCCESS"]
+    # weights output overlapping the logits
+    assert f(FAKE, 0, 4, 8, 2, 1, FAKE + 8192, FAKE + 16, None) == S["MOE_ERROR_ARGUMENT"]
+
+
+def test_dispatch_validation():
+    f = moe.lib().moe_dispatch
+    ws_need = moe.lib().moe_dispatch_workspace_size(64, 2, 8)
+    assert ws_need > 0
+    args = lambda **kw: dict(dict(idx=FAKE, T=64, k=2, E=8, x=FAKE + 2**20, dt=2, H=128, xd=FAKE + 2**21,  # noqa: E731
+                                  off=FAKE + 2**22, sor=FAKE + 2**23, ros=FAKE + 2**24,
+                                  ws=FAKE + 2**25, wsb=ws_need), **kw)
+
+    def call(**kw):
+        a = args(**kw)
+        return f(a["idx"], a["T"], a["k"], a["E"], a["x"], a["dt"], a["H"], a["xd"], a["off"],
+                 a["sor"], a["ros"], a["ws"], a["wsb"], None)
+
+    assert call(k=0) == S["MOE_ERROR_ARGUMENT"]
+    assert call(H=-8) == S["MOE_ERROR_SHAPE"]
+    assert call(H=100) == S["MOE_ERROR_UNSUPPORTED"]
+    assert call(dt=5) == S["MOE_ERROR_DTYPE"]
+    assert call(off=None) == S["MOE_ERROR_NULL_POINTER"]
+    assert call(x=None) == S["MOE_ERROR_NULL_POINTER"]
+    assert call(wsb=ws_need - 1) == S["MOE_ERROR_WORKSPACE"]
+    assert call(ws=FAKE + 2**25 + 8) == S["MOE_ERROR_WORKSPACE"]
+    assert call(ws=None) == S["MOE_ERROR_WORKSPACE"]
+    assert call(sor=FAKE + 2**24 + 64) == S["MOE_ERROR_ARGUMENT"]  # overlaps row_of_slot
+
+
+def test_experts_validation():
+    lib = moe.lib()
+    f = lib.moe_experts_forward_dispatched
+    need = lib.moe_experts_workspace_size(128, 8, 128, 256, 2)
+    assert need > 128 * 256 * 2
+    base = [FAKE, FAKE + 2**20, 128, 8, 128, 256, FAKE + 2**21, FAKE + 2**22, FAKE + 2**23, 2,
+            FAKE + 2**24, FAKE + 2**26, need, None]
+
+    def call(i=None, v=None):
+        a = list(base)
+        if i is not None:
+            a[i] = v
+        return f(*a)
+
+    assert call(4, 0) == S["MOE_ERROR_SHAPE"]
+    assert call(4, 132) == S["MOE_ERROR_UNSUPPORTED"]
+    assert call(5, 260) == S["MOE_ERROR_UNSUPPORTED"]
+    assert call(3, 2000) == S["MOE_ERROR_UNSUPPORTED"]
+    assert call(9, 3) == S["MOE_ERROR_DTYPE"]
+    assert call(8, None) == S["MOE_ERROR_NULL_POINTER"]
+    assert call(12, need - 256) == S["MOE_ERROR_WORKSPACE"]
+    assert call(10, FAKE + 2**21 + 512) == S["MOE_ERROR_ARGUMENT"]  # expert_out inside w_gate
+    assert call(2, 0) == S["MOE_SUCCESS"]  # no rows: no-op
+
+
+def test_combine_and_norm_validation():
+    lib = moe.lib()
+    c = lib.moe_combine
+    assert c(FAKE, FAKE + 2**20, FAKE + 2**21, 0, 16, 0, 64, 2, FAKE + 2**22, None) == S["MOE_ERROR_SHAPE"]
+    assert c(FAKE, FAKE + 2**20, FAKE + 2**21, 9, 16, 2, 64, 2, FAKE + 2**22, None) == S["MOE_ERROR_DTYPE"]
+    assert c(FAKE, FAKE + 2**20, FAKE + 2**21, 0, 16, 2, 60, 2, FAKE + 2**22, None) == S["MOE_ERROR_UNSUPPORTED"]
+    assert c(FAKE, FAKE + 2**20, FAKE + 2**21, 0, 16, 2, 64, 2, FAKE + 64, None) == S["MOE_ERROR_ARGUMENT"]
+    n = lib.moe_combine_add_rmsnorm
+    args = [FAKE, FAKE + 2**20, FAKE + 2**21, 0, None, FAKE + 2**22, FAKE + 2**23, 1e-6, 16, 2, 64,
+            2, FAKE + 2**24, FAKE + 2**25, FAKE + 2**26, None]
+    for eps in (0.0, -1.0, float("inf"), float("nan")):
+        a = list(args)
+        a[7] = eps
+        assert n(*a) == S["MOE_ERROR_ARGUMENT"], eps
+    a = list(args)
+    a[10] = 40000
+    assert n(*a) == S["MOE_ERROR_UNSUPPORTED"]
+    a = list(args)
+    a[13] = FAKE + 2**24 + 64  # x_out overlaps y
+    assert n(*a) == S["MOE_ERROR_ARGUMENT"]
+
+
+def test_forward_validation_and_workspace_query():
+    lib = moe.lib()
+    q = lib.moe_forward_workspace_size
+    need = q(4096, 4096, 14336, 8, 2, 2, 0)
+    # h [T*k, I] and expert_out [T*k, H] in bf16 dominate
+    assert need >= 4096 * 2 * (14336 + 4096) * 2
+    assert q(4, 128, 256, 8, 9, 2, 0) == 0
+    f = lib.moe_forward
+    base = [FAKE, FAKE + 2**20, 0, 64, 128, 256, 8, 2, 1, FAKE + 2**21, FAKE + 2**22, FAKE + 2**23,
+            0, FAKE + 2**24, None, None, FAKE + 2**26, q(64, 128, 256, 8, 2, 0, 0), None]
+
+    def call(i=None, v=None):
+        a = list(base)
+        if i is not None:
+            a[i] = v
+        return f(*a)
+
+    assert call(7, 9) == S["MOE_ERROR_ARGUMENT"]
+    assert call(12, 4) == S["MOE_ERROR_DTYPE"]
+    assert call(5, 250) == S["MOE_ERROR_UNSUPPORTED"]
+    assert call(17, 10) == S["MOE_ERROR_WORKSPACE"]
+    assert call(0, None) == S["MOE_ERROR_NULL_POINTER"]
+    assert call(3, 0) == S["MOE_SUCCESS"]
+    assert call(13, FAKE + 64) == S["MOE_ERROR_ARGUMENT"]  # out overlaps x
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(moe, "_lib", None)
+    monkeypatch.setattr(moe, "_LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        moe.lib()

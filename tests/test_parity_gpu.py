@@ -1,0 +1,354 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle on
+the same seeded inputs.
+
+Bit-exact: expert indices, dispatch offsets and both maps, x_disp rows.
+Tolerance (|gpu - ref| <= atol + rtol |ref|, NaN positions identical):
+fp32 1e-4 / 1e-4, bf16 1e-2 / 2e-2, fp16 1e-3 / 2e-3; routing weights in fp32
+at the fp32 tolerance.
+Small cases run the oracle on every output; the five named workloads run at
+their full sizes through the same entry points the benchmark times, with the
+oracle on sampled tokens where the full oracle would take minutes.
+"""
+import numpy as np
+import pytest
+import torch
+
+from mixture_experts_ffn_top_amd import inputs as I
+from mixture_experts_ffn_top_amd import moe
+from oracle import moe_oracle as O
+from parity_helpers import assert_close, dev, host, upload_expert_weights
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    moe.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+# ------------------------------------------------------------------ routing --
+ROUTE_SHAPES = [(1, 1), (2, 1), (3, 2), (8, 2), (8, 8), (33, 5), (64, 6), (65, 3), (128, 8),
+                (256, 8), (1000, 17), (1024, 1), (1024, 64)]
+
+
+def _check_route(z, ldt, k, renorm):
+    T, E = z.shape
+    idx_ref, w_ref = O.route(z, ldt, k, renorm)
+    idx, w = moe.moe_route(dev(z, ldt), k, renorm)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(idx).astype(np.uint32), idx_ref), f"indices E={E} k={k}"
+    assert_close(host(w), w_ref, ldt, f"weights E={E} k={k} {ldt}")
+
+
+@pytest.mark.parametrize("E,k", ROUTE_SHAPES)
+def test_route_random(E, k):
+    say("route", E, k)
+    z = I.gapped_logits(100 + E, 301, E, k)
+    for renorm in (True, False):
+        _check_route(z, "f32", k, renorm)
+
+
+@pytest.mark.parametrize("ldt", ["bf16", "f16"])
+@pytest.mark.parametrize("E,k", [(8, 2), (128, 8), (256, 8)])
+def test_route_half_logits(E, k, ldt):
+    z32 = I.gapped_logits(7 + E, 257, E, k)
+    z = O.round_to(z32.astype(np.float64), ldt)
+    for renorm in (True, False):
+        _check_route(z, ldt, k, renorm)
+
+
+@pytest.mark.parametrize("E,k", [(4, 2), (8, 8), (64, 6), (256, 8), (1024, 16)])
+def test_route_ties(E, k):
+    g = np.random.default_rng(E)
+    # logits quantised to 0.5 steps: many exact ties, inside and at the top-k boundary
+    z = (g.integers(-4, 5, size=(200, E)) * 0.5).astype(np.float32)
+    z[0] = 0.25  # all equal
+    z[1] = -7.0
+    for renorm in (True, False):
+        _check_route(z, "f32", k, renorm)
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (64, 4), (128, 8), (1024, 3)])
+def test_route_nan_inf_rows(E, k):
+    z = I.gapped_logits(5, 12, E, k)
+    z[0, 0] = np.nan
+    z[1, E - 1] = np.nan
+    z[2, 0] = np.inf
+    z[3, E - 1] = np.inf
+    z[4, :] = -np.inf
+    z[5, : E - 1] = -np.inf  # one finite value left
+    z[6, ::2] = -np.inf      # partial -inf row
+    z[7, 1] = -np.inf
+    z[7, 2] = np.nan         # NaN and -inf together
+    for renorm in (True, False):
+        _check_route(z, "f32", k, renorm)
+
+
+def test_route_empty():
+    idx, w = moe.moe_route(torch.empty((0, 8), device="cuda"), 2, True)
+    assert idx.shape == (0, 2)
+
+
+def test_route_workloads_full():
+    for name in I.WORKLOADS:
+        w = I.workload(name)
+        say("route workload", name)
+        _check_route(I.logits_for(w), "f32", w.top_k, w.renormalize)
+
+
+# ----------------------------------------------------------------- dispatch --
+def _check_dispatch(idx, E, x, dtype):
+    ref = O.dispatch(idx, E, x)
+    got = moe.moe_dispatch(dev(idx.astype(np.int64).astype(np.int32)), E, dev(x, dtype))
+    torch.cuda.synchronize()
+    n = int(ref["offsets"][-1])
+    assert np.array_equal(host(got["offsets"]), ref["offsets"])
+    assert np.array_equal(host(got["row_of_slot"]), ref["row_of_slot"])
+    assert np.array_equal(host(got["slot_of_row"])[:n], ref["slot_of_row"])
+    assert np.array_equal(host(got["x_disp"])[:n], ref["x_disp"])
+
+
+@pytest.mark.parametrize("T,k,E,H", [(1, 1, 1, 8), (37, 3, 5, 136), (300, 2, 8, 64),
+                                     (4096, 8, 128, 64), (2048, 8, 256, 16), (8192, 8, 1024, 8)])
+def test_dispatch_random(T, k, E, H):
+    say("dispatch", T, k, E, H)
+    g = np.random.default_rng(T + E)
+    idx = np.stack([g.permutation(E)[:k] for _ in range(T)]).astype(np.uint32)
+    x = O.round_to(g.standard_normal((T, H)), "bf16")
+    _check_dispatch(idx, E, x, "bf16")
+
+
+def test_dispatch_skew_and_many_blocks():
+    g = np.random.default_rng(3)
+    T, k, E = 131072, 8, 64  # 2^20 slots: several chunks per block
+    idx = g.integers(0, E, size=(T, k)).astype(np.uint32)
+    idx[: T // 2] = 0  # half the slots go to expert 0
+    x = g.standard_normal((T, 8)).astype(np.float32)
+    _check_dispatch(idx, E, x, "f32")
+
+
+def test_dispatch_out_of_range_ids():
+    g = np.random.default_rng(4)
+    T, k, E = 500, 4, 16
+    idx = g.integers(0, E, size=(T, k)).astype(np.uint32)
+    idx[::7, 1] = E
+    idx[::11, 3] = 0xFFFFFFFF
+    x = g.standard_normal((T, 16)).astype(np.float32)
+    _check_dispatch(idx, E, x, "f32")
+
+
+def test_dispatch_workloads_full():
+    for name in I.WORKLOADS:
+        w = I.workload(name)
+        say("dispatch workload", name)
+        idx, _ = O.route(I.logits_for(w), "f32", w.top_k, w.renormalize)
+        x = I.store(np.random.default_rng(0).standard_normal((w.T, 8), dtype=np.float32), w.dtype)
+        _check_dispatch(idx, w.E, x, w.dtype)
+
+
+# ------------------------------------------------------------------ experts --
+EXPERT_CASES = [
+    # (T, k, E, H, I, dtype): ragged rows / N / K tails, several M- and N-tiles
+    (37, 3, 5, 136, 200, "bf16"),
+    (1000, 2, 3, 264, 392, "bf16"),
+    (600, 4, 7, 512, 640, "f16"),
+    (64, 2, 8, 128, 256, "f32"),
+    (150, 3, 4, 72, 104, "f32"),
+    (1, 1, 1, 8, 8, "bf16"),
+]
+
+
+def _random_experts(g, E, H, I_, dtype):
+    st = lambda a: I.store(a.astype(np.float32), dtype) if dtype != "f16" else a.astype(np.float16)  # noqa: E731
+    wg = st(g.standard_normal((E, I_, H)) / np.sqrt(H))
+    wu = st(g.standard_normal((E, I_, H)) / np.sqrt(H))
+    wd = st(g.standard_normal((E, H, I_)) / np.sqrt(I_))
+    return wg, wu, wd
+
+
+def _store(a, dtype):
+    return a.astype(np.float16) if dtype == "f16" else I.store(a.astype(np.float32), dtype)
+
+
+@pytest.mark.parametrize("T,k,E,H,I_,dtype", EXPERT_CASES)
+def test_experts_dispatched(T, k, E, H, I_, dtype):
+    say("experts", T, k, E, H, I_, dtype)
+    g = np.random.default_rng(T * 7 + H)
+    x = _store(g.standard_normal((T, H)), dtype)
+    z = I.gapped_logits(T, T, E, k)
+    idx, _ = O.route(z, "f32", k, True)
+    d = O.dispatch(idx, E, x)
+    wg, wu, wd = _random_experts(g, E, H, I_, dtype)
+    ref = O.experts_forward_dispatched(d["x_disp"], d["offsets"], lambda e: (wg[e], wu[e], wd[e]), dtype)
+    got = moe.moe_experts_forward_dispatched(dev(d["x_disp"], dtype), dev(d["offsets"]), dev(wg, dtype),
+                                             dev(wu, dtype), dev(wd, dtype))
+    torch.cuda.synchronize()
+    assert_close(host(got), ref, dtype, f"expert_out {dtype}")
+
+
+def test_experts_all_rows_one_expert():
+    g = np.random.default_rng(9)
+    T, k, E, H, I_ = 700, 1, 6, 128, 256
+    x = I.store(g.standard_normal((T, H)).astype(np.float32), "bf16")
+    idx = np.full((T, 1), 4, np.uint32)
+    d = O.dispatch(idx, E, x)
+    wg, wu, wd = _random_experts(g, E, H, I_, "bf16")
+    ref = O.experts_forward_dispatched(d["x_disp"], d["offsets"], lambda e: (wg[e], wu[e], wd[e]), "bf16")
+    got = moe.moe_experts_forward_dispatched(dev(d["x_disp"], "bf16"), dev(d["offsets"]), dev(wg, "bf16"),
+                                             dev(wu, "bf16"), dev(wd, "bf16"))
+    torch.cuda.synchronize()
+    assert_close(host(got), ref, "bf16", "expert_out one expert")
+
+
+# ------------------------------------------------------------------ combine --
+@pytest.mark.parametrize("T,k,H,dtype,wdt", [(50, 3, 136, "bf16", "f32"), (7, 8, 4096, "bf16", "f32"),
+                                             (33, 2, 64, "f32", "f32"), (20, 4, 256, "f16", "f16"),
+                                             (64, 2, 24, "bf16", "bf16")])
+def test_combine(T, k, H, dtype, wdt):
+    g = np.random.default_rng(T + H)
+    y = _store(g.standard_normal((T * k, H)), dtype)
+    ros = g.permutation(T * k).astype(np.int32)
+    ros[3 % (T * k)] = -1  # one slot not dispatched -> NaN row
+    w = _store(g.random((T, k)), wdt)
+    w32 = w if wdt != "bf16" else w
+    ref = O.combine(y, ros, w32, wdt, T, k, dtype)
+    got = moe.moe_combine(dev(y, dtype), dev(ros), dev(w, wdt))
+    torch.cuda.synchronize()
+    assert_close(host(got), ref, dtype, "combine")
+
+
+@pytest.mark.parametrize("T,k,H,dtype,shared", [(40, 8, 7168, "bf16", True), (9, 2, 136, "bf16", False),
+                                                (16, 3, 64, "f32", True), (5, 1, 32768, "bf16", True),
+                                                (12, 4, 1024, "f16", False)])
+def test_combine_add_rmsnorm(T, k, H, dtype, shared):
+    g = np.random.default_rng(T * 3 + H)
+    y = _store(g.standard_normal((T * k, H)), dtype)
+    ros = g.permutation(T * k).astype(np.int32)
+    _, w = O.route(I.gapped_logits(1, T, max(k, 8), k), "f32", k, True)
+    w[2] = np.nan  # NaN-weight row
+    sh = _store(g.standard_normal((T, H)), dtype) if shared else None
+    res = _store(g.standard_normal((T, H)), dtype)
+    gamma = g.uniform(0.5, 1.5, H).astype(np.float32)
+    yr, xr, rr = O.combine_add_rmsnorm(y, ros, w, "f32", sh, res, gamma, 1e-6, T, k, dtype)
+    yg, xg, rg = moe.moe_combine_add_rmsnorm(dev(y, dtype), dev(ros), dev(w, "f32"), dev(res, dtype),
+                                             dev(gamma, "f32"), 1e-6,
+                                             shared=dev(sh, dtype) if shared else None)
+    torch.cuda.synchronize()
+    assert_close(host(xg), xr, dtype, "x_out")
+    assert_close(host(yg), yr, dtype, "y")
+    assert_close(host(rg), rr, "f32", "rstd")
+
+
+# ------------------------------------------------------------- whole forward --
+def _forward_small(T, k, E, H, I_, dtype, renorm, seed):
+    g = np.random.default_rng(seed)
+    x = _store(g.standard_normal((T, H)), dtype)
+    z = I.gapped_logits(seed, T, E, k)
+    wg, wu, wd = _random_experts(g, E, H, I_, dtype)
+    idx_r, w_r, d_r, y_r, out_r = O.forward(x, z, "f32", k, renorm, lambda e: (wg[e], wu[e], wd[e]), E, dtype)
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    out = moe.moe_forward(dev(x, dtype), dev(z, "f32"), k, renorm, dev(wg, dtype), dev(wu, dtype),
+                          dev(wd, dtype), indices_out=idx, weights_out=wts)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(idx).astype(np.uint32), idx_r)
+    assert_close(host(wts), w_r, "f32", "routing weights")
+    assert_close(host(out), out_r, dtype, "out")
+    return out
+
+
+@pytest.mark.parametrize("T,k,E,H,I_,dtype,renorm", [(37, 3, 5, 136, 200, "bf16", True),
+                                                     (300, 2, 4, 256, 384, "bf16", False),
+                                                     (100, 1, 1, 64, 128, "bf16", True),
+                                                     (77, 2, 8, 128, 256, "f32", True),
+                                                     (90, 4, 16, 64, 96, "f16", True)])
+def test_forward_small(T, k, E, H, I_, dtype, renorm):
+    say("forward small", T, k, E, H, I_, dtype)
+    _forward_small(T, k, E, H, I_, dtype, renorm, T + E)
+
+
+def test_forward_deterministic():
+    a = _forward_small(300, 2, 4, 256, 384, "bf16", True, 5)
+    b = _forward_small(300, 2, 4, 256, 384, "bf16", True, 5)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_forward_empty_batch():
+    out = torch.full((0, 64), 1.0, device="cuda")
+    moe.moe_forward(torch.empty((0, 64), device="cuda"), torch.empty((0, 8), device="cuda"), 2, True,
+                    torch.empty((8, 64, 64), device="cuda"), torch.empty((8, 64, 64), device="cuda"),
+                    torch.empty((8, 64, 64), device="cuda"), out=out)
+
+
+def _workload_inputs(name, n_sample):
+    w = I.workload(name)
+    z = I.logits_for(w)
+    x = I.tokens_for(w)
+    idx_r, w_r = O.route(z, "f32", w.top_k, w.renormalize)
+    if n_sample is None or n_sample >= w.T:
+        sample = np.arange(w.T)
+    else:
+        sample = np.unique(np.concatenate([[0, w.T - 1], np.random.default_rng(1).choice(w.T, n_sample, False)]))
+    keep = sorted(set(int(e) for e in idx_r[sample].ravel()))
+    say("workload", name, "generating weights")
+    wg, wu, wd, kept = upload_expert_weights(w, keep)
+    return w, z, x, idx_r, w_r, sample, (wg, wu, wd), kept
+
+
+def _sampled_expert_rows(w, x, idx_r, sample, kept):
+    return O.expert_out_rows(x, idx_r, [int(t) for t in sample], lambda e: kept[e], w.dtype)
+
+
+@pytest.mark.parametrize("name,n_sample", [("tiny_fp32", None), ("decode_nan_rows_bf16", None),
+                                           ("mixtral_8x_bf16", 48), ("many_expert_zipf_bf16", 64)])
+def test_forward_workload_full_size(name, n_sample):
+    w, z, x, idx_r, w_r, sample, (wg, wu, wd), kept = _workload_inputs(name, n_sample)
+    say("workload", name, "forward")
+    idx = torch.empty((w.T, w.top_k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((w.T, w.top_k), dtype=torch.float32, device="cuda")
+    out = moe.moe_forward(dev(x, w.dtype), dev(z, "f32"), w.top_k, w.renormalize, wg, wu, wd,
+                          indices_out=idx, weights_out=wts)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(idx).astype(np.uint32), idx_r)
+    assert_close(host(wts), w_r, "f32", "routing weights")
+    rows = _sampled_expert_rows(w, x, idx_r, sample, kept)
+    S, k = len(sample), w.top_k
+    y = np.stack([rows[(int(t), j)] for t in sample for j in range(k)])
+    ref = O.combine(y, np.arange(S * k, dtype=np.int32), w_r[sample], "f32", S, k, w.dtype)
+    assert_close(host(out)[sample], ref, w.dtype, f"{name} out")
+    if w.special_rows:
+        assert np.isnan(host(out)[[3, 7, 11]].astype(np.float64) if w.dtype == "f32" else
+                        (host(out)[[3, 7, 11]].astype(np.uint32) << 16).view(np.float32)).all()
+
+
+def test_workload_with_rmsnorm_epilogue_full_size():
+    """DeepSeek-V3-shaped share (E=256, k=8, H=7168, I=2048) through the split
+    calls: route -> dispatch (x_disp) -> experts -> combine + Add + RMSNorm."""
+    name = "dsv3_share_rmsnorm_bf16"
+    w, z, x, idx_r, w_r, sample, (wg, wu, wd), kept = _workload_inputs(name, 8)
+    shared, residual, gamma = I.epilogue_inputs(w)
+    say("workload", name, "forward")
+    idx, wts = moe.moe_route(dev(z, "f32"), w.top_k, w.renormalize)
+    d = moe.moe_dispatch(idx, w.E, dev(x, w.dtype))
+    y = moe.moe_experts_forward_dispatched(d["x_disp"], d["offsets"], wg, wu, wd)
+    yo, xo, rs = moe.moe_combine_add_rmsnorm(y, d["row_of_slot"], wts, dev(residual, w.dtype),
+                                             dev(gamma, "f32"), w.eps, shared=dev(shared, w.dtype))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(idx).astype(np.uint32), idx_r)
+    d_r = O.dispatch(idx_r, w.E)
+    assert np.array_equal(host(d["offsets"]), d_r["offsets"])
+    rows = _sampled_expert_rows(w, x, idx_r, sample, kept)
+    S, k = len(sample), w.top_k
+    yrows = np.stack([rows[(int(t), j)] for t in sample for j in range(k)])
+    yr, xr, rr = O.combine_add_rmsnorm(yrows, np.arange(S * k, dtype=np.int32), w_r[sample], "f32",
+                                       shared[sample], residual[sample], gamma, w.eps, S, k, w.dtype)
+    assert_close(host(xo)[sample], xr, w.dtype, "x_out")
+    assert_close(host(yo)[sample], yr, w.dtype, "y")
+    assert_close(host(rs)[sample], rr, "f32", "rstd")
