@@ -31,6 +31,21 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
 
 
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE runs (profiles/counters.json, scaled by the copy-kernel
+    calibration), or None when the GEMM source changed after they were taken."""
+    import hashlib
+    try:
+        data = json.load(open(os.path.join(ROOT, "profiles", "counters.json")))[workload]
+        src = open(os.path.join(ROOT, "mixture_experts_ffn_top_amd", "csrc", "gemm.hip"), "rb").read()
+    except (OSError, KeyError, ValueError):
+        return None
+    if hashlib.sha256(src).hexdigest()[:16] != data.get("gemm_source_sha16"):
+        return None
+    return data["traffic_bytes_per_launch"].get(kernel)
+
+
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
@@ -44,6 +59,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens of the workload the CPU oracle runs on")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes 5 times (the "
+                         "reference kernel for scaling HBM byte counters), then exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no "
@@ -51,6 +69,16 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.calibrate_copy:
+        a = torch.ones(args.calibrate_copy, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "copy", "bytes_read": args.calibrate_copy,
+                          "bytes_written": args.calibrate_copy, "launches": 5}), flush=True)
+        return
 
     from mixture_experts_ffn_top_amd import inputs as I
     from mixture_experts_ffn_top_amd import moe
@@ -159,7 +187,8 @@ def main():
     es = 2 if w.dtype == "bf16" else 4
     combine_bytes = R * H * es + R * 4 + R * 4 + T * H * es
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": None,
+                "frac": round(achieved / peak, 4),
+                "traffic": measured_traffic(args.workload, "mfma_gemm_kernel<bf16,gate_up>"),
                 "kernel": "mfma_gemm_kernel<bf16, gate/up+SiLU>" if w.dtype == "bf16" else "gate/up GEMM",
                 "flops_per_launch": flops_gate_up}
     expert_tflops = (flops_gate_up + flops_down) / ((stage_ms["gate_up"] + stage_ms["down"]) / 1e3) / 1e12
