@@ -12,20 +12,34 @@
 // workgroups past the device tile count exit at once. Expert counts never
 // travel to the host.
 //
-// bf16/f16 kernel (gfx950 MFMA 32x32x16): workgroup tile 256 x 256 x 64, 512
-// threads = 8 wavefronts as 4 (M) x 2 (N), 64 x 128 per wavefront. A and B
-// tiles are staged through LDS, double-buffered, with a register prefetch of
-// the next K-step issued before the current step's MFMAs. LDS rows are 64
-// elements (eight 16-byte chunks); chunk c of row r is stored at c ^ (r & 7),
-// so the 16-byte fragment reads of eight consecutive rows hit eight distinct
-// chunk positions. In GEMM 1 the B tile holds 128 gate rows and the same 128
-// up rows, and every wavefront owns matching gate and up accumulators, so
-// SiLU(g) * u is formed in registers and only h reaches memory.
+// bf16/f16 kernel (gfx950 MFMA 32x32x16): workgroup tile 256 x kBNB x 64,
+// 512 threads = 8 wavefronts as 4 (M) x 2 (N), 64 x kBNB/2 per wavefront.
+// Global tiles go straight into LDS with buffer loads (buffer_load_dwordx4
+// ... lds): each lane's 16 bytes land at LDS base + 16 * lane, so the
+// swizzle is applied by choosing which global chunk each lane fetches. A
+// load past the buffer's byte count returns zeros, which covers the N tail
+// of the weights and (with a deliberately out-of-range offset) the K tail.
+// Two LDS stages; the next K-step's loads are issued before the current
+// step's MFMAs and waited for (vmcnt) just before the step's barrier.
+// Fragment registers are double-buffered across the four k16 sub-steps so
+// LDS reads for sub-step s+1 overlap the MFMAs of sub-step s.
+//
+// LDS rows are 64 elements (eight 16-byte chunks). gfx950 serves a 128-bit
+// LDS read 16 lanes per cycle across 64 banks, so the 16 rows read together
+// must hit 16 distinct (row parity, chunk) slots: chunk c of row r is stored
+// at c ^ (r & 7) ^ ((r >> 3) & 1).
+//
+// In GEMM 1 the B tile holds 128 gate rows and the same 128 up rows, and
+// every wavefront owns matching gate and up accumulators, so SiLU(g) * u is
+// formed in registers and only h reaches memory.
 //
 // Workgroup order: the hardware deals workgroups round-robin to the 8 XCDs;
-// the kernel remaps its id so that each XCD receives a contiguous range of
-// logical tiles, M-tile fastest, so the workgroups sharing one weight tile run
-// on the same XCD and share its L2.
+// the kernel remaps its id so each XCD receives a contiguous range of
+// logical tiles. Logical tiles sweep groups of 8 N-tiles, M-tile by M-tile
+// inside a group, so the ~32 workgroups resident on one XCD share 8 weight
+// tiles and a few activation tiles through its L2.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -33,10 +47,14 @@ namespace moe {
 namespace {
 
 constexpr int kBM = 256;      // rows per M-tile (MFMA path)
-constexpr int kBK = 64;       // K per pipeline step
-constexpr int kBNB = 256;     // B-tile rows per workgroup
+constexpr int kBK = 32;       // K per pipeline stage
+constexpr int kChunks = kBK / 8;  // 16-byte chunks per LDS row
 constexpr int kThreads = 512;
 constexpr int kBMSimt = 64;   // rows per M-tile (fp32 path)
+constexpr int kGroupN = 8;    // N-tiles per rasterisation group
+// Third dword of a raw buffer resource on gfx9-family parts (no format, no swizzle).
+constexpr int kRsrcFlags = 0x00020000;
+constexpr uint32_t kOutOfRange = 0x80000000u;  // voffset past any buffer we build (< 2^31 bytes)
 
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ offsets, int E,
                                                      int rows, int bm, int max_tiles,
@@ -62,10 +80,10 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
 }
 
 struct GemmArgs {
-  const void* a;           // [*, K] rows of X (or h)
+  const void* a;           // [a_rows, K] rows of X (or h)
   const int32_t* a_map;    // optional: A row r is a[a_map[r] / a_div]
   int a_div;
-  int a_rows;              // rows of `a` when a_map is given (gather bound)
+  int a_rows;              // rows of `a`
   const void* b0;          // [E, N, K] gate (GEMM 1) or down (GEMM 2)
   const void* b1;          // [E, N, K] up (GEMM 1 only)
   void* c;                 // [rows, N]
@@ -91,135 +109,231 @@ template <> struct Mfma<f16> {
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
+// LDS slot of 16-byte chunk c in row r is c ^ swizzle(r) (see the header comment).
+__device__ __forceinline__ int swizzle(int r) { return (r >> 2) & 3; }
+
+__host__ __device__ inline int grid_tiles(int max_tiles, int n_tiles_n) {
+  const int groups = (n_tiles_n + kGroupN - 1) / kGroupN;
+  return (max_tiles * groups * kGroupN + 7) / 8 * 8;
+}
+
 // Maps the workgroup id to (M-tile, N-tile); false if this workgroup has no tile.
 __device__ __forceinline__ bool tile_of_block(const GemmArgs& p, int& m_t, int& n_t) {
   const int G = gridDim.x;  // multiple of 8
   const int bid = blockIdx.x;
   const int logical = (bid & 7) * (G >> 3) + (bid >> 3);
-  m_t = logical % p.max_tiles;
-  n_t = logical / p.max_tiles;
+  const int group_size = p.max_tiles * kGroupN;
+  const int g = logical / group_size;
+  const int r = logical - g * group_size;
+  m_t = r / kGroupN;
+  n_t = g * kGroupN + (r - m_t * kGroupN);
   if (n_t >= p.n_tiles_n) return false;
   return m_t < *p.tile_count;
 }
 
-template <typename T, bool kSwiGlu>
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, void* lds, uint32_t voffset,
+                                           uint32_t soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds, 16, voffset, soffset, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// One LDS object per (operand, stage): with distinct objects the compiler's
+// wait-count pass can tell that an LDS-DMA load into one stage does not
+// alias fragment reads from another, and does not stall the reads on vmcnt.
+template <typename T, int kElems, int kOperand, int kStage>
+__device__ __forceinline__ T* stage_buf() {
+  __shared__ __attribute__((aligned(1024))) T buf[kElems];
+  return buf;
+}
+
+template <typename T, bool kSwiGlu, int kBNB, int kStages>
 __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(GemmArgs p) {
   typedef typename Mfma<T>::Frag Frag;
-  __shared__ __attribute__((aligned(16))) T lds_a[2][kBM * kBK];
-  __shared__ __attribute__((aligned(16))) T lds_b[2][kBNB * kBK];
+  constexpr int kNB = kBNB / 64;                     // 32-column blocks per wavefront
+  constexpr int kLoadsA = kBM * kChunks / kThreads;  // 16-byte chunks per thread per stage
+  constexpr int kLoadsB = kBNB * kChunks / kThreads;
+  constexpr int kLoads = kLoadsA + kLoadsB;
+  static_assert(!kSwiGlu || kBNB == 256, "fused gate/up uses 128 + 128 B rows");
+  static_assert(kStages >= 3, "at least two stages in flight");
 
   int m_t, n_t;
   if (!tile_of_block(p, m_t, n_t)) return;
-  const int e = p.tiles[2 * m_t];
-  const int row0 = p.tiles[2 * m_t + 1];
-  const int row_end = min(p.offsets[e + 1], p.rows);
+  const int e = __builtin_amdgcn_readfirstlane(p.tiles[2 * m_t]);
+  const int row0 = __builtin_amdgcn_readfirstlane(p.tiles[2 * m_t + 1]);
+  const int row_end = min(__builtin_amdgcn_readfirstlane(p.offsets[e + 1]), p.rows);
   const int mrows = min(kBM, row_end - row0);
   if (mrows <= 0) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1;  // 0..3
   const int wn = wave & 1;   // 0..1
   const int K = p.K;
   const int N = p.N;
+  const uint32_t row_bytes = (uint32_t)K * sizeof(T);
 
-  // Global -> LDS copy assignment: thread owns chunk lc of rows lr + 64*i.
-  const int lr = tid >> 3;
-  const int lc = tid & 7;
-  const T* a_ptr[4];
-  const T* b_ptr[4];
-  const T* A = static_cast<const T*>(p.a);
+  const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(p.a), (short)0, (int)((uint32_t)p.a_rows * row_bytes), kRsrcFlags);
+  const int64_t expert_elems = (int64_t)e * N * K;
+  const int b_bytes = (int)((uint32_t)N * row_bytes);
+  const __amdgpu_buffer_rsrc_t rsrc_b0 = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T*>(static_cast<const T*>(p.b0) + expert_elems), (short)0, b_bytes, kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rsrc_b1 = kSwiGlu
+      ? __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(static_cast<const T*>(p.b1) + expert_elems),
+                                          (short)0, b_bytes, kRsrcFlags)
+      : rsrc_b0;
+
+  // Copy assignment: instruction j of wavefront w fills LDS chunks
+  // (j*8 + w)*64 + lane, i.e. row (j*8 + w)*16 + lane/4, slot lane%4.
+  uint32_t vo_a[kLoadsA], vo_b[kLoadsB];
+  int kc_a[kLoadsA], kc_b[kLoadsB];  // element offset of the chunk within the stage
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int grow = row0 + min(lr + 64 * i, mrows - 1);
-    const int64_t src = p.a_map ? (int64_t)min(max(p.a_map[grow] / p.a_div, 0), p.a_rows - 1)
-                                : (int64_t)grow;
-    a_ptr[i] = A + src * K + lc * 8;
-    const int brow = lr + 64 * i;
-    int n;
-    const T* base;
-    if (kSwiGlu) {
-      n = n_t * (kBNB / 2) + (brow & (kBNB / 2 - 1));
-      base = static_cast<const T*>(brow < kBNB / 2 ? p.b0 : p.b1);
-    } else {
-      n = n_t * kBNB + brow;
-      base = static_cast<const T*>(p.b0);
-    }
-    n = min(n, N - 1);
-    b_ptr[i] = base + ((int64_t)e * N + n) * K + lc * 8;
+  for (int j = 0; j < kLoadsA; ++j) {
+    const int r = (j * 8 + wave) * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ swizzle(r);
+    const int grow = row0 + min(r, mrows - 1);
+    const int src = p.a_map ? min(max(p.a_map[grow] / p.a_div, 0), p.a_rows - 1) : grow;
+    vo_a[j] = (uint32_t)src * row_bytes + (uint32_t)c * 16u;
+    kc_a[j] = c * 8;
   }
-  int st_off[4];  // swizzled LDS element offset of this thread's chunks
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = lr + 64 * i;
-    st_off[i] = r * kBK + ((lc ^ (r & 7)) * 8);
+  for (int j = 0; j < kLoadsB; ++j) {
+    const int r = (j * 8 + wave) * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ swizzle(r);
+    // rows past N fall beyond the buffer and read as zero
+    const int n = kSwiGlu ? n_t * (kBNB / 2) + (r & (kBNB / 2 - 1)) : n_t * kBNB + r;
+    vo_b[j] = (uint32_t)n * row_bytes + (uint32_t)c * 16u;
+    kc_b[j] = c * 8;
   }
 
-  f32x16 acc[2][4];
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
-
-  uint4 ra[4], rb[4];
-  auto load_step = [&](int kt) {
+  auto issue_loads = [&](int kt, T* la, T* lb) {
     const int k0 = kt * kBK;
-    const bool ok = k0 + lc * 8 < K;
+    const uint32_t soff = (uint32_t)k0 * sizeof(T);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = ok ? *reinterpret_cast<const uint4*>(a_ptr[i] + k0) : make_uint4(0, 0, 0, 0);
-      rb[i] = ok ? *reinterpret_cast<const uint4*>(b_ptr[i] + k0) : make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < kLoadsA; ++j) {
+      const uint32_t vo = (k0 + kc_a[j] < K) ? vo_a[j] : kOutOfRange;
+      load_lds16(rsrc_a, la + (j * 8 + wave) * 64 * 8, vo, soff);
     }
-  };
-  auto store_step = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<uint4*>(&lds_a[buf][st_off[i]]) = ra[i];
-      *reinterpret_cast<uint4*>(&lds_b[buf][st_off[i]]) = rb[i];
+    for (int j = 0; j < kLoadsB; ++j) {
+      const uint32_t vo = (k0 + kc_b[j] < K) ? vo_b[j] : kOutOfRange;
+      // fused gate/up: B rows 0..127 come from gate (j = 0), 128..255 from up (j = 1)
+      load_lds16(kSwiGlu && j * 8 * 16 >= kBNB / 2 ? rsrc_b1 : rsrc_b0,
+                 lb + (j * 8 + wave) * 64 * 8, vo, soff);
     }
   };
 
   // Fragment rows of this wavefront (MFMA A: lane holds row lane%32; B: lane
-  // holds column lane%32, i.e. weight row).
-  int a_row[2], b_row[4];
+  // holds column lane%32, i.e. weight row). All block bases are multiples of
+  // 32, so every fragment row has the same swizzle as row lane%32.
+  int a_row[2], b_row[kNB];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) a_row[mb] = wm * 64 + mb * 32 + (lane & 31);
+  for (int mb = 0; mb < 2; ++mb) a_row[mb] = (wm * 64 + mb * 32 + (lane & 31)) * kBK;
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    if (kSwiGlu)
-      b_row[nb] = (nb >> 1) * (kBNB / 2) + wn * 64 + (nb & 1) * 32 + (lane & 31);
-    else
-      b_row[nb] = wn * 128 + nb * 32 + (lane & 31);
+  for (int nb = 0; nb < kNB; ++nb) {
+    const int r = kSwiGlu ? (nb >> 1) * (kBNB / 2) + wn * 64 + (nb & 1) * 32 + (lane & 31)
+                          : wn * (kBNB / 2) + nb * 32 + (lane & 31);
+    b_row[nb] = r * kBK;
   }
-  const int sw = lane & 7;  // == row & 7 for every fragment row above
+  const int sw = swizzle(lane & 31);
+
+  f32x16 acc[2][kNB];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
+
+  Frag fa[2][2], fb[2][kNB];
+  auto read_frags = [&](const T* la, const T* lb, int s, int slot) {
+    const int c = ((2 * s + (lane >> 5)) ^ sw) * 8;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) fa[slot][mb] = *reinterpret_cast<const Frag*>(la + a_row[mb] + c);
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) fb[slot][nb] = *reinterpret_cast<const Frag*>(lb + b_row[nb] + c);
+  };
 
   const int nk = (K + kBK - 1) / kBK;
-  load_step(0);
-  store_step(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) load_step(kt + 1);
-    const T* la = lds_a[cur];
-    const T* lb = lds_b[cur];
+  constexpr int kMfma = 2 * kNB;  // MFMAs per k16 sub-step
+  constexpr int kReads = 2 + kNB;  // fragment reads per sub-step
+
+  // One K-stage: compute from stage S while stage S-1 (read in the previous
+  // step) is refilled for k-step kt + kStages - 1. Stages kt+1 .. kt+kStages-1
+  // are in flight; before the barrier only the oldest (kt+1) must have landed,
+  // so the wait is vmcnt((kStages-2) * loads). The barrier is a plain
+  // s_barrier (a scheduling boundary): a fenced __syncthreads would make the
+  // compiler drain every LDS-DMA load in flight.
+  // Order: [loads, sub-step 0 MFMAs interleaved with sub-step 1 fragment
+  // reads, half of sub-step 1] barrier [next stage's sub-step 0 fragment
+  // reads overlapping the other half of sub-step 1].
+  auto step = [&](auto stage, int kt) {
+    constexpr int S = decltype(stage)::value;
+    constexpr int F = (S + kStages - 1) % kStages;
+    constexpr int X = (S + 1) % kStages;
+    T* ca = stage_buf<T, kBM * kBK, 0, S>();
+    T* cb = stage_buf<T, kBNB * kBK, 1, S>();
+    issue_loads(kt + kStages - 1, stage_buf<T, kBM * kBK, 0, F>(), stage_buf<T, kBNB * kBK, 1, F>());
+    read_frags(ca, cb, 1, 1);
 #pragma unroll
-    for (int s = 0; s < kBK / 16; ++s) {
-      const int c = ((2 * s + (lane >> 5)) ^ sw) * 8;
-      Frag fa[2], fb[4];
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) fa[mb] = *reinterpret_cast<const Frag*>(la + a_row[mb] * kBK + c);
+      for (int nb = 0; nb < kNB; ++nb)
+        acc[mb][nb] = Mfma<T>::run(fa[0][mb], fb[0][nb], acc[mb][nb]);
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) fb[nb] = *reinterpret_cast<const Frag*>(lb + b_row[nb] * kBK + c);
+    for (int i = 0; i < kMfma / 2; ++i)
+      acc[i / kNB][i % kNB] = Mfma<T>::run(fa[1][i / kNB], fb[1][i % kNB], acc[i / kNB][i % kNB]);
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = Mfma<T>::run(fa[mb], fb[nb], acc[mb][nb]);
+    for (int i = 0; i < kMfma; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < kLoads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      if (i < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    if (kt + 1 < nk) store_step(cur ^ 1);
-    __syncthreads();
+    __builtin_amdgcn_sched_group_barrier(0x008, kMfma / 2, 0);
+    wait_vmem<(kStages - 2) * kLoads>();
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    read_frags(stage_buf<T, kBM * kBK, 0, X>(), stage_buf<T, kBNB * kBK, 1, X>(), 0, 0);
+#pragma unroll
+    for (int i = kMfma / 2; i < kMfma; ++i)
+      acc[i / kNB][i % kNB] = Mfma<T>::run(fa[1][i / kNB], fb[1][i % kNB], acc[i / kNB][i % kNB]);
+#pragma unroll
+    for (int i = 0; i < kReads; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (i < kMfma / 2) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+  };
+
+  // Prologue: stages 0 .. kStages-2 in flight, wait for stage 0.
+  issue_loads(0, stage_buf<T, kBM * kBK, 0, 0>(), stage_buf<T, kBNB * kBK, 1, 0>());
+  issue_loads(1, stage_buf<T, kBM * kBK, 0, 1>(), stage_buf<T, kBNB * kBK, 1, 1>());
+  if constexpr (kStages > 3)
+    issue_loads(2, stage_buf<T, kBM * kBK, 0, 2 % kStages>(), stage_buf<T, kBNB * kBK, 1, 2 % kStages>());
+  if constexpr (kStages > 4)
+    issue_loads(3, stage_buf<T, kBM * kBK, 0, 3 % kStages>(), stage_buf<T, kBNB * kBK, 1, 3 % kStages>());
+  wait_vmem<(kStages - 2) * kLoads>();
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  read_frags(stage_buf<T, kBM * kBK, 0, 0>(), stage_buf<T, kBNB * kBK, 1, 0>(), 0, 0);
+
+  // Main loop, unrolled by kStages so every LDS pointer is a fixed object.
+  // The trip count is padded to a multiple of kStages: loads past K are
+  // masked to zeros, so the padding steps add nothing to the accumulators,
+  // and the body stays one straight-line block.
+  const int nk_pad = (nk + kStages - 1) / kStages * kStages;
+  for (int kt = 0; kt < nk_pad; kt += kStages) {
+    step(std::integral_constant<int, 0>{}, kt);
+    step(std::integral_constant<int, 1>{}, kt + 1);
+    step(std::integral_constant<int, 2 % kStages>{}, kt + 2);
+    if constexpr (kStages > 3) step(std::integral_constant<int, 3 % kStages>{}, kt + 3);
+    if constexpr (kStages > 4) step(std::integral_constant<int, 4 % kStages>{}, kt + 4);
   }
 
   // Epilogue. Accumulator element v of lane l sits at row
@@ -245,8 +359,8 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int col = n_t * kBNB + wn * 128 + nb * 32 + col_lane;
+      for (int nb = 0; nb < kNB; ++nb) {
+        const int col = n_t * kBNB + wn * (kBNB / 2) + nb * 32 + col_lane;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int lrow = wm * 64 + mb * 32 + (v >> 2) * 8 + row_lane + (v & 3);
@@ -346,8 +460,6 @@ __global__ __launch_bounds__(256) void simt_gemm_kernel(GemmArgs p) {
   }
 }
 
-inline int round_up8(int64_t g) { return (int)((g + 7) / 8 * 8); }
-
 }  // namespace
 
 ExpertsPlan experts_plan(int64_t rows, int64_t E, int dt) {
@@ -388,35 +500,57 @@ GemmArgs plan_tiles(const int32_t* offsets, int rows, int E, int dt, void* scrat
   return g;
 }
 
-template <bool kSwiGlu>
-void launch_gemm(const GemmArgs& g, int dt, hipStream_t s) {
-  const dim3 grid(round_up8((int64_t)g.max_tiles * g.n_tiles_n));
-  if (dt == kF32)
-    hipLaunchKernelGGL(simt_gemm_kernel<kSwiGlu>, grid, dim3(256), 0, s, g);
-  else if (dt == kF16)
-    hipLaunchKernelGGL((mfma_gemm_kernel<f16, kSwiGlu>), grid, dim3(kThreads), 0, s, g);
-  else
-    hipLaunchKernelGGL((mfma_gemm_kernel<bf16, kSwiGlu>), grid, dim3(kThreads), 0, s, g);
+constexpr int kCUs = 256;
+constexpr int kStagesGemm = 4;
+
+// B-tile rows of the down GEMM: 256, or 128 when 256-wide tiles would leave
+// the 256 CUs with fewer than four workgroups each.
+int down_bnb(int max_tiles, int N) {
+  return (int64_t)max_tiles * ((N + 255) / 256) < 4 * kCUs ? 128 : 256;
 }
 
-int n_tiles(int N, int dt, bool swiglu) {
-  const int bn = dt == kF32 ? 64 : (swiglu ? kBNB / 2 : kBNB);
-  return (N + bn - 1) / bn;
+template <typename T>
+void launch_mfma(GemmArgs g, bool swiglu, hipStream_t s) {
+  if (swiglu) {
+    g.n_tiles_n = (g.N + 127) / 128;
+    hipLaunchKernelGGL((mfma_gemm_kernel<T, true, 256, kStagesGemm>), dim3(grid_tiles(g.max_tiles, g.n_tiles_n)),
+                       dim3(kThreads), 0, s, g);
+  } else if (down_bnb(g.max_tiles, g.N) == 128) {
+    g.n_tiles_n = (g.N + 127) / 128;
+    hipLaunchKernelGGL((mfma_gemm_kernel<T, false, 128, kStagesGemm>), dim3(grid_tiles(g.max_tiles, g.n_tiles_n)),
+                       dim3(kThreads), 0, s, g);
+  } else {
+    g.n_tiles_n = (g.N + 255) / 256;
+    hipLaunchKernelGGL((mfma_gemm_kernel<T, false, 256, kStagesGemm>), dim3(grid_tiles(g.max_tiles, g.n_tiles_n)),
+                       dim3(kThreads), 0, s, g);
+  }
+}
+
+template <bool kSwiGlu>
+void launch_gemm(GemmArgs g, int dt, hipStream_t s) {
+  if (dt == kF32) {
+    g.n_tiles_n = (g.N + 63) / 64;
+    hipLaunchKernelGGL(simt_gemm_kernel<kSwiGlu>, dim3(grid_tiles(g.max_tiles, g.n_tiles_n)),
+                       dim3(256), 0, s, g);
+  } else if (dt == kF16) {
+    launch_mfma<f16>(g, kSwiGlu, s);
+  } else {
+    launch_mfma<bf16>(g, kSwiGlu, s);
+  }
 }
 
 void setup_gate_up(GemmArgs& g, const void* a, const int32_t* a_map, int a_div, int H, int I,
-                   const void* w_gate, const void* w_up, int dt, void* h) {
+                   const void* w_gate, const void* w_up, void* h) {
   g.a = a; g.a_map = a_map; g.a_div = a_div > 0 ? a_div : 1;
-  g.a_rows = (g.rows + g.a_div - 1) / g.a_div;
+  g.a_rows = a_map ? (g.rows + g.a_div - 1) / g.a_div : g.rows;
   g.b0 = w_gate; g.b1 = w_up; g.c = h;
-  g.N = I; g.K = H; g.n_tiles_n = n_tiles(I, dt, true);
+  g.N = I; g.K = H;
 }
 
-void setup_down(GemmArgs& g, const void* h, int H, int I, const void* w_down, int dt,
-                void* expert_out) {
-  g.a = h; g.a_map = nullptr; g.a_div = 1;
+void setup_down(GemmArgs& g, const void* h, int H, int I, const void* w_down, void* expert_out) {
+  g.a = h; g.a_map = nullptr; g.a_div = 1; g.a_rows = g.rows;
   g.b0 = w_down; g.b1 = nullptr; g.c = expert_out;
-  g.N = H; g.K = I; g.n_tiles_n = n_tiles(H, dt, false);
+  g.N = H; g.K = I;
 }
 
 }  // namespace
@@ -426,7 +560,7 @@ hipError_t launch_gate_up(const void* a, const int32_t* a_map, int a_div, const 
                           int dt, void* h, void* scratch, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   GemmArgs g = plan_tiles(offsets, rows, E, dt, scratch, s);
-  setup_gate_up(g, a, a_map, a_div, H, I, w_gate, w_up, dt, h);
+  setup_gate_up(g, a, a_map, a_div, H, I, w_gate, w_up, h);
   launch_gemm<true>(g, dt, s);
   return hipGetLastError();
 }
@@ -436,7 +570,7 @@ hipError_t launch_down(const void* h, const int32_t* offsets, int rows, int E, i
                        hipStream_t s) {
   if (rows == 0) return hipSuccess;
   GemmArgs g = plan_tiles(offsets, rows, E, dt, scratch, s);
-  setup_down(g, h, H, I, w_down, dt, expert_out);
+  setup_down(g, h, H, I, w_down, expert_out);
   launch_gemm<false>(g, dt, s);
   return hipGetLastError();
 }
@@ -449,8 +583,8 @@ hipError_t launch_experts(const void* a, const int32_t* a_map, int a_div,
   void* h = static_cast<char*>(scratch) + tile_scratch_bytes(rows, E, dt);
   GemmArgs g1 = plan_tiles(offsets, rows, E, dt, scratch, s);
   GemmArgs g2 = g1;
-  setup_gate_up(g1, a, a_map, a_div, H, I, w_gate, w_up, dt, h);
-  setup_down(g2, h, H, I, w_down, dt, expert_out);
+  setup_gate_up(g1, a, a_map, a_div, H, I, w_gate, w_up, h);
+  setup_down(g2, h, H, I, w_down, expert_out);
   launch_gemm<true>(g1, dt, s);
   launch_gemm<false>(g2, dt, s);
   return hipGetLastError();
