@@ -1,16 +1,15 @@
 """Benchmark of the local MoE FFN forward on one MI355X.
 
-One step = one pass of the whole path over one batch of synthetic input:
-route -> dispatch (maps) -> experts gate/up (+SiLU*up) -> experts down ->
-combine, each through the C ABI on the current stream, inputs resident in
-HBM. Default workload: the Mixtral-shaped bf16 batch (T=4096, H=4096,
+One step = one moe_forward call through the C ABI (route -> dispatch maps
+-> gate/up GEMM with fused SiLU*up -> down GEMM -> combine) on the current
+stream over one batch of synthetic input, inputs resident in HBM. Default workload: the Mixtral-shaped bf16 batch (T=4096, H=4096,
 I=14336, E=8, top_k=2, renormalize). Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
-The dominant kernel (the gate/up grouped GEMM) is bracketed by HIP events on
-the stream it runs on, every timed step; its average duration gives the
-roofline figure. The CPU baseline times the oracle on the first tokens of the
+moe_forward records HIP events on its stream at the stage boundaries of
+every timed step; the gate/up stage (the dominant kernel, plus its one-block
+tile plan) gives the roofline figure. The CPU baseline times the oracle on the first tokens of the
 same workload.
 """
 from __future__ import annotations
@@ -127,34 +126,15 @@ def main():
     # ---- buffers ----------------------------------------------------------
     idx = torch.empty((T, k), dtype=torch.int32, device=dev)
     wts = torch.empty((T, k), dtype=torch.float32, device=dev)
-    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
-    sor = torch.empty(R, dtype=torch.int32, device=dev)
-    ros = torch.empty(R, dtype=torch.int32, device=dev)
-    h = torch.empty((R, I_), dtype=td, device=dev)
-    y = torch.empty((R, H), dtype=td, device=dev)
     out = torch.empty((T, H), dtype=td, device=dev)
-    ws_d = torch.empty(max(moe.moe_dispatch_workspace_size(T, k, E), 1), dtype=torch.uint8, device=dev)
-    ws_g = torch.empty(max(moe.moe_experts_gemm_workspace_size(R, E, td), 1), dtype=torch.uint8, device=dev)
-    ws_g2 = torch.empty_like(ws_g)
+    ws = torch.empty(moe.moe_forward_workspace_size(T, H, I_, E, k, td, torch.float32),
+                     dtype=torch.uint8, device=dev)
 
     stages = ["route", "dispatch", "gate_up", "down", "combine"]
 
     def step(ev=None):
-        def mark(i):
-            if ev is not None:
-                ev[i].record()
-        mark(0)
-        moe.moe_route(zd, k, w.renormalize, indices=idx, weights=wts)
-        mark(1)
-        moe.moe_dispatch(idx, E, ws=ws_d, offsets=offsets, slot_of_row=sor, row_of_slot=ros)
-        mark(2)
-        moe.moe_experts_gate_up(xd, offsets, wt["w_gate"], wt["w_up"], row_map=sor, map_div=k,
-                                rows=R, h=h, ws=ws_g)
-        mark(3)
-        moe.moe_experts_down(h, offsets, wt["w_down"], expert_out=y, ws=ws_g2)
-        mark(4)
-        moe.moe_combine(y, ros, wts, out=out)
-        mark(5)
+        moe.moe_forward(xd, zd, k, w.renormalize, wt["w_gate"], wt["w_up"], wt["w_down"], out=out,
+                        indices_out=idx, weights_out=wts, ws=ws, stage_events=ev)
 
     for _ in range(args.warmup):
         step()
@@ -162,6 +142,9 @@ def main():
     log(f"warmup done ({args.warmup} steps)")
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    for ev in evs:  # create the events before the timed region
+        for e_ in ev:
+            e_.record()
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for s in range(args.steps):
@@ -170,6 +153,8 @@ def main():
     t_end = time.perf_counter()
     elapsed = t_end - t_start
     log(f"timed {args.steps} steps in {elapsed:.3f}s")
+    offsets = torch.from_numpy(np.concatenate([[0], np.cumsum(np.bincount(idx.cpu().numpy().ravel(),
+                                                                            minlength=E))])).int()
 
     stage_ms = {name: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
                 for i, name in enumerate(stages)}

@@ -143,8 +143,9 @@ size_t moe_experts_workspace_size(int64_t rows, int64_t E, int64_t H, int64_t I,
  *     moe_dispatch and map_div = top_k to read tokens without materialising
  *     x_disp. Map entries are clamped to the rows of x.
  *   moe_experts_down:  expert_out[r] = W_down[e] h[r], expert_out [rows, H] dt.
- *   ws / ws_bytes: at least moe_experts_gemm_workspace_size(rows, E, dt)
- *   (the device-built tile list); one workspace per in-flight call.
+ *   ws / ws_bytes: at least moe_experts_gemm_workspace_size(rows, E, H, I, dt)
+ *   (the device-built tile list, and for the down GEMM possibly fp32
+ *   split-K partial sums); one workspace per in-flight call.
  * Errors: ARGUMENT if row_map is given and map_div is not in [1, rows].
  */
 moe_status moe_experts_gate_up(const void* x, const int32_t* row_map, int64_t map_div,
@@ -154,7 +155,8 @@ moe_status moe_experts_gate_up(const void* x, const int32_t* row_map, int64_t ma
 moe_status moe_experts_down(const void* h, const int32_t* expert_offsets, int64_t rows, int64_t E,
                             int64_t H, int64_t I, const void* w_down, moe_dtype dt,
                             void* expert_out, void* ws, size_t ws_bytes, hipStream_t stream);
-size_t moe_experts_gemm_workspace_size(int64_t rows, int64_t E, moe_dtype dt);
+size_t moe_experts_gemm_workspace_size(int64_t rows, int64_t E, int64_t H, int64_t I,
+                                       moe_dtype dt);
 
 /*
  * moe_combine - restore token order and merge expert outputs.
@@ -181,12 +183,15 @@ moe_status moe_combine(const void* expert_out, const int32_t* row_of_slot, const
  *   indices_out [T, top_k] uint32 and weights_out [T, top_k] logits_dt are
  *   optional copies of the routing plan (NULL to skip).
  *   ws / ws_bytes scratch, at least moe_forward_workspace_size(...).
+ *   stage_events: NULL, or 6 caller-created HIP events recorded on `stream`
+ *   before route, after route, after dispatch, after the gate/up GEMM, after
+ *   the down GEMM and after the combine (per-stage timing).
  */
 moe_status moe_forward(const void* x, const void* logits, moe_dtype logits_dt, int64_t T,
                        int64_t H, int64_t I, int64_t E, int64_t top_k, int renormalize,
                        const void* w_gate, const void* w_up, const void* w_down, moe_dtype dt,
                        void* out, uint32_t* indices_out, void* weights_out,
-                       void* ws, size_t ws_bytes, hipStream_t stream);
+                       void* ws, size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream);
 size_t moe_forward_workspace_size(int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k,
                                   moe_dtype dt, moe_dtype logits_dt);
 

@@ -95,7 +95,7 @@ ForwardLayout forward_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t
   L.row_of_slot = o; o += align256(slots * 4);
   L.dispatch = o;    o += align256(dispatch_scratch_bytes((int64_t)slots, E));
   L.expert_out = o;  o += align256(slots * (size_t)H * dtype_size(dt));
-  L.experts = o;     o += align256(experts_scratch_bytes((int64_t)slots, E, I, dt));
+  L.experts = o;     o += align256(experts_scratch_bytes((int64_t)slots, E, H, I, dt));
   L.total = o;
   return L;
 }
@@ -176,7 +176,7 @@ moe_status moe_dispatch(const uint32_t* indices, int64_t T, int64_t top_k, int64
 size_t moe_experts_workspace_size(int64_t rows, int64_t E, int64_t H, int64_t I, moe_dtype dt) {
   if (rows < 0 || E < 1 || E > kMaxE || rows > INT32_MAX || H < 1 || I < 1 || !valid_dt(dt))
     return 0;
-  return align256(experts_scratch_bytes(rows, E, I, dt));
+  return align256(experts_scratch_bytes(rows, E, H, I, dt));
 }
 
 moe_status moe_experts_forward_dispatched(const void* x_disp, const int32_t* expert_offsets,
@@ -206,9 +206,11 @@ moe_status moe_experts_forward_dispatched(const void* x_disp, const int32_t* exp
                                  (int)I, w_gate, w_up, w_down, dt, expert_out, ws, stream));
 }
 
-size_t moe_experts_gemm_workspace_size(int64_t rows, int64_t E, moe_dtype dt) {
-  if (rows < 0 || E < 1 || E > kMaxE || rows > INT32_MAX || !valid_dt(dt)) return 0;
-  return align256(tile_scratch_bytes(rows, E, dt));
+size_t moe_experts_gemm_workspace_size(int64_t rows, int64_t E, int64_t H, int64_t I,
+                                       moe_dtype dt) {
+  if (rows < 0 || E < 1 || E > kMaxE || rows > INT32_MAX || H < 1 || I < 1 || !valid_dt(dt))
+    return 0;
+  return align256(gemm_scratch_bytes(rows, E, H, I, dt));
 }
 
 moe_status moe_experts_gate_up(const void* x, const int32_t* row_map, int64_t map_div,
@@ -222,7 +224,7 @@ moe_status moe_experts_gate_up(const void* x, const int32_t* row_map, int64_t ma
     return MOE_ERROR_UNSUPPORTED;
   if (rows == 0) return MOE_SUCCESS;
   if (!x || !expert_offsets || !w_gate || !w_up || !h) return MOE_ERROR_NULL_POINTER;
-  const size_t need = moe_experts_gemm_workspace_size(rows, E, dt);
+  const size_t need = moe_experts_gemm_workspace_size(rows, E, H, I, dt);
   if (!ws || ((uintptr_t)ws & 255) || ws_bytes < need) return MOE_ERROR_WORKSPACE;
   const size_t ds = dtype_size(dt), wbytes = (size_t)E * (size_t)I * (size_t)H * ds;
   const size_t x_rows = row_map ? (size_t)((rows + map_div - 1) / map_div) : (size_t)rows;
@@ -246,7 +248,7 @@ moe_status moe_experts_down(const void* h, const int32_t* expert_offsets, int64_
     return MOE_ERROR_UNSUPPORTED;
   if (rows == 0) return MOE_SUCCESS;
   if (!h || !expert_offsets || !w_down || !expert_out) return MOE_ERROR_NULL_POINTER;
-  const size_t need = moe_experts_gemm_workspace_size(rows, E, dt);
+  const size_t need = moe_experts_gemm_workspace_size(rows, E, H, I, dt);
   if (!ws || ((uintptr_t)ws & 255) || ws_bytes < need) return MOE_ERROR_WORKSPACE;
   const size_t ds = dtype_size(dt), wbytes = (size_t)E * (size_t)I * (size_t)H * ds;
   const Span outs[] = {{expert_out, (size_t)rows * (size_t)H * ds}, {ws, need}};
@@ -318,7 +320,7 @@ moe_status moe_forward(const void* x, const void* logits, moe_dtype logits_dt, i
                        int64_t H, int64_t I, int64_t E, int64_t top_k, int renormalize,
                        const void* w_gate, const void* w_up, const void* w_down, moe_dtype dt,
                        void* out, uint32_t* indices_out, void* weights_out, void* ws,
-                       size_t ws_bytes, hipStream_t stream) {
+                       size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream) {
   if (H < 1 || I < 1) return MOE_ERROR_SHAPE;
   moe_status st = check_route_args(T, E, top_k, logits_dt);
   if (st != MOE_SUCCESS) return st;
@@ -346,18 +348,38 @@ moe_status moe_forward(const void* x, const void* logits, moe_dtype logits_dt, i
   int32_t* ros = reinterpret_cast<int32_t*>(base + L.row_of_slot);
   void* y = base + L.expert_out;
 
-  hipError_t e = launch_route(logits, logits_dt, (int)T, (int)E, (int)top_k,
-                              renormalize ? 1 : 0, idx, w, stream);
+  auto mark = [&](int i) -> hipError_t {
+    return stage_events ? hipEventRecord(stage_events[i], stream) : hipSuccess;
+  };
+  hipError_t e = mark(0);
+  if (e == hipSuccess)
+    e = launch_route(logits, logits_dt, (int)T, (int)E, (int)top_k, renormalize ? 1 : 0, idx, w,
+                     stream);
+  if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess)
     e = launch_dispatch_maps(idx, (int)slots, (int)E, offsets, sor, ros,
                              reinterpret_cast<int32_t*>(base + L.dispatch), stream);
-  // The expert GEMM gathers token rows through slot_of_row; x_disp is never
+  if (e == hipSuccess) e = mark(2);
+  // The gate/up GEMM gathers token rows through slot_of_row; x_disp is never
   // materialised on this path.
+  void* h = base + L.experts + gemm_scratch_bytes((int64_t)slots, E, H, I, dt);
   if (e == hipSuccess)
-    e = launch_experts(x, sor, (int)top_k, offsets, (int)slots, (int)E, (int)H, (int)I, w_gate,
-                       w_up, w_down, dt, y, base + L.experts, stream);
+    e = launch_gate_up(x, sor, (int)top_k, offsets, (int)slots, (int)E, (int)H, (int)I, w_gate,
+                       w_up, dt, h, base + L.experts, stream);
+  if (e == hipSuccess) e = mark(3);
+  // When the down GEMM splits K, its fp32 partial sums go straight to the
+  // combine, which rounds each expert row exactly as expert_out would be.
+  DownPartials part;
   if (e == hipSuccess)
-    e = launch_combine(y, ros, w, logits_dt, (int)T, (int)top_k, (int)H, dt, out, stream);
+    e = launch_down(h, offsets, (int)slots, (int)E, (int)H, (int)I, w_down, dt, y,
+                    base + L.experts, stream, &part);
+  if (e == hipSuccess) e = mark(4);
+  if (e == hipSuccess)
+    e = part.splits > 1
+            ? launch_combine_partials(part, ros, w, logits_dt, (int)T, (int)top_k, (int)H, dt, out,
+                                      stream)
+            : launch_combine(y, ros, w, logits_dt, (int)T, (int)top_k, (int)H, dt, out, stream);
+  if (e == hipSuccess) e = mark(5);
   return from_hip(e);
 }
 

@@ -38,6 +38,7 @@
 // logical tiles. Logical tiles sweep groups of 8 N-tiles, M-tile by M-tile
 // inside a group, so the ~32 workgroups resident on one XCD share 8 weight
 // tiles and a few activation tiles through its L2.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -49,7 +50,6 @@ namespace {
 constexpr int kBM = 256;      // rows per M-tile (MFMA path)
 constexpr int kBK = 32;       // K per pipeline stage
 constexpr int kChunks = kBK / 8;  // 16-byte chunks per LDS row
-constexpr int kThreads = 512;
 constexpr int kBMSimt = 64;   // rows per M-tile (fp32 path)
 constexpr int kGroupN = 8;    // N-tiles per rasterisation group
 // Third dword of a raw buffer resource on gfx9-family parts (no format, no swizzle).
@@ -91,6 +91,11 @@ struct GemmArgs {
   const int32_t* tiles;    // [max_tiles][2]
   const int32_t* tile_count;
   int rows, N, K, max_tiles, n_tiles_n;
+  // Split-K (GEMM 2 only): k_splits workgroups share one output tile, each
+  // over k_chunk elements of K, writing fp32 partial sums to
+  // partial[split][rows][N]; the caller reduces them in split order.
+  int k_splits, k_chunk;
+  float* partial;
 };
 
 template <typename T> struct Mfma;
@@ -112,17 +117,22 @@ __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g));
 // LDS slot of 16-byte chunk c in row r is c ^ swizzle(r) (see the header comment).
 __device__ __forceinline__ int swizzle(int r) { return (r >> 2) & 3; }
 
-__host__ __device__ inline int grid_tiles(int max_tiles, int n_tiles_n) {
+__host__ __device__ inline int grid_tiles(int max_tiles, int n_tiles_n, int k_splits = 1) {
   const int groups = (n_tiles_n + kGroupN - 1) / kGroupN;
-  return (max_tiles * groups * kGroupN + 7) / 8 * 8;
+  return (max_tiles * groups * kGroupN * k_splits + 7) / 8 * 8;
 }
 
-// Maps the workgroup id to (M-tile, N-tile); false if this workgroup has no tile.
-__device__ __forceinline__ bool tile_of_block(const GemmArgs& p, int& m_t, int& n_t) {
+// Maps the workgroup id to (M-tile, N-tile, K-split); false if this
+// workgroup has no tile. Splits are the slowest-varying index.
+__device__ __forceinline__ bool tile_of_block(const GemmArgs& p, int& m_t, int& n_t, int& ks) {
   const int G = gridDim.x;  // multiple of 8
   const int bid = blockIdx.x;
-  const int logical = (bid & 7) * (G >> 3) + (bid >> 3);
+  int logical = (bid & 7) * (G >> 3) + (bid >> 3);
   const int group_size = p.max_tiles * kGroupN;
+  const int per_split = group_size * ((p.n_tiles_n + kGroupN - 1) / kGroupN);
+  ks = logical / per_split;
+  if (ks >= p.k_splits) return false;
+  logical -= ks * per_split;
   const int g = logical / group_size;
   const int r = logical - g * group_size;
   m_t = r / kGroupN;
@@ -154,28 +164,38 @@ __device__ __forceinline__ T* stage_buf() {
   return buf;
 }
 
-template <typename T, bool kSwiGlu, int kBNB, int kStages>
-__global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(GemmArgs p) {
+// kWaveM: rows per wavefront, 64 (8 wavefronts, 4 x 2) or 128 (4 wavefronts,
+// 2 x 2; 256 accumulators per lane, one wavefront per SIMD).
+template <int kWaveM>
+constexpr int gemm_threads() { return 64 * (kBM / kWaveM) * 2; }
+
+template <typename T, bool kSwiGlu, int kBNB, int kStages, int kWaveM>
+__global__ __launch_bounds__(gemm_threads<kWaveM>()) void mfma_gemm_kernel(GemmArgs p) {
   typedef typename Mfma<T>::Frag Frag;
-  constexpr int kNB = kBNB / 64;                     // 32-column blocks per wavefront
-  constexpr int kLoadsA = kBM * kChunks / kThreads;  // 16-byte chunks per thread per stage
-  constexpr int kLoadsB = kBNB * kChunks / kThreads;
+  constexpr int kWaves = (kBM / kWaveM) * 2;
+  constexpr int kThreadsK = 64 * kWaves;
+  constexpr int kMB = kWaveM / 32;                    // 32-row blocks per wavefront
+  constexpr int kNB = kBNB / 64;                      // 32-column blocks per wavefront
+  constexpr int kLoadsA = kBM * kChunks / kThreadsK;  // 16-byte chunks per thread per stage
+  constexpr int kLoadsB = kBNB * kChunks / kThreadsK;
   constexpr int kLoads = kLoadsA + kLoadsB;
   static_assert(!kSwiGlu || kBNB == 256, "fused gate/up uses 128 + 128 B rows");
   static_assert(kStages >= 3, "at least two stages in flight");
 
-  int m_t, n_t;
-  if (!tile_of_block(p, m_t, n_t)) return;
+  int m_t, n_t, ks;
+  if (!tile_of_block(p, m_t, n_t, ks)) return;
   const int e = __builtin_amdgcn_readfirstlane(p.tiles[2 * m_t]);
   const int row0 = __builtin_amdgcn_readfirstlane(p.tiles[2 * m_t + 1]);
   const int row_end = min(__builtin_amdgcn_readfirstlane(p.offsets[e + 1]), p.rows);
   const int mrows = min(kBM, row_end - row0);
   if (mrows <= 0) return;
+  const int k_begin = ks * p.k_chunk;
+  const int k_end = min(p.K, k_begin + p.k_chunk);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1;  // 0..3
+  const int wm = wave >> 1;  // 0 .. kWaves/2 - 1
   const int wn = wave & 1;   // 0..1
   const int K = p.K;
   const int N = p.N;
@@ -193,12 +213,12 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(GemmArgs p) {
       : rsrc_b0;
 
   // Copy assignment: instruction j of wavefront w fills LDS chunks
-  // (j*8 + w)*64 + lane, i.e. row (j*8 + w)*16 + lane/4, slot lane%4.
+  // (j*kWaves + w)*64 + lane, i.e. row (j*kWaves + w)*16 + lane/4, slot lane%4.
   uint32_t vo_a[kLoadsA], vo_b[kLoadsB];
   int kc_a[kLoadsA], kc_b[kLoadsB];  // element offset of the chunk within the stage
 #pragma unroll
   for (int j = 0; j < kLoadsA; ++j) {
-    const int r = (j * 8 + wave) * 16 + (lane >> 2);
+    const int r = (j * kWaves + wave) * 16 + (lane >> 2);
     const int c = (lane & 3) ^ swizzle(r);
     const int grow = row0 + min(r, mrows - 1);
     const int src = p.a_map ? min(max(p.a_map[grow] / p.a_div, 0), p.a_rows - 1) : grow;
@@ -207,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(GemmArgs p) {
   }
 #pragma unroll
   for (int j = 0; j < kLoadsB; ++j) {
-    const int r = (j * 8 + wave) * 16 + (lane >> 2);
+    const int r = (j * kWaves + wave) * 16 + (lane >> 2);
     const int c = (lane & 3) ^ swizzle(r);
     // rows past N fall beyond the buffer and read as zero
     const int n = kSwiGlu ? n_t * (kBNB / 2) + (r & (kBNB / 2 - 1)) : n_t * kBNB + r;
@@ -216,28 +236,29 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(GemmArgs p) {
   }
 
   auto issue_loads = [&](int kt, T* la, T* lb) {
-    const int k0 = kt * kBK;
+    const int k0 = k_begin + kt * kBK;
     const uint32_t soff = (uint32_t)k0 * sizeof(T);
 #pragma unroll
     for (int j = 0; j < kLoadsA; ++j) {
-      const uint32_t vo = (k0 + kc_a[j] < K) ? vo_a[j] : kOutOfRange;
-      load_lds16(rsrc_a, la + (j * 8 + wave) * 64 * 8, vo, soff);
+      const uint32_t vo = (k0 + kc_a[j] < k_end) ? vo_a[j] : kOutOfRange;
+      load_lds16(rsrc_a, la + (j * kWaves + wave) * 64 * 8, vo, soff);
     }
 #pragma unroll
     for (int j = 0; j < kLoadsB; ++j) {
-      const uint32_t vo = (k0 + kc_b[j] < K) ? vo_b[j] : kOutOfRange;
-      // fused gate/up: B rows 0..127 come from gate (j = 0), 128..255 from up (j = 1)
-      load_lds16(kSwiGlu && j * 8 * 16 >= kBNB / 2 ? rsrc_b1 : rsrc_b0,
-                 lb + (j * 8 + wave) * 64 * 8, vo, soff);
+      const uint32_t vo = (k0 + kc_b[j] < k_end) ? vo_b[j] : kOutOfRange;
+      // fused gate/up: B rows 0..127 come from gate, 128..255 from up; the
+      // split falls between instructions (row (j*kWaves + w)*16, w < kWaves)
+      load_lds16(kSwiGlu && j * kWaves * 16 >= kBNB / 2 ? rsrc_b1 : rsrc_b0,
+                 lb + (j * kWaves + wave) * 64 * 8, vo, soff);
     }
   };
 
   // Fragment rows of this wavefront (MFMA A: lane holds row lane%32; B: lane
   // holds column lane%32, i.e. weight row). All block bases are multiples of
   // 32, so every fragment row has the same swizzle as row lane%32.
-  int a_row[2], b_row[kNB];
+  int a_row[kMB], b_row[kNB];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) a_row[mb] = (wm * 64 + mb * 32 + (lane & 31)) * kBK;
+  for (int mb = 0; mb < kMB; ++mb) a_row[mb] = (wm * kWaveM + mb * 32 + (lane & 31)) * kBK;
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) {
     const int r = kSwiGlu ? (nb >> 1) * (kBNB / 2) + wn * 64 + (nb & 1) * 32 + (lane & 31)
@@ -246,26 +267,26 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(GemmArgs p) {
   }
   const int sw = swizzle(lane & 31);
 
-  f32x16 acc[2][kNB];
+  f32x16 acc[kMB][kNB];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
 
-  Frag fa[2][2], fb[2][kNB];
+  Frag fa[2][kMB], fb[2][kNB];
   auto read_frags = [&](const T* la, const T* lb, int s, int slot) {
     const int c = ((2 * s + (lane >> 5)) ^ sw) * 8;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) fa[slot][mb] = *reinterpret_cast<const Frag*>(la + a_row[mb] + c);
+    for (int mb = 0; mb < kMB; ++mb) fa[slot][mb] = *reinterpret_cast<const Frag*>(la + a_row[mb] + c);
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) fb[slot][nb] = *reinterpret_cast<const Frag*>(lb + b_row[nb] + c);
   };
 
-  const int nk = (K + kBK - 1) / kBK;
-  constexpr int kMfma = 2 * kNB;  // MFMAs per k16 sub-step
-  constexpr int kReads = 2 + kNB;  // fragment reads per sub-step
+  const int nk = (k_end - k_begin + kBK - 1) / kBK;
+  constexpr int kMfma = kMB * kNB;  // MFMAs per k16 sub-step
+  constexpr int kReads = kMB + kNB;  // fragment reads per sub-step
 
   // One K-stage: compute from stage S while stage S-1 (read in the previous
   // step) is refilled for k-step kt + kStages - 1. Stages kt+1 .. kt+kStages-1
@@ -285,7 +306,7 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(GemmArgs p) {
     issue_loads(kt + kStages - 1, stage_buf<T, kBM * kBK, 0, F>(), stage_buf<T, kBNB * kBK, 1, F>());
     read_frags(ca, cb, 1, 1);
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb)
         acc[mb][nb] = Mfma<T>::run(fa[0][mb], fb[0][nb], acc[mb][nb]);
@@ -343,13 +364,13 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(GemmArgs p) {
   const int row_lane = (lane >> 5) * 4;
   if (kSwiGlu) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         const int col = n_t * (kBNB / 2) + wn * 64 + nb * 32 + col_lane;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int lrow = wm * 64 + mb * 32 + (v >> 2) * 8 + row_lane + (v & 3);
+          const int lrow = wm * kWaveM + mb * 32 + (v >> 2) * 8 + row_lane + (v & 3);
           if (lrow < mrows && col < N)
             C[(int64_t)(row0 + lrow) * N + col] =
                 from_f32<T>(silu(acc[mb][nb][v]) * acc[mb][nb + 2][v]);
@@ -357,15 +378,20 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(GemmArgs p) {
       }
   } else {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb) {
         const int col = n_t * kBNB + wn * (kBNB / 2) + nb * 32 + col_lane;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int lrow = wm * 64 + mb * 32 + (v >> 2) * 8 + row_lane + (v & 3);
-          if (lrow < mrows && col < N)
-            C[(int64_t)(row0 + lrow) * N + col] = from_f32<T>(acc[mb][nb][v]);
+          const int lrow = wm * kWaveM + mb * 32 + (v >> 2) * 8 + row_lane + (v & 3);
+          if (lrow < mrows && col < N) {
+            const int64_t at = (int64_t)(row0 + lrow) * N + col;
+            if (p.partial)
+              p.partial[(int64_t)ks * p.rows * N + at] = acc[mb][nb][v];
+            else
+              C[at] = from_f32<T>(acc[mb][nb][v]);
+          }
         }
       }
   }
@@ -379,8 +405,8 @@ __global__ __launch_bounds__(256) void simt_gemm_kernel(GemmArgs p) {
   __shared__ float sa[BK][kBMSimt + 4];
   __shared__ float sb[BK][BNB + 4];
 
-  int m_t, n_t;
-  if (!tile_of_block(p, m_t, n_t)) return;
+  int m_t, n_t, ks;
+  if (!tile_of_block(p, m_t, n_t, ks)) return;
   const int e = p.tiles[2 * m_t];
   const int row0 = p.tiles[2 * m_t + 1];
   const int mrows = min(kBMSimt, min(p.offsets[e + 1], p.rows) - row0);
@@ -462,30 +488,92 @@ __global__ __launch_bounds__(256) void simt_gemm_kernel(GemmArgs p) {
 
 }  // namespace
 
-ExpertsPlan experts_plan(int64_t rows, int64_t E, int dt) {
-  ExpertsPlan p;
-  p.bm = dt == kF32 ? kBMSimt : kBM;
-  p.max_tiles = (int)((rows + p.bm - 1) / p.bm + (E < rows ? E : rows));
-  return p;
-}
+constexpr int kCUs = 256;
+// Pipeline depth (LDS stages of 32 KB for 256-row B tiles); a build-time knob.
+#ifndef MOE_GEMM_STAGES
+#define MOE_GEMM_STAGES 4
+#endif
+constexpr int kStagesGemm = MOE_GEMM_STAGES;
+constexpr int kWaveMGemm = 64;
 
 static size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
-size_t tile_scratch_bytes(int64_t rows, int64_t E, int dt) {
-  const ExpertsPlan p = experts_plan(rows, E, dt);
+// Split-K of the down GEMM: when its output tiles would give the 256 CUs
+// fewer than four workgroups each, K is split so the last round of
+// workgroups is not left mostly empty; each split keeps >= 64 K-steps.
+ExpertsPlan experts_plan(int64_t rows, int64_t E, int64_t H, int64_t I, int dt) {
+  ExpertsPlan p;
+  p.bm = dt == kF32 ? kBMSimt : kBM;
+  p.max_tiles = (int)((rows + p.bm - 1) / p.bm + (E < rows ? E : rows));
+  p.splits = 1;
+  p.k_chunk = (int)I;
+  if (dt != kF32) {
+    const int64_t tiles = (int64_t)p.max_tiles * ((H + 255) / 256);
+    const int64_t ksteps = (I + kBK - 1) / kBK;
+    if (tiles < 4 * kCUs) {
+      int64_t sp = (4 * kCUs + tiles - 1) / tiles;
+      sp = std::min<int64_t>(sp, std::max<int64_t>(1, ksteps / 64));
+      p.splits = (int)std::min<int64_t>(sp, 8);
+    }
+    p.k_chunk = (int)((ksteps + p.splits - 1) / p.splits * kBK);
+  }
+  return p;
+}
+
+static size_t tile_list_bytes(const ExpertsPlan& p) {
   return align256((size_t)p.max_tiles * 2 * sizeof(int32_t)) + 256;
 }
 
-size_t experts_scratch_bytes(int64_t rows, int64_t E, int64_t I, int dt) {
-  return tile_scratch_bytes(rows, E, dt) + align256((size_t)rows * (size_t)I * dtype_size(dt));
+size_t gemm_scratch_bytes(int64_t rows, int64_t E, int64_t H, int64_t I, int dt) {
+  const ExpertsPlan p = experts_plan(rows, E, H, I, dt);
+  size_t b = tile_list_bytes(p);
+  if (p.splits > 1) b += align256((size_t)p.splits * (size_t)rows * (size_t)H * sizeof(float));
+  return b;
+}
+
+size_t experts_scratch_bytes(int64_t rows, int64_t E, int64_t H, int64_t I, int dt) {
+  return gemm_scratch_bytes(rows, E, H, I, dt) + align256((size_t)rows * (size_t)I * dtype_size(dt));
 }
 
 namespace {
 
-// Carves the tile list out of `scratch` and enqueues the plan kernel.
-GemmArgs plan_tiles(const int32_t* offsets, int rows, int E, int dt, void* scratch,
-                    hipStream_t s) {
-  const ExpertsPlan plan = experts_plan(rows, E, dt);
+// out[r] = sum over splits (in split order) of partial[s][r], for rows below
+// the device row count; N is a multiple of 8.
+template <typename T>
+__global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restrict__ partial,
+                                                             int splits, int rows, int N,
+                                                             const int32_t* __restrict__ offsets_end,
+                                                             T* __restrict__ out) {
+  const int vec = N / 8;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = i / vec;
+  const int v = (int)(i % vec);
+  if (row >= min(*offsets_end, rows)) return;
+  const int64_t at = row * N + v * 8;
+  const int64_t stride = (int64_t)rows * N;
+  float acc[8];
+  {
+    const float4 a0 = *reinterpret_cast<const float4*>(partial + at);
+    const float4 a1 = *reinterpret_cast<const float4*>(partial + at + 4);
+    acc[0] = a0.x; acc[1] = a0.y; acc[2] = a0.z; acc[3] = a0.w;
+    acc[4] = a1.x; acc[5] = a1.y; acc[6] = a1.z; acc[7] = a1.w;
+  }
+  for (int s = 1; s < splits; ++s) {
+    const float4 a0 = *reinterpret_cast<const float4*>(partial + s * stride + at);
+    const float4 a1 = *reinterpret_cast<const float4*>(partial + s * stride + at + 4);
+    acc[0] += a0.x; acc[1] += a0.y; acc[2] += a0.z; acc[3] += a0.w;
+    acc[4] += a1.x; acc[5] += a1.y; acc[6] += a1.z; acc[7] += a1.w;
+  }
+  Vec8<T> o;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o.set(j, acc[j]);
+  o.store(out + at);
+}
+
+// Carves the tile list (and split-K partials) out of `scratch` and enqueues
+// the plan kernel.
+GemmArgs plan_tiles(const ExpertsPlan& plan, const int32_t* offsets, int rows, int E,
+                    void* scratch, hipStream_t s) {
   char* ws = static_cast<char*>(scratch);
   GemmArgs g = {};
   int32_t* tiles = reinterpret_cast<int32_t*>(ws);
@@ -497,32 +585,28 @@ GemmArgs plan_tiles(const int32_t* offsets, int rows, int E, int dt, void* scrat
   g.tile_count = tile_count;
   g.rows = rows;
   g.max_tiles = plan.max_tiles;
+  g.k_splits = 1;
+  g.partial = nullptr;
   return g;
 }
 
-constexpr int kCUs = 256;
-constexpr int kStagesGemm = 4;
-
-// B-tile rows of the down GEMM: 256, or 128 when 256-wide tiles would leave
-// the 256 CUs with fewer than four workgroups each.
-int down_bnb(int max_tiles, int N) {
-  return (int64_t)max_tiles * ((N + 255) / 256) < 4 * kCUs ? 128 : 256;
+float* partial_buffer(const ExpertsPlan& plan, void* scratch) {
+  return plan.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(scratch) + tile_list_bytes(plan))
+                         : nullptr;
 }
 
 template <typename T>
 void launch_mfma(GemmArgs g, bool swiglu, hipStream_t s) {
   if (swiglu) {
     g.n_tiles_n = (g.N + 127) / 128;
-    hipLaunchKernelGGL((mfma_gemm_kernel<T, true, 256, kStagesGemm>), dim3(grid_tiles(g.max_tiles, g.n_tiles_n)),
-                       dim3(kThreads), 0, s, g);
-  } else if (down_bnb(g.max_tiles, g.N) == 128) {
-    g.n_tiles_n = (g.N + 127) / 128;
-    hipLaunchKernelGGL((mfma_gemm_kernel<T, false, 128, kStagesGemm>), dim3(grid_tiles(g.max_tiles, g.n_tiles_n)),
-                       dim3(kThreads), 0, s, g);
+    hipLaunchKernelGGL((mfma_gemm_kernel<T, true, 256, kStagesGemm, kWaveMGemm>),
+                       dim3(grid_tiles(g.max_tiles, g.n_tiles_n)),
+                       dim3(gemm_threads<kWaveMGemm>()), 0, s, g);
   } else {
     g.n_tiles_n = (g.N + 255) / 256;
-    hipLaunchKernelGGL((mfma_gemm_kernel<T, false, 256, kStagesGemm>), dim3(grid_tiles(g.max_tiles, g.n_tiles_n)),
-                       dim3(kThreads), 0, s, g);
+    hipLaunchKernelGGL((mfma_gemm_kernel<T, false, 256, kStagesGemm, kWaveMGemm>),
+                       dim3(grid_tiles(g.max_tiles, g.n_tiles_n, g.k_splits)),
+                       dim3(gemm_threads<kWaveMGemm>()), 0, s, g);
   }
 }
 
@@ -545,12 +629,30 @@ void setup_gate_up(GemmArgs& g, const void* a, const int32_t* a_map, int a_div, 
   g.a_rows = a_map ? (g.rows + g.a_div - 1) / g.a_div : g.rows;
   g.b0 = w_gate; g.b1 = w_up; g.c = h;
   g.N = I; g.K = H;
+  g.k_splits = 1; g.k_chunk = H; g.partial = nullptr;
 }
 
-void setup_down(GemmArgs& g, const void* h, int H, int I, const void* w_down, void* expert_out) {
+void setup_down(GemmArgs& g, const ExpertsPlan& plan, void* scratch, const void* h, int H, int I,
+                const void* w_down, void* expert_out) {
   g.a = h; g.a_map = nullptr; g.a_div = 1; g.a_rows = g.rows;
   g.b0 = w_down; g.b1 = nullptr; g.c = expert_out;
   g.N = H; g.K = I;
+  g.k_splits = plan.splits; g.k_chunk = plan.k_chunk;
+  g.partial = partial_buffer(plan, scratch);
+}
+
+hipError_t reduce_splits(const ExpertsPlan& plan, void* scratch, const int32_t* offsets, int rows,
+                         int E, int H, int dt, void* expert_out, hipStream_t s) {
+  const int64_t n = (int64_t)rows * (H / 8);
+  const float* part = partial_buffer(plan, scratch);
+  const int blocks = (int)((n + 255) / 256);
+  if (dt == kF16)
+    hipLaunchKernelGGL(reduce_splits_kernel<f16>, dim3(blocks), dim3(256), 0, s, part, plan.splits,
+                       rows, H, offsets + E, static_cast<f16*>(expert_out));
+  else
+    hipLaunchKernelGGL(reduce_splits_kernel<bf16>, dim3(blocks), dim3(256), 0, s, part,
+                       plan.splits, rows, H, offsets + E, static_cast<bf16*>(expert_out));
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -559,7 +661,8 @@ hipError_t launch_gate_up(const void* a, const int32_t* a_map, int a_div, const 
                           int rows, int E, int H, int I, const void* w_gate, const void* w_up,
                           int dt, void* h, void* scratch, hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  GemmArgs g = plan_tiles(offsets, rows, E, dt, scratch, s);
+  const ExpertsPlan plan = experts_plan(rows, E, H, I, dt);
+  GemmArgs g = plan_tiles(plan, offsets, rows, E, scratch, s);
   setup_gate_up(g, a, a_map, a_div, H, I, w_gate, w_up, h);
   launch_gemm<true>(g, dt, s);
   return hipGetLastError();
@@ -567,27 +670,34 @@ hipError_t launch_gate_up(const void* a, const int32_t* a_map, int a_div, const 
 
 hipError_t launch_down(const void* h, const int32_t* offsets, int rows, int E, int H, int I,
                        const void* w_down, int dt, void* expert_out, void* scratch,
-                       hipStream_t s) {
+                       hipStream_t s, DownPartials* keep) {
   if (rows == 0) return hipSuccess;
-  GemmArgs g = plan_tiles(offsets, rows, E, dt, scratch, s);
-  setup_down(g, h, H, I, w_down, expert_out);
+  const ExpertsPlan plan = experts_plan(rows, E, H, I, dt);
+  GemmArgs g = plan_tiles(plan, offsets, rows, E, scratch, s);
+  setup_down(g, plan, scratch, h, H, I, w_down, expert_out);
   launch_gemm<false>(g, dt, s);
+  if (plan.splits > 1) {
+    if (keep) {
+      keep->partial = g.partial;
+      keep->splits = plan.splits;
+      keep->split_stride = (int64_t)rows * H;
+      return hipGetLastError();
+    }
+    return reduce_splits(plan, scratch, offsets, rows, E, H, dt, expert_out, s);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_experts(const void* a, const int32_t* a_map, int a_div,
                           const int32_t* offsets, int rows, int E, int H, int I,
                           const void* w_gate, const void* w_up, const void* w_down, int dt,
-                          void* expert_out, void* scratch, hipStream_t s) {
+                          void* expert_out, void* scratch, hipStream_t s, DownPartials* keep) {
   if (rows == 0) return hipSuccess;
-  void* h = static_cast<char*>(scratch) + tile_scratch_bytes(rows, E, dt);
-  GemmArgs g1 = plan_tiles(offsets, rows, E, dt, scratch, s);
-  GemmArgs g2 = g1;
-  setup_gate_up(g1, a, a_map, a_div, H, I, w_gate, w_up, h);
-  setup_down(g2, h, H, I, w_down, expert_out);
-  launch_gemm<true>(g1, dt, s);
-  launch_gemm<false>(g2, dt, s);
-  return hipGetLastError();
+  void* h = static_cast<char*>(scratch) + gemm_scratch_bytes(rows, E, H, I, dt);
+  hipError_t e = launch_gate_up(a, a_map, a_div, offsets, rows, E, H, I, w_gate, w_up, dt, h,
+                                scratch, s);
+  if (e != hipSuccess) return e;
+  return launch_down(h, offsets, rows, E, H, I, w_down, dt, expert_out, scratch, s, keep);
 }
 
 }  // namespace moe

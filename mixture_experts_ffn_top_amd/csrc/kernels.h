@@ -36,31 +36,52 @@ hipError_t launch_gather_rows(const void* x, int dt, int H, int k, const int32_t
 
 // ---- experts (grouped GEMMs) ---------------------------------------------------
 // The M-tile list: for each tile, (expert, first row). Built on the device
-// from the expert offsets; its length is stored at tile_count.
+// from the expert offsets; its length is stored at tile_count. The down GEMM
+// may split K (fp32 partial sums, reduced in split order).
 struct ExpertsPlan {
   int bm;         // rows per M-tile
   int max_tiles;  // host upper bound of the tile count
+  int splits;     // K splits of the down GEMM
+  int k_chunk;    // K elements per split
 };
-ExpertsPlan experts_plan(int64_t rows, int64_t E, int dt);
-size_t experts_scratch_bytes(int64_t rows, int64_t E, int64_t I, int dt);
-// Scratch of one GEMM call on its own (the tile list only).
-size_t tile_scratch_bytes(int64_t rows, int64_t E, int dt);
+ExpertsPlan experts_plan(int64_t rows, int64_t E, int64_t H, int64_t I, int dt);
+// Scratch of one GEMM call (tile list + split-K partials).
+size_t gemm_scratch_bytes(int64_t rows, int64_t E, int64_t H, int64_t I, int dt);
+// Scratch of both GEMMs (the above + h).
+size_t experts_scratch_bytes(int64_t rows, int64_t E, int64_t H, int64_t I, int dt);
+
+// Split-K partial sums left for the caller (moe_forward reduces them inside
+// the combine): partial[s * split_stride + r * H + c].
+struct DownPartials {
+  const float* partial = nullptr;
+  int splits = 1;
+  int64_t split_stride = 0;
+};
+
+// a_map: optional; when given, A row r is row a_map[r] / a_div of `a`
+// (gathering tokens straight from x instead of a materialised x_disp).
 hipError_t launch_gate_up(const void* a, const int32_t* a_map, int a_div, const int32_t* offsets,
                           int rows, int E, int H, int I, const void* w_gate, const void* w_up,
                           int dt, void* h, void* scratch, hipStream_t s);
+// With keep != NULL and a split K, the partial sums stay in scratch and are
+// described in *keep instead of being reduced into expert_out.
 hipError_t launch_down(const void* h, const int32_t* offsets, int rows, int E, int H, int I,
                        const void* w_down, int dt, void* expert_out, void* scratch,
-                       hipStream_t s);
-// a_map: optional; when given, A row r is row a_map[r] / a_div of `a`
-// (gathering tokens straight from x instead of a materialised x_disp).
+                       hipStream_t s, DownPartials* keep = nullptr);
 hipError_t launch_experts(const void* a, const int32_t* a_map, int a_div,
                           const int32_t* offsets, int rows, int E, int H, int I,
                           const void* w_gate, const void* w_up, const void* w_down, int dt,
-                          void* expert_out, void* scratch, hipStream_t s);
+                          void* expert_out, void* scratch, hipStream_t s,
+                          DownPartials* keep = nullptr);
 
 // ---- combine ------------------------------------------------------------------
 hipError_t launch_combine(const void* expert_out, const int32_t* row_of_slot, const void* weights,
                           int w_dt, int T, int k, int H, int dt, void* out, hipStream_t s);
+// Combine from split-K partial sums: each expert row is first summed over
+// the splits and rounded to the model dtype, exactly as expert_out would be.
+hipError_t launch_combine_partials(const DownPartials& part, const int32_t* row_of_slot,
+                                   const void* weights, int w_dt, int T, int k, int H, int dt,
+                                   void* out, hipStream_t s);
 hipError_t launch_combine_add_rmsnorm(const void* expert_out, const int32_t* row_of_slot,
                                       const void* weights, int w_dt, const void* shared,
                                       const void* residual, const float* gamma, float eps, int T,

@@ -43,9 +43,9 @@ _SIGS = {
     "moe_experts_workspace_size": ([I64, I64, I64, I64, I32], SZ),
     "moe_experts_gate_up": ([P, P, I64, P, I64, I64, I64, I64, P, P, I32, P, P, SZ, P], I32),
     "moe_experts_down": ([P, P, I64, I64, I64, I64, P, I32, P, P, SZ, P], I32),
-    "moe_experts_gemm_workspace_size": ([I64, I64, I32], SZ),
+    "moe_experts_gemm_workspace_size": ([I64, I64, I64, I64, I32], SZ),
     "moe_combine": ([P, P, P, I32, I64, I64, I64, I32, P, P], I32),
-    "moe_forward": ([P, P, I32, I64, I64, I64, I64, I64, I32, P, P, P, I32, P, P, P, P, SZ, P], I32),
+    "moe_forward": ([P, P, I32, I64, I64, I64, I64, I64, I32, P, P, P, I32, P, P, P, P, SZ, P, P], I32),
     "moe_forward_workspace_size": ([I64, I64, I64, I64, I64, I32, I32], SZ),
     "moe_combine_add_rmsnorm": ([P, P, P, I32, P, P, P, ctypes.c_float, I64, I64, I64, I32, P, P,
                                  P, P], I32),
@@ -145,8 +145,8 @@ def moe_experts_forward_dispatched(x_disp, expert_offsets, w_gate, w_up, w_down,
     return expert_out
 
 
-def moe_experts_gemm_workspace_size(rows: int, E: int, dt: torch.dtype) -> int:
-    return lib().moe_experts_gemm_workspace_size(rows, E, dtype_code(dt))
+def moe_experts_gemm_workspace_size(rows: int, E: int, H: int, I: int, dt: torch.dtype) -> int:
+    return lib().moe_experts_gemm_workspace_size(rows, E, H, I, dtype_code(dt))
 
 
 def moe_experts_gate_up(x, expert_offsets, w_gate, w_up, row_map=None, map_div: int = 1, rows=None,
@@ -160,7 +160,7 @@ def moe_experts_gate_up(x, expert_offsets, w_gate, w_up, row_map=None, map_div: 
     if h is None:
         h = torch.empty((rows, I), dtype=x.dtype, device=x.device)
     if ws is None:
-        ws = _workspace(moe_experts_gemm_workspace_size(rows, E, x.dtype), x.device)
+        ws = _workspace(moe_experts_gemm_workspace_size(rows, E, H, I, x.dtype), x.device)
     _check(lib().moe_experts_gate_up(_ptr(x), _ptr(row_map), map_div, _ptr(expert_offsets), rows, E, H,
                                      I, _ptr(w_gate), _ptr(w_up), dtype_code(x.dtype), _ptr(h),
                                      _ptr(ws), ws.numel(), _stream()), "moe_experts_gate_up")
@@ -173,7 +173,7 @@ def moe_experts_down(h, expert_offsets, w_down, expert_out=None, ws=None):
     if expert_out is None:
         expert_out = torch.empty((rows, H), dtype=h.dtype, device=h.device)
     if ws is None:
-        ws = _workspace(moe_experts_gemm_workspace_size(rows, E, h.dtype), h.device)
+        ws = _workspace(moe_experts_gemm_workspace_size(rows, E, H, I, h.dtype), h.device)
     _check(lib().moe_experts_down(_ptr(h), _ptr(expert_offsets), rows, E, H, I, _ptr(w_down),
                                   dtype_code(h.dtype), _ptr(expert_out), _ptr(ws), ws.numel(),
                                   _stream()), "moe_experts_down")
@@ -196,7 +196,9 @@ def moe_forward_workspace_size(T, H, I, E, top_k, dt, logits_dt) -> int:
 
 
 def moe_forward(x, logits, top_k: int, renormalize: bool, w_gate, w_up, w_down, out=None,
-                indices_out=None, weights_out=None, ws=None):
+                indices_out=None, weights_out=None, ws=None, stage_events=None):
+    """stage_events: optional list of 6 torch.cuda.Event (recorded at the stage
+    boundaries on the current stream, for per-stage timing)."""
     T, H = x.shape
     E = logits.shape[1]
     I = w_gate.shape[1]
@@ -204,11 +206,23 @@ def moe_forward(x, logits, top_k: int, renormalize: bool, w_gate, w_up, w_down, 
         out = torch.empty((T, H), dtype=x.dtype, device=x.device)
     if ws is None:
         ws = _workspace(moe_forward_workspace_size(T, H, I, E, top_k, x.dtype, logits.dtype), x.device)
+    ev = None
+    if stage_events is not None:
+        if len(stage_events) != 6:
+            raise ValueError("stage_events needs 6 events")
+        ev = (ctypes.c_void_p * 6)(*[_event_handle(e) for e in stage_events])
     _check(lib().moe_forward(_ptr(x), _ptr(logits), dtype_code(logits.dtype), T, H, I, E, top_k,
                              int(renormalize), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
                              dtype_code(x.dtype), _ptr(out), _ptr(indices_out), _ptr(weights_out),
-                             _ptr(ws), ws.numel(), _stream()), "moe_forward")
+                             _ptr(ws), ws.numel(), ev, _stream()), "moe_forward")
     return out
+
+
+def _event_handle(e) -> int:
+    """hipEvent_t of a torch.cuda.Event (torch creates it lazily on first record)."""
+    if not e.cuda_event:
+        e.record()
+    return e.cuda_event
 
 
 def moe_combine_add_rmsnorm(expert_out, row_of_slot, weights, residual, gamma, eps: float,

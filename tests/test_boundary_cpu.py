@@ -135,7 +135,7 @@ def test_forward_validation_and_workspace_query():
     assert q(4, 128, 256, 8, 9, 2, 0) == 0
     f = lib.moe_forward
     base = [FAKE, FAKE + 2**20, 0, 64, 128, 256, 8, 2, 1, FAKE + 2**21, FAKE + 2**22, FAKE + 2**23,
-            0, FAKE + 2**24, None, None, FAKE + 2**26, q(64, 128, 256, 8, 2, 0, 0), None]
+            0, FAKE + 2**24, None, None, FAKE + 2**26, q(64, 128, 256, 8, 2, 0, 0), None, None]
 
     def call(i=None, v=None):
         a = list(base)

@@ -207,6 +207,49 @@ def test_experts_all_rows_one_expert():
     assert_close(host(got), ref, "bf16", "expert_out one expert")
 
 
+def test_experts_split_k_and_halves():
+    """Long K with few output tiles: the down GEMM splits K (fp32 partials,
+    reduced in order). Checked through forward_dispatched, through the two
+    halves (gate/up reading tokens via the dispatch map) and through
+    moe_forward (partials reduced inside the combine)."""
+    g = np.random.default_rng(21)
+    T, k, E, H, I_ = 300, 2, 3, 512, 4096
+    x = I.store(g.standard_normal((T, H)).astype(np.float32), "bf16")
+    z = I.gapped_logits(21, T, E, k)
+    wg, wu, wd = _random_experts(g, E, H, I_, "bf16")
+    wo = lambda e: (wg[e], wu[e], wd[e])  # noqa: E731
+    idx, w_r, d, y_ref, out_ref = O.forward(x, z, "f32", k, True, wo, E, "bf16")
+    n = int(d["offsets"][-1])
+    dg = [dev(a, "bf16") for a in (wg, wu, wd)]
+    got = moe.moe_experts_forward_dispatched(dev(d["x_disp"], "bf16"), dev(d["offsets"]), *dg)
+    torch.cuda.synchronize()
+    assert_close(host(got)[:n], y_ref, "bf16", "expert_out split-K")
+    xd, off, sor = dev(x, "bf16"), dev(d["offsets"]), dev(d["slot_of_row"])
+    h = moe.moe_experts_gate_up(xd, off, dg[0], dg[1], row_map=sor, map_div=k, rows=T * k)
+    y2 = moe.moe_experts_down(h, off, dg[2])
+    torch.cuda.synchronize()
+    assert_close(host(y2)[:n], y_ref, "bf16", "expert_out via halves")
+    out = moe.moe_forward(xd, dev(z, "f32"), k, True, *dg)
+    torch.cuda.synchronize()
+    assert_close(host(out), out_ref, "bf16", "forward split-K")
+
+
+def test_forward_stage_events():
+    g = np.random.default_rng(22)
+    T, k, E, H, I_ = 64, 2, 4, 128, 256
+    x = I.store(g.standard_normal((T, H)).astype(np.float32), "bf16")
+    z = I.gapped_logits(22, T, E, k)
+    wg, wu, wd = _random_experts(g, E, H, I_, "bf16")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    out = moe.moe_forward(dev(x, "bf16"), dev(z, "f32"), k, True, dev(wg, "bf16"), dev(wu, "bf16"),
+                          dev(wd, "bf16"), stage_events=ev)
+    torch.cuda.synchronize()
+    times = [ev[i].elapsed_time(ev[i + 1]) for i in range(5)]
+    assert all(t >= 0 for t in times)
+    _, _, _, _, ref = O.forward(x, z, "f32", k, True, lambda e: (wg[e], wu[e], wd[e]), E, "bf16")
+    assert_close(host(out), ref, "bf16", "forward with events")
+
+
 # ------------------------------------------------------------------ combine --
 @pytest.mark.parametrize("T,k,H,dtype,wdt", [(50, 3, 136, "bf16", "f32"), (7, 8, 4096, "bf16", "f32"),
                                              (33, 2, 64, "f32", "f32"), (20, 4, 256, "f16", "f16"),
