@@ -28,6 +28,14 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE fwd tokens/s; expert GEMM TFLOP/s (% MFMA peak); combine GB/s (% HBM)"
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
+# Which roof bounds the gate/up GEMM of each workload (flops per weight byte:
+# ~2*rows-per-expert; the MI355X ridge is ~310 bf16 FLOP per HBM byte).
+# Tokens of each workload the CPU oracle runs on (its cost is dominated by
+# decoding the touched experts' weights to fp64 and the fp64 GEMMs).
+CPU_TOKENS = {"tiny_fp32": 64, "mixtral_8x_bf16": 4096, "many_expert_zipf_bf16": 1024,
+              "dsv3_share_rmsnorm_bf16": 8, "decode_nan_rows_bf16": 16}
+BOUND = {"tiny_fp32": "alu", "mixtral_8x_bf16": "mfma", "many_expert_zipf_bf16": "mfma",
+         "dsv3_share_rmsnorm_bf16": "hbm", "decode_nan_rows_bf16": "hbm"}
 
 
 def measured_traffic(workload: str, kernel: str):
@@ -56,8 +64,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral_8x_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=2048,
-                    help="tokens of the workload the CPU oracle runs on")
+    ap.add_argument("--cpu-tokens", type=int, default=0,
+                    help="tokens of the workload the CPU oracle runs on (default: a per-workload "
+                         "sample of roughly 5-30 s)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 5 times (the "
                          "reference kernel for scaling HBM byte counters), then exit")
@@ -86,6 +95,8 @@ def main():
     T, H, I_, E, k = w.T, w.H, w.I, w.E, w.top_k
     R = T * k
     td = {"bf16": torch.bfloat16, "f32": torch.float32}[w.dtype]
+    if args.workload not in BOUND:
+        raise SystemExit(f"unknown workload {args.workload}")
     dev = "cuda"
     torch.cuda.set_device(0)
     moe.lib()
@@ -99,7 +110,7 @@ def main():
     t0 = time.time()
     z = I.logits_for(w)
     x = I.tokens_for(w)
-    n_cpu = min(args.cpu_tokens, T)
+    n_cpu = min(args.cpu_tokens or CPU_TOKENS[args.workload], T)
     keep = set()
     if not args.no_cpu_baseline:
         from oracle import moe_oracle as O
@@ -131,10 +142,44 @@ def main():
                      dtype=torch.uint8, device=dev)
 
     stages = ["route", "dispatch", "gate_up", "down", "combine"]
+    if w.epilogue:
+        # combine fused with the shared-expert term, residual Add and RMSNorm:
+        # the split calls, with events recorded between them on this stream
+        sh, res, gam = I.epilogue_inputs(w)
+        shd, resd, gamd = to_dev(sh), to_dev(res), to_dev(gam, "f32")
+        offsets_d = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        sor = torch.empty(R, dtype=torch.int32, device=dev)
+        ros = torch.empty(R, dtype=torch.int32, device=dev)
+        h = torch.empty((R, I_), dtype=td, device=dev)
+        y = torch.empty((R, H), dtype=td, device=dev)
+        yo = torch.empty((T, H), dtype=td, device=dev)
+        rstd = torch.empty(T, dtype=torch.float32, device=dev)
+        ws_d = torch.empty(moe.moe_dispatch_workspace_size(T, k, E), dtype=torch.uint8, device=dev)
+        ws_g = torch.empty(moe.moe_experts_gemm_workspace_size(R, E, H, I_, td), dtype=torch.uint8,
+                           device=dev)
+        stages[-1] = "combine_add_rmsnorm"
 
-    def step(ev=None):
-        moe.moe_forward(xd, zd, k, w.renormalize, wt["w_gate"], wt["w_up"], wt["w_down"], out=out,
-                        indices_out=idx, weights_out=wts, ws=ws, stage_events=ev)
+        def step(ev=None):
+            def mark(i):
+                if ev is not None:
+                    ev[i].record()
+            mark(0)
+            moe.moe_route(zd, k, w.renormalize, indices=idx, weights=wts)
+            mark(1)
+            moe.moe_dispatch(idx, E, ws=ws_d, offsets=offsets_d, slot_of_row=sor, row_of_slot=ros)
+            mark(2)
+            moe.moe_experts_gate_up(xd, offsets_d, wt["w_gate"], wt["w_up"], row_map=sor, map_div=k,
+                                    rows=R, h=h, ws=ws_g)
+            mark(3)
+            moe.moe_experts_down(h, offsets_d, wt["w_down"], expert_out=y, ws=ws_g)
+            mark(4)
+            moe.moe_combine_add_rmsnorm(y, ros, wts, resd, gamd, w.eps, shared=shd, y=yo, x_out=out,
+                                        rstd=rstd)
+            mark(5)
+    else:
+        def step(ev=None):
+            moe.moe_forward(xd, zd, k, w.renormalize, wt["w_gate"], wt["w_up"], wt["w_down"],
+                            out=out, indices_out=idx, weights_out=wts, ws=ws, stage_events=ev)
 
     for _ in range(args.warmup):
         step()
@@ -162,27 +207,41 @@ def main():
     tokens_per_s = T * args.steps / elapsed
 
     # ---- roofline of the dominant kernel (gate/up grouped GEMM) -----------
-    flops_gate_up = 4.0 * R * H * I_  # two [R,H]x[H,I] products per launch
-    flops_down = 2.0 * R * H * I_
-    gu_s = stage_ms["gate_up"] / 1e3
-    achieved = flops_gate_up / gu_s / 1e12
-    peak = PEAK_TFLOPS[w.dtype]
+    es = 2 if w.dtype == "bf16" else 4
     counts = np.diff(offsets.cpu().numpy())
     touched = int((counts > 0).sum())
-    es = 2 if w.dtype == "bf16" else 4
-    combine_bytes = R * H * es + R * 4 + R * 4 + T * H * es
-    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+    flops_gate_up = 4.0 * R * H * I_  # two [R,H]x[H,I] products per launch
+    flops_down = 2.0 * R * H * I_
+    # bytes a launch must move at least: touched experts' weights, its input
+    # rows and its output rows
+    bytes_gate_up = touched * 2 * I_ * H * es + T * H * es + R * I_ * es
+    bytes_down = touched * H * I_ * es + R * I_ * es + R * H * es
+    gu_s = stage_ms["gate_up"] / 1e3
+    bound = BOUND[args.workload]
+    if bound == "hbm":
+        achieved, peak, unit = bytes_gate_up / gu_s / 1e9, PEAK_HBM_GBS, "GB/s"
+    else:
+        achieved, peak, unit = flops_gate_up / gu_s / 1e12, PEAK_TFLOPS[w.dtype], "TFLOP/s"
+    kname = {"bf16": "mfma_gemm_kernel<bf16,gate_up>", "f32": "simt_gemm_kernel<gate_up>"}[w.dtype]
+    roofline = {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4),
-                "traffic": measured_traffic(args.workload, "mfma_gemm_kernel<bf16,gate_up>"),
-                "kernel": "mfma_gemm_kernel<bf16, gate/up+SiLU>" if w.dtype == "bf16" else "gate/up GEMM",
-                "flops_per_launch": flops_gate_up}
-    expert_tflops = (flops_gate_up + flops_down) / ((stage_ms["gate_up"] + stage_ms["down"]) / 1e3) / 1e12
+                "traffic": measured_traffic(args.workload, kname),
+                "kernel": kname,
+                "algorithmic_per_launch": flops_gate_up if bound != "hbm" else bytes_gate_up}
+    gemm_s = (stage_ms["gate_up"] + stage_ms["down"]) / 1e3
+    expert_tflops = (flops_gate_up + flops_down) / gemm_s / 1e12
+    if w.epilogue:  # expert rows, weights, maps, shared, residual, gamma in; y, x_out, rstd out
+        comb_bytes = R * H * es + R * 4 + R * 4 + 4 * T * H * es + 4 * H + 4 * T
+    else:
+        comb_bytes = R * H * es + R * 4 + R * 4 + T * H * es
+    comb_gbs = comb_bytes / (stage_ms[stages[-1]] / 1e3) / 1e9
     extra = {
         "stages_ms": {k_: round(v, 4) for k_, v in stage_ms.items()},
         "expert_gemm_tflops": round(expert_tflops, 1),
-        "expert_gemm_frac_peak": round(expert_tflops / peak, 4),
-        "combine_gbs": round(combine_bytes / (stage_ms["combine"] / 1e3) / 1e9, 1),
-        "combine_frac_hbm": round(combine_bytes / (stage_ms["combine"] / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+        "expert_gemm_frac_peak": round(expert_tflops / PEAK_TFLOPS[w.dtype], 4),
+        "expert_gemm_weight_gbs": round((bytes_gate_up + bytes_down) / gemm_s / 1e9, 1),
+        "combine_gbs": round(comb_gbs, 1),
+        "combine_frac_hbm": round(comb_gbs / PEAK_HBM_GBS, 4),
         "experts_touched": touched,
     }
 

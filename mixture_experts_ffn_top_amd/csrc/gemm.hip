@@ -222,7 +222,8 @@ __global__ __launch_bounds__(gemm_threads<kWaveM>()) void mfma_gemm_kernel(GemmA
     const int c = (lane & 3) ^ swizzle(r);
     const int grow = row0 + min(r, mrows - 1);
     const int src = p.a_map ? min(max(p.a_map[grow] / p.a_div, 0), p.a_rows - 1) : grow;
-    vo_a[j] = (uint32_t)src * row_bytes + (uint32_t)c * 16u;
+    // rows past the expert's last row are not fetched (they read as zero)
+    vo_a[j] = r < mrows ? (uint32_t)src * row_bytes + (uint32_t)c * 16u : kOutOfRange;
     kc_a[j] = c * 8;
   }
 #pragma unroll
@@ -297,13 +298,21 @@ __global__ __launch_bounds__(gemm_threads<kWaveM>()) void mfma_gemm_kernel(GemmA
   // Order: [loads, sub-step 0 MFMAs interleaved with sub-step 1 fragment
   // reads, half of sub-step 1] barrier [next stage's sub-step 0 fragment
   // reads overlapping the other half of sub-step 1].
-  auto step = [&](auto stage, int kt) {
+  // A wavefront whose rows all lie past the expert's last row (short
+  // M-tiles) runs the same loads and barriers without reads or MFMAs.
+  auto step = [&](auto stage, auto compute, int kt) {
     constexpr int S = decltype(stage)::value;
+    constexpr bool kCompute = decltype(compute)::value;
     constexpr int F = (S + kStages - 1) % kStages;
     constexpr int X = (S + 1) % kStages;
     T* ca = stage_buf<T, kBM * kBK, 0, S>();
     T* cb = stage_buf<T, kBNB * kBK, 1, S>();
     issue_loads(kt + kStages - 1, stage_buf<T, kBM * kBK, 0, F>(), stage_buf<T, kBNB * kBK, 1, F>());
+    if constexpr (!kCompute) {
+      wait_vmem<(kStages - 2) * kLoads>();
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      return;
+    }
     read_frags(ca, cb, 1, 1);
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb)
@@ -342,20 +351,29 @@ __global__ __launch_bounds__(gemm_threads<kWaveM>()) void mfma_gemm_kernel(GemmA
     issue_loads(3, stage_buf<T, kBM * kBK, 0, 3 % kStages>(), stage_buf<T, kBNB * kBK, 1, 3 % kStages>());
   wait_vmem<(kStages - 2) * kLoads>();
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  read_frags(stage_buf<T, kBM * kBK, 0, 0>(), stage_buf<T, kBNB * kBK, 1, 0>(), 0, 0);
 
   // Main loop, unrolled by kStages so every LDS pointer is a fixed object.
   // The trip count is padded to a multiple of kStages: loads past K are
   // masked to zeros, so the padding steps add nothing to the accumulators,
   // and the body stays one straight-line block.
   const int nk_pad = (nk + kStages - 1) / kStages * kStages;
-  for (int kt = 0; kt < nk_pad; kt += kStages) {
-    step(std::integral_constant<int, 0>{}, kt);
-    step(std::integral_constant<int, 1>{}, kt + 1);
-    step(std::integral_constant<int, 2 % kStages>{}, kt + 2);
-    if constexpr (kStages > 3) step(std::integral_constant<int, 3 % kStages>{}, kt + 3);
-    if constexpr (kStages > 4) step(std::integral_constant<int, 4 % kStages>{}, kt + 4);
-  }
+  auto main_loop = [&](auto compute) {
+    if constexpr (decltype(compute)::value)
+      read_frags(stage_buf<T, kBM * kBK, 0, 0>(), stage_buf<T, kBNB * kBK, 1, 0>(), 0, 0);
+    for (int kt = 0; kt < nk_pad; kt += kStages) {
+      step(std::integral_constant<int, 0>{}, compute, kt);
+      step(std::integral_constant<int, 1>{}, compute, kt + 1);
+      step(std::integral_constant<int, 2 % kStages>{}, compute, kt + 2);
+      if constexpr (kStages > 3) step(std::integral_constant<int, 3 % kStages>{}, compute, kt + 3);
+      if constexpr (kStages > 4) step(std::integral_constant<int, 4 % kStages>{}, compute, kt + 4);
+    }
+  };
+  const bool has_rows = wm * kWaveM < mrows;
+  if (has_rows)
+    main_loop(std::true_type{});
+  else
+    main_loop(std::false_type{});
+  if (!has_rows) return;
 
   // Epilogue. Accumulator element v of lane l sits at row
   // (v/4)*8 + (l/32)*4 + v%4 and column l%32 of its 32x32 block.
@@ -394,6 +412,146 @@ __global__ __launch_bounds__(gemm_threads<kWaveM>()) void mfma_gemm_kernel(GemmA
           }
         }
       }
+  }
+}
+
+// Skinny grouped GEMM for a few rows per expert (decode): weight-bandwidth
+// bound, so weights stream from HBM straight into registers (no LDS, no
+// reuse to stage) and the MFMA work is sized to the rows that exist.
+// One wavefront per (expert, block of 64 weight rows, group of 16 rows of
+// A). MFMA 16x16x32 with A = 16 weight rows and B = 16 rows of X (tokens),
+// D[weight row][token]. Within a K-iteration of 128, lane group g = lane/16
+// holds 32 consecutive k of its row (64 contiguous bytes): MFMA step s uses
+// k = kb + 32g + 8s + [0, 8) in both operands, which is a fixed permutation
+// of the 128 k and therefore leaves the dot products unchanged. The next
+// iteration's loads are issued before the current one's MFMAs.
+// GEMM 1 blocks hold 32 gate rows and the same 32 up rows.
+constexpr int kSkinnyWaveRows = 64;  // weight rows per wavefront (4 MFMA tiles)
+constexpr int kSkinnyTokens = 16;
+constexpr int kSkinnyKIter = 128;
+
+template <typename T> struct Mfma16;
+template <> struct Mfma16<bf16> {
+  typedef bf16x8 Frag;
+  static __device__ __forceinline__ f32x4 run(Frag a, Frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct Mfma16<f16> {
+  typedef f16x8 Frag;
+  static __device__ __forceinline__ f32x4 run(Frag a, Frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+struct SkinnyArgs {
+  GemmArgs g;
+  int E;
+  int n_blocks;  // weight-row blocks per expert
+};
+
+template <typename T, bool kSwiGlu>
+__global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs sa) {
+  typedef typename Mfma16<T>::Frag Frag;
+  const GemmArgs& p = sa.g;
+  const int lane = threadIdx.x & 63;
+  const int wid = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int e = wid / sa.n_blocks;
+  const int nb = wid - e * sa.n_blocks;
+  if (e >= sa.E) return;
+  const int r_begin = max(__builtin_amdgcn_readfirstlane(p.offsets[e]), 0);
+  const int r_end = min(__builtin_amdgcn_readfirstlane(p.offsets[e + 1]), p.rows);
+  if (r_end <= r_begin) return;
+
+  const int K = p.K, N = p.N;
+  const uint32_t row_bytes = (uint32_t)K * sizeof(T);
+  const int64_t expert_elems = (int64_t)e * N * K;
+  const int b_bytes = (int)((uint32_t)N * row_bytes);
+  const __amdgpu_buffer_rsrc_t rw0 = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T*>(static_cast<const T*>(p.b0) + expert_elems), (short)0, b_bytes, kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rw1 = kSwiGlu
+      ? __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(static_cast<const T*>(p.b1) + expert_elems),
+                                          (short)0, b_bytes, kRsrcFlags)
+      : rw0;
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(p.a), (short)0, (int)((uint32_t)p.a_rows * row_bytes), kRsrcFlags);
+
+  // Weight rows of the 4 tiles (rows past N read as zero).
+  const int g = lane >> 4;
+  uint32_t vo_w[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int n = kSwiGlu ? nb * 32 + (t & 1) * 16 + (lane & 15) : nb * kSkinnyWaveRows + t * 16 + (lane & 15);
+    vo_w[t] = (uint32_t)n * row_bytes + (uint32_t)g * 64u;
+  }
+
+  T* C = static_cast<T*>(p.c);
+  for (int rg = r_begin; rg < r_end; rg += kSkinnyTokens) {
+    const int xr = rg + (lane & 15);
+    uint32_t vo_x = kOutOfRange;
+    if (xr < r_end) {
+      const int src = p.a_map ? min(max(p.a_map[xr] / p.a_div, 0), p.a_rows - 1) : xr;
+      vo_x = (uint32_t)src * row_bytes + (uint32_t)g * 64u;
+    }
+    f32x4 acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Two register buffers, named (not indexed) so they stay in registers;
+    // the iteration count is padded to even: loads past K read as zero.
+    uint4 wa[4][4], xa[4], wb[4][4], xb[4];
+    auto load = [&](int kb, uint4 (&w)[4][4], uint4 (&x)[4]) {
+      const uint32_t soff = (uint32_t)kb * sizeof(T);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const bool ok = kb + g * 32 + c * 8 < K;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          w[t][c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+              (kSwiGlu && t >= 2) ? rw1 : rw0, ok ? vo_w[t] + c * 16u : kOutOfRange, soff, 0));
+        x[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+            rx, ok ? vo_x + c * 16u : kOutOfRange, soff, 0));
+      }
+    };
+    auto compute = [&](const uint4 (&w)[4][4], const uint4 (&x)[4]) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          acc[t] = Mfma16<T>::run(__builtin_bit_cast(Frag, w[t][c]), __builtin_bit_cast(Frag, x[c]),
+                                  acc[t]);
+    };
+    const int n_iter = (K + kSkinnyKIter - 1) / kSkinnyKIter;
+    load(0, wa, xa);
+    for (int it = 0; it < n_iter; it += 2) {
+      load((it + 1) * kSkinnyKIter, wb, xb);
+      compute(wa, xa);
+      load((it + 2) * kSkinnyKIter, wa, xa);
+      compute(wb, xb);
+    }
+
+    // D element v of lane l: weight row (l/16)*4 + v of the tile, token l%16.
+    const int tok = rg + (lane & 15);
+    if (tok < r_end) {
+      T* crow = C + (int64_t)tok * N;
+      if (kSwiGlu) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int col = nb * 32 + t * 16 + g * 4;
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (col + v < N) crow[col + v] = from_f32<T>(silu(acc[t][v]) * acc[t + 2][v]);
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int col = nb * kSkinnyWaveRows + t * 16 + g * 4;
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (col + v < N) crow[col + v] = from_f32<T>(acc[t][v]);
+        }
+      }
+    }
   }
 }
 
@@ -641,6 +799,24 @@ void setup_down(GemmArgs& g, const ExpertsPlan& plan, void* scratch, const void*
   g.partial = partial_buffer(plan, scratch);
 }
 
+// Few rows per expert (decode-shaped batches): weight streaming dominates.
+bool use_skinny(int rows, int E, int dt) { return dt != kF32 && rows <= 4 * E; }
+
+void launch_skinny(const GemmArgs& g, int E, int dt, bool swiglu, hipStream_t s) {
+  SkinnyArgs sa;
+  sa.g = g;
+  sa.E = E;
+  sa.n_blocks = swiglu ? (g.N + 31) / 32 : (g.N + kSkinnyWaveRows - 1) / kSkinnyWaveRows;
+  const dim3 grid((unsigned)(((int64_t)E * sa.n_blocks + 3) / 4));
+  if (dt == kF16) {
+    if (swiglu) hipLaunchKernelGGL((skinny_gemm_kernel<f16, true>), grid, dim3(256), 0, s, sa);
+    else hipLaunchKernelGGL((skinny_gemm_kernel<f16, false>), grid, dim3(256), 0, s, sa);
+  } else {
+    if (swiglu) hipLaunchKernelGGL((skinny_gemm_kernel<bf16, true>), grid, dim3(256), 0, s, sa);
+    else hipLaunchKernelGGL((skinny_gemm_kernel<bf16, false>), grid, dim3(256), 0, s, sa);
+  }
+}
+
 hipError_t reduce_splits(const ExpertsPlan& plan, void* scratch, const int32_t* offsets, int rows,
                          int E, int H, int dt, void* expert_out, hipStream_t s) {
   const int64_t n = (int64_t)rows * (H / 8);
@@ -661,6 +837,13 @@ hipError_t launch_gate_up(const void* a, const int32_t* a_map, int a_div, const 
                           int rows, int E, int H, int I, const void* w_gate, const void* w_up,
                           int dt, void* h, void* scratch, hipStream_t s) {
   if (rows == 0) return hipSuccess;
+  if (use_skinny(rows, E, dt)) {
+    GemmArgs g = {};
+    g.offsets = offsets; g.rows = rows;
+    setup_gate_up(g, a, a_map, a_div, H, I, w_gate, w_up, h);
+    launch_skinny(g, E, dt, true, s);
+    return hipGetLastError();
+  }
   const ExpertsPlan plan = experts_plan(rows, E, H, I, dt);
   GemmArgs g = plan_tiles(plan, offsets, rows, E, scratch, s);
   setup_gate_up(g, a, a_map, a_div, H, I, w_gate, w_up, h);
@@ -672,6 +855,14 @@ hipError_t launch_down(const void* h, const int32_t* offsets, int rows, int E, i
                        const void* w_down, int dt, void* expert_out, void* scratch,
                        hipStream_t s, DownPartials* keep) {
   if (rows == 0) return hipSuccess;
+  if (use_skinny(rows, E, dt)) {
+    GemmArgs g = {};
+    g.offsets = offsets; g.rows = rows;
+    setup_down(g, ExpertsPlan{kBM, 0, 1, I}, nullptr, h, H, I, w_down, expert_out);
+    g.partial = nullptr;
+    launch_skinny(g, E, dt, false, s);
+    return hipGetLastError();
+  }
   const ExpertsPlan plan = experts_plan(rows, E, H, I, dt);
   GemmArgs g = plan_tiles(plan, offsets, rows, E, scratch, s);
   setup_down(g, plan, scratch, h, H, I, w_down, expert_out);

@@ -207,6 +207,40 @@ def test_experts_all_rows_one_expert():
     assert_close(host(got), ref, "bf16", "expert_out one expert")
 
 
+SKINNY_CASES = [
+    # rows <= 4 * E selects the weight-streaming kernel (decode-shaped batches)
+    (10, 2, 8, 136, 200, "bf16", False),
+    (12, 3, 16, 264, 392, "f16", False),
+    (40, 1, 16, 128, 256, "bf16", True),   # one expert holds all 40 rows: 3 row groups
+    (3, 2, 64, 520, 1000, "bf16", False),  # N tails inside a 64-row block
+]
+
+
+@pytest.mark.parametrize("T,k,E,H,I_,dtype,one_expert", SKINNY_CASES)
+def test_experts_few_rows_per_expert(T, k, E, H, I_, dtype, one_expert):
+    say("skinny", T, k, E, H, I_, dtype)
+    g = np.random.default_rng(T * 11 + E)
+    x = _store(g.standard_normal((T, H)), dtype)
+    if one_expert:
+        idx = np.full((T, k), 5, np.uint32)
+    else:
+        idx, _ = O.route(I.gapped_logits(T + E, T, E, k), "f32", k, True)
+    d = O.dispatch(idx, E, x)
+    wg, wu, wd = _random_experts(g, E, H, I_, dtype)
+    ref = O.experts_forward_dispatched(d["x_disp"], d["offsets"], lambda e: (wg[e], wu[e], wd[e]), dtype)
+    got = moe.moe_experts_forward_dispatched(dev(d["x_disp"], dtype), dev(d["offsets"]), dev(wg, dtype),
+                                             dev(wu, dtype), dev(wd, dtype))
+    torch.cuda.synchronize()
+    assert_close(host(got), ref, dtype, f"skinny expert_out {dtype}")
+    # gate/up through the dispatch map (tokens read from x), then down
+    off, sor = dev(d["offsets"]), dev(d["slot_of_row"])
+    h = moe.moe_experts_gate_up(dev(x, dtype), off, dev(wg, dtype), dev(wu, dtype), row_map=sor,
+                                map_div=k, rows=T * k)
+    y2 = moe.moe_experts_down(h, off, dev(wd, dtype))
+    torch.cuda.synchronize()
+    assert_close(host(y2), ref, dtype, f"skinny halves {dtype}")
+
+
 def test_experts_split_k_and_halves():
     """Long K with few output tiles: the down GEMM splits K (fp32 partials,
     reduced in order). Checked through forward_dispatched, through the two
