@@ -416,19 +416,22 @@ __global__ __launch_bounds__(gemm_threads<kWaveM>()) void mfma_gemm_kernel(GemmA
 }
 
 // Skinny grouped GEMM for a few rows per expert (decode): weight-bandwidth
-// bound, so weights stream from HBM straight into registers (no LDS, no
-// reuse to stage) and the MFMA work is sized to the rows that exist.
-// One wavefront per (expert, block of 64 weight rows, group of 16 rows of
-// A). MFMA 16x16x32 with A = 16 weight rows and B = 16 rows of X (tokens),
-// D[weight row][token]. Within a K-iteration of 128, lane group g = lane/16
-// holds 32 consecutive k of its row (64 contiguous bytes): MFMA step s uses
-// k = kb + 32g + 8s + [0, 8) in both operands, which is a fixed permutation
-// of the 128 k and therefore leaves the dot products unchanged. The next
-// iteration's loads are issued before the current one's MFMAs.
+// bound, so weights stream from HBM straight into registers (no reuse to
+// stage through LDS) and the MFMA work is sized to the rows that exist.
+// One workgroup of 4 wavefronts per (expert, block of 64 weight rows); the
+// wavefronts split K four ways and their partial sums meet in LDS, so the
+// grid has enough independent streams to keep every CU busy. Rows of A
+// (tokens) are taken 16 at a time. MFMA 16x16x32 with A = 16 weight rows and
+// B = 16 rows of X, D[weight row][token]. In a K-iteration of 128, load c
+// (= MFMA step c) gives lane group g = lane/16 the 8 elements at
+// k = kb + 32c + 8g, the MFMA's own operand layout, so the four lanes of a
+// row read 64 contiguous bytes per load. All loads of the next iteration are
+// issued before the current one's MFMAs.
 // GEMM 1 blocks hold 32 gate rows and the same 32 up rows.
-constexpr int kSkinnyWaveRows = 64;  // weight rows per wavefront (4 MFMA tiles)
+constexpr int kSkinnyWaveRows = 64;  // weight rows per workgroup (4 MFMA tiles)
 constexpr int kSkinnyTokens = 16;
 constexpr int kSkinnyKIter = 128;
+constexpr int kSkinnyWaves = 4;
 
 template <typename T> struct Mfma16;
 template <> struct Mfma16<bf16> {
@@ -448,22 +451,26 @@ struct SkinnyArgs {
   GemmArgs g;
   int E;
   int n_blocks;  // weight-row blocks per expert
+  int k_quarter; // K elements per wavefront (multiple of kSkinnyKIter)
 };
 
 template <typename T, bool kSwiGlu>
-__global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs sa) {
+__global__ __launch_bounds__(64 * kSkinnyWaves) void skinny_gemm_kernel(SkinnyArgs sa) {
   typedef typename Mfma16<T>::Frag Frag;
+  __shared__ f32x4 red[kSkinnyWaves - 1][4][64];
   const GemmArgs& p = sa.g;
   const int lane = threadIdx.x & 63;
-  const int wid = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int e = wid / sa.n_blocks;
-  const int nb = wid - e * sa.n_blocks;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int e = blockIdx.x / sa.n_blocks;
+  const int nb = blockIdx.x - e * sa.n_blocks;
   if (e >= sa.E) return;
   const int r_begin = max(__builtin_amdgcn_readfirstlane(p.offsets[e]), 0);
   const int r_end = min(__builtin_amdgcn_readfirstlane(p.offsets[e + 1]), p.rows);
   if (r_end <= r_begin) return;
 
   const int K = p.K, N = p.N;
+  const int k_lo = wave * sa.k_quarter;
+  const int k_hi = min(K, k_lo + sa.k_quarter);
   const uint32_t row_bytes = (uint32_t)K * sizeof(T);
   const int64_t expert_elems = (int64_t)e * N * K;
   const int b_bytes = (int)((uint32_t)N * row_bytes);
@@ -482,7 +489,7 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs sa) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int n = kSwiGlu ? nb * 32 + (t & 1) * 16 + (lane & 15) : nb * kSkinnyWaveRows + t * 16 + (lane & 15);
-    vo_w[t] = (uint32_t)n * row_bytes + (uint32_t)g * 64u;
+    vo_w[t] = (uint32_t)n * row_bytes + (uint32_t)g * 16u;
   }
 
   T* C = static_cast<T*>(p.c);
@@ -491,26 +498,26 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs sa) {
     uint32_t vo_x = kOutOfRange;
     if (xr < r_end) {
       const int src = p.a_map ? min(max(p.a_map[xr] / p.a_div, 0), p.a_rows - 1) : xr;
-      vo_x = (uint32_t)src * row_bytes + (uint32_t)g * 64u;
+      vo_x = (uint32_t)src * row_bytes + (uint32_t)g * 16u;
     }
     f32x4 acc[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // Two register buffers, named (not indexed) so they stay in registers;
-    // the iteration count is padded to even: loads past K read as zero.
+    // loads past this wavefront's K range read as zero.
     uint4 wa[4][4], xa[4], wb[4][4], xb[4];
     auto load = [&](int kb, uint4 (&w)[4][4], uint4 (&x)[4]) {
       const uint32_t soff = (uint32_t)kb * sizeof(T);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const bool ok = kb + g * 32 + c * 8 < K;
+        const bool ok = kb + c * 32 + g * 8 < k_hi;
 #pragma unroll
         for (int t = 0; t < 4; ++t)
           w[t][c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-              (kSwiGlu && t >= 2) ? rw1 : rw0, ok ? vo_w[t] + c * 16u : kOutOfRange, soff, 0));
+              (kSwiGlu && t >= 2) ? rw1 : rw0, ok ? vo_w[t] + c * 64u : kOutOfRange, soff, 0));
         x[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-            rx, ok ? vo_x + c * 16u : kOutOfRange, soff, 0));
+            rx, ok ? vo_x + c * 64u : kOutOfRange, soff, 0));
       }
     };
     auto compute = [&](const uint4 (&w)[4][4], const uint4 (&x)[4]) {
@@ -521,37 +528,60 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs sa) {
           acc[t] = Mfma16<T>::run(__builtin_bit_cast(Frag, w[t][c]), __builtin_bit_cast(Frag, x[c]),
                                   acc[t]);
     };
-    const int n_iter = (K + kSkinnyKIter - 1) / kSkinnyKIter;
-    load(0, wa, xa);
-    for (int it = 0; it < n_iter; it += 2) {
-      load((it + 1) * kSkinnyKIter, wb, xb);
-      compute(wa, xa);
-      load((it + 2) * kSkinnyKIter, wa, xa);
-      compute(wb, xb);
+    const int n_iter = (k_hi - k_lo + kSkinnyKIter - 1) / kSkinnyKIter;
+    if (n_iter > 0) {
+      load(k_lo, wa, xa);
+      // keep every load of the next iteration ahead of this one's MFMAs
+      constexpr int kLoadsPerIter = 4 * 4 + 4;
+      int it = 0;
+      for (; it + 2 <= n_iter; it += 2) {
+        load(k_lo + (it + 1) * kSkinnyKIter, wb, xb);
+        compute(wa, xa);
+        __builtin_amdgcn_sched_group_barrier(0x020, kLoadsPerIter, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+        load(k_lo + (it + 2) * kSkinnyKIter, wa, xa);
+        compute(wb, xb);
+        __builtin_amdgcn_sched_group_barrier(0x020, kLoadsPerIter, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+      }
+      if (it < n_iter) compute(wa, xa);  // odd count: wa holds the last iteration
     }
 
-    // D element v of lane l: weight row (l/16)*4 + v of the tile, token l%16.
-    const int tok = rg + (lane & 15);
-    if (tok < r_end) {
-      T* crow = C + (int64_t)tok * N;
-      if (kSwiGlu) {
+    // Partial sums of wavefronts 1..3 meet wavefront 0's in LDS (fixed order).
+    if (wave > 0) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int col = nb * 32 + t * 16 + g * 4;
+      for (int t = 0; t < 4; ++t) red[wave - 1][t][lane] = acc[t];
+    }
+    __syncthreads();
+    if (wave == 0) {
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
-            if (col + v < N) crow[col + v] = from_f32<T>(silu(acc[t][v]) * acc[t + 2][v]);
-        }
-      } else {
+      for (int w = 0; w < kSkinnyWaves - 1; ++w)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int col = nb * kSkinnyWaveRows + t * 16 + g * 4;
+        for (int t = 0; t < 4; ++t) acc[t] += red[w][t][lane];
+      // D element v of lane l: weight row (l/16)*4 + v of the tile, token l%16.
+      const int tok = rg + (lane & 15);
+      if (tok < r_end) {
+        T* crow = C + (int64_t)tok * N;
+        if (kSwiGlu) {
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
-            if (col + v < N) crow[col + v] = from_f32<T>(acc[t][v]);
+          for (int t = 0; t < 2; ++t) {
+            const int col = nb * 32 + t * 16 + g * 4;
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              if (col + v < N) crow[col + v] = from_f32<T>(silu(acc[t][v]) * acc[t + 2][v]);
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int col = nb * kSkinnyWaveRows + t * 16 + g * 4;
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              if (col + v < N) crow[col + v] = from_f32<T>(acc[t][v]);
+          }
         }
       }
     }
+    __syncthreads();  // red[] is reused by the next row group
   }
 }
 
@@ -807,13 +837,15 @@ void launch_skinny(const GemmArgs& g, int E, int dt, bool swiglu, hipStream_t s)
   sa.g = g;
   sa.E = E;
   sa.n_blocks = swiglu ? (g.N + 31) / 32 : (g.N + kSkinnyWaveRows - 1) / kSkinnyWaveRows;
-  const dim3 grid((unsigned)(((int64_t)E * sa.n_blocks + 3) / 4));
+  const int iters = (g.K + kSkinnyKIter - 1) / kSkinnyKIter;
+  sa.k_quarter = (iters + kSkinnyWaves - 1) / kSkinnyWaves * kSkinnyKIter;
+  const dim3 grid((unsigned)((int64_t)E * sa.n_blocks));
   if (dt == kF16) {
-    if (swiglu) hipLaunchKernelGGL((skinny_gemm_kernel<f16, true>), grid, dim3(256), 0, s, sa);
-    else hipLaunchKernelGGL((skinny_gemm_kernel<f16, false>), grid, dim3(256), 0, s, sa);
+    if (swiglu) hipLaunchKernelGGL((skinny_gemm_kernel<f16, true>), grid, dim3(64 * kSkinnyWaves), 0, s, sa);
+    else hipLaunchKernelGGL((skinny_gemm_kernel<f16, false>), grid, dim3(64 * kSkinnyWaves), 0, s, sa);
   } else {
-    if (swiglu) hipLaunchKernelGGL((skinny_gemm_kernel<bf16, true>), grid, dim3(256), 0, s, sa);
-    else hipLaunchKernelGGL((skinny_gemm_kernel<bf16, false>), grid, dim3(256), 0, s, sa);
+    if (swiglu) hipLaunchKernelGGL((skinny_gemm_kernel<bf16, true>), grid, dim3(64 * kSkinnyWaves), 0, s, sa);
+    else hipLaunchKernelGGL((skinny_gemm_kernel<bf16, false>), grid, dim3(64 * kSkinnyWaves), 0, s, sa);
   }
 }
 
