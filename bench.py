@@ -38,17 +38,28 @@ BOUND = {"tiny_fp32": "alu", "mixtral_8x_bf16": "mfma", "many_expert_zipf_bf16":
          "dsv3_share_rmsnorm_bf16": "hbm", "decode_nan_rows_bf16": "hbm"}
 
 
+def kernel_source_hash() -> str:
+    """sha256/16 over the HIP sources, in name order: counters taken on other
+    sources no longer describe the kernels."""
+    import hashlib
+    d = os.path.join(ROOT, "mixture_experts_ffn_top_amd", "csrc")
+    h = hashlib.sha256()
+    for n in sorted(os.listdir(d)):
+        if n.endswith((".hip", ".h")):
+            h.update(n.encode())
+            h.update(open(os.path.join(d, n), "rb").read())
+    return h.hexdigest()[:16]
+
+
 def measured_traffic(workload: str, kernel: str):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE runs (profiles/counters.json, scaled by the copy-kernel
-    calibration), or None when the GEMM source changed after they were taken."""
-    import hashlib
+    calibration), or None when the kernel sources changed after they were taken."""
     try:
         data = json.load(open(os.path.join(ROOT, "profiles", "counters.json")))[workload]
-        src = open(os.path.join(ROOT, "mixture_experts_ffn_top_amd", "csrc", "gemm.hip"), "rb").read()
     except (OSError, KeyError, ValueError):
         return None
-    if hashlib.sha256(src).hexdigest()[:16] != data.get("gemm_source_sha16"):
+    if kernel_source_hash() != data.get("kernel_source_sha16"):
         return None
     return data["traffic_bytes_per_launch"].get(kernel)
 
@@ -222,7 +233,12 @@ def main():
         achieved, peak, unit = bytes_gate_up / gu_s / 1e9, PEAK_HBM_GBS, "GB/s"
     else:
         achieved, peak, unit = flops_gate_up / gu_s / 1e12, PEAK_TFLOPS[w.dtype], "TFLOP/s"
-    kname = {"bf16": "mfma_gemm_kernel<bf16,gate_up>", "f32": "simt_gemm_kernel<gate_up>"}[w.dtype]
+    if w.dtype == "f32":
+        kname = "simt_gemm_kernel<gate_up>"
+    elif R <= 4 * E:  # the library's weight-streaming path for decode-sized batches
+        kname = "skinny_gemm_kernel<bf16,gate_up>"
+    else:
+        kname = "mfma_gemm_kernel<bf16,gate_up>"
     roofline = {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4),
                 "traffic": measured_traffic(args.workload, kname),

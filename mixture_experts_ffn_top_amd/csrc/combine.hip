@@ -14,8 +14,16 @@
 namespace moe {
 namespace {
 
+constexpr int kChunkK = 8;  // expert rows whose loads are issued together
+
+// The fused epilogue touches every byte once: streaming (non-temporal)
+// loads and stores.
+#define LOAD(v, p) (v).load_nt(p)
+#define STORE(v, p) (v).store_nt(p)
+
 // Grid T * ceil(H/8/256) (token-major); each thread produces 8 consecutive
-// outputs.
+// outputs. The k expert rows are fetched kChunkK at a time, all loads of a
+// chunk issued before any is used, then summed in slot order.
 template <typename T, typename WT>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y,
                                                        const int32_t* __restrict__ row_of_slot,
@@ -27,14 +35,26 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y,
   if (v * 8 >= H) return;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   bool lost = false;
-  for (int j = 0; j < k; ++j) {
-    const int r = row_of_slot[(int64_t)t * k + j];
-    const float wj = to_f32(w[(int64_t)t * k + j]);
-    if (r < 0) { lost = true; continue; }
-    Vec8<T> d;
-    d.load(y + (int64_t)r * H + v * 8);
+  for (int j0 = 0; j0 < k; j0 += kChunkK) {
+    Vec8<T> d[kChunkK];
+    float wj[kChunkK];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, d.get(i), acc[i]);
+    for (int j = 0; j < kChunkK; ++j) {
+      wj[j] = 0.f;
+      if (j0 + j < k) {
+        const int r = row_of_slot[(int64_t)t * k + j0 + j];
+        wj[j] = to_f32(w[(int64_t)t * k + j0 + j]);
+        if (r < 0) lost = true;
+        else d[j].load(y + (int64_t)r * H + v * 8);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kChunkK; ++j) {
+      if (j0 + j < k && !lost) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj[j], d[j].get(i), acc[i]);
+      }
+    }
   }
   Vec8<T> o;
 #pragma unroll
@@ -54,26 +74,46 @@ __global__ __launch_bounds__(256) void combine_partials_kernel(
   if (v * 8 >= H) return;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   bool lost = false;
-  for (int j = 0; j < k; ++j) {
-    const int r = row_of_slot[(int64_t)t * k + j];
-    const float wj = to_f32(w[(int64_t)t * k + j]);
-    if (r < 0) { lost = true; continue; }
-    const float* src = partial + (int64_t)r * H + v * 8;
-    float y[8];
-    {
-      const float4 a0 = *reinterpret_cast<const float4*>(src);
-      const float4 a1 = *reinterpret_cast<const float4*>(src + 4);
-      y[0] = a0.x; y[1] = a0.y; y[2] = a0.z; y[3] = a0.w;
-      y[4] = a1.x; y[5] = a1.y; y[6] = a1.z; y[7] = a1.w;
+  constexpr int kC = 4;
+  for (int j0 = 0; j0 < k; j0 += kC) {
+    float4 a0[kC], a1[kC];
+    float wj[kC];
+    const float* src[kC];
+#pragma unroll
+    for (int j = 0; j < kC; ++j) {
+      wj[j] = 0.f;
+      src[j] = nullptr;
+      if (j0 + j < k) {
+        const int r = row_of_slot[(int64_t)t * k + j0 + j];
+        wj[j] = to_f32(w[(int64_t)t * k + j0 + j]);
+        if (r < 0) {
+          lost = true;
+        } else {
+          src[j] = partial + (int64_t)r * H + v * 8;
+          a0[j] = *reinterpret_cast<const float4*>(src[j]);
+          a1[j] = *reinterpret_cast<const float4*>(src[j] + 4);
+        }
+      }
     }
-    for (int s = 1; s < splits; ++s) {
-      const float4 a0 = *reinterpret_cast<const float4*>(src + s * split_stride);
-      const float4 a1 = *reinterpret_cast<const float4*>(src + s * split_stride + 4);
-      y[0] += a0.x; y[1] += a0.y; y[2] += a0.z; y[3] += a0.w;
-      y[4] += a1.x; y[5] += a1.y; y[6] += a1.z; y[7] += a1.w;
+    for (int sp = 1; sp < splits; ++sp) {
+#pragma unroll
+      for (int j = 0; j < kC; ++j) {
+        if (src[j]) {
+          const float4 b0 = *reinterpret_cast<const float4*>(src[j] + sp * split_stride);
+          const float4 b1 = *reinterpret_cast<const float4*>(src[j] + sp * split_stride + 4);
+          a0[j].x += b0.x; a0[j].y += b0.y; a0[j].z += b0.z; a0[j].w += b0.w;
+          a1[j].x += b1.x; a1[j].y += b1.y; a1[j].z += b1.z; a1[j].w += b1.w;
+        }
+      }
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, to_f32(from_f32<T>(y[i])), acc[i]);
+    for (int j = 0; j < kC; ++j) {
+      if (src[j]) {
+        const float y[8] = {a0[j].x, a0[j].y, a0[j].z, a0[j].w, a1[j].x, a1[j].y, a1[j].z, a1[j].w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj[j], to_f32(from_f32<T>(y[i])), acc[i]);
+      }
+    }
   }
   Vec8<T> o;
 #pragma unroll
@@ -81,19 +121,20 @@ __global__ __launch_bounds__(256) void combine_partials_kernel(
   o.store(out + (int64_t)t * H + v * 8);
 }
 
-constexpr int kNormThreads = 256;
-
-// One workgroup per token; thread owns VPT groups of 8 columns, strided by
-// the workgroup, and keeps x in registers between the two passes.
+// One workgroup per token, up to 1024 threads; thread owns VPT groups of 8
+// columns strided by the workgroup and keeps x in registers between the sum
+// of squares and the scaling. The k expert rows of a group are fetched
+// kChunkK at a time with all loads issued before any is used.
 template <typename T, typename WT, int VPT>
-__global__ __launch_bounds__(kNormThreads) void combine_norm_kernel(
+__global__ __launch_bounds__(1024) void combine_norm_kernel(
     const T* __restrict__ y, const int32_t* __restrict__ row_of_slot, const WT* __restrict__ w,
     const T* __restrict__ shared, const T* __restrict__ residual, const float* __restrict__ gamma,
     float eps, int k, int H, T* __restrict__ y_out, T* __restrict__ x_out,
     float* __restrict__ rstd_out) {
-  __shared__ float red[kNormThreads / kWave];
+  __shared__ float red[1024 / kWave];
   const int t = blockIdx.x;
   const int nvec = H / 8;
+  const int nthreads = blockDim.x;
   float x[VPT][8];
 #pragma unroll
   for (int q = 0; q < VPT; ++q)
@@ -102,31 +143,46 @@ __global__ __launch_bounds__(kNormThreads) void combine_norm_kernel(
 
   float wsum = 0.f;
   bool lost = false;
-  for (int j = 0; j < k; ++j) {
-    const int r = row_of_slot[(int64_t)t * k + j];
-    const float wj = to_f32(w[(int64_t)t * k + j]);
-    wsum += wj;
-    if (r < 0) { lost = true; continue; }
+  for (int j0 = 0; j0 < k; j0 += kChunkK) {
+    int rows[kChunkK];
+    float wj[kChunkK];
+#pragma unroll
+    for (int j = 0; j < kChunkK; ++j) {
+      rows[j] = -1;
+      wj[j] = 0.f;
+      if (j0 + j < k) {
+        rows[j] = row_of_slot[(int64_t)t * k + j0 + j];
+        wj[j] = to_f32(w[(int64_t)t * k + j0 + j]);
+        wsum += wj[j];
+        if (rows[j] < 0) lost = true;
+      }
+    }
 #pragma unroll
     for (int q = 0; q < VPT; ++q) {
-      const int v = threadIdx.x + q * kNormThreads;
+      const int v = threadIdx.x + q * nthreads;
       if (v < nvec) {
-        Vec8<T> d;
-        d.load(y + (int64_t)r * H + v * 8);
+        Vec8<T> d[kChunkK];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) x[q][i] = fmaf(wj, d.get(i), x[q][i]);
+        for (int j = 0; j < kChunkK; ++j)
+          if (rows[j] >= 0) LOAD(d[j], y + (int64_t)rows[j] * H + v * 8);
+#pragma unroll
+        for (int j = 0; j < kChunkK; ++j)
+          if (rows[j] >= 0) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[q][i] = fmaf(wj[j], d[j].get(i), x[q][i]);
+          }
       }
     }
   }
   float ss = 0.f;
 #pragma unroll
   for (int q = 0; q < VPT; ++q) {
-    const int v = threadIdx.x + q * kNormThreads;
+    const int v = threadIdx.x + q * nthreads;
     if (v < nvec) {
       Vec8<T> rs;
-      rs.load(residual + (int64_t)t * H + v * 8);
+      LOAD(rs, residual + (int64_t)t * H + v * 8);
       Vec8<T> sh;
-      if (shared) sh.load(shared + (int64_t)t * H + v * 8);
+      if (shared) LOAD(sh, shared + (int64_t)t * H + v * 8);
       Vec8<T> xo;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -138,7 +194,7 @@ __global__ __launch_bounds__(kNormThreads) void combine_norm_kernel(
         ss = fmaf(xv, xv, ss);
         xo.set(i, xv);
       }
-      xo.store(x_out + (int64_t)t * H + v * 8);
+      STORE(xo, x_out + (int64_t)t * H + v * 8);
     }
   }
 #pragma unroll
@@ -146,13 +202,12 @@ __global__ __launch_bounds__(kNormThreads) void combine_norm_kernel(
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
   float tot = 0.f;
-#pragma unroll
-  for (int i = 0; i < kNormThreads / kWave; ++i) tot += red[i];
+  for (int i = 0; i < nthreads / kWave; ++i) tot += red[i];
   const float rstd = 1.0f / sqrtf(tot / (float)H + eps);
   if (threadIdx.x == 0) rstd_out[t] = rstd;
 #pragma unroll
   for (int q = 0; q < VPT; ++q) {
-    const int v = threadIdx.x + q * kNormThreads;
+    const int v = threadIdx.x + q * nthreads;
     if (v < nvec) {
       const float4 g0 = *reinterpret_cast<const float4*>(gamma + v * 8);
       const float4 g1 = *reinterpret_cast<const float4*>(gamma + v * 8 + 4);
@@ -160,7 +215,7 @@ __global__ __launch_bounds__(kNormThreads) void combine_norm_kernel(
       Vec8<T> yo;
 #pragma unroll
       for (int i = 0; i < 8; ++i) yo.set(i, x[q][i] * rstd * g[i]);
-      yo.store(y_out + (int64_t)t * H + v * 8);
+      STORE(yo, y_out + (int64_t)t * H + v * 8);
     }
   }
 }
@@ -189,23 +244,31 @@ template <typename T, typename WT, int VPT>
 hipError_t norm_launch(const void* y, const int32_t* ros, const void* w, const void* sh,
                        const void* res, const float* gamma, float eps, int T_, int k, int H,
                        void* yo, void* xo, float* rstd, hipStream_t s) {
-  hipLaunchKernelGGL((combine_norm_kernel<T, WT, VPT>), dim3(T_), dim3(kNormThreads), 0, s,
+  const int nvec = H / 8;
+  int threads = (nvec + VPT - 1) / VPT;
+  threads = (threads + kWave - 1) / kWave * kWave;
+  hipLaunchKernelGGL((combine_norm_kernel<T, WT, VPT>), dim3(T_), dim3(threads), 0, s,
                      static_cast<const T*>(y), ros, static_cast<const WT*>(w),
                      static_cast<const T*>(sh), static_cast<const T*>(res), gamma, eps, k, H,
                      static_cast<T*>(yo), static_cast<T*>(xo), rstd);
   return hipGetLastError();
 }
 
+// Groups of 8 columns per thread: at least two (measured best on the
+// DeepSeek-V3-shaped epilogue), more once H/8 exceeds 1024 threads.
+#ifndef MOE_NORM_MIN_VPT
+#define MOE_NORM_MIN_VPT 2
+#endif
 template <typename T, typename WT>
 hipError_t norm_vpt(const void* y, const int32_t* ros, const void* w, const void* sh,
                     const void* res, const float* gamma, float eps, int T_, int k, int H,
                     void* yo, void* xo, float* rstd, hipStream_t s) {
-  const int per = (H / 8 + kNormThreads - 1) / kNormThreads;
+  int per = (H / 8 + 1023) / 1024;
+  if (per < MOE_NORM_MIN_VPT) per = MOE_NORM_MIN_VPT;
   if (per <= 1) return norm_launch<T, WT, 1>(y, ros, w, sh, res, gamma, eps, T_, k, H, yo, xo, rstd, s);
   if (per <= 2) return norm_launch<T, WT, 2>(y, ros, w, sh, res, gamma, eps, T_, k, H, yo, xo, rstd, s);
   if (per <= 4) return norm_launch<T, WT, 4>(y, ros, w, sh, res, gamma, eps, T_, k, H, yo, xo, rstd, s);
-  if (per <= 8) return norm_launch<T, WT, 8>(y, ros, w, sh, res, gamma, eps, T_, k, H, yo, xo, rstd, s);
-  return norm_launch<T, WT, 16>(y, ros, w, sh, res, gamma, eps, T_, k, H, yo, xo, rstd, s);
+  return norm_launch<T, WT, 8>(y, ros, w, sh, res, gamma, eps, T_, k, H, yo, xo, rstd, s);
 }
 
 template <typename T>

@@ -13,6 +13,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kMaxExperts = 1024;
@@ -40,6 +41,17 @@ struct Vec8 {
     uint4* q = reinterpret_cast<uint4*>(p);
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) q[i] = raw[i];
+  }
+  // Streaming variants: data touched once, marked non-temporal.
+  __device__ __forceinline__ void load_nt(const T* p) {
+    const u32x4* q = reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) raw[i] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(q + i));
+  }
+  __device__ __forceinline__ void store_nt(T* p) const {
+    u32x4* q = reinterpret_cast<u32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) __builtin_nontemporal_store(__builtin_bit_cast(u32x4, raw[i]), q + i);
   }
   __device__ __forceinline__ float get(int i) const {
     return to_f32(reinterpret_cast<const T*>(raw)[i]);

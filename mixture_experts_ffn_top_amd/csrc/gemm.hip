@@ -12,22 +12,28 @@
 // workgroups past the device tile count exit at once. Expert counts never
 // travel to the host.
 //
-// bf16/f16 kernel (gfx950 MFMA 32x32x16): workgroup tile 256 x kBNB x 64,
-// 512 threads = 8 wavefronts as 4 (M) x 2 (N), 64 x kBNB/2 per wavefront.
-// Global tiles go straight into LDS with buffer loads (buffer_load_dwordx4
-// ... lds): each lane's 16 bytes land at LDS base + 16 * lane, so the
-// swizzle is applied by choosing which global chunk each lane fetches. A
-// load past the buffer's byte count returns zeros, which covers the N tail
-// of the weights and (with a deliberately out-of-range offset) the K tail.
-// Two LDS stages; the next K-step's loads are issued before the current
-// step's MFMAs and waited for (vmcnt) just before the step's barrier.
-// Fragment registers are double-buffered across the four k16 sub-steps so
-// LDS reads for sub-step s+1 overlap the MFMAs of sub-step s.
+// bf16/f16 kernel (gfx950 MFMA 32x32x16): workgroup tile 256 x kBNB, K
+// staged 32 at a time; 512 threads = 8 wavefronts as 4 (M) x 2 (N), 64 x
+// kBNB/2 outputs per wavefront. Global tiles go straight into LDS with
+// buffer loads (buffer_load_dwordx4 ... lds): each lane's 16 bytes land at
+// LDS base + 16 * lane, so the swizzle is applied by choosing which global
+// chunk each lane fetches. A load past the buffer's byte count returns
+// zeros, which covers the N tail of the weights, A rows past the expert's
+// last row and (with a deliberately out-of-range offset) the K tail.
+// kStages (4) LDS stages: loads for k-step kt+3 are issued at the top of
+// k-step kt, and a stage is waited for (vmcnt) only just before the barrier
+// that precedes its first read. Fragment registers are double-buffered
+// across the two k16 sub-steps of a stage so LDS reads overlap MFMAs.
 //
-// LDS rows are 64 elements (eight 16-byte chunks). gfx950 serves a 128-bit
-// LDS read 16 lanes per cycle across 64 banks, so the 16 rows read together
-// must hit 16 distinct (row parity, chunk) slots: chunk c of row r is stored
-// at c ^ (r & 7) ^ ((r >> 3) & 1).
+// LDS rows are 32 elements (four 16-byte chunks). gfx950 serves a 128-bit
+// LDS read 16 lanes per cycle across 64 banks (four rows of 64 bytes), so
+// the 16 rows read together must cover all 16 (row mod 4, chunk) slots:
+// chunk c of row r is stored at c ^ ((r >> 2) & 3).
+//
+// Split-K (GEMM 2, when the M x N tiles alone cannot fill the chip): k_splits
+// workgroups per output tile each cover one K range and write fp32 partials;
+// a separate pass (or the combine) sums them in split order, so results do
+// not depend on scheduling.
 //
 // In GEMM 1 the B tile holds 128 gate rows and the same 128 up rows, and
 // every wavefront owns matching gate and up accumulators, so SiLU(g) * u is
