@@ -5,12 +5,23 @@
 // Weights are [E, N, K] with K contiguous, like the rows of X, so both MFMA
 // operands are read along K.
 //
-// Tile list. The rows of expert e are offsets[e]..offsets[e+1]-1 (device
-// data). A one-block plan kernel cuts every expert into M-tiles of BM rows and
-// writes (expert, first row) per tile plus the tile count; the GEMM grid is
-// sized on the host from the bound ceil(rows/BM) + min(E, rows) and
-// workgroups past the device tile count exit at once. Expert counts never
+// Schedule. The rows of expert e are offsets[e]..offsets[e+1]-1 (device
+// data). A one-block plan kernel cuts every expert into M-tiles of BM rows
+// and writes, for every workgroup of the GEMM grid, one 16-byte entry
+// (expert and K-split, first row, end row, N-tile) or "no tile". The grid is
+// sized on the host from the bound ceil(rows/BM) + min(E, rows) on the
+// M-tile count; workgroups without a tile exit at once. Expert counts never
 // travel to the host.
+//
+// Order of the schedule. The hardware deals workgroups round-robin to the 8
+// XCDs (each with its own L2), so workgroup b runs on XCD b % 8, and each XCD
+// starts its workgroups in the order b / 8. The plan gives XCD x a contiguous
+// slice of the tile list, so the ~32 workgroups resident on one XCD at a time
+// are neighbours in the list. Inside an expert the list takes groups of up to
+// 8 M-tiles, and inside such a group runs of N-tiles wide enough that one run
+// covers about 32 tiles (4 M-tiles x 8 N-tiles, 5 x 6, 1 x 32 ...): the
+// tiles resident together share their weight tiles and activation tiles
+// through that XCD's L2, and a run never mixes two experts' weights.
 //
 // bf16/f16 kernel (gfx950 MFMA 32x32x16): workgroup tile 256 x kBNB, K
 // staged 32 at a time; 512 threads = 8 wavefronts as 4 (M) x 2 (N), 64 x
@@ -38,51 +49,84 @@
 // In GEMM 1 the B tile holds 128 gate rows and the same 128 up rows, and
 // every wavefront owns matching gate and up accumulators, so SiLU(g) * u is
 // formed in registers and only h reaches memory.
-//
-// Workgroup order: the hardware deals workgroups round-robin to the 8 XCDs;
-// the kernel remaps its id so each XCD receives a contiguous range of
-// logical tiles. Logical tiles sweep groups of 8 N-tiles, M-tile by M-tile
-// inside a group, so the ~32 workgroups resident on one XCD share 8 weight
-// tiles and a few activation tiles through its L2.
 #include <algorithm>
 #include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
 
+
 namespace moe {
 namespace {
 
 constexpr int kBM = 256;      // rows per M-tile (MFMA path)
-constexpr int kBK = 32;       // K per pipeline stage
-constexpr int kChunks = kBK / 8;  // 16-byte chunks per LDS row
+constexpr int kBK = 64;       // K per LDS stage
 constexpr int kBMSimt = 64;   // rows per M-tile (fp32 path)
-constexpr int kGroupN = 8;    // N-tiles per rasterisation group
+constexpr int kXcds = 8;
+constexpr int kResident = 32;  // workgroups resident on one XCD (one per CU)
+constexpr int kGroupM = 8;     // M-tiles per schedule group
 // Third dword of a raw buffer resource on gfx9-family parts (no format, no swizzle).
 constexpr int kRsrcFlags = 0x00020000;
 constexpr uint32_t kOutOfRange = 0x80000000u;  // voffset past any buffer we build (< 2^31 bytes)
 
+// One schedule entry per workgroup: x = expert | (K-split << 16), y = first
+// row, z = end row (exclusive), w = N-tile; x < 0: no tile.
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ offsets, int E,
                                                      int rows, int bm, int max_tiles,
-                                                     int32_t* __restrict__ tiles,
-                                                     int32_t* __restrict__ tile_count) {
+                                                     int n_tiles_n, int k_splits, int grid,
+                                                     int4* __restrict__ sched) {
+  __shared__ int s_first[kMaxExperts + 1], s_lo[kMaxExperts], s_hi[kMaxExperts];
   const int e = threadIdx.x;
-  int lo = 0, n = 0;
+  int lo = 0, hi = 0, n = 0;
   if (e < E) {
     lo = max(offsets[e], 0);
-    const int hi = min(offsets[e + 1], rows);
+    hi = min(offsets[e + 1], rows);
     n = hi > lo ? (hi - lo + bm - 1) / bm : 0;
   }
   int total = 0;
   const int first = block_exclusive_scan(n, &total);
-  for (int i = 0; i < n; ++i) {
-    const int t = first + i;
-    if (t < max_tiles) {
-      tiles[2 * t] = e;
-      tiles[2 * t + 1] = lo + i * bm;
-    }
+  if (e < E) {
+    s_first[e] = first;
+    s_lo[e] = lo;
+    s_hi[e] = hi;
   }
-  if (threadIdx.x == 0) *tile_count = min(total, max_tiles);
+  if (e == 0) s_first[E] = total;
+  __syncthreads();
+  const int per_split = min(total, max_tiles) * n_tiles_n;
+  const int n_real = per_split * k_splits;
+  const int chunk = (n_real + kXcds - 1) / kXcds;
+  for (int b = threadIdx.x; b < grid; b += blockDim.x) {
+    const int slot = b / kXcds;
+    const int L = (b % kXcds) * chunk + slot;
+    int4 t = make_int4(-1, 0, 0, 0);
+    if (slot < chunk && L < n_real) {
+      const int ks = L / per_split;
+      const int idx = L - ks * per_split;
+      // expert: the last e with s_first[e] * n_tiles_n <= idx
+      int lo_e = 0, hi_e = E - 1;
+      while (lo_e < hi_e) {
+        const int mid = (lo_e + hi_e + 1) / 2;
+        if (s_first[mid] * n_tiles_n <= idx) lo_e = mid;
+        else hi_e = mid - 1;
+      }
+      const int ex = lo_e;
+      const int local = idx - s_first[ex] * n_tiles_n;
+      const int me = s_first[ex + 1] - s_first[ex];
+      const int mg = min(me, kGroupM);
+      const int ng = max(1, kResident / mg);
+      const int mgi = local / (mg * n_tiles_n);
+      const int mgw = min(mg, me - mgi * mg);
+      const int j = local - mgi * mg * n_tiles_n;
+      const int ngi = j / (mgw * ng);
+      const int w = min(ng, n_tiles_n - ngi * ng);
+      const int r = j - ngi * mgw * ng;
+      t.x = ex | (ks << 16);
+      t.y = s_lo[ex] + (mgi * mg + r / w) * bm;
+      t.z = s_hi[ex];
+      t.w = ngi * ng + r % w;
+    }
+    sched[b] = t;
+  }
 }
 
 struct GemmArgs {
@@ -94,9 +138,8 @@ struct GemmArgs {
   const void* b1;          // [E, N, K] up (GEMM 1 only)
   void* c;                 // [rows, N]
   const int32_t* offsets;  // [E+1]
-  const int32_t* tiles;    // [max_tiles][2]
-  const int32_t* tile_count;
-  int rows, N, K, max_tiles, n_tiles_n;
+  const int4* sched;       // [grid] entries written by plan_kernel
+  int rows, N, K, max_tiles, n_tiles_n, grid;
   // Split-K (GEMM 2 only): k_splits workgroups share one output tile, each
   // over k_chunk elements of K, writing fp32 partial sums to
   // partial[split][rows][N]; the caller reduces them in split order.
@@ -120,31 +163,26 @@ template <> struct Mfma<f16> {
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
-// LDS slot of 16-byte chunk c in row r is c ^ swizzle(r) (see the header comment).
-__device__ __forceinline__ int swizzle(int r) { return (r >> 2) & 3; }
-
-__host__ __device__ inline int grid_tiles(int max_tiles, int n_tiles_n, int k_splits = 1) {
-  const int groups = (n_tiles_n + kGroupN - 1) / kGroupN;
-  return (max_tiles * groups * kGroupN * k_splits + 7) / 8 * 8;
+inline int64_t grid_tiles(int64_t max_tiles, int64_t n_tiles_n, int64_t k_splits) {
+  return (max_tiles * n_tiles_n * k_splits + kXcds - 1) / kXcds * kXcds;
 }
 
-// Maps the workgroup id to (M-tile, N-tile, K-split); false if this
-// workgroup has no tile. Splits are the slowest-varying index.
-__device__ __forceinline__ bool tile_of_block(const GemmArgs& p, int& m_t, int& n_t, int& ks) {
-  const int G = gridDim.x;  // multiple of 8
-  const int bid = blockIdx.x;
-  int logical = (bid & 7) * (G >> 3) + (bid >> 3);
-  const int group_size = p.max_tiles * kGroupN;
-  const int per_split = group_size * ((p.n_tiles_n + kGroupN - 1) / kGroupN);
-  ks = logical / per_split;
-  if (ks >= p.k_splits) return false;
-  logical -= ks * per_split;
-  const int g = logical / group_size;
-  const int r = logical - g * group_size;
-  m_t = r / kGroupN;
-  n_t = g * kGroupN + (r - m_t * kGroupN);
-  if (n_t >= p.n_tiles_n) return false;
-  return m_t < *p.tile_count;
+struct Tile {
+  int e, ks, row0, row_end, n_t;
+};
+
+// Schedule entry v (wave-uniform); false past the grid or if it holds no tile.
+__device__ __forceinline__ bool tile_of_block(const GemmArgs& p, int v, Tile& t) {
+  if (v >= p.grid) return false;
+  const int4 e = p.sched[v];
+  const int x = __builtin_amdgcn_readfirstlane(e.x);
+  if (x < 0) return false;
+  t.e = x & 0xFFFF;
+  t.ks = x >> 16;
+  t.row0 = __builtin_amdgcn_readfirstlane(e.y);
+  t.row_end = __builtin_amdgcn_readfirstlane(e.z);
+  t.n_t = __builtin_amdgcn_readfirstlane(e.w);
+  return t.row0 < t.row_end;
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -170,33 +208,60 @@ __device__ __forceinline__ T* stage_buf() {
   return buf;
 }
 
+// LDS slot of 16-byte chunk c in row r is c ^ swizzle(r). A 128-bit LDS
+// read is served 16 lanes at a time, and the MFMA fragment reads of those 16
+// lanes touch 16 consecutive rows at one logical chunk, so the slots must
+// fall in 16 distinct 16-byte bank groups of the 256-byte bank window:
+//  - 64-byte rows (4 chunks): a window holds 4 rows; rows r..r+3 differ in
+//    r & 3, and (r >> 2) & 3 spreads the four 4-row groups over the chunks.
+//  - 128-byte rows (8 chunks): a window holds 2 rows; (r >> 1) & 7 gives the
+//    8 even and the 8 odd rows of a 16-row group 8 distinct chunks each.
+template <int kChunksT>
+__device__ __forceinline__ int swizzle(int r) {
+  static_assert(kChunksT == 4 || kChunksT == 8, "64- or 128-byte LDS rows");
+  return kChunksT == 4 ? (r >> 2) & 3 : (r >> 1) & 7;
+}
+
 // kWaveM: rows per wavefront, 64 (8 wavefronts, 4 x 2) or 128 (4 wavefronts,
 // 2 x 2; 256 accumulators per lane, one wavefront per SIMD).
 template <int kWaveM>
 constexpr int gemm_threads() { return 64 * (kBM / kWaveM) * 2; }
 
-template <typename T, bool kSwiGlu, int kBNB, int kStages, int kWaveM>
+// Persistent grouped GEMM. The grid holds one workgroup per CU; workgroup b
+// takes schedule entries b, b + G, b + 2G, ... (G = grid size, a multiple of
+// 8, so every entry it takes belongs to its own XCD's slice of the list).
+//
+// K is staged kBKT (64) elements at a time through two LDS stages. A stage
+// row is 128 bytes, and each buffer load instruction fills 8 rows with
+// 128-byte row segments, which move through the load path about twice as
+// fast as 64-byte ones. The loads of k-step kt+1 are issued at the top of
+// k-step kt and waited for just before the barrier that ends it.
+//
+// Between tiles: once every wavefront has finished reading LDS, the first
+// stage of the next tile is requested, and only then are the finished
+// tile's results written out, so the store traffic overlaps the next tile's
+// first loads instead of leaving the CU idle.
+template <typename T, bool kSwiGlu, int kBNB, int kBKT, int kWaveM>
 __global__ __launch_bounds__(gemm_threads<kWaveM>()) void mfma_gemm_kernel(GemmArgs p) {
   typedef typename Mfma<T>::Frag Frag;
+  constexpr int kStages = 2;
   constexpr int kWaves = (kBM / kWaveM) * 2;
   constexpr int kThreadsK = 64 * kWaves;
+  constexpr int kCh = kBKT / 8;                       // 16-byte chunks per LDS row
+  constexpr int kRowsPerInst = 64 / kCh;              // rows filled by one load instruction
+  constexpr int kSub = kBKT / 16;                     // MFMA k16 sub-steps per stage
   constexpr int kMB = kWaveM / 32;                    // 32-row blocks per wavefront
   constexpr int kNB = kBNB / 64;                      // 32-column blocks per wavefront
-  constexpr int kLoadsA = kBM * kChunks / kThreadsK;  // 16-byte chunks per thread per stage
-  constexpr int kLoadsB = kBNB * kChunks / kThreadsK;
+  constexpr int kLoadsA = kBM * kCh / kThreadsK;      // 16-byte chunks per thread per stage
+  constexpr int kLoadsB = kBNB * kCh / kThreadsK;
   constexpr int kLoads = kLoadsA + kLoadsB;
   static_assert(!kSwiGlu || kBNB == 256, "fused gate/up uses 128 + 128 B rows");
-  static_assert(kStages >= 3, "at least two stages in flight");
+  static_assert(kSub >= 2, "at least two k16 sub-steps per stage");
+  static_assert((kBNB / 2) % (kWaves * kRowsPerInst) == 0, "gate/up split between instructions");
 
-  int m_t, n_t, ks;
-  if (!tile_of_block(p, m_t, n_t, ks)) return;
-  const int e = __builtin_amdgcn_readfirstlane(p.tiles[2 * m_t]);
-  const int row0 = __builtin_amdgcn_readfirstlane(p.tiles[2 * m_t + 1]);
-  const int row_end = min(__builtin_amdgcn_readfirstlane(p.offsets[e + 1]), p.rows);
-  const int mrows = min(kBM, row_end - row0);
-  if (mrows <= 0) return;
-  const int k_begin = ks * p.k_chunk;
-  const int k_end = min(p.K, k_begin + p.k_chunk);
+  int v = blockIdx.x;
+  Tile tile;
+  if (!tile_of_block(p, v, tile)) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -206,58 +271,63 @@ __global__ __launch_bounds__(gemm_threads<kWaveM>()) void mfma_gemm_kernel(GemmA
   const int K = p.K;
   const int N = p.N;
   const uint32_t row_bytes = (uint32_t)K * sizeof(T);
-
   const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<void*>(p.a), (short)0, (int)((uint32_t)p.a_rows * row_bytes), kRsrcFlags);
-  const int64_t expert_elems = (int64_t)e * N * K;
   const int b_bytes = (int)((uint32_t)N * row_bytes);
-  const __amdgpu_buffer_rsrc_t rsrc_b0 = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<T*>(static_cast<const T*>(p.b0) + expert_elems), (short)0, b_bytes, kRsrcFlags);
-  const __amdgpu_buffer_rsrc_t rsrc_b1 = kSwiGlu
-      ? __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(static_cast<const T*>(p.b1) + expert_elems),
-                                          (short)0, b_bytes, kRsrcFlags)
-      : rsrc_b0;
 
   // Copy assignment: instruction j of wavefront w fills LDS chunks
-  // (j*kWaves + w)*64 + lane, i.e. row (j*kWaves + w)*16 + lane/4, slot lane%4.
-  uint32_t vo_a[kLoadsA], vo_b[kLoadsB];
-  int kc_a[kLoadsA], kc_b[kLoadsB];  // element offset of the chunk within the stage
-#pragma unroll
-  for (int j = 0; j < kLoadsA; ++j) {
-    const int r = (j * kWaves + wave) * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ swizzle(r);
-    const int grow = row0 + min(r, mrows - 1);
-    const int src = p.a_map ? min(max(p.a_map[grow] / p.a_div, 0), p.a_rows - 1) : grow;
-    // rows past the expert's last row are not fetched (they read as zero)
-    vo_a[j] = r < mrows ? (uint32_t)src * row_bytes + (uint32_t)c * 16u : kOutOfRange;
-    kc_a[j] = c * 8;
-  }
-#pragma unroll
-  for (int j = 0; j < kLoadsB; ++j) {
-    const int r = (j * kWaves + wave) * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ swizzle(r);
-    // rows past N fall beyond the buffer and read as zero
-    const int n = kSwiGlu ? n_t * (kBNB / 2) + (r & (kBNB / 2 - 1)) : n_t * kBNB + r;
-    vo_b[j] = (uint32_t)n * row_bytes + (uint32_t)c * 16u;
-    kc_b[j] = c * 8;
-  }
+  // (j*kWaves + w)*64 + lane, i.e. row (j*kWaves + w)*kRowsPerInst +
+  // lane/kCh, slot lane%kCh; the lane fetches the global chunk that the
+  // swizzle puts in that slot. The slot's chunk is the same for every j.
+  const int c_lane = (lane % kCh) ^ swizzle<kCh>(wave * kRowsPerInst + lane / kCh);
+  const int kc = c_lane * 8;  // element offset of this lane's chunk within a stage
 
-  auto issue_loads = [&](int kt, T* la, T* lb) {
-    const int k0 = k_begin + kt * kBK;
-    const uint32_t soff = (uint32_t)k0 * sizeof(T);
+  // Per-tile load state.
+  __amdgpu_buffer_rsrc_t rsrc_b0, rsrc_b1;
+  uint32_t vo_a[kLoadsA], vo_b[kLoadsB];
+  int e, ks, row0, n_t, mrows, k_begin, k_end;
+  auto setup = [&](const Tile& t) {
+    e = t.e; ks = t.ks; row0 = t.row0; n_t = t.n_t;
+    mrows = min(kBM, t.row_end - row0);
+    k_begin = ks * p.k_chunk;
+    k_end = min(K, k_begin + p.k_chunk);
+    const int64_t expert_elems = (int64_t)e * N * K;
+    rsrc_b0 = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T*>(static_cast<const T*>(p.b0) + expert_elems), (short)0, b_bytes, kRsrcFlags);
+    rsrc_b1 = kSwiGlu
+        ? __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(static_cast<const T*>(p.b1) + expert_elems),
+                                            (short)0, b_bytes, kRsrcFlags)
+        : rsrc_b0;
 #pragma unroll
     for (int j = 0; j < kLoadsA; ++j) {
-      const uint32_t vo = (k0 + kc_a[j] < k_end) ? vo_a[j] : kOutOfRange;
-      load_lds16(rsrc_a, la + (j * kWaves + wave) * 64 * 8, vo, soff);
+      const int r = (j * kWaves + wave) * kRowsPerInst + lane / kCh;
+      const int grow = row0 + min(r, mrows - 1);
+      const int src = p.a_map ? min(max(p.a_map[grow] / p.a_div, 0), p.a_rows - 1) : grow;
+      // rows past the expert's last row are not fetched (they read as zero)
+      vo_a[j] = r < mrows ? (uint32_t)src * row_bytes + (uint32_t)c_lane * 16u : kOutOfRange;
     }
 #pragma unroll
     for (int j = 0; j < kLoadsB; ++j) {
-      const uint32_t vo = (k0 + kc_b[j] < k_end) ? vo_b[j] : kOutOfRange;
-      // fused gate/up: B rows 0..127 come from gate, 128..255 from up; the
-      // split falls between instructions (row (j*kWaves + w)*16, w < kWaves)
-      load_lds16(kSwiGlu && j * kWaves * 16 >= kBNB / 2 ? rsrc_b1 : rsrc_b0,
-                 lb + (j * kWaves + wave) * 64 * 8, vo, soff);
+      const int r = (j * kWaves + wave) * kRowsPerInst + lane / kCh;
+      // rows past N fall beyond the buffer and read as zero
+      const int n = kSwiGlu ? n_t * (kBNB / 2) + (r & (kBNB / 2 - 1)) : n_t * kBNB + r;
+      vo_b[j] = (uint32_t)n * row_bytes + (uint32_t)c_lane * 16u;
     }
+  };
+
+  auto issue_loads = [&](int kt, T* la, T* lb) {
+    const int k0 = k_begin + kt * kBKT;
+    const uint32_t soff = (uint32_t)k0 * sizeof(T);
+    const bool in_k = k0 + kc < k_end;
+#pragma unroll
+    for (int j = 0; j < kLoadsA; ++j)
+      load_lds16(rsrc_a, la + (j * kWaves + wave) * 64 * 8, in_k ? vo_a[j] : kOutOfRange, soff);
+#pragma unroll
+    for (int j = 0; j < kLoadsB; ++j)
+      // fused gate/up: B rows 0..127 come from gate, 128..255 from up; the
+      // split falls between instructions
+      load_lds16(kSwiGlu && j * kWaves * kRowsPerInst >= kBNB / 2 ? rsrc_b1 : rsrc_b0,
+                 lb + (j * kWaves + wave) * 64 * 8, in_k ? vo_b[j] : kOutOfRange, soff);
   };
 
   // Fragment rows of this wavefront (MFMA A: lane holds row lane%32; B: lane
@@ -265,23 +335,16 @@ __global__ __launch_bounds__(gemm_threads<kWaveM>()) void mfma_gemm_kernel(GemmA
   // 32, so every fragment row has the same swizzle as row lane%32.
   int a_row[kMB], b_row[kNB];
 #pragma unroll
-  for (int mb = 0; mb < kMB; ++mb) a_row[mb] = (wm * kWaveM + mb * 32 + (lane & 31)) * kBK;
+  for (int mb = 0; mb < kMB; ++mb) a_row[mb] = (wm * kWaveM + mb * 32 + (lane & 31)) * kBKT;
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) {
     const int r = kSwiGlu ? (nb >> 1) * (kBNB / 2) + wn * 64 + (nb & 1) * 32 + (lane & 31)
                           : wn * (kBNB / 2) + nb * 32 + (lane & 31);
-    b_row[nb] = r * kBK;
+    b_row[nb] = r * kBKT;
   }
-  const int sw = swizzle(lane & 31);
+  const int sw = swizzle<kCh>(lane & 31);
 
   f32x16 acc[kMB][kNB];
-#pragma unroll
-  for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < kNB; ++nb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
-
   Frag fa[2][kMB], fb[2][kNB];
   auto read_frags = [&](const T* la, const T* lb, int s, int slot) {
     const int c = ((2 * s + (lane >> 5)) ^ sw) * 8;
@@ -290,134 +353,146 @@ __global__ __launch_bounds__(gemm_threads<kWaveM>()) void mfma_gemm_kernel(GemmA
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) fb[slot][nb] = *reinterpret_cast<const Frag*>(lb + b_row[nb] + c);
   };
-
-  const int nk = (k_end - k_begin + kBK - 1) / kBK;
-  constexpr int kMfma = kMB * kNB;  // MFMAs per k16 sub-step
+  auto mfmas = [&](int slot, int from, int to) {
+#pragma unroll
+    for (int i = from; i < to; ++i)
+      acc[i / kNB][i % kNB] = Mfma<T>::run(fa[slot][i / kNB], fb[slot][i % kNB], acc[i / kNB][i % kNB]);
+  };
+  constexpr int kMfma = kMB * kNB;   // MFMAs per k16 sub-step
   constexpr int kReads = kMB + kNB;  // fragment reads per sub-step
 
-  // One K-stage: compute from stage S while stage S-1 (read in the previous
-  // step) is refilled for k-step kt + kStages - 1. Stages kt+1 .. kt+kStages-1
-  // are in flight; before the barrier only the oldest (kt+1) must have landed,
-  // so the wait is vmcnt((kStages-2) * loads). The barrier is a plain
-  // s_barrier (a scheduling boundary): a fenced __syncthreads would make the
-  // compiler drain every LDS-DMA load in flight.
-  // Order: [loads, sub-step 0 MFMAs interleaved with sub-step 1 fragment
-  // reads, half of sub-step 1] barrier [next stage's sub-step 0 fragment
-  // reads overlapping the other half of sub-step 1].
-  // A wavefront whose rows all lie past the expert's last row (short
-  // M-tiles) runs the same loads and barriers without reads or MFMAs.
-  auto step = [&](auto stage, auto compute, int kt) {
+  // One K-stage: compute from stage S while the other stage is refilled for
+  // k-step kt+1 (none after the tile's last padded step). The barrier is a
+  // plain s_barrier (a scheduling boundary): a fenced __syncthreads would
+  // make the compiler drain every LDS-DMA load in flight.
+  // Order: [loads, sub-step s MFMAs interleaved with sub-step s+1 fragment
+  // reads ..., half of the last sub-step] wait + barrier [next stage's
+  // sub-step 0 fragment reads overlapping the other half of the last
+  // sub-step]. A wavefront whose rows all lie past the expert's last row
+  // (short M-tiles) runs the same loads and barriers without reads or MFMAs.
+  auto step = [&](auto stage, auto compute, int kt, int nk_pad) {
     constexpr int S = decltype(stage)::value;
     constexpr bool kCompute = decltype(compute)::value;
-    constexpr int F = (S + kStages - 1) % kStages;
-    constexpr int X = (S + 1) % kStages;
-    T* ca = stage_buf<T, kBM * kBK, 0, S>();
-    T* cb = stage_buf<T, kBNB * kBK, 1, S>();
-    issue_loads(kt + kStages - 1, stage_buf<T, kBM * kBK, 0, F>(), stage_buf<T, kBNB * kBK, 1, F>());
+    constexpr int X = S ^ 1;
+    T* ca = stage_buf<T, kBM * kBKT, 0, S>();
+    T* cb = stage_buf<T, kBNB * kBKT, 1, S>();
+    if (kt + 1 < nk_pad) issue_loads(kt + 1, stage_buf<T, kBM * kBKT, 0, X>(), stage_buf<T, kBNB * kBKT, 1, X>());
     if constexpr (!kCompute) {
-      wait_vmem<(kStages - 2) * kLoads>();
+      wait_vmem<0>();
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       return;
     }
-    read_frags(ca, cb, 1, 1);
 #pragma unroll
-    for (int mb = 0; mb < kMB; ++mb)
+    for (int sub = 0; sub + 1 < kSub; ++sub) {
+      read_frags(ca, cb, sub + 1, (sub + 1) & 1);
+      mfmas(sub & 1, 0, kMfma);
 #pragma unroll
-      for (int nb = 0; nb < kNB; ++nb)
-        acc[mb][nb] = Mfma<T>::run(fa[0][mb], fb[0][nb], acc[mb][nb]);
-#pragma unroll
-    for (int i = 0; i < kMfma / 2; ++i)
-      acc[i / kNB][i % kNB] = Mfma<T>::run(fa[1][i / kNB], fb[1][i % kNB], acc[i / kNB][i % kNB]);
-#pragma unroll
-    for (int i = 0; i < kMfma; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i < kLoads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      if (i < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      for (int i = 0; i < kMfma; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (sub == 0 && i < kLoads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        if (i < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
     }
+    constexpr int kLast = (kSub - 1) & 1;
+    mfmas(kLast, 0, kMfma / 2);
     __builtin_amdgcn_sched_group_barrier(0x008, kMfma / 2, 0);
-    wait_vmem<(kStages - 2) * kLoads>();
+    // MFMAs are not memory operations and would otherwise drift across the
+    // barrier, leaving too few of them to cover the next stage's reads.
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmem<0>();
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    read_frags(stage_buf<T, kBM * kBK, 0, X>(), stage_buf<T, kBNB * kBK, 1, X>(), 0, 0);
-#pragma unroll
-    for (int i = kMfma / 2; i < kMfma; ++i)
-      acc[i / kNB][i % kNB] = Mfma<T>::run(fa[1][i / kNB], fb[1][i % kNB], acc[i / kNB][i % kNB]);
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(stage_buf<T, kBM * kBKT, 0, X>(), stage_buf<T, kBNB * kBKT, 1, X>(), 0, 0);
+    mfmas(kLast, kMfma / 2, kMfma);
 #pragma unroll
     for (int i = 0; i < kReads; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       if (i < kMfma / 2) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
   };
-
-  // Prologue: stages 0 .. kStages-2 in flight, wait for stage 0.
-  issue_loads(0, stage_buf<T, kBM * kBK, 0, 0>(), stage_buf<T, kBNB * kBK, 1, 0>());
-  issue_loads(1, stage_buf<T, kBM * kBK, 0, 1>(), stage_buf<T, kBNB * kBK, 1, 1>());
-  if constexpr (kStages > 3)
-    issue_loads(2, stage_buf<T, kBM * kBK, 0, 2 % kStages>(), stage_buf<T, kBNB * kBK, 1, 2 % kStages>());
-  if constexpr (kStages > 4)
-    issue_loads(3, stage_buf<T, kBM * kBK, 0, 3 % kStages>(), stage_buf<T, kBNB * kBK, 1, 3 % kStages>());
-  wait_vmem<(kStages - 2) * kLoads>();
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-
-  // Main loop, unrolled by kStages so every LDS pointer is a fixed object.
-  // The trip count is padded to a multiple of kStages: loads past K are
-  // masked to zeros, so the padding steps add nothing to the accumulators,
-  // and the body stays one straight-line block.
-  const int nk_pad = (nk + kStages - 1) / kStages * kStages;
-  auto main_loop = [&](auto compute) {
+  // Main loop over one tile, unrolled by the two stages so every LDS pointer
+  // is a fixed object. The trip count is padded to an even number: loads
+  // past K are masked to zeros, so a padding step adds nothing.
+  auto main_loop = [&](auto compute, int nk_pad) {
     if constexpr (decltype(compute)::value)
-      read_frags(stage_buf<T, kBM * kBK, 0, 0>(), stage_buf<T, kBNB * kBK, 1, 0>(), 0, 0);
-    for (int kt = 0; kt < nk_pad; kt += kStages) {
-      step(std::integral_constant<int, 0>{}, compute, kt);
-      step(std::integral_constant<int, 1>{}, compute, kt + 1);
-      step(std::integral_constant<int, 2 % kStages>{}, compute, kt + 2);
-      if constexpr (kStages > 3) step(std::integral_constant<int, 3 % kStages>{}, compute, kt + 3);
-      if constexpr (kStages > 4) step(std::integral_constant<int, 4 % kStages>{}, compute, kt + 4);
+      read_frags(stage_buf<T, kBM * kBKT, 0, 0>(), stage_buf<T, kBNB * kBKT, 1, 0>(), 0, 0);
+    for (int kt = 0; kt < nk_pad; kt += 2) {
+      step(std::integral_constant<int, 0>{}, compute, kt, nk_pad);
+      step(std::integral_constant<int, 1>{}, compute, kt + 1, nk_pad);
     }
   };
-  const bool has_rows = wm * kWaveM < mrows;
-  if (has_rows)
-    main_loop(std::true_type{});
-  else
-    main_loop(std::false_type{});
-  if (!has_rows) return;
 
-  // Epilogue. Accumulator element v of lane l sits at row
-  // (v/4)*8 + (l/32)*4 + v%4 and column l%32 of its 32x32 block.
+  setup(tile);
+  issue_loads(0, stage_buf<T, kBM * kBKT, 0, 0>(), stage_buf<T, kBNB * kBKT, 1, 0>());
   T* C = static_cast<T*>(p.c);
   const int col_lane = lane & 31;
   const int row_lane = (lane >> 5) * 4;
-  if (kSwiGlu) {
+  for (;;) {
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int col = n_t * (kBNB / 2) + wn * 64 + nb * 32 + col_lane;
+      for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int lrow = wm * kWaveM + mb * 32 + (v >> 2) * 8 + row_lane + (v & 3);
-          if (lrow < mrows && col < N)
-            C[(int64_t)(row0 + lrow) * N + col] =
-                from_f32<T>(silu(acc[mb][nb][v]) * acc[mb][nb + 2][v]);
-        }
-      }
-  } else {
+        for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
+    const int nk = (k_end - k_begin + kBKT - 1) / kBKT;
+    const int nk_pad = (nk + 1) & ~1;
+    // stage 0 of this tile has been requested; wait for it
+    wait_vmem<0>();
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const bool has_rows = wm * kWaveM < mrows;
+    if (has_rows)
+      main_loop(std::true_type{}, nk_pad);
+    else
+      main_loop(std::false_type{}, nk_pad);
+    // Every wavefront is done with LDS before the next tile's loads land.
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const int t_row0 = row0, t_mrows = mrows, t_nt = n_t, t_ks = ks;
+    v += gridDim.x;
+    Tile next;
+    const bool more = tile_of_block(p, v, next);
+    if (more) {
+      setup(next);
+      issue_loads(0, stage_buf<T, kBM * kBKT, 0, 0>(), stage_buf<T, kBNB * kBKT, 1, 0>());
+    }
+
+    // Epilogue. Accumulator element i of lane l sits at row
+    // (i/4)*8 + (l/32)*4 + i%4 and column l%32 of its 32x32 block.
+    if (has_rows) {
+      if (kSwiGlu) {
 #pragma unroll
-    for (int mb = 0; mb < kMB; ++mb)
+        for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < kNB; ++nb) {
-        const int col = n_t * kBNB + wn * (kBNB / 2) + nb * 32 + col_lane;
+          for (int nb = 0; nb < 2; ++nb) {
+            const int col = t_nt * (kBNB / 2) + wn * 64 + nb * 32 + col_lane;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int lrow = wm * kWaveM + mb * 32 + (v >> 2) * 8 + row_lane + (v & 3);
-          if (lrow < mrows && col < N) {
-            const int64_t at = (int64_t)(row0 + lrow) * N + col;
-            if (p.partial)
-              p.partial[(int64_t)ks * p.rows * N + at] = acc[mb][nb][v];
-            else
-              C[at] = from_f32<T>(acc[mb][nb][v]);
+            for (int i = 0; i < 16; ++i) {
+              const int lrow = wm * kWaveM + mb * 32 + (i >> 2) * 8 + row_lane + (i & 3);
+              if (lrow < t_mrows && col < N)
+                C[(int64_t)(t_row0 + lrow) * N + col] =
+                    from_f32<T>(silu(acc[mb][nb][i]) * acc[mb][nb + 2][i]);
+            }
           }
-        }
+      } else {
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < kNB; ++nb) {
+            const int col = t_nt * kBNB + wn * (kBNB / 2) + nb * 32 + col_lane;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int lrow = wm * kWaveM + mb * 32 + (i >> 2) * 8 + row_lane + (i & 3);
+              if (lrow < t_mrows && col < N) {
+                const int64_t at = (int64_t)(t_row0 + lrow) * N + col;
+                if (p.partial)
+                  p.partial[(int64_t)t_ks * p.rows * N + at] = acc[mb][nb][i];
+                else
+                  C[at] = from_f32<T>(acc[mb][nb][i]);
+              }
+            }
+          }
       }
+    }
+    if (!more) break;
   }
 }
 
@@ -599,12 +674,10 @@ __global__ __launch_bounds__(256) void simt_gemm_kernel(GemmArgs p) {
   __shared__ float sa[BK][kBMSimt + 4];
   __shared__ float sb[BK][BNB + 4];
 
-  int m_t, n_t, ks;
-  if (!tile_of_block(p, m_t, n_t, ks)) return;
-  const int e = p.tiles[2 * m_t];
-  const int row0 = p.tiles[2 * m_t + 1];
-  const int mrows = min(kBMSimt, min(p.offsets[e + 1], p.rows) - row0);
-  if (mrows <= 0) return;
+  Tile tile;
+  if (!tile_of_block(p, blockIdx.x, tile)) return;
+  const int e = tile.e, row0 = tile.row0, n_t = tile.n_t;
+  const int mrows = min(kBMSimt, tile.row_end - row0);
   const int K = p.K, N = p.N, tid = threadIdx.x;
   const int ty = tid / 16, tx = tid % 16;
   const float* A = static_cast<const float*>(p.a);
@@ -683,14 +756,20 @@ __global__ __launch_bounds__(256) void simt_gemm_kernel(GemmArgs p) {
 }  // namespace
 
 constexpr int kCUs = 256;
-// Pipeline depth (LDS stages of 32 KB for 256-row B tiles); a build-time knob.
-#ifndef MOE_GEMM_STAGES
-#define MOE_GEMM_STAGES 4
+
+#ifndef MOE_GEMM_WAVE_M
+#define MOE_GEMM_WAVE_M 64
 #endif
-constexpr int kStagesGemm = MOE_GEMM_STAGES;
-constexpr int kWaveMGemm = 64;
+constexpr int kWaveMGemm = MOE_GEMM_WAVE_M;
 
 static size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+
+// N-tile width of each GEMM kernel: 128 h columns (256 gate + up weight rows)
+// or 256 output columns on the MFMA path, 64 on the fp32 path.
+static int64_t tile_n(int64_t N, int dt, bool swiglu) {
+  const int64_t w = dt == kF32 ? 64 : (swiglu ? 128 : 256);
+  return (N + w - 1) / w;
+}
 
 // Split-K of the down GEMM: when its output tiles would give the 256 CUs
 // fewer than four workgroups each, K is split so the last round of
@@ -711,11 +790,14 @@ ExpertsPlan experts_plan(int64_t rows, int64_t E, int64_t H, int64_t I, int dt) 
     }
     p.k_chunk = (int)((ksteps + p.splits - 1) / p.splits * kBK);
   }
+  const int64_t n_gate_up = tile_n(I, dt, true), n_down = tile_n(H, dt, false);
+  p.sched_entries = std::max(grid_tiles(p.max_tiles, n_gate_up, 1),
+                             grid_tiles(p.max_tiles, n_down, p.splits));
   return p;
 }
 
 static size_t tile_list_bytes(const ExpertsPlan& p) {
-  return align256((size_t)p.max_tiles * 2 * sizeof(int32_t)) + 256;
+  return align256((size_t)p.sched_entries * sizeof(int4));
 }
 
 size_t gemm_scratch_bytes(int64_t rows, int64_t E, int64_t H, int64_t I, int dt) {
@@ -764,24 +846,17 @@ __global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restr
   o.store(out + at);
 }
 
-// Carves the tile list (and split-K partials) out of `scratch` and enqueues
-// the plan kernel.
-GemmArgs plan_tiles(const ExpertsPlan& plan, const int32_t* offsets, int rows, int E,
-                    void* scratch, hipStream_t s) {
-  char* ws = static_cast<char*>(scratch);
-  GemmArgs g = {};
-  int32_t* tiles = reinterpret_cast<int32_t*>(ws);
-  int32_t* tile_count = reinterpret_cast<int32_t*>(ws + align256((size_t)plan.max_tiles * 2 * sizeof(int32_t)));
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, offsets, E, rows, plan.bm,
-                     plan.max_tiles, tiles, tile_count);
-  g.offsets = offsets;
-  g.tiles = tiles;
-  g.tile_count = tile_count;
-  g.rows = rows;
+// Carves the schedule out of `scratch` and enqueues the plan kernel for the
+// GEMM described by g (N, k_splits already set).
+void plan_tiles(GemmArgs& g, const ExpertsPlan& plan, int E, int dt, bool swiglu, void* scratch,
+                hipStream_t s) {
   g.max_tiles = plan.max_tiles;
-  g.k_splits = 1;
-  g.partial = nullptr;
-  return g;
+  g.n_tiles_n = (int)tile_n(g.N, dt, swiglu);
+  g.grid = (int)grid_tiles(plan.max_tiles, g.n_tiles_n, g.k_splits);
+  int4* sched = static_cast<int4*>(scratch);
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, g.offsets, E, g.rows, plan.bm,
+                     plan.max_tiles, g.n_tiles_n, g.k_splits, g.grid, sched);
+  g.sched = sched;
 }
 
 float* partial_buffer(const ExpertsPlan& plan, void* scratch) {
@@ -789,27 +864,36 @@ float* partial_buffer(const ExpertsPlan& plan, void* scratch) {
                          : nullptr;
 }
 
-template <typename T>
-void launch_mfma(GemmArgs g, bool swiglu, hipStream_t s) {
-  if (swiglu) {
-    g.n_tiles_n = (g.N + 127) / 128;
-    hipLaunchKernelGGL((mfma_gemm_kernel<T, true, 256, kStagesGemm, kWaveMGemm>),
-                       dim3(grid_tiles(g.max_tiles, g.n_tiles_n)),
-                       dim3(gemm_threads<kWaveMGemm>()), 0, s, g);
-  } else {
-    g.n_tiles_n = (g.N + 255) / 256;
-    hipLaunchKernelGGL((mfma_gemm_kernel<T, false, 256, kStagesGemm, kWaveMGemm>),
-                       dim3(grid_tiles(g.max_tiles, g.n_tiles_n, g.k_splits)),
-                       dim3(gemm_threads<kWaveMGemm>()), 0, s, g);
+// Workgroups of the persistent MFMA GEMM: one per CU (its 128 KB of LDS
+// stages leave room for no second one), at most one per schedule entry; a
+// multiple of 8 so each workgroup stays on the XCD its entries belong to.
+static int persistent_grid(int entries) {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cus[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8) n = kCUs;
+    cus[dev] = n / 8 * 8;
   }
+  return std::min(entries, cus[dev]);
+}
+
+template <typename T>
+void launch_mfma(const GemmArgs& g, bool swiglu, hipStream_t s) {
+  const dim3 grid(persistent_grid(g.grid));
+  if (swiglu)
+    hipLaunchKernelGGL((mfma_gemm_kernel<T, true, 256, kBK, kWaveMGemm>), grid,
+                       dim3(gemm_threads<kWaveMGemm>()), 0, s, g);
+  else
+    hipLaunchKernelGGL((mfma_gemm_kernel<T, false, 256, kBK, kWaveMGemm>), grid,
+                       dim3(gemm_threads<kWaveMGemm>()), 0, s, g);
 }
 
 template <bool kSwiGlu>
-void launch_gemm(GemmArgs g, int dt, hipStream_t s) {
+void launch_gemm(const GemmArgs& g, int dt, hipStream_t s) {
   if (dt == kF32) {
-    g.n_tiles_n = (g.N + 63) / 64;
-    hipLaunchKernelGGL(simt_gemm_kernel<kSwiGlu>, dim3(grid_tiles(g.max_tiles, g.n_tiles_n)),
-                       dim3(256), 0, s, g);
+    hipLaunchKernelGGL(simt_gemm_kernel<kSwiGlu>, dim3(g.grid), dim3(256), 0, s, g);
   } else if (dt == kF16) {
     launch_mfma<f16>(g, kSwiGlu, s);
   } else {
@@ -883,8 +967,10 @@ hipError_t launch_gate_up(const void* a, const int32_t* a_map, int a_div, const 
     return hipGetLastError();
   }
   const ExpertsPlan plan = experts_plan(rows, E, H, I, dt);
-  GemmArgs g = plan_tiles(plan, offsets, rows, E, scratch, s);
+  GemmArgs g = {};
+  g.offsets = offsets; g.rows = rows;
   setup_gate_up(g, a, a_map, a_div, H, I, w_gate, w_up, h);
+  plan_tiles(g, plan, E, dt, true, scratch, s);
   launch_gemm<true>(g, dt, s);
   return hipGetLastError();
 }
@@ -896,14 +982,16 @@ hipError_t launch_down(const void* h, const int32_t* offsets, int rows, int E, i
   if (use_skinny(rows, E, dt)) {
     GemmArgs g = {};
     g.offsets = offsets; g.rows = rows;
-    setup_down(g, ExpertsPlan{kBM, 0, 1, I}, nullptr, h, H, I, w_down, expert_out);
+    setup_down(g, ExpertsPlan{kBM, 0, 1, I, 0}, nullptr, h, H, I, w_down, expert_out);
     g.partial = nullptr;
     launch_skinny(g, E, dt, false, s);
     return hipGetLastError();
   }
   const ExpertsPlan plan = experts_plan(rows, E, H, I, dt);
-  GemmArgs g = plan_tiles(plan, offsets, rows, E, scratch, s);
+  GemmArgs g = {};
+  g.offsets = offsets; g.rows = rows;
   setup_down(g, plan, scratch, h, H, I, w_down, expert_out);
+  plan_tiles(g, plan, E, dt, false, scratch, s);
   launch_gemm<false>(g, dt, s);
   if (plan.splits > 1) {
     if (keep) {

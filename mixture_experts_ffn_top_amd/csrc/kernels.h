@@ -43,9 +43,10 @@ struct ExpertsPlan {
   int max_tiles;  // host upper bound of the tile count
   int splits;     // K splits of the down GEMM
   int k_chunk;    // K elements per split
+  int64_t sched_entries;  // workgroup schedule entries, the larger GEMM grid
 };
 ExpertsPlan experts_plan(int64_t rows, int64_t E, int64_t H, int64_t I, int dt);
-// Scratch of one GEMM call (tile list + split-K partials).
+// Scratch of one GEMM call (workgroup schedule + split-K partials).
 size_t gemm_scratch_bytes(int64_t rows, int64_t E, int64_t H, int64_t I, int dt);
 // Scratch of both GEMMs (the above + h).
 size_t experts_scratch_bytes(int64_t rows, int64_t E, int64_t H, int64_t I, int dt);
