@@ -161,7 +161,8 @@ template <> struct Mfma<f16> {
   }
 };
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+// SiLU with the hardware reciprocal (1 ulp) in place of a full division.
+__device__ __forceinline__ float silu(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 inline int64_t grid_tiles(int64_t max_tiles, int64_t n_tiles_n, int64_t k_splits) {
   return (max_tiles * n_tiles_n * k_splits + kXcds - 1) / kXcds * kXcds;
@@ -184,6 +185,34 @@ __device__ __forceinline__ bool tile_of_block(const GemmArgs& p, int v, Tile& t)
   t.n_t = __builtin_amdgcn_readfirstlane(e.w);
   return t.row0 < t.row_end;
 }
+
+// One butterfly round of a 4 x 4 transpose across the lanes of a quad: the
+// lane swaps with lane ^ kBit the two values whose index bit kBit differs
+// from its own lane bit, through a quad-permute DPP move.
+template <int kBit>
+__device__ __forceinline__ void transpose4_round(float (&x)[4], int lane) {
+  constexpr int kCtrl = kBit == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] or [2,3,0,1]
+  const bool hi = (lane & kBit) != 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (i & kBit) continue;
+    const float send = hi ? x[i] : x[i | kBit];
+    const float recv = __builtin_bit_cast(float,
+        __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, send), kCtrl, 0xF, 0xF, false));
+    if (hi) x[i] = recv;
+    else x[i | kBit] = recv;
+  }
+}
+
+// 4 x 4 transpose across the 4 lanes of each quad: on return x[c] of lane j
+// holds what x[j] of lane c held.
+__device__ __forceinline__ void transpose4(float (&x)[4], int lane) {
+  transpose4_round<1>(x, lane);
+  transpose4_round<2>(x, lane);
+}
+
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -244,7 +273,6 @@ constexpr int gemm_threads() { return 64 * (kBM / kWaveM) * 2; }
 template <typename T, bool kSwiGlu, int kBNB, int kBKT, int kWaveM>
 __global__ __launch_bounds__(gemm_threads<kWaveM>()) void mfma_gemm_kernel(GemmArgs p) {
   typedef typename Mfma<T>::Frag Frag;
-  constexpr int kStages = 2;
   constexpr int kWaves = (kBM / kWaveM) * 2;
   constexpr int kThreadsK = 64 * kWaves;
   constexpr int kCh = kBKT / 8;                       // 16-byte chunks per LDS row
@@ -425,8 +453,11 @@ __global__ __launch_bounds__(gemm_threads<kWaveM>()) void mfma_gemm_kernel(GemmA
   setup(tile);
   issue_loads(0, stage_buf<T, kBM * kBKT, 0, 0>(), stage_buf<T, kBNB * kBKT, 1, 0>());
   T* C = static_cast<T*>(p.c);
-  const int col_lane = lane & 31;
   const int row_lane = (lane >> 5) * 4;
+  // Epilogue stores per computing wavefront: 4 per 32x32 output block.
+  constexpr int kStores = (kSwiGlu ? kMB * 2 : kMB * kNB) * 4;
+  static_assert(kStores < 64, "vmcnt holds 6 bits");
+  int stores_prev = 0;
   for (;;) {
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb)
@@ -436,8 +467,12 @@ __global__ __launch_bounds__(gemm_threads<kWaveM>()) void mfma_gemm_kernel(GemmA
         for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
     const int nk = (k_end - k_begin + kBKT - 1) / kBKT;
     const int nk_pad = (nk + 1) & ~1;
-    // stage 0 of this tile has been requested; wait for it
-    wait_vmem<0>();
+    // Stage 0 of this tile has been requested; wait for it (not for the
+    // previous tile's stores, issued after it).
+    if (stores_prev)
+      wait_vmem<kStores>();
+    else
+      wait_vmem<0>();
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     const bool has_rows = wm * kWaveM < mrows;
     if (has_rows)
@@ -456,43 +491,74 @@ __global__ __launch_bounds__(gemm_threads<kWaveM>()) void mfma_gemm_kernel(GemmA
     }
 
     // Epilogue. Accumulator element i of lane l sits at row
-    // (i/4)*8 + (l/32)*4 + i%4 and column l%32 of its 32x32 block.
+    // (i/4)*8 + (l/32)*4 + i%4 and column l%32 of its 32x32 block. Each run
+    // of 4 rows is transposed within the quad of lanes holding 4 adjacent
+    // columns, after which lane l holds columns 4*((l%32)/4) .. +3 of one
+    // row: one 8-byte store (16 for fp32 partials) in place of four 2-byte
+    // ones. Stores go through a buffer resource covering this tile's rows,
+    // with out-of-range offsets for rows past the expert or columns past N
+    // (N is a multiple of 8, so 4 columns are all in or all out); every
+    // wavefront that computed thus issues exactly kStores stores, issued
+    // after the next tile's first loads, and the next tile waits for its
+    // loads with vmcnt(kStores) without draining the stores.
+    int stores_out = 0;
     if (has_rows) {
+      const bool part = !kSwiGlu && p.partial != nullptr;
+      const int esz = part ? 4 : (int)sizeof(T);
+      char* base = part ? reinterpret_cast<char*>(p.partial + (int64_t)t_ks * p.rows * N + (int64_t)t_row0 * N)
+                        : reinterpret_cast<char*>(C + (int64_t)t_row0 * N);
+      const __amdgpu_buffer_rsrc_t rsrc_c =
+          __builtin_amdgcn_make_buffer_rsrc(base, (short)0, t_mrows * N * esz, kRsrcFlags);
+      const int col4 = (lane & 31) & ~3;
+      auto store_block = [&](float (&val)[16], int row_base, int col_base) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float x[4] = {val[4 * g], val[4 * g + 1], val[4 * g + 2], val[4 * g + 3]};
+          transpose4(x, lane);
+          const int lrow = row_base + g * 8 + row_lane + (lane & 3);
+          const int col = col_base + col4;
+          const uint32_t vo = (lrow < t_mrows && col < N) ? (uint32_t)(lrow * N + col) * (uint32_t)esz
+                                                          : kOutOfRange;
+          if (part) {
+            const i32x4 d = {__builtin_bit_cast(int, x[0]), __builtin_bit_cast(int, x[1]),
+                             __builtin_bit_cast(int, x[2]), __builtin_bit_cast(int, x[3])};
+            __builtin_amdgcn_raw_buffer_store_b128(d, rsrc_c, vo, 0, 0);
+          } else {
+            const T h0 = from_f32<T>(x[0]), h1 = from_f32<T>(x[1]);
+            const T h2 = from_f32<T>(x[2]), h3 = from_f32<T>(x[3]);
+            const i32x2 d = {(int)((uint32_t)__builtin_bit_cast(uint16_t, h0) |
+                                   ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16)),
+                             (int)((uint32_t)__builtin_bit_cast(uint16_t, h2) |
+                                   ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16))};
+            __builtin_amdgcn_raw_buffer_store_b64(d, rsrc_c, vo, 0, 0);
+          }
+        }
+      };
       if (kSwiGlu) {
 #pragma unroll
         for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
           for (int nb = 0; nb < 2; ++nb) {
-            const int col = t_nt * (kBNB / 2) + wn * 64 + nb * 32 + col_lane;
+            float val[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int lrow = wm * kWaveM + mb * 32 + (i >> 2) * 8 + row_lane + (i & 3);
-              if (lrow < t_mrows && col < N)
-                C[(int64_t)(t_row0 + lrow) * N + col] =
-                    from_f32<T>(silu(acc[mb][nb][i]) * acc[mb][nb + 2][i]);
-            }
+            for (int i = 0; i < 16; ++i) val[i] = silu(acc[mb][nb][i]) * acc[mb][nb + 2][i];
+            store_block(val, wm * kWaveM + mb * 32, t_nt * (kBNB / 2) + wn * 64 + nb * 32);
           }
       } else {
 #pragma unroll
         for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
           for (int nb = 0; nb < kNB; ++nb) {
-            const int col = t_nt * kBNB + wn * (kBNB / 2) + nb * 32 + col_lane;
+            float val[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int lrow = wm * kWaveM + mb * 32 + (i >> 2) * 8 + row_lane + (i & 3);
-              if (lrow < t_mrows && col < N) {
-                const int64_t at = (int64_t)(t_row0 + lrow) * N + col;
-                if (p.partial)
-                  p.partial[(int64_t)t_ks * p.rows * N + at] = acc[mb][nb][i];
-                else
-                  C[at] = from_f32<T>(acc[mb][nb][i]);
-              }
-            }
+            for (int i = 0; i < 16; ++i) val[i] = acc[mb][nb][i];
+            store_block(val, wm * kWaveM + mb * 32, t_nt * kBNB + wn * (kBNB / 2) + nb * 32);
           }
       }
+      stores_out = 1;
     }
     if (!more) break;
+    stores_prev = stores_out;
   }
 }
 
