@@ -139,6 +139,108 @@ def route(logits: np.ndarray, logits_dtype: str, top_k: int, renormalize: bool):
 
 
 # --------------------------------------------------------------------------
+# grouped-limited sigmoid routing  (ruDNN user guide, "10. Grouped-limited
+# sigmoid MoE routing")
+# --------------------------------------------------------------------------
+def sigmoid_fp32(logits: np.ndarray, logits_dtype: str) -> np.ndarray:
+    """s = 1 / (1 + exp(-z)) delivered in fp32: computed in fp64 and rounded
+    once. sigmoid(+inf) = 1, sigmoid(-inf) = 0, NaN stays NaN."""
+    z = decode(logits, logits_dtype)
+    with np.errstate(over="ignore"):
+        s = 1.0 / (1.0 + np.exp(-z))
+    return s.astype(np.float32)
+
+
+def grouped_sigmoid_scores(logits, logits_dtype, bias, groups, group_top_two):
+    """The quantities the grouped router decides on, all fp32 [T, ...]:
+    s (raw sigmoid scores, [T, E]), c = s + bias (the corrected scores used
+    for selection only, one fp32 addition, [T, E]) and the group scores
+    [T, groups]: the sum of the two largest corrected scores of each group
+    (one fp32 addition of the largest and the second largest), or the
+    group's largest corrected score. Expert e belongs to group e // (E/groups)."""
+    s = sigmoid_fp32(logits, logits_dtype)
+    T, E = s.shape
+    b = np.zeros(E, np.float32) if bias is None else np.asarray(bias, np.float32)
+    c = s + b  # float32 + float32: IEEE fp32 addition
+    c = c + np.float32(0.0)  # -0 -> +0, so equal scores compare as ties
+    cg = np.sort(c.reshape(T, groups, E // groups), axis=-1)[..., ::-1]
+    if group_top_two:
+        g = cg[..., 0] + cg[..., 1]
+    else:
+        g = cg[..., 0].copy()
+    return s, c, g
+
+
+def route_sigmoid_grouped(logits, logits_dtype, bias, top_k, groups, selected_groups,
+                          group_top_two, renormalize, scale):
+    """Routing plan (indices uint32 [T, k], weights [T, k] in logits dtype).
+
+    1. s = sigmoid(z) in fp32; c = s + bias (bias [E] fp32, absent = 0).
+    2. Experts are split into `groups` equal contiguous groups; each group is
+       scored by its two largest c summed (group_top_two) or its largest c.
+    3. The `selected_groups` best groups are kept (equal scores: lower group
+       first); experts of the other groups cannot be chosen.
+    4. Among the kept experts the k largest c are chosen, largest first,
+       equal scores favouring the lower expert id.
+    5. Weights use the raw s of the chosen experts (the bias only steers the
+       choice): divided by their sum when renormalize is set, then times
+       scale, then cast to the logits dtype.
+    A row whose corrected scores contain a NaN (a NaN logit or bias) has all
+    scores tied as NaN: its indices are 0..k-1 and every weight is NaN, as
+    for the softmax router."""
+    z = decode(logits, logits_dtype)
+    T, E = z.shape
+    if not (1 <= groups <= 128 and E % groups == 0 and 1 <= E <= 1024):
+        raise ValueError("groups must divide E, 1 <= groups <= 128, 1 <= E <= 1024")
+    gs = E // groups
+    if not (1 <= selected_groups <= groups) or not (1 <= top_k <= min(64, selected_groups * gs)):
+        raise ValueError("need 1 <= selected_groups <= groups and 1 <= top_k <= min(64, selected experts)")
+    if group_top_two and gs < 2:
+        raise ValueError("group_top_two needs at least two experts per group")
+    if not (np.isfinite(scale) and scale > 0):
+        raise ValueError("scale must be finite and positive")
+    s, c, g = grouped_sigmoid_scores(logits, logits_dtype, bias, groups, group_top_two)
+    bad = np.isnan(c).any(axis=1)
+    gid = np.broadcast_to(np.arange(groups), (T, groups))
+    gorder = np.lexsort((gid, -g.astype(np.float64)), axis=-1)  # key 1: -score, key 2: group id
+    kept = np.zeros((T, groups), bool)
+    np.put_along_axis(kept, gorder[:, :selected_groups], True, axis=1)
+    masked = np.where(np.repeat(kept, gs, axis=1), c.astype(np.float64), -np.inf)
+    ids = np.broadcast_to(np.arange(E), (T, E))
+    order = np.lexsort((ids, -masked), axis=-1)
+    order[bad] = np.arange(E)
+    idx = order[:, :top_k]
+    w = np.take_along_axis(s, idx, axis=1).astype(np.float64)
+    if renormalize:
+        w = w / w.sum(axis=1, keepdims=True)
+    w = w * float(scale)
+    w[bad] = np.nan
+    return idx.astype(np.uint32), round_to(w, logits_dtype)
+
+
+def route_sigmoid_grouped_margins(logits, logits_dtype, bias, top_k, groups, selected_groups,
+                                  group_top_two):
+    """Per row, the smallest gap the grouped router's decisions rest on: between
+    the last kept and the first dropped group score, and between consecutive
+    corrected scores among the k+1 best kept experts. Rows with a margin of a
+    few fp32 ulps may legitimately differ between two fp32 implementations."""
+    s, c, g = grouped_sigmoid_scores(logits, logits_dtype, bias, groups, group_top_two)
+    T, E = c.shape
+    gs = E // groups
+    gsorted = -np.sort(-g.astype(np.float64), axis=1)
+    gm = (gsorted[:, selected_groups - 1] - gsorted[:, selected_groups]) if selected_groups < groups \
+        else np.full(T, np.inf)
+    gid = np.broadcast_to(np.arange(groups), (T, groups))
+    gorder = np.lexsort((gid, -g.astype(np.float64)), axis=-1)
+    kept = np.zeros((T, groups), bool)
+    np.put_along_axis(kept, gorder[:, :selected_groups], True, axis=1)
+    masked = np.where(np.repeat(kept, gs, axis=1), c.astype(np.float64), -np.inf)
+    top = -np.sort(-masked, axis=1)[:, :min(top_k + 1, selected_groups * gs)]
+    em = np.diff(-top, axis=1).min(axis=1) if top.shape[1] > 1 else np.full(T, np.inf)
+    return np.minimum(gm, em)
+
+
+# --------------------------------------------------------------------------
 # dispatch  (ruDNN user guide, "5. Expert weights and dispatch")
 # --------------------------------------------------------------------------
 def dispatch(indices: np.ndarray, E: int, x: np.ndarray | None = None):

@@ -405,3 +405,134 @@ def test_rmsnorm_nan_weights_propagate_to_row_only():
                                          np.zeros((T, H), np.float32), np.ones(H, np.float32), 1e-6, T, k, "f32")
     assert np.isnan(yo[1]).all() and np.isnan(rstd[1])
     assert np.isfinite(yo[[0, 2]]).all()
+
+
+# --------------------------------------------------------------------------
+# grouped-limited sigmoid routing (ruDNN user guide, "10. Grouped-limited
+# sigmoid MoE routing")
+# --------------------------------------------------------------------------
+def _sig(z):
+    return torch.sigmoid(torch.tensor(z, dtype=torch.float64)).float().numpy()
+
+
+def test_grouped_sigmoid_one_group_is_topk_of_sigmoid():
+    """One group holding every expert: selection is the plain top-k of the
+    sigmoid scores (torch.topk on torch.sigmoid); weights are those scores,
+    divided by their sum when renormalised, times scale."""
+    rng = np.random.default_rng(11)
+    z = rng.standard_normal((64, 48)).astype(np.float32)
+    for renorm, scale in ((True, 2.5), (False, 1.0)):
+        idx, w = O.route_sigmoid_grouped(z, "f32", None, 6, 1, 1, False, renorm, scale)
+        s = _sig(z)
+        ref_w, ref_i = torch.topk(torch.tensor(s), 6, dim=1)
+        np.testing.assert_array_equal(idx, ref_i.numpy())
+        rw = ref_w.double().numpy()
+        if renorm:
+            rw = rw / rw.sum(axis=1, keepdims=True)
+        np.testing.assert_allclose(w, rw * scale, rtol=2e-7, atol=0)
+
+
+def test_grouped_sigmoid_bias_steers_choice_not_weight():
+    """With one group, selection is the top-k of sigmoid + bias (torch.topk on
+    the corrected scores) while the weights stay the uncorrected sigmoid."""
+    rng = np.random.default_rng(12)
+    z = rng.standard_normal((32, 40)).astype(np.float32)
+    bias = (rng.standard_normal(40) * 0.3).astype(np.float32)
+    idx, w = O.route_sigmoid_grouped(z, "f32", bias, 5, 1, 1, False, False, 1.0)
+    s = _sig(z)
+    _, ref_i = torch.topk(torch.tensor(s) + torch.tensor(bias), 5, dim=1)
+    np.testing.assert_array_equal(idx, ref_i.numpy())
+    np.testing.assert_array_equal(w, np.take_along_axis(s, idx.astype(np.int64), axis=1))
+    # the bias really changes the choice on these rows
+    plain, _ = O.route_sigmoid_grouped(z, "f32", None, 5, 1, 1, False, False, 1.0)
+    assert (plain != idx).any()
+
+
+def test_grouped_sigmoid_all_ties_closed_form():
+    """All logits 0, no bias: every score is 1/2 and every group ties, so the
+    lowest groups and the lowest ids win; weights are 1/k (renormalised) or
+    1/2, times scale."""
+    z = np.zeros((3, 8), np.float32)
+    idx, w = O.route_sigmoid_grouped(z, "f32", None, 3, 4, 2, True, True, 3.0)
+    np.testing.assert_array_equal(idx, np.tile([0, 1, 2], (3, 1)))
+    np.testing.assert_array_equal(w, np.full((3, 3), np.float32(1.0)))
+    idx, w = O.route_sigmoid_grouped(z, "f32", None, 3, 4, 2, True, False, 3.0)
+    np.testing.assert_array_equal(w, np.full((3, 3), np.float32(1.5)))
+
+
+def test_grouped_sigmoid_group_score_definitions():
+    """Hand-built row where the two group scores disagree. Group 0 = experts
+    {0, 1} with z = (3, -3): top-two sum sigmoid(3)+sigmoid(-3) = 1, max 0.9526.
+    Group 1 = {2, 3} with z = (2, 2): sum 1.7616, max 0.8808. Others z = -5.
+    Keeping one group, the sum picks group 1 (expert 2, the lower of a tie),
+    the max picks group 0 (expert 0)."""
+    z = np.array([[3, -3, 2, 2, -5, -5, -5, -5]], np.float32)
+    i2, w2 = O.route_sigmoid_grouped(z, "f32", None, 1, 4, 1, True, True, 1.0)
+    i1, _ = O.route_sigmoid_grouped(z, "f32", None, 1, 4, 1, False, True, 1.0)
+    assert i2.tolist() == [[2]] and i1.tolist() == [[0]]
+    assert w2.tolist() == [[1.0]]
+    # k = 2 inside the kept group: the tied pair, lower id first
+    i, w = O.route_sigmoid_grouped(z, "f32", None, 2, 4, 1, True, False, 1.0)
+    assert i.tolist() == [[2, 3]]
+    np.testing.assert_allclose(w, [[1 / (1 + np.exp(-2.0))] * 2], rtol=1e-7)
+
+
+def test_grouped_sigmoid_group_boundary_tie_goes_to_lower_group():
+    """Groups 1 and 3 tie for the last kept slot (equal logits); group 0 is
+    best. The lower of the tied groups (1) is kept."""
+    z = np.array([[4, 4, 1, 1, -3, -3, 1, 1]], np.float32)
+    idx, _ = O.route_sigmoid_grouped(z, "f32", None, 4, 4, 2, True, True, 1.0)
+    assert idx.tolist() == [[0, 1, 2, 3]]
+
+
+def test_grouped_sigmoid_invariants_random():
+    """On random rows: the kept groups are the best by group score (checked by
+    an independent sort), every chosen expert lies in a kept group, no
+    unchosen kept expert beats a chosen one, weights are proportional to the
+    sigmoid and sum to scale when renormalised."""
+    rng = np.random.default_rng(13)
+    T, E, G, SG, k = 200, 64, 8, 3, 7
+    z = rng.standard_normal((T, E)).astype(np.float32)
+    bias = (rng.standard_normal(E) * 0.1).astype(np.float32)
+    idx, w = O.route_sigmoid_grouped(z, "f32", bias, k, G, SG, True, True, 1.7)
+    s = _sig(z)
+    c = (s + bias).astype(np.float32)
+    gs = E // G
+    for t in range(T):
+        top2 = [np.sort(c[t, g * gs:(g + 1) * gs])[-2:].sum(dtype=np.float32) for g in range(G)]
+        kept = sorted(range(G), key=lambda g: (-top2[g], g))[:SG]
+        chosen = idx[t].astype(int)
+        assert all(e // gs in kept for e in chosen)
+        pool = [e for e in range(E) if e // gs in kept and e not in chosen]
+        assert max(c[t, pool]) <= min(c[t, chosen])
+        assert list(c[t, chosen]) == sorted(c[t, chosen], reverse=True)
+        np.testing.assert_allclose(w[t], s[t, chosen] / s[t, chosen].astype(np.float64).sum() * 1.7,
+                                   rtol=1e-6)
+        assert abs(w[t].astype(np.float64).sum() - 1.7) < 1e-5
+
+
+def test_grouped_sigmoid_special_values():
+    """A NaN logit makes its row's scores NaN: ids 0..k-1, NaN weights; other
+    rows are untouched. +inf and -inf are ordinary inputs (scores 1 and 0)."""
+    z = np.zeros((3, 8), np.float32)
+    z[0, 5] = np.nan
+    z[1, 6] = np.inf
+    z[2, :] = -np.inf
+    z[2, 3] = 0.0
+    idx, w = O.route_sigmoid_grouped(z, "f32", None, 2, 4, 2, True, False, 1.0)
+    assert idx[0].tolist() == [0, 1] and np.isnan(w[0]).all()
+    assert idx[1, 0] == 6 and w[1, 0] == 1.0
+    assert idx[2, 0] == 3 and w[2, 0] == 0.5 and w[2, 1] == 0.0
+
+
+def test_grouped_sigmoid_argument_checks():
+    z = np.zeros((1, 12), np.float32)
+    bad = [dict(groups=5), dict(groups=0), dict(selected_groups=0), dict(selected_groups=5),
+           dict(top_k=7, selected_groups=2), dict(top_k=0), dict(scale=0.0), dict(scale=np.inf),
+           dict(groups=12, group_top_two=True)]
+    for b in bad:
+        a = dict(top_k=2, groups=4, selected_groups=2, group_top_two=True, renormalize=True, scale=1.0)
+        a.update(b)
+        with pytest.raises(ValueError):
+            O.route_sigmoid_grouped(z, "f32", None, a["top_k"], a["groups"], a["selected_groups"],
+                                    a["group_top_two"], a["renormalize"], a["scale"])
