@@ -39,15 +39,15 @@ BOUND = {"tiny_fp32": "alu", "mixtral_8x_bf16": "mfma", "many_expert_zipf_bf16":
 
 
 def kernel_source_hash() -> str:
-    """sha256/16 over the HIP sources, in name order: counters taken on other
-    sources no longer describe the kernels."""
+    """sha256/16 over the sources the profiled kernels are compiled from (the
+    GEMM and combine kernels and their device helpers): counters taken on
+    other sources no longer describe the kernels."""
     import hashlib
     d = os.path.join(ROOT, "mixture_experts_ffn_top_amd", "csrc")
     h = hashlib.sha256()
-    for n in sorted(os.listdir(d)):
-        if n.endswith((".hip", ".h")):
-            h.update(n.encode())
-            h.update(open(os.path.join(d, n), "rb").read())
+    for n in ("combine.hip", "common.h", "gemm.hip"):
+        h.update(n.encode())
+        h.update(open(os.path.join(d, n), "rb").read())
     return h.hexdigest()[:16]
 
 

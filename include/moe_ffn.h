@@ -196,6 +196,55 @@ size_t moe_forward_workspace_size(int64_t T, int64_t H, int64_t I, int64_t E, in
                                   moe_dtype dt, moe_dtype logits_dt);
 
 /*
+ * moe_route_sigmoid_grouped - grouped-limited sigmoid routing with an
+ * optional correction bias.
+ * Passage: ruDNN user guide, "10. Grouped-limited sigmoid MoE routing"
+ * (route_sigmoid_grouped and GroupRoutingOptions).
+ *   logits   [T, E], dtype logits_dt (F32, F16 or BF16), read only.
+ *   bias     [E] fp32 correction bias, read only; NULL = no bias.
+ *   For each token: s = sigmoid(z) in fp32 and c = s + bias. The E experts
+ *   form `groups` equal contiguous groups (expert e in group e / (E/groups));
+ *   a group's score is the sum of its two largest c when group_top_two != 0,
+ *   else its largest c. The `selected_groups` best groups are kept (equal
+ *   scores: lower group first); among their experts the top_k largest c are
+ *   selected, largest first, equal c favouring the lower id. The bias only
+ *   steers the selection: weights are the selected s, divided by their sum
+ *   when renormalize != 0, then multiplied by scale and converted to
+ *   logits_dt. A row whose c contains a NaN gets indices 0..top_k-1 and NaN
+ *   weights (the convention of moe_route).
+ *   indices  [T, top_k] uint32, written.  weights [T, top_k] logits_dt, written.
+ * Errors: ARGUMENT unless 1 <= groups <= 128, groups divides E,
+ *   1 <= selected_groups <= groups, 1 <= top_k <= min(64, selected_groups *
+ *   E / groups), E / groups >= 2 when group_top_two, scale finite and > 0;
+ *   UNSUPPORTED if E > 1024.
+ */
+moe_status moe_route_sigmoid_grouped(const void* logits, moe_dtype logits_dt, int64_t T, int64_t E,
+                                     const float* bias, int64_t top_k, int64_t groups,
+                                     int64_t selected_groups, int group_top_two, int renormalize,
+                                     float scale, uint32_t* indices, void* weights,
+                                     hipStream_t stream);
+
+/*
+ * moe_forward_sigmoid_grouped - moe_forward with the grouped-limited sigmoid
+ * router of moe_route_sigmoid_grouped in place of the softmax router.
+ * Passage: ruDNN user guide, "10. Grouped-limited sigmoid MoE routing"
+ * (SwiGluExperts::forward_sigmoid_grouped: routing, dispatch, experts and
+ * combine in one call; shared experts and residuals stay with the caller).
+ *   Arguments as in moe_forward, plus bias / groups / selected_groups /
+ *   group_top_two / scale as in moe_route_sigmoid_grouped (same checks).
+ *   Workspace: moe_forward_workspace_size(T, H, I, E, top_k, dt, logits_dt).
+ */
+moe_status moe_forward_sigmoid_grouped(const void* x, const void* logits, moe_dtype logits_dt,
+                                       int64_t T, int64_t H, int64_t I, int64_t E,
+                                       const float* bias, int64_t top_k, int64_t groups,
+                                       int64_t selected_groups, int group_top_two,
+                                       int renormalize, float scale, const void* w_gate,
+                                       const void* w_up, const void* w_down, moe_dtype dt,
+                                       void* out, uint32_t* indices_out, void* weights_out,
+                                       void* ws, size_t ws_bytes, hipEvent_t* stage_events,
+                                       hipStream_t stream);
+
+/*
  * moe_combine_add_rmsnorm - combine fused with the shared-expert term, the
  * residual Add and RMSNorm.
  * Passages: aclnnMoeDistributeCombineAddRmsNormV2, "function description"

@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include "kernels.h"
+#include <cmath>
 #include "moe_ffn.h"
 
 using namespace moe;
@@ -77,6 +78,34 @@ moe_status check_route_args(int64_t T, int64_t E, int64_t top_k, moe_dtype logit
 }
 
 bool row_len_ok(int64_t n) { return n > 0 && n % 8 == 0; }
+
+// Options of the grouped-limited sigmoid router (ruDNN user guide, "10.
+// Grouped-limited sigmoid MoE routing"), validated after check_route_args.
+moe_status check_grouped_args(int64_t E, int64_t top_k, int64_t groups, int64_t selected_groups,
+                              int group_top_two, float scale) {
+  if (groups < 1 || groups > 128 || E % groups != 0) return MOE_ERROR_ARGUMENT;
+  if (selected_groups < 1 || selected_groups > groups) return MOE_ERROR_ARGUMENT;
+  const int64_t gs = E / groups;
+  if (top_k > 64 || top_k > selected_groups * gs) return MOE_ERROR_ARGUMENT;
+  if (group_top_two && gs < 2) return MOE_ERROR_ARGUMENT;
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return MOE_ERROR_ARGUMENT;
+  return MOE_SUCCESS;
+}
+
+// Routing step of a forward pass: writes indices [T,k] and weights [T,k].
+struct Router {
+  bool grouped = false;
+  int renormalize = 0;
+  const float* bias = nullptr;
+  int groups = 1, selected_groups = 1, group_top_two = 0;
+  float scale = 1.0f;
+  hipError_t run(const void* logits, int logits_dt, int T, int E, int k, uint32_t* idx, void* w,
+                 hipStream_t s) const {
+    return grouped ? launch_route_grouped(logits, logits_dt, bias, T, E, k, groups, selected_groups,
+                                          group_top_two, renormalize, scale, idx, w, s)
+                   : launch_route(logits, logits_dt, T, E, k, renormalize, idx, w, s);
+  }
+};
 
 // Layout of the moe_forward workspace; every piece 256-byte aligned.
 struct ForwardLayout {
@@ -316,14 +345,17 @@ size_t moe_forward_workspace_size(int64_t T, int64_t H, int64_t I, int64_t E, in
   return forward_layout(T, H, I, E, top_k, dt, logits_dt).total;
 }
 
-moe_status moe_forward(const void* x, const void* logits, moe_dtype logits_dt, int64_t T,
-                       int64_t H, int64_t I, int64_t E, int64_t top_k, int renormalize,
-                       const void* w_gate, const void* w_up, const void* w_down, moe_dtype dt,
-                       void* out, uint32_t* indices_out, void* weights_out, void* ws,
-                       size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+moe_status forward_impl(const void* x, const void* logits, moe_dtype logits_dt, int64_t T,
+                        int64_t H, int64_t I, int64_t E, int64_t top_k, const Router& router,
+                        const void* w_gate, const void* w_up, const void* w_down, moe_dtype dt,
+                        void* out, uint32_t* indices_out, void* weights_out, void* ws,
+                        size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream) {
   if (H < 1 || I < 1) return MOE_ERROR_SHAPE;
-  moe_status st = check_route_args(T, E, top_k, logits_dt);
-  if (st != MOE_SUCCESS) return st;
+  moe_status st = MOE_SUCCESS;
   if (!valid_dt(dt)) return MOE_ERROR_DTYPE;
   if (!row_len_ok(H) || !row_len_ok(I)) return MOE_ERROR_UNSUPPORTED;
   if (T == 0) return MOE_SUCCESS;
@@ -336,9 +368,10 @@ moe_status moe_forward(const void* x, const void* logits, moe_dtype logits_dt, i
                        {weights_out, weights_out ? slots * ls : 0}, {ws, L.total}};
   const Span ins[] = {{x, (size_t)T * (size_t)H * ds}, {logits, (size_t)(T * E) * ls},
                       {w_gate, wbytes}, {w_up, wbytes}, {w_down, wbytes}};
-  if (any_overlap(outs, 4, ins, 5)) return MOE_ERROR_ARGUMENT;
-  const void* ptrs[] = {x, logits, w_gate, w_up, w_down, out, indices_out, weights_out, ws};
-  if ((st = check_device(ptrs, 9, stream)) != MOE_SUCCESS) return st;
+  const Span bias_in[] = {{router.bias, router.bias ? (size_t)E * 4 : 0}};
+  if (any_overlap(outs, 4, ins, 5) || any_overlap(outs, 4, bias_in, 1)) return MOE_ERROR_ARGUMENT;
+  const void* ptrs[] = {x, logits, w_gate, w_up, w_down, out, indices_out, weights_out, ws, router.bias};
+  if ((st = check_device(ptrs, 10, stream)) != MOE_SUCCESS) return st;
 
   char* base = static_cast<char*>(ws);
   uint32_t* idx = indices_out ? indices_out : reinterpret_cast<uint32_t*>(base + L.indices);
@@ -352,9 +385,7 @@ moe_status moe_forward(const void* x, const void* logits, moe_dtype logits_dt, i
     return stage_events ? hipEventRecord(stage_events[i], stream) : hipSuccess;
   };
   hipError_t e = mark(0);
-  if (e == hipSuccess)
-    e = launch_route(logits, logits_dt, (int)T, (int)E, (int)top_k, renormalize ? 1 : 0, idx, w,
-                     stream);
+  if (e == hipSuccess) e = router.run(logits, logits_dt, (int)T, (int)E, (int)top_k, idx, w, stream);
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess)
     e = launch_dispatch_maps(idx, (int)slots, (int)E, offsets, sor, ros,
@@ -381,6 +412,72 @@ moe_status moe_forward(const void* x, const void* logits, moe_dtype logits_dt, i
             : launch_combine(y, ros, w, logits_dt, (int)T, (int)top_k, (int)H, dt, out, stream);
   if (e == hipSuccess) e = mark(5);
   return from_hip(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_forward(const void* x, const void* logits, moe_dtype logits_dt, int64_t T,
+                       int64_t H, int64_t I, int64_t E, int64_t top_k, int renormalize,
+                       const void* w_gate, const void* w_up, const void* w_down, moe_dtype dt,
+                       void* out, uint32_t* indices_out, void* weights_out, void* ws,
+                       size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream) {
+  if (H < 1 || I < 1) return MOE_ERROR_SHAPE;
+  const moe_status st = check_route_args(T, E, top_k, logits_dt);
+  if (st != MOE_SUCCESS) return st;
+  Router r;
+  r.renormalize = renormalize ? 1 : 0;
+  return forward_impl(x, logits, logits_dt, T, H, I, E, top_k, r, w_gate, w_up, w_down, dt, out,
+                      indices_out, weights_out, ws, ws_bytes, stage_events, stream);
+}
+
+moe_status moe_route_sigmoid_grouped(const void* logits, moe_dtype logits_dt, int64_t T, int64_t E,
+                                     const float* bias, int64_t top_k, int64_t groups,
+                                     int64_t selected_groups, int group_top_two, int renormalize,
+                                     float scale, uint32_t* indices, void* weights,
+                                     hipStream_t stream) {
+  moe_status st = check_route_args(T, E, top_k, logits_dt);
+  if (st != MOE_SUCCESS) return st;
+  if ((st = check_grouped_args(E, top_k, groups, selected_groups, group_top_two, scale)) != MOE_SUCCESS)
+    return st;
+  if (T == 0) return MOE_SUCCESS;
+  if (!logits || !indices || !weights) return MOE_ERROR_NULL_POINTER;
+  const size_t ls = dtype_size(logits_dt);
+  const Span outs[] = {{indices, (size_t)(T * top_k) * 4}, {weights, (size_t)(T * top_k) * ls}};
+  const Span ins[] = {{logits, (size_t)(T * E) * ls}, {bias, bias ? (size_t)E * 4 : 0}};
+  if (any_overlap(outs, 2, ins, 2)) return MOE_ERROR_ARGUMENT;
+  const void* ptrs[] = {logits, indices, weights, bias};
+  if ((st = check_device(ptrs, 4, stream)) != MOE_SUCCESS) return st;
+  return from_hip(launch_route_grouped(logits, logits_dt, bias, (int)T, (int)E, (int)top_k,
+                                       (int)groups, (int)selected_groups, group_top_two ? 1 : 0,
+                                       renormalize ? 1 : 0, scale, indices, weights, stream));
+}
+
+moe_status moe_forward_sigmoid_grouped(const void* x, const void* logits, moe_dtype logits_dt,
+                                       int64_t T, int64_t H, int64_t I, int64_t E,
+                                       const float* bias, int64_t top_k, int64_t groups,
+                                       int64_t selected_groups, int group_top_two,
+                                       int renormalize, float scale, const void* w_gate,
+                                       const void* w_up, const void* w_down, moe_dtype dt,
+                                       void* out, uint32_t* indices_out, void* weights_out,
+                                       void* ws, size_t ws_bytes, hipEvent_t* stage_events,
+                                       hipStream_t stream) {
+  if (H < 1 || I < 1) return MOE_ERROR_SHAPE;
+  moe_status st = check_route_args(T, E, top_k, logits_dt);
+  if (st != MOE_SUCCESS) return st;
+  if ((st = check_grouped_args(E, top_k, groups, selected_groups, group_top_two, scale)) != MOE_SUCCESS)
+    return st;
+  Router r;
+  r.grouped = true;
+  r.renormalize = renormalize ? 1 : 0;
+  r.bias = bias;
+  r.groups = (int)groups;
+  r.selected_groups = (int)selected_groups;
+  r.group_top_two = group_top_two ? 1 : 0;
+  r.scale = scale;
+  return forward_impl(x, logits, logits_dt, T, H, I, E, top_k, r, w_gate, w_up, w_down, dt, out,
+                      indices_out, weights_out, ws, ws_bytes, stage_events, stream);
 }
 
 }  // extern "C"

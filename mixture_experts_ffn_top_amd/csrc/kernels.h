@@ -16,6 +16,10 @@ inline size_t dtype_size(int dt) { return dt == kF32 ? 4 : 2; }
 // ---- routing ----------------------------------------------------------------
 hipError_t launch_route(const void* logits, int logits_dt, int T, int E, int k, int renorm,
                         uint32_t* indices, void* weights, hipStream_t s);
+// Grouped-limited sigmoid routing; bias may be null. Arguments validated by the caller.
+hipError_t launch_route_grouped(const void* logits, int logits_dt, const float* bias, int T, int E,
+                                int k, int groups, int sel_groups, int top_two, int renorm,
+                                float scale, uint32_t* indices, void* weights, hipStream_t s);
 
 // ---- dispatch ---------------------------------------------------------------
 // Scratch: one int32 histogram row of E entries per block of slots.

@@ -169,6 +169,169 @@ hipError_t dispatch_shape(const void* logits, int T, int E, int k, int renorm, u
   return launch<LT, 64, 16>(logits, T, E, k, renorm, idx, w, s);
 }
 
+// ---------------------------------------------------------------------------
+// Grouped-limited sigmoid routing (ruDNN user guide, "10. Grouped-limited
+// sigmoid MoE routing"): s = sigmoid(z) in fp32, corrected score c = s + bias
+// (selection only), experts in `groups` equal contiguous groups, each scored
+// by the sum of its two largest c (or its largest c); the `selected_groups`
+// best groups are kept (ties: lower group), then the k largest c among their
+// experts (ties: lower id). Weights: the raw s, divided by their sum when
+// renormalising, times scale.
+//
+// One token per wavefront, kGroupedWaves tokens per block. Corrected and raw
+// scores go to LDS; group scores are reduced by 64 / P lanes per group
+// (P = groups rounded up to a power of two, at most 64; more than 64 groups
+// take two passes), then each group counts the groups ranked above it. The
+// k rounds of selection are 64-bit max-reductions over
+// (order-preserving bits of c) << 32 | ~id; experts of dropped groups and
+// padding get key 0, below every real key. A row whose corrected scores
+// contain a NaN selects ids 0..k-1 with NaN weights.
+constexpr int kGroupedWaves = 4;
+constexpr int kMaxGroups = 128;
+
+// Monotone map of an fp32 (not NaN) to uint32: a < b  <=>  ord(a) < ord(b).
+__device__ __forceinline__ uint32_t ordered_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ void top2_push(float x, float& m1, float& m2) {
+  if (x > m1) { m2 = m1; m1 = x; }
+  else if (x > m2) { m2 = x; }
+}
+
+template <typename LT, int VPL>
+__global__ __launch_bounds__(64 * kGroupedWaves) void route_grouped_kernel(
+    const LT* __restrict__ logits, const float* __restrict__ bias, int T, int E, int k, int groups,
+    int sel_groups, int top_two, int renorm, float scale, uint32_t* __restrict__ indices,
+    LT* __restrict__ weights) {
+  __shared__ float s_c[kGroupedWaves][kMaxExperts];
+  __shared__ float s_s[kGroupedWaves][kMaxExperts];
+  __shared__ float s_g[kGroupedWaves][kMaxGroups];
+  __shared__ int s_kept[kGroupedWaves][kMaxGroups];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int t = blockIdx.x * kGroupedWaves + wv;
+  const bool active = t < T;  // whole wavefronts share t
+  const int gs = E / groups;
+
+  float c_reg[VPL];
+  int nan_seen = 0;
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    const int e = lane + 64 * v;
+    c_reg[v] = 0.f;
+    if (active && e < E) {
+      const float z = to_f32(logits[(int64_t)t * E + e]);
+      const float sg = 1.0f / (1.0f + expf(-z));
+      const float c = sg + (bias ? bias[e] : 0.0f) + 0.0f;  // + 0: -0 -> +0
+      if (__builtin_isnan(c)) nan_seen = 1;
+      s_s[wv][e] = sg;
+      s_c[wv][e] = c;
+      c_reg[v] = c;
+    }
+  }
+  const bool bad = __any(nan_seen);
+  __syncthreads();
+
+  // Group scores: P = groups rounded up to a power of two (<= 64), 64 / P
+  // lanes per group, each scanning a strided share of the group.
+  int P = 1;
+  while (P < groups && P < 64) P <<= 1;
+  const int lpg = 64 / P;
+  const int sub = lane % lpg;
+  for (int pass = 0; pass * P < groups; ++pass) {
+    const int g = lane / lpg + pass * P;
+    float m1 = -INFINITY, m2 = -INFINITY;
+    if (active && g < groups)
+      for (int e = g * gs + sub; e < (g + 1) * gs; e += lpg) top2_push(s_c[wv][e], m1, m2);
+    for (int d = 1; d < lpg; d <<= 1) {
+      const float o1 = __shfl_xor(m1, d, 64);
+      const float o2 = __shfl_xor(m2, d, 64);
+      const float hi = fmaxf(m1, o1), lo = fminf(m1, o1);
+      m2 = fmaxf(lo, fmaxf(m2, o2));
+      m1 = hi;
+    }
+    if (active && g < groups && sub == 0) s_g[wv][g] = top_two ? m1 + m2 : m1;
+  }
+  __syncthreads();
+
+  // Rank of each group: groups with a larger score, or an equal score and a
+  // lower index, come first; the first sel_groups are kept.
+  for (int g = lane; g < groups; g += 64) {
+    if (!active) break;
+    const float sc = s_g[wv][g];
+    int rank = 0;
+    for (int g2 = 0; g2 < groups; ++g2) {
+      const float o = s_g[wv][g2];
+      rank += (o > sc) || (o == sc && g2 < g);
+    }
+    s_kept[wv][g] = rank < sel_groups;
+  }
+  __syncthreads();
+  if (!active) return;
+
+  uint64_t key[VPL];
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    const uint32_t e = (uint32_t)(lane + 64 * v);
+    key[v] = (e < (uint32_t)E && !bad && s_kept[wv][e / gs])
+                 ? (((uint64_t)ordered_bits(c_reg[v]) << 32) | (uint32_t)~e)
+                 : 0ull;
+  }
+  uint32_t mine_e = (uint32_t)lane;
+  float mine_s = NAN;
+  float sel_sum = 0.f;
+  if (!bad) {
+    for (int r = 0; r < k; ++r) {
+      uint64_t best = 0;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) best = key[v] > best ? key[v] : best;
+      best = group_max_u64<64>(best);
+      // best == 0 cannot happen for validated arguments (k <= kept experts);
+      // the clamp keeps the LDS read in bounds regardless.
+      const uint32_t eb = best ? ~(uint32_t)best : 0u;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v)
+        if ((uint32_t)(lane + 64 * v) == eb) key[v] = 0ull;
+      const float sb = s_s[wv][eb];
+      if (lane == r) { mine_e = eb; mine_s = sb; }
+      sel_sum += sb;  // same order in every lane
+    }
+  }
+  if (lane < k) {
+    float wv_out = mine_s;
+    if (!bad) {
+      if (renorm) wv_out = wv_out / sel_sum;
+      wv_out = wv_out * scale;
+    }
+    indices[(int64_t)t * k + lane] = mine_e;
+    weights[(int64_t)t * k + lane] = from_f32<LT>(wv_out);
+  }
+}
+
+template <typename LT, int VPL>
+hipError_t launch_grouped(const void* logits, const float* bias, int T, int E, int k, int groups,
+                          int sel_groups, int top_two, int renorm, float scale, uint32_t* idx,
+                          void* w, hipStream_t s) {
+  const int blocks = (T + kGroupedWaves - 1) / kGroupedWaves;
+  hipLaunchKernelGGL((route_grouped_kernel<LT, VPL>), dim3(blocks), dim3(64 * kGroupedWaves), 0, s,
+                     static_cast<const LT*>(logits), bias, T, E, k, groups, sel_groups, top_two,
+                     renorm, scale, idx, static_cast<LT*>(w));
+  return hipGetLastError();
+}
+
+template <typename LT>
+hipError_t grouped_shape(const void* logits, const float* bias, int T, int E, int k, int groups,
+                         int sel_groups, int top_two, int renorm, float scale, uint32_t* idx,
+                         void* w, hipStream_t s) {
+  if (E <= 64) return launch_grouped<LT, 1>(logits, bias, T, E, k, groups, sel_groups, top_two, renorm, scale, idx, w, s);
+  if (E <= 128) return launch_grouped<LT, 2>(logits, bias, T, E, k, groups, sel_groups, top_two, renorm, scale, idx, w, s);
+  if (E <= 256) return launch_grouped<LT, 4>(logits, bias, T, E, k, groups, sel_groups, top_two, renorm, scale, idx, w, s);
+  if (E <= 512) return launch_grouped<LT, 8>(logits, bias, T, E, k, groups, sel_groups, top_two, renorm, scale, idx, w, s);
+  return launch_grouped<LT, 16>(logits, bias, T, E, k, groups, sel_groups, top_two, renorm, scale, idx, w, s);
+}
+
 }  // namespace
 
 hipError_t launch_route(const void* logits, int logits_dt, int T, int E, int k, int renorm,
@@ -177,6 +340,17 @@ hipError_t launch_route(const void* logits, int logits_dt, int T, int E, int k, 
     case kF32: return dispatch_shape<float>(logits, T, E, k, renorm, indices, weights, s);
     case kF16: return dispatch_shape<f16>(logits, T, E, k, renorm, indices, weights, s);
     default: return dispatch_shape<bf16>(logits, T, E, k, renorm, indices, weights, s);
+  }
+}
+
+hipError_t launch_route_grouped(const void* logits, int logits_dt, const float* bias, int T, int E,
+                                int k, int groups, int sel_groups, int top_two, int renorm,
+                                float scale, uint32_t* indices, void* weights, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  switch (logits_dt) {
+    case kF32: return grouped_shape<float>(logits, bias, T, E, k, groups, sel_groups, top_two, renorm, scale, indices, weights, s);
+    case kF16: return grouped_shape<f16>(logits, bias, T, E, k, groups, sel_groups, top_two, renorm, scale, indices, weights, s);
+    default: return grouped_shape<bf16>(logits, bias, T, E, k, groups, sel_groups, top_two, renorm, scale, indices, weights, s);
   }
 }
 

@@ -47,6 +47,10 @@ _SIGS = {
     "moe_combine": ([P, P, P, I32, I64, I64, I64, I32, P, P], I32),
     "moe_forward": ([P, P, I32, I64, I64, I64, I64, I64, I32, P, P, P, I32, P, P, P, P, SZ, P, P], I32),
     "moe_forward_workspace_size": ([I64, I64, I64, I64, I64, I32, I32], SZ),
+    "moe_route_sigmoid_grouped": ([P, I32, I64, I64, P, I64, I64, I64, I32, I32, ctypes.c_float, P, P, P],
+                                  I32),
+    "moe_forward_sigmoid_grouped": ([P, P, I32, I64, I64, I64, I64, P, I64, I64, I64, I32, I32,
+                                     ctypes.c_float, P, P, P, I32, P, P, P, P, SZ, P, P], I32),
     "moe_combine_add_rmsnorm": ([P, P, P, I32, P, P, P, ctypes.c_float, I64, I64, I64, I32, P, P,
                                  P, P], I32),
 }
@@ -215,6 +219,48 @@ def moe_forward(x, logits, top_k: int, renormalize: bool, w_gate, w_up, w_down, 
                              int(renormalize), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
                              dtype_code(x.dtype), _ptr(out), _ptr(indices_out), _ptr(weights_out),
                              _ptr(ws), ws.numel(), ev, _stream()), "moe_forward")
+    return out
+
+
+def moe_route_sigmoid_grouped(logits, top_k: int, groups: int, selected_groups: int,
+                              group_top_two: bool, renormalize: bool, scale: float, bias=None,
+                              indices=None, weights=None):
+    """Grouped-limited sigmoid routing; bias: optional fp32 [E].
+    Returns (indices uint32 [T,k] as int32 storage, weights [T,k] logits dtype)."""
+    T, E = logits.shape
+    if indices is None:
+        indices = torch.empty((T, top_k), dtype=torch.int32, device=logits.device)
+    if weights is None:
+        weights = torch.empty((T, top_k), dtype=logits.dtype, device=logits.device)
+    _check(lib().moe_route_sigmoid_grouped(_ptr(logits), dtype_code(logits.dtype), T, E, _ptr(bias),
+                                           top_k, groups, selected_groups, int(group_top_two),
+                                           int(renormalize), float(scale), _ptr(indices),
+                                           _ptr(weights), _stream()), "moe_route_sigmoid_grouped")
+    return indices, weights
+
+
+def moe_forward_sigmoid_grouped(x, logits, top_k: int, groups: int, selected_groups: int,
+                                group_top_two: bool, renormalize: bool, scale: float, w_gate, w_up,
+                                w_down, bias=None, out=None, indices_out=None, weights_out=None,
+                                ws=None, stage_events=None):
+    """moe_forward with the grouped-limited sigmoid router."""
+    T, H = x.shape
+    E = logits.shape[1]
+    I = w_gate.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=x.dtype, device=x.device)
+    if ws is None:
+        ws = _workspace(moe_forward_workspace_size(T, H, I, E, top_k, x.dtype, logits.dtype), x.device)
+    ev = None
+    if stage_events is not None:
+        if len(stage_events) != 6:
+            raise ValueError("stage_events needs 6 events")
+        ev = (ctypes.c_void_p * 6)(*[_event_handle(e) for e in stage_events])
+    _check(lib().moe_forward_sigmoid_grouped(
+        _ptr(x), _ptr(logits), dtype_code(logits.dtype), T, H, I, E, _ptr(bias), top_k, groups,
+        selected_groups, int(group_top_two), int(renormalize), float(scale), _ptr(w_gate),
+        _ptr(w_up), _ptr(w_down), dtype_code(x.dtype), _ptr(out), _ptr(indices_out),
+        _ptr(weights_out), _ptr(ws), ws.numel(), ev, _stream()), "moe_forward_sigmoid_grouped")
     return out
 
 

@@ -212,7 +212,8 @@ def route_sigmoid_grouped(logits, logits_dtype, bias, top_k, groups, selected_gr
     idx = order[:, :top_k]
     w = np.take_along_axis(s, idx, axis=1).astype(np.float64)
     if renormalize:
-        w = w / w.sum(axis=1, keepdims=True)
+        with np.errstate(invalid="ignore"):  # NaN rows, overwritten below
+            w = w / w.sum(axis=1, keepdims=True)
     w = w * float(scale)
     w[bad] = np.nan
     return idx.astype(np.uint32), round_to(w, logits_dtype)
@@ -359,6 +360,21 @@ def combine_add_rmsnorm(expert_out, row_of_slot, weights, w_dtype, shared, resid
 # --------------------------------------------------------------------------
 def forward(x, logits, logits_dtype, top_k, renormalize, weights_of, E, dtype):
     idx, w = route(logits, logits_dtype, top_k, renormalize)
+    d = dispatch(idx, E, x)
+    T = x.shape[0]
+    y = experts_forward_dispatched(d["x_disp"], d["offsets"], weights_of, dtype)
+    if y is None:
+        return idx, w, d, None, round_to(np.zeros((T, x.shape[1])), dtype)
+    return idx, w, d, y, combine(y, d["row_of_slot"], w, logits_dtype, T, top_k, dtype)
+
+
+def forward_sigmoid_grouped(x, logits, logits_dtype, bias, top_k, groups, selected_groups,
+                            group_top_two, renormalize, scale, weights_of, E, dtype):
+    """SwiGluExperts::forward_sigmoid_grouped (ruDNN user guide, "10. Grouped-
+    limited sigmoid MoE routing"): the grouped sigmoid routing plan, then the
+    same dispatch, experts and combine as forward()."""
+    idx, w = route_sigmoid_grouped(logits, logits_dtype, bias, top_k, groups, selected_groups,
+                                   group_top_two, renormalize, scale)
     d = dispatch(idx, E, x)
     T = x.shape[0]
     y = experts_forward_dispatched(d["x_disp"], d["offsets"], weights_of, dtype)

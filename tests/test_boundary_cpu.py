@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     lib = moe.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -150,6 +150,48 @@ def test_forward_validation_and_workspace_query():
     assert call(0, None) == S["MOE_ERROR_NULL_POINTER"]
     assert call(3, 0) == S["MOE_SUCCESS"]
     assert call(13, FAKE + 64) == S["MOE_ERROR_ARGUMENT"]  # out overlaps x
+
+
+def test_grouped_route_validation():
+    f = moe.lib().moe_route_sigmoid_grouped
+    # logits, dt, T, E, bias, k, groups, selected, top_two, renorm, scale, idx, w, stream
+    base = [FAKE, 0, 4, 256, None, 8, 8, 4, 1, 1, 2.5, FAKE + 2**20, FAKE + 2**21, None]
+
+    def call(**kw):
+        a = list(base)
+        names = ["logits", "dt", "T", "E", "bias", "k", "groups", "sel", "two", "renorm", "scale"]
+        for n, v in kw.items():
+            a[names.index(n)] = v
+        return f(*a)
+
+    assert call(groups=3) == S["MOE_ERROR_ARGUMENT"]        # does not divide E
+    assert call(groups=256) == S["MOE_ERROR_ARGUMENT"]      # more than 128 groups
+    assert call(groups=0) == S["MOE_ERROR_ARGUMENT"]
+    assert call(sel=0) == S["MOE_ERROR_ARGUMENT"]
+    assert call(sel=9) == S["MOE_ERROR_ARGUMENT"]
+    assert call(k=65) == S["MOE_ERROR_ARGUMENT"]            # more than 64
+    assert call(k=33, sel=1) == S["MOE_ERROR_ARGUMENT"]     # more than the kept experts
+    assert call(E=128, groups=128, k=4) == S["MOE_ERROR_ARGUMENT"]  # top-two with one expert a group
+    for sc in (0.0, -1.0, float("inf"), float("nan")):
+        assert call(scale=sc) == S["MOE_ERROR_ARGUMENT"], sc
+    assert call(E=2048, groups=8) == S["MOE_ERROR_UNSUPPORTED"]
+    assert call(dt=7) == S["MOE_ERROR_DTYPE"]
+    assert call(logits=None) == S["MOE_ERROR_NULL_POINTER"]
+    assert call(T=0, logits=None) == S["MOE_SUCCESS"]
+    assert call(bias=FAKE + 2**20 + 8) == S["MOE_ERROR_ARGUMENT"]  # bias overlaps indices
+    g = moe.lib().moe_forward_sigmoid_grouped
+    q = moe.lib().moe_forward_workspace_size(64, 128, 256, 16, 4, 2, 0)
+    fb = [FAKE, FAKE + 2**20, 0, 64, 128, 256, 16, None, 4, 4, 2, 1, 1, 1.0, FAKE + 2**21,
+          FAKE + 2**22, FAKE + 2**23, 2, FAKE + 2**24, None, None, FAKE + 2**26, q, None, None]
+    a = list(fb)
+    a[9] = 5  # groups must divide E = 16
+    assert g(*a) == S["MOE_ERROR_ARGUMENT"]
+    a = list(fb)
+    a[13] = 0.0
+    assert g(*a) == S["MOE_ERROR_ARGUMENT"]
+    a = list(fb)
+    a[3] = 0
+    assert g(*a) == S["MOE_SUCCESS"]
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

@@ -429,3 +429,132 @@ def test_workload_with_rmsnorm_epilogue_full_size():
     assert_close(host(xo)[sample], xr, w.dtype, "x_out")
     assert_close(host(yo)[sample], yr, w.dtype, "y")
     assert_close(host(rs)[sample], rr, "f32", "rstd")
+
+
+# --------------------------------------------- grouped-limited sigmoid routing --
+# (E, groups, selected_groups, top_k, group_top_two)
+GROUPED_CASES = [(256, 8, 4, 8, True), (256, 8, 4, 8, False), (64, 8, 3, 6, True),
+                 (64, 1, 1, 6, False), (128, 128, 16, 8, False), (1024, 128, 32, 64, True),
+                 (96, 3, 2, 5, True), (8, 4, 2, 3, True), (1000, 100, 10, 17, True), (2, 1, 1, 2, True)]
+MARGIN = 1e-6  # decisions resting on a smaller gap (~10 fp32 ulps) may differ between two fp32 implementations
+
+
+def _check_grouped(z, ldt, bias, k, G, SG, two, renorm, scale, what, robust_only=True):
+    idx_r, w_r = O.route_sigmoid_grouped(z, ldt, bias, k, G, SG, two, renorm, scale)
+    idx, w = moe.moe_route_sigmoid_grouped(dev(z, ldt), k, G, SG, two, renorm, scale,
+                                           bias=None if bias is None else dev(bias, "f32"))
+    torch.cuda.synchronize()
+    idx, w = host(idx).astype(np.uint32), host(w)
+    rows = np.ones(z.shape[0], bool)
+    if robust_only:
+        margin = O.route_sigmoid_grouped_margins(z, ldt, bias, k, G, SG, two)
+        rows = ~(margin < MARGIN)
+        assert rows.mean() > 0.95, f"{what}: too many near-tie rows ({(~rows).sum()})"
+    assert np.array_equal(idx[rows], idx_r[rows]), f"{what}: indices"
+    assert_close(w[rows], w_r[rows], ldt, f"{what}: weights")
+    return rows
+
+
+@pytest.mark.parametrize("E,G,SG,k,two", GROUPED_CASES)
+def test_route_grouped_random(E, G, SG, k, two):
+    say("route grouped", E, G, SG, k, two)
+    g = np.random.default_rng(E * 7 + G)
+    z = g.standard_normal((300, E)).astype(np.float32)
+    bias = (g.standard_normal(E) * 0.05).astype(np.float32)
+    for b, renorm, scale in ((bias, True, 2.5), (None, False, 1.0), (bias, False, 0.75)):
+        _check_grouped(z, "f32", b, k, G, SG, two, renorm, scale, f"E={E} G={G} k={k}")
+
+
+@pytest.mark.parametrize("ldt", ["bf16", "f16"])
+def test_route_grouped_half_logits(ldt):
+    g = np.random.default_rng(5)
+    z = O.round_to(g.standard_normal((400, 256)), ldt)
+    bias = (g.standard_normal(256) * 0.05).astype(np.float32)
+    _check_grouped(z, ldt, bias, 8, 8, 4, True, True, 2.5, ldt)
+
+
+def test_route_grouped_ties_and_special_rows():
+    """Exact ties (equal logits give equal scores on both sides) and the
+    NaN / +inf / -inf rows are compared on every row."""
+    g = np.random.default_rng(9)
+    E = 64
+    z = (g.integers(-3, 4, size=(256, E)) * 0.5).astype(np.float32)
+    z[0] = 0.0
+    z[1, 5] = np.nan
+    z[2, 63] = np.inf
+    z[3] = -np.inf
+    z[4, 0] = np.inf
+    z[4, 40] = np.inf
+    for renorm in (True, False):
+        # max group score: group ties only between equal maxima (equal logits)
+        _check_grouped(z, "f32", None, 6, 8, 3, False, renorm, 1.0, "ties", robust_only=False)
+    idx, w = moe.moe_route_sigmoid_grouped(dev(z, "f32"), 6, 8, 3, True, True, 1.0)
+    torch.cuda.synchronize()
+    assert host(idx)[1].tolist() == list(range(6)) and np.isnan(host(w)[1]).all()
+
+
+def test_route_grouped_dsv3_shape_full():
+    """DeepSeek-V3-shaped routing at full batch: 2048 tokens, 256 experts in 8
+    groups, 4 groups kept, top-8, top-two group scores, bias, scale 2.5."""
+    g = np.random.default_rng(33)
+    z = g.standard_normal((2048, 256)).astype(np.float32)
+    bias = (g.standard_normal(256) * 0.05).astype(np.float32)
+    _check_grouped(z, "f32", bias, 8, 8, 4, True, True, 2.5, "dsv3 shape")
+
+
+def test_forward_sigmoid_grouped_small():
+    T, E, H, I_, k, G, SG = 200, 32, 256, 128, 4, 4, 2
+    g = np.random.default_rng(21)
+    x = _store(g.standard_normal((T, H)), "bf16")
+    z = g.standard_normal((T, E)).astype(np.float32)
+    bias = (g.standard_normal(E) * 0.05).astype(np.float32)
+    wg, wu, wd = _random_experts(g, E, H, I_, "bf16")
+    idx_r, w_r, _, _, out_r = O.forward_sigmoid_grouped(x, z, "f32", bias, k, G, SG, True, True, 2.5,
+                                                        lambda e: (wg[e], wu[e], wd[e]), E, "bf16")
+    rows = ~(O.route_sigmoid_grouped_margins(z, "f32", bias, k, G, SG, True) < MARGIN)
+    assert rows.mean() > 0.95
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    out = moe.moe_forward_sigmoid_grouped(dev(x, "bf16"), dev(z, "f32"), k, G, SG, True, True, 2.5,
+                                          dev(wg, "bf16"), dev(wu, "bf16"), dev(wd, "bf16"),
+                                          bias=dev(bias, "f32"), indices_out=idx, weights_out=wts)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(idx).astype(np.uint32)[rows], idx_r[rows])
+    assert_close(host(wts)[rows], w_r[rows], "f32", "grouped forward weights")
+    assert_close(host(out)[rows], out_r[rows], "bf16", "grouped forward out")
+
+
+def test_forward_sigmoid_grouped_dsv3_full_size():
+    """The DeepSeek-V3-shaped workload (T 2048, H 7168, I 2048, E 256, top-8)
+    through moe_forward_sigmoid_grouped with 8 groups, 4 kept, top-two group
+    scores, a correction bias and scale 2.5; the oracle on sampled tokens."""
+    w = I.workload("dsv3_share_rmsnorm_bf16")
+    z = I.logits_for(w)
+    x = I.tokens_for(w)
+    g = np.random.default_rng(44)
+    bias = (g.standard_normal(w.E) * 0.05).astype(np.float32)
+    args = (w.top_k, 8, 4, True, True, 2.5)
+    idx_r, w_r = O.route_sigmoid_grouped(z, "f32", bias, w.top_k, 8, 4, True, True, 2.5)
+    margin = O.route_sigmoid_grouped_margins(z, "f32", bias, w.top_k, 8, 4, True)
+    robust = np.flatnonzero(~(margin < MARGIN))
+    sample = np.unique(np.concatenate([robust[:1], robust[-1:], g.choice(robust, 24, False)]))
+    keep = sorted(set(int(e) for e in idx_r[sample].ravel()))
+    say("grouped dsv3: generating weights")
+    wg, wu, wd, kept = upload_expert_weights(w, keep)
+    idx = torch.empty((w.T, w.top_k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((w.T, w.top_k), dtype=torch.float32, device="cuda")
+    say("grouped dsv3: forward")
+    out = moe.moe_forward_sigmoid_grouped(dev(x, w.dtype), dev(z, "f32"), *args, wg, wu, wd,
+                                          bias=dev(bias, "f32"), indices_out=idx, weights_out=wts)
+    torch.cuda.synchronize()
+    rows = ~(margin < MARGIN)
+    assert rows.mean() > 0.95
+    assert np.array_equal(host(idx).astype(np.uint32)[rows], idx_r[rows])
+    assert_close(host(wts)[rows], w_r[rows], "f32", "weights")
+    yrows = O.expert_out_rows(x, idx_r, [int(t) for t in sample], lambda e: kept[e], w.dtype)
+    S, k = len(sample), w.top_k
+    y = np.stack([yrows[(int(t), j)] for t in sample for j in range(k)])
+    ref = O.combine(y, np.arange(S * k, dtype=np.int32), w_r[sample], "f32", S, k, w.dtype)
+    assert_close(host(out)[sample], ref, w.dtype, "grouped dsv3 out")
+    del wg, wu, wd
+    torch.cuda.empty_cache()
