@@ -108,6 +108,29 @@ moe_status moe_dispatch(const uint32_t* indices, int64_t T, int64_t top_k, int64
 size_t moe_dispatch_workspace_size(int64_t T, int64_t top_k, int64_t E);
 
 /*
+ * moe_dispatch_masked - moe_dispatch with an activity mask.
+ * Passages: ruDNN user guide, "5. Expert weights and dispatch"; the mask is
+ * the xActiveMaskOptional input of aclnnMoeDistributeCombineAddRmsNormV2
+ * (a per-token flag, or one flag per (token, expert slot); a token whose
+ * flags are all off takes no part).
+ *   active     NULL (mask_dims 0: every slot active), or uint8 [T]
+ *              (mask_dims 1: one flag per token) or [T, top_k] (mask_dims 2:
+ *              one flag per slot); nonzero = active. Any pattern is accepted
+ *              (the page's "active tokens first" rule serves its
+ *              communication layout, not this computation).
+ *   Slots that are inactive or whose id is >= E are not dispatched
+ *   (row_of_slot = -1); ids >= E may name special experts handled by
+ *   moe_combine_special. top_k may exceed E. Other arguments, results and
+ *   errors as moe_dispatch; ARGUMENT if mask_dims is not 0..2 or does not
+ *   match whether active is given.
+ */
+moe_status moe_dispatch_masked(const uint32_t* indices, const uint8_t* active, int mask_dims,
+                               int64_t T, int64_t top_k, int64_t E, const void* x, moe_dtype dt,
+                               int64_t H, void* x_disp, int32_t* expert_offsets,
+                               int32_t* slot_of_row, int32_t* row_of_slot, void* ws,
+                               size_t ws_bytes, hipStream_t stream);
+
+/*
  * moe_experts_forward_dispatched - bias-free SwiGLU experts on dispatched rows.
  * Passages: ruDNN user guide, "3. MoE workflow" (SwiGluExperts::new builds
  * bias-free expert weights; forward_dispatched computes the dispatched
@@ -266,6 +289,61 @@ moe_status moe_combine_add_rmsnorm(const void* expert_out, const int32_t* row_of
                                    const void* residual, const float* gamma, float eps,
                                    int64_t T, int64_t top_k, int64_t H, moe_dtype dt,
                                    void* y, void* x_out, float* rstd, hipStream_t stream);
+
+/*
+ * moe_combine_special - combine with special experts and an activity mask.
+ * Passage: aclnnMoeDistributeCombineAddRmsNormV2, "function description"
+ * (special experts: Moe(oriX) = 0 for zero experts, oriX for copy experts,
+ * constExpertAlpha1 * oriX + constExpertAlpha2 * constExpertV for constant
+ * experts) and its parameters zeroExpertNum / copyExpertNum /
+ * constExpertNum, oriXOptional, constExpertAlpha1Optional /
+ * constExpertAlpha2Optional / constExpertVOptional, xActiveMaskOptional and
+ * sharedExpertXOptional.
+ *   For each token t: out[t] = sum over active slots j of
+ *     weights[t,j] * (m_j + shared[t])  (shared may be NULL: term omitted)
+ *   with e = indices[t,j] and
+ *     e < E                                expert_out[row_of_slot[t*k+j]]
+ *     E <= e < E+zero_num                  0
+ *     next copy_num ids                    ori_x[t]
+ *     next const_num ids (constant q)      const_alpha1[q]*ori_x[t] + const_alpha2[q]*const_v[q]
+ *   Any other id, or a real-expert slot that was not dispatched, makes the
+ *   token's row NaN; a token with no active slot combines to 0. fp32
+ *   arithmetic, out rounded once to dt.
+ *   expert_out [rows, H] dt; row_of_slot [T*top_k] int32 (from moe_dispatch
+ *   or moe_dispatch_masked with the same mask); indices [T, top_k] uint32;
+ *   weights [T, top_k] w_dt; ori_x [T, H] dt (needed when copy_num or
+ *   const_num > 0); const_alpha1, const_alpha2 [const_num] dt; const_v
+ *   [const_num, H] dt; active / mask_dims as in moe_dispatch_masked;
+ *   out [T, H] dt (written).
+ * Errors: ARGUMENT for negative counts, E + counts > 2^31 - 1 or a bad mask
+ *   description; NULL_POINTER when a needed input is missing; UNSUPPORTED if
+ *   H is not a multiple of 8 or exceeds 32768.
+ */
+moe_status moe_combine_special(const void* expert_out, const int32_t* row_of_slot,
+                               const uint32_t* indices, const void* weights, moe_dtype w_dt,
+                               int64_t T, int64_t top_k, int64_t H, moe_dtype dt, int64_t E,
+                               int64_t zero_num, int64_t copy_num, int64_t const_num,
+                               const void* ori_x, const void* const_alpha1,
+                               const void* const_alpha2, const void* const_v,
+                               const uint8_t* active, int mask_dims, const void* shared,
+                               void* out, hipStream_t stream);
+
+/*
+ * moe_combine_add_rmsnorm_special - moe_combine_special followed by the
+ * residual Add and RMSNorm of moe_combine_add_rmsnorm (the whole
+ * aclnnMoeDistributeCombineAddRmsNormV2 formula with special experts and the
+ * activity mask): x = combined + residual, rstd = 1/sqrt(mean(x^2) + eps),
+ * y = x * rstd * gamma; x_out = x and y in dt, rstd fp32. A token with no
+ * active slot gets x = residual.
+ * Errors: as moe_combine_special, plus ARGUMENT if eps is not finite or <= 0.
+ */
+moe_status moe_combine_add_rmsnorm_special(
+    const void* expert_out, const int32_t* row_of_slot, const uint32_t* indices,
+    const void* weights, moe_dtype w_dt, int64_t T, int64_t top_k, int64_t H, moe_dtype dt,
+    int64_t E, int64_t zero_num, int64_t copy_num, int64_t const_num, const void* ori_x,
+    const void* const_alpha1, const void* const_alpha2, const void* const_v,
+    const uint8_t* active, int mask_dims, const void* shared, const void* residual,
+    const float* gamma, float eps, void* y, void* x_out, float* rstd, hipStream_t stream);
 
 #ifdef __cplusplus
 }

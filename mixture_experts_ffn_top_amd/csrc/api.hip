@@ -169,13 +169,18 @@ size_t moe_dispatch_workspace_size(int64_t T, int64_t top_k, int64_t E) {
   return align256(dispatch_scratch_bytes(T * top_k, E));
 }
 
-moe_status moe_dispatch(const uint32_t* indices, int64_t T, int64_t top_k, int64_t E,
-                        const void* x, moe_dtype dt, int64_t H, void* x_disp,
-                        int32_t* expert_offsets, int32_t* slot_of_row, int32_t* row_of_slot,
-                        void* ws, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+moe_status dispatch_impl(const uint32_t* indices, const uint8_t* active, int mask_dims, int64_t T,
+                         int64_t top_k, int64_t E, const void* x, moe_dtype dt, int64_t H,
+                         void* x_disp, int32_t* expert_offsets, int32_t* slot_of_row,
+                         int32_t* row_of_slot, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (T < 0 || E < 1 || H < 0) return MOE_ERROR_SHAPE;
   if (!valid_dt(dt)) return MOE_ERROR_DTYPE;
-  if (top_k < 1 || top_k > E) return MOE_ERROR_ARGUMENT;
+  if (top_k < 1) return MOE_ERROR_ARGUMENT;
+  if (mask_dims < 0 || mask_dims > 2 || (mask_dims > 0) != (active != nullptr)) return MOE_ERROR_ARGUMENT;
   if (E > kMaxE || T * top_k > INT32_MAX) return MOE_ERROR_UNSUPPORTED;
   if (x_disp && !row_len_ok(H)) return MOE_ERROR_UNSUPPORTED;
   if (!expert_offsets) return MOE_ERROR_NULL_POINTER;
@@ -189,17 +194,41 @@ moe_status moe_dispatch(const uint32_t* indices, int64_t T, int64_t top_k, int64
                        {slot_of_row, slots * 4},
                        {row_of_slot, slots * 4},
                        {ws, need}};
-  const Span ins[] = {{indices, slots * 4}, {x, x ? (size_t)T * (size_t)H * ds : 0}};
-  if (any_overlap(outs, 5, ins, 2)) return MOE_ERROR_ARGUMENT;
-  const void* ptrs[] = {indices, x, x_disp, expert_offsets, slot_of_row, row_of_slot, ws};
-  moe_status st = check_device(ptrs, 7, stream);
+  const Span ins[] = {{indices, slots * 4}, {x, x ? (size_t)T * (size_t)H * ds : 0},
+                      {active, mask_dims == 1 ? (size_t)T : mask_dims == 2 ? slots : 0}};
+  if (any_overlap(outs, 5, ins, 3)) return MOE_ERROR_ARGUMENT;
+  const void* ptrs[] = {indices, x, x_disp, expert_offsets, slot_of_row, row_of_slot, ws, active};
+  moe_status st = check_device(ptrs, 8, stream);
   if (st != MOE_SUCCESS) return st;
   hipError_t e = launch_dispatch_maps(indices, (int)slots, (int)E, expert_offsets, slot_of_row,
-                                      row_of_slot, static_cast<int32_t*>(ws), stream);
+                                      row_of_slot, static_cast<int32_t*>(ws), stream, active,
+                                      mask_dims, (int)top_k);
   if (e == hipSuccess && x_disp && slots)
     e = launch_gather_rows(x, dt, (int)H, (int)top_k, slot_of_row, expert_offsets + E, (int)slots,
                            x_disp, stream);
   return from_hip(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_dispatch(const uint32_t* indices, int64_t T, int64_t top_k, int64_t E,
+                        const void* x, moe_dtype dt, int64_t H, void* x_disp,
+                        int32_t* expert_offsets, int32_t* slot_of_row, int32_t* row_of_slot,
+                        void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (top_k > E && E >= 1) return MOE_ERROR_ARGUMENT;
+  return dispatch_impl(indices, nullptr, 0, T, top_k, E, x, dt, H, x_disp, expert_offsets,
+                       slot_of_row, row_of_slot, ws, ws_bytes, stream);
+}
+
+moe_status moe_dispatch_masked(const uint32_t* indices, const uint8_t* active, int mask_dims,
+                               int64_t T, int64_t top_k, int64_t E, const void* x, moe_dtype dt,
+                               int64_t H, void* x_disp, int32_t* expert_offsets,
+                               int32_t* slot_of_row, int32_t* row_of_slot, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+  return dispatch_impl(indices, active, mask_dims, T, top_k, E, x, dt, H, x_disp, expert_offsets,
+                       slot_of_row, row_of_slot, ws, ws_bytes, stream);
 }
 
 size_t moe_experts_workspace_size(int64_t rows, int64_t E, int64_t H, int64_t I, moe_dtype dt) {
@@ -478,6 +507,95 @@ moe_status moe_forward_sigmoid_grouped(const void* x, const void* logits, moe_dt
   r.scale = scale;
   return forward_impl(x, logits, logits_dt, T, H, I, E, top_k, r, w_gate, w_up, w_down, dt, out,
                       indices_out, weights_out, ws, ws_bytes, stage_events, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+moe_status combine_special_impl(const void* expert_out, const int32_t* row_of_slot,
+                                const uint32_t* indices, const void* weights, moe_dtype w_dt,
+                                int64_t T, int64_t top_k, int64_t H, moe_dtype dt, int64_t E,
+                                int64_t zero_num, int64_t copy_num, int64_t const_num,
+                                const void* ori_x, const void* const_alpha1,
+                                const void* const_alpha2, const void* const_v,
+                                const uint8_t* active, int mask_dims, const void* shared,
+                                const void* residual, const float* gamma, float eps, void* out,
+                                void* x_out, float* rstd, hipStream_t stream) {
+  const bool norm = residual != nullptr || gamma != nullptr || x_out != nullptr || rstd != nullptr;
+  if (T < 0 || top_k < 1 || H < 1 || E < 1) return MOE_ERROR_SHAPE;
+  if (!valid_dt(dt) || !valid_dt(w_dt)) return MOE_ERROR_DTYPE;
+  if (zero_num < 0 || copy_num < 0 || const_num < 0 ||
+      E + zero_num + copy_num + const_num > INT32_MAX)
+    return MOE_ERROR_ARGUMENT;
+  if (mask_dims < 0 || mask_dims > 2 || (mask_dims > 0) != (active != nullptr)) return MOE_ERROR_ARGUMENT;
+  if (norm && (!isfinite(eps) || eps <= 0.f)) return MOE_ERROR_ARGUMENT;
+  if (T * top_k > INT32_MAX || !row_len_ok(H) || H > kMaxNormH) return MOE_ERROR_UNSUPPORTED;
+  if (T == 0) return MOE_SUCCESS;
+  if (!expert_out || !row_of_slot || !indices || !weights || !out) return MOE_ERROR_NULL_POINTER;
+  if ((copy_num > 0 || const_num > 0) && !ori_x) return MOE_ERROR_NULL_POINTER;
+  if (const_num > 0 && (!const_alpha1 || !const_alpha2 || !const_v)) return MOE_ERROR_NULL_POINTER;
+  if (norm && (!residual || !gamma || !x_out || !rstd)) return MOE_ERROR_NULL_POINTER;
+  const size_t ds = dtype_size(dt), slots = (size_t)(T * top_k), th = (size_t)T * (size_t)H * ds;
+  const size_t nq = (size_t)const_num;
+  const Span outs[] = {{out, th}, {x_out, x_out ? th : 0}, {rstd, rstd ? (size_t)T * 4 : 0}};
+  const Span ins[] = {{expert_out, slots * (size_t)H * ds}, {row_of_slot, slots * 4},
+                      {indices, slots * 4}, {weights, slots * dtype_size(w_dt)},
+                      {ori_x, ori_x ? th : 0}, {const_alpha1, const_alpha1 ? nq * ds : 0},
+                      {const_alpha2, const_alpha2 ? nq * ds : 0},
+                      {const_v, const_v ? nq * (size_t)H * ds : 0},
+                      {active, mask_dims == 1 ? (size_t)T : mask_dims == 2 ? slots : 0},
+                      {shared, shared ? th : 0}, {residual, residual ? th : 0},
+                      {gamma, gamma ? (size_t)H * 4 : 0}};
+  if (any_overlap(outs, 3, ins, 12)) return MOE_ERROR_ARGUMENT;
+  const void* ptrs[] = {expert_out, row_of_slot, indices, weights, ori_x, const_alpha1, const_alpha2,
+                        const_v, active, shared, residual, gamma, out, x_out, rstd};
+  moe_status st = check_device(ptrs, 15, stream);
+  if (st != MOE_SUCCESS) return st;
+  SpecialCombine c;
+  c.expert_out = expert_out; c.row_of_slot = row_of_slot; c.indices = indices; c.weights = weights;
+  c.w_dt = w_dt; c.dt = dt; c.k = (int)top_k; c.H = (int)H; c.E = (int)E;
+  c.n_zero = (int)zero_num; c.n_copy = (int)copy_num; c.n_const = (int)const_num;
+  c.ori_x = ori_x; c.alpha1 = const_alpha1; c.alpha2 = const_alpha2; c.const_v = const_v;
+  c.active = active; c.mask_dims = mask_dims; c.shared = shared;
+  c.residual = norm ? residual : nullptr; c.gamma = gamma; c.eps = eps;
+  c.out = out; c.x_out = x_out; c.rstd = rstd;
+  return from_hip(launch_combine_special(c, (int)T, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_combine_special(const void* expert_out, const int32_t* row_of_slot,
+                               const uint32_t* indices, const void* weights, moe_dtype w_dt,
+                               int64_t T, int64_t top_k, int64_t H, moe_dtype dt, int64_t E,
+                               int64_t zero_num, int64_t copy_num, int64_t const_num,
+                               const void* ori_x, const void* const_alpha1,
+                               const void* const_alpha2, const void* const_v,
+                               const uint8_t* active, int mask_dims, const void* shared,
+                               void* out, hipStream_t stream) {
+  return combine_special_impl(expert_out, row_of_slot, indices, weights, w_dt, T, top_k, H, dt, E,
+                              zero_num, copy_num, const_num, ori_x, const_alpha1, const_alpha2,
+                              const_v, active, mask_dims, shared, nullptr, nullptr, 0.f, out,
+                              nullptr, nullptr, stream);
+}
+
+moe_status moe_combine_add_rmsnorm_special(
+    const void* expert_out, const int32_t* row_of_slot, const uint32_t* indices,
+    const void* weights, moe_dtype w_dt, int64_t T, int64_t top_k, int64_t H, moe_dtype dt,
+    int64_t E, int64_t zero_num, int64_t copy_num, int64_t const_num, const void* ori_x,
+    const void* const_alpha1, const void* const_alpha2, const void* const_v,
+    const uint8_t* active, int mask_dims, const void* shared, const void* residual,
+    const float* gamma, float eps, void* y, void* x_out, float* rstd, hipStream_t stream) {
+  if (!residual || !gamma || !x_out || !rstd) {
+    if (T < 0 || top_k < 1 || H < 1 || E < 1) return MOE_ERROR_SHAPE;
+    if (T > 0) return MOE_ERROR_NULL_POINTER;
+  }
+  return combine_special_impl(expert_out, row_of_slot, indices, weights, w_dt, T, top_k, H, dt, E,
+                              zero_num, copy_num, const_num, ori_x, const_alpha1, const_alpha2,
+                              const_v, active, mask_dims, shared, residual, gamma, eps, y, x_out,
+                              rstd, stream);
 }
 
 }  // extern "C"

@@ -20,9 +20,23 @@ namespace {
 
 constexpr int kMaxBlocks = 256;
 
+// Expert id slot s is dispatched to, or E for "not dispatched": ids >= E and
+// slots switched off by the activity mask (mask_dims 1: one flag per token,
+// 2: one per slot; 0: no mask) are not dispatched.
+__device__ __forceinline__ uint32_t slot_expert(const uint32_t* idx, int64_t s, int E,
+                                                const uint8_t* active, int mask_dims, int k) {
+  uint32_t e = idx[s];
+  if (e > (uint32_t)E) e = (uint32_t)E;
+  if (mask_dims == 1 && !active[s / k]) e = (uint32_t)E;
+  if (mask_dims == 2 && !active[s]) e = (uint32_t)E;
+  return e;
+}
+
 __global__ __launch_bounds__(kWave) void hist_kernel(const uint32_t* __restrict__ idx, int n_slots,
                                                       int E, int per_block,
-                                                      int32_t* __restrict__ hist) {
+                                                      int32_t* __restrict__ hist,
+                                                      const uint8_t* __restrict__ active,
+                                                      int mask_dims, int k) {
   __shared__ int cnt[kMaxExperts];
   for (int e = threadIdx.x; e < E; e += kWave) cnt[e] = 0;
   __syncthreads();
@@ -30,7 +44,7 @@ __global__ __launch_bounds__(kWave) void hist_kernel(const uint32_t* __restrict_
   for (int i = threadIdx.x; i < per_block; i += kWave) {
     const int64_t s = s0 + i;
     if (s < n_slots) {
-      const uint32_t e = idx[s];
+      const uint32_t e = slot_expert(idx, s, E, active, mask_dims, k);
       if (e < (uint32_t)E) atomicAdd(&cnt[e], 1);
     }
   }
@@ -63,7 +77,9 @@ __global__ __launch_bounds__(kWave) void scatter_kernel(const uint32_t* __restri
                                                          int n_slots, int E, int per_block,
                                                          const int32_t* __restrict__ base,
                                                          int32_t* __restrict__ slot_of_row,
-                                                         int32_t* __restrict__ row_of_slot) {
+                                                         int32_t* __restrict__ row_of_slot,
+                                                         const uint8_t* __restrict__ active,
+                                                         int mask_dims, int k) {
   __shared__ int run[kMaxExperts];
   for (int e = threadIdx.x; e < E; e += kWave) run[e] = base[(int64_t)blockIdx.x * E + e];
   __syncthreads();
@@ -73,8 +89,7 @@ __global__ __launch_bounds__(kWave) void scatter_kernel(const uint32_t* __restri
   for (int c = 0; c < per_block; c += kWave) {
     const int64_t s = s0 + c + lane;
     const bool in = s < n_slots;
-    uint32_t e = in ? idx[s] : (uint32_t)E;
-    if (e > (uint32_t)E) e = (uint32_t)E;
+    const uint32_t e = in ? slot_expert(idx, s, E, active, mask_dims, k) : (uint32_t)E;
     uint64_t same = __ballot(in);
     for (int b = 0; b < nbits; ++b) {
       const bool bit = (e >> b) & 1u;
@@ -133,13 +148,15 @@ size_t dispatch_scratch_bytes(int64_t n_slots, int64_t E) {
 
 hipError_t launch_dispatch_maps(const uint32_t* indices, int n_slots, int E, int32_t* offsets,
                                 int32_t* slot_of_row, int32_t* row_of_slot, int32_t* scratch,
-                                hipStream_t s) {
+                                hipStream_t s, const uint8_t* active, int mask_dims, int k) {
   const DispatchPlan p = dispatch_plan(n_slots, E);
+  if (!active) mask_dims = 0;
+  if (k < 1) k = 1;
   hipLaunchKernelGGL(hist_kernel, dim3(p.n_blocks), dim3(kWave), 0, s, indices, n_slots, E,
-                     p.slots_per_block, scratch);
+                     p.slots_per_block, scratch, active, mask_dims, k);
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, scratch, p.n_blocks, E, offsets);
   hipLaunchKernelGGL(scatter_kernel, dim3(p.n_blocks), dim3(kWave), 0, s, indices, n_slots, E,
-                     p.slots_per_block, scratch, slot_of_row, row_of_slot);
+                     p.slots_per_block, scratch, slot_of_row, row_of_slot, active, mask_dims, k);
   return hipGetLastError();
 }
 

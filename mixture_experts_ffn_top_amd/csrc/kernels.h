@@ -32,7 +32,8 @@ DispatchPlan dispatch_plan(int64_t n_slots, int64_t E);
 size_t dispatch_scratch_bytes(int64_t n_slots, int64_t E);
 hipError_t launch_dispatch_maps(const uint32_t* indices, int n_slots, int E, int32_t* offsets,
                                 int32_t* slot_of_row, int32_t* row_of_slot, int32_t* scratch,
-                                hipStream_t s);
+                                hipStream_t s,
+                                const uint8_t* active = nullptr, int mask_dims = 0, int k = 1);
 // x_disp[r] = x[slot_of_row[r] / k] for r < offsets[E] (read on the device).
 hipError_t launch_gather_rows(const void* x, int dt, int H, int k, const int32_t* slot_of_row,
                               const int32_t* offsets_end, int max_rows, void* x_disp,
@@ -92,5 +93,29 @@ hipError_t launch_combine_add_rmsnorm(const void* expert_out, const int32_t* row
                                       const void* residual, const float* gamma, float eps, int T,
                                       int k, int H, int dt, void* y, void* x_out, float* rstd,
                                       hipStream_t s);
+
+// Combine with special experts (zero / copy / constant) and an activity mask;
+// with residual != nullptr the residual Add + RMSNorm follow (out = y).
+struct SpecialCombine {
+  const void* expert_out;
+  const int32_t* row_of_slot;
+  const uint32_t* indices;
+  const void* weights;
+  int w_dt, dt, k, H, E, n_zero, n_copy, n_const;
+  const void* ori_x;
+  const void* alpha1;
+  const void* alpha2;
+  const void* const_v;
+  const uint8_t* active;
+  int mask_dims;
+  const void* shared;
+  const void* residual;
+  const float* gamma;
+  float eps;
+  void* out;
+  void* x_out;
+  float* rstd;
+};
+hipError_t launch_combine_special(const SpecialCombine& c, int T, hipStream_t s);
 
 }  // namespace moe

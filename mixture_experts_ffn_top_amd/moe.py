@@ -47,6 +47,11 @@ _SIGS = {
     "moe_combine": ([P, P, P, I32, I64, I64, I64, I32, P, P], I32),
     "moe_forward": ([P, P, I32, I64, I64, I64, I64, I64, I32, P, P, P, I32, P, P, P, P, SZ, P, P], I32),
     "moe_forward_workspace_size": ([I64, I64, I64, I64, I64, I32, I32], SZ),
+    "moe_dispatch_masked": ([P, P, I32, I64, I64, I64, P, I32, I64, P, P, P, P, P, SZ, P], I32),
+    "moe_combine_special": ([P, P, P, P, I32, I64, I64, I64, I32, I64, I64, I64, I64, P, P, P, P, P, I32,
+                             P, P, P], I32),
+    "moe_combine_add_rmsnorm_special": ([P, P, P, P, I32, I64, I64, I64, I32, I64, I64, I64, I64, P, P,
+                                         P, P, P, I32, P, P, P, ctypes.c_float, P, P, P, P], I32),
     "moe_route_sigmoid_grouped": ([P, I32, I64, I64, P, I64, I64, I64, I32, I32, ctypes.c_float, P, P, P],
                                   I32),
     "moe_forward_sigmoid_grouped": ([P, P, I32, I64, I64, I64, I64, P, I64, I64, I64, I32, I32,
@@ -128,6 +133,62 @@ def moe_dispatch(indices, E: int, x=None, with_x_disp: bool = True, ws=None, off
     _check(lib().moe_dispatch(_ptr(indices), T, k, E, _ptr(x), dt, H, _ptr(x_disp), _ptr(offsets),
                               _ptr(sor), _ptr(ros), _ptr(ws), ws.numel(), _stream()), "moe_dispatch")
     return dict(offsets=offsets, slot_of_row=sor, row_of_slot=ros, x_disp=x_disp)
+
+
+def moe_dispatch_masked(indices, E: int, active=None, x=None, with_x_disp: bool = True, ws=None):
+    """moe_dispatch with an activity mask: active None, uint8/bool [T] (per token)
+    or [T, k] (per slot). Returns the same dict as moe_dispatch."""
+    T, k = indices.shape
+    dev = indices.device
+    H = x.shape[1] if x is not None else 0
+    dt = dtype_code(x.dtype) if x is not None else BF16
+    x_disp = torch.empty((T * k, H), dtype=x.dtype, device=dev) if (x is not None and with_x_disp) else None
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    sor = torch.empty(T * k, dtype=torch.int32, device=dev)
+    ros = torch.empty(T * k, dtype=torch.int32, device=dev)
+    mask_dims, act = _mask(active)
+    if ws is None:
+        ws = _workspace(moe_dispatch_workspace_size(T, k, E), dev)
+    _check(lib().moe_dispatch_masked(_ptr(indices), _ptr(act), mask_dims, T, k, E, _ptr(x), dt, H,
+                                     _ptr(x_disp), _ptr(offsets), _ptr(sor), _ptr(ros), _ptr(ws),
+                                     ws.numel(), _stream()), "moe_dispatch_masked")
+    return dict(offsets=offsets, slot_of_row=sor, row_of_slot=ros, x_disp=x_disp)
+
+
+def _mask(active):
+    if active is None:
+        return 0, None
+    a = active.to(torch.uint8).contiguous()
+    return a.dim(), a
+
+
+def moe_combine_special(expert_out, row_of_slot, indices, weights, E: int, zero_num: int = 0,
+                        copy_num: int = 0, const_num: int = 0, ori_x=None, const_alpha1=None,
+                        const_alpha2=None, const_v=None, active=None, shared=None, out=None,
+                        residual=None, gamma=None, eps: float = 1e-6):
+    """Combine with special experts (ids E.. : zero, copy, constant) and an
+    activity mask. Without residual returns out [T, H]; with residual and gamma
+    the residual Add + RMSNorm follow and (y, x_out, rstd) is returned."""
+    T, k = indices.shape
+    H = expert_out.shape[1]
+    dev = expert_out.device
+    mask_dims, act = _mask(active)
+    args_head = (_ptr(expert_out), _ptr(row_of_slot), _ptr(indices), _ptr(weights),
+                 dtype_code(weights.dtype), T, k, H, dtype_code(expert_out.dtype), E, zero_num,
+                 copy_num, const_num, _ptr(ori_x), _ptr(const_alpha1), _ptr(const_alpha2),
+                 _ptr(const_v), _ptr(act), mask_dims, _ptr(shared))
+    if residual is None:
+        if out is None:
+            out = torch.empty((T, H), dtype=expert_out.dtype, device=dev)
+        _check(lib().moe_combine_special(*args_head, _ptr(out), _stream()), "moe_combine_special")
+        return out
+    y = torch.empty((T, H), dtype=expert_out.dtype, device=dev) if out is None else out
+    x_out = torch.empty((T, H), dtype=expert_out.dtype, device=dev)
+    rstd = torch.empty(T, dtype=torch.float32, device=dev)
+    _check(lib().moe_combine_add_rmsnorm_special(*args_head, _ptr(residual), _ptr(gamma), float(eps),
+                                                 _ptr(y), _ptr(x_out), _ptr(rstd), _stream()),
+           "moe_combine_add_rmsnorm_special")
+    return y, x_out, rstd
 
 
 def moe_experts_workspace_size(rows: int, E: int, H: int, I: int, dt: torch.dtype) -> int:

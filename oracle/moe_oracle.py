@@ -244,7 +244,7 @@ def route_sigmoid_grouped_margins(logits, logits_dtype, bias, top_k, groups, sel
 # --------------------------------------------------------------------------
 # dispatch  (ruDNN user guide, "5. Expert weights and dispatch")
 # --------------------------------------------------------------------------
-def dispatch(indices: np.ndarray, E: int, x: np.ndarray | None = None):
+def dispatch(indices: np.ndarray, E: int, x: np.ndarray | None = None, active=None):
     """Compact grouping of the T*k (token, slot) pairs by expert, no capacity
     drop. Within an expert, pairs keep (token, slot) order (the pages leave
     this order free; this build fixes it). Returns
@@ -252,9 +252,15 @@ def dispatch(indices: np.ndarray, E: int, x: np.ndarray | None = None):
       slot_of_row int32 [R]    flat slot t*k+j held by dispatched row r
       row_of_slot int32 [T*k]  inverse map; -1 for an out-of-range expert id
       x_disp      [R, H]       x_disp[r] = x[slot_of_row[r] // k]   (if x given)
-    where R = number of in-range pairs."""
+    where R = number of in-range pairs. active (optional, the xActiveMaskOptional
+    input of aclnnMoeDistributeCombineAddRmsNormV2): bool [T] per token or
+    [T, k] per slot; inactive pairs are not dispatched either."""
     T, k = indices.shape
     flat = indices.reshape(-1).astype(np.int64)
+    if active is not None:
+        a = np.asarray(active, bool)
+        on = np.repeat(a, k) if a.ndim == 1 else a.reshape(-1)
+        flat = np.where(on, flat, -1)
     slots_by_expert = [np.nonzero(flat == e)[0] for e in range(E)]
     counts = np.array([len(s) for s in slots_by_expert], dtype=np.int64)
     offsets = np.zeros(E + 1, dtype=np.int32)
@@ -349,6 +355,73 @@ def combine_add_rmsnorm(expert_out, row_of_slot, weights, w_dtype, shared, resid
         wsum = decode(weights, w_dtype).reshape(T, k).sum(axis=1)
         c = c + wsum[:, None] * decode(shared, dtype)
     x = c + decode(residual, dtype)
+    rstd = 1.0 / np.sqrt((x * x).mean(axis=1) + float(eps))
+    y = x * rstd[:, None] * np.asarray(gamma, dtype=np.float32).astype(np.float64)[None, :]
+    return round_to(y, dtype), round_to(x, dtype), rstd.astype(np.float32)
+
+
+def combine_special_fp64(expert_out, row_of_slot, indices, weights, w_dtype, T, k, dtype, E,
+                         zero_num=0, copy_num=0, const_num=0, ori_x=None, alpha1=None,
+                         alpha2=None, const_v=None, active=None, shared=None):
+    """aclnnMoeDistributeCombineAddRmsNormV2 with special experts and the
+    activity mask (local part), in fp64:
+      c[t] = sum over active slots j of w[t,j] * (Moe_j + s[t])
+    where, for e = indices[t, j]:
+      e < E                      Moe = expert_out[row_of_slot[t*k+j]]
+      E <= e < E+zero_num        Moe = 0                         (zero expert)
+      next copy_num ids          Moe = ori_x[t]                  (copy expert)
+      next const_num ids (q)     Moe = alpha1[q]*ori_x[t] + alpha2[q]*V[q]
+    Any other id, or a real-expert slot that was not dispatched (row -1), makes
+    the row NaN. A token with no active slot combines to 0."""
+    idx = np.asarray(indices).reshape(T, k).astype(np.int64)
+    rows = np.asarray(row_of_slot).reshape(T, k).astype(np.int64)
+    w = decode(weights, w_dtype).reshape(T, k)
+    H = expert_out.shape[1]
+    y = decode(expert_out, dtype)
+    ox = decode(ori_x, dtype) if ori_x is not None else None
+    a1 = decode(alpha1, dtype) if const_num else None
+    a2 = decode(alpha2, dtype) if const_num else None
+    V = decode(const_v, dtype) if const_num else None
+    sh = decode(shared, dtype) if shared is not None else None
+    if active is None:
+        on = np.ones((T, k), bool)
+    else:
+        a = np.asarray(active, bool)
+        on = np.repeat(a[:, None], k, axis=1) if a.ndim == 1 else a.reshape(T, k)
+    c = np.zeros((T, H), dtype=np.float64)
+    for t in range(T):
+        for j in range(k):
+            if not on[t, j]:
+                continue
+            e, d = idx[t, j], idx[t, j] - E
+            if d < 0:
+                m = y[rows[t, j]] if rows[t, j] >= 0 else np.full(H, np.nan)
+            elif d < zero_num:
+                m = np.zeros(H)
+            elif d < zero_num + copy_num:
+                m = ox[t]
+            elif d < zero_num + copy_num + const_num:
+                q = d - zero_num - copy_num
+                m = a1[q] * ox[t] + a2[q] * V[q]
+            else:
+                m = np.full(H, np.nan)
+            c[t] += w[t, j] * (m + (sh[t] if sh is not None else 0.0))
+    return c
+
+
+def combine_special(*args, **kw):
+    """out [T, H] in the model dtype; arguments as combine_special_fp64."""
+    dtype = args[7] if len(args) > 7 else kw["dtype"]
+    return round_to(combine_special_fp64(*args, **kw), dtype)
+
+
+def combine_add_rmsnorm_special(residual, gamma, eps, *args, **kw):
+    """The whole aclnnMoeDistributeCombineAddRmsNormV2 formula with special
+    experts and the activity mask: x = combine_special_fp64(...) + residual,
+    rstd = 1/sqrt(mean_H(x^2) + eps), y = x * rstd * gamma. Returns (y, x_out)
+    in the model dtype and rstd fp32 [T]."""
+    dtype = args[7] if len(args) > 7 else kw["dtype"]
+    x = combine_special_fp64(*args, **kw) + decode(residual, dtype)
     rstd = 1.0 / np.sqrt((x * x).mean(axis=1) + float(eps))
     y = x * rstd[:, None] * np.asarray(gamma, dtype=np.float32).astype(np.float64)[None, :]
     return round_to(y, dtype), round_to(x, dtype), rstd.astype(np.float32)

@@ -536,3 +536,107 @@ def test_grouped_sigmoid_argument_checks():
         with pytest.raises(ValueError):
             O.route_sigmoid_grouped(z, "f32", None, a["top_k"], a["groups"], a["selected_groups"],
                                     a["group_top_two"], a["renormalize"], a["scale"])
+
+
+# --------------------------------------------------------------------------
+# special experts and the activity mask (aclnnMoeDistributeCombineAddRmsNormV2:
+# zero / copy / constant experts, xActiveMaskOptional)
+# --------------------------------------------------------------------------
+def _bf16(a):
+    return O.round_to(np.asarray(a, np.float64), "bf16")
+
+
+def test_masked_dispatch_counts_and_broadcast():
+    rng = np.random.default_rng(31)
+    T, k, E = 50, 3, 6
+    idx = rng.integers(0, E + 3, size=(T, k)).astype(np.uint32)  # some ids past E
+    act2 = rng.random((T, k)) < 0.7
+    d = O.dispatch(idx, E, active=act2)
+    flat = np.where(act2.reshape(-1) & (idx.reshape(-1) < E), idx.reshape(-1).astype(np.int64), E)
+    np.testing.assert_array_equal(np.diff(d["offsets"]), np.bincount(flat, minlength=E + 1)[:E])
+    # same as the unmasked dispatch of ids with the inactive slots pointed past E
+    ref = O.dispatch(np.where(act2, idx, E).astype(np.uint32), E)
+    for key in ("offsets", "slot_of_row", "row_of_slot"):
+        np.testing.assert_array_equal(d[key], ref[key])
+    act1 = rng.random(T) < 0.6
+    np.testing.assert_array_equal(O.dispatch(idx, E, active=act1)["row_of_slot"],
+                                  O.dispatch(idx, E, active=np.repeat(act1[:, None], k, 1))["row_of_slot"])
+    np.testing.assert_array_equal(O.dispatch(idx, E, active=np.ones((T, k), bool))["row_of_slot"],
+                                  O.dispatch(idx, E)["row_of_slot"])
+
+
+def test_special_combine_reduces_to_plain_combine():
+    rng = np.random.default_rng(32)
+    T, k, E, H = 40, 2, 5, 16
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.uint32)
+    d = O.dispatch(idx, E)
+    y = _bf16(rng.standard_normal((T * k, H)))
+    w = rng.random((T, k)).astype(np.float32)
+    a = O.combine_special_fp64(y, d["row_of_slot"], idx, w, "f32", T, k, "bf16", E)
+    b = O.combine_fp64(y, d["row_of_slot"], w, "f32", T, k, "bf16")
+    np.testing.assert_array_equal(a, b)
+
+
+def test_special_experts_closed_forms():
+    rng = np.random.default_rng(33)
+    T, H, E = 6, 24, 4
+    ori = _bf16(rng.standard_normal((T, H)))
+    V = _bf16(rng.standard_normal((2, H)))
+    a1 = _bf16([0.0, 1.0])
+    a2 = _bf16([1.0, 0.0])
+    y = _bf16(np.zeros((1, H)))
+    nores = np.full(T, -1, np.int32)
+    one = np.ones((T, 1), np.float32)
+    # copy expert (id E + zero_num), weight 1: the token itself, bit for bit
+    idx = np.full((T, 1), E + 2, np.uint32)
+    out = O.combine_special(y, nores, idx, one, "f32", T, 1, "bf16", E, 2, 1, 2, ori, a1, a2, V)
+    np.testing.assert_array_equal(out, ori)
+    # constant expert 0 (alpha1 = 0, alpha2 = 1): V[0]; constant 1 (1, 0): the token
+    idx[:] = E + 3
+    out = O.combine_special(y, nores, idx, one, "f32", T, 1, "bf16", E, 2, 1, 2, ori, a1, a2, V)
+    np.testing.assert_array_equal(out, np.repeat(V[:1], T, 0))
+    idx[:] = E + 4
+    out = O.combine_special(y, nores, idx, one, "f32", T, 1, "bf16", E, 2, 1, 2, ori, a1, a2, V)
+    np.testing.assert_array_equal(out, ori)
+    # zero experts: nothing, except the shared term w * s of their slot
+    idx = np.full((T, 2), E, np.uint32)
+    w2 = np.full((T, 2), 0.25, np.float32)
+    c = O.combine_special_fp64(y, np.full(2 * T, -1, np.int32), idx, w2, "f32", T, 2, "bf16", E, 2,
+                               0, 0, shared=ori)
+    np.testing.assert_array_equal(c, 0.5 * O.decode(ori, "bf16"))
+    # an id past every range: NaN row
+    idx = np.full((T, 1), E + 5, np.uint32)
+    c = O.combine_special_fp64(y, nores, idx, one, "f32", T, 1, "bf16", E, 2, 1, 2, ori, a1, a2, V)
+    assert np.isnan(c).all()
+
+
+def test_activity_mask_is_a_zero_weight_and_empty_token_normalises_residual():
+    rng = np.random.default_rng(34)
+    T, k, E, H = 30, 3, 6, 32
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.uint32)
+    act = rng.random((T, k)) < 0.6
+    act[0] = False
+    d = O.dispatch(idx, E, active=act)
+    y = _bf16(rng.standard_normal((T * k, H)))
+    w = rng.random((T, k)).astype(np.float32)
+    c = O.combine_special_fp64(y, d["row_of_slot"], idx, w, "f32", T, k, "bf16", E, active=act)
+    dfull = O.dispatch(idx, E)
+    # rows of active slots agree between the two dispatches only through the slot map, so
+    # compare against the unmasked combine with inactive weights zeroed on the same rows
+    y_full = np.zeros((T * k, H), np.uint16)
+    for s_ in range(T * k):
+        r = d["row_of_slot"][s_]
+        if r >= 0:
+            y_full[dfull["row_of_slot"][s_]] = y[r]
+    ref = O.combine_fp64(y_full, dfull["row_of_slot"], np.where(act, w, 0).astype(np.float32), "f32",
+                         T, k, "bf16")
+    np.testing.assert_allclose(c, ref, rtol=1e-12, atol=1e-12)
+    assert (c[0] == 0).all()
+    res = _bf16(rng.standard_normal((T, H)))
+    gamma = rng.uniform(0.5, 1.5, H).astype(np.float32)
+    yo, xo, rs = O.combine_add_rmsnorm_special(res, gamma, 1e-6, y, d["row_of_slot"], idx, w, "f32", T,
+                                               k, "bf16", E, active=act)
+    np.testing.assert_array_equal(xo[0], res[0])
+    ref0 = torch.nn.functional.rms_norm(torch.tensor(O.decode(res[:1], "bf16")), (H,),
+                                        torch.tensor(gamma.astype(np.float64)), 1e-6)
+    np.testing.assert_array_equal(yo[0], O.round_to(ref0.numpy()[0], "bf16"))

@@ -558,3 +558,92 @@ def test_forward_sigmoid_grouped_dsv3_full_size():
     assert_close(host(out)[sample], ref, w.dtype, "grouped dsv3 out")
     del wg, wu, wd
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------ special experts and the activity mask --
+def _special_case(g, dtype, T, k, E, nz, nc, nq, H, mask_kind):
+    n_ids = E + nz + nc + nq
+    idx = np.stack([g.permutation(n_ids)[:k] for _ in range(T)]).astype(np.uint32)
+    idx[5, 0] = n_ids + 3  # an id past every range: NaN row
+    active = None
+    if mask_kind == 1:
+        active = g.random(T) < 0.8
+        active[7] = False
+    elif mask_kind == 2:
+        active = g.random((T, k)) < 0.8
+        active[7] = False
+    ori = _store(g.standard_normal((T, H)), dtype)
+    a1 = _store(g.standard_normal(nq), dtype)
+    a2 = _store(g.standard_normal(nq), dtype)
+    V = _store(g.standard_normal((nq, H)), dtype)
+    w = g.random((T, k)).astype(np.float32)
+    return idx, active, ori, a1, a2, V, w
+
+
+@pytest.mark.parametrize("dtype,mask_kind,with_shared,norm", [("bf16", 2, True, True), ("bf16", 1, False, False),
+                                                              ("f32", 0, True, False), ("f16", 2, False, True),
+                                                              ("bf16", 2, False, False), ("f32", 1, True, True)])
+def test_special_experts_and_mask(dtype, mask_kind, with_shared, norm):
+    say("special", dtype, mask_kind, with_shared, norm)
+    g = np.random.default_rng(70 + mask_kind)
+    T, k, E, nz, nc, nq, H = 300, 4, 8, 2, 1, 3, 136
+    idx, active, ori, a1, a2, V, w = _special_case(g, dtype, T, k, E, nz, nc, nq, H, mask_kind)
+    act_dev = None if active is None else torch.from_numpy(active.astype(np.uint8)).cuda()
+    d = moe.moe_dispatch_masked(dev(idx), E, active=act_dev)
+    ref = O.dispatch(idx, E, active=active)
+    torch.cuda.synchronize()
+    for key in ("offsets", "row_of_slot"):
+        assert np.array_equal(host(d[key]), ref[key]), key
+    n = int(ref["offsets"][-1])
+    assert np.array_equal(host(d["slot_of_row"])[:n], ref["slot_of_row"])
+    y = _store(g.standard_normal((T * k, H)), dtype)
+    shared = _store(g.standard_normal((T, H)), dtype) if with_shared else None
+    args = (y, ref["row_of_slot"], idx, w, "f32", T, k, dtype, E, nz, nc, nq, ori, a1, a2, V, active, shared)
+    kw = dict(zero_num=nz, copy_num=nc, const_num=nq, ori_x=dev(ori, dtype), const_alpha1=dev(a1, dtype),
+              const_alpha2=dev(a2, dtype), const_v=dev(V, dtype), active=act_dev,
+              shared=None if shared is None else dev(shared, dtype))
+    if not norm:
+        out = moe.moe_combine_special(dev(y, dtype), d["row_of_slot"], dev(idx), dev(w, "f32"), E, **kw)
+        torch.cuda.synchronize()
+        assert_close(host(out), O.combine_special(*args), dtype, "special combine")
+    else:
+        res = _store(g.standard_normal((T, H)), dtype)
+        gamma = g.uniform(0.5, 1.5, H).astype(np.float32)
+        yo, xo, rs = moe.moe_combine_special(dev(y, dtype), d["row_of_slot"], dev(idx), dev(w, "f32"), E,
+                                             residual=dev(res, dtype), gamma=dev(gamma, "f32"), eps=1e-6, **kw)
+        torch.cuda.synchronize()
+        y_r, x_r, r_r = O.combine_add_rmsnorm_special(res, gamma, 1e-6, *args)
+        assert_close(host(yo), y_r, dtype, "special y")
+        assert_close(host(xo), x_r, dtype, "special x_out")
+        assert_close(host(rs), r_r, "f32", "special rstd")
+
+
+def test_special_experts_end_to_end_with_expert_gemms():
+    """masked dispatch -> SwiGLU experts on the dispatched rows -> special
+    combine + Add + RMSNorm, against the oracle's same chain."""
+    g = np.random.default_rng(81)
+    T, k, E, nz, nc, nq, H, I_ = 200, 3, 6, 1, 1, 2, 128, 256
+    idx, active, ori, a1, a2, V, w = _special_case(g, "bf16", T, k, E, nz, nc, nq, H, 2)
+    x = ori
+    wg, wu, wd = _random_experts(g, E, H, I_, "bf16")
+    act_dev = torch.from_numpy(active.astype(np.uint8)).cuda()
+    d = moe.moe_dispatch_masked(dev(idx), E, active=act_dev, x=dev(x, "bf16"))
+    ref = O.dispatch(idx, E, x=x, active=active)
+    n = int(ref["offsets"][-1])
+    # rows = T*k (host bound); the kernels read the dispatched count from the device offsets
+    yd = moe.moe_experts_forward_dispatched(d["x_disp"], d["offsets"], dev(wg, "bf16"),
+                                            dev(wu, "bf16"), dev(wd, "bf16"))
+    y_r = O.experts_forward_dispatched(ref["x_disp"], ref["offsets"], lambda e: (wg[e], wu[e], wd[e]), "bf16")
+    res = _store(g.standard_normal((T, H)), "bf16")
+    gamma = g.uniform(0.5, 1.5, H).astype(np.float32)
+    yo, xo, rs = moe.moe_combine_special(yd, d["row_of_slot"], dev(idx), dev(w, "f32"), E, zero_num=nz,
+                                         copy_num=nc, const_num=nq, ori_x=dev(ori, "bf16"),
+                                         const_alpha1=dev(a1, "bf16"), const_alpha2=dev(a2, "bf16"),
+                                         const_v=dev(V, "bf16"), active=act_dev, residual=dev(res, "bf16"),
+                                         gamma=dev(gamma, "f32"), eps=1e-6)
+    torch.cuda.synchronize()
+    assert_close(host(yd)[:n], y_r, "bf16", "expert rows")
+    yy, xx, rr = O.combine_add_rmsnorm_special(res, gamma, 1e-6, y_r, ref["row_of_slot"], idx, w, "f32", T, k,
+                                               "bf16", E, nz, nc, nq, ori, a1, a2, V, active)
+    assert_close(host(xo), xx, "bf16", "x_out")
+    assert_close(host(yo), yy, "bf16", "y")
