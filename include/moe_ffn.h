@@ -345,6 +345,60 @@ moe_status moe_combine_add_rmsnorm_special(
     const uint8_t* active, int mask_dims, const void* shared, const void* residual,
     const float* gamma, float eps, void* y, void* x_out, float* rstd, hipStream_t stream);
 
+/*
+ * moe_experts_forward_dispatched_quant - bias-free SwiGLU experts with
+ * weight-only INT8 / INT4 weights, for decode-sized batches.
+ * Passage: aclnnFFN, "Formula", pseudo-quantization scenario
+ * (y = activation(x * ((W1 + antiquantOffset1) * antiquantScale1)) *
+ * ((W2 + antiquantOffset2) * antiquantScale2), here with the SwiGLU of
+ * moe_experts_forward_dispatched), and its constraints (INT8 or INT4
+ * weights; per-group scales only with INT4; the group count divides both
+ * input sizes; INT4 rows of even length).
+ *   Weights keep the K-contiguous layout of the bf16 ones:
+ *     bits = 8: w_gate, w_up [E, I, H] int8; w_down [E, H, I] int8.
+ *     bits = 4: the same shapes with two values per byte along K (element
+ *               k in byte k/2, low nibble first, two's complement -8..7).
+ *   Each weight enters as (q + offset) * scale with
+ *     scale_gate, scale_up [E, I, groups], scale_down [E, H, groups] in dt,
+ *     offset_*: same shapes, or NULL for 0;
+ *   group j of a row covers input channels j*K/groups .. (j+1)*K/groups - 1
+ *   (groups = 1: one scale per output channel). The dequantised weight is
+ *   a value of dt: (q + offset) * scale is formed in fp32 and rounded once
+ *   to dt before it enters the product (exact before that rounding for
+ *   integer offsets), so the result equals moe_experts_forward_dispatched
+ *   given those dt weights.
+ *   Other arguments as moe_experts_forward_dispatched; workspace:
+ *   moe_experts_quant_workspace_size(rows, E, H, I, dt) (holds h).
+ * Errors: ARGUMENT if bits is not 8 or 4, groups < 1 or does not divide H
+ *   and I, or groups > 1 with bits = 8; UNSUPPORTED for dt F32, for
+ *   groups > 1 unless H/groups and I/groups are multiples of 128, and for
+ *   rows > 4 * E (this path streams weights for decode-sized batches).
+ */
+moe_status moe_experts_forward_dispatched_quant(
+    const void* x_disp, const int32_t* expert_offsets, int64_t rows, int64_t E, int64_t H, int64_t I,
+    const void* w_gate, const void* w_up, const void* w_down, int bits, int64_t groups,
+    const void* scale_gate, const void* scale_up, const void* scale_down, const void* offset_gate,
+    const void* offset_up, const void* offset_down, moe_dtype dt, void* expert_out, void* ws,
+    size_t ws_bytes, hipStream_t stream);
+size_t moe_experts_quant_workspace_size(int64_t rows, int64_t E, int64_t H, int64_t I,
+                                        moe_dtype dt);
+
+/*
+ * moe_forward_quant - moe_forward with the weight-only quantised experts of
+ * moe_experts_forward_dispatched_quant (same weight, scale and offset
+ * arguments and checks; rows = T * top_k). Passages: ruDNN user guide, "6.
+ * Calling MoE"; aclnnFFN, pseudo-quantization scenario.
+ * Workspace: moe_forward_workspace_size(T, H, I, E, top_k, dt, logits_dt).
+ */
+moe_status moe_forward_quant(const void* x, const void* logits, moe_dtype logits_dt, int64_t T,
+                             int64_t H, int64_t I, int64_t E, int64_t top_k, int renormalize,
+                             const void* w_gate, const void* w_up, const void* w_down, int bits,
+                             int64_t groups, const void* scale_gate, const void* scale_up,
+                             const void* scale_down, const void* offset_gate,
+                             const void* offset_up, const void* offset_down, moe_dtype dt,
+                             void* out, uint32_t* indices_out, void* weights_out, void* ws,
+                             size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

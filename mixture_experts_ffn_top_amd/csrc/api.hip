@@ -92,6 +92,31 @@ moe_status check_grouped_args(int64_t E, int64_t top_k, int64_t groups, int64_t 
   return MOE_SUCCESS;
 }
 
+// Weight-only quantised experts (aclnnFFN, pseudo-quantization scenario).
+struct QuantWeights {
+  int bits = 0;  // 8 or 4; 0: not quantised
+  int64_t groups = 1;
+  const void *s_gate = nullptr, *s_up = nullptr, *s_down = nullptr;
+  const void *o_gate = nullptr, *o_up = nullptr, *o_down = nullptr;
+};
+
+moe_status check_quant_args(int64_t rows, int64_t E, int64_t H, int64_t I, int bits, int64_t groups,
+                            moe_dtype dt) {
+  if (bits != 8 && bits != 4) return MOE_ERROR_ARGUMENT;
+  if (groups < 1 || H % groups != 0 || I % groups != 0) return MOE_ERROR_ARGUMENT;
+  if (groups > 1 && bits != 4) return MOE_ERROR_ARGUMENT;  // per-group mode is INT4 only
+  if (dt != MOE_BF16 && dt != MOE_F16) return MOE_ERROR_UNSUPPORTED;
+  if (groups > 1 && ((H / groups) % 128 != 0 || (I / groups) % 128 != 0)) return MOE_ERROR_UNSUPPORTED;
+  if (!row_len_ok(H) || !row_len_ok(I) || E > kMaxE) return MOE_ERROR_UNSUPPORTED;
+  if (rows > 4 * E) return MOE_ERROR_UNSUPPORTED;  // decode-sized batches only
+  return MOE_SUCCESS;
+}
+
+// Bytes of one quantised weight tensor [E, N, K].
+size_t quant_bytes(int64_t E, int64_t N, int64_t K, int bits) {
+  return (size_t)E * (size_t)N * (size_t)K * (size_t)bits / 8;
+}
+
 // Routing step of a forward pass: writes indices [T,k] and weights [T,k].
 struct Router {
   bool grouped = false;
@@ -382,7 +407,8 @@ moe_status forward_impl(const void* x, const void* logits, moe_dtype logits_dt, 
                         int64_t H, int64_t I, int64_t E, int64_t top_k, const Router& router,
                         const void* w_gate, const void* w_up, const void* w_down, moe_dtype dt,
                         void* out, uint32_t* indices_out, void* weights_out, void* ws,
-                        size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream) {
+                        size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream,
+                        const QuantWeights* quant = nullptr) {
   if (H < 1 || I < 1) return MOE_ERROR_SHAPE;
   moe_status st = MOE_SUCCESS;
   if (!valid_dt(dt)) return MOE_ERROR_DTYPE;
@@ -392,7 +418,7 @@ moe_status forward_impl(const void* x, const void* logits, moe_dtype logits_dt, 
   const ForwardLayout L = forward_layout(T, H, I, E, top_k, dt, logits_dt);
   if (!ws || ((uintptr_t)ws & 255) || ws_bytes < L.total) return MOE_ERROR_WORKSPACE;
   const size_t ds = dtype_size(dt), ls = dtype_size(logits_dt), slots = (size_t)(T * top_k);
-  const size_t wbytes = (size_t)E * (size_t)I * (size_t)H * ds;
+  const size_t wbytes = quant ? quant_bytes(E, I, H, quant->bits) : (size_t)E * (size_t)I * (size_t)H * ds;
   const Span outs[] = {{out, (size_t)T * (size_t)H * ds}, {indices_out, indices_out ? slots * 4 : 0},
                        {weights_out, weights_out ? slots * ls : 0}, {ws, L.total}};
   const Span ins[] = {{x, (size_t)T * (size_t)H * ds}, {logits, (size_t)(T * E) * ls},
@@ -423,6 +449,23 @@ moe_status forward_impl(const void* x, const void* logits, moe_dtype logits_dt, 
   // The gate/up GEMM gathers token rows through slot_of_row; x_disp is never
   // materialised on this path.
   void* h = base + L.experts + gemm_scratch_bytes((int64_t)slots, E, H, I, dt);
+  if (quant) {
+    QuantExperts q = {};
+    q.x = x; q.row_map = sor; q.map_div = (int)top_k; q.offsets = offsets;
+    q.rows = (int)slots; q.E = (int)E; q.H = (int)H; q.I = (int)I; q.dt = dt;
+    q.bits = quant->bits; q.groups = (int)quant->groups;
+    q.w_gate = w_gate; q.w_up = w_up; q.w_down = w_down;
+    q.s_gate = quant->s_gate; q.s_up = quant->s_up; q.s_down = quant->s_down;
+    q.o_gate = quant->o_gate; q.o_up = quant->o_up; q.o_down = quant->o_down;
+    q.h = h; q.expert_out = y;
+    if (e == hipSuccess) e = launch_experts_quant(q, stream);
+    if (e == hipSuccess) e = mark(3);
+    if (e == hipSuccess) e = mark(4);
+    if (e == hipSuccess)
+      e = launch_combine(y, ros, w, logits_dt, (int)T, (int)top_k, (int)H, dt, out, stream);
+    if (e == hipSuccess) e = mark(5);
+    return from_hip(e);
+  }
   if (e == hipSuccess)
     e = launch_gate_up(x, sor, (int)top_k, offsets, (int)slots, (int)E, (int)H, (int)I, w_gate,
                        w_up, dt, h, base + L.experts, stream);
@@ -596,6 +639,84 @@ moe_status moe_combine_add_rmsnorm_special(
                               zero_num, copy_num, const_num, ori_x, const_alpha1, const_alpha2,
                               const_v, active, mask_dims, shared, residual, gamma, eps, y, x_out,
                               rstd, stream);
+}
+
+size_t moe_experts_quant_workspace_size(int64_t rows, int64_t E, int64_t H, int64_t I,
+                                        moe_dtype dt) {
+  if (rows < 0 || E < 1 || H < 1 || I < 1 || !valid_dt(dt)) return 0;
+  return align256((size_t)rows * (size_t)I * dtype_size(dt)) + 256;
+}
+
+moe_status moe_experts_forward_dispatched_quant(
+    const void* x_disp, const int32_t* expert_offsets, int64_t rows, int64_t E, int64_t H, int64_t I,
+    const void* w_gate, const void* w_up, const void* w_down, int bits, int64_t groups,
+    const void* scale_gate, const void* scale_up, const void* scale_down, const void* offset_gate,
+    const void* offset_up, const void* offset_down, moe_dtype dt, void* expert_out, void* ws,
+    size_t ws_bytes, hipStream_t stream) {
+  if (rows < 0 || E < 1 || H < 1 || I < 1) return MOE_ERROR_SHAPE;
+  if (!valid_dt(dt)) return MOE_ERROR_DTYPE;
+  moe_status st = check_quant_args(rows, E, H, I, bits, groups, dt);
+  if (st != MOE_SUCCESS) return st;
+  if (rows == 0) return MOE_SUCCESS;
+  if (!x_disp || !expert_offsets || !w_gate || !w_up || !w_down || !expert_out || !scale_gate ||
+      !scale_up || !scale_down)
+    return MOE_ERROR_NULL_POINTER;
+  const size_t need = moe_experts_quant_workspace_size(rows, E, H, I, dt);
+  if (!ws || ((uintptr_t)ws & 255) || ws_bytes < need) return MOE_ERROR_WORKSPACE;
+  const size_t ds = dtype_size(dt), qb = quant_bytes(E, I, H, bits);
+  const size_t sb = (size_t)E * (size_t)groups * ds;
+  const Span outs[] = {{expert_out, (size_t)rows * (size_t)H * ds}, {ws, need}};
+  const Span ins[] = {{x_disp, (size_t)rows * (size_t)H * ds}, {expert_offsets, (size_t)(E + 1) * 4},
+                      {w_gate, qb}, {w_up, qb}, {w_down, qb},
+                      {scale_gate, sb * (size_t)I}, {scale_up, sb * (size_t)I}, {scale_down, sb * (size_t)H},
+                      {offset_gate, offset_gate ? sb * (size_t)I : 0}, {offset_up, offset_up ? sb * (size_t)I : 0},
+                      {offset_down, offset_down ? sb * (size_t)H : 0}};
+  if (any_overlap(outs, 2, ins, 11)) return MOE_ERROR_ARGUMENT;
+  const void* ptrs[] = {x_disp, expert_offsets, w_gate, w_up, w_down, scale_gate, scale_up,
+                        scale_down, offset_gate, offset_up, offset_down, expert_out, ws};
+  if ((st = check_device(ptrs, 13, stream)) != MOE_SUCCESS) return st;
+  QuantExperts q = {};
+  q.x = x_disp; q.row_map = nullptr; q.map_div = 1; q.offsets = expert_offsets;
+  q.rows = (int)rows; q.E = (int)E; q.H = (int)H; q.I = (int)I; q.dt = dt;
+  q.bits = bits; q.groups = (int)groups;
+  q.w_gate = w_gate; q.w_up = w_up; q.w_down = w_down;
+  q.s_gate = scale_gate; q.s_up = scale_up; q.s_down = scale_down;
+  q.o_gate = offset_gate; q.o_up = offset_up; q.o_down = offset_down;
+  q.h = ws; q.expert_out = expert_out;
+  return from_hip(launch_experts_quant(q, stream));
+}
+
+moe_status moe_forward_quant(const void* x, const void* logits, moe_dtype logits_dt, int64_t T,
+                             int64_t H, int64_t I, int64_t E, int64_t top_k, int renormalize,
+                             const void* w_gate, const void* w_up, const void* w_down, int bits,
+                             int64_t groups, const void* scale_gate, const void* scale_up,
+                             const void* scale_down, const void* offset_gate,
+                             const void* offset_up, const void* offset_down, moe_dtype dt,
+                             void* out, uint32_t* indices_out, void* weights_out, void* ws,
+                             size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream) {
+  if (H < 1 || I < 1) return MOE_ERROR_SHAPE;
+  moe_status st = check_route_args(T, E, top_k, logits_dt);
+  if (st != MOE_SUCCESS) return st;
+  if (!valid_dt(dt)) return MOE_ERROR_DTYPE;
+  if ((st = check_quant_args(T * top_k, E, H, I, bits, groups, dt)) != MOE_SUCCESS) return st;
+  if (T > 0 && (!scale_gate || !scale_up || !scale_down)) return MOE_ERROR_NULL_POINTER;
+  const size_t ds = dtype_size(dt), sb = (size_t)E * (size_t)groups * ds;
+  const Span scales[] = {{scale_gate, sb * (size_t)I}, {scale_up, sb * (size_t)I},
+                         {scale_down, sb * (size_t)H}, {offset_gate, offset_gate ? sb * (size_t)I : 0},
+                         {offset_up, offset_up ? sb * (size_t)I : 0},
+                         {offset_down, offset_down ? sb * (size_t)H : 0}};
+  const Span outs[] = {{out, (size_t)T * (size_t)H * ds}, {ws, ws_bytes}};
+  if (any_overlap(outs, 2, scales, 6)) return MOE_ERROR_ARGUMENT;
+  const void* sptrs[] = {scale_gate, scale_up, scale_down, offset_gate, offset_up, offset_down};
+  if (T > 0 && (st = check_device(sptrs, 6, stream)) != MOE_SUCCESS) return st;
+  Router r;
+  r.renormalize = renormalize ? 1 : 0;
+  QuantWeights qw;
+  qw.bits = bits; qw.groups = groups;
+  qw.s_gate = scale_gate; qw.s_up = scale_up; qw.s_down = scale_down;
+  qw.o_gate = offset_gate; qw.o_up = offset_up; qw.o_down = offset_down;
+  return forward_impl(x, logits, logits_dt, T, H, I, E, top_k, r, w_gate, w_up, w_down, dt, out,
+                      indices_out, weights_out, ws, ws_bytes, stage_events, stream, &qw);
 }
 
 }  // extern "C"

@@ -118,4 +118,26 @@ struct SpecialCombine {
 };
 hipError_t launch_combine_special(const SpecialCombine& c, int T, hipStream_t s);
 
+// Weight-only quantised experts (INT8 / INT4 with per-channel or per-group
+// scale and offset) on the decode path: both GEMMs, h in the caller's buffer.
+struct QuantExperts {
+  const void* x;            // tokens [*, H] read through row_map / map_div, or dispatched rows
+  const int32_t* row_map;
+  int map_div;
+  const int32_t* offsets;   // [E+1]
+  int rows, E, H, I, dt, bits, groups;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  const void* s_gate;
+  const void* s_up;
+  const void* s_down;
+  const void* o_gate;
+  const void* o_up;
+  const void* o_down;
+  void* h;                  // [rows, I]
+  void* expert_out;         // [rows, H]
+};
+hipError_t launch_experts_quant(const QuantExperts& q, hipStream_t s);
+
 }  // namespace moe

@@ -1,0 +1,296 @@
+// Weight-only quantised experts on the decode path (aclnnFFN, formula of the
+// pseudo-quantization scenario: each weight matrix W, stored as INT8 or
+// INT4, enters the product as (W + antiquantOffset) * antiquantScale, with
+// one scale/offset per output channel, or, for INT4, per group of
+// consecutive input channels).
+//
+// Layouts (K = input channels, contiguous like the bf16 weights):
+//   INT8  [E, N, K] int8;  INT4 [E, N, K/2] bytes, element k in byte k/2,
+//   low nibble first, two's complement (-8..7);
+//   scale, offset [E, N, G] in the model dtype, G groups of K/G consecutive
+//   input channels (G = 1: per channel; K/G a multiple of 128, so a
+//   128-channel K-iteration never straddles two groups); offset may be
+//   absent (0).
+//
+// Same structure as the bf16 weight-streaming kernel: one workgroup of 4
+// wavefronts per (expert, block of 64 weight rows), K split four ways and
+// reduced in LDS, MFMA 16x16x32 with A = 16 weight rows and B = 16 token
+// rows. A lane's 8 weights per MFMA step are 8 (INT8) or 4 (INT4) bytes;
+// they are dequantised in registers as q * s + (o * s) in fp32 and packed to
+// the model dtype before the MFMA. The next K-iteration's weight, scale and
+// activation loads are issued before the current iteration's MFMAs.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int kRsrcFlagsQ = 0x00020000;
+constexpr uint32_t kOutOfRangeQ = 0x80000000u;
+constexpr int kQRows = 64;     // weight rows per workgroup (4 MFMA tiles of 16)
+constexpr int kQTokens = 16;
+constexpr int kQKIter = 128;
+constexpr int kQWaves = 4;
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+template <typename T> struct MfmaQ;
+template <> struct MfmaQ<bf16> {
+  typedef bf16x8 Frag;
+  static __device__ __forceinline__ f32x4 run(Frag a, Frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct MfmaQ<f16> {
+  typedef f16x8 Frag;
+  static __device__ __forceinline__ f32x4 run(Frag a, Frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+__device__ __forceinline__ float silu_q(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
+
+// 8 quantised weights of one lane (one MFMA operand fragment).
+template <int kBits> struct QWords;
+template <> struct QWords<8> { u32x2 v; };
+template <> struct QWords<4> { uint32_t v; };
+
+template <int kBits>
+__device__ __forceinline__ QWords<kBits> load_q(__amdgpu_buffer_rsrc_t r, uint32_t vo, uint32_t soff) {
+  QWords<kBits> q;
+  if constexpr (kBits == 8)
+    q.v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, vo, soff, 0));
+  else
+    q.v = __builtin_amdgcn_raw_buffer_load_b32(r, vo, soff, 0);
+  return q;
+}
+
+// Signed value i (0..7) of a fragment.
+template <int kBits>
+__device__ __forceinline__ float q_at(const QWords<kBits>& q, int i) {
+  if constexpr (kBits == 8) {
+    const uint32_t w = i < 4 ? q.v.x : q.v.y;
+    return (float)(int)(int8_t)(w >> (8 * (i & 3)));
+  } else {
+    return (float)((int)(q.v << (28 - 4 * i)) >> 28);
+  }
+}
+
+struct QuantArgs {
+  const void* a;          // activations [a_rows, K]
+  const int32_t* a_map;   // optional: A row r is a[a_map[r] / a_div]
+  int a_div, a_rows;
+  const uint8_t* b0;      // quantised gate (GEMM 1) or down (GEMM 2)
+  const uint8_t* b1;      // quantised up (GEMM 1)
+  const void* s0;         // scales  [E, N, G]
+  const void* s1;
+  const void* o0;         // offsets [E, N, G] or null
+  const void* o1;
+  void* c;                // [rows, N]
+  const int32_t* offsets; // [E+1]
+  int rows, N, K, G, E, n_blocks, k_quarter;
+};
+
+template <typename T, bool kSwiGlu, int kBits>
+__global__ __launch_bounds__(64 * kQWaves) void skinny_quant_kernel(QuantArgs p) {
+  typedef typename MfmaQ<T>::Frag Frag;
+  __shared__ f32x4 red[kQWaves - 1][4][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int e = blockIdx.x / p.n_blocks;
+  const int nb = blockIdx.x - e * p.n_blocks;
+  if (e >= p.E) return;
+  const int r_begin = max(__builtin_amdgcn_readfirstlane(p.offsets[e]), 0);
+  const int r_end = min(__builtin_amdgcn_readfirstlane(p.offsets[e + 1]), p.rows);
+  if (r_end <= r_begin) return;
+
+  const int K = p.K, N = p.N, G = p.G;
+  const int gsz = K / G;  // input channels per group (multiple of 8)
+  const int k_lo = wave * p.k_quarter;
+  const int k_hi = min(K, k_lo + p.k_quarter);
+  const uint32_t qrow = (uint32_t)K * kBits / 8;  // bytes per quantised row
+  const int64_t expert_rows = (int64_t)e * N;
+  const int q_bytes = (int)((uint32_t)N * qrow);
+  const __amdgpu_buffer_rsrc_t rw0 = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.b0 + expert_rows * qrow), (short)0, q_bytes, kRsrcFlagsQ);
+  const __amdgpu_buffer_rsrc_t rw1 = kSwiGlu
+      ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.b1 + expert_rows * qrow), (short)0,
+                                          q_bytes, kRsrcFlagsQ)
+      : rw0;
+  const uint32_t xrow = (uint32_t)K * sizeof(T);
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(p.a), (short)0, (int)((uint32_t)p.a_rows * xrow), kRsrcFlagsQ);
+
+  // Weight rows of the 4 tiles; rows past N read as zero and get scale 0.
+  const int g = lane >> 4;
+  uint32_t vo_w[4];
+  int wrow[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int n = kSwiGlu ? nb * 32 + (t & 1) * 16 + (lane & 15) : nb * kQRows + t * 16 + (lane & 15);
+    wrow[t] = n;
+    vo_w[t] = (uint32_t)n * qrow + (uint32_t)g * kBits;  // 8 values = kBits bytes
+  }
+  const T* sp0 = static_cast<const T*>(p.s0) + expert_rows * G;
+  const T* sp1 = kSwiGlu ? static_cast<const T*>(p.s1) + expert_rows * G : sp0;
+  const T* op0 = p.o0 ? static_cast<const T*>(p.o0) + expert_rows * G : nullptr;
+  const T* op1 = kSwiGlu ? (p.o1 ? static_cast<const T*>(p.o1) + expert_rows * G : nullptr) : op0;
+
+  T* C = static_cast<T*>(p.c);
+  for (int rg = r_begin; rg < r_end; rg += kQTokens) {
+    const int xr = rg + (lane & 15);
+    uint32_t vo_x = kOutOfRangeQ;
+    if (xr < r_end) {
+      const int src = p.a_map ? min(max(p.a_map[xr] / p.a_div, 0), p.a_rows - 1) : xr;
+      vo_x = (uint32_t)src * xrow + (uint32_t)g * 16u;
+    }
+    f32x4 acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Scale and offset*scale of tile t for the group holding the 128
+    // input channels kb .. kb+127 (groups are multiples of 128 long).
+    auto load_sc = [&](int kb, float (&sc)[4], float (&os)[4]) {
+      const int grp = min(kb, K - 1) / gsz;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const bool up = kSwiGlu && t >= 2;
+        const int n = wrow[t];
+        float s = 0.f, o = 0.f;
+        if (n < N && kb < k_hi) {
+          s = to_f32((up ? sp1 : sp0)[(int64_t)n * G + grp]);
+          const T* op = up ? op1 : op0;
+          o = op ? to_f32(op[(int64_t)n * G + grp]) : 0.f;
+        }
+        sc[t] = s;
+        os[t] = o * s;
+      }
+    };
+    QWords<kBits> wa[4][4], wb[4][4];
+    uint4 xa[4], xb[4];
+    float sa_[4], oa[4], sb_[4], ob[4];
+    auto load = [&](int kb, QWords<kBits> (&w)[4][4], uint4 (&x)[4], float (&sc)[4], float (&os)[4]) {
+      const uint32_t soff_q = (uint32_t)kb * kBits / 8;
+      const uint32_t soff_x = (uint32_t)kb * sizeof(T);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const bool ok = kb + c * 32 + g * 8 < k_hi;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          w[t][c] = load_q<kBits>((kSwiGlu && t >= 2) ? rw1 : rw0,
+                                  ok ? vo_w[t] + (uint32_t)c * 4u * kBits : kOutOfRangeQ, soff_q);
+        x[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+            rx, ok ? vo_x + c * 64u : kOutOfRangeQ, soff_x, 0));
+      }
+      load_sc(kb, sc, os);
+    };
+    auto compute = [&](const QWords<kBits> (&w)[4][4], const uint4 (&x)[4], const float (&sc)[4],
+                       const float (&os)[4]) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          Frag f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) f[i] = from_f32<T>(fmaf(q_at<kBits>(w[t][c], i), sc[t], os[t]));
+          acc[t] = MfmaQ<T>::run(f, __builtin_bit_cast(Frag, x[c]), acc[t]);
+        }
+    };
+    const int n_iter = (k_hi - k_lo + kQKIter - 1) / kQKIter;
+    if (n_iter > 0) {
+      load(k_lo, wa, xa, sa_, oa);
+      int it = 0;
+      for (; it + 2 <= n_iter; it += 2) {
+        load(k_lo + (it + 1) * kQKIter, wb, xb, sb_, ob);
+        compute(wa, xa, sa_, oa);
+        load(k_lo + (it + 2) * kQKIter, wa, xa, sa_, oa);
+        compute(wb, xb, sb_, ob);
+      }
+      if (it < n_iter) compute(wa, xa, sa_, oa);  // odd count: wa holds the last iteration
+    }
+
+    // Partial sums of wavefronts 1..3 meet wavefront 0's in LDS (fixed order).
+    if (wave > 0) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) red[wave - 1][t][lane] = acc[t];
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int w = 0; w < kQWaves - 1; ++w)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[t] += red[w][t][lane];
+      // D element v of lane l: weight row (l/16)*4 + v of the tile, token l%16.
+      const int tok = rg + (lane & 15);
+      if (tok < r_end) {
+        T* crow = C + (int64_t)tok * N;
+        if (kSwiGlu) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int col = nb * 32 + t * 16 + g * 4;
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              if (col + v < N) crow[col + v] = from_f32<T>(silu_q(acc[t][v]) * acc[t + 2][v]);
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int col = nb * kQRows + t * 16 + g * 4;
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              if (col + v < N) crow[col + v] = from_f32<T>(acc[t][v]);
+          }
+        }
+      }
+    }
+    __syncthreads();  // red[] is reused by the next row group
+  }
+}
+
+template <typename T, int kBits>
+void launch_q(QuantArgs p, bool swiglu, hipStream_t s) {
+  p.n_blocks = swiglu ? (p.N + 31) / 32 : (p.N + kQRows - 1) / kQRows;
+  const int iters = (p.K + kQKIter - 1) / kQKIter;
+  p.k_quarter = (iters + kQWaves - 1) / kQWaves * kQKIter;
+  const dim3 grid((unsigned)((int64_t)p.E * p.n_blocks));
+  if (swiglu)
+    hipLaunchKernelGGL((skinny_quant_kernel<T, true, kBits>), grid, dim3(64 * kQWaves), 0, s, p);
+  else
+    hipLaunchKernelGGL((skinny_quant_kernel<T, false, kBits>), grid, dim3(64 * kQWaves), 0, s, p);
+}
+
+template <typename T>
+void launch_q_bits(const QuantArgs& p, int bits, bool swiglu, hipStream_t s) {
+  if (bits == 8) launch_q<T, 8>(p, swiglu, s);
+  else launch_q<T, 4>(p, swiglu, s);
+}
+
+}  // namespace
+
+hipError_t launch_experts_quant(const QuantExperts& q, hipStream_t s) {
+  if (q.rows == 0) return hipSuccess;
+  QuantArgs p = {};
+  p.offsets = q.offsets;
+  p.rows = q.rows;
+  p.E = q.E;
+  // GEMM 1: h = SiLU(x Wg^T) * (x Wu^T), K = H, N = I
+  p.a = q.x; p.a_map = q.row_map; p.a_div = q.map_div > 0 ? q.map_div : 1;
+  p.a_rows = q.row_map ? (q.rows + p.a_div - 1) / p.a_div : q.rows;
+  p.b0 = static_cast<const uint8_t*>(q.w_gate); p.b1 = static_cast<const uint8_t*>(q.w_up);
+  p.s0 = q.s_gate; p.s1 = q.s_up; p.o0 = q.o_gate; p.o1 = q.o_up;
+  p.c = q.h; p.N = q.I; p.K = q.H; p.G = q.groups;
+  if (q.dt == kF16) launch_q_bits<f16>(p, q.bits, true, s);
+  else launch_q_bits<bf16>(p, q.bits, true, s);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  // GEMM 2: expert_out = h Wd^T, K = I, N = H
+  p.a = q.h; p.a_map = nullptr; p.a_div = 1; p.a_rows = q.rows;
+  p.b0 = static_cast<const uint8_t*>(q.w_down); p.b1 = nullptr;
+  p.s0 = q.s_down; p.s1 = nullptr; p.o0 = q.o_down; p.o1 = nullptr;
+  p.c = q.expert_out; p.N = q.H; p.K = q.I;
+  if (q.dt == kF16) launch_q_bits<f16>(p, q.bits, false, s);
+  else launch_q_bits<bf16>(p, q.bits, false, s);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -52,6 +52,11 @@ _SIGS = {
                              P, P, P], I32),
     "moe_combine_add_rmsnorm_special": ([P, P, P, P, I32, I64, I64, I64, I32, I64, I64, I64, I64, P, P,
                                          P, P, P, I32, P, P, P, ctypes.c_float, P, P, P, P], I32),
+    "moe_experts_forward_dispatched_quant": ([P, P, I64, I64, I64, I64, P, P, P, I32, I64, P, P, P, P, P, P,
+                                              I32, P, P, SZ, P], I32),
+    "moe_experts_quant_workspace_size": ([I64, I64, I64, I64, I32], SZ),
+    "moe_forward_quant": ([P, P, I32, I64, I64, I64, I64, I64, I32, P, P, P, I32, I64, P, P, P, P, P, P, I32,
+                           P, P, P, P, SZ, P, P], I32),
     "moe_route_sigmoid_grouped": ([P, I32, I64, I64, P, I64, I64, I64, I32, I32, ctypes.c_float, P, P, P],
                                   I32),
     "moe_forward_sigmoid_grouped": ([P, P, I32, I64, I64, I64, I64, P, I64, I64, I64, I32, I32,
@@ -322,6 +327,50 @@ def moe_forward_sigmoid_grouped(x, logits, top_k: int, groups: int, selected_gro
         selected_groups, int(group_top_two), int(renormalize), float(scale), _ptr(w_gate),
         _ptr(w_up), _ptr(w_down), dtype_code(x.dtype), _ptr(out), _ptr(indices_out),
         _ptr(weights_out), _ptr(ws), ws.numel(), ev, _stream()), "moe_forward_sigmoid_grouped")
+    return out
+
+
+def moe_experts_forward_dispatched_quant(x_disp, expert_offsets, w_gate, w_up, w_down, bits: int,
+                                         scales, offsets=(None, None, None), groups: int = 1,
+                                         expert_out=None, ws=None):
+    """Weight-only quantised experts (decode-sized batches). w_*: uint8/int8
+    tensors [E, N, K*bits/8]; scales/offsets: (gate, up, down) tensors
+    [E, N, groups] in x_disp's dtype (offsets None for 0)."""
+    rows, H = x_disp.shape
+    E, I = w_gate.shape[0], w_gate.shape[1]
+    if expert_out is None:
+        expert_out = torch.empty((rows, H), dtype=x_disp.dtype, device=x_disp.device)
+    if ws is None:
+        ws = _workspace(lib().moe_experts_quant_workspace_size(rows, E, H, I, dtype_code(x_disp.dtype)),
+                        x_disp.device)
+    _check(lib().moe_experts_forward_dispatched_quant(
+        _ptr(x_disp), _ptr(expert_offsets), rows, E, H, I, _ptr(w_gate), _ptr(w_up), _ptr(w_down), bits,
+        groups, *[_ptr(t) for t in scales], *[_ptr(t) for t in offsets], dtype_code(x_disp.dtype),
+        _ptr(expert_out), _ptr(ws), ws.numel(), _stream()), "moe_experts_forward_dispatched_quant")
+    return expert_out
+
+
+def moe_forward_quant(x, logits, top_k: int, renormalize: bool, w_gate, w_up, w_down, bits: int, scales,
+                      offsets=(None, None, None), groups: int = 1, out=None, indices_out=None,
+                      weights_out=None, ws=None, stage_events=None):
+    """moe_forward with weight-only quantised experts (see the dispatched variant)."""
+    T, H = x.shape
+    E = logits.shape[1]
+    I = w_gate.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=x.dtype, device=x.device)
+    if ws is None:
+        ws = _workspace(moe_forward_workspace_size(T, H, I, E, top_k, x.dtype, logits.dtype), x.device)
+    ev = None
+    if stage_events is not None:
+        if len(stage_events) != 6:
+            raise ValueError("stage_events needs 6 events")
+        ev = (ctypes.c_void_p * 6)(*[_event_handle(e) for e in stage_events])
+    _check(lib().moe_forward_quant(
+        _ptr(x), _ptr(logits), dtype_code(logits.dtype), T, H, I, E, top_k, int(renormalize), _ptr(w_gate),
+        _ptr(w_up), _ptr(w_down), bits, groups, *[_ptr(t) for t in scales], *[_ptr(t) for t in offsets],
+        dtype_code(x.dtype), _ptr(out), _ptr(indices_out), _ptr(weights_out), _ptr(ws), ws.numel(), ev,
+        _stream()), "moe_forward_quant")
     return out
 
 

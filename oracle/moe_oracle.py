@@ -297,6 +297,69 @@ def swiglu_expert(x_rows: np.ndarray, w_gate_e: np.ndarray, w_up_e: np.ndarray,
     return round_to(h @ decode(w_down_e, dtype).T, dtype)
 
 
+def swiglu_expert_f64(x_rows, w_gate, w_up, w_down, dtype):
+    """swiglu_expert with the three weight matrices given as fp64 arrays (the
+    decoded dequantised weights); x_rows stored in dtype; same roundings of h
+    and y."""
+    x = decode(x_rows, dtype)
+    g = x @ w_gate.T
+    u = x @ w_up.T
+    h = decode(round_to(silu(g) * u, dtype), dtype)
+    return round_to(h @ w_down.T, dtype)
+
+
+# --------------------------------------------------------------------------
+# weight-only quantised experts  (aclnnFFN, "Formula", pseudo-quantization
+# scenario: W enters as (W + antiquantOffset) * antiquantScale)
+# --------------------------------------------------------------------------
+def unpack_int4(packed: np.ndarray) -> np.ndarray:
+    """[..., K/2] bytes -> [..., K] integers: element k lives in byte k // 2,
+    low nibble for even k, as a two's complement 4-bit value (-8 .. 7)."""
+    b = np.asarray(packed, np.uint8)
+    lo = (b & 0x0F).astype(np.int16)
+    hi = (b >> 4).astype(np.int16)
+    out = np.stack([lo, hi], axis=-1).reshape(*b.shape[:-1], b.shape[-1] * 2)
+    return np.where(out >= 8, out - 16, out)
+
+
+def dequant_weight(q, bits, scale, offset, groups, dtype):
+    """One expert's weight matrix [N, K] in the model dtype, returned as the
+    fp64 values of its stored elements:
+    w[n, k] = dtype((q[n, k] + offset[n, j]) * scale[n, j]), j = k // (K / groups).
+    The pseudo-quantisation formula brackets the dequantised weight as a
+    tensor of its own and gives scale and offset the activation dtype; it
+    does not say in what precision that tensor is held. Reading taken: it is
+    held in the activation dtype, as the weights of the unquantised path are,
+    so (q + offset) * scale is formed exactly and rounded once to dtype.
+    q: int8 [N, K] (bits 8) or packed int4 bytes [N, K/2] (bits 4); scale,
+    offset: [N, groups] stored in dtype (offset None = 0)."""
+    qi = unpack_int4(q) if bits == 4 else np.asarray(q).view(np.int8).astype(np.int16)
+    N, K = qi.shape
+    gs = K // groups
+    sc = np.repeat(decode(scale, dtype).reshape(N, groups), gs, axis=1)
+    off = 0.0 if offset is None else np.repeat(decode(offset, dtype).reshape(N, groups), gs, axis=1)
+    return decode(round_to((qi.astype(np.float64) + off) * sc, dtype), dtype)
+
+
+def experts_forward_quant(x_disp, offsets, quant_of, bits, groups, dtype):
+    """Expert outputs for every dispatched row with quantised weights.
+    quant_of(e) -> ((q_gate, s_gate, o_gate), (q_up, s_up, o_up),
+    (q_down, s_down, o_down)) for expert e."""
+    def weights_f64(e):
+        return [dequant_weight(q, bits, sc, off, groups, dtype) for q, sc, off in quant_of(e)]
+    R = int(offsets[-1])
+    out = None
+    for e in range(len(offsets) - 1):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if a == b:
+            continue
+        y = swiglu_expert_f64(x_disp[a:b], *weights_f64(e), dtype)
+        if out is None:
+            out = np.empty((R, y.shape[1]), dtype=y.dtype)
+        out[a:b] = y
+    return out
+
+
 def experts_forward_dispatched(x_disp: np.ndarray, offsets: np.ndarray, weights_of, dtype: str):
     """Expert outputs for every dispatched row, in dispatched order.
     weights_of(e) -> (gate [I,H], up [I,H], down [H,I]) for expert e."""

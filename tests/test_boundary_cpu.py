@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 21, names
     lib = moe.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -199,3 +199,29 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(moe, "_LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(RuntimeError, match="missing"):
         moe.lib()
+
+
+def test_quant_validation():
+    f = moe.lib().moe_experts_forward_dispatched_quant
+    need = moe.lib().moe_experts_quant_workspace_size(64, 16, 512, 384, 2)
+    # x, offsets, rows, E, H, I, wg, wu, wd, bits, groups, sg, su, sd, og, ou, od, dt, out, ws, wsb, stream
+    base = [FAKE, FAKE + 2**20, 64, 16, 512, 384, FAKE + 2**21, FAKE + 2**22, FAKE + 2**23, 8, 1,
+            FAKE + 2**24, FAKE + 2**25, FAKE + 2**26, None, None, None, 2, FAKE + 2**27, FAKE + 2**28, need, None]
+
+    def call(i=None, v=None, **kw):
+        a = list(base)
+        if i is not None:
+            a[i] = v
+        return f(*a)
+
+    assert call(9, 5) == S["MOE_ERROR_ARGUMENT"]          # bits
+    assert call(10, 3) == S["MOE_ERROR_ARGUMENT"]         # groups does not divide 384? 512 % 3
+    assert call(10, 4) == S["MOE_ERROR_ARGUMENT"]         # per-group with INT8
+    assert call(17, 0) == S["MOE_ERROR_UNSUPPORTED"]      # fp32
+    assert call(2, 65) == S["MOE_ERROR_UNSUPPORTED"]      # rows > 4 * E: not a decode batch
+    a = list(base)
+    a[9], a[10] = 4, 2                                    # INT4, 2 groups: 512/2 and 384/2 not multiples of 128
+    assert f(*a) == S["MOE_ERROR_UNSUPPORTED"]
+    assert call(11, None) == S["MOE_ERROR_NULL_POINTER"]  # scale missing
+    assert call(20, need - 1) == S["MOE_ERROR_WORKSPACE"]
+    assert call(2, 0) == S["MOE_SUCCESS"]

@@ -640,3 +640,63 @@ def test_activity_mask_is_a_zero_weight_and_empty_token_normalises_residual():
     ref0 = torch.nn.functional.rms_norm(torch.tensor(O.decode(res[:1], "bf16")), (H,),
                                         torch.tensor(gamma.astype(np.float64)), 1e-6)
     np.testing.assert_array_equal(yo[0], O.round_to(ref0.numpy()[0], "bf16"))
+
+
+# --------------------------------------------------------------------------
+# weight-only quantised experts (aclnnFFN, pseudo-quantization scenario)
+# --------------------------------------------------------------------------
+def test_int4_unpacking_hand_values():
+    """Bytes 0x21, 0x8F, 0x7F: low nibble first, two's complement."""
+    got = O.unpack_int4(np.array([[0x21, 0x8F, 0x7F]], np.uint8))
+    assert got.tolist() == [[1, 2, -1, -8, -1, 7]]
+
+
+def test_dequant_closed_forms():
+    # INT8 per channel: (q + o) * s with s = 0.5, o = -1 on row 0; s = 2, no offset on row 1
+    q = np.array([[3, -4, 127, -128], [1, 2, 3, 4]], np.int8)
+    sc = _bf16([[0.5], [2.0]])
+    off = _bf16([[-1.0], [0.0]])
+    w = O.dequant_weight(q.view(np.uint8), 8, sc, off, 1, "bf16")
+    np.testing.assert_array_equal(w, [[1.0, -2.5, 63.0, -64.5], [2, 4, 6, 8]])
+    # INT4 per group: two groups of two channels with scales 1 and 0.25
+    packed = np.array([[0x21, 0x8F]], np.uint8)  # values 1, 2, -1, -8
+    w = O.dequant_weight(packed, 4, _bf16([[1.0, 0.25]]), None, 2, "bf16")
+    np.testing.assert_array_equal(w, [[1.0, 2.0, -0.25, -2.0]])
+
+
+def test_dequant_rounds_once_to_model_dtype():
+    """Scale 1 + 2^-7 (exact in bf16). bf16 spacing is 2^-6 in [2, 4), 2^-5
+    in [4, 8) and 2^-1 in [64, 128):
+    127 * s = 127.9921875 -> 128;  2 * s = 2.015625 exact;
+    -5 * s = -5.0390625 (-161.25 steps of 2^-5) -> -5.03125;
+    3 * s = 3.0234375 is a tie (193.5 steps of 2^-6) -> even, 3.03125.
+    With offset 0.5: 2.5 * s = 2.51953125 -> 2.515625; -4.5 * s =
+    -4.53515625 -> -4.53125; 3.5 * s = 3.52734375 (225.75 steps) -> 3.53125.
+    In fp16 (spacing 2^-9 in [2, 4)) 3 * s = 3.0234375 is exact, while
+    127 * s still rounds to 128 (spacing 2^-4 in [64, 128))."""
+    q = np.array([[127, 2, -5, 3]], np.int8)
+    sc = _bf16([[1.0 + 2.0 ** -7]])
+    w = O.dequant_weight(q.view(np.uint8), 8, sc, None, 1, "bf16")
+    np.testing.assert_array_equal(w, [[128.0, 2.015625, -5.03125, 3.03125]])
+    w = O.dequant_weight(q.view(np.uint8), 8, sc, _bf16([[0.5]]), 1, "bf16")
+    np.testing.assert_array_equal(w, [[128.0, 2.515625, -4.53125, 3.53125]])
+    w = O.dequant_weight(q.view(np.uint8), 8, np.array([[1.0 + 2.0 ** -7]], np.float16), None, 1, "f16")
+    np.testing.assert_array_equal(w[0, [0, 3]], [128.0, 3.0234375])
+
+
+def test_quant_expert_reduces_to_plain_expert():
+    """Integer weights with scale 1 and offset 0 are the same expert as the
+    bf16 weights holding those integers (exact in bf16)."""
+    rng = np.random.default_rng(41)
+    H, I_ = 32, 48
+    x = _bf16(rng.standard_normal((7, H)))
+    qs = [rng.integers(-8, 8, size=s).astype(np.int8) for s in ((I_, H), (I_, H), (H, I_))]
+    packs = [((q[:, 0::2] & 0xF) | ((q[:, 1::2] & 0xF) << 4)).astype(np.uint8) for q in qs]
+    ones = [_bf16(np.ones((q.shape[0], 1))) for q in qs]
+    y4 = O.swiglu_expert_f64(x, *[O.dequant_weight(p, 4, o, None, 1, "bf16") for p, o in zip(packs, ones)],
+                             "bf16")
+    ref = O.swiglu_expert(x, *[_bf16(q.astype(np.float64)) for q in qs], "bf16")
+    np.testing.assert_array_equal(y4, ref)
+    y8 = O.swiglu_expert_f64(x, *[O.dequant_weight(q.view(np.uint8), 8, o, None, 1, "bf16")
+                                  for q, o in zip(qs, ones)], "bf16")
+    np.testing.assert_array_equal(y8, ref)

@@ -647,3 +647,70 @@ def test_special_experts_end_to_end_with_expert_gemms():
                                                "bf16", E, nz, nc, nq, ori, a1, a2, V, active)
     assert_close(host(xo), xx, "bf16", "x_out")
     assert_close(host(yo), yy, "bf16", "y")
+
+
+# ------------------------------------------------- weight-only quantised experts --
+def _quant_experts(g, E, H, I_, bits, groups, dtype, with_offset):
+    """Random quantised gate/up/down weights with scales keeping activations O(1)."""
+    def one(N, K):
+        if bits == 8:
+            q = g.integers(-127, 128, size=(E, N, K)).astype(np.int8).view(np.uint8)
+            spread = 73.0
+        else:
+            v = g.integers(-8, 8, size=(E, N, K)).astype(np.int16)
+            q = ((v[..., 0::2] & 0xF) | ((v[..., 1::2] & 0xF) << 4)).astype(np.uint8)
+            spread = 4.6
+        sc = _store(np.abs(g.standard_normal((E, N, groups))) / (spread * np.sqrt(K)) + 1e-5, dtype)
+        off = _store(g.integers(-2, 3, size=(E, N, groups)).astype(np.float64), dtype) if with_offset else None
+        return q, sc, off
+    return one(I_, H), one(I_, H), one(H, I_)
+
+
+def _qdev(t, dtype):
+    q, sc, off = t
+    return (torch.from_numpy(np.ascontiguousarray(q)).cuda(), dev(sc, dtype),
+            None if off is None else dev(off, dtype))
+
+
+@pytest.mark.parametrize("bits,groups,dtype,with_offset,H,I_", [(8, 1, "bf16", True, 512, 384),
+                                                                (4, 1, "f16", False, 512, 384),
+                                                                (4, 4, "bf16", True, 1024, 512),
+                                                                (8, 1, "bf16", False, 136, 264)])
+def test_quant_experts_dispatched(bits, groups, dtype, with_offset, H, I_):
+    say("quant experts", bits, groups, dtype)
+    g = np.random.default_rng(bits * 10 + groups)
+    E, T, k = 16, 12, 4
+    idx = np.stack([g.permutation(E)[:k] for _ in range(T)]).astype(np.uint32)
+    x = _store(g.standard_normal((T, H)), dtype)
+    d = O.dispatch(idx, E, x)
+    wq = _quant_experts(g, E, H, I_, bits, groups, dtype, with_offset)
+    gd, ud, dd = (_qdev(t, dtype) for t in wq)
+    y = moe.moe_experts_forward_dispatched_quant(dev(d["x_disp"], dtype), dev(d["offsets"]), gd[0], ud[0], dd[0],
+                                                 bits, (gd[1], ud[1], dd[1]), (gd[2], ud[2], dd[2]), groups)
+    torch.cuda.synchronize()
+    quant_of = lambda e: tuple((t[0][e], t[1][e], None if t[2] is None else t[2][e]) for t in wq)  # noqa: E731
+    ref = O.experts_forward_quant(d["x_disp"], d["offsets"], quant_of, bits, groups, dtype)
+    assert_close(host(y), ref, dtype, "quantised experts")
+
+
+@pytest.mark.parametrize("bits,groups", [(8, 1), (4, 4)])
+def test_forward_quant_decode_shape(bits, groups):
+    """The decode workload's shape (T 16, H 4096, I 1536, E 128, top-8, NaN
+    rows) through moe_forward_quant; the oracle on every token."""
+    w = I.workload("decode_nan_rows_bf16")
+    z = I.logits_for(w)
+    x = I.tokens_for(w)
+    g = np.random.default_rng(55 + bits)
+    wq = _quant_experts(g, w.E, w.H, w.I, bits, groups, "bf16", True)
+    gd, ud, dd = (_qdev(t, "bf16") for t in wq)
+    idx = torch.empty((w.T, w.top_k), dtype=torch.int32, device="cuda")
+    out = moe.moe_forward_quant(dev(x, "bf16"), dev(z, "f32"), w.top_k, w.renormalize, gd[0], ud[0], dd[0], bits,
+                                (gd[1], ud[1], dd[1]), (gd[2], ud[2], dd[2]), groups, indices_out=idx)
+    torch.cuda.synchronize()
+    idx_r, w_r = O.route(z, "f32", w.top_k, w.renormalize)
+    assert np.array_equal(host(idx).astype(np.uint32), idx_r)
+    d = O.dispatch(idx_r, w.E, x)
+    quant_of = lambda e: tuple((t[0][e], t[1][e], t[2][e]) for t in wq)  # noqa: E731
+    y = O.experts_forward_quant(d["x_disp"], d["offsets"], quant_of, bits, groups, "bf16")
+    ref = O.combine(y, d["row_of_slot"], w_r, "f32", w.T, w.top_k, "bf16")
+    assert_close(host(out), ref, "bf16", "quantised forward")
