@@ -8,7 +8,13 @@ What it computes (ruDNN user guide, "3. MoE workflow"): logits -> fp32 softmax
 over all experts -> top-k -> compact dispatch -> bias-free SwiGLU experts ->
 weighted combine in token order; plus the fused combine + residual Add +
 RMSNorm epilogue of the CANN page aclnnMoeDistributeCombineAddRmsNormV2
-("function description", formula).
+("function description", formula). Also the next steps built on the same
+data structures: grouped sigmoid routing (ruDNN user guide, "10."), special
+experts and the activity mask (the CANN combine page), weight-only INT8/INT4
+experts (aclnnFFN, pseudo-quantization scenario) and first-order training
+(ruDNN user guide, "12. MoE first-order training": router weights for a fixed
+selection and their backward, combine_backward, the experts' training cache
+and backward, dispatch_backward).
 
 Precision policy:
   * softmax: computed exactly (fp64) from the fp32-widened logits and rounded
@@ -24,8 +30,8 @@ Every function is a direct statement of the definition, vectorised with numpy
 where that keeps it readable. Library primitives used: exp, sum, matmul,
 lexsort.
 
-Parity pins for every function live in tests/test_oracle_pins.py; no function
-here is "parity unpinned".
+Parity pins for every function live in tests/test_oracle_pins.py and
+tests/test_oracle_training_pins.py; no function here is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -535,3 +541,201 @@ def expert_out_rows(x, indices, tokens, weights_of, dtype):
         for (t, j), yr in zip(pairs, y):
             out[(t, j)] = yr
     return out
+
+
+# --------------------------------------------------------------------------
+# training: weights for a fixed selection and the backward pass  (ruDNN
+# user guide, "12. MoE first-order training")
+# --------------------------------------------------------------------------
+SOFTMAX, SIGMOID = 0, 1
+
+
+def _index_rows_invalid(indices, E):
+    """Rows holding an index outside [0, E): their weights and gradients are NaN."""
+    i = np.asarray(indices).astype(np.int64)
+    return ((i < 0) | (i >= E)).any(axis=1)
+
+
+def router_selected_weights(logits, logits_dtype, indices, scoring, normalize, scale):
+    """selected_router_weights: fp32 [T, k] weights of a fixed selection.
+    scoring SOFTMAX: the fp32 softmax over all E gathered at the indices;
+    SIGMOID: the fp32 sigmoid of the selected logits. Repeated indices gather
+    the same score again. With normalize the k gathered scores are divided by
+    their sum; then every weight is multiplied by scale. A row holding an
+    index outside [0, E) is NaN throughout."""
+    z = decode(logits, logits_dtype)
+    T, E = z.shape
+    idx = np.asarray(indices).astype(np.int64)
+    bad = _index_rows_invalid(idx, E)
+    safe = np.where(bad[:, None], 0, idx)
+    score = softmax_fp32(logits, logits_dtype) if scoring == SOFTMAX else sigmoid_fp32(logits, logits_dtype)
+    s = np.take_along_axis(score, safe, axis=1).astype(np.float64)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        w = s / s.sum(axis=1, keepdims=True) if normalize else s
+    w = w * float(np.float32(scale))
+    w[bad] = np.nan
+    return w.astype(np.float32)
+
+
+def router_selected_backward(logits, logits_dtype, indices, grad_weights, scoring, normalize, scale):
+    """selected_router_backward: d loss / d logits [T, E] in the logits dtype,
+    for the weights of router_selected_weights with the selection held fixed.
+    By the chain rule, with a the gathered score of slot j, S the sum of the
+    gathered scores (normalize) and c the scale:
+        w_j = c * a_j / S            (S = 1 without normalize)
+        dw_j/dz_e = c * (da_j/dz_e / S - a_j / S^2 * sum_m da_m/dz_e)
+    where for the softmax da_j/dz_e = p_{i_j} (delta(i_j, e) - p_e) and for
+    the sigmoid da_j/dz_e = delta(i_j, e) s_e (1 - s_e). The scores are the
+    exact fp64 ones; the Jacobian is formed explicitly, token by token."""
+    z = decode(logits, logits_dtype)
+    T, E = z.shape
+    idx = np.asarray(indices).astype(np.int64)
+    k = idx.shape[1]
+    g = np.asarray(grad_weights, np.float32).astype(np.float64).reshape(T, k)
+    c = float(np.float32(scale))
+    bad = _index_rows_invalid(idx, E)
+    out = np.full((T, E), np.nan)
+    for t in range(T):
+        if bad[t]:
+            continue
+        zt = z[t]
+        if scoring == SOFTMAX:
+            if invalid_rows(zt[None, :])[0]:
+                continue
+            a_all = np.exp(zt - zt.max())
+            p = a_all / a_all.sum()
+            dscore = np.diag(p) - np.outer(p, p)      # d p_a / d z_e
+            score = p
+        else:
+            with np.errstate(over="ignore"):
+                s = 1.0 / (1.0 + np.exp(-zt))
+            dscore = np.diag(s * (1.0 - s))
+            score = s
+        a = score[idx[t]]                              # [k]
+        da = dscore[idx[t]]                            # [k, E]
+        if normalize:
+            S = a.sum()
+            jac = c * (da / S - np.outer(a, da.sum(axis=0)) / S ** 2)
+        else:
+            jac = c * da
+        out[t] = g[t] @ jac
+    return round_to(out, logits_dtype)
+
+
+def combine_backward(expert_out, row_of_slot, weights, w_dtype, grad_out, T, k, dtype):
+    """combine_backward of out[t] = sum_j w[t,j] y[row(t,j)]:
+      dexpert[row(t,j)] = w[t,j] * grad_out[t]          (model dtype, one rounding)
+      dweights[t, j]    = sum_h grad_out[t,h] y[row(t,j),h]   (fp32)
+    A slot without a dispatched row has dweights NaN (the forward made that
+    token's row NaN) and no dexpert row."""
+    rows = np.asarray(row_of_slot).astype(np.int64).reshape(T, k)
+    w = decode(weights, w_dtype).reshape(T, k)
+    go = decode(grad_out, dtype)
+    y = decode(expert_out, dtype)
+    R, H = y.shape
+    dexp = np.zeros((R, H))
+    dw = np.full((T, k), np.nan)
+    for t in range(T):
+        for j in range(k):
+            r = rows[t, j]
+            if r < 0:
+                continue
+            dexp[r] = w[t, j] * go[t]
+            dw[t, j] = go[t] @ y[r]
+    return round_to(dexp, dtype), dw.astype(np.float32)
+
+
+def swiglu_expert_training(x_rows, w_gate_e, w_up_e, w_down_e, dtype):
+    """Training forward of one expert: returns (y, g, u, h), all in the model
+    dtype. The cache keeps the gate and up projections rounded to the model
+    dtype, and h is formed from those cached values:
+      g = round(x W_gate^T), u = round(x W_up^T), h = round(SiLU(g) u),
+      y = round(h W_down^T)."""
+    x = decode(x_rows, dtype)
+    g = round_to(x @ decode(w_gate_e, dtype).T, dtype)
+    u = round_to(x @ decode(w_up_e, dtype).T, dtype)
+    h = round_to(silu(decode(g, dtype)) * decode(u, dtype), dtype)
+    y = round_to(decode(h, dtype) @ decode(w_down_e, dtype).T, dtype)
+    return y, g, u, h
+
+
+def swiglu_expert_backward(x_rows, w_gate_e, w_up_e, w_down_e, g, u, h, dy, dtype):
+    """cache.backward of one expert, from its training cache (g, u, h) and the
+    gradient dy of its output rows:
+      dh = dy W_down                                   (not rounded)
+      sigma = 1 / (1 + exp(-g)),  SiLU'(g) = sigma (1 + g (1 - sigma))
+      dg = round(dh * u * SiLU'(g)),  du = round(dh * SiLU(g))
+      dinput = round(dg W_gate + du W_up)              [n, H], model dtype
+      dgate = dg^T x, dup = du^T x, ddown = dy^T h     fp32
+    Returns (dinput, dgate [I, H], dup [I, H], ddown [H, I])."""
+    x = decode(x_rows, dtype)
+    wg, wu, wd = decode(w_gate_e, dtype), decode(w_up_e, dtype), decode(w_down_e, dtype)
+    gv, uv, hv, dyv = decode(g, dtype), decode(u, dtype), decode(h, dtype), decode(dy, dtype)
+    dh = dyv @ wd
+    with np.errstate(over="ignore"):
+        sig = 1.0 / (1.0 + np.exp(-gv))
+    dg = decode(round_to(dh * uv * sig * (1.0 + gv * (1.0 - sig)), dtype), dtype)
+    du = decode(round_to(dh * gv * sig, dtype), dtype)
+    dinput = round_to(dg @ wg + du @ wu, dtype)
+    return (dinput, (dg.T @ x).astype(np.float32), (du.T @ x).astype(np.float32),
+            (dyv.T @ hv).astype(np.float32))
+
+
+def experts_forward_training(x_disp, offsets, weights_of, dtype):
+    """forward_dispatched_training over all experts: (expert_out [R, H],
+    g [R, I], u [R, I], h [R, I]), rows in dispatched order."""
+    R = int(offsets[-1])
+    parts = None
+    for e in range(len(offsets) - 1):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if a == b:
+            continue
+        outs = swiglu_expert_training(x_disp[a:b], *weights_of(e), dtype)
+        if parts is None:
+            parts = [np.empty((R,) + o.shape[1:], dtype=o.dtype) for o in outs]
+        for p, o in zip(parts, outs):
+            p[a:b] = o
+    return parts
+
+
+def experts_backward(x_disp, offsets, weights_of, g, u, h, dexpert, dtype):
+    """cache.backward over all experts: (dinput [R, H] model dtype, dgate
+    [E, I, H], dup [E, I, H], ddown [E, H, I] fp32). Experts without rows get
+    zero weight gradients."""
+    E = len(offsets) - 1
+    R = int(offsets[-1])
+    H = x_disp.shape[1] if R else 0
+    dinput = None
+    dgate = dup = ddown = None
+    for e in range(E):
+        wg, wu, wd = weights_of(e)
+        if dgate is None:
+            I_, Hh = wg.shape
+            dgate = np.zeros((E, I_, Hh), np.float32)
+            dup = np.zeros((E, I_, Hh), np.float32)
+            ddown = np.zeros((E, Hh, I_), np.float32)
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if a == b:
+            continue
+        di, dgt, dut, ddn = swiglu_expert_backward(x_disp[a:b], wg, wu, wd, g[a:b], u[a:b], h[a:b],
+                                                   dexpert[a:b], dtype)
+        if dinput is None:
+            dinput = np.empty((R, H), dtype=di.dtype)
+        dinput[a:b] = di
+        dgate[e], dup[e], ddown[e] = dgt, dut, ddn
+    return dinput, dgate, dup, ddown
+
+
+def dispatch_backward(dinput, row_of_slot, T, k, H, dtype):
+    """dispatch_backward: dx[t] = sum over the slots j of token t that have a
+    dispatched row of dinput[row(t,j)], without the routing weight (the
+    weight was applied in combine_backward); one rounding to the model dtype.
+    A token with no dispatched slot gets zeros."""
+    rows = np.asarray(row_of_slot).astype(np.int64).reshape(T, k)
+    d = decode(dinput, dtype) if dinput is not None and len(dinput) else np.zeros((0, H))
+    dx = np.zeros((T, H))
+    for t in range(T):
+        for j in range(k):
+            if rows[t, j] >= 0:
+                dx[t] += d[rows[t, j]]
+    return round_to(dx, dtype)
