@@ -399,6 +399,127 @@ moe_status moe_forward_quant(const void* x, const void* logits, moe_dtype logits
                              void* out, uint32_t* indices_out, void* weights_out, void* ws,
                              size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream);
 
+/* ===================== first-order training ===================== */
+/*
+ * Passage for everything below: ruDNN user guide, "12. MoE first-order
+ * training" (router weights for a fixed selection and their backward;
+ * forward_dispatched_training keeping a cache; the backward order
+ * combine_backward -> expert backward -> dispatch_backward -> router
+ * backward; weight gradients and dweights in FP32). Gradients are taken with
+ * the selection held fixed: top-k and group decisions are not differentiated.
+ */
+typedef enum moe_scoring {
+  MOE_SCORE_SOFTMAX = 0, /* softmax over all E experts, gathered at the indices */
+  MOE_SCORE_SIGMOID = 1  /* sigmoid of the selected logits */
+} moe_scoring;
+
+typedef enum moe_index_dtype {
+  MOE_IDX_U32 = 0,
+  MOE_IDX_I32 = 1,
+  MOE_IDX_I64 = 2
+} moe_index_dtype;
+
+/*
+ * moe_router_weights - weights of a fixed selection (selected_router_weights).
+ *   logits   [T, E] logits_dt, read; indices [T, top_k] idx_dt, read.
+ *   a[t,j] = softmax(logits[t])[idx] (fp32, over all E) or
+ *            sigmoid(logits[t, idx]); repeated indices gather again.
+ *   normalize != 0: a[t,j] /= sum_j a[t,j]. Then weights = a * scale.
+ *   weights  [T, top_k] fp32, written. A row holding an index outside
+ *            [0, E) is NaN throughout (nothing is read out of bounds).
+ * Errors: ARGUMENT if top_k not in [1, min(E, 64)], scoring unknown, or
+ *   scale not finite and > 0; DTYPE for an unknown idx_dt.
+ */
+moe_status moe_router_weights(const void* logits, moe_dtype logits_dt, const void* indices,
+                              moe_index_dtype idx_dt, int64_t T, int64_t E, int64_t top_k,
+                              moe_scoring scoring, int normalize, float scale, float* weights,
+                              hipStream_t stream);
+
+/*
+ * moe_router_backward - d loss / d logits for the weights of
+ * moe_router_weights (selected_router_backward), same arguments plus
+ *   grad_weights [T, top_k] fp32, read;
+ *   grad_logits  [T, E] logits_dt, written (every element). Unselected
+ *   experts receive the softmax coupling term (no normalize) or 0. A row
+ *   with an invalid index, and a softmax row whose logits contain NaN or
+ *   +inf or are all -inf, is NaN throughout.
+ */
+moe_status moe_router_backward(const void* logits, moe_dtype logits_dt, const void* indices,
+                               moe_index_dtype idx_dt, const float* grad_weights, int64_t T,
+                               int64_t E, int64_t top_k, moe_scoring scoring, int normalize,
+                               float scale, void* grad_logits, hipStream_t stream);
+
+/*
+ * moe_combine_backward - gradient of moe_combine (combine_backward).
+ *   expert_out [rows, H] dt, row_of_slot [T*top_k], weights [T, top_k] w_dt,
+ *   grad_out [T, H] dt: read. rows (<= T*top_k) is the number of
+ *   dispatched rows the two row buffers hold; every row_of_slot entry must
+ *   be -1 or below it.
+ *   dexpert  [rows, H] dt, written for every dispatched row:
+ *            dexpert[row(t,j)] = weights[t,j] * grad_out[t].
+ *   dweights [T, top_k] fp32, written: <grad_out[t], expert_out[row(t,j)]>
+ *            accumulated in fp32; NaN for a slot without a row (-1).
+ */
+moe_status moe_combine_backward(const void* expert_out, const int32_t* row_of_slot,
+                                const void* weights, moe_dtype w_dt, const void* grad_out,
+                                int64_t T, int64_t top_k, int64_t H, int64_t rows, moe_dtype dt,
+                                void* dexpert, float* dweights, hipStream_t stream);
+
+/*
+ * moe_experts_forward_training - the experts' forward keeping a cache
+ * (forward_dispatched_training). Arguments as moe_experts_forward_dispatched,
+ * plus
+ *   cache [rows, 3*I] dt (moe_experts_training_cache_size bytes), written:
+ *         the first rows*2*I elements hold (g | u) per row, g = x W_gate^T and
+ *         u = x W_up^T rounded to dt; then rows*I elements hold
+ *         h = SiLU(g) * u computed from the cached g, u and rounded to dt.
+ *   expert_out = h W_down^T, as the inference path.
+ *   ws: moe_experts_forward_training_workspace_size(rows, E, H, I, dt).
+ * x_disp, the weights and the cache must stay unchanged until
+ * moe_experts_backward has run. Errors: UNSUPPORTED for dt F32 (this path
+ * runs on the bf16/f16 matrix cores).
+ */
+moe_status moe_experts_forward_training(const void* x_disp, const int32_t* expert_offsets,
+                                        int64_t rows, int64_t E, int64_t H, int64_t I,
+                                        const void* w_gate, const void* w_up, const void* w_down,
+                                        moe_dtype dt, void* expert_out, void* cache, void* ws,
+                                        size_t ws_bytes, hipStream_t stream);
+size_t moe_experts_training_cache_size(int64_t rows, int64_t I, moe_dtype dt);
+size_t moe_experts_forward_training_workspace_size(int64_t rows, int64_t E, int64_t H, int64_t I,
+                                                   moe_dtype dt);
+
+/*
+ * moe_experts_backward - cache.backward(dexpert).
+ *   dexpert [rows, H] dt (from moe_combine_backward), read.
+ *   With dh = dexpert W_down (fp32, not rounded), s = sigmoid(g):
+ *     dg = dh * u * s * (1 + g (1 - s)), du = dh * SiLU(g), both rounded to dt;
+ *   dinput [rows, H] dt, written: dg W_gate + du W_up;
+ *   dgate, dup [E, I, H] fp32, written: dg^T x_disp, du^T x_disp per expert;
+ *   ddown [E, H, I] fp32, written: dexpert^T h per expert.
+ *   An expert without rows gets zero weight gradients (also for rows = 0).
+ *   ws: moe_experts_backward_workspace_size(rows, E, H, I, dt).
+ */
+moe_status moe_experts_backward(const void* x_disp, const int32_t* expert_offsets, int64_t rows,
+                                int64_t E, int64_t H, int64_t I, const void* w_gate,
+                                const void* w_up, const void* w_down, moe_dtype dt,
+                                const void* cache, const void* dexpert, void* dinput,
+                                float* dgate, float* dup, float* ddown, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
+size_t moe_experts_backward_workspace_size(int64_t rows, int64_t E, int64_t H, int64_t I,
+                                           moe_dtype dt);
+
+/*
+ * moe_dispatch_backward - dispatch_backward: dx[t] = sum over the slots j of
+ * token t with a dispatched row of dinput[row_of_slot[t*top_k+j]], in fp32
+ * in j order, stored in dt; the routing weight is not applied again (it was
+ * applied in moe_combine_backward). A token without rows gets zeros.
+ *   dinput [rows, H] dt (rows <= T*top_k), row_of_slot [T*top_k]: read;
+ *   dx [T, H] dt: written.
+ */
+moe_status moe_dispatch_backward(const void* dinput, const int32_t* row_of_slot, int64_t T,
+                                 int64_t top_k, int64_t H, int64_t rows, moe_dtype dt, void* dx,
+                                 hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

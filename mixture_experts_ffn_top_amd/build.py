@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe_ffn.so")
-SOURCES = ["route.hip", "dispatch.hip", "gemm.hip", "combine.hip", "special.hip", "quant.hip", "api.hip"]
+SOURCES = ["route.hip", "dispatch.hip", "gemm.hip", "combine.hip", "special.hip", "quant.hip", "train.hip", "api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -719,4 +719,184 @@ moe_status moe_forward_quant(const void* x, const void* logits, moe_dtype logits
                       indices_out, weights_out, ws, ws_bytes, stage_events, stream, &qw);
 }
 
+// ---- first-order training (ruDNN user guide, "12. MoE first-order training") ----
+
+static size_t index_size(int idx_dt) { return idx_dt == MOE_IDX_I64 ? 8 : 4; }
+
+static moe_status router_grad_impl(const void* logits, moe_dtype logits_dt, const void* indices,
+                                   moe_index_dtype idx_dt, const float* grad_weights, int64_t T,
+                                   int64_t E, int64_t top_k, moe_scoring scoring, int normalize,
+                                   float scale, float* weights, void* grad_logits,
+                                   hipStream_t stream) {
+  if (T < 0 || E < 1) return MOE_ERROR_SHAPE;
+  if (!valid_dt(logits_dt)) return MOE_ERROR_DTYPE;
+  if (idx_dt != MOE_IDX_U32 && idx_dt != MOE_IDX_I32 && idx_dt != MOE_IDX_I64) return MOE_ERROR_DTYPE;
+  if (top_k < 1 || top_k > E || top_k > 64) return MOE_ERROR_ARGUMENT;
+  if (scoring != MOE_SCORE_SOFTMAX && scoring != MOE_SCORE_SIGMOID) return MOE_ERROR_ARGUMENT;
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return MOE_ERROR_ARGUMENT;
+  if (E > kMaxE || T * top_k > INT32_MAX) return MOE_ERROR_UNSUPPORTED;
+  if (T == 0) return MOE_SUCCESS;
+  const bool bwd = grad_logits != nullptr;
+  if (!logits || !indices || (bwd ? !grad_weights : !weights)) return MOE_ERROR_NULL_POINTER;
+  const size_t slots = (size_t)(T * top_k);
+  const Span ins[] = {{logits, (size_t)T * (size_t)E * dtype_size(logits_dt)},
+                      {indices, slots * index_size(idx_dt)}, {grad_weights, bwd ? slots * 4 : 0}};
+  const Span outs[] = {bwd ? Span{grad_logits, (size_t)T * (size_t)E * dtype_size(logits_dt)}
+                           : Span{weights, slots * 4}};
+  if (any_overlap(outs, 1, ins, 3)) return MOE_ERROR_ARGUMENT;
+  const void* ptrs[] = {logits, indices, bwd ? (const void*)grad_weights : nullptr,
+                        bwd ? grad_logits : (void*)weights};
+  moe_status st = check_device(ptrs, 4, stream);
+  if (st != MOE_SUCCESS) return st;
+  RouterGrad r = {};
+  r.logits = logits; r.logits_dt = logits_dt; r.indices = indices; r.idx_dt = idx_dt;
+  r.T = (int)T; r.E = (int)E; r.k = (int)top_k; r.scoring = scoring; r.normalize = normalize ? 1 : 0;
+  r.scale = scale; r.weights = weights; r.grad_weights = bwd ? grad_weights : nullptr;
+  r.grad_logits = grad_logits;
+  return from_hip(launch_router_grad(r, stream));
+}
+
+moe_status moe_router_weights(const void* logits, moe_dtype logits_dt, const void* indices,
+                              moe_index_dtype idx_dt, int64_t T, int64_t E, int64_t top_k,
+                              moe_scoring scoring, int normalize, float scale, float* weights,
+                              hipStream_t stream) {
+  if (T > 0 && !weights) return MOE_ERROR_NULL_POINTER;
+  return router_grad_impl(logits, logits_dt, indices, idx_dt, nullptr, T, E, top_k, scoring,
+                          normalize, scale, weights, nullptr, stream);
+}
+
+moe_status moe_router_backward(const void* logits, moe_dtype logits_dt, const void* indices,
+                               moe_index_dtype idx_dt, const float* grad_weights, int64_t T,
+                               int64_t E, int64_t top_k, moe_scoring scoring, int normalize,
+                               float scale, void* grad_logits, hipStream_t stream) {
+  if (T > 0 && !grad_logits) return MOE_ERROR_NULL_POINTER;
+  return router_grad_impl(logits, logits_dt, indices, idx_dt, grad_weights, T, E, top_k, scoring,
+                          normalize, scale, nullptr, grad_logits, stream);
+}
+
+moe_status moe_combine_backward(const void* expert_out, const int32_t* row_of_slot,
+                                const void* weights, moe_dtype w_dt, const void* grad_out,
+                                int64_t T, int64_t top_k, int64_t H, int64_t rows, moe_dtype dt,
+                                void* dexpert, float* dweights, hipStream_t stream) {
+  if (T < 0 || top_k < 1 || H < 1 || rows < 0 || rows > T * top_k) return MOE_ERROR_SHAPE;
+  if (!valid_dt(dt) || !valid_dt(w_dt)) return MOE_ERROR_DTYPE;
+  if (T * top_k > INT32_MAX || !row_len_ok(H)) return MOE_ERROR_UNSUPPORTED;
+  if (T == 0) return MOE_SUCCESS;
+  if (!expert_out || !row_of_slot || !weights || !grad_out || !dexpert || !dweights)
+    return MOE_ERROR_NULL_POINTER;
+  const size_t ds = dtype_size(dt), slots = (size_t)(T * top_k);
+  const Span outs[] = {{dexpert, (size_t)rows * (size_t)H * ds}, {dweights, slots * 4}};
+  const Span ins[] = {{expert_out, (size_t)rows * (size_t)H * ds}, {row_of_slot, slots * 4},
+                      {weights, slots * dtype_size(w_dt)}, {grad_out, (size_t)T * (size_t)H * ds}};
+  if (any_overlap(outs, 2, ins, 4)) return MOE_ERROR_ARGUMENT;
+  const void* ptrs[] = {expert_out, row_of_slot, weights, grad_out, dexpert, dweights};
+  moe_status st = check_device(ptrs, 6, stream);
+  if (st != MOE_SUCCESS) return st;
+  return from_hip(launch_combine_backward(expert_out, row_of_slot, weights, w_dt, grad_out, (int)T,
+                                          (int)top_k, (int)H, dt, dexpert, dweights, stream));
+}
+
+moe_status moe_dispatch_backward(const void* dinput, const int32_t* row_of_slot, int64_t T,
+                                 int64_t top_k, int64_t H, int64_t rows, moe_dtype dt, void* dx,
+                                 hipStream_t stream) {
+  if (T < 0 || top_k < 1 || H < 1 || rows < 0 || rows > T * top_k) return MOE_ERROR_SHAPE;
+  if (!valid_dt(dt)) return MOE_ERROR_DTYPE;
+  if (T * top_k > INT32_MAX || !row_len_ok(H)) return MOE_ERROR_UNSUPPORTED;
+  if (T == 0) return MOE_SUCCESS;
+  if (!dinput || !row_of_slot || !dx) return MOE_ERROR_NULL_POINTER;
+  const size_t ds = dtype_size(dt), slots = (size_t)(T * top_k);
+  const Span outs[] = {{dx, (size_t)T * (size_t)H * ds}};
+  const Span ins[] = {{dinput, (size_t)rows * (size_t)H * ds}, {row_of_slot, slots * 4}};
+  if (any_overlap(outs, 1, ins, 2)) return MOE_ERROR_ARGUMENT;
+  const void* ptrs[] = {dinput, row_of_slot, dx};
+  moe_status st = check_device(ptrs, 3, stream);
+  if (st != MOE_SUCCESS) return st;
+  return from_hip(launch_dispatch_backward(dinput, row_of_slot, (int)T, (int)top_k, (int)H, dt, dx,
+                                           stream));
+}
+
+static moe_status check_train_args(int64_t rows, int64_t E, int64_t H, int64_t I, moe_dtype dt) {
+  if (rows < 0 || E < 1 || H < 1 || I < 1) return MOE_ERROR_SHAPE;
+  if (!valid_dt(dt)) return MOE_ERROR_DTYPE;
+  if (dt == MOE_F32) return MOE_ERROR_UNSUPPORTED;  // the matrix-core path is bf16 / f16
+  if (E > kMaxE || rows > INT32_MAX || !row_len_ok(H) || !row_len_ok(I)) return MOE_ERROR_UNSUPPORTED;
+  if ((int64_t)E * I * H > INT64_MAX / 8 || 2 * I > INT32_MAX) return MOE_ERROR_UNSUPPORTED;
+  return MOE_SUCCESS;
+}
+
+size_t moe_experts_training_cache_size(int64_t rows, int64_t I, moe_dtype dt) {
+  if (rows < 0 || I < 1 || !valid_dt(dt)) return 0;
+  return (size_t)rows * (size_t)I * 3 * dtype_size(dt);
+}
+
+size_t moe_experts_forward_training_workspace_size(int64_t rows, int64_t E, int64_t H, int64_t I,
+                                                   moe_dtype dt) {
+  if (check_train_args(rows, E, H, I, dt) != MOE_SUCCESS) return 0;
+  return train_prefix_bytes(E) + align256(gemm_scratch_bytes(rows, E, H, I, dt));
+}
+
+size_t moe_experts_backward_workspace_size(int64_t rows, int64_t E, int64_t H, int64_t I,
+                                           moe_dtype dt) {
+  if (check_train_args(rows, E, H, I, dt) != MOE_SUCCESS) return 0;
+  return train_prefix_bytes(E) + align256((size_t)rows * (size_t)I * 2 * dtype_size(dt));
+}
+
+moe_status moe_experts_forward_training(const void* x_disp, const int32_t* expert_offsets,
+                                        int64_t rows, int64_t E, int64_t H, int64_t I,
+                                        const void* w_gate, const void* w_up, const void* w_down,
+                                        moe_dtype dt, void* expert_out, void* cache, void* ws,
+                                        size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_train_args(rows, E, H, I, dt);
+  if (st != MOE_SUCCESS) return st;
+  if (rows == 0) return MOE_SUCCESS;
+  if (!x_disp || !expert_offsets || !w_gate || !w_up || !w_down || !expert_out || !cache)
+    return MOE_ERROR_NULL_POINTER;
+  const size_t need = moe_experts_forward_training_workspace_size(rows, E, H, I, dt);
+  if (!ws || ((uintptr_t)ws & 255) || ws_bytes < need) return MOE_ERROR_WORKSPACE;
+  const size_t ds = dtype_size(dt), wbytes = (size_t)E * (size_t)I * (size_t)H * ds;
+  const Span outs[] = {{expert_out, (size_t)rows * (size_t)H * ds},
+                       {cache, moe_experts_training_cache_size(rows, I, dt)}, {ws, need}};
+  const Span ins[] = {{x_disp, (size_t)rows * (size_t)H * ds}, {expert_offsets, (size_t)(E + 1) * 4},
+                      {w_gate, wbytes}, {w_up, wbytes}, {w_down, wbytes}};
+  if (any_overlap(outs, 3, ins, 5)) return MOE_ERROR_ARGUMENT;
+  const void* ptrs[] = {x_disp, expert_offsets, w_gate, w_up, w_down, expert_out, cache, ws};
+  if ((st = check_device(ptrs, 8, stream)) != MOE_SUCCESS) return st;
+  TrainExperts q = {};
+  q.x = x_disp; q.offsets = expert_offsets; q.rows = (int)rows; q.E = (int)E; q.H = (int)H;
+  q.I = (int)I; q.dt = dt; q.w_gate = w_gate; q.w_up = w_up; q.w_down = w_down;
+  q.cache = cache; q.y = expert_out; q.ws = ws;
+  return from_hip(launch_experts_forward_training(q, stream));
+}
+
+moe_status moe_experts_backward(const void* x_disp, const int32_t* expert_offsets, int64_t rows,
+                                int64_t E, int64_t H, int64_t I, const void* w_gate,
+                                const void* w_up, const void* w_down, moe_dtype dt,
+                                const void* cache, const void* dexpert, void* dinput,
+                                float* dgate, float* dup, float* ddown, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  moe_status st = check_train_args(rows, E, H, I, dt);
+  if (st != MOE_SUCCESS) return st;
+  if (!expert_offsets || !w_gate || !w_up || !w_down || !dgate || !dup || !ddown)
+    return MOE_ERROR_NULL_POINTER;
+  if (rows > 0 && (!x_disp || !cache || !dexpert || !dinput)) return MOE_ERROR_NULL_POINTER;
+  const size_t need = moe_experts_backward_workspace_size(rows, E, H, I, dt);
+  if (!ws || ((uintptr_t)ws & 255) || ws_bytes < need) return MOE_ERROR_WORKSPACE;
+  const size_t ds = dtype_size(dt), wbytes = (size_t)E * (size_t)I * (size_t)H * ds;
+  const size_t gbytes = (size_t)E * (size_t)I * (size_t)H * 4, rh = (size_t)rows * (size_t)H * ds;
+  const Span outs[] = {{dinput, rh}, {dgate, gbytes}, {dup, gbytes}, {ddown, gbytes}, {ws, need}};
+  const Span ins[] = {{x_disp, rh}, {expert_offsets, (size_t)(E + 1) * 4}, {w_gate, wbytes},
+                      {w_up, wbytes}, {w_down, wbytes},
+                      {cache, moe_experts_training_cache_size(rows, I, dt)}, {dexpert, rh}};
+  if (any_overlap(outs, 5, ins, 7)) return MOE_ERROR_ARGUMENT;
+  const void* ptrs[] = {x_disp, expert_offsets, w_gate, w_up, w_down, cache, dexpert, dinput,
+                        dgate, dup, ddown, ws};
+  if ((st = check_device(ptrs, 12, stream)) != MOE_SUCCESS) return st;
+  TrainExperts q = {};
+  q.x = x_disp; q.offsets = expert_offsets; q.rows = (int)rows; q.E = (int)E; q.H = (int)H;
+  q.I = (int)I; q.dt = dt; q.w_gate = w_gate; q.w_up = w_up; q.w_down = w_down;
+  q.cache = const_cast<void*>(cache); q.dy = dexpert; q.dx = dinput;
+  q.d_gate = dgate; q.d_up = dup; q.d_down = ddown; q.ws = ws;
+  return from_hip(launch_experts_backward(q, stream));
+}
+
 }  // extern "C"

@@ -140,4 +140,49 @@ struct QuantExperts {
 };
 hipError_t launch_experts_quant(const QuantExperts& q, hipStream_t s);
 
+// ---- first-order training ------------------------------------------------------
+// Experts' training forward (fills the cache, then the down GEMM) and backward.
+// cache: [rows, 2I] = (g | u) followed by [rows, I] = h, all in dt (bf16/f16).
+// ws: train_prefix_bytes(E), then for the forward gemm_scratch_bytes(...),
+// for the backward [rows, 2I] dt (dg | du).
+struct TrainExperts {
+  const void* x;            // dispatched rows [rows, H]
+  const int32_t* offsets;   // [E+1]
+  int rows, E, H, I, dt;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  void* cache;
+  void* y;                  // forward: expert_out [rows, H]
+  const void* dy;           // backward: dexpert [rows, H]
+  void* dx;                 // backward: dinput [rows, H]
+  float* d_gate;            // backward: [E, I, H]
+  float* d_up;              // backward: [E, I, H]
+  float* d_down;            // backward: [E, H, I]
+  void* ws;
+};
+size_t train_prefix_bytes(int64_t E);
+hipError_t launch_experts_forward_training(const TrainExperts& q, hipStream_t s);
+hipError_t launch_experts_backward(const TrainExperts& q, hipStream_t s);
+
+// Router weights of a fixed selection (grad_weights == nullptr) or their
+// gradient with respect to the logits.
+struct RouterGrad {
+  const void* logits;
+  int logits_dt;
+  const void* indices;
+  int idx_dt;               // 0 uint32, 1 int32, 2 int64
+  int T, E, k, scoring, normalize;
+  float scale;
+  float* weights;
+  const float* grad_weights;
+  void* grad_logits;
+};
+hipError_t launch_router_grad(const RouterGrad& r, hipStream_t s);
+hipError_t launch_combine_backward(const void* y, const int32_t* row_of_slot, const void* w, int w_dt,
+                                   const void* grad_out, int T, int k, int H, int dt, void* dexpert,
+                                   float* dweights, hipStream_t s);
+hipError_t launch_dispatch_backward(const void* dinput, const int32_t* row_of_slot, int T, int k,
+                                    int H, int dt, void* dx, hipStream_t s);
+
 }  // namespace moe

@@ -1,0 +1,658 @@
+// First-order training of the MoE FFN (ruDNN user guide, "12. MoE
+// first-order training"): router weights for a fixed selection and their
+// gradient, combine_backward, the experts' training forward (with its
+// cache) and backward, and dispatch_backward.
+//
+// Expert GEMMs of the backward pass (per expert e, rows n_e):
+//   dh     = dY W_down[e]            [n_e, I]  K = H   W_down read along N
+//   dinput = [dg | du] [W_gate; W_up] [n_e, H]  K = 2I  weights read along N
+//   ddown  = dY^T h                  [H, I]    K = n_e rows
+//   dgate | dup = [dg | du]^T X      [2I, H]   K = n_e rows
+// and of the training forward the plain projection [g | u] = X [W_gate;
+// W_up]^T (K = H, both operands along K). One MFMA kernel serves them all:
+// each operand is either K-contiguous (element (mn, k) at mn * ld + k) or
+// MN-contiguous (at k * ld + mn), and may be split in two tensors along its
+// outer index (gate and up weights, dg and du). MN-contiguous tiles are
+// transposed on their way into LDS (pairs of k packed into one 32-bit LDS
+// write), so the MFMA always reads 16-byte K-runs.
+//
+// Grouping. "M-grouped" GEMMs take their rows from the expert offsets (one
+// M-tile never spans two experts; tiles are found through a device-built
+// prefix of M-tiles per expert). "K-grouped" GEMMs (the weight gradients)
+// run one output tile per (expert, M-tile, N-tile) and loop over the
+// expert's rows as K; an expert without rows writes zeros.
+#include <math.h>
+
+#include <algorithm>
+#include <type_traits>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int kTBM = 128;       // output tile rows
+constexpr int kTBN = 128;       // output tile columns
+constexpr int kTBK = 32;        // K per LDS stage
+constexpr int kTThreads = 256;  // 4 wavefronts as 2 x 2, 64 x 64 outputs each
+constexpr int kLdsRow = 40;     // LDS row: 32 elements + 8 padding (80 bytes)
+constexpr int kNGroup = 8;      // N-tiles per group in the M-grouped tile order
+
+enum Epilogue { kEpiStore = 0, kEpiStoreF32 = 1, kEpiSwiGluBwd = 2 };
+
+struct Operand {
+  const void* p0;   // index < split
+  const void* p1;   // index >= split (index - split)
+  int64_t split;    // split along mn (K-contiguous) or along k (MN-contiguous)
+  int64_t ld;       // elements between consecutive outer rows
+  int64_t estride;  // elements between experts (0: rows shared by all experts)
+};
+
+struct TrainGemm {
+  Operand a, b;
+  const int32_t* offsets;      // [E+1]
+  const int32_t* tile_prefix;  // M-grouped: [E+1] prefix of M-tiles per expert
+  int E;
+  int M, N, K;                 // M-grouped: M unused; K-grouped: K unused
+  int m_tiles, n_tiles;        // M-grouped: m_tiles is the bound the grid is sized for
+  void* out0;
+  void* out1;
+  int64_t out_split;           // output rows >= out_split go to out1
+  int64_t ldc;
+  int64_t out_estride;         // K-grouped outputs: elements between experts
+  const void* gu;              // SwiGLU backward: cache [rows, 2N] = (g | u)
+};
+
+template <typename T> struct TMfma;
+template <> struct TMfma<bf16> {
+  static __device__ __forceinline__ f32x16 run(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct TMfma<f16> {
+  static __device__ __forceinline__ f32x16 run(f16x8 a, f16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+template <typename T> using Frag = typename std::conditional<std::is_same<T, bf16>::value, bf16x8, f16x8>::type;
+
+__device__ __forceinline__ uint32_t half_of(const uint4& v, int i) {
+  const uint32_t w = i < 2 ? (i == 0 ? v.x : v.y) : (i == 2 ? v.z : v.w);
+  return w;
+}
+
+// 16-bit element i (0..7) of a 16-byte chunk.
+__device__ __forceinline__ uint32_t elem16(const uint4& v, int i) {
+  return (half_of(v, i >> 1) >> ((i & 1) * 16)) & 0xFFFFu;
+}
+
+template <typename T>
+__device__ __forceinline__ const T* seg_ptr(const Operand& op, int e, int64_t outer) {
+  const bool hi = outer >= op.split;
+  const T* base = static_cast<const T*>(hi ? op.p1 : op.p0);
+  return base + (int64_t)e * op.estride + (hi ? outer - op.split : outer) * op.ld;
+}
+
+// K-contiguous operand: a tile of kTBM rows (mn) x kTBK (k); two 16-byte
+// chunks per thread. Rows >= mn_end and k >= k_end read as zeros.
+template <typename T>
+__device__ __forceinline__ void load_kc(const Operand& op, int e, int64_t mn0, int64_t mn_end,
+                                        int64_t k0, int64_t k_end, uint4 (&r)[2]) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = threadIdx.x + i * kTThreads;
+    const int64_t mn = mn0 + (c >> 2), k = k0 + (c & 3) * 8;
+    r[i] = make_uint4(0, 0, 0, 0);
+    if (mn < mn_end && k < k_end) r[i] = *reinterpret_cast<const uint4*>(seg_ptr<T>(op, e, mn) + k);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store_kc(T* lds, const uint4 (&r)[2]) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = threadIdx.x + i * kTThreads;
+    *reinterpret_cast<uint4*>(lds + (c >> 2) * kLdsRow + (c & 3) * 8) = r[i];
+  }
+}
+
+// MN-contiguous operand: kTBK rows (k) x kTBM (mn). Thread t reads the k-pair
+// 2p, 2p+1 (p = t % 16) at mn chunk t / 16 (8 elements). Rows k >= k_end and
+// chunks at or past mn_end read as zeros (mn_end is a multiple of 8).
+template <typename T>
+__device__ __forceinline__ void load_mn(const Operand& op, int e, int64_t mn0, int64_t mn_end,
+                                        int64_t k0, int64_t k_end, uint4 (&r)[2]) {
+  const int p = threadIdx.x & 15, c = threadIdx.x >> 4;
+  const int64_t mn = mn0 + c * 8;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int64_t k = k0 + 2 * p + h;
+    r[h] = make_uint4(0, 0, 0, 0);
+    if (k < k_end && mn < mn_end) r[h] = *reinterpret_cast<const uint4*>(seg_ptr<T>(op, e, k) + mn);
+  }
+}
+
+// Transposes the two k-rows into the K-contiguous LDS layout: element
+// (mn, k) at mn * kLdsRow + k; one 32-bit write holds k = 2p and 2p + 1.
+template <typename T>
+__device__ __forceinline__ void store_mn(T* lds, const uint4 (&r)[2]) {
+  const int p = threadIdx.x & 15, c = threadIdx.x >> 4;
+  uint32_t* base = reinterpret_cast<uint32_t*>(lds + (c * 8) * kLdsRow + 2 * p);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) base[i * (kLdsRow / 2)] = elem16(r[0], i) | (elem16(r[1], i) << 16);
+}
+
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+template <typename T, bool kAK, bool kBK, int kEpi, bool kGroupK>
+__global__ __launch_bounds__(kTThreads) void train_gemm_kernel(TrainGemm p) {
+  __shared__ __attribute__((aligned(16))) T lds_a[2][kTBM * kLdsRow];
+  __shared__ __attribute__((aligned(16))) T lds_b[2][kTBN * kLdsRow];
+
+  // ---- which tile ----
+  int e, m_idx, n_idx;
+  int64_t m0, m_end, k_start, k_end;
+  if (kGroupK) {
+    const int per_e = p.m_tiles * p.n_tiles;
+    e = blockIdx.x / per_e;
+    const int t = blockIdx.x % per_e;
+    m_idx = t / p.n_tiles;
+    n_idx = t % p.n_tiles;
+    m0 = (int64_t)m_idx * kTBM;
+    m_end = p.M;
+    k_start = p.offsets[e];
+    k_end = p.offsets[e + 1];
+  } else {
+    const int per_group = kNGroup * p.m_tiles;
+    const int g = blockIdx.x / per_group;
+    const int within = blockIdx.x % per_group;
+    const int n_in = min(kNGroup, p.n_tiles - g * kNGroup);
+    m_idx = within / n_in;
+    n_idx = g * kNGroup + within % n_in;
+    if (m_idx >= p.tile_prefix[p.E]) return;
+    int lo = 0, hi = p.E - 1;  // the expert e with prefix[e] <= m_idx < prefix[e+1]
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.tile_prefix[mid] <= m_idx) lo = mid; else hi = mid - 1;
+    }
+    e = lo;
+    m0 = p.offsets[e] + (int64_t)(m_idx - p.tile_prefix[e]) * kTBM;
+    m_end = p.offsets[e + 1];
+    k_start = 0;
+    k_end = p.K;
+  }
+  const int64_t n0 = (int64_t)n_idx * kTBN;
+  // Operands holding dispatched rows have no expert stride; weights do.
+  const int ea = e, eb = e;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  const int64_t nk = (k_end - k_start + kTBK - 1) / kTBK;
+  uint4 ra[2], rb[2];
+  auto load = [&](int64_t kt) {
+    const int64_t k0 = k_start + kt * kTBK;
+    if (kAK) load_kc<T>(p.a, ea, m0, m_end, k0, k_end, ra);
+    else load_mn<T>(p.a, ea, m0, m_end, k0, k_end, ra);
+    if (kBK) load_kc<T>(p.b, eb, n0, p.N, k0, k_end, rb);
+    else load_mn<T>(p.b, eb, n0, p.N, k0, k_end, rb);
+  };
+  auto store = [&](int buf) {
+    if (kAK) store_kc<T>(lds_a[buf], ra); else store_mn<T>(lds_a[buf], ra);
+    if (kBK) store_kc<T>(lds_b[buf], rb); else store_mn<T>(lds_b[buf], rb);
+  };
+
+  if (nk > 0) {
+    load(0);
+    store(0);
+    __syncthreads();
+  }
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    const int buf = (int)(kt & 1);
+    if (kt + 1 < nk) load(kt + 1);
+#pragma unroll
+    for (int ks = 0; ks < kTBK / 16; ++ks) {
+      Frag<T> fa[2], fb[2];
+      const int koff = ks * 16 + (lane >> 5) * 8;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        fa[i] = *reinterpret_cast<const Frag<T>*>(&lds_a[buf][(wm * 64 + i * 32 + (lane & 31)) * kLdsRow + koff]);
+        fb[i] = *reinterpret_cast<const Frag<T>*>(&lds_b[buf][(wn * 64 + i * 32 + (lane & 31)) * kLdsRow + koff]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = TMfma<T>::run(fa[i], fb[j], acc[i][j]);
+    }
+    if (kt + 1 < nk) store(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: D row (v/4)*8 + (lane/32)*4 + v%4, column lane%32 ----
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t m = m0 + wm * 64 + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+        const int64_t n = n0 + wn * 64 + j * 32 + (lane & 31);
+        if (m >= m_end || n >= p.N) continue;
+        const float x = acc[i][j][v];
+        if (kEpi == kEpiSwiGluBwd) {
+          // dh = x; g, u from the cache; dg, du into out0 (same [rows, 2N] layout)
+          const int64_t at = m * 2 * (int64_t)p.N + n;
+          const float g = to_f32(static_cast<const T*>(p.gu)[at]);
+          const float u = to_f32(static_cast<const T*>(p.gu)[at + p.N]);
+          const float s = sigmoidf_(g);
+          T* o = static_cast<T*>(p.out0);
+          o[at] = from_f32<T>(x * u * s * (1.0f + g * (1.0f - s)));
+          o[at + p.N] = from_f32<T>(x * g * s);
+        } else {
+          const bool hi = m >= p.out_split;
+          const int64_t row = hi ? m - p.out_split : m;
+          const int64_t at = (kGroupK ? (int64_t)e * p.out_estride : 0) + row * p.ldc + n;
+          void* base = hi ? p.out1 : p.out0;
+          if (kEpi == kEpiStoreF32) static_cast<float*>(base)[at] = x;
+          else static_cast<T*>(base)[at] = from_f32<T>(x);
+        }
+      }
+}
+
+// prefix[e] = number of M-tiles of experts before e; prefix[E] = total.
+__global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __restrict__ offsets,
+                                                           int E, int bm, int32_t* __restrict__ prefix) {
+  const int e = threadIdx.x;
+  int n = 0;
+  if (e < E) n = (offsets[e + 1] - offsets[e] + bm - 1) / bm;
+  int total = 0;
+  const int before = block_exclusive_scan(n, &total);
+  if (e < E) prefix[e] = before;
+  if (e == 0) prefix[E] = total;
+}
+
+// h = SiLU(g) * u from the cached projections, 8 columns per thread.
+template <typename T>
+__global__ __launch_bounds__(256) void swiglu_cache_kernel(const T* __restrict__ gu, T* __restrict__ h,
+                                                          int64_t rows, int I) {
+  const int64_t chunks = (int64_t)I / 8;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= rows * chunks) return;
+  const int64_t r = idx / chunks, c = (idx % chunks) * 8;
+  Vec8<T> g, u, o;
+  g.load(gu + r * 2 * I + c);
+  u.load(gu + r * 2 * I + I + c);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float gv = g.get(i);
+    o.set(i, gv * sigmoidf_(gv) * u.get(i));
+  }
+  o.store(h + r * I + c);
+}
+
+// ---- combine / dispatch backward -------------------------------------------------
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
+  return v;
+}
+
+// One block per token: dexpert[row(t,j)] = w[t,j] * grad_out[t]; dweights[t,j]
+// = <grad_out[t], expert_out[row(t,j)]> (fp32); NaN for a slot without a row.
+template <typename T, typename WT>
+__global__ __launch_bounds__(256) void combine_backward_kernel(
+    const T* __restrict__ y, const int32_t* __restrict__ row_of_slot, const WT* __restrict__ w,
+    const T* __restrict__ go, int k, int H, T* __restrict__ dexp, float* __restrict__ dw) {
+  __shared__ float part[4][64];
+  const int t = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int chunks = H / 8;
+  for (int j = 0; j < k; ++j) {
+    const int r = row_of_slot[(int64_t)t * k + j];
+    float dot = 0.f;
+    if (r >= 0) {
+      const float wj = to_f32(w[(int64_t)t * k + j]);
+      for (int c = threadIdx.x; c < chunks; c += blockDim.x) {
+        Vec8<T> g, yv, d;
+        g.load(go + (int64_t)t * H + c * 8);
+        yv.load(y + (int64_t)r * H + c * 8);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          dot = fmaf(g.get(i), yv.get(i), dot);
+          d.set(i, wj * g.get(i));
+        }
+        d.store(dexp + (int64_t)r * H + c * 8);
+      }
+    }
+    dot = wave_sum(dot);
+    if (lane == 0) part[wave][j & 63] = r >= 0 ? dot : __builtin_nanf("");
+    if ((j & 63) == 63 || j == k - 1) {
+      __syncthreads();
+      const int jj = threadIdx.x;
+      const int base = j & ~63;
+      if (jj <= (j & 63)) dw[(int64_t)t * k + base + jj] = part[0][jj] + part[1][jj] + part[2][jj] + part[3][jj];
+      __syncthreads();
+    }
+  }
+}
+
+// One block per token: dx[t] = sum over dispatched slots of dinput[row(t,j)].
+template <typename T>
+__global__ __launch_bounds__(256) void dispatch_backward_kernel(const T* __restrict__ dinput,
+                                                               const int32_t* __restrict__ row_of_slot,
+                                                               int k, int H, T* __restrict__ dx) {
+  const int t = blockIdx.x;
+  for (int c = threadIdx.x; c < H / 8; c += blockDim.x) {
+    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+      const int r = row_of_slot[(int64_t)t * k + j];
+      if (r < 0) continue;
+      Vec8<T> v;
+      v.load(dinput + (int64_t)r * H + c * 8);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s[i] += v.get(i);
+    }
+    Vec8<T> o;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o.set(i, s[i]);
+    o.store(dx + (int64_t)t * H + c * 8);
+  }
+}
+
+// ---- router weights and their gradient for a fixed selection ---------------------
+
+template <typename IT>
+__device__ __forceinline__ int64_t read_index(const IT* idx, int64_t at) { return (int64_t)idx[at]; }
+
+// Per token (one wavefront): the max and the sum of exp over the row for the
+// softmax (fp32, as the routing contract computes it).
+template <typename LT>
+__device__ __forceinline__ void softmax_stats(const LT* z, int E, float* zmax, float* zsum) {
+  const int lane = __lane_id();
+  float m = -INFINITY;
+  bool nan = false;
+  for (int e = lane; e < E; e += kWave) {
+    const float v = to_f32(z[e]);
+    nan |= v != v;
+    m = fmaxf(m, v);
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, kWave));
+  float s = 0.f;
+  for (int e = lane; e < E; e += kWave) s += expf(to_f32(z[e]) - m);
+  s = wave_sum(s);
+  const bool any_nan = __any(nan);
+  *zmax = m;
+  *zsum = any_nan ? __builtin_nanf("") : s;
+}
+
+template <typename LT, typename IT>
+__global__ __launch_bounds__(256) void router_weights_kernel(const LT* __restrict__ logits,
+                                                             const IT* __restrict__ indices, int T,
+                                                             int E, int k, int scoring, int normalize,
+                                                             float scale, float* __restrict__ w) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int lane = threadIdx.x & 63;
+  const LT* z = logits + (int64_t)t * E;
+  float zmax = 0.f, zsum = 1.f;
+  if (scoring == 0) softmax_stats(z, E, &zmax, &zsum);
+  int64_t i = 0;
+  bool bad = false;
+  float a = 0.f;
+  if (lane < k) {
+    i = read_index(indices, (int64_t)t * k + lane);
+    bad = i < 0 || i >= E;
+    if (!bad) {
+      const float v = to_f32(z[i]);
+      a = scoring == 0 ? expf(v - zmax) / zsum : sigmoidf_(v);
+    }
+  }
+  const bool row_bad = __any(bad);
+  const float S = normalize ? wave_sum(lane < k ? a : 0.f) : 1.f;
+  if (lane < k) w[(int64_t)t * k + lane] = row_bad ? __builtin_nanf("") : (normalize ? a / S : a) * scale;
+}
+
+// Gradient for the fixed selection (c = scale, a_j the gathered score, S the
+// sum of gathered scores when normalising, G_e = sum of grad_weights over the
+// slots selecting e, n_e their number):
+//   softmax:  dz_e = c p_e (G_e - sum_j g_j p_{i_j})               no normalize
+//             dz_e = c p_e / S (G_e - n_e sum_j g_j p_{i_j} / S)   normalize
+//   sigmoid:  dz_e = c s_e (1 - s_e) G_e                           no normalize
+//             dz_e = c s_e (1 - s_e) / S (G_e - n_e sum_j g_j s_{i_j} / S)
+// An unselected expert of a sigmoid row has no dependence: 0.
+template <typename LT, typename IT>
+__global__ __launch_bounds__(256) void router_backward_kernel(
+    const LT* __restrict__ logits, const IT* __restrict__ indices, const float* __restrict__ gw,
+    int T, int E, int k, int scoring, int normalize, float scale, LT* __restrict__ dz) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int lane = threadIdx.x & 63;
+  const LT* z = logits + (int64_t)t * E;
+  LT* out = dz + (int64_t)t * E;
+  float zmax = 0.f, zsum = 1.f;
+  if (scoring == 0) softmax_stats(z, E, &zmax, &zsum);
+  int my_i = -1;
+  bool bad = false;
+  float a = 0.f, g = 0.f;
+  if (lane < k) {
+    const int64_t i = read_index(indices, (int64_t)t * k + lane);
+    bad = i < 0 || i >= E;
+    my_i = bad ? -1 : (int)i;
+    g = gw[(int64_t)t * k + lane];
+    if (!bad) {
+      const float v = to_f32(z[i]);
+      a = scoring == 0 ? expf(v - zmax) / zsum : sigmoidf_(v);
+    }
+  }
+  const float S = normalize ? wave_sum(lane < k ? a : 0.f) : 1.f;
+  // An invalid index, or normalising by a sum that is zero or NaN (0/0 in
+  // every term of the derivative), makes the whole row NaN.
+  if (__any(bad) || !(S > 0.f)) {
+    for (int e = lane; e < E; e += kWave) out[e] = from_f32<LT>(__builtin_nanf(""));
+    return;
+  }
+  const float A = wave_sum(lane < k ? g * a : 0.f);
+  for (int e = lane; e < E; e += kWave) {
+    float G = 0.f;
+    int n = 0;
+    for (int j = 0; j < k; ++j) {
+      const int ij = __shfl(my_i, j, kWave);
+      const float gj = __shfl(g, j, kWave);
+      if (ij == e) { G += gj; ++n; }
+    }
+    const float v = to_f32(z[e]);
+    float d;
+    if (scoring == 0) {
+      const float pe = expf(v - zmax) / zsum;
+      d = normalize ? scale * pe / S * (G - n * A / S) : scale * pe * (G - A);
+    } else if (n == 0) {
+      d = 0.f;  // a sigmoid score depends on its own logit only
+    } else {
+      const float s = sigmoidf_(v);
+      const float ds = s * (1.0f - s);
+      d = normalize ? scale * ds / S * (G - n * A / S) : scale * ds * G;
+    }
+    out[e] = from_f32<LT>(d);
+  }
+}
+
+// ---- launch helpers ------------------------------------------------------------
+
+int64_t mtile_bound(int64_t rows, int64_t E) {
+  return (rows + kTBM - 1) / kTBM + std::min<int64_t>(E, rows);
+}
+
+template <typename T, bool kAK, bool kBK, int kEpi, bool kGroupK>
+void launch_tg(const TrainGemm& p, hipStream_t s) {
+  const int64_t blocks = (int64_t)p.m_tiles * p.n_tiles * (kGroupK ? p.E : 1);
+  if (blocks == 0) return;
+  hipLaunchKernelGGL((train_gemm_kernel<T, kAK, kBK, kEpi, kGroupK>), dim3((unsigned)blocks),
+                     dim3(kTThreads), 0, s, p);
+}
+
+Operand opnd(const void* p0, const void* p1, int64_t split, int64_t ld, int64_t estride) {
+  return Operand{p0, p1 ? p1 : p0, p1 ? split : INT64_MAX, ld, estride};
+}
+
+template <typename T>
+hipError_t experts_forward_training_t(const TrainExperts& q, hipStream_t s) {
+  const int64_t R = q.rows, H = q.H, I = q.I;
+  int32_t* prefix = static_cast<int32_t*>(q.ws);
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, s, q.offsets, q.E, kTBM, prefix);
+  T* gu = static_cast<T*>(q.cache);
+  T* h = gu + R * 2 * I;
+  TrainGemm p = {};
+  p.offsets = q.offsets; p.tile_prefix = prefix; p.E = q.E;
+  // [g | u] = X [W_gate; W_up]^T : N = 2I, K = H
+  p.a = opnd(q.x, nullptr, 0, H, 0);
+  p.b = opnd(q.w_gate, q.w_up, I, H, I * H);
+  p.N = (int)(2 * I); p.K = (int)H;
+  p.m_tiles = (int)mtile_bound(R, q.E); p.n_tiles = (int)((2 * I + kTBN - 1) / kTBN);
+  p.out0 = gu; p.out1 = gu; p.out_split = INT64_MAX; p.ldc = 2 * I;
+  launch_tg<T, true, true, kEpiStore, false>(p, s);
+  const int64_t n8 = R * (I / 8);
+  hipLaunchKernelGGL(swiglu_cache_kernel<T>, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, gu, h, R, (int)I);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t experts_backward_t(const TrainExperts& q, hipStream_t s) {
+  const int64_t R = q.rows, H = q.H, I = q.I;
+  int32_t* prefix = static_cast<int32_t*>(q.ws);
+  T* dgu = reinterpret_cast<T*>(static_cast<char*>(q.ws) + train_prefix_bytes(q.E));
+  const T* gu = static_cast<const T*>(q.cache);
+  const T* h = gu + R * 2 * I;
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, s, q.offsets, q.E, kTBM, prefix);
+  TrainGemm p = {};
+  p.offsets = q.offsets; p.tile_prefix = prefix; p.E = q.E;
+  p.m_tiles = (int)mtile_bound(R, q.E);
+  // dh = dY W_down (W_down [H, I] read along I), fused SwiGLU backward -> dg | du
+  p.a = opnd(q.dy, nullptr, 0, H, 0);
+  p.b = opnd(q.w_down, nullptr, 0, I, H * I);
+  p.N = (int)I; p.K = (int)H; p.n_tiles = (int)((I + kTBN - 1) / kTBN);
+  p.out0 = dgu; p.gu = gu;
+  launch_tg<T, true, false, kEpiSwiGluBwd, false>(p, s);
+  // dinput = [dg | du] [W_gate; W_up]  (weights [I, H] read along H), K = 2I
+  p.a = opnd(dgu, nullptr, 0, 2 * I, 0);
+  p.b = opnd(q.w_gate, q.w_up, I, H, I * H);
+  p.N = (int)H; p.K = (int)(2 * I); p.n_tiles = (int)((H + kTBN - 1) / kTBN);
+  p.out0 = q.dx; p.out1 = q.dx; p.out_split = INT64_MAX; p.ldc = H; p.gu = nullptr;
+  launch_tg<T, true, false, kEpiStore, false>(p, s);
+  // ddown[e] = dY_e^T h_e  [H, I], K = rows of e
+  TrainGemm w = {};
+  w.offsets = q.offsets; w.E = q.E;
+  w.a = opnd(q.dy, nullptr, 0, H, 0);
+  w.b = opnd(h, nullptr, 0, I, 0);
+  w.M = (int)H; w.N = (int)I;
+  w.m_tiles = (int)((H + kTBM - 1) / kTBM); w.n_tiles = (int)((I + kTBN - 1) / kTBN);
+  w.out0 = q.d_down; w.out1 = q.d_down; w.out_split = INT64_MAX; w.ldc = I; w.out_estride = H * I;
+  launch_tg<T, false, false, kEpiStoreF32, true>(w, s);
+  // dgate[e] | dup[e] = [dg | du]_e^T X_e  [2I, H], K = rows of e
+  w.a = opnd(dgu, nullptr, 0, 2 * I, 0);
+  w.b = opnd(q.x, nullptr, 0, H, 0);
+  w.M = (int)(2 * I); w.N = (int)H;
+  w.m_tiles = (int)((2 * I + kTBM - 1) / kTBM); w.n_tiles = (int)((H + kTBN - 1) / kTBN);
+  w.out0 = q.d_gate; w.out1 = q.d_up; w.out_split = I; w.ldc = H; w.out_estride = I * H;
+  launch_tg<T, false, false, kEpiStoreF32, true>(w, s);
+  return hipGetLastError();
+}
+
+template <typename LT, typename IT>
+void launch_router_t(const RouterGrad& r, hipStream_t s) {
+  const dim3 grid((unsigned)((r.T + 3) / 4)), block(256);
+  if (r.grad_weights)
+    hipLaunchKernelGGL((router_backward_kernel<LT, IT>), grid, block, 0, s,
+                       static_cast<const LT*>(r.logits), static_cast<const IT*>(r.indices),
+                       r.grad_weights, r.T, r.E, r.k, r.scoring, r.normalize, r.scale,
+                       static_cast<LT*>(r.grad_logits));
+  else
+    hipLaunchKernelGGL((router_weights_kernel<LT, IT>), grid, block, 0, s,
+                       static_cast<const LT*>(r.logits), static_cast<const IT*>(r.indices), r.T,
+                       r.E, r.k, r.scoring, r.normalize, r.scale, r.weights);
+}
+
+template <typename LT>
+void launch_router_lt(const RouterGrad& r, hipStream_t s) {
+  if (r.idx_dt == 0) launch_router_t<LT, uint32_t>(r, s);
+  else if (r.idx_dt == 1) launch_router_t<LT, int32_t>(r, s);
+  else launch_router_t<LT, int64_t>(r, s);
+}
+
+template <typename T, typename WT>
+void launch_cb(const void* y, const int32_t* ros, const void* w, const void* go, int T_, int k, int H,
+               void* dexp, float* dw, hipStream_t s) {
+  hipLaunchKernelGGL((combine_backward_kernel<T, WT>), dim3(T_), dim3(256), 0, s,
+                     static_cast<const T*>(y), ros, static_cast<const WT*>(w),
+                     static_cast<const T*>(go), k, H, static_cast<T*>(dexp), dw);
+}
+
+template <typename T>
+void launch_cb_w(const void* y, const int32_t* ros, const void* w, int w_dt, const void* go, int T_,
+                 int k, int H, void* dexp, float* dw, hipStream_t s) {
+  if (w_dt == kF32) launch_cb<T, float>(y, ros, w, go, T_, k, H, dexp, dw, s);
+  else if (w_dt == kF16) launch_cb<T, f16>(y, ros, w, go, T_, k, H, dexp, dw, s);
+  else launch_cb<T, bf16>(y, ros, w, go, T_, k, H, dexp, dw, s);
+}
+
+}  // namespace
+
+size_t train_prefix_bytes(int64_t E) { return ((size_t)(E + 1) * 4 + 255) / 256 * 256; }
+
+hipError_t launch_experts_forward_training(const TrainExperts& q, hipStream_t s) {
+  if (q.rows == 0) return hipSuccess;
+  hipError_t e = q.dt == kF16 ? experts_forward_training_t<f16>(q, s) : experts_forward_training_t<bf16>(q, s);
+  if (e != hipSuccess) return e;
+  void* h = static_cast<char*>(q.cache) + (size_t)q.rows * 2 * q.I * 2;
+  void* scratch = static_cast<char*>(q.ws) + train_prefix_bytes(q.E);
+  return launch_down(h, q.offsets, q.rows, q.E, q.H, q.I, q.w_down, q.dt, q.y, scratch, s);
+}
+
+hipError_t launch_experts_backward(const TrainExperts& q, hipStream_t s) {
+  return q.dt == kF16 ? experts_backward_t<f16>(q, s) : experts_backward_t<bf16>(q, s);
+}
+
+hipError_t launch_router_grad(const RouterGrad& r, hipStream_t s) {
+  if (r.T == 0) return hipSuccess;
+  if (r.logits_dt == kF32) launch_router_lt<float>(r, s);
+  else if (r.logits_dt == kF16) launch_router_lt<f16>(r, s);
+  else launch_router_lt<bf16>(r, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_backward(const void* y, const int32_t* row_of_slot, const void* w, int w_dt,
+                                   const void* grad_out, int T, int k, int H, int dt, void* dexpert,
+                                   float* dweights, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (dt == kF32) launch_cb_w<float>(y, row_of_slot, w, w_dt, grad_out, T, k, H, dexpert, dweights, s);
+  else if (dt == kF16) launch_cb_w<f16>(y, row_of_slot, w, w_dt, grad_out, T, k, H, dexpert, dweights, s);
+  else launch_cb_w<bf16>(y, row_of_slot, w, w_dt, grad_out, T, k, H, dexpert, dweights, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch_backward(const void* dinput, const int32_t* row_of_slot, int T, int k,
+                                    int H, int dt, void* dx, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (dt == kF32)
+    hipLaunchKernelGGL(dispatch_backward_kernel<float>, dim3(T), dim3(256), 0, s,
+                       static_cast<const float*>(dinput), row_of_slot, k, H, static_cast<float*>(dx));
+  else if (dt == kF16)
+    hipLaunchKernelGGL(dispatch_backward_kernel<f16>, dim3(T), dim3(256), 0, s,
+                       static_cast<const f16*>(dinput), row_of_slot, k, H, static_cast<f16*>(dx));
+  else
+    hipLaunchKernelGGL(dispatch_backward_kernel<bf16>, dim3(T), dim3(256), 0, s,
+                       static_cast<const bf16*>(dinput), row_of_slot, k, H, static_cast<bf16*>(dx));
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -63,6 +63,15 @@ _SIGS = {
                                      ctypes.c_float, P, P, P, I32, P, P, P, P, SZ, P, P], I32),
     "moe_combine_add_rmsnorm": ([P, P, P, I32, P, P, P, ctypes.c_float, I64, I64, I64, I32, P, P,
                                  P, P], I32),
+    "moe_router_weights": ([P, I32, P, I32, I64, I64, I64, I32, I32, ctypes.c_float, P, P], I32),
+    "moe_router_backward": ([P, I32, P, I32, P, I64, I64, I64, I32, I32, ctypes.c_float, P, P], I32),
+    "moe_combine_backward": ([P, P, P, I32, P, I64, I64, I64, I64, I32, P, P, P], I32),
+    "moe_dispatch_backward": ([P, P, I64, I64, I64, I64, I32, P, P], I32),
+    "moe_experts_forward_training": ([P, P, I64, I64, I64, I64, P, P, P, I32, P, P, P, SZ, P], I32),
+    "moe_experts_training_cache_size": ([I64, I64, I32], SZ),
+    "moe_experts_forward_training_workspace_size": ([I64, I64, I64, I64, I32], SZ),
+    "moe_experts_backward": ([P, P, I64, I64, I64, I64, P, P, P, I32, P, P, P, P, P, P, P, SZ, P], I32),
+    "moe_experts_backward_workspace_size": ([I64, I64, I64, I64, I32], SZ),
 }
 
 
@@ -394,3 +403,111 @@ def moe_combine_add_rmsnorm(expert_out, row_of_slot, weights, residual, gamma, e
         _ptr(residual), _ptr(gamma), float(eps), T, k, H, dtype_code(dt), _ptr(y), _ptr(x_out),
         _ptr(rstd), _stream()), "moe_combine_add_rmsnorm")
     return y, x_out, rstd
+
+
+# ---- first-order training (ruDNN user guide, "12. MoE first-order training") ----
+SOFTMAX, SIGMOID = 0, 1
+_IDX = {torch.int32: 1, torch.int64: 2}
+
+
+def _idx_code(indices, unsigned: bool):
+    """int32 storage is read as uint32 when unsigned (the routing plan's ids)."""
+    if indices.dtype == torch.int32 and unsigned:
+        return 0
+    if indices.dtype not in _IDX:
+        raise MoeError(3, "indices dtype")
+    return _IDX[indices.dtype]
+
+
+def moe_router_weights(logits, indices, scoring: int, normalize: bool, scale: float = 1.0,
+                       unsigned: bool = True, weights=None):
+    """fp32 [T, k] weights of the fixed selection `indices`."""
+    T, E = logits.shape
+    k = indices.shape[1]
+    if weights is None:
+        weights = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _check(lib().moe_router_weights(_ptr(logits), dtype_code(logits.dtype), _ptr(indices),
+                                    _idx_code(indices, unsigned), T, E, k, scoring, int(normalize),
+                                    scale, _ptr(weights), _stream()), "moe_router_weights")
+    return weights
+
+
+def moe_router_backward(logits, indices, grad_weights, scoring: int, normalize: bool,
+                        scale: float = 1.0, unsigned: bool = True, grad_logits=None):
+    """d loss / d logits [T, E] (logits dtype) for the fixed selection."""
+    T, E = logits.shape
+    k = indices.shape[1]
+    if grad_logits is None:
+        grad_logits = torch.empty_like(logits)
+    _check(lib().moe_router_backward(_ptr(logits), dtype_code(logits.dtype), _ptr(indices),
+                                     _idx_code(indices, unsigned), _ptr(grad_weights), T, E, k,
+                                     scoring, int(normalize), scale, _ptr(grad_logits), _stream()),
+           "moe_router_backward")
+    return grad_logits
+
+
+def moe_combine_backward(expert_out, row_of_slot, weights, grad_out, top_k: int,
+                         dexpert=None, dweights=None):
+    """Returns (dexpert [rows, H] model dtype, dweights [T, k] fp32)."""
+    T, H = grad_out.shape
+    if dexpert is None:
+        dexpert = torch.empty_like(expert_out)
+    if dweights is None:
+        dweights = torch.empty((T, top_k), dtype=torch.float32, device=grad_out.device)
+    _check(lib().moe_combine_backward(_ptr(expert_out), _ptr(row_of_slot), _ptr(weights),
+                                      dtype_code(weights.dtype), _ptr(grad_out), T, top_k, H,
+                                      expert_out.shape[0], dtype_code(grad_out.dtype), _ptr(dexpert),
+                                      _ptr(dweights),
+                                      _stream()), "moe_combine_backward")
+    return dexpert, dweights
+
+
+def moe_dispatch_backward(dinput, row_of_slot, T: int, top_k: int, dx=None):
+    """dx [T, H]: sum of each token's dispatched rows of dinput."""
+    H = dinput.shape[1]
+    if dx is None:
+        dx = torch.empty((T, H), dtype=dinput.dtype, device=dinput.device)
+    _check(lib().moe_dispatch_backward(_ptr(dinput), _ptr(row_of_slot), T, top_k, H, dinput.shape[0],
+                                       dtype_code(dinput.dtype), _ptr(dx), _stream()),
+           "moe_dispatch_backward")
+    return dx
+
+
+def moe_experts_forward_training(x_disp, offsets, w_gate, w_up, w_down, rows: int | None = None,
+                                 expert_out=None, cache=None, ws=None):
+    """Returns (expert_out [rows, H], cache [rows * 3I] holding (g | u) then h)."""
+    E, I_, H = w_gate.shape
+    rows = x_disp.shape[0] if rows is None else rows
+    dt = dtype_code(x_disp.dtype)
+    if expert_out is None:
+        expert_out = torch.empty((rows, H), dtype=x_disp.dtype, device=x_disp.device)
+    if cache is None:
+        cache = torch.empty(rows * 3 * I_, dtype=x_disp.dtype, device=x_disp.device)
+    if ws is None:
+        ws = _workspace(lib().moe_experts_forward_training_workspace_size(rows, E, H, I_, dt), x_disp.device)
+    _check(lib().moe_experts_forward_training(_ptr(x_disp), _ptr(offsets), rows, E, H, I_, _ptr(w_gate),
+                                              _ptr(w_up), _ptr(w_down), dt, _ptr(expert_out), _ptr(cache),
+                                              _ptr(ws), ws.numel(), _stream()),
+           "moe_experts_forward_training")
+    return expert_out, cache
+
+
+def moe_experts_backward(x_disp, offsets, w_gate, w_up, w_down, cache, dexpert, rows: int | None = None,
+                         dinput=None, dgate=None, dup=None, ddown=None, ws=None):
+    """Returns (dinput [rows, H] model dtype, dgate, dup [E, I, H] fp32, ddown [E, H, I] fp32)."""
+    E, I_, H = w_gate.shape
+    rows = x_disp.shape[0] if rows is None else rows
+    dt = dtype_code(w_gate.dtype)
+    dev = w_gate.device
+    if dinput is None:
+        dinput = torch.empty((rows, H), dtype=w_gate.dtype, device=dev)
+    dgate = torch.empty((E, I_, H), dtype=torch.float32, device=dev) if dgate is None else dgate
+    dup = torch.empty((E, I_, H), dtype=torch.float32, device=dev) if dup is None else dup
+    ddown = torch.empty((E, H, I_), dtype=torch.float32, device=dev) if ddown is None else ddown
+    if ws is None:
+        ws = _workspace(lib().moe_experts_backward_workspace_size(rows, E, H, I_, dt), dev)
+    _check(lib().moe_experts_backward(_ptr(x_disp), _ptr(offsets), rows, E, H, I_, _ptr(w_gate), _ptr(w_up),
+                                      _ptr(w_down), dt, _ptr(cache), _ptr(dexpert), _ptr(dinput),
+                                      _ptr(dgate), _ptr(dup), _ptr(ddown), _ptr(ws), ws.numel(), _stream()),
+           "moe_experts_backward")
+    return dinput, dgate, dup, ddown

@@ -615,7 +615,8 @@ def router_selected_backward(logits, logits_dtype, indices, grad_weights, scorin
         da = dscore[idx[t]]                            # [k, E]
         if normalize:
             S = a.sum()
-            jac = c * (da / S - np.outer(a, da.sum(axis=0)) / S ** 2)
+            with np.errstate(invalid="ignore", divide="ignore"):
+                jac = c * (da / S - np.outer(a, da.sum(axis=0)) / S ** 2)
         else:
             jac = c * da
         out[t] = g[t] @ jac

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 21, names
+    assert len(names) == 30, names
     lib = moe.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -225,3 +225,78 @@ def test_quant_validation():
     assert call(11, None) == S["MOE_ERROR_NULL_POINTER"]  # scale missing
     assert call(20, need - 1) == S["MOE_ERROR_WORKSPACE"]
     assert call(2, 0) == S["MOE_SUCCESS"]
+
+
+def test_training_validation():
+    lib = moe.lib()
+    # router weights: logits, logits_dt, indices, idx_dt, T, E, k, scoring, normalize, scale, weights, stream
+    f = lib.moe_router_weights
+    ok = [FAKE, 0, FAKE + 2**20, 0, 4, 8, 2, 0, 1, 1.0, FAKE + 2**21, None]
+
+    def call(fn, base, i, v):
+        a = list(base)
+        a[i] = v
+        return fn(*a)
+    assert call(f, ok, 6, 0) == S["MOE_ERROR_ARGUMENT"]       # top_k 0
+    assert call(f, ok, 6, 9) == S["MOE_ERROR_ARGUMENT"]       # top_k > E
+    assert call(f, ok, 7, 2) == S["MOE_ERROR_ARGUMENT"]       # unknown scoring
+    assert call(f, ok, 9, 0.0) == S["MOE_ERROR_ARGUMENT"]     # scale must be > 0
+    assert call(f, ok, 9, float("inf")) == S["MOE_ERROR_ARGUMENT"]
+    assert call(f, ok, 3, 3) == S["MOE_ERROR_DTYPE"]          # index dtype
+    assert call(f, ok, 1, 5) == S["MOE_ERROR_DTYPE"]
+    assert call(f, ok, 5, 1025) == S["MOE_ERROR_UNSUPPORTED"]
+    assert call(f, ok, 10, None) == S["MOE_ERROR_NULL_POINTER"]
+    assert call(f, ok, 10, FAKE + 8) == S["MOE_ERROR_ARGUMENT"]  # output overlaps the logits
+    assert call(f, ok, 4, 0) == S["MOE_SUCCESS"]
+    a = list(ok)
+    a[5], a[6] = 128, 65
+    assert f(*a) == S["MOE_ERROR_ARGUMENT"]                    # top_k > 64
+    g = lib.moe_router_backward
+    okb = [FAKE, 0, FAKE + 2**20, 0, FAKE + 2**21, 4, 8, 2, 1, 0, 1.0, FAKE + 2**22, None]
+    assert call(g, okb, 4, None) == S["MOE_ERROR_NULL_POINTER"]  # grad_weights
+    assert call(g, okb, 11, None) == S["MOE_ERROR_NULL_POINTER"]
+    assert call(g, okb, 11, FAKE + 2**20 + 4) == S["MOE_ERROR_ARGUMENT"]  # overlaps the indices
+    # combine backward: y, ros, w, w_dt, go, T, k, H, dt, dexp, dw, stream
+    c = lib.moe_combine_backward
+    okc = [FAKE, FAKE + 2**20, FAKE + 2**21, 0, FAKE + 2**22, 4, 2, 64, 8, 2, FAKE + 2**23, FAKE + 2**24, None]
+    assert call(c, okc, 7, 60) == S["MOE_ERROR_UNSUPPORTED"]
+    assert call(c, okc, 9, 9) == S["MOE_ERROR_DTYPE"]
+    assert call(c, okc, 8, 9) == S["MOE_ERROR_SHAPE"]           # rows > T * top_k
+    assert call(c, okc, 11, None) == S["MOE_ERROR_NULL_POINTER"]
+    assert call(c, okc, 10, FAKE + 16) == S["MOE_ERROR_ARGUMENT"]
+    assert call(c, okc, 5, 0) == S["MOE_ERROR_SHAPE"]            # rows 8 > 0 * 2
+    a = list(okc)
+    a[5], a[8] = 0, 0
+    assert c(*a) == S["MOE_SUCCESS"]
+    d = lib.moe_dispatch_backward
+    okd = [FAKE, FAKE + 2**20, 4, 2, 64, 8, 2, FAKE + 2**21, None]
+    assert call(d, okd, 7, FAKE + 64) == S["MOE_ERROR_ARGUMENT"]
+    assert call(d, okd, 3, 0) == S["MOE_ERROR_SHAPE"]
+    assert call(d, okd, 5, -1) == S["MOE_ERROR_SHAPE"]
+    a = list(okd)
+    a[2], a[5] = 0, 0
+    assert d(*a) == S["MOE_SUCCESS"]
+    # experts training forward / backward
+    need_f = lib.moe_experts_forward_training_workspace_size(64, 8, 512, 384, 2)
+    need_b = lib.moe_experts_backward_workspace_size(64, 8, 512, 384, 2)
+    assert need_f > 0 and need_b >= 64 * 384 * 2 * 2
+    assert lib.moe_experts_backward_workspace_size(64, 8, 512, 384, 0) == 0  # fp32 unsupported
+    assert lib.moe_experts_training_cache_size(64, 384, 2) == 64 * 3 * 384 * 2
+    ft = lib.moe_experts_forward_training
+    okf = [FAKE, FAKE + 2**20, 64, 8, 512, 384, FAKE + 2**24, FAKE + 2**25, FAKE + 2**26, 2,
+           FAKE + 2**27, FAKE + 2**28, FAKE + 2**29, need_f, None]
+    assert call(ft, okf, 9, 0) == S["MOE_ERROR_UNSUPPORTED"]
+    assert call(ft, okf, 5, 380) == S["MOE_ERROR_UNSUPPORTED"]
+    assert call(ft, okf, 11, None) == S["MOE_ERROR_NULL_POINTER"]
+    assert call(ft, okf, 13, need_f - 1) == S["MOE_ERROR_WORKSPACE"]
+    assert call(ft, okf, 12, FAKE + 2**29 + 8) == S["MOE_ERROR_WORKSPACE"]  # misaligned
+    assert call(ft, okf, 11, FAKE + 2**27 + 64) == S["MOE_ERROR_ARGUMENT"]  # cache overlaps expert_out
+    assert call(ft, okf, 2, 0) == S["MOE_SUCCESS"]
+    bw = lib.moe_experts_backward
+    okw = [FAKE, FAKE + 2**20, 64, 8, 512, 384, FAKE + 2**24, FAKE + 2**25, FAKE + 2**26, 2,
+           FAKE + 2**27, FAKE + 2**28, FAKE + 2**29, FAKE + 2**31, FAKE + 2**32, FAKE + 2**33,
+           FAKE + 2**34, need_b, None]
+    assert call(bw, okw, 9, 0) == S["MOE_ERROR_UNSUPPORTED"]
+    assert call(bw, okw, 14, None) == S["MOE_ERROR_NULL_POINTER"]
+    assert call(bw, okw, 17, need_b - 1) == S["MOE_ERROR_WORKSPACE"]
+    assert call(bw, okw, 14, FAKE + 2**31 + 4) == S["MOE_ERROR_ARGUMENT"]  # dup overlaps dgate

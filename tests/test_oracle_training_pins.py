@@ -15,7 +15,7 @@ import torch
 
 from oracle import moe_oracle as O
 
-torch.set_default_dtype(torch.float64)
+F64 = torch.float64
 
 
 def _f32(a):
@@ -222,7 +222,7 @@ def test_dispatch_backward_is_the_gather_adjoint():
     R = int(d["offsets"][-1])
     dinput = _f32(r.standard_normal((R, H)))
     dx = O.dispatch_backward(dinput, d["row_of_slot"], T, k, H, "f32")
-    xt = torch.zeros((T, H), requires_grad=True)
+    xt = torch.zeros((T, H), dtype=F64, requires_grad=True)
     tok = torch.tensor(d["slot_of_row"].astype(np.int64) // k)
     (xt[tok] * torch.tensor(dinput.astype(np.float64))).sum().backward()
     np.testing.assert_allclose(dx, xt.grad.numpy(), rtol=1e-6, atol=1e-7)
@@ -254,7 +254,7 @@ def test_training_chain_matches_autograd(scoring, normalize):
     xt = torch.tensor(x.astype(np.float64), requires_grad=True)
     Wt = [[torch.tensor(a.astype(np.float64), requires_grad=True) for a in We] for We in W]
     wt = _torch_router_weights(zt, torch.tensor(idx.astype(np.int64)), scoring, normalize, 1.25)
-    out = torch.zeros((T, H))
+    out = torch.zeros((T, H), dtype=F64)
     for t in range(T):
         for j in range(k):
             e = int(idx[t, j])
