@@ -78,6 +78,9 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="tokens of the workload the CPU oracle runs on (default: a per-workload "
                          "sample of roughly 5-30 s)")
+    ap.add_argument("--train", action="store_true",
+                    help="time one first-order training step (forward with the experts' cache, "
+                         "then combine, expert, dispatch and router backward) instead of the forward")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 5 times (the "
                          "reference kernel for scaling HBM byte counters), then exit")
@@ -144,6 +147,9 @@ def main():
     xd, zd = to_dev(x), to_dev(z, "f32")
     torch.cuda.synchronize()
     log(f"inputs ready in {time.time() - t0:.1f}s: {args.workload} T={T} H={H} I={I_} E={E} k={k}")
+
+    if args.train:
+        return run_train(args, w, x, z, xd, zd, wt, kept, n_cpu)
 
     # ---- buffers ----------------------------------------------------------
     idx = torch.empty((T, k), dtype=torch.int32, device=dev)
@@ -285,6 +291,150 @@ def main():
         "roofline": roofline, "cpu_baseline": cpu,
     }
     res.update(extra)
+    print(json.dumps(res), flush=True)
+
+
+TRAIN_STAGES = ["route", "router_weights", "dispatch", "experts_fwd", "combine",
+                "combine_bwd", "experts_bwd", "dispatch_bwd", "router_bwd"]
+TRAIN_CPU_TOKENS = {"tiny_fp32": 64, "mixtral_8x_bf16": 16, "many_expert_zipf_bf16": 64,
+                    "dsv3_share_rmsnorm_bf16": 4, "decode_nan_rows_bf16": 16}
+
+
+def run_train(args, w, x, z, xd, zd, wt, kept, n_cpu):
+    """One training step through the C ABI: the routing plan's selection, its
+    fp32 weights (selected_router_weights), dispatch with x_disp, the experts'
+    training forward (cache of g, u, h), combine; then combine_backward,
+    the experts' backward, dispatch_backward and the router backward, with a
+    fixed synthetic gradient of the output. Stage events on this stream."""
+    import torch
+    from mixture_experts_ffn_top_amd import moe
+
+    T, H, I_, E, k = w.T, w.H, w.I, w.E, w.top_k
+    R = T * k
+    if w.dtype != "bf16":
+        raise SystemExit("the training path runs on the bf16/f16 matrix cores; pick a bf16 workload")
+    td, dev = torch.bfloat16, "cuda"
+    from mixture_experts_ffn_top_amd import inputs as I
+    go_host = I.grad_output_for(w)
+    grad_out = torch.from_numpy(go_host.view(np.int16)).view(td).to(dev)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    wts_plan = torch.empty((T, k), dtype=torch.float32, device=dev)
+    wts = torch.empty((T, k), dtype=torch.float32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    sor = torch.empty(R, dtype=torch.int32, device=dev)
+    ros = torch.empty(R, dtype=torch.int32, device=dev)
+    x_disp = torch.empty((R, H), dtype=td, device=dev)
+    y = torch.empty((R, H), dtype=td, device=dev)
+    out = torch.empty((T, H), dtype=td, device=dev)
+    cache = torch.empty(R * 3 * I_, dtype=td, device=dev)
+    dexp = torch.empty((R, H), dtype=td, device=dev)
+    dw = torch.empty((T, k), dtype=torch.float32, device=dev)
+    dinput = torch.empty((R, H), dtype=td, device=dev)
+    dgate = torch.empty((E, I_, H), dtype=torch.float32, device=dev)
+    dup = torch.empty_like(dgate)
+    ddown = torch.empty((E, H, I_), dtype=torch.float32, device=dev)
+    dx = torch.empty((T, H), dtype=td, device=dev)
+    dz = torch.empty((T, E), dtype=torch.float32, device=dev)
+    ws_d = torch.empty(moe.moe_dispatch_workspace_size(T, k, E), dtype=torch.uint8, device=dev)
+    ws_f = torch.empty(moe.lib().moe_experts_forward_training_workspace_size(R, E, H, I_, moe.BF16),
+                       dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(moe.lib().moe_experts_backward_workspace_size(R, E, H, I_, moe.BF16),
+                       dtype=torch.uint8, device=dev)
+    scoring = moe.SOFTMAX
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        moe.moe_route(zd, k, w.renormalize, indices=idx, weights=wts_plan)
+        mark(1)
+        moe.moe_router_weights(zd, idx, scoring, w.renormalize, 1.0, weights=wts)
+        mark(2)
+        moe.moe_dispatch(idx, E, xd, ws=ws_d, offsets=offsets, slot_of_row=sor, row_of_slot=ros,
+                         x_disp=x_disp)
+        mark(3)
+        moe.moe_experts_forward_training(x_disp, offsets, wt["w_gate"], wt["w_up"], wt["w_down"], rows=R,
+                                         expert_out=y, cache=cache, ws=ws_f)
+        mark(4)
+        moe.moe_combine(y, ros, wts, out=out)
+        mark(5)
+        moe.moe_combine_backward(y, ros, wts, grad_out, k, dexpert=dexp, dweights=dw)
+        mark(6)
+        moe.moe_experts_backward(x_disp, offsets, wt["w_gate"], wt["w_up"], wt["w_down"], cache, dexp, rows=R,
+                                 dinput=dinput, dgate=dgate, dup=dup, ddown=ddown, ws=ws_b)
+        mark(7)
+        moe.moe_dispatch_backward(dinput, ros, T, k, dx=dx)
+        mark(8)
+        moe.moe_router_backward(zd, idx, dw, scoring, w.renormalize, 1.0, grad_logits=dz)
+        mark(9)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"train warmup done ({args.warmup} steps)")
+    n_ev = len(TRAIN_STAGES) + 1
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    for ev in evs:
+        for e_ in ev:
+            e_.record()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s_ in range(args.steps):
+        step(evs[s_])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    log(f"timed {args.steps} training steps in {elapsed:.3f}s")
+    stage_ms = {name: float(np.mean([evs[s_][i].elapsed_time(evs[s_][i + 1]) for s_ in range(args.steps)]))
+                for i, name in enumerate(TRAIN_STAGES)}
+    # the experts' backward: dh (2RHI), dinput (4RHI), ddown (2RHI), dgate|dup (4RHI)
+    flops_bwd = 12.0 * R * H * I_
+    flops_fwd = 6.0 * R * H * I_
+    bwd_tf = flops_bwd / (stage_ms["experts_bwd"] / 1e3) / 1e12
+    fwd_tf = flops_fwd / (stage_ms["experts_fwd"] / 1e3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(bwd_tf, 1), "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
+                "frac": round(bwd_tf / PEAK_TFLOPS["bf16"], 4), "traffic": None,
+                "kernel": "moe_experts_backward (4 train_gemm_kernel launches + tile prefix)",
+                "algorithmic_per_launch": flops_bwd}
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import moe_oracle as O
+        n = min(args.cpu_tokens or TRAIN_CPU_TOKENS.get(args.workload, 16), T)
+        cores = len(os.sched_getaffinity(0))
+        idx_s, _ = O.route(z[:n], "f32", k, w.renormalize)
+        need = sorted(set(int(e) for e in idx_s.ravel()))
+        if all(e in kept for e in need):
+            wo = lambda e: (kept[e]["w_gate"], kept[e]["w_up"], kept[e]["w_down"])  # noqa: E731
+            sub = {e: i for i, e in enumerate(need)}
+            go = go_host[:n]
+            log(f"cpu baseline: oracle training step on {n} tokens")
+            c0 = time.perf_counter()
+            wr = O.router_selected_weights(z[:n], "f32", idx_s, O.SOFTMAX, w.renormalize, 1.0)
+            idx_l = np.vectorize(sub.get)(idx_s).astype(np.uint32)
+            d = O.dispatch(idx_l, len(need), x[:n])
+            wl = lambda i: wo(need[i])  # noqa: E731
+            y_r, g_r, u_r, h_r = O.experts_forward_training(d["x_disp"], d["offsets"], wl, w.dtype)
+            O.combine(y_r, d["row_of_slot"], wr, "f32", n, k, w.dtype)
+            de, dwr = O.combine_backward(y_r, d["row_of_slot"], wr, "f32", go, n, k, w.dtype)
+            di, _, _, _ = O.experts_backward(d["x_disp"], d["offsets"], wl, g_r, u_r, h_r, de, w.dtype)
+            O.dispatch_backward(di, d["row_of_slot"], n, k, H, w.dtype)
+            O.router_selected_backward(z[:n], "f32", idx_s, dwr, O.SOFTMAX, w.renormalize, 1.0)
+            c_el = time.perf_counter() - c0
+            cpu = {"value": round(n / c_el, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+                   "sample": f"training step on the first {n} of {T} tokens of {args.workload} "
+                             f"({len(need)} experts); {c_el:.1f}s wall"}
+    res = {
+        "metric": "MoE training step tokens/s (forward with cache + backward)",
+        "value": round(T * args.steps / elapsed, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": args.workload + "+train", "T": T, "H": H, "I": I_, "E": E, "top_k": k,
+                   "scoring": "softmax", "normalize": w.renormalize},
+        "roofline": roofline, "cpu_baseline": cpu,
+        "stages_ms": {k_: round(v, 4) for k_, v in stage_ms.items()},
+        "experts_fwd_tflops": round(fwd_tf, 1), "experts_bwd_tflops": round(bwd_tf, 1),
+    }
     print(json.dumps(res), flush=True)
 
 

@@ -191,6 +191,11 @@ def expert_weights(w: Workload, which: str, experts=None, threads: int | None = 
     return out
 
 
+def grad_output_for(w: Workload) -> np.ndarray:
+    """Gradient of the MoE output for a training step: [T, H] ~ N(0, 1) in the model dtype."""
+    return store(normal(w.seed, "grad_out", (w.T, w.H)), w.dtype)
+
+
 def epilogue_inputs(w: Workload):
     """Shared-expert output and residual [T, H] ~ N(0,1); gamma fp32 [H] ~ U(0.5, 1.5)."""
     shared = store(normal(w.seed, "shared", (w.T, w.H)), w.dtype)

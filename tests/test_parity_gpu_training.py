@@ -18,9 +18,10 @@ import numpy as np
 import pytest
 import torch
 
+from mixture_experts_ffn_top_amd import inputs as I
 from mixture_experts_ffn_top_amd import moe
 from oracle import moe_oracle as O
-from parity_helpers import TOL, assert_close, decode, dev, host
+from parity_helpers import TOL, assert_close, decode, dev, host, upload_expert_weights
 
 pytestmark = pytest.mark.gpu
 
@@ -280,3 +281,98 @@ def test_training_step_chain(scoring, normalize):
     # dweights and dlogits inherit the bf16 rounding of expert_out: bf16 tolerance, scaled
     _assert_scaled(host(dw), dw_ref, dtype, "dweights")
     _assert_scaled(host(dz), dz_ref, dtype, "dlogits")
+
+
+# ------------------------------------------------- full-size training step --
+def test_training_step_mixtral_shape_sampled():
+    """The Mixtral-shaped workload (T=4096, H=4096, I=14336, E=8, top-2) through
+    the same entry points the training benchmark times. Routing weights,
+    offsets and maps are compared in full; expert outputs, the cache, dexpert,
+    dweights, dinput, dx and dlogits on sampled tokens (first, middle, last,
+    random); weight gradients on sampled columns of I for three experts, from
+    all of each expert's rows (the oracle's experts are separable over I)."""
+    w = I.workload("mixtral_8x_bf16")
+    T, H, I_, E, k, dt = w.T, w.H, w.I, w.E, w.top_k, w.dtype
+    R = T * k
+    say("training mixtral-shaped: inputs")
+    z = I.logits_for(w)
+    x = I.tokens_for(w)
+    go = I.grad_output_for(w)
+    wg, wu, wd, W = upload_expert_weights(w, keep=range(E))
+    zd, xd, god = dev(z, "f32"), dev(x, dt), dev(go, dt)
+    say("training mixtral-shaped: gpu step")
+    idx, _ = moe.moe_route(zd, k, True)
+    wts = moe.moe_router_weights(zd, idx, O.SOFTMAX, True, 1.0)
+    d = moe.moe_dispatch(idx, E, xd)
+    y, cache = moe.moe_experts_forward_training(d["x_disp"], d["offsets"], wg, wu, wd, rows=R)
+    dexp, dw = moe.moe_combine_backward(y, d["row_of_slot"], wts, god, k)
+    dinput, dgate, dup, ddown = moe.moe_experts_backward(d["x_disp"], d["offsets"], wg, wu, wd, cache, dexp,
+                                                         rows=R)
+    dx = moe.moe_dispatch_backward(dinput, d["row_of_slot"], T, k)
+    dz = moe.moe_router_backward(zd, idx, dw, O.SOFTMAX, True, 1.0)
+    torch.cuda.synchronize()
+    say("training mixtral-shaped: oracle")
+    idx_ref, _ = O.route(z, "f32", k, True)
+    assert np.array_equal(host(idx).astype(np.uint32), idx_ref)
+    w_ref = O.router_selected_weights(z, "f32", idx_ref, O.SOFTMAX, True, 1.0)
+    assert_close(host(wts), w_ref, "f32", "weights")
+    od = O.dispatch(idx_ref, E)
+    for key in ("offsets", "slot_of_row", "row_of_slot"):
+        assert np.array_equal(host(d[key]), od[key]), key
+    c = host(cache)
+    gu_gpu, h_gpu = c[:R * 2 * I_].reshape(R, 2 * I_), c[R * 2 * I_:].reshape(R, I_)
+    y_g, dexp_g, dinput_g = host(y), host(dexp), host(dinput)
+    rng = np.random.default_rng(3)
+    tokens = sorted({0, 1, T // 2, T - 1, *rng.integers(0, T, 4).tolist()})
+    pairs = [(t, j) for t in tokens for j in range(k)]
+    by_e = {}
+    for t, j in pairs:
+        by_e.setdefault(int(idx_ref[t, j]), []).append((t, j))
+    fwd = {}
+    for e, pj in by_e.items():  # one oracle call per expert over its sampled rows
+        outs = O.swiglu_expert_training(x[[t for t, _ in pj]], *W[e], dt)
+        for n, tj in enumerate(pj):
+            fwd[tj] = tuple(o[n:n + 1] for o in outs)
+    de, dwt = {}, {}
+    for t in tokens:
+        y_rows = np.concatenate([fwd[(t, j)][0] for j in range(k)])
+        d_, w_ = O.combine_backward(y_rows, np.arange(k, dtype=np.int32), w_ref[t:t + 1], "f32", go[t:t + 1],
+                                    1, k, dt)
+        dwt[t] = w_
+        for j in range(k):
+            de[(t, j)] = d_[j:j + 1]
+    di = {}
+    for e, pj in by_e.items():
+        cat = lambda i: np.concatenate([fwd[tj][i] for tj in pj])  # noqa: E731
+        d_in = O.swiglu_expert_backward(x[[t for t, _ in pj]], *W[e], cat(1), cat(2), cat(3),
+                                        np.concatenate([de[tj] for tj in pj]), dt)[0]
+        for n, tj in enumerate(pj):
+            di[tj] = d_in[n:n + 1]
+    for t in tokens:
+        for j in range(k):
+            r = od["row_of_slot"][t * k + j]
+            yr, g_, u_, h_ = fwd[(t, j)]
+            assert_close(y_g[r:r + 1], yr, dt, f"expert_out t={t}")
+            assert_close(gu_gpu[r:r + 1, :I_], g_, dt, f"cache g t={t}")
+            assert_close(gu_gpu[r:r + 1, I_:], u_, dt, f"cache u t={t}")
+            assert_close(h_gpu[r:r + 1], h_, dt, f"cache h t={t}")
+            assert_close(dexp_g[r:r + 1], de[(t, j)], dt, f"dexpert t={t}")
+            assert_close(dinput_g[r:r + 1], di[(t, j)], dt, f"dinput t={t}")
+        _assert_scaled(host(dw)[t], dwt[t][0], dt, f"dweights t={t}")
+        dx_ref = O.dispatch_backward(np.concatenate([di[(t, j)] for j in range(k)]),
+                                     np.arange(k, dtype=np.int32), 1, k, H, dt)
+        assert_close(host(dx)[t:t + 1], dx_ref, dt, f"dx t={t}")
+        dz_ref = O.router_selected_backward(z[t:t + 1], "f32", idx_ref[t:t + 1], dwt[t], O.SOFTMAX, True, 1.0)
+        _assert_scaled(host(dz)[t], dz_ref[0], dt, f"dlogits t={t}")
+    # weight gradients: sampled columns of I, all rows of the expert
+    dexp_all, _ = O.combine_backward(np.zeros((R, H), np.uint16), od["row_of_slot"], w_ref, "f32", go, T, k, dt)
+    for e in (0, 3, E - 1):
+        a, b = int(od["offsets"][e]), int(od["offsets"][e + 1])
+        xe = x[od["slot_of_row"][a:b] // k]
+        isel = np.sort(rng.choice(I_, 8, replace=False))
+        wge, wue, wde = W[e][0][isel], W[e][1][isel], np.ascontiguousarray(W[e][2][:, isel])
+        _, g_, u_, h_ = O.swiglu_expert_training(xe, wge, wue, wde, dt)
+        _, dg_ref, du_ref, dd_ref = O.swiglu_expert_backward(xe, wge, wue, wde, g_, u_, h_, dexp_all[a:b], dt)
+        _assert_scaled(host(dgate[e])[isel], dg_ref, dt, f"dgate e={e}")
+        _assert_scaled(host(dup[e])[isel], du_ref, dt, f"dup e={e}")
+        _assert_scaled(host(ddown[e])[:, isel], dd_ref, dt, f"ddown e={e}")
