@@ -32,29 +32,36 @@
 namespace moe {
 namespace {
 
-constexpr int kTBM = 128;       // output tile rows
-constexpr int kTBN = 128;       // output tile columns
-constexpr int kTBK = 32;        // K per LDS stage
-constexpr int kTThreads = 256;  // 4 wavefronts as 2 x 2, 64 x 64 outputs each
-constexpr int kLdsRow = 40;     // LDS row: 32 elements + 8 padding (80 bytes)
-constexpr int kNGroup = 8;      // N-tiles per group in the M-grouped tile order
+constexpr int kTM = 256;           // output tile rows
+constexpr int kTN = 256;           // output tile columns
+constexpr int kTK = 64;            // K per LDS stage
+constexpr int kTWaves = 8;         // 4 (M) x 2 (N); 64 x 128 outputs per wavefront
+constexpr int kTThreads = 64 * kTWaves;
+constexpr int kNGroup = 8;         // N-tiles per group in the M-grouped tile order
+constexpr int kRsrcFlags = 0x00020000;  // raw buffer, no format, no swizzle (gfx9 family)
+constexpr uint32_t kOOR = 0x80000000u;  // voffset past every buffer built here: reads zeros
+constexpr int kRecords = 0x7FFFFFF0;    // buffer size in bytes: every real offset is smaller
 
 enum Epilogue { kEpiStore = 0, kEpiStoreF32 = 1, kEpiSwiGluBwd = 2 };
 
-struct Operand {
-  const void* p0;   // index < split
-  const void* p1;   // index >= split (index - split)
-  int64_t split;    // split along mn (K-contiguous) or along k (MN-contiguous)
-  int64_t ld;       // elements between consecutive outer rows
-  int64_t estride;  // elements between experts (0: rows shared by all experts)
+// One GEMM operand. Element (mn, k) of K-segment s for expert e lies at
+//   K-contiguous:  p[s] + e * estride + mn * ld + kofs[s] + k
+//   MN-contiguous: p[s] + e * estride + (kofs[s] + k) * ld + mn
+struct TOp {
+  const void* p[2];
+  int64_t ld;
+  int64_t estride;
+  int64_t kofs[2];
 };
 
 struct TrainGemm {
-  Operand a, b;
+  TOp a, b;
+  int nseg;                    // M-grouped: K segments (1 or 2), each a multiple of 8 long
+  int64_t seg_len[2];
   const int32_t* offsets;      // [E+1]
   const int32_t* tile_prefix;  // M-grouped: [E+1] prefix of M-tiles per expert
   int E;
-  int M, N, K;                 // M-grouped: M unused; K-grouped: K unused
+  int M, N;                    // M-grouped: M unused
   int m_tiles, n_tiles;        // M-grouped: m_tiles is the bound the grid is sized for
   void* out0;
   void* out1;
@@ -77,92 +84,124 @@ template <> struct TMfma<f16> {
 };
 template <typename T> using Frag = typename std::conditional<std::is_same<T, bf16>::value, bf16x8, f16x8>::type;
 
-__device__ __forceinline__ uint32_t half_of(const uint4& v, int i) {
-  const uint32_t w = i < 2 ? (i == 0 ? v.x : v.y) : (i == 2 ? v.z : v.w);
-  return w;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// One LDS object per (operand, stage), 32 KB each: 256 rows x 64 k (K-
+// contiguous operand) or 64 k-rows x 256 (MN-contiguous operand).
+template <typename T, int kOperand, int kStage>
+__device__ __forceinline__ T* tbuf() {
+  __shared__ __attribute__((aligned(1024))) T buf[kTM * kTK];
+  return buf;
 }
 
-// 16-bit element i (0..7) of a 16-byte chunk.
-__device__ __forceinline__ uint32_t elem16(const uint4& v, int i) {
-  return (half_of(v, i >> 1) >> ((i & 1) * 16)) & 0xFFFFu;
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-template <typename T>
-__device__ __forceinline__ const T* seg_ptr(const Operand& op, int e, int64_t outer) {
-  const bool hi = outer >= op.split;
-  const T* base = static_cast<const T*>(hi ? op.p1 : op.p0);
-  return base + (int64_t)e * op.estride + (hi ? outer - op.split : outer) * op.ld;
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t vo) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, vo, 0, 0, 0);
 }
 
-// K-contiguous operand: a tile of kTBM rows (mn) x kTBK (k); two 16-byte
-// chunks per thread. Rows >= mn_end and k >= k_end read as zeros.
-template <typename T>
-__device__ __forceinline__ void load_kc(const Operand& op, int e, int64_t mn0, int64_t mn_end,
-                                        int64_t k0, int64_t k_end, uint4 (&r)[2]) {
+// Copies one operand's k-tile into LDS with buffer loads straight to LDS:
+// instruction j of wavefront w fills the 1 KB block q = 8j + w, lane l its
+// 16 bytes at 16 l; the lane fetches the global chunk the swizzle puts there.
+//  K-contiguous: block q = rows 8q .. 8q+7 (128-byte rows, 8 chunks); chunk c
+//    of row r sits in slot c ^ ((r >> 1) & 7), so the 16 lanes of a 128-bit
+//    fragment read (16 consecutive rows, one chunk) hit 16 bank groups.
+//  MN-contiguous: block q = k-rows 2q, 2q+1 (512-byte rows, 32 chunks); chunk
+//    c of k-row k sits in slot c ^ 4 (k & 3), so a transposed read (4 k-rows x
+//    64 bytes per 32 lanes) hits 16 distinct bank groups.
+// Rows at or past mn_end, and k at or past k_valid, read as zeros.
+template <typename T, bool kKC>
+__device__ __forceinline__ void load_tile(const TOp& op, int seg, int e, int64_t mn0, int64_t mn_end,
+                                          int64_t kbase, int k_valid, T* dst, int wave, int lane) {
+  if (kKC) {
+    const T* base = static_cast<const T*>(op.p[seg]) + (int64_t)e * op.estride + mn0 * op.ld + kbase;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base), (short)0, kRecords, kRsrcFlags);
+    const int c = (lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7);
+    const bool kok = c * 8 < k_valid;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = threadIdx.x + i * kTThreads;
-    const int64_t mn = mn0 + (c >> 2), k = k0 + (c & 3) * 8;
-    r[i] = make_uint4(0, 0, 0, 0);
-    if (mn < mn_end && k < k_end) r[i] = *reinterpret_cast<const uint4*>(seg_ptr<T>(op, e, mn) + k);
+    for (int j = 0; j < 4; ++j) {
+      const int q = j * kTWaves + wave;
+      const int r = q * 8 + (lane >> 3);
+      const bool ok = kok && mn0 + r < mn_end;
+      dma16(rs, dst + q * 512, ok ? (uint32_t)(((int64_t)r * op.ld + c * 8) * (int64_t)sizeof(T)) : kOOR);
+    }
+  } else {
+    const T* base = static_cast<const T*>(op.p[seg]) + (int64_t)e * op.estride + kbase * op.ld + mn0;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base), (short)0, kRecords, kRsrcFlags);
+    const int c = (lane & 31) ^ (4 * ((2 * (wave & 1) + (lane >> 5)) & 3));
+    const bool mok = mn0 + c * 8 < mn_end;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int q = j * kTWaves + wave;
+      const int kr = q * 2 + (lane >> 5);
+      const bool ok = mok && kr < k_valid;
+      dma16(rs, dst + q * 512, ok ? (uint32_t)(((int64_t)kr * op.ld + c * 8) * (int64_t)sizeof(T)) : kOOR);
+    }
   }
 }
 
+// MFMA 32x32x16 operand fragment: lane l holds row (or column) R0 + l % 32 at
+// k = 16 s + 8 (l / 32) .. +7.
 template <typename T>
-__device__ __forceinline__ void store_kc(T* lds, const uint4 (&r)[2]) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = threadIdx.x + i * kTThreads;
-    *reinterpret_cast<uint4*>(lds + (c >> 2) * kLdsRow + (c & 3) * 8) = r[i];
-  }
+__device__ __forceinline__ Frag<T> frag_kc(const T* buf, int R0, int s, int lane) {
+  const int r = R0 + (lane & 31);
+  const int c = (2 * s + (lane >> 5)) ^ ((r >> 1) & 7);
+  return *reinterpret_cast<const Frag<T>*>(buf + r * kTK + c * 8);
 }
 
-// MN-contiguous operand: kTBK rows (k) x kTBM (mn). Thread t reads the k-pair
-// 2p, 2p+1 (p = t % 16) at mn chunk t / 16 (8 elements). Rows k >= k_end and
-// chunks at or past mn_end read as zeros (mn_end is a multiple of 8).
+// The same fragment from an MN-contiguous tile with two transposed 8-byte
+// LDS reads: in each group of 16 lanes, lane i receives element i % 4 of the
+// 8-byte pieces addressed by lanes 4m + i / 4 (m = 0..3). Lane j of group g
+// addresses k-row k0 + j / 4 at column C0 + 16 (g & 1) + 4 (j % 4), so lane i
+// ends up with column C0 + 16 (g & 1) + i at k0 .. k0 + 3, k0 = 16 s + 8 (g / 2)
+// (+ 4 for the second read).
 template <typename T>
-__device__ __forceinline__ void load_mn(const Operand& op, int e, int64_t mn0, int64_t mn_end,
-                                        int64_t k0, int64_t k_end, uint4 (&r)[2]) {
-  const int p = threadIdx.x & 15, c = threadIdx.x >> 4;
-  const int64_t mn = mn0 + c * 8;
+__device__ __forceinline__ Frag<T> frag_mn(const T* buf, int C0, int s, int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  const int mn = C0 + (g & 1) * 16 + 4 * (i & 3);
+  s16x4 v[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int64_t k = k0 + 2 * p + h;
-    r[h] = make_uint4(0, 0, 0, 0);
-    if (k < k_end && mn < mn_end) r[h] = *reinterpret_cast<const uint4*>(seg_ptr<T>(op, e, k) + mn);
+    const int k = s * 16 + (g >> 1) * 8 + h * 4 + (i >> 2);
+    const int off = k * kTM + (((mn >> 3) ^ (4 * (k & 3))) << 3) + (mn & 7);
+    v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(buf + off));
   }
-}
-
-// Transposes the two k-rows into the K-contiguous LDS layout: element
-// (mn, k) at mn * kLdsRow + k; one 32-bit write holds k = 2p and 2p + 1.
-template <typename T>
-__device__ __forceinline__ void store_mn(T* lds, const uint4 (&r)[2]) {
-  const int p = threadIdx.x & 15, c = threadIdx.x >> 4;
-  uint32_t* base = reinterpret_cast<uint32_t*>(lds + (c * 8) * kLdsRow + 2 * p);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) base[i * (kLdsRow / 2)] = elem16(r[0], i) | (elem16(r[1], i) << 16);
+  const s16x8 w = {v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]};
+  return __builtin_bit_cast(Frag<T>, w);
 }
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
 
+// Grouped GEMM C[m, n] = sum_k A(m, k) B(n, k) over 256 x 256 tiles, 8
+// wavefronts, K staged 64 at a time through two LDS stages: the loads of
+// k-step t+1 are issued before the MFMAs of k-step t and waited for at its end.
 template <typename T, bool kAK, bool kBK, int kEpi, bool kGroupK>
 __global__ __launch_bounds__(kTThreads) void train_gemm_kernel(TrainGemm p) {
-  __shared__ __attribute__((aligned(16))) T lds_a[2][kTBM * kLdsRow];
-  __shared__ __attribute__((aligned(16))) T lds_b[2][kTBN * kLdsRow];
-
-  // ---- which tile ----
   int e, m_idx, n_idx;
-  int64_t m0, m_end, k_start, k_end;
+  int64_t m0, m_end, kstart;
+  int64_t seg_len[2];
+  int nseg;
   if (kGroupK) {
     const int per_e = p.m_tiles * p.n_tiles;
     e = blockIdx.x / per_e;
     const int t = blockIdx.x % per_e;
     m_idx = t / p.n_tiles;
     n_idx = t % p.n_tiles;
-    m0 = (int64_t)m_idx * kTBM;
+    m0 = (int64_t)m_idx * kTM;
     m_end = p.M;
-    k_start = p.offsets[e];
-    k_end = p.offsets[e + 1];
+    kstart = p.offsets[e];
+    nseg = 1;
+    seg_len[0] = p.offsets[e + 1] - kstart;
+    seg_len[1] = 0;
   } else {
     const int per_group = kNGroup * p.m_tiles;
     const int g = blockIdx.x / per_group;
@@ -177,75 +216,81 @@ __global__ __launch_bounds__(kTThreads) void train_gemm_kernel(TrainGemm p) {
       if (p.tile_prefix[mid] <= m_idx) lo = mid; else hi = mid - 1;
     }
     e = lo;
-    m0 = p.offsets[e] + (int64_t)(m_idx - p.tile_prefix[e]) * kTBM;
+    m0 = p.offsets[e] + (int64_t)(m_idx - p.tile_prefix[e]) * kTM;
     m_end = p.offsets[e + 1];
-    k_start = 0;
-    k_end = p.K;
+    kstart = 0;
+    nseg = p.nseg;
+    seg_len[0] = p.seg_len[0];
+    seg_len[1] = p.seg_len[1];
   }
-  const int64_t n0 = (int64_t)n_idx * kTBN;
-  // Operands holding dispatched rows have no expert stride; weights do.
-  const int ea = e, eb = e;
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t n0 = (int64_t)n_idx * kTN;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
-  f32x16 acc[2][2];
+  const int64_t nk0 = (seg_len[0] + kTK - 1) / kTK;
+  const int64_t nk = nk0 + (nseg > 1 ? (seg_len[1] + kTK - 1) / kTK : 0);
+  const int64_t nk_pad = (nk + 1) & ~(int64_t)1;
+
+  auto issue = [&](int64_t t, T* la, T* lb) {
+    const int seg = t >= nk0 ? 1 : 0;
+    const int64_t k0 = (t - (seg ? nk0 : 0)) * kTK;
+    const int kval = t < nk ? (int)min((int64_t)kTK, seg_len[seg] - k0) : 0;
+    load_tile<T, kAK>(p.a, seg, e, m0, m_end, kstart + p.a.kofs[seg] + k0, kval, la, wave, lane);
+    load_tile<T, kBK>(p.b, seg, e, n0, p.N, kstart + p.b.kofs[seg] + k0, kval, lb, wave, lane);
+  };
+
+  f32x16 acc[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  const int64_t nk = (k_end - k_start + kTBK - 1) / kTBK;
-  uint4 ra[2], rb[2];
-  auto load = [&](int64_t kt) {
-    const int64_t k0 = k_start + kt * kTBK;
-    if (kAK) load_kc<T>(p.a, ea, m0, m_end, k0, k_end, ra);
-    else load_mn<T>(p.a, ea, m0, m_end, k0, k_end, ra);
-    if (kBK) load_kc<T>(p.b, eb, n0, p.N, k0, k_end, rb);
-    else load_mn<T>(p.b, eb, n0, p.N, k0, k_end, rb);
-  };
-  auto store = [&](int buf) {
-    if (kAK) store_kc<T>(lds_a[buf], ra); else store_mn<T>(lds_a[buf], ra);
-    if (kBK) store_kc<T>(lds_b[buf], rb); else store_mn<T>(lds_b[buf], rb);
-  };
-
-  if (nk > 0) {
-    load(0);
-    store(0);
-    __syncthreads();
-  }
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    const int buf = (int)(kt & 1);
-    if (kt + 1 < nk) load(kt + 1);
+  auto compute = [&](const T* la, const T* lb) {
 #pragma unroll
-    for (int ks = 0; ks < kTBK / 16; ++ks) {
-      Frag<T> fa[2], fb[2];
-      const int koff = ks * 16 + (lane >> 5) * 8;
+    for (int s = 0; s < kTK / 16; ++s) {
+      Frag<T> fa[2], fb[4];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        fa[i] = *reinterpret_cast<const Frag<T>*>(&lds_a[buf][(wm * 64 + i * 32 + (lane & 31)) * kLdsRow + koff]);
-        fb[i] = *reinterpret_cast<const Frag<T>*>(&lds_b[buf][(wn * 64 + i * 32 + (lane & 31)) * kLdsRow + koff]);
-      }
+      for (int i = 0; i < 2; ++i)
+        fa[i] = kAK ? frag_kc<T>(la, wm * 64 + i * 32, s, lane) : frag_mn<T>(la, wm * 64 + i * 32, s, lane);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        fb[j] = kBK ? frag_kc<T>(lb, wn * 128 + j * 32, s, lane) : frag_mn<T>(lb, wn * 128 + j * 32, s, lane);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = TMfma<T>::run(fa[i], fb[j], acc[i][j]);
+        for (int j = 0; j < 4; ++j) acc[i][j] = TMfma<T>::run(fa[i], fb[j], acc[i][j]);
     }
-    if (kt + 1 < nk) store(buf ^ 1);
-    __syncthreads();
+  };
+  auto sync = [&]() {
+    wait_vmem<0>();
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+
+  if (nk_pad > 0) {
+    issue(0, tbuf<T, 0, 0>(), tbuf<T, 1, 0>());
+    sync();
+  }
+  for (int64_t t = 0; t < nk_pad; t += 2) {
+    issue(t + 1, tbuf<T, 0, 1>(), tbuf<T, 1, 1>());
+    compute(tbuf<T, 0, 0>(), tbuf<T, 1, 0>());
+    sync();
+    if (t + 2 < nk_pad) issue(t + 2, tbuf<T, 0, 0>(), tbuf<T, 1, 0>());
+    compute(tbuf<T, 0, 1>(), tbuf<T, 1, 1>());
+    sync();
   }
 
   // ---- epilogue: D row (v/4)*8 + (lane/32)*4 + v%4, column lane%32 ----
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int64_t m = m0 + wm * 64 + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-        const int64_t n = n0 + wn * 64 + j * 32 + (lane & 31);
+        const int64_t n = n0 + wn * 128 + j * 32 + (lane & 31);
         if (m >= m_end || n >= p.N) continue;
         const float x = acc[i][j][v];
         if (kEpi == kEpiSwiGluBwd) {
@@ -253,10 +298,10 @@ __global__ __launch_bounds__(kTThreads) void train_gemm_kernel(TrainGemm p) {
           const int64_t at = m * 2 * (int64_t)p.N + n;
           const float g = to_f32(static_cast<const T*>(p.gu)[at]);
           const float u = to_f32(static_cast<const T*>(p.gu)[at + p.N]);
-          const float s = sigmoidf_(g);
+          const float sg = sigmoidf_(g);
           T* o = static_cast<T*>(p.out0);
-          o[at] = from_f32<T>(x * u * s * (1.0f + g * (1.0f - s)));
-          o[at + p.N] = from_f32<T>(x * g * s);
+          o[at] = from_f32<T>(x * u * sg * (1.0f + g * (1.0f - sg)));
+          o[at + p.N] = from_f32<T>(x * g * sg);
         } else {
           const bool hi = m >= p.out_split;
           const int64_t row = hi ? m - p.out_split : m;
@@ -490,7 +535,7 @@ __global__ __launch_bounds__(256) void router_backward_kernel(
 // ---- launch helpers ------------------------------------------------------------
 
 int64_t mtile_bound(int64_t rows, int64_t E) {
-  return (rows + kTBM - 1) / kTBM + std::min<int64_t>(E, rows);
+  return (rows + kTM - 1) / kTM + std::min<int64_t>(E, rows);
 }
 
 template <typename T, bool kAK, bool kBK, int kEpi, bool kGroupK>
@@ -501,25 +546,32 @@ void launch_tg(const TrainGemm& p, hipStream_t s) {
                      dim3(kTThreads), 0, s, p);
 }
 
-Operand opnd(const void* p0, const void* p1, int64_t split, int64_t ld, int64_t estride) {
-  return Operand{p0, p1 ? p1 : p0, p1 ? split : INT64_MAX, ld, estride};
+// Operand with one K-segment, or two (p1 and its K offset for segment 1).
+TOp opnd(const void* p0, int64_t ld, int64_t estride, const void* p1 = nullptr, int64_t kofs0 = 0,
+         int64_t kofs1 = 0) {
+  return TOp{{p0, p1 ? p1 : p0}, ld, estride, {kofs0, kofs1}};
 }
 
 template <typename T>
 hipError_t experts_forward_training_t(const TrainExperts& q, hipStream_t s) {
   const int64_t R = q.rows, H = q.H, I = q.I;
   int32_t* prefix = static_cast<int32_t*>(q.ws);
-  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, s, q.offsets, q.E, kTBM, prefix);
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, s, q.offsets, q.E, kTM, prefix);
   T* gu = static_cast<T*>(q.cache);
   T* h = gu + R * 2 * I;
   TrainGemm p = {};
   p.offsets = q.offsets; p.tile_prefix = prefix; p.E = q.E;
-  // [g | u] = X [W_gate; W_up]^T : N = 2I, K = H
-  p.a = opnd(q.x, nullptr, 0, H, 0);
-  p.b = opnd(q.w_gate, q.w_up, I, H, I * H);
-  p.N = (int)(2 * I); p.K = (int)H;
-  p.m_tiles = (int)mtile_bound(R, q.E); p.n_tiles = (int)((2 * I + kTBN - 1) / kTBN);
-  p.out0 = gu; p.out1 = gu; p.out_split = INT64_MAX; p.ldc = 2 * I;
+  p.m_tiles = (int)mtile_bound(R, q.E);
+  p.nseg = 1; p.seg_len[0] = H;
+  p.N = (int)I; p.n_tiles = (int)((I + kTN - 1) / kTN);
+  p.out_split = INT64_MAX; p.ldc = 2 * I;
+  p.a = opnd(q.x, H, 0);
+  // g = X W_gate^T into columns [0, I) of the cache, u = X W_up^T into [I, 2I)
+  p.b = opnd(q.w_gate, H, I * H);
+  p.out0 = p.out1 = gu;
+  launch_tg<T, true, true, kEpiStore, false>(p, s);
+  p.b = opnd(q.w_up, H, I * H);
+  p.out0 = p.out1 = gu + I;
   launch_tg<T, true, true, kEpiStore, false>(p, s);
   const int64_t n8 = R * (I / 8);
   hipLaunchKernelGGL(swiglu_cache_kernel<T>, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, gu, h, R, (int)I);
@@ -533,36 +585,38 @@ hipError_t experts_backward_t(const TrainExperts& q, hipStream_t s) {
   T* dgu = reinterpret_cast<T*>(static_cast<char*>(q.ws) + train_prefix_bytes(q.E));
   const T* gu = static_cast<const T*>(q.cache);
   const T* h = gu + R * 2 * I;
-  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, s, q.offsets, q.E, kTBM, prefix);
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, s, q.offsets, q.E, kTM, prefix);
   TrainGemm p = {};
   p.offsets = q.offsets; p.tile_prefix = prefix; p.E = q.E;
   p.m_tiles = (int)mtile_bound(R, q.E);
   // dh = dY W_down (W_down [H, I] read along I), fused SwiGLU backward -> dg | du
-  p.a = opnd(q.dy, nullptr, 0, H, 0);
-  p.b = opnd(q.w_down, nullptr, 0, I, H * I);
-  p.N = (int)I; p.K = (int)H; p.n_tiles = (int)((I + kTBN - 1) / kTBN);
+  p.a = opnd(q.dy, H, 0);
+  p.b = opnd(q.w_down, I, H * I);
+  p.nseg = 1; p.seg_len[0] = H;
+  p.N = (int)I; p.n_tiles = (int)((I + kTN - 1) / kTN);
   p.out0 = dgu; p.gu = gu;
   launch_tg<T, true, false, kEpiSwiGluBwd, false>(p, s);
-  // dinput = [dg | du] [W_gate; W_up]  (weights [I, H] read along H), K = 2I
-  p.a = opnd(dgu, nullptr, 0, 2 * I, 0);
-  p.b = opnd(q.w_gate, q.w_up, I, H, I * H);
-  p.N = (int)H; p.K = (int)(2 * I); p.n_tiles = (int)((H + kTBN - 1) / kTBN);
-  p.out0 = q.dx; p.out1 = q.dx; p.out_split = INT64_MAX; p.ldc = H; p.gu = nullptr;
+  // dinput = dg W_gate + du W_up: two K-segments of I (weights [I, H] read along H)
+  p.a = opnd(dgu, 2 * I, 0, dgu, 0, I);
+  p.b = opnd(q.w_gate, H, I * H, q.w_up, 0, 0);
+  p.nseg = 2; p.seg_len[0] = I; p.seg_len[1] = I;
+  p.N = (int)H; p.n_tiles = (int)((H + kTN - 1) / kTN);
+  p.out0 = p.out1 = q.dx; p.out_split = INT64_MAX; p.ldc = H; p.gu = nullptr;
   launch_tg<T, true, false, kEpiStore, false>(p, s);
   // ddown[e] = dY_e^T h_e  [H, I], K = rows of e
   TrainGemm w = {};
-  w.offsets = q.offsets; w.E = q.E;
-  w.a = opnd(q.dy, nullptr, 0, H, 0);
-  w.b = opnd(h, nullptr, 0, I, 0);
+  w.offsets = q.offsets; w.E = q.E; w.nseg = 1;
+  w.a = opnd(q.dy, H, 0);
+  w.b = opnd(h, I, 0);
   w.M = (int)H; w.N = (int)I;
-  w.m_tiles = (int)((H + kTBM - 1) / kTBM); w.n_tiles = (int)((I + kTBN - 1) / kTBN);
-  w.out0 = q.d_down; w.out1 = q.d_down; w.out_split = INT64_MAX; w.ldc = I; w.out_estride = H * I;
+  w.m_tiles = (int)((H + kTM - 1) / kTM); w.n_tiles = (int)((I + kTN - 1) / kTN);
+  w.out0 = w.out1 = q.d_down; w.out_split = INT64_MAX; w.ldc = I; w.out_estride = H * I;
   launch_tg<T, false, false, kEpiStoreF32, true>(w, s);
   // dgate[e] | dup[e] = [dg | du]_e^T X_e  [2I, H], K = rows of e
-  w.a = opnd(dgu, nullptr, 0, 2 * I, 0);
-  w.b = opnd(q.x, nullptr, 0, H, 0);
+  w.a = opnd(dgu, 2 * I, 0);
+  w.b = opnd(q.x, H, 0);
   w.M = (int)(2 * I); w.N = (int)H;
-  w.m_tiles = (int)((2 * I + kTBM - 1) / kTBM); w.n_tiles = (int)((H + kTBN - 1) / kTBN);
+  w.m_tiles = (int)((2 * I + kTM - 1) / kTM); w.n_tiles = (int)((H + kTN - 1) / kTN);
   w.out0 = q.d_gate; w.out1 = q.d_up; w.out_split = I; w.ldc = H; w.out_estride = I * H;
   launch_tg<T, false, false, kEpiStoreF32, true>(w, s);
   return hipGetLastError();
