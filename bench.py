@@ -81,6 +81,10 @@ def main():
     ap.add_argument("--train", action="store_true",
                     help="time one first-order training step (forward with the experts' cache, "
                          "then combine, expert, dispatch and router backward) instead of the forward")
+    ap.add_argument("--quant", type=int, default=0, choices=(0, 4, 8),
+                    help="time the forward with weight-only INT8 or INT4 experts (decode-sized workloads)")
+    ap.add_argument("--groups", type=int, default=0,
+                    help="scale groups along K for --quant (default 1 for INT8, 4 for INT4)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 5 times (the "
                          "reference kernel for scaling HBM byte counters), then exit")
@@ -124,6 +128,8 @@ def main():
     t0 = time.time()
     z = I.logits_for(w)
     x = I.tokens_for(w)
+    if args.quant:
+        return run_quant(args, w, x, z, to_dev)
     n_cpu = min(args.cpu_tokens or CPU_TOKENS[args.workload], T)
     keep = set()
     if not args.no_cpu_baseline:
@@ -291,6 +297,97 @@ def main():
         "roofline": roofline, "cpu_baseline": cpu,
     }
     res.update(extra)
+    print(json.dumps(res), flush=True)
+
+
+def run_quant(args, w, x, z, to_dev):
+    """The forward with weight-only quantised experts (moe_forward_quant) on
+    the current stream; stage events as moe_forward. Roofline: the gate/up
+    stage's weight-streaming bytes (codes + scales of the touched experts,
+    tokens, h) against HBM."""
+    import torch
+    from mixture_experts_ffn_top_amd import inputs as I
+    from mixture_experts_ffn_top_amd import moe
+
+    T, H, I_, E, k = w.T, w.H, w.I, w.E, w.top_k
+    R = T * k
+    bits = args.quant
+    groups = args.groups or (1 if bits == 8 else 4)
+    if R > 4 * E or w.dtype != "bf16":
+        raise SystemExit("the quantised path serves decode-sized bf16 batches (T * top_k <= 4 E)")
+    t0 = time.time()
+    q, sc = {}, {}
+    for name in ("w_gate", "w_up", "w_down"):
+        qh, sh = I.quant_expert_weights(w, name, bits, groups)
+        q[name], sc[name] = torch.from_numpy(qh).cuda(), to_dev(sh)
+        if not args.no_cpu_baseline:
+            q[name + "_host"], sc[name + "_host"] = qh, sh
+    xd, zd = to_dev(x), to_dev(z, "f32")
+    torch.cuda.synchronize()
+    log(f"quantised inputs ready in {time.time() - t0:.1f}s: INT{bits}, {groups} group(s)")
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(moe.moe_forward_workspace_size(T, H, I_, E, k, torch.bfloat16, torch.float32),
+                     dtype=torch.uint8, device="cuda")
+    scales = (sc["w_gate"], sc["w_up"], sc["w_down"])
+
+    def step(ev=None):
+        moe.moe_forward_quant(xd, zd, k, w.renormalize, q["w_gate"], q["w_up"], q["w_down"], bits, scales,
+                              groups=groups, out=out, indices_out=idx, weights_out=wts, ws=ws, stage_events=ev)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    for ev in evs:
+        for e_ in ev:
+            e_.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for s_ in range(args.steps):
+        step(evs[s_])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t1
+    stages = ["route", "dispatch", "gate_up", "down", "combine"]
+    stage_ms = {n: float(np.mean([evs[s_][i].elapsed_time(evs[s_][i + 1]) for s_ in range(args.steps)]))
+                for i, n in enumerate(stages)}
+    touched = len(np.unique(idx.cpu().numpy()))
+    wbytes_gu = touched * 2 * I_ * H * bits // 8 + touched * 2 * I_ * groups * 2
+    wbytes_dn = touched * H * I_ * bits // 8 + touched * H * groups * 2
+    bytes_gu = wbytes_gu + T * H * 2 + R * I_ * 2
+    gbs = bytes_gu / (stage_ms["gate_up"] / 1e3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                "kernel": f"skinny_quant_kernel<bf16,gate_up,{bits}>", "algorithmic_per_launch": bytes_gu}
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import moe_oracle as O
+        n = min(args.cpu_tokens or 4, T)
+        cores = len(os.sched_getaffinity(0))
+        idx_s, w_s = O.route(z[:n], "f32", k, w.renormalize)
+        d = O.dispatch(idx_s, E, x[:n])
+        quant_of = lambda e: tuple((q[nm + "_host"][e], sc[nm + "_host"][e], None)  # noqa: E731
+                                   for nm in ("w_gate", "w_up", "w_down"))
+        c0 = time.perf_counter()
+        y = O.experts_forward_quant(d["x_disp"], d["offsets"], quant_of, bits, groups, w.dtype)
+        O.combine(y, d["row_of_slot"], w_s, "f32", n, k, w.dtype)
+        c_el = time.perf_counter() - c0
+        cpu = {"value": round(n / c_el, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+               "sample": f"first {n} of {T} tokens of {args.workload} with INT{bits} experts; dequantised "
+                         f"fp64 SwiGLU experts and combine; {c_el:.1f}s wall"}
+    res = {
+        "metric": f"MoE fwd tokens/s with weight-only INT{bits} experts", "value": round(T * args.steps / elapsed, 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{args.workload}+int{bits}", "T": T, "H": H, "I": I_, "E": E, "top_k": k,
+                   "bits": bits, "groups": groups},
+        "roofline": roofline, "cpu_baseline": cpu,
+        "stages_ms": {k_: round(v, 4) for k_, v in stage_ms.items()},
+        "weight_stream_gbs": round((wbytes_gu + wbytes_dn) / ((stage_ms["gate_up"] + stage_ms["down"]) / 1e3) / 1e9, 1),
+        "experts_touched": touched,
+    }
     print(json.dumps(res), flush=True)
 
 

@@ -15,10 +15,14 @@
 // Same structure as the bf16 weight-streaming kernel: one workgroup of 4
 // wavefronts per (expert, block of 64 weight rows), K split four ways and
 // reduced in LDS, MFMA 16x16x32 with A = 16 weight rows and B = 16 token
-// rows. A lane's 8 weights per MFMA step are 8 (INT8) or 4 (INT4) bytes;
-// they are dequantised in registers as q * s + (o * s) in fp32 and packed to
-// the model dtype before the MFMA. The next K-iteration's weight, scale and
-// activation loads are issued before the current iteration's MFMAs.
+// rows. Every weight load is 16 bytes per lane, four lanes side by side on a
+// row (64 contiguous bytes per row and instruction): 16 INT8 or 32 INT4
+// codes, i.e. 2 or 4 MFMA k-slices of 8. The k order inside a lane's span
+// differs from the MFMA's native one, and the activations are loaded in the
+// same order, so the contraction is unchanged. The codes are dequantised in
+// registers as q * s + (o * s) in fp32 and rounded to the model dtype before
+// the MFMA. The next K-iteration's weight, scale and activation loads are
+// issued before the current iteration's MFMAs.
 #include "common.h"
 #include "kernels.h"
 
@@ -50,30 +54,21 @@ template <> struct MfmaQ<f16> {
 
 __device__ __forceinline__ float silu_q(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
-// 8 quantised weights of one lane (one MFMA operand fragment).
-template <int kBits> struct QWords;
-template <> struct QWords<8> { u32x2 v; };
-template <> struct QWords<4> { uint32_t v; };
+// K-iteration geometry: one 16-byte load per lane covers kSpan / 4 values of
+// a row (kSpan across the 4 lanes of the row); an iteration of kQKIter = 128
+// input channels takes kLoads such loads per tile and kMf MFMAs per load.
+template <int kBits> struct QGeo {
+  static constexpr int kSpan = kBits == 8 ? 64 : 128;
+  static constexpr int kLoads = 128 / kSpan;
+  static constexpr int kMf = kSpan / 32;
+};
 
+// Signed code j (0 .. 15 for INT8, 0 .. 31 for INT4) of a lane's 16 bytes.
 template <int kBits>
-__device__ __forceinline__ QWords<kBits> load_q(__amdgpu_buffer_rsrc_t r, uint32_t vo, uint32_t soff) {
-  QWords<kBits> q;
-  if constexpr (kBits == 8)
-    q.v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, vo, soff, 0));
-  else
-    q.v = __builtin_amdgcn_raw_buffer_load_b32(r, vo, soff, 0);
-  return q;
-}
-
-// Signed value i (0..7) of a fragment.
-template <int kBits>
-__device__ __forceinline__ float q_at(const QWords<kBits>& q, int i) {
-  if constexpr (kBits == 8) {
-    const uint32_t w = i < 4 ? q.v.x : q.v.y;
-    return (float)(int)(int8_t)(w >> (8 * (i & 3)));
-  } else {
-    return (float)((int)(q.v << (28 - 4 * i)) >> 28);
-  }
+__device__ __forceinline__ float q_val(const uint4& q, int j) {
+  const uint32_t w = (j * kBits) < 64 ? ((j * kBits) < 32 ? q.x : q.y) : ((j * kBits) < 96 ? q.z : q.w);
+  if constexpr (kBits == 8) return (float)(int)(int8_t)(w >> (8 * (j & 3)));
+  else return (float)((int)(w << (28 - 4 * (j & 7))) >> 28);
 }
 
 struct QuantArgs {
@@ -122,6 +117,7 @@ __global__ __launch_bounds__(64 * kQWaves) void skinny_quant_kernel(QuantArgs p)
       const_cast<void*>(p.a), (short)0, (int)((uint32_t)p.a_rows * xrow), kRsrcFlagsQ);
 
   // Weight rows of the 4 tiles; rows past N read as zero and get scale 0.
+  typedef QGeo<kBits> Geo;
   const int g = lane >> 4;
   uint32_t vo_w[4];
   int wrow[4];
@@ -129,7 +125,7 @@ __global__ __launch_bounds__(64 * kQWaves) void skinny_quant_kernel(QuantArgs p)
   for (int t = 0; t < 4; ++t) {
     const int n = kSwiGlu ? nb * 32 + (t & 1) * 16 + (lane & 15) : nb * kQRows + t * 16 + (lane & 15);
     wrow[t] = n;
-    vo_w[t] = (uint32_t)n * qrow + (uint32_t)g * kBits;  // 8 values = kBits bytes
+    vo_w[t] = (uint32_t)n * qrow + (uint32_t)g * 16u;  // this lane's 16 bytes of each span
   }
   const T* sp0 = static_cast<const T*>(p.s0) + expert_rows * G;
   const T* sp1 = kSwiGlu ? static_cast<const T*>(p.s1) + expert_rows * G : sp0;
@@ -142,7 +138,7 @@ __global__ __launch_bounds__(64 * kQWaves) void skinny_quant_kernel(QuantArgs p)
     uint32_t vo_x = kOutOfRangeQ;
     if (xr < r_end) {
       const int src = p.a_map ? min(max(p.a_map[xr] / p.a_div, 0), p.a_rows - 1) : xr;
-      vo_x = (uint32_t)src * xrow + (uint32_t)g * 16u;
+      vo_x = (uint32_t)src * xrow + (uint32_t)(g * (Geo::kSpan / 4)) * (uint32_t)sizeof(T);
     }
     f32x4 acc[4];
 #pragma unroll
@@ -166,35 +162,49 @@ __global__ __launch_bounds__(64 * kQWaves) void skinny_quant_kernel(QuantArgs p)
         os[t] = o * s;
       }
     };
-    QWords<kBits> wa[4][4], wb[4][4];
-    uint4 xa[4], xb[4];
+    // Per iteration at input channel kb: load w of tile t holds channels
+    // kb + w*kSpan + g*kSpan/4 .. +kSpan/4-1 of the tile's row; MFMA m of that
+    // load takes its codes 8m .. 8m+7, and activation chunk [w][m] holds the
+    // same 8 channels. Codes past K or past this wavefront's K range meet
+    // activations masked to zero (8-channel granularity).
+    uint4 wa[4][Geo::kLoads], wb[4][Geo::kLoads];
+    uint4 xa[Geo::kLoads][Geo::kMf], xb[Geo::kLoads][Geo::kMf];
     float sa_[4], oa[4], sb_[4], ob[4];
-    auto load = [&](int kb, QWords<kBits> (&w)[4][4], uint4 (&x)[4], float (&sc)[4], float (&os)[4]) {
+    auto load = [&](int kb, uint4 (&w)[4][Geo::kLoads], uint4 (&x)[Geo::kLoads][Geo::kMf], float (&sc)[4],
+                    float (&os)[4]) {
       const uint32_t soff_q = (uint32_t)kb * kBits / 8;
       const uint32_t soff_x = (uint32_t)kb * sizeof(T);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const bool ok = kb + c * 32 + g * 8 < k_hi;
+      for (int l = 0; l < Geo::kLoads; ++l) {
+        const int k0 = kb + l * Geo::kSpan + g * (Geo::kSpan / 4);
+        const bool okw = k0 < k_hi;
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-          w[t][c] = load_q<kBits>((kSwiGlu && t >= 2) ? rw1 : rw0,
-                                  ok ? vo_w[t] + (uint32_t)c * 4u * kBits : kOutOfRangeQ, soff_q);
-        x[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-            rx, ok ? vo_x + c * 64u : kOutOfRangeQ, soff_x, 0));
+          w[t][l] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+              (kSwiGlu && t >= 2) ? rw1 : rw0,
+              okw ? vo_w[t] + (uint32_t)(l * Geo::kSpan * kBits / 8) : kOutOfRangeQ, soff_q, 0));
+#pragma unroll
+        for (int m = 0; m < Geo::kMf; ++m) {
+          const bool okx = k0 + m * 8 < k_hi;
+          x[l][m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+              rx, okx ? vo_x + (uint32_t)((l * Geo::kSpan + m * 8) * (int)sizeof(T)) : kOutOfRangeQ, soff_x, 0));
+        }
       }
       load_sc(kb, sc, os);
     };
-    auto compute = [&](const QWords<kBits> (&w)[4][4], const uint4 (&x)[4], const float (&sc)[4],
-                       const float (&os)[4]) {
+    auto compute = [&](const uint4 (&w)[4][Geo::kLoads], const uint4 (&x)[Geo::kLoads][Geo::kMf],
+                       const float (&sc)[4], const float (&os)[4]) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
+      for (int l = 0; l < Geo::kLoads; ++l)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          Frag f;
+        for (int m = 0; m < Geo::kMf; ++m)
 #pragma unroll
-          for (int i = 0; i < 8; ++i) f[i] = from_f32<T>(fmaf(q_at<kBits>(w[t][c], i), sc[t], os[t]));
-          acc[t] = MfmaQ<T>::run(f, __builtin_bit_cast(Frag, x[c]), acc[t]);
-        }
+          for (int t = 0; t < 4; ++t) {
+            Frag f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) f[i] = from_f32<T>(fmaf(q_val<kBits>(w[t][l], m * 8 + i), sc[t], os[t]));
+            acc[t] = MfmaQ<T>::run(f, __builtin_bit_cast(Frag, x[l][m]), acc[t]);
+          }
     };
     const int n_iter = (k_hi - k_lo + kQKIter - 1) / kQKIter;
     if (n_iter > 0) {

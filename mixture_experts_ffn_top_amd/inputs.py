@@ -191,6 +191,21 @@ def expert_weights(w: Workload, which: str, experts=None, threads: int | None = 
     return out
 
 
+def quant_expert_weights(w: Workload, which: str, bits: int, groups: int):
+    """Synthetic weight-only quantised weights of all experts for one
+    projection: integer codes [E, N, K] (bits 8: one int8 per byte; bits 4:
+    two codes per byte along K, uniform over all byte values) and positive
+    scales [E, N, groups] in the model dtype, |N(0, 1)| / (spread * sqrt(K)) +
+    1e-5 with spread 73 (int8) or 4.6 (int4), so that dequantised products
+    keep activations O(1). No offsets."""
+    N, K = (w.I, w.H) if which in ("w_gate", "w_up") else (w.H, w.I)
+    g = stream(w.seed, "quant_" + which, bits, groups)
+    q = g.integers(0, 256, size=(w.E, N, K * bits // 8), dtype=np.uint8)
+    spread = 73.0 if bits == 8 else 4.6
+    sc = np.abs(g.standard_normal((w.E, N, groups), dtype=np.float32)) / np.float32(spread * np.sqrt(K))
+    return q, store(sc + np.float32(1e-5), w.dtype)
+
+
 def grad_output_for(w: Workload) -> np.ndarray:
     """Gradient of the MoE output for a training step: [T, H] ~ N(0, 1) in the model dtype."""
     return store(normal(w.seed, "grad_out", (w.T, w.H)), w.dtype)
