@@ -355,11 +355,17 @@ def run_quant(args, w, x, z, to_dev):
     touched = len(np.unique(idx.cpu().numpy()))
     wbytes_gu = touched * 2 * I_ * H * bits // 8 + touched * 2 * I_ * groups * 2
     wbytes_dn = touched * H * I_ * bits // 8 + touched * H * groups * 2
-    bytes_gu = wbytes_gu + T * H * 2 + R * I_ * 2
-    gbs = bytes_gu / (stage_ms["gate_up"] / 1e3) / 1e9
+    # moe_forward_quant runs both expert GEMMs between the gate_up and down
+    # events: the roofline covers the two launches of skinny_quant_kernel
+    # (codes + scales of the touched experts, tokens in, h out and back in,
+    # expert rows out) over that stage
+    bytes_experts = wbytes_gu + wbytes_dn + T * H * 2 + 2 * R * I_ * 2 + R * H * 2
+    exp_s = (stage_ms["gate_up"] + stage_ms["down"]) / 1e3
+    gbs = bytes_experts / exp_s / 1e9
     roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
-                "kernel": f"skinny_quant_kernel<bf16,gate_up,{bits}>", "algorithmic_per_launch": bytes_gu}
+                "kernel": f"skinny_quant_kernel<bf16,gate_up|down,INT{bits}> (both launches)",
+                "algorithmic_per_launch": bytes_experts}
     cpu = None
     if not args.no_cpu_baseline:
         from oracle import moe_oracle as O
@@ -385,7 +391,7 @@ def run_quant(args, w, x, z, to_dev):
                    "bits": bits, "groups": groups},
         "roofline": roofline, "cpu_baseline": cpu,
         "stages_ms": {k_: round(v, 4) for k_, v in stage_ms.items()},
-        "weight_stream_gbs": round((wbytes_gu + wbytes_dn) / ((stage_ms["gate_up"] + stage_ms["down"]) / 1e3) / 1e9, 1),
+        "weight_stream_gbs": round((wbytes_gu + wbytes_dn) / exp_s / 1e9, 1),
         "experts_touched": touched,
     }
     print(json.dumps(res), flush=True)
