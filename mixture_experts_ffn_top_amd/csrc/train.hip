@@ -181,6 +181,18 @@ __device__ __forceinline__ Frag<T> frag_mn(const T* buf, int C0, int s, int lane
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
 
+// Scheduling order for one k16 sub-step: each of its 8 MFMAs followed by
+// its share of the next sub-step's kReads LDS reads.
+template <int kReads, int X>
+__device__ __forceinline__ void interleave() {
+  if constexpr (X < 8) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    constexpr int n = (kReads + 7 - X) / 8;
+    if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x100, n, 0);
+    interleave<kReads, X + 1>();
+  }
+}
+
 // Grouped GEMM C[m, n] = sum_k A(m, k) B(n, k) over 256 x 256 tiles, 8
 // wavefronts, K staged 64 at a time through two LDS stages: the loads of
 // k-step t+1 are issued before the MFMAs of k-step t and waited for at its end.
@@ -248,38 +260,53 @@ __global__ __launch_bounds__(kTThreads) void train_gemm_kernel(TrainGemm p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  auto compute = [&](const T* la, const T* lb) {
+  // Fragments are double-buffered across the four k16 sub-steps: the reads
+  // of sub-step s+1 are interleaved with the MFMAs of sub-step s. The last
+  // sub-step's MFMAs are split around the stage barrier: half before it, and
+  // half after, overlapping the first fragment reads of the next stage, so a
+  // wavefront that reaches the barrier early still has MFMAs queued.
+  Frag<T> fa[2][2], fb[2][4];
+  auto read = [&](const T* la, const T* lb, int s, int slot) {
 #pragma unroll
-    for (int s = 0; s < kTK / 16; ++s) {
-      Frag<T> fa[2], fb[4];
+    for (int i = 0; i < 2; ++i)
+      fa[slot][i] = kAK ? frag_kc<T>(la, wm * 64 + i * 32, s, lane) : frag_mn<T>(la, wm * 64 + i * 32, s, lane);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        fa[i] = kAK ? frag_kc<T>(la, wm * 64 + i * 32, s, lane) : frag_mn<T>(la, wm * 64 + i * 32, s, lane);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        fb[j] = kBK ? frag_kc<T>(lb, wn * 128 + j * 32, s, lane) : frag_mn<T>(lb, wn * 128 + j * 32, s, lane);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = TMfma<T>::run(fa[i], fb[j], acc[i][j]);
-    }
+    for (int j = 0; j < 4; ++j)
+      fb[slot][j] = kBK ? frag_kc<T>(lb, wn * 128 + j * 32, s, lane) : frag_mn<T>(lb, wn * 128 + j * 32, s, lane);
   };
-  auto sync = [&]() {
+  auto mfmas = [&](int slot, int from, int to) {
+#pragma unroll
+    for (int x = from; x < to; ++x) acc[x >> 2][x & 3] = TMfma<T>::run(fa[slot][x >> 2], fb[slot][x & 3], acc[x >> 2][x & 3]);
+  };
+  constexpr int kReads = (kAK ? 2 : 4) + (kBK ? 4 : 8);  // LDS read instructions per sub-step
+  // One k-step from stage (la, lb); (na, nb) is the stage the next k-step reads.
+  auto step = [&](const T* la, const T* lb, const T* na, const T* nb, bool more) {
+#pragma unroll
+    for (int s = 0; s + 1 < kTK / 16; ++s) {
+      read(la, lb, s + 1, (s + 1) & 1);
+      mfmas(s & 1, 0, 8);
+      interleave<kReads, 0>();
+    }
+    mfmas(1, 0, 4);
+    __builtin_amdgcn_sched_barrier(0);
     wait_vmem<0>();
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) read(na, nb, 0, 0);
+    mfmas(1, 4, 8);
   };
 
   if (nk_pad > 0) {
     issue(0, tbuf<T, 0, 0>(), tbuf<T, 1, 0>());
-    sync();
+    wait_vmem<0>();
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    read(tbuf<T, 0, 0>(), tbuf<T, 1, 0>(), 0, 0);
   }
   for (int64_t t = 0; t < nk_pad; t += 2) {
     issue(t + 1, tbuf<T, 0, 1>(), tbuf<T, 1, 1>());
-    compute(tbuf<T, 0, 0>(), tbuf<T, 1, 0>());
-    sync();
+    step(tbuf<T, 0, 0>(), tbuf<T, 1, 0>(), tbuf<T, 0, 1>(), tbuf<T, 1, 1>(), true);
     if (t + 2 < nk_pad) issue(t + 2, tbuf<T, 0, 0>(), tbuf<T, 1, 0>());
-    compute(tbuf<T, 0, 1>(), tbuf<T, 1, 1>());
-    sync();
+    step(tbuf<T, 0, 1>(), tbuf<T, 1, 1>(), tbuf<T, 0, 0>(), tbuf<T, 1, 0>(), t + 2 < nk_pad);
   }
 
   // ---- epilogue: D row (v/4)*8 + (lane/32)*4 + v%4, column lane%32 ----
