@@ -9,7 +9,7 @@
 //   low nibble first, two's complement (-8..7);
 //   scale, offset [E, N, G] in the model dtype, G groups of K/G consecutive
 //   input channels (G = 1: per channel; K/G a multiple of 128, so a
-//   128-channel K-iteration never straddles two groups); offset may be
+//   K-iteration (64 or 128 channels) never straddles two groups); offset may be
 //   absent (0).
 //
 // Same structure as the bf16 weight-streaming kernel: one workgroup of 4
@@ -21,8 +21,11 @@
 // differs from the MFMA's native one, and the activations are loaded in the
 // same order, so the contraction is unchanged. The codes are dequantised in
 // registers as q * s + (o * s) in fp32 and rounded to the model dtype before
-// the MFMA. The next K-iteration's weight, scale and activation loads are
+// the MFMA (INT4 as (q + 8) * s + (o - 8) * s, the same value for integer
+// offsets). The next K-iteration's weight, scale and activation loads are
 // issued before the current iteration's MFMAs.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -33,7 +36,6 @@ constexpr int kRsrcFlagsQ = 0x00020000;
 constexpr uint32_t kOutOfRangeQ = 0x80000000u;
 constexpr int kQRows = 64;     // weight rows per workgroup (4 MFMA tiles of 16)
 constexpr int kQTokens = 16;
-constexpr int kQKIter = 128;
 constexpr int kQWaves = 4;
 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -54,21 +56,67 @@ template <> struct MfmaQ<f16> {
 
 __device__ __forceinline__ float silu_q(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
-// K-iteration geometry: one 16-byte load per lane covers kSpan / 4 values of
-// a row (kSpan across the 4 lanes of the row); an iteration of kQKIter = 128
-// input channels takes kLoads such loads per tile and kMf MFMAs per load.
+// K-iteration geometry: one 16-byte load per lane and tile covers kSpan / 4
+// codes of a row (kSpan across the 4 lanes of the row), i.e. kMf MFMA
+// k-slices of 8; one K-iteration is one such load per tile (kIter = kSpan
+// input channels: 64 for INT8, 128 for INT4; scale groups are multiples of
+// 128 channels, so an iteration never straddles two groups).
 template <int kBits> struct QGeo {
   static constexpr int kSpan = kBits == 8 ? 64 : 128;
-  static constexpr int kLoads = 128 / kSpan;
+  static constexpr int kIter = kSpan;
+  static constexpr int kLoads = 1;
   static constexpr int kMf = kSpan / 32;
 };
 
-// Signed code j (0 .. 15 for INT8, 0 .. 31 for INT4) of a lane's 16 bytes.
-template <int kBits>
-__device__ __forceinline__ float q_val(const uint4& q, int j) {
-  const uint32_t w = (j * kBits) < 64 ? ((j * kBits) < 32 ? q.x : q.y) : ((j * kBits) < 96 ? q.z : q.w);
-  if constexpr (kBits == 8) return (float)(int)(int8_t)(w >> (8 * (j & 3)));
-  else return (float)((int)(w << (28 - 4 * (j & 7))) >> 28);
+typedef float f32x2q __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2q __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2q __attribute__((ext_vector_type(2)));
+
+// Two fp32 values rounded to nearest even into one dword of T (a first).
+template <typename T>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  if constexpr (std::is_same<T, bf16>::value)
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2q{a, b}, bf16x2q));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2q{a, b}, f16x2q));
+}
+
+__device__ __forceinline__ uint32_t word_of(const uint4& q, int i) {
+  return i < 2 ? (i == 0 ? q.x : q.y) : (i == 2 ? q.z : q.w);
+}
+
+// The 8 dequantised weights of MFMA slice m of a lane's 16 bytes, as an MFMA
+// operand: w = fma(c, s, os) in fp32, rounded to T.
+//  INT8: codes 8m .. 8m+7 are the signed bytes of words 2m, 2m+1; c = q,
+//        os = o s.
+//  INT4: codes 8m .. 8m+7 are the nibbles of word m, low nibble first. With
+//        each nibble's top bit flipped, u = q + 8 is the unsigned nibble; the
+//        nibbles are split into the bytes of two words (even codes, odd
+//        codes) and converted with byte conversions; c = u, os = (o - 8) s.
+template <typename T, int kBits>
+__device__ __forceinline__ uint4 dequant8(const uint4& q, int m, float sc, float os, uint32_t nib_mask) {
+  float f[8];
+  if constexpr (kBits == 8) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = (float)(int)(int8_t)(word_of(q, 2 * m + (i >> 2)) >> (8 * (i & 3)));
+  } else {
+    const uint32_t x = word_of(q, m) ^ 0x88888888u;
+    // nib_mask (0x0F0F0F0F) comes from the kernel arguments: a compile-time
+    // mask lets the compiler fold it into one bit-field extract per code
+    // instead of one byte-select conversion
+    const uint32_t lo = x & nib_mask, hi = (x >> 4) & nib_mask;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      f[2 * b] = (float)((lo >> (8 * b)) & 0xFFu);
+      f[2 * b + 1] = (float)((hi >> (8 * b)) & 0xFFu);
+    }
+  }
+  uint4 r;
+  r.x = pack2<T>(fmaf(f[0], sc, os), fmaf(f[1], sc, os));
+  r.y = pack2<T>(fmaf(f[2], sc, os), fmaf(f[3], sc, os));
+  r.z = pack2<T>(fmaf(f[4], sc, os), fmaf(f[5], sc, os));
+  r.w = pack2<T>(fmaf(f[6], sc, os), fmaf(f[7], sc, os));
+  return r;
 }
 
 struct QuantArgs {
@@ -84,10 +132,11 @@ struct QuantArgs {
   void* c;                // [rows, N]
   const int32_t* offsets; // [E+1]
   int rows, N, K, G, E, n_blocks, k_quarter;
+  uint32_t nib_mask;      // 0x0F0F0F0F
 };
 
 template <typename T, bool kSwiGlu, int kBits>
-__global__ __launch_bounds__(64 * kQWaves) void skinny_quant_kernel(QuantArgs p) {
+__global__ __launch_bounds__(64 * kQWaves, 3) void skinny_quant_kernel(QuantArgs p) {
   typedef typename MfmaQ<T>::Frag Frag;
   __shared__ f32x4 red[kQWaves - 1][4][64];
   const int lane = threadIdx.x & 63;
@@ -145,7 +194,7 @@ __global__ __launch_bounds__(64 * kQWaves) void skinny_quant_kernel(QuantArgs p)
     for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // Scale and offset*scale of tile t for the group holding the 128
-    // input channels kb .. kb+127 (groups are multiples of 128 long).
+    // input channels of the K-iteration at kb (groups are multiples of 128 long).
     auto load_sc = [&](int kb, float (&sc)[4], float (&os)[4]) {
       const int grp = min(kb, K - 1) / gsz;
 #pragma unroll
@@ -159,7 +208,7 @@ __global__ __launch_bounds__(64 * kQWaves) void skinny_quant_kernel(QuantArgs p)
           o = op ? to_f32(op[(int64_t)n * G + grp]) : 0.f;
         }
         sc[t] = s;
-        os[t] = o * s;
+        os[t] = (kBits == 8 ? o : o - 8.0f) * s;  // INT4 codes enter as q + 8
       }
     };
     // Per iteration at input channel kb: load w of tile t holds channels
@@ -200,20 +249,18 @@ __global__ __launch_bounds__(64 * kQWaves) void skinny_quant_kernel(QuantArgs p)
         for (int m = 0; m < Geo::kMf; ++m)
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
-            Frag f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) f[i] = from_f32<T>(fmaf(q_val<kBits>(w[t][l], m * 8 + i), sc[t], os[t]));
+            const Frag f = __builtin_bit_cast(Frag, dequant8<T, kBits>(w[t][l], m, sc[t], os[t], p.nib_mask));
             acc[t] = MfmaQ<T>::run(f, __builtin_bit_cast(Frag, x[l][m]), acc[t]);
           }
     };
-    const int n_iter = (k_hi - k_lo + kQKIter - 1) / kQKIter;
+    const int n_iter = (k_hi - k_lo + Geo::kIter - 1) / Geo::kIter;
     if (n_iter > 0) {
       load(k_lo, wa, xa, sa_, oa);
       int it = 0;
       for (; it + 2 <= n_iter; it += 2) {
-        load(k_lo + (it + 1) * kQKIter, wb, xb, sb_, ob);
+        load(k_lo + (it + 1) * Geo::kIter, wb, xb, sb_, ob);
         compute(wa, xa, sa_, oa);
-        load(k_lo + (it + 2) * kQKIter, wa, xa, sa_, oa);
+        load(k_lo + (it + 2) * Geo::kIter, wa, xa, sa_, oa);
         compute(wb, xb, sb_, ob);
       }
       if (it < n_iter) compute(wa, xa, sa_, oa);  // odd count: wa holds the last iteration
@@ -260,8 +307,9 @@ __global__ __launch_bounds__(64 * kQWaves) void skinny_quant_kernel(QuantArgs p)
 template <typename T, int kBits>
 void launch_q(QuantArgs p, bool swiglu, hipStream_t s) {
   p.n_blocks = swiglu ? (p.N + 31) / 32 : (p.N + kQRows - 1) / kQRows;
-  const int iters = (p.K + kQKIter - 1) / kQKIter;
-  p.k_quarter = (iters + kQWaves - 1) / kQWaves * kQKIter;
+  constexpr int kIter = QGeo<kBits>::kIter;
+  const int iters = (p.K + kIter - 1) / kIter;
+  p.k_quarter = (iters + kQWaves - 1) / kQWaves * kIter;
   const dim3 grid((unsigned)((int64_t)p.E * p.n_blocks));
   if (swiglu)
     hipLaunchKernelGGL((skinny_quant_kernel<T, true, kBits>), grid, dim3(64 * kQWaves), 0, s, p);
@@ -280,6 +328,7 @@ void launch_q_bits(const QuantArgs& p, int bits, bool swiglu, hipStream_t s) {
 hipError_t launch_experts_quant(const QuantExperts& q, hipStream_t s) {
   if (q.rows == 0) return hipSuccess;
   QuantArgs p = {};
+  p.nib_mask = 0x0F0F0F0Fu;
   p.offsets = q.offsets;
   p.rows = q.rows;
   p.E = q.E;
