@@ -145,6 +145,9 @@ struct GemmArgs {
   // partial[split][rows][N]; the caller reduces them in split order.
   int k_splits, k_chunk;
   float* partial;
+  // GEMM 1 of the experts' training forward: also store g and u, rounded to
+  // T, into cache[rows, 2N] = (g | u), and form h from those rounded values.
+  void* cache;
 };
 
 template <typename T> struct Mfma;
@@ -270,7 +273,7 @@ constexpr int gemm_threads() { return 64 * (kBM / kWaveM) * 2; }
 // stage of the next tile is requested, and only then are the finished
 // tile's results written out, so the store traffic overlaps the next tile's
 // first loads instead of leaving the CU idle.
-template <typename T, bool kSwiGlu, int kBNB, int kBKT, int kWaveM>
+template <typename T, bool kSwiGlu, int kBNB, int kBKT, int kWaveM, bool kCache = false>
 __global__ __launch_bounds__(gemm_threads<kWaveM>()) void mfma_gemm_kernel(GemmArgs p) {
   typedef typename Mfma<T>::Frag Frag;
   constexpr int kWaves = (kBM / kWaveM) * 2;
@@ -454,8 +457,9 @@ __global__ __launch_bounds__(gemm_threads<kWaveM>()) void mfma_gemm_kernel(GemmA
   issue_loads(0, stage_buf<T, kBM * kBKT, 0, 0>(), stage_buf<T, kBNB * kBKT, 1, 0>());
   T* C = static_cast<T*>(p.c);
   const int row_lane = (lane >> 5) * 4;
-  // Epilogue stores per computing wavefront: 4 per 32x32 output block.
-  constexpr int kStores = (kSwiGlu ? kMB * 2 : kMB * kNB) * 4;
+  // Epilogue stores per computing wavefront: 4 per 32x32 output block (3
+  // blocks, h, g and u, per h block when the training cache is written).
+  constexpr int kStores = (kSwiGlu ? kMB * 2 : kMB * kNB) * 4 * (kCache ? 3 : 1);
   static_assert(kStores < 64, "vmcnt holds 6 bits");
   int stores_prev = 0;
   for (;;) {
@@ -534,7 +538,46 @@ __global__ __launch_bounds__(gemm_threads<kWaveM>()) void mfma_gemm_kernel(GemmA
           }
         }
       };
-      if (kSwiGlu) {
+      if (kSwiGlu && kCache) {
+        // g and u rounded to T go to the cache ([rows, 2N], g then u); h is
+        // formed from the rounded values
+        const __amdgpu_buffer_rsrc_t rsrc_gu = __builtin_amdgcn_make_buffer_rsrc(
+            static_cast<T*>(p.cache) + (int64_t)t_row0 * 2 * N, (short)0, t_mrows * 2 * N * (int)sizeof(T),
+            kRsrcFlags);
+        auto store_gu = [&](float (&val)[16], int row_base, int col_base) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            float x[4] = {val[4 * g], val[4 * g + 1], val[4 * g + 2], val[4 * g + 3]};
+            transpose4(x, lane);
+            const int lrow = row_base + g * 8 + row_lane + (lane & 3);
+            const int col = col_base + col4;  // < 2N: u columns are offset by N
+            const int in_n = col_base >= N ? col - N : col;
+            const uint32_t vo = (lrow < t_mrows && in_n < N) ? (uint32_t)(lrow * 2 * N + col) * (uint32_t)sizeof(T)
+                                                            : kOutOfRange;
+            const i32x2 d = {(int)((uint32_t)__builtin_bit_cast(uint16_t, from_f32<T>(x[0])) |
+                                   ((uint32_t)__builtin_bit_cast(uint16_t, from_f32<T>(x[1])) << 16)),
+                             (int)((uint32_t)__builtin_bit_cast(uint16_t, from_f32<T>(x[2])) |
+                                   ((uint32_t)__builtin_bit_cast(uint16_t, from_f32<T>(x[3])) << 16))};
+            __builtin_amdgcn_raw_buffer_store_b64(d, rsrc_gu, vo, 0, 0);
+          }
+        };
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            const int col_base = t_nt * (kBNB / 2) + wn * 64 + nb * 32;
+            float g[16], u[16], val[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              g[i] = to_f32(from_f32<T>(acc[mb][nb][i]));
+              u[i] = to_f32(from_f32<T>(acc[mb][nb + 2][i]));
+              val[i] = silu(g[i]) * u[i];
+            }
+            store_gu(g, wm * kWaveM + mb * 32, col_base);
+            store_gu(u, wm * kWaveM + mb * 32, N + col_base);
+            store_block(val, wm * kWaveM + mb * 32, col_base);
+          }
+      } else if (kSwiGlu) {
 #pragma unroll
         for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
@@ -948,7 +991,10 @@ static int persistent_grid(int entries) {
 template <typename T>
 void launch_mfma(const GemmArgs& g, bool swiglu, hipStream_t s) {
   const dim3 grid(persistent_grid(g.grid));
-  if (swiglu)
+  if (swiglu && g.cache)
+    hipLaunchKernelGGL((mfma_gemm_kernel<T, true, 256, kBK, kWaveMGemm, true>), grid,
+                       dim3(gemm_threads<kWaveMGemm>()), 0, s, g);
+  else if (swiglu)
     hipLaunchKernelGGL((mfma_gemm_kernel<T, true, 256, kBK, kWaveMGemm>), grid,
                        dim3(gemm_threads<kWaveMGemm>()), 0, s, g);
   else
@@ -1021,10 +1067,15 @@ hipError_t reduce_splits(const ExpertsPlan& plan, void* scratch, const int32_t* 
 
 }  // namespace
 
+bool gate_up_can_cache(int64_t rows, int64_t E, int dt) {
+  return dt != kF32 && !use_skinny(rows, E, dt);
+}
+
 hipError_t launch_gate_up(const void* a, const int32_t* a_map, int a_div, const int32_t* offsets,
                           int rows, int E, int H, int I, const void* w_gate, const void* w_up,
-                          int dt, void* h, void* scratch, hipStream_t s) {
+                          int dt, void* h, void* scratch, hipStream_t s, void* cache) {
   if (rows == 0) return hipSuccess;
+  if (cache && !gate_up_can_cache(rows, E, dt)) return hipErrorInvalidValue;
   if (use_skinny(rows, E, dt)) {
     GemmArgs g = {};
     g.offsets = offsets; g.rows = rows;
@@ -1036,6 +1087,7 @@ hipError_t launch_gate_up(const void* a, const int32_t* a_map, int a_div, const 
   GemmArgs g = {};
   g.offsets = offsets; g.rows = rows;
   setup_gate_up(g, a, a_map, a_div, H, I, w_gate, w_up, h);
+  g.cache = cache;
   plan_tiles(g, plan, E, dt, true, scratch, s);
   launch_gemm<true>(g, dt, s);
   return hipGetLastError();

@@ -66,9 +66,13 @@ struct DownPartials {
 
 // a_map: optional; when given, A row r is row a_map[r] / a_div of `a`
 // (gathering tokens straight from x instead of a materialised x_disp).
+// cache (optional): also write g and u rounded to dt into cache[rows, 2I] and
+// form h from those rounded values (the experts' training forward); only
+// where gate_up_can_cache() holds (the MFMA path, not the decode path).
 hipError_t launch_gate_up(const void* a, const int32_t* a_map, int a_div, const int32_t* offsets,
                           int rows, int E, int H, int I, const void* w_gate, const void* w_up,
-                          int dt, void* h, void* scratch, hipStream_t s);
+                          int dt, void* h, void* scratch, hipStream_t s, void* cache = nullptr);
+bool gate_up_can_cache(int64_t rows, int64_t E, int dt);
 // With keep != NULL and a split K, the partial sums stay in scratch and are
 // described in *keep instead of being reduced into expert_out.
 hipError_t launch_down(const void* h, const int32_t* offsets, int rows, int E, int H, int I,

@@ -692,10 +692,16 @@ size_t train_prefix_bytes(int64_t E) { return ((size_t)(E + 1) * 4 + 255) / 256 
 
 hipError_t launch_experts_forward_training(const TrainExperts& q, hipStream_t s) {
   if (q.rows == 0) return hipSuccess;
-  hipError_t e = q.dt == kF16 ? experts_forward_training_t<f16>(q, s) : experts_forward_training_t<bf16>(q, s);
-  if (e != hipSuccess) return e;
   void* h = static_cast<char*>(q.cache) + (size_t)q.rows * 2 * q.I * 2;
   void* scratch = static_cast<char*>(q.ws) + train_prefix_bytes(q.E);
+  hipError_t e;
+  if (gate_up_can_cache(q.rows, q.E, q.dt))
+    // the inference gate/up GEMM, also writing the rounded g and u
+    e = launch_gate_up(q.x, nullptr, 1, q.offsets, q.rows, q.E, q.H, q.I, q.w_gate, q.w_up, q.dt, h,
+                       scratch, s, q.cache);
+  else
+    e = q.dt == kF16 ? experts_forward_training_t<f16>(q, s) : experts_forward_training_t<bf16>(q, s);
+  if (e != hipSuccess) return e;
   return launch_down(h, q.offsets, q.rows, q.E, q.H, q.I, q.w_down, q.dt, q.y, scratch, s);
 }
 
