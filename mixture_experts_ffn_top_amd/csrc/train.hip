@@ -9,12 +9,14 @@
 //   ddown  = dY^T h                  [H, I]    K = n_e rows
 //   dgate | dup = [dg | du]^T X      [2I, H]   K = n_e rows
 // and of the training forward the plain projection [g | u] = X [W_gate;
-// W_up]^T (K = H, both operands along K). One MFMA kernel serves them all:
-// each operand is either K-contiguous (element (mn, k) at mn * ld + k) or
-// MN-contiguous (at k * ld + mn), and may be split in two tensors along its
-// outer index (gate and up weights, dg and du). MN-contiguous tiles are
-// transposed on their way into LDS (pairs of k packed into one 32-bit LDS
-// write), so the MFMA always reads 16-byte K-runs.
+// W_up]^T (K = H, both operands along K; used for decode-sized batches, the
+// larger ones take the inference gate/up GEMM with a cache epilogue). One
+// MFMA kernel serves them all: each operand is either K-contiguous (element
+// (mn, k) at mn * ld + k) or MN-contiguous (at k * ld + mn), and K may run
+// over two segments held by different tensors (dg with W_gate, du with
+// W_up). Both kinds of tile go to LDS as they lie in memory; MN-contiguous
+// ones are read back with gfx950's transposing LDS read, so the MFMA gets
+// its 8-element K-runs either way.
 //
 // Grouping. "M-grouped" GEMMs take their rows from the expert offsets (one
 // M-tile never spans two experts; tiles are found through a device-built
