@@ -183,6 +183,30 @@ __device__ __forceinline__ Frag<T> frag_mn(const T* buf, int C0, int s, int lane
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
 
+// One butterfly round of a 4 x 4 transpose across the lanes of a quad: the
+// lane swaps with lane ^ kBit the two values whose index bit kBit differs
+// from its own lane bit (quad-permute DPP moves).
+template <int kBit>
+__device__ __forceinline__ void quad_round(float (&x)[4], int lane) {
+  constexpr int kCtrl = kBit == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] or [2,3,0,1]
+  const bool hi = (lane & kBit) != 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (i & kBit) continue;
+    const float send = hi ? x[i] : x[i | kBit];
+    const float recv = __builtin_bit_cast(float,
+        __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, send), kCtrl, 0xF, 0xF, false));
+    if (hi) x[i] = recv;
+    else x[i | kBit] = recv;
+  }
+}
+
+// On return x[c] of lane q of a quad holds what x[q] of lane c held.
+__device__ __forceinline__ void quad_transpose(float (&x)[4], int lane) {
+  quad_round<1>(x, lane);
+  quad_round<2>(x, lane);
+}
+
 // Scheduling order for one k16 sub-step: each of its 8 MFMAs followed by
 // its share of the next sub-step's kReads LDS reads.
 template <int kReads, int X>
@@ -311,36 +335,60 @@ __global__ __launch_bounds__(kTThreads) void train_gemm_kernel(TrainGemm p) {
     step(tbuf<T, 0, 1>(), tbuf<T, 1, 1>(), tbuf<T, 0, 0>(), tbuf<T, 1, 0>(), t + 2 < nk_pad);
   }
 
-  // ---- epilogue: D row (v/4)*8 + (lane/32)*4 + v%4, column lane%32 ----
+  // ---- epilogue ----
+  // Accumulator element v of lane l sits at row (v/4)*8 + (l/32)*4 + v%4 and
+  // column l%32 of its 32 x 32 block. Each run of 4 rows is transposed within
+  // the quad of lanes holding 4 adjacent columns, after which lane l holds
+  // columns 4*((l%32)/4) .. +3 of one row: one 16-byte (fp32) or 8-byte
+  // store instead of four. N is a multiple of 8, so the 4 columns are all
+  // inside or all outside.
+  const int col4 = (lane & 31) & ~3;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t m = m0 + wm * 64 + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-        const int64_t n = n0 + wn * 128 + j * 32 + (lane & 31);
+      for (int g4 = 0; g4 < 4; ++g4) {
+        float x[4] = {acc[i][j][4 * g4], acc[i][j][4 * g4 + 1], acc[i][j][4 * g4 + 2], acc[i][j][4 * g4 + 3]};
+        quad_transpose(x, lane);
+        const int64_t m = m0 + wm * 64 + i * 32 + g4 * 8 + (lane >> 5) * 4 + (lane & 3);
+        const int64_t n = n0 + wn * 128 + j * 32 + col4;
         if (m >= m_end || n >= p.N) continue;
-        const float x = acc[i][j][v];
         if (kEpi == kEpiSwiGluBwd) {
           // dh = x; g, u from the cache; dg, du into out0 (same [rows, 2N] layout)
           const int64_t at = m * 2 * (int64_t)p.N + n;
-          const float g = to_f32(static_cast<const T*>(p.gu)[at]);
-          const float u = to_f32(static_cast<const T*>(p.gu)[at + p.N]);
-          const float sg = sigmoidf_(g);
+          const uint2 gw = *reinterpret_cast<const uint2*>(static_cast<const T*>(p.gu) + at);
+          const uint2 uw = *reinterpret_cast<const uint2*>(static_cast<const T*>(p.gu) + at + p.N);
+          const T* gv = reinterpret_cast<const T*>(&gw);
+          const T* uv = reinterpret_cast<const T*>(&uw);
+          T dg[4], du[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float g = to_f32(gv[c]), u = to_f32(uv[c]);
+            const float sg = sigmoidf_(g);
+            dg[c] = from_f32<T>(x[c] * u * sg * (1.0f + g * (1.0f - sg)));
+            du[c] = from_f32<T>(x[c] * g * sg);
+          }
           T* o = static_cast<T*>(p.out0);
-          o[at] = from_f32<T>(x * u * sg * (1.0f + g * (1.0f - sg)));
-          o[at + p.N] = from_f32<T>(x * g * sg);
+          *reinterpret_cast<uint2*>(o + at) = *reinterpret_cast<const uint2*>(dg);
+          *reinterpret_cast<uint2*>(o + at + p.N) = *reinterpret_cast<const uint2*>(du);
         } else {
           const bool hi = m >= p.out_split;
           const int64_t row = hi ? m - p.out_split : m;
           const int64_t at = (kGroupK ? (int64_t)e * p.out_estride : 0) + row * p.ldc + n;
           void* base = hi ? p.out1 : p.out0;
-          if (kEpi == kEpiStoreF32) static_cast<float*>(base)[at] = x;
-          else static_cast<T*>(base)[at] = from_f32<T>(x);
+          if (kEpi == kEpiStoreF32) {
+            *reinterpret_cast<float4*>(static_cast<float*>(base) + at) = make_float4(x[0], x[1], x[2], x[3]);
+          } else {
+            T h[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) h[c] = from_f32<T>(x[c]);
+            *reinterpret_cast<uint2*>(static_cast<T*>(base) + at) = *reinterpret_cast<const uint2*>(h);
+          }
         }
       }
 }
+
 
 // prefix[e] = number of M-tiles of experts before e; prefix[E] = total.
 __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __restrict__ offsets,
