@@ -371,8 +371,9 @@ moe_status moe_combine_add_rmsnorm_special(
  *   moe_experts_quant_workspace_size(rows, E, H, I, dt) (holds h).
  * Errors: ARGUMENT if bits is not 8 or 4, groups < 1 or does not divide H
  *   and I, or groups > 1 with bits = 8; UNSUPPORTED for dt F32, for
- *   groups > 1 unless H/groups and I/groups are multiples of 128, and for
- *   rows > 4 * E (this path streams weights for decode-sized batches).
+ *   groups > 1 unless H/groups and I/groups are multiples of 128, for
+ *   rows > 4 * E (this path streams weights for decode-sized batches), and
+ *   when one expert's codes or 4*E activation rows exceed 2^31 bytes.
  */
 moe_status moe_experts_forward_dispatched_quant(
     const void* x_disp, const int32_t* expert_offsets, int64_t rows, int64_t E, int64_t H, int64_t I,
@@ -477,7 +478,7 @@ moe_status moe_combine_backward(const void* expert_out, const int32_t* row_of_sl
  *   ws: moe_experts_forward_training_workspace_size(rows, E, H, I, dt).
  * x_disp, the weights and the cache must stay unchanged until
  * moe_experts_backward has run. Errors: UNSUPPORTED for dt F32 (this path
- * runs on the bf16/f16 matrix cores).
+ * runs on the bf16/f16 matrix cores) and for H or 2*I above 2^22 elements.
  */
 moe_status moe_experts_forward_training(const void* x_disp, const int32_t* expert_offsets,
                                         int64_t rows, int64_t E, int64_t H, int64_t I,

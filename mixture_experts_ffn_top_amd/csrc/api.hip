@@ -1,6 +1,8 @@
 // C ABI of libmoe_ffn: host-side validation, workspace carving and launches.
 // Every check runs before anything is enqueued; on error nothing is enqueued.
 #include <math.h>
+
+#include <algorithm>
 #include <stdint.h>
 
 #include "kernels.h"
@@ -109,6 +111,8 @@ moe_status check_quant_args(int64_t rows, int64_t E, int64_t H, int64_t I, int b
   if (groups > 1 && ((H / groups) % 128 != 0 || (I / groups) % 128 != 0)) return MOE_ERROR_UNSUPPORTED;
   if (!row_len_ok(H) || !row_len_ok(I) || E > kMaxE) return MOE_ERROR_UNSUPPORTED;
   if (rows > 4 * E) return MOE_ERROR_UNSUPPORTED;  // decode-sized batches only
+  // one expert's codes and the activation rows are addressed with 32-bit offsets
+  if (H * I * bits / 8 > INT32_MAX || 4 * E * std::max(H, I) * 2 > INT32_MAX) return MOE_ERROR_UNSUPPORTED;
   return MOE_SUCCESS;
 }
 
@@ -821,6 +825,12 @@ static moe_status check_train_args(int64_t rows, int64_t E, int64_t H, int64_t I
   if (dt == MOE_F32) return MOE_ERROR_UNSUPPORTED;  // the matrix-core path is bf16 / f16
   if (E > kMaxE || rows > INT32_MAX || !row_len_ok(H) || !row_len_ok(I)) return MOE_ERROR_UNSUPPORTED;
   if ((int64_t)E * I * H > INT64_MAX / 8 || 2 * I > INT32_MAX) return MOE_ERROR_UNSUPPORTED;
+  // the training GEMM keeps a lane's offset inside a 256-row tile in 32 bits
+  // (leading dimensions up to 2^22 elements) and numbers its tiles in int
+  if (H > (1 << 22) || 2 * I > (1 << 22)) return MOE_ERROR_UNSUPPORTED;
+  const int64_t n_tiles = (std::max<int64_t>(H, 2 * I) + 255) / 256;
+  if (((rows + 255) / 256 + E) * n_tiles > INT32_MAX || E * n_tiles * n_tiles > INT32_MAX)
+    return MOE_ERROR_UNSUPPORTED;
   return MOE_SUCCESS;
 }
 

@@ -101,7 +101,10 @@ def test_experts_validation():
     assert call(8, None) == S["MOE_ERROR_NULL_POINTER"]
     assert call(12, need - 256) == S["MOE_ERROR_WORKSPACE"]
     assert call(10, FAKE + 2**21 + 512) == S["MOE_ERROR_ARGUMENT"]  # expert_out inside w_gate
-    assert call(2, 0) == S["MOE_SUCCESS"]  # no rows: no-op
+    assert call(2, 0) == S["MOE_SUCCESS"]
+    a = list(base)
+    a[4], a[5] = 65536, 65536                             # one expert's INT8 codes: 4 GiB
+    assert f(*a) == S["MOE_ERROR_UNSUPPORTED"]  # no rows: no-op
 
 
 def test_combine_and_norm_validation():
@@ -225,6 +228,9 @@ def test_quant_validation():
     assert call(11, None) == S["MOE_ERROR_NULL_POINTER"]  # scale missing
     assert call(20, need - 1) == S["MOE_ERROR_WORKSPACE"]
     assert call(2, 0) == S["MOE_SUCCESS"]
+    a = list(base)
+    a[4], a[5] = 65536, 65536                             # one expert's INT8 codes: 4 GiB
+    assert f(*a) == S["MOE_ERROR_UNSUPPORTED"]
 
 
 def test_training_validation():
@@ -292,6 +298,8 @@ def test_training_validation():
     assert call(ft, okf, 12, FAKE + 2**29 + 8) == S["MOE_ERROR_WORKSPACE"]  # misaligned
     assert call(ft, okf, 11, FAKE + 2**27 + 64) == S["MOE_ERROR_ARGUMENT"]  # cache overlaps expert_out
     assert call(ft, okf, 2, 0) == S["MOE_SUCCESS"]
+    assert call(ft, okf, 4, (1 << 22) + 8) == S["MOE_ERROR_UNSUPPORTED"]   # H past 2^22
+    assert call(ft, okf, 5, (1 << 21) + 8) == S["MOE_ERROR_UNSUPPORTED"]   # 2I past 2^22
     bw = lib.moe_experts_backward
     okw = [FAKE, FAKE + 2**20, 64, 8, 512, 384, FAKE + 2**24, FAKE + 2**25, FAKE + 2**26, 2,
            FAKE + 2**27, FAKE + 2**28, FAKE + 2**29, FAKE + 2**31, FAKE + 2**32, FAKE + 2**33,
