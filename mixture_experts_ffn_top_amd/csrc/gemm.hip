@@ -544,16 +544,18 @@ __global__ __launch_bounds__(gemm_threads<kWaveM>()) void mfma_gemm_kernel(GemmA
         const __amdgpu_buffer_rsrc_t rsrc_gu = __builtin_amdgcn_make_buffer_rsrc(
             static_cast<T*>(p.cache) + (int64_t)t_row0 * 2 * N, (short)0, t_mrows * 2 * N * (int)sizeof(T),
             kRsrcFlags);
-        auto store_gu = [&](float (&val)[16], int row_base, int col_base) {
+        // col_base: the block's column of h; half 0 stores into the g half of
+        // the cache row, half 1 into the u half (N further on)
+        auto store_gu = [&](float (&val)[16], int row_base, int col_base, int half) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             float x[4] = {val[4 * g], val[4 * g + 1], val[4 * g + 2], val[4 * g + 3]};
             transpose4(x, lane);
             const int lrow = row_base + g * 8 + row_lane + (lane & 3);
-            const int col = col_base + col4;  // < 2N: u columns are offset by N
-            const int in_n = col_base >= N ? col - N : col;
-            const uint32_t vo = (lrow < t_mrows && in_n < N) ? (uint32_t)(lrow * 2 * N + col) * (uint32_t)sizeof(T)
-                                                            : kOutOfRange;
+            const int col = col_base + col4;
+            const uint32_t vo = (lrow < t_mrows && col < N)
+                                    ? (uint32_t)(lrow * 2 * N + half * N + col) * (uint32_t)sizeof(T)
+                                    : kOutOfRange;
             const i32x2 d = {(int)((uint32_t)__builtin_bit_cast(uint16_t, from_f32<T>(x[0])) |
                                    ((uint32_t)__builtin_bit_cast(uint16_t, from_f32<T>(x[1])) << 16)),
                              (int)((uint32_t)__builtin_bit_cast(uint16_t, from_f32<T>(x[2])) |
@@ -573,8 +575,8 @@ __global__ __launch_bounds__(gemm_threads<kWaveM>()) void mfma_gemm_kernel(GemmA
               u[i] = to_f32(from_f32<T>(acc[mb][nb + 2][i]));
               val[i] = silu(g[i]) * u[i];
             }
-            store_gu(g, wm * kWaveM + mb * 32, col_base);
-            store_gu(u, wm * kWaveM + mb * 32, N + col_base);
+            store_gu(g, wm * kWaveM + mb * 32, col_base, 0);
+            store_gu(u, wm * kWaveM + mb * 32, col_base, 1);
             store_block(val, wm * kWaveM + mb * 32, col_base);
           }
       } else if (kSwiGlu) {

@@ -675,7 +675,10 @@ def _qdev(t, dtype):
 @pytest.mark.parametrize("bits,groups,dtype,with_offset,H,I_", [(8, 1, "bf16", True, 512, 384),
                                                                 (4, 1, "f16", False, 512, 384),
                                                                 (4, 4, "bf16", True, 1024, 512),
-                                                                (8, 1, "bf16", False, 136, 264)])
+                                                                (8, 1, "bf16", False, 136, 264),
+                                                                (8, 1, "f16", True, 264, 136),
+                                                                (4, 2, "f16", True, 256, 768),
+                                                                (4, 1, "bf16", True, 72, 200)])
 def test_quant_experts_dispatched(bits, groups, dtype, with_offset, H, I_):
     say("quant experts", bits, groups, dtype)
     g = np.random.default_rng(bits * 10 + groups)

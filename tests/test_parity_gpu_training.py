@@ -172,6 +172,9 @@ EXPERT_CASES = [
     (8, 512, 384, [64] * 8, "f16"),
     (3, 128, 136, [1, 300, 5], "bf16"),
     (16, 256, 512, list(range(0, 160, 10)), "bf16"),
+    (1, 392, 328, [513], "bf16"),               # one expert takes every row
+    (5, 256, 264, [0, 0, 600, 0, 0], "bf16"),   # every row on one of several experts
+    (2, 1032, 1544, [200, 311], "f16"),         # larger and ragged, fp16
 ]
 
 
@@ -235,14 +238,15 @@ def test_experts_backward_deterministic_and_no_rows():
 
 
 # -------------------------------------------------------------- whole chain --
-@pytest.mark.parametrize("scoring,normalize", [(O.SOFTMAX, True), (O.SIGMOID, False)])
-def test_training_step_chain(scoring, normalize):
+@pytest.mark.parametrize("scoring,normalize,k", [(O.SOFTMAX, True, 2), (O.SIGMOID, False, 2), (O.SOFTMAX, False, 1),
+                                                 (O.SIGMOID, True, 3)])
+def test_training_step_chain(scoring, normalize, k):
     """route (fixed selection) -> weights -> dispatch -> experts (training)
     -> combine; then combine_backward -> experts backward -> dispatch_backward
     -> router backward, each step through the C ABI, against the oracle chain."""
-    say("training chain", scoring, normalize)
-    r = np.random.default_rng(5 + scoring)
-    T, E, k, H, I_, dtype = 96, 8, 2, 256, 384, "bf16"
+    say("training chain", scoring, normalize, k)
+    r = np.random.default_rng(5 + scoring + 10 * k)
+    T, E, H, I_, dtype = 96, 8, 256, 384, "bf16"
     z = _store(r.standard_normal((T, E)), "f32")
     x = _store(r.standard_normal((T, H)), dtype)
     W = [tuple(_store(r.standard_normal(s) / np.sqrt(s[-1]), dtype) for s in ((I_, H), (I_, H), (H, I_)))
