@@ -660,7 +660,7 @@ def swiglu_expert_training(x_rows, w_gate_e, w_up_e, w_down_e, dtype):
     return y, g, u, h
 
 
-def swiglu_expert_backward(x_rows, w_gate_e, w_up_e, w_down_e, g, u, h, dy, dtype):
+def swiglu_expert_backward(x_rows, w_gate_e, w_up_e, w_down_e, g, u, h, dy, dtype, terms=False):
     """cache.backward of one expert, from its training cache (g, u, h) and the
     gradient dy of its output rows:
       dh = dy W_down                                   (not rounded)
@@ -668,7 +668,8 @@ def swiglu_expert_backward(x_rows, w_gate_e, w_up_e, w_down_e, g, u, h, dy, dtyp
       dg = round(dh * u * SiLU'(g)),  du = round(dh * SiLU(g))
       dinput = round(dg W_gate + du W_up)              [n, H], model dtype
       dgate = dg^T x, dup = du^T x, ddown = dy^T h     fp32
-    Returns (dinput, dgate [I, H], dup [I, H], ddown [H, I])."""
+    Returns (dinput, dgate [I, H], dup [I, H], ddown [H, I]), and with
+    terms=True also the rounded dg and du as fp64 values."""
     x = decode(x_rows, dtype)
     wg, wu, wd = decode(w_gate_e, dtype), decode(w_up_e, dtype), decode(w_down_e, dtype)
     gv, uv, hv, dyv = decode(g, dtype), decode(u, dtype), decode(h, dtype), decode(dy, dtype)
@@ -678,8 +679,9 @@ def swiglu_expert_backward(x_rows, w_gate_e, w_up_e, w_down_e, g, u, h, dy, dtyp
     dg = decode(round_to(dh * uv * sig * (1.0 + gv * (1.0 - sig)), dtype), dtype)
     du = decode(round_to(dh * gv * sig, dtype), dtype)
     dinput = round_to(dg @ wg + du @ wu, dtype)
-    return (dinput, (dg.T @ x).astype(np.float32), (du.T @ x).astype(np.float32),
-            (dyv.T @ hv).astype(np.float32))
+    out = (dinput, (dg.T @ x).astype(np.float32), (du.T @ x).astype(np.float32),
+           (dyv.T @ hv).astype(np.float32))
+    return out + (dg, du) if terms else out
 
 
 def experts_forward_training(x_disp, offsets, weights_of, dtype):
@@ -699,10 +701,11 @@ def experts_forward_training(x_disp, offsets, weights_of, dtype):
     return parts
 
 
-def experts_backward(x_disp, offsets, weights_of, g, u, h, dexpert, dtype):
+def experts_backward(x_disp, offsets, weights_of, g, u, h, dexpert, dtype, terms=False):
     """cache.backward over all experts: (dinput [R, H] model dtype, dgate
-    [E, I, H], dup [E, I, H], ddown [E, H, I] fp32). Experts without rows get
-    zero weight gradients."""
+    [E, I, H], dup [E, I, H], ddown [E, H, I] fp32), and with terms=True also
+    dg, du [R, I] (fp64 values of the rounded terms). Experts without rows
+    get zero weight gradients."""
     E = len(offsets) - 1
     R = int(offsets[-1])
     H = x_disp.shape[1] if R else 0
@@ -718,12 +721,18 @@ def experts_backward(x_disp, offsets, weights_of, g, u, h, dexpert, dtype):
         a, b = int(offsets[e]), int(offsets[e + 1])
         if a == b:
             continue
-        di, dgt, dut, ddn = swiglu_expert_backward(x_disp[a:b], wg, wu, wd, g[a:b], u[a:b], h[a:b],
-                                                   dexpert[a:b], dtype)
+        di, dgt, dut, ddn, dgv, duv = swiglu_expert_backward(x_disp[a:b], wg, wu, wd, g[a:b], u[a:b], h[a:b],
+                                                             dexpert[a:b], dtype, terms=True)
         if dinput is None:
             dinput = np.empty((R, H), dtype=di.dtype)
+            dg_all, du_all = np.zeros((R, I_)), np.zeros((R, I_))
         dinput[a:b] = di
+        dg_all[a:b], du_all[a:b] = dgv, duv
         dgate[e], dup[e], ddown[e] = dgt, dut, ddn
+    if terms:
+        if dinput is None:
+            dg_all = du_all = np.zeros((0, dgate.shape[1] if dgate is not None else 0))
+        return dinput, dgate, dup, ddown, dg_all, du_all
     return dinput, dgate, dup, ddown
 
 

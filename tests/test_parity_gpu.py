@@ -162,6 +162,9 @@ EXPERT_CASES = [
     (64, 2, 8, 128, 256, "f32"),
     (150, 3, 4, 72, 104, "f32"),
     (1, 1, 1, 8, 8, "bf16"),
+    # several tiles per persistent workgroup, with ragged column and K tails
+    (2560, 4, 256, 264, 200, "bf16"),
+    (6000, 4, 96, 136, 328, "f16"),
 ]
 
 
