@@ -57,7 +57,8 @@ typedef enum moe_status {
                                  an output overlaps an input or another output */
   MOE_ERROR_DEVICE = 5,       /* a pointer is not device memory of the stream's device */
   MOE_ERROR_WORKSPACE = 6,    /* workspace NULL, misaligned or too small */
-  MOE_ERROR_UNSUPPORTED = 7,  /* E > 1024, T*top_k > INT32_MAX, H or I not a multiple of 8 */
+  MOE_ERROR_UNSUPPORTED = 7,  /* E > 1024, T*top_k > INT32_MAX, H or I not a multiple of 8,
+                                 a row of H elements longer than INT32_MAX bytes */
   MOE_ERROR_HIP = 8           /* a HIP launch or query failed */
 } moe_status;
 

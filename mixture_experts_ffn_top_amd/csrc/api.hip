@@ -80,6 +80,9 @@ moe_status check_route_args(int64_t T, int64_t E, int64_t top_k, moe_dtype logit
 }
 
 bool row_len_ok(int64_t n) { return n > 0 && n % 8 == 0; }
+// The combine kernels address one expert row through a buffer resource whose
+// 32-bit range is the row's byte length.
+bool row_bytes_ok(int64_t H, moe_dtype dt) { return H * (int64_t)dtype_size(dt) <= INT32_MAX; }
 
 // Options of the grouped-limited sigmoid router (ruDNN user guide, "10.
 // Grouped-limited sigmoid MoE routing"), validated after check_route_args.
@@ -354,7 +357,7 @@ moe_status moe_combine(const void* expert_out, const int32_t* row_of_slot, const
                        void* out, hipStream_t stream) {
   if (T < 0 || top_k < 1 || H < 1) return MOE_ERROR_SHAPE;
   if (!valid_dt(dt) || !valid_dt(w_dt)) return MOE_ERROR_DTYPE;
-  if (T * top_k > INT32_MAX || !row_len_ok(H)) return MOE_ERROR_UNSUPPORTED;
+  if (T * top_k > INT32_MAX || !row_len_ok(H) || !row_bytes_ok(H, dt)) return MOE_ERROR_UNSUPPORTED;
   if (T == 0) return MOE_SUCCESS;
   if (!expert_out || !row_of_slot || !weights || !out) return MOE_ERROR_NULL_POINTER;
   const size_t ds = dtype_size(dt), slots = (size_t)(T * top_k);
@@ -416,7 +419,7 @@ moe_status forward_impl(const void* x, const void* logits, moe_dtype logits_dt, 
   if (H < 1 || I < 1) return MOE_ERROR_SHAPE;
   moe_status st = MOE_SUCCESS;
   if (!valid_dt(dt)) return MOE_ERROR_DTYPE;
-  if (!row_len_ok(H) || !row_len_ok(I)) return MOE_ERROR_UNSUPPORTED;
+  if (!row_len_ok(H) || !row_len_ok(I) || !row_bytes_ok(H, dt)) return MOE_ERROR_UNSUPPORTED;
   if (T == 0) return MOE_SUCCESS;
   if (!x || !logits || !w_gate || !w_up || !w_down || !out) return MOE_ERROR_NULL_POINTER;
   const ForwardLayout L = forward_layout(T, H, I, E, top_k, dt, logits_dt);

@@ -21,9 +21,80 @@ constexpr int kChunkK = 8;  // expert rows whose loads are issued together
 #define LOAD(v, p) (v).load_nt(p)
 #define STORE(v, p) (v).store_nt(p)
 
+// One expert output row as a buffer resource. A dropped slot (row < 0) gets
+// an empty range, so its loads read zeros without touching memory and no
+// load has to sit behind a branch.
+template <typename T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const T* y, int row, int H) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(y + (int64_t)max(row, 0) * H), (short)0,
+                                           row >= 0 ? H * (int)sizeof(T) : 0, kBufferFlags);
+}
+
+// Adds w_j * y[row_of_slot[s0 + j]] for the C slots s0 .. s0 + C - 1, in slot
+// order, to this thread's VPT groups of 8 columns (group q starts at column
+// 8 * (v0 + q * vstride); groups past the row read zeros). The C indices and
+// weights are read first, then the row loads are issued for QB column groups
+// at a time (at most kPieces 16-byte pieces held at once) before any is used.
+// wsum gets the weights' sum; lost is set if a slot has no row.
+template <int C, int VPT, int kPieces, typename T, typename WT>
+__device__ __forceinline__ void add_slots(const T* __restrict__ y,
+                                          const int32_t* __restrict__ row_of_slot,
+                                          const WT* __restrict__ w, int64_t s0, int H, int v0,
+                                          int vstride, float (&x)[VPT][8], float& wsum,
+                                          bool& lost) {
+  __amdgpu_buffer_rsrc_t r[C];
+  float wj[C];
+#pragma unroll
+  for (int j = 0; j < C; ++j) {
+    const int row = row_of_slot[s0 + j];
+    wj[j] = to_f32(w[s0 + j]);
+    wsum += wj[j];
+    lost = lost || row < 0;
+    r[j] = row_rsrc(y, row, H);
+  }
+  constexpr int kPer = C * Vec8<T>::kChunks;  // pieces per column group
+  constexpr int QB = VPT * kPer <= kPieces ? VPT : (kPieces / kPer > 0 ? kPieces / kPer : 1);
+#pragma unroll
+  for (int q0 = 0; q0 < VPT; q0 += QB) {
+    Vec8<T> d[QB][C];
+#pragma unroll
+    for (int q = 0; q < QB; ++q)
+#pragma unroll
+      for (int j = 0; j < C; ++j)
+        d[q][j].load_nt(r[j], (uint32_t)(v0 + (q0 + q) * vstride) * (uint32_t)sizeof(Vec8<T>));
+#pragma unroll
+    for (int q = 0; q < QB; ++q)
+#pragma unroll
+      for (int j = 0; j < C; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[q0 + q][i] = fmaf(wj[j], d[q][j].get(i), x[q0 + q][i]);
+  }
+}
+
+// All k slots of token t: chunks of kChunkK, then a tail of 4, 2 and 1.
+template <int VPT, int kPieces, typename T, typename WT>
+__device__ __forceinline__ void add_token_slots(const T* __restrict__ y,
+                                                const int32_t* __restrict__ row_of_slot,
+                                                const WT* __restrict__ w, int t, int k, int H,
+                                                int v0, int vstride, float (&x)[VPT][8],
+                                                float& wsum, bool& lost) {
+  const int64_t s = (int64_t)t * k;
+  int j = 0;
+  for (; j + kChunkK <= k; j += kChunkK)
+    add_slots<kChunkK, VPT, kPieces>(y, row_of_slot, w, s + j, H, v0, vstride, x, wsum, lost);
+  if (k - j >= 4) {
+    add_slots<4, VPT, kPieces>(y, row_of_slot, w, s + j, H, v0, vstride, x, wsum, lost);
+    j += 4;
+  }
+  if (k - j >= 2) {
+    add_slots<2, VPT, kPieces>(y, row_of_slot, w, s + j, H, v0, vstride, x, wsum, lost);
+    j += 2;
+  }
+  if (k - j >= 1) add_slots<1, VPT, kPieces>(y, row_of_slot, w, s + j, H, v0, vstride, x, wsum, lost);
+}
+
 // Grid T * ceil(H/8/256) (token-major); each thread produces 8 consecutive
-// outputs. The k expert rows are fetched kChunkK at a time, all loads of a
-// chunk issued before any is used, then summed in slot order.
+// outputs, the k expert rows summed in slot order.
 template <typename T, typename WT>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y,
                                                        const int32_t* __restrict__ row_of_slot,
@@ -32,33 +103,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y,
                                                        T* __restrict__ out) {
   const int t = blockIdx.x / blocks_per_token;
   const int v = (blockIdx.x % blocks_per_token) * blockDim.x + threadIdx.x;
-  if (v * 8 >= H) return;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float x[1][8] = {{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}};
+  float wsum = 0.f;
   bool lost = false;
-  for (int j0 = 0; j0 < k; j0 += kChunkK) {
-    Vec8<T> d[kChunkK];
-    float wj[kChunkK];
-#pragma unroll
-    for (int j = 0; j < kChunkK; ++j) {
-      wj[j] = 0.f;
-      if (j0 + j < k) {
-        const int r = row_of_slot[(int64_t)t * k + j0 + j];
-        wj[j] = to_f32(w[(int64_t)t * k + j0 + j]);
-        if (r < 0) lost = true;
-        else d[j].load(y + (int64_t)r * H + v * 8);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < kChunkK; ++j) {
-      if (j0 + j < k && !lost) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj[j], d[j].get(i), acc[i]);
-      }
-    }
-  }
+  add_token_slots<1, 16>(y, row_of_slot, w, t, k, H, v, 0, x, wsum, lost);
+  if (v * 8 >= H) return;
   Vec8<T> o;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) o.set(i, lost ? NAN : acc[i]);
+  for (int i = 0; i < 8; ++i) o.set(i, lost ? NAN : x[0][i]);
   o.store(out + (int64_t)t * H + v * 8);
 }
 
@@ -123,8 +175,7 @@ __global__ __launch_bounds__(256) void combine_partials_kernel(
 
 // One workgroup per token, up to 1024 threads; thread owns VPT groups of 8
 // columns strided by the workgroup and keeps x in registers between the sum
-// of squares and the scaling. The k expert rows of a group are fetched
-// kChunkK at a time with all loads issued before any is used.
+// of squares and the scaling.
 template <typename T, typename WT, int VPT>
 __global__ __launch_bounds__(1024) void combine_norm_kernel(
     const T* __restrict__ y, const int32_t* __restrict__ row_of_slot, const WT* __restrict__ w,
@@ -141,55 +192,40 @@ __global__ __launch_bounds__(1024) void combine_norm_kernel(
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[q][i] = 0.f;
 
+  // The residual and shared rows do not depend on the routing: when the
+  // registers allow, their loads go out first, ahead of the map reads the
+  // expert rows wait on.
+  constexpr bool kEarly = VPT * Vec8<T>::kChunks <= 2;
+  Vec8<T> rs[VPT], sh[VPT];
+  auto load_rs = [&](int q) {
+    const int v = threadIdx.x + q * nthreads;
+    if (v < nvec) {
+      LOAD(rs[q], residual + (int64_t)t * H + v * 8);
+      if (shared) LOAD(sh[q], shared + (int64_t)t * H + v * 8);
+    }
+  };
+  if (kEarly) {
+#pragma unroll
+    for (int q = 0; q < VPT; ++q) load_rs(q);
+  }
+
   float wsum = 0.f;
   bool lost = false;
-  for (int j0 = 0; j0 < k; j0 += kChunkK) {
-    int rows[kChunkK];
-    float wj[kChunkK];
-#pragma unroll
-    for (int j = 0; j < kChunkK; ++j) {
-      rows[j] = -1;
-      wj[j] = 0.f;
-      if (j0 + j < k) {
-        rows[j] = row_of_slot[(int64_t)t * k + j0 + j];
-        wj[j] = to_f32(w[(int64_t)t * k + j0 + j]);
-        wsum += wj[j];
-        if (rows[j] < 0) lost = true;
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < VPT; ++q) {
-      const int v = threadIdx.x + q * nthreads;
-      if (v < nvec) {
-        Vec8<T> d[kChunkK];
-#pragma unroll
-        for (int j = 0; j < kChunkK; ++j)
-          if (rows[j] >= 0) LOAD(d[j], y + (int64_t)rows[j] * H + v * 8);
-#pragma unroll
-        for (int j = 0; j < kChunkK; ++j)
-          if (rows[j] >= 0) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) x[q][i] = fmaf(wj[j], d[j].get(i), x[q][i]);
-          }
-      }
-    }
-  }
+  add_token_slots<VPT, kEarly ? 16 : 8>(y, row_of_slot, w, t, k, H, threadIdx.x, nthreads, x, wsum,
+                                        lost);
   float ss = 0.f;
 #pragma unroll
   for (int q = 0; q < VPT; ++q) {
     const int v = threadIdx.x + q * nthreads;
     if (v < nvec) {
-      Vec8<T> rs;
-      LOAD(rs, residual + (int64_t)t * H + v * 8);
-      Vec8<T> sh;
-      if (shared) LOAD(sh, shared + (int64_t)t * H + v * 8);
+      if (!kEarly) load_rs(q);
       Vec8<T> xo;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         // sum_j w_j * (y_j + s) = sum_j w_j y_j + (sum_j w_j) s
         float xv = x[q][i];
-        if (shared) xv = fmaf(wsum, sh.get(i), xv);
-        xv = lost ? NAN : xv + rs.get(i);
+        if (shared) xv = fmaf(wsum, sh[q].get(i), xv);
+        xv = lost ? NAN : xv + rs[q].get(i);
         x[q][i] = xv;
         ss = fmaf(xv, xv, ss);
         xo.set(i, xv);

@@ -17,6 +17,10 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kMaxExperts = 1024;
+// Buffer resources: word-3 flags of a raw (unswizzled, stride 0) buffer and
+// the non-temporal cache policy of buffer loads.
+constexpr int kBufferFlags = 0x00020000;
+constexpr int kCachePolicyNT = 2;
 
 __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(f16 v) { return (float)v; }
@@ -52,6 +56,14 @@ struct Vec8 {
     u32x4* q = reinterpret_cast<u32x4*>(p);
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) __builtin_nontemporal_store(__builtin_bit_cast(u32x4, raw[i]), q + i);
+  }
+  // Streaming load at byte offset `off` of a buffer resource; an offset past
+  // the resource's range reads zeros and touches no memory.
+  __device__ __forceinline__ void load_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i)
+      raw[i] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16u * (uint32_t)i, 0, kCachePolicyNT));
   }
   __device__ __forceinline__ float get(int i) const {
     return to_f32(reinterpret_cast<const T*>(raw)[i]);

@@ -110,6 +110,9 @@ def test_combine_and_norm_validation():
     assert c(FAKE, FAKE + 2**20, FAKE + 2**21, 0, 16, 0, 64, 2, FAKE + 2**22, None) == S["MOE_ERROR_SHAPE"]
     assert c(FAKE, FAKE + 2**20, FAKE + 2**21, 9, 16, 2, 64, 2, FAKE + 2**22, None) == S["MOE_ERROR_DTYPE"]
     assert c(FAKE, FAKE + 2**20, FAKE + 2**21, 0, 16, 2, 60, 2, FAKE + 2**22, None) == S["MOE_ERROR_UNSUPPORTED"]
+    # an fp32 row of 2^29 elements is 2 GiB: past the 32-bit range of a row's buffer resource
+    assert c(FAKE, FAKE + 2**20, FAKE + 2**21, 0, 1, 1, 2**29, 0, FAKE + 2**22, None) == S["MOE_ERROR_UNSUPPORTED"]
+    assert c(FAKE, FAKE + 2**20, FAKE + 2**21, 0, 1, 1, 2**28, 0, FAKE + 2**22, None) != S["MOE_ERROR_UNSUPPORTED"]
     assert c(FAKE, FAKE + 2**20, FAKE + 2**21, 0, 16, 2, 64, 2, FAKE + 64, None) == S["MOE_ERROR_ARGUMENT"]
     n = lib.moe_combine_add_rmsnorm
     args = [FAKE, FAKE + 2**20, FAKE + 2**21, 0, None, FAKE + 2**22, FAKE + 2**23, 1e-6, 16, 2, 64,
