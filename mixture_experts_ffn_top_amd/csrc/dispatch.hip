@@ -11,7 +11,10 @@
 //                plus its rank among equal ids in the chunk (a match mask
 //                built from one ballot per id bit).
 // Rows inside an expert therefore follow increasing flat slot t*k+j, the same
-// for every run. A fourth launch gathers the token rows into x_disp.
+// for every run. Up to kOneBlockSlots slots the same three steps run in one
+// workgroup, with its 16 wavefronts in the role of the blocks and the counts
+// in LDS (one launch instead of three). A further launch gathers the token
+// rows into x_disp.
 #include "common.h"
 #include "kernels.h"
 
@@ -20,16 +23,62 @@ namespace {
 
 constexpr int kMaxBlocks = 256;
 
-// Expert id slot s is dispatched to, or E for "not dispatched": ids >= E and
-// slots switched off by the activity mask (mask_dims 1: one flag per token,
-// 2: one per slot; 0: no mask) are not dispatched.
-__device__ __forceinline__ uint32_t slot_expert(const uint32_t* idx, int64_t s, int E,
-                                                const uint8_t* active, int mask_dims, int k) {
-  uint32_t e = idx[s];
-  if (e > (uint32_t)E) e = (uint32_t)E;
-  if (mask_dims == 1 && !active[s / k]) e = (uint32_t)E;
-  if (mask_dims == 2 && !active[s]) e = (uint32_t)E;
-  return e;
+// The ids of kIdBatch chunks of 64 slots starting at c, read at once
+// (indices clamped into range, so no load waits behind a branch); slots at or
+// past s_end, ids > E and inactive slots give E.
+constexpr int kIdBatch = 4;
+
+__device__ __forceinline__ void load_ids(const uint32_t* __restrict__ idx, int64_t c, int s_end,
+                                         int n_slots, int E, const uint8_t* __restrict__ active,
+                                         int mask_dims, int k, uint32_t (&e)[kIdBatch]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int sc[kIdBatch];  // clamped below n_slots: fits in int
+#pragma unroll
+  for (int b = 0; b < kIdBatch; ++b) {
+    const int64_t s = c + b * kWave + lane;
+    sc[b] = s < n_slots ? (int)s : n_slots - 1;
+    e[b] = idx[sc[b]];
+  }
+  uint8_t on[kIdBatch];
+#pragma unroll
+  for (int b = 0; b < kIdBatch; ++b) on[b] = mask_dims ? active[mask_dims == 1 ? sc[b] / k : sc[b]] : 1;
+#pragma unroll
+  for (int b = 0; b < kIdBatch; ++b) {
+    const int64_t s = c + b * kWave + lane;
+    if (e[b] > (uint32_t)E || !on[b] || s >= s_end) e[b] = (uint32_t)E;
+  }
+}
+
+// Rows of a batch of ids, in slot order: an expert's running row (run[e])
+// plus the rank among equal ids of the same 64-slot chunk, found with one
+// ballot per id bit; the lane holding the last equal id advances run[e]. All
+// lanes read run[] before that write (one wavefront, LDS operations in order).
+__device__ __forceinline__ void place_batch(const uint32_t (&ev)[kIdBatch], int64_t c, int s_end,
+                                            int E, int nbits, int* run,
+                                            int32_t* __restrict__ slot_of_row,
+                                            int32_t* __restrict__ row_of_slot) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int b = 0; b < kIdBatch; ++b) {
+    const int64_t s = c + b * kWave + lane;
+    const bool in = s < s_end;
+    const uint32_t e = ev[b];
+    uint64_t same = __ballot(in);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool v = (e >> bit) & 1u;
+      const uint64_t m = __ballot(v);
+      same &= v ? m : ~m;
+    }
+    const int rank = __popcll(same & lanemask_lt());
+    const bool last = (same >> lane) == 1ull;  // no equal id in a higher lane
+    int row = -1;
+    if (in && e < (uint32_t)E) {
+      row = run[e] + rank;
+      slot_of_row[row] = (int32_t)s;
+    }
+    if (in) row_of_slot[s] = row;
+    if (in && e < (uint32_t)E && last) run[e] = row + 1;
+  }
 }
 
 __global__ __launch_bounds__(kWave) void hist_kernel(const uint32_t* __restrict__ idx, int n_slots,
@@ -40,36 +89,55 @@ __global__ __launch_bounds__(kWave) void hist_kernel(const uint32_t* __restrict_
   __shared__ int cnt[kMaxExperts];
   for (int e = threadIdx.x; e < E; e += kWave) cnt[e] = 0;
   __syncthreads();
-  const int64_t s0 = (int64_t)blockIdx.x * per_block;
-  for (int i = threadIdx.x; i < per_block; i += kWave) {
-    const int64_t s = s0 + i;
-    if (s < n_slots) {
-      const uint32_t e = slot_expert(idx, s, E, active, mask_dims, k);
-      if (e < (uint32_t)E) atomicAdd(&cnt[e], 1);
-    }
+  const int s0 = (int)std::min<int64_t>((int64_t)blockIdx.x * per_block, n_slots);
+  const int s_end = (int)std::min<int64_t>((int64_t)s0 + per_block, n_slots);
+  for (int64_t c = s0; c < s_end; c += kIdBatch * kWave) {
+    uint32_t e[kIdBatch];
+    load_ids(idx, c, s_end, n_slots, E, active, mask_dims, k, e);
+#pragma unroll
+    for (int b = 0; b < kIdBatch; ++b)
+      if (e[b] < (uint32_t)E) atomicAdd(&cnt[e[b]], 1);
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += kWave) hist[(int64_t)blockIdx.x * E + e] = cnt[e];
 }
 
-// One block of 1024 threads, thread e owns expert e.
+// One block of 1024 threads, thread e owns expert e. The per-block counts are
+// read kScanBatch blocks at a time (block index clamped into range, so the
+// loads of a batch are all in flight together): once for the totals, once
+// more to write each block's first row.
+constexpr int kScanBatch = 16;
+
 __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ hist, int n_blocks,
                                                      int E, int32_t* __restrict__ offsets) {
   const int e = threadIdx.x;
+  const bool mine = e < E;
+  const int ec = min(e, E - 1);
   int total = 0;
-  if (e < E) {
-    for (int b = 0; b < n_blocks; ++b) {
-      const int c = hist[(int64_t)b * E + e];
-      hist[(int64_t)b * E + e] = total;
-      total += c;
-    }
+  for (int b0 = 0; b0 < n_blocks; b0 += kScanBatch) {
+    int c[kScanBatch];
+#pragma unroll
+    for (int i = 0; i < kScanBatch; ++i) c[i] = hist[(int64_t)min(b0 + i, n_blocks - 1) * E + ec];
+#pragma unroll
+    for (int i = 0; i < kScanBatch; ++i)
+      if (mine && b0 + i < n_blocks) total += c[i];
   }
   int all = 0;
   const int off = block_exclusive_scan(total, &all);
-  if (e < E) {
-    offsets[e] = off;
-    for (int b = 0; b < n_blocks; ++b) hist[(int64_t)b * E + e] += off;
+  int run = off;
+  for (int b0 = 0; b0 < n_blocks; b0 += kScanBatch) {
+    int c[kScanBatch];
+#pragma unroll
+    for (int i = 0; i < kScanBatch; ++i) c[i] = hist[(int64_t)min(b0 + i, n_blocks - 1) * E + ec];
+#pragma unroll
+    for (int i = 0; i < kScanBatch; ++i) {
+      if (mine && b0 + i < n_blocks) {
+        hist[(int64_t)(b0 + i) * E + e] = run;
+        run += c[i];
+      }
+    }
   }
+  if (mine) offsets[e] = off;
   if (e == 0) offsets[E] = all;
 }
 
@@ -83,30 +151,73 @@ __global__ __launch_bounds__(kWave) void scatter_kernel(const uint32_t* __restri
   __shared__ int run[kMaxExperts];
   for (int e = threadIdx.x; e < E; e += kWave) run[e] = base[(int64_t)blockIdx.x * E + e];
   __syncthreads();
-  const int lane = threadIdx.x;
   const int nbits = 32 - __clz(E);  // ids 0..E (E = "not dispatched") fit in nbits
-  const int64_t s0 = (int64_t)blockIdx.x * per_block;
-  for (int c = 0; c < per_block; c += kWave) {
-    const int64_t s = s0 + c + lane;
-    const bool in = s < n_slots;
-    const uint32_t e = in ? slot_expert(idx, s, E, active, mask_dims, k) : (uint32_t)E;
-    uint64_t same = __ballot(in);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = (e >> b) & 1u;
-      const uint64_t m = __ballot(bit);
-      same &= bit ? m : ~m;
+  const int s0 = (int)std::min<int64_t>((int64_t)blockIdx.x * per_block, n_slots);
+  const int s_end = (int)std::min<int64_t>((int64_t)s0 + per_block, n_slots);
+  for (int64_t c = s0; c < s_end; c += kIdBatch * kWave) {
+    uint32_t ev[kIdBatch];
+    load_ids(idx, c, s_end, n_slots, E, active, mask_dims, k, ev);
+    place_batch(ev, c, s_end, E, nbits, run, slot_of_row, row_of_slot);
+  }
+}
+
+// One workgroup of kOneBlockWaves wavefronts; wavefront w owns the slots
+// [w * per, (w + 1) * per) and its counts per expert live in LDS. Up to
+// kOneBlockSlots slots (measured: faster than the three launches up to 16K
+// slots, slower at 64K, where one CU walks all of them).
+constexpr int kOneBlockWaves = 16;
+constexpr int kOneBlockSlots = 16384;
+
+__global__ __launch_bounds__(kOneBlockWaves * kWave) void dispatch_one_block_kernel(
+    const uint32_t* __restrict__ idx, int n_slots, int E, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ slot_of_row, int32_t* __restrict__ row_of_slot,
+    const uint8_t* __restrict__ active, int mask_dims, int k) {
+  __shared__ int cnt[kOneBlockWaves * kMaxExperts];  // [wave][E]
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  for (int i = threadIdx.x; i < kOneBlockWaves * E; i += blockDim.x) cnt[i] = 0;
+  __syncthreads();
+  const int per = ((n_slots + kOneBlockWaves - 1) / kOneBlockWaves + kWave - 1) / kWave * kWave;
+  const int s_begin = min(wave * per, n_slots);
+  const int s_end = min(s_begin + per, n_slots);
+  int* my = cnt + wave * E;
+
+  // 1. counts of this wavefront's slots per expert
+  for (int64_t c = s_begin; c < s_end; c += kIdBatch * kWave) {
+    uint32_t e[kIdBatch];
+    load_ids(idx, c, s_end, n_slots, E, active, mask_dims, k, e);
+#pragma unroll
+    for (int b = 0; b < kIdBatch; ++b)
+      if (e[b] < (uint32_t)E) atomicAdd(&my[e[b]], 1);
+  }
+  __syncthreads();
+
+  // 2. thread e: expert e's offset and each wavefront's first row in it
+  const int e = threadIdx.x;
+  int total = 0;
+  if (e < E) {
+    for (int w = 0; w < kOneBlockWaves; ++w) {
+      const int c = cnt[w * E + e];
+      cnt[w * E + e] = total;
+      total += c;
     }
-    const int rank = __popcll(same & lanemask_lt());
-    const bool last = (same >> lane) == 1ull;  // no equal id in a higher lane
-    int row = -1;
-    if (in && e < (uint32_t)E) {
-      row = run[e] + rank;
-      slot_of_row[row] = (int32_t)s;
-    }
-    if (in) row_of_slot[s] = row;
-    // All lanes have read run[] above (same instruction stream, LDS ops in
-    // order); the last lane of each id advances that expert's counter.
-    if (in && e < (uint32_t)E && last) run[e] = row + 1;
+  }
+  int all = 0;
+  const int off = block_exclusive_scan(total, &all);
+  if (e < E) {
+    offsets[e] = off;
+    for (int w = 0; w < kOneBlockWaves; ++w) cnt[w * E + e] += off;
+  }
+  if (e == 0) offsets[E] = all;
+  __syncthreads();
+
+  // 3. rows in slot order: running row per expert plus the rank among equal
+  // ids of the chunk (as scatter_kernel)
+  const int nbits = 32 - __clz(E);
+  for (int64_t c = s_begin; c < s_end; c += kIdBatch * kWave) {
+    uint32_t ev[kIdBatch];
+    load_ids(idx, c, s_end, n_slots, E, active, mask_dims, k, ev);
+    place_batch(ev, c, s_end, E, nbits, my, slot_of_row, row_of_slot);
   }
 }
 
@@ -149,9 +260,14 @@ size_t dispatch_scratch_bytes(int64_t n_slots, int64_t E) {
 hipError_t launch_dispatch_maps(const uint32_t* indices, int n_slots, int E, int32_t* offsets,
                                 int32_t* slot_of_row, int32_t* row_of_slot, int32_t* scratch,
                                 hipStream_t s, const uint8_t* active, int mask_dims, int k) {
-  const DispatchPlan p = dispatch_plan(n_slots, E);
   if (!active) mask_dims = 0;
   if (k < 1) k = 1;
+  if (n_slots <= kOneBlockSlots) {
+    hipLaunchKernelGGL(dispatch_one_block_kernel, dim3(1), dim3(kOneBlockWaves * kWave), 0, s,
+                       indices, n_slots, E, offsets, slot_of_row, row_of_slot, active, mask_dims, k);
+    return hipGetLastError();
+  }
+  const DispatchPlan p = dispatch_plan(n_slots, E);
   hipLaunchKernelGGL(hist_kernel, dim3(p.n_blocks), dim3(kWave), 0, s, indices, n_slots, E,
                      p.slots_per_block, scratch, active, mask_dims, k);
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, scratch, p.n_blocks, E, offsets);

@@ -95,7 +95,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   const int per_split = min(total, max_tiles) * n_tiles_n;
   const int n_real = per_split * k_splits;
   const int chunk = (n_real + kXcds - 1) / kXcds;
-  for (int b = threadIdx.x; b < grid; b += blockDim.x) {
+  for (int b = blockIdx.x * blockDim.x + threadIdx.x; b < grid; b += gridDim.x * blockDim.x) {
     const int slot = b / kXcds;
     const int L = (b % kXcds) * chunk + slot;
     int4 t = make_int4(-1, 0, 0, 0);
@@ -965,7 +965,11 @@ void plan_tiles(GemmArgs& g, const ExpertsPlan& plan, int E, int dt, bool swiglu
   g.n_tiles_n = (int)tile_n(g.N, dt, swiglu);
   g.grid = (int)grid_tiles(plan.max_tiles, g.n_tiles_n, g.k_splits);
   int4* sched = static_cast<int4*>(scratch);
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, g.offsets, E, g.rows, plan.bm,
+  // Each workgroup repeats the expert scan and fills 1024 entries: the entry
+  // arithmetic (a binary search and several divisions) dominates, and one
+  // workgroup on one CU would take it in series.
+  const int blocks = std::max(1, std::min((g.grid + 1023) / 1024, 64));
+  hipLaunchKernelGGL(plan_kernel, dim3(blocks), dim3(1024), 0, s, g.offsets, E, g.rows, plan.bm,
                      plan.max_tiles, g.n_tiles_n, g.k_splits, g.grid, sched);
   g.sched = sched;
 }

@@ -17,37 +17,67 @@
 namespace moe {
 namespace {
 
-template <int G>
-__device__ __forceinline__ uint64_t group_max_u64(uint64_t v) {
-#pragma unroll
-  for (int d = 1; d < G; d <<= 1) {
-    uint32_t lo = __shfl_xor((uint32_t)v, d, G);
-    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), d, G);
-    uint64_t o = ((uint64_t)hi << 32) | lo;
-    v = o > v ? o : v;
+// Reductions over an aligned group of G lanes (G a power of two <= 64) that
+// leave every lane of the group with the result, without LDS. Each step pairs
+// a lane with one lane of the other half of its aligned block of twice the
+// span: DPP quad permutes for spans 1 and 2 (lane ^ 1, lane ^ 2), then the
+// half-row mirror (i <-> 7 - i) and the row mirror (i <-> 15 - i). Rows of 16
+// lanes are combined through readlane. Partners always lie in the lane's own
+// group, so a group switched off as a whole does not disturb the others.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppRowHalfMirror = 0x141, kDppRowMirror = 0x140;
+
+template <int kCtrl>
+__device__ __forceinline__ uint32_t xlane(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kCtrl, 0xF, 0xF, false);
+}
+template <int kCtrl>
+__device__ __forceinline__ float xlane(float v) {
+  return __uint_as_float(xlane<kCtrl>(__float_as_uint(v)));
+}
+template <int kCtrl>
+__device__ __forceinline__ uint64_t xlane(uint64_t v) {
+  return ((uint64_t)xlane<kCtrl>((uint32_t)(v >> 32)) << 32) | xlane<kCtrl>((uint32_t)v);
+}
+__device__ __forceinline__ uint32_t lane_value(uint32_t v, int l) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+__device__ __forceinline__ float lane_value(float v, int l) {
+  return __uint_as_float(lane_value(__float_as_uint(v), l));
+}
+__device__ __forceinline__ uint64_t lane_value(uint64_t v, int l) {
+  return ((uint64_t)lane_value((uint32_t)(v >> 32), l) << 32) | lane_value((uint32_t)v, l);
+}
+
+template <int G, typename V, typename Op>
+__device__ __forceinline__ V group_reduce(V v, Op op) {
+  if constexpr (G >= 2) v = op(v, xlane<kDppXor1>(v));
+  if constexpr (G >= 4) v = op(v, xlane<kDppXor2>(v));
+  if constexpr (G >= 8) v = op(v, xlane<kDppRowHalfMirror>(v));
+  if constexpr (G >= 16) v = op(v, xlane<kDppRowMirror>(v));
+  if constexpr (G >= 32) {
+    const V lo = op(lane_value(v, 0), lane_value(v, 16));
+    const V hi = op(lane_value(v, 32), lane_value(v, 48));
+    if constexpr (G == 64) v = op(lo, hi);
+    else v = __lane_id() < 32 ? lo : hi;
   }
   return v;
 }
 
 template <int G>
-__device__ __forceinline__ float group_max_f32(float v) {
-#pragma unroll
-  for (int d = 1; d < G; d <<= 1) v = fmaxf(v, __shfl_xor(v, d, G));
-  return v;
+__device__ __forceinline__ uint64_t group_max_u64(uint64_t v) {
+  return group_reduce<G>(v, [](uint64_t a, uint64_t b) { return a > b ? a : b; });
 }
-
+template <int G>
+__device__ __forceinline__ float group_max_f32(float v) {
+  return group_reduce<G>(v, [](float a, float b) { return fmaxf(a, b); });
+}
 template <int G>
 __device__ __forceinline__ float group_sum_f32(float v) {
-#pragma unroll
-  for (int d = 1; d < G; d <<= 1) v += __shfl_xor(v, d, G);
-  return v;
+  return group_reduce<G>(v, [](float a, float b) { return a + b; });
 }
-
 template <int G>
 __device__ __forceinline__ int group_or(int v) {
-#pragma unroll
-  for (int d = 1; d < G; d <<= 1) v |= __shfl_xor(v, d, G);
-  return v;
+  return (int)group_reduce<G>((uint32_t)v, [](uint32_t a, uint32_t b) { return a | b; });
 }
 
 constexpr int kRouteThreads = 256;
@@ -63,16 +93,16 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
 
   float z[VPL];
   int flags = 0;  // bit0: NaN seen, bit1: +inf seen, bit2: a value other than -inf seen
+  // Every load is issued (indices clamped into the row), then masked.
+  const int64_t row = (int64_t)min(t, T - 1) * E;
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) z[v] = to_f32(logits[row + min(gl + G * v, E - 1)]);
 #pragma unroll
   for (int v = 0; v < VPL; ++v) {
-    const int e = gl + G * v;
-    z[v] = -INFINITY;
-    if (active && e < E) {
-      z[v] = to_f32(logits[(int64_t)t * E + e]);
-      if (__builtin_isnan(z[v])) flags |= 1;
-      if (z[v] == INFINITY) flags |= 2;
-      if (z[v] != -INFINITY) flags |= 4;
-    }
+    if (!active || gl + G * v >= E) z[v] = -INFINITY;
+    if (__builtin_isnan(z[v])) flags |= 1;
+    if (z[v] == INFINITY) flags |= 2;
+    if (z[v] != -INFINITY) flags |= 4;
   }
   flags = group_or<G>(flags);
   const bool bad = (flags & 3) || !(flags & 4);
