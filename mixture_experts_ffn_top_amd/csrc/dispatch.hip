@@ -108,10 +108,44 @@ __global__ __launch_bounds__(kWave) void hist_kernel(const uint32_t* __restrict_
 // more to write each block's first row.
 constexpr int kScanBatch = 16;
 
+// When the whole table fits in LDS (kScanLds counts) it is instead staged
+// there with coalesced loads, all issued at once, and written back the same way.
+constexpr int kScanLds = 16384;
+
 __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ hist, int n_blocks,
                                                      int E, int32_t* __restrict__ offsets) {
+  __shared__ int tab[kScanLds];
   const int e = threadIdx.x;
   const bool mine = e < E;
+  const int n = n_blocks * E;
+  if (n <= kScanLds) {
+    constexpr int kPer = kScanLds / 1024;
+    int c[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) c[i] = hist[min(i * 1024 + e, n - 1)];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      if (i * 1024 + e < n) tab[i * 1024 + e] = c[i];
+    __syncthreads();
+    int total = 0;
+    if (mine)
+      for (int b = 0; b < n_blocks; ++b) total += tab[b * E + e];
+    int all = 0;
+    const int off = block_exclusive_scan(total, &all);
+    if (mine) {
+      int run = off;
+      for (int b = 0; b < n_blocks; ++b) {
+        const int cnt = tab[b * E + e];
+        tab[b * E + e] = run;
+        run += cnt;
+      }
+      offsets[e] = off;
+    }
+    if (e == 0) offsets[E] = all;
+    __syncthreads();
+    for (int i = e; i < n; i += 1024) hist[i] = tab[i];
+    return;
+  }
   const int ec = min(e, E - 1);
   int total = 0;
   for (int b0 = 0; b0 < n_blocks; b0 += kScanBatch) {

@@ -117,7 +117,7 @@ def _check_dispatch(idx, E, x, dtype):
 
 @pytest.mark.parametrize("T,k,E,H", [(1, 1, 1, 8), (37, 3, 5, 136), (300, 2, 8, 64), (16, 8, 128, 8),
                                      (4096, 8, 128, 64), (2048, 8, 256, 16), (8192, 8, 1024, 8),
-                                     (8193, 8, 64, 8), (65537, 1, 7, 8)])
+                                     (8193, 8, 64, 8), (8193, 8, 1024, 8), (65537, 1, 7, 8)])
 def test_dispatch_random(T, k, E, H):
     say("dispatch", T, k, E, H)
     g = np.random.default_rng(T + E)
