@@ -180,6 +180,9 @@ __global__ __launch_bounds__(64 * kQWaves, 3) void skinny_quant_kernel(QuantArgs
   const T* sp1 = kSwiGlu ? static_cast<const T*>(p.s1) + expert_rows * G : sp0;
   const T* op0 = p.o0 ? static_cast<const T*>(p.o0) + expert_rows * G : nullptr;
   const T* op1 = kSwiGlu ? (p.o1 ? static_cast<const T*>(p.o1) + expert_rows * G : nullptr) : op0;
+  const bool has_o0 = op0 != nullptr, has_o1 = op1 != nullptr;
+  const T* ob0 = has_o0 ? op0 : sp0;
+  const T* ob1 = has_o1 ? op1 : sp1;
 
   T* C = static_cast<T*>(p.c);
   for (int rg = r_begin; rg < r_end; rg += kQTokens) {
@@ -195,18 +198,28 @@ __global__ __launch_bounds__(64 * kQWaves, 3) void skinny_quant_kernel(QuantArgs
 
     // Scale and offset*scale of tile t for the group holding the 128
     // input channels of the K-iteration at kb (groups are multiples of 128 long).
+    // Every load is issued (row and group clamped into range), then masked,
+    // so none waits behind a branch.
     auto load_sc = [&](int kb, float (&sc)[4], float (&os)[4]) {
       const int grp = min(kb, K - 1) / gsz;
+      T sv[4], ov[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const bool up = kSwiGlu && t >= 2;
-        const int n = wrow[t];
-        float s = 0.f, o = 0.f;
-        if (n < N && kb < k_hi) {
-          s = to_f32((up ? sp1 : sp0)[(int64_t)n * G + grp]);
-          const T* op = up ? op1 : op0;
-          o = op ? to_f32(op[(int64_t)n * G + grp]) : 0.f;
-        }
+        const int64_t at = (int64_t)min(wrow[t], N - 1) * G + grp;
+        sv[t] = (up ? sp1 : sp0)[at];
+        ov[t] = (up ? ob1 : ob0)[at];  // the scales stand in for absent offsets
+      }
+      // Masked by clearing the bits (+0), not by a select the compiler would
+      // turn back into a branch around the load.
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const bool up = kSwiGlu && t >= 2;
+        const bool on = wrow[t] < N && kb < k_hi;
+        const uint16_t ms = on ? 0xFFFFu : 0u;
+        const uint16_t mo = on && (up ? has_o1 : has_o0) ? 0xFFFFu : 0u;
+        const float s = to_f32(__builtin_bit_cast(T, (uint16_t)(__builtin_bit_cast(uint16_t, sv[t]) & ms)));
+        const float o = to_f32(__builtin_bit_cast(T, (uint16_t)(__builtin_bit_cast(uint16_t, ov[t]) & mo)));
         sc[t] = s;
         os[t] = (kBits == 8 ? o : o - 8.0f) * s;  // INT4 codes enter as q + 8
       }
