@@ -19,9 +19,11 @@
 // slice of the tile list, so the ~32 workgroups resident on one XCD at a time
 // are neighbours in the list. Inside an expert the list takes groups of up to
 // 8 M-tiles, and inside such a group runs of N-tiles wide enough that one run
-// covers about 32 tiles (4 M-tiles x 8 N-tiles, 5 x 6, 1 x 32 ...): the
-// tiles resident together share their weight tiles and activation tiles
-// through that XCD's L2, and a run never mixes two experts' weights.
+// covers about 8 tiles (4 M-tiles x 2 N-tiles, 8 x 1, 1 x 8 ...), N first
+// inside a run: the ~32 tiles resident together (four consecutive runs) share
+// their weight tiles and activation tiles through that XCD's L2, and a run
+// never mixes two experts' weights. (Runs of 8 measured about 1 % faster than
+// one run of 32 covering the same tiles.)
 //
 // bf16/f16 kernel (gfx950 MFMA 32x32x16): workgroup tile 256 x kBNB, K
 // staged 32 at a time; 512 threads = 8 wavefronts as 4 (M) x 2 (N), 64 x
@@ -63,7 +65,7 @@ constexpr int kBM = 256;      // rows per M-tile (MFMA path)
 constexpr int kBK = 64;       // K per LDS stage
 constexpr int kBMSimt = 64;   // rows per M-tile (fp32 path)
 constexpr int kXcds = 8;
-constexpr int kResident = 32;  // workgroups resident on one XCD (one per CU)
+constexpr int kRunTiles = 8;   // tiles per run of the schedule order
 constexpr int kGroupM = 8;     // M-tiles per schedule group
 // Third dword of a raw buffer resource on gfx9-family parts (no format, no swizzle).
 constexpr int kRsrcFlags = 0x00020000;
@@ -113,7 +115,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
       const int local = idx - s_first[ex] * n_tiles_n;
       const int me = s_first[ex + 1] - s_first[ex];
       const int mg = min(me, kGroupM);
-      const int ng = max(1, kResident / mg);
+      const int ng = max(1, kRunTiles / mg);
       const int mgi = local / (mg * n_tiles_n);
       const int mgw = min(mg, me - mgi * mg);
       const int j = local - mgi * mg * n_tiles_n;
