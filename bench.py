@@ -26,6 +26,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MoE fwd tokens/s; expert GEMM TFLOP/s (% MFMA peak); combine GB/s (% HBM)"
+# Grouped-limited sigmoid router of --router grouped (the DeepSeek-V3 family's settings).
+GROUPED = {"groups": 8, "selected_groups": 4, "group_top_two": True, "scale": 2.5}
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
 # Which roof bounds the gate/up GEMM of each workload (flops per weight byte:
@@ -85,6 +87,12 @@ def main():
                     help="time the forward with weight-only INT8 or INT4 experts (decode-sized workloads)")
     ap.add_argument("--groups", type=int, default=0,
                     help="scale groups along K for --quant (default 1 for INT8, 4 for INT4)")
+    ap.add_argument("--router", choices=("softmax", "grouped"), default="softmax",
+                    help="grouped: the grouped-limited sigmoid router (8 groups, 4 kept, top-two "
+                         "group scores, a correction bias, scale 2.5) in place of the softmax top-k")
+    ap.add_argument("--special", action="store_true",
+                    help="E/32 zero, E/32 copy and E/32 constant experts after the E experts and a "
+                         "per-token activity mask (7/8 of the tokens active) in the combine")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 5 times (the "
                          "reference kernel for scaling HBM byte counters), then exit")
@@ -126,16 +134,35 @@ def main():
 
     # ---- inputs (host generation, then resident in HBM) --------------------
     t0 = time.time()
-    z = I.logits_for(w)
+    grouped = args.router == "grouped"
+    if (grouped or args.special) and (args.quant or args.train):
+        raise SystemExit("--router grouped and --special time the forward; not with --quant / --train")
+    if grouped and args.special:
+        raise SystemExit("--router grouped and --special are separate lines")
+    if grouped and (E % GROUPED["groups"] or E // GROUPED["groups"] < 2
+                    or k > GROUPED["selected_groups"] * (E // GROUPED["groups"])):
+        raise SystemExit("--router grouped needs E divisible by 8 with at least two experts a group "
+                         "(top-two group scores) and top_k within the kept groups")
     x = I.tokens_for(w)
+    bias = I.router_bias(w) if grouped else None
+    n_sp = max(1, E // 32)
+    if args.special:
+        z, sp_a1, sp_a2, sp_v, sp_active = I.special_expert_inputs(w, n_sp, n_sp, n_sp)
+    else:
+        z = I.logits_for(w)
     if args.quant:
         return run_quant(args, w, x, z, to_dev)
     n_cpu = min(args.cpu_tokens or CPU_TOKENS[args.workload], T)
     keep = set()
     if not args.no_cpu_baseline:
         from oracle import moe_oracle as O
-        idx_s, _ = O.route(z[:n_cpu], "f32", k, w.renormalize)
-        keep = set(int(e) for e in idx_s.ravel())
+        if grouped:
+            idx_s, _ = O.route_sigmoid_grouped(z[:n_cpu], "f32", bias, k, GROUPED["groups"],
+                                               GROUPED["selected_groups"], True, w.renormalize,
+                                               GROUPED["scale"])
+        else:
+            idx_s, _ = O.route(z[:n_cpu], "f32", k, w.renormalize)
+        keep = set(int(e) for e in idx_s.ravel() if int(e) < E)
     wt = {}
     kept = {e: {} for e in keep}
     for name in ("w_gate", "w_up", "w_down"):
@@ -165,39 +192,67 @@ def main():
                      dtype=torch.uint8, device=dev)
 
     stages = ["route", "dispatch", "gate_up", "down", "combine"]
-    if w.epilogue:
-        # combine fused with the shared-expert term, residual Add and RMSNorm:
-        # the split calls, with events recorded between them on this stream
-        sh, res, gam = I.epilogue_inputs(w)
-        shd, resd, gamd = to_dev(sh), to_dev(res), to_dev(gam, "f32")
+    if w.epilogue or grouped or args.special:
+        # the split calls, with events recorded between them on this stream:
+        # the combine fused with the shared-expert term, residual Add and
+        # RMSNorm (epilogue workloads), the grouped router, special experts
         offsets_d = torch.empty(E + 1, dtype=torch.int32, device=dev)
         sor = torch.empty(R, dtype=torch.int32, device=dev)
         ros = torch.empty(R, dtype=torch.int32, device=dev)
         h = torch.empty((R, I_), dtype=td, device=dev)
         y = torch.empty((R, H), dtype=td, device=dev)
-        yo = torch.empty((T, H), dtype=td, device=dev)
-        rstd = torch.empty(T, dtype=torch.float32, device=dev)
         ws_d = torch.empty(moe.moe_dispatch_workspace_size(T, k, E), dtype=torch.uint8, device=dev)
         ws_g = torch.empty(moe.moe_experts_gemm_workspace_size(R, E, H, I_, td), dtype=torch.uint8,
                            device=dev)
-        stages[-1] = "combine_add_rmsnorm"
+        if w.epilogue:
+            sh, res, gam = I.epilogue_inputs(w)
+            shd, resd, gamd = to_dev(sh), to_dev(res), to_dev(gam, "f32")
+            yo = torch.empty((T, H), dtype=td, device=dev)
+            rstd = torch.empty(T, dtype=torch.float32, device=dev)
+            stages[-1] = "combine_add_rmsnorm"
+        if args.special:
+            a1d, a2d, vd = to_dev(sp_a1), to_dev(sp_a2), to_dev(sp_v)
+            actd = torch.from_numpy(sp_active).to(dev)
+            stages[-1] = "combine_special" + ("_add_rmsnorm" if w.epilogue else "")
+        bd = to_dev(bias, "f32") if grouped else None
 
         def step(ev=None):
             def mark(i):
                 if ev is not None:
                     ev[i].record()
             mark(0)
-            moe.moe_route(zd, k, w.renormalize, indices=idx, weights=wts)
+            if grouped:
+                moe.moe_route_sigmoid_grouped(zd, k, GROUPED["groups"], GROUPED["selected_groups"],
+                                              GROUPED["group_top_two"], w.renormalize,
+                                              GROUPED["scale"], bias=bd, indices=idx, weights=wts)
+            else:
+                moe.moe_route(zd, k, w.renormalize, indices=idx, weights=wts)
             mark(1)
-            moe.moe_dispatch(idx, E, ws=ws_d, offsets=offsets_d, slot_of_row=sor, row_of_slot=ros)
+            if args.special:
+                moe.moe_dispatch_masked(idx, E, active=actd, ws=ws_d, offsets=offsets_d,
+                                        slot_of_row=sor, row_of_slot=ros)
+            else:
+                moe.moe_dispatch(idx, E, ws=ws_d, offsets=offsets_d, slot_of_row=sor, row_of_slot=ros)
             mark(2)
             moe.moe_experts_gate_up(xd, offsets_d, wt["w_gate"], wt["w_up"], row_map=sor, map_div=k,
                                     rows=R, h=h, ws=ws_g)
             mark(3)
             moe.moe_experts_down(h, offsets_d, wt["w_down"], expert_out=y, ws=ws_g)
             mark(4)
-            moe.moe_combine_add_rmsnorm(y, ros, wts, resd, gamd, w.eps, shared=shd, y=yo, x_out=out,
-                                        rstd=rstd)
+            if args.special:
+                moe.moe_combine_special(y, ros, idx, wts, E, n_sp, n_sp, n_sp, ori_x=xd,
+                                        const_alpha1=a1d, const_alpha2=a2d, const_v=vd, active=actd,
+                                        shared=shd if w.epilogue else None,
+                                        out=yo if w.epilogue else out,
+                                        residual=resd if w.epilogue else None,
+                                        gamma=gamd if w.epilogue else None, eps=w.eps,
+                                        x_out=out if w.epilogue else None,
+                                        rstd=rstd if w.epilogue else None)
+            elif w.epilogue:
+                moe.moe_combine_add_rmsnorm(y, ros, wts, resd, gamd, w.eps, shared=shd, y=yo,
+                                            x_out=out, rstd=rstd)
+            else:
+                moe.moe_combine(y, ros, wts, out=out)
             mark(5)
     else:
         def step(ev=None):
@@ -221,8 +276,12 @@ def main():
     t_end = time.perf_counter()
     elapsed = t_end - t_start
     log(f"timed {args.steps} steps in {elapsed:.3f}s")
-    offsets = torch.from_numpy(np.concatenate([[0], np.cumsum(np.bincount(idx.cpu().numpy().ravel(),
-                                                                            minlength=E))])).int()
+    if w.epilogue or grouped or args.special:
+        offsets = offsets_d.cpu()
+    else:
+        offsets = torch.from_numpy(np.concatenate([[0], np.cumsum(np.bincount(idx.cpu().numpy().ravel(),
+                                                                                minlength=E))])).int()
+    R_disp = int(offsets[E])  # dispatched rows (fewer than T*k with special experts or the mask)
 
     stage_ms = {name: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
                 for i, name in enumerate(stages)}
@@ -233,12 +292,12 @@ def main():
     es = 2 if w.dtype == "bf16" else 4
     counts = np.diff(offsets.cpu().numpy())
     touched = int((counts > 0).sum())
-    flops_gate_up = 4.0 * R * H * I_  # two [R,H]x[H,I] products per launch
-    flops_down = 2.0 * R * H * I_
+    flops_gate_up = 4.0 * R_disp * H * I_  # two [R,H]x[H,I] products per launch
+    flops_down = 2.0 * R_disp * H * I_
     # bytes a launch must move at least: touched experts' weights, its input
     # rows and its output rows
-    bytes_gate_up = touched * 2 * I_ * H * es + T * H * es + R * I_ * es
-    bytes_down = touched * H * I_ * es + R * I_ * es + R * H * es
+    bytes_gate_up = touched * 2 * I_ * H * es + T * H * es + R_disp * I_ * es
+    bytes_down = touched * H * I_ * es + R_disp * I_ * es + R_disp * H * es
     gu_s = stage_ms["gate_up"] / 1e3
     bound = BOUND[args.workload]
     if bound == "hbm":
@@ -258,7 +317,16 @@ def main():
                 "algorithmic_per_launch": flops_gate_up if bound != "hbm" else bytes_gate_up}
     gemm_s = (stage_ms["gate_up"] + stage_ms["down"]) / 1e3
     expert_tflops = (flops_gate_up + flops_down) / gemm_s / 1e12
-    if w.epilogue:  # expert rows, weights, maps, shared, residual, gamma in; y, x_out, rstd out
+    if args.special:
+        # dispatched expert rows; the token row once for each token with a
+        # copy or constant slot; the constant experts' rows; ids, weights,
+        # maps and the mask; then as below
+        ids = idx.cpu().numpy().astype(np.int64)
+        on = sp_active.astype(bool)[:, None]
+        cc = ((ids >= E + n_sp) & (ids < E + 3 * n_sp) & on).any(axis=1).sum()
+        comb_bytes = R_disp * H * es + int(cc) * H * es + n_sp * H * es + R * 12 + T
+        comb_bytes += (4 * T * H * es + 4 * H + 4 * T) if w.epilogue else T * H * es
+    elif w.epilogue:  # expert rows, weights, maps, shared, residual, gamma in; y, x_out, rstd out
         comb_bytes = R * H * es + R * 4 + R * 4 + 4 * T * H * es + 4 * H + 4 * T
     else:
         comb_bytes = R * H * es + R * 4 + R * 4 + T * H * es
@@ -272,6 +340,11 @@ def main():
         "combine_frac_hbm": round(comb_gbs / PEAK_HBM_GBS, 4),
         "experts_touched": touched,
     }
+    if grouped:  # the grouped router's own kernel: logits, bias in; ids, weights out
+        route_bytes = 4 * T * E + 4 * E + 8 * T * k
+        extra["route_gbs"] = round(route_bytes / (stage_ms["route"] / 1e3) / 1e9, 1)
+    if args.special:
+        extra["rows_dispatched"] = R_disp
 
     # ---- CPU baseline: the oracle on the first tokens of the workload -----
     cpu = None
@@ -281,11 +354,33 @@ def main():
         wo = lambda e: (kept[e]["w_gate"], kept[e]["w_up"], kept[e]["w_down"])  # noqa: E731
         log(f"cpu baseline: oracle on {n_cpu} tokens")
         c0 = time.perf_counter()
-        O.forward(x[:n_cpu], z[:n_cpu], "f32", k, w.renormalize, wo, E, w.dtype)
+        xs, zs = x[:n_cpu], z[:n_cpu]
+        if grouped:
+            O.forward_sigmoid_grouped(xs, zs, "f32", bias, k, GROUPED["groups"],
+                                      GROUPED["selected_groups"], GROUPED["group_top_two"],
+                                      w.renormalize, GROUPED["scale"], wo, E, w.dtype)
+            what = "grouped sigmoid route, dispatch, fp64 SwiGLU experts, combine"
+        elif args.special:
+            ids_s, wts_s = O.route(zs, "f32", k, w.renormalize)
+            act_s = sp_active[:n_cpu]
+            d_s = O.dispatch(ids_s, E, xs, active=act_s)
+            y_s = O.experts_forward_dispatched(d_s["x_disp"], d_s["offsets"], wo, w.dtype)
+            if y_s is None:
+                y_s = O.round_to(np.zeros((0, H)), w.dtype)
+            sp_args = (y_s, d_s["row_of_slot"], ids_s, wts_s, "f32", n_cpu, k, w.dtype, E, n_sp, n_sp,
+                       n_sp, xs, sp_a1, sp_a2, sp_v, act_s)
+            if w.epilogue:
+                sh_s, res_s, gam_s = I.epilogue_inputs(w)
+                O.combine_add_rmsnorm_special(res_s[:n_cpu], gam_s, w.eps, *sp_args, shared=sh_s[:n_cpu])
+            else:
+                O.combine_special(*sp_args)
+            what = "route over experts and special experts, masked dispatch, fp64 SwiGLU experts, special combine"
+        else:
+            O.forward(xs, zs, "f32", k, w.renormalize, wo, E, w.dtype)
+            what = "route, dispatch, fp64 SwiGLU experts, combine"
         c_el = time.perf_counter() - c0
         cpu = {"value": round(n_cpu / c_el, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-               "sample": f"first {n_cpu} of {T} tokens of {args.workload}; route, dispatch, "
-                         f"fp64 SwiGLU experts, combine; {c_el:.1f}s wall"}
+               "sample": f"first {n_cpu} of {T} tokens of {args.workload}; {what}; {c_el:.1f}s wall"}
 
     res = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -296,6 +391,13 @@ def main():
                    "renormalize": w.renormalize, "logits_dtype": "f32"},
         "roofline": roofline, "cpu_baseline": cpu,
     }
+    if grouped:
+        res["config"]["router"] = dict(GROUPED, kind="sigmoid_grouped", bias="N(0, 0.05^2)")
+        res["metric"] = METRIC + "; grouped-limited sigmoid router"
+    if args.special:
+        res["config"]["special_experts"] = {"zero": n_sp, "copy": n_sp, "const": n_sp,
+                                            "active_tokens": int(sp_active.sum())}
+        res["metric"] = METRIC + "; special experts and activity mask in the combine"
     res.update(extra)
     print(json.dumps(res), flush=True)
 

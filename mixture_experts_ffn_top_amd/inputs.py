@@ -217,3 +217,28 @@ def epilogue_inputs(w: Workload):
     residual = store(normal(w.seed, "residual", (w.T, w.H)), w.dtype)
     gamma = stream(w.seed, "gamma").uniform(0.5, 1.5, w.H).astype(np.float32)
     return shared, residual, gamma
+
+
+def router_bias(w: Workload) -> np.ndarray:
+    """Correction bias of the grouped-limited sigmoid router: fp32 [E] ~ N(0, 0.05^2)."""
+    return (stream(w.seed, "router_bias").standard_normal(w.E) * 0.05).astype(np.float32)
+
+
+def special_expert_inputs(w: Workload, n_zero: int, n_copy: int, n_const: int,
+                          active_frac: float = 0.875):
+    """Routing over the E experts plus n_zero zero, n_copy copy and n_const
+    constant experts (ids E ..), for a forward with special experts:
+    logits fp32 [T, E + n_zero + n_copy + n_const] (gapped like logits_for),
+    alpha1 and alpha2 [n_const] ~ U(0.5, 1.5) and v [n_const, H] ~ N(0, 1) in
+    the model dtype, and a per-token activity mask (uint8 [T]) whose first
+    round(active_frac * T) tokens are active."""
+    n_ids = w.E + n_zero + n_copy + n_const
+    z = gapped_logits(w.seed, w.T, n_ids, w.top_k, name="logits_special")
+    g = stream(w.seed, "special_consts", n_zero, n_copy, n_const)
+    a1 = store(g.uniform(0.5, 1.5, n_const).astype(np.float32), w.dtype)
+    a2 = store(g.uniform(0.5, 1.5, n_const).astype(np.float32), w.dtype)
+    v = store(normal(w.seed, "special_v", (n_const, w.H)), w.dtype)
+    active = np.zeros(w.T, dtype=np.uint8)
+    active[: int(round(active_frac * w.T))] = 1
+    return z, a1, a2, v, active
+

@@ -149,7 +149,8 @@ def moe_dispatch(indices, E: int, x=None, with_x_disp: bool = True, ws=None, off
     return dict(offsets=offsets, slot_of_row=sor, row_of_slot=ros, x_disp=x_disp)
 
 
-def moe_dispatch_masked(indices, E: int, active=None, x=None, with_x_disp: bool = True, ws=None):
+def moe_dispatch_masked(indices, E: int, active=None, x=None, with_x_disp: bool = True, ws=None,
+                        offsets=None, slot_of_row=None, row_of_slot=None):
     """moe_dispatch with an activity mask: active None, uint8/bool [T] (per token)
     or [T, k] (per slot). Returns the same dict as moe_dispatch."""
     T, k = indices.shape
@@ -157,9 +158,9 @@ def moe_dispatch_masked(indices, E: int, active=None, x=None, with_x_disp: bool 
     H = x.shape[1] if x is not None else 0
     dt = dtype_code(x.dtype) if x is not None else BF16
     x_disp = torch.empty((T * k, H), dtype=x.dtype, device=dev) if (x is not None and with_x_disp) else None
-    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
-    sor = torch.empty(T * k, dtype=torch.int32, device=dev)
-    ros = torch.empty(T * k, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev) if offsets is None else offsets
+    sor = torch.empty(T * k, dtype=torch.int32, device=dev) if slot_of_row is None else slot_of_row
+    ros = torch.empty(T * k, dtype=torch.int32, device=dev) if row_of_slot is None else row_of_slot
     mask_dims, act = _mask(active)
     if ws is None:
         ws = _workspace(moe_dispatch_workspace_size(T, k, E), dev)
@@ -179,7 +180,7 @@ def _mask(active):
 def moe_combine_special(expert_out, row_of_slot, indices, weights, E: int, zero_num: int = 0,
                         copy_num: int = 0, const_num: int = 0, ori_x=None, const_alpha1=None,
                         const_alpha2=None, const_v=None, active=None, shared=None, out=None,
-                        residual=None, gamma=None, eps: float = 1e-6):
+                        residual=None, gamma=None, eps: float = 1e-6, x_out=None, rstd=None):
     """Combine with special experts (ids E.. : zero, copy, constant) and an
     activity mask. Without residual returns out [T, H]; with residual and gamma
     the residual Add + RMSNorm follow and (y, x_out, rstd) is returned."""
@@ -197,8 +198,8 @@ def moe_combine_special(expert_out, row_of_slot, indices, weights, E: int, zero_
         _check(lib().moe_combine_special(*args_head, _ptr(out), _stream()), "moe_combine_special")
         return out
     y = torch.empty((T, H), dtype=expert_out.dtype, device=dev) if out is None else out
-    x_out = torch.empty((T, H), dtype=expert_out.dtype, device=dev)
-    rstd = torch.empty(T, dtype=torch.float32, device=dev)
+    x_out = torch.empty((T, H), dtype=expert_out.dtype, device=dev) if x_out is None else x_out
+    rstd = torch.empty(T, dtype=torch.float32, device=dev) if rstd is None else rstd
     _check(lib().moe_combine_add_rmsnorm_special(*args_head, _ptr(residual), _ptr(gamma), float(eps),
                                                  _ptr(y), _ptr(x_out), _ptr(rstd), _stream()),
            "moe_combine_add_rmsnorm_special")

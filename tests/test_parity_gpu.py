@@ -435,6 +435,65 @@ def test_workload_with_rmsnorm_epilogue_full_size():
     assert_close(host(rs)[sample], rr, "f32", "rstd")
 
 
+def test_special_experts_workload_full_size():
+    """The DeepSeek-V3-shaped workload with E/32 zero, E/32 copy and E/32
+    constant experts after the E experts and a per-token activity mask (the
+    first 7/8 of the tokens active), through the calls bench.py --special
+    times: route over every id -> masked dispatch -> gate/up -> down ->
+    special combine + Add + RMSNorm; sampled tokens against the oracle."""
+    w = I.workload("dsv3_share_rmsnorm_bf16")
+    T, k, E, H = w.T, w.top_k, w.E, w.H
+    n = E // 32
+    z, a1, a2, v, active = I.special_expert_inputs(w, n, n, n)
+    x = I.tokens_for(w)
+    idx_r, w_r = O.route(z, "f32", k, w.renormalize)
+    on = active.astype(bool)
+    cc = np.flatnonzero(((idx_r >= E + n) & (idx_r < E + 3 * n)).any(axis=1) & on)
+    zr = np.flatnonzero((idx_r >= E) & (idx_r < E + n)).tolist()
+    g = np.random.default_rng(6)
+    sample = np.unique(np.concatenate([[0, int(on.sum()) - 1, int(on.sum()), T - 1], cc[:6],
+                                       np.array(zr[:1], dtype=np.int64) // k, g.choice(T, 8, False)]))
+    keep = sorted(set(int(e) for e in idx_r[sample].ravel() if e < E))
+    say("special workload: generating weights")
+    wg, wu, wd, kept = upload_expert_weights(w, keep)
+    sh, res, gam = I.epilogue_inputs(w)
+    say("special workload: forward")
+    xd = dev(x, w.dtype)
+    actd = torch.from_numpy(active).cuda()
+    idx, wts = moe.moe_route(dev(z, "f32"), k, w.renormalize)
+    d = moe.moe_dispatch_masked(idx, E, active=actd)
+    h = moe.moe_experts_gate_up(xd, d["offsets"], wg, wu, row_map=d["slot_of_row"], map_div=k,
+                                rows=T * k)
+    y = moe.moe_experts_down(h, d["offsets"], wd)
+    yo, xo, rs = moe.moe_combine_special(y, d["row_of_slot"], idx, wts, E, n, n, n, ori_x=xd,
+                                         const_alpha1=dev(a1, w.dtype), const_alpha2=dev(a2, w.dtype),
+                                         const_v=dev(v, w.dtype), active=actd,
+                                         shared=dev(sh, w.dtype), residual=dev(res, w.dtype),
+                                         gamma=dev(gam, "f32"), eps=w.eps)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(idx).astype(np.uint32), idx_r)
+    d_r = O.dispatch(idx_r, E, active=on)
+    assert np.array_equal(host(d["offsets"]), d_r["offsets"])
+    # the sampled tokens' expert rows, one by one; slots without a row point nowhere
+    S = len(sample)
+    ys = O.round_to(np.zeros((S * k, H)), w.dtype)
+    ros = np.full(S * k, -1, dtype=np.int32)
+    for i, t in enumerate(sample):
+        for j in range(k):
+            e = int(idx_r[t, j])
+            if e < E and on[t]:
+                ys[i * k + j] = O.swiglu_expert(x[t:t + 1], *kept[e], w.dtype)[0]
+                ros[i * k + j] = i * k + j
+    yr, xr, rr = O.combine_add_rmsnorm_special(res[sample], gam, w.eps, ys, ros, idx_r[sample],
+                                               w_r[sample], "f32", S, k, w.dtype, E, n, n, n,
+                                               x[sample], a1, a2, v, on[sample], shared=sh[sample])
+    assert_close(host(xo)[sample], xr, w.dtype, "x_out")
+    assert_close(host(yo)[sample], yr, w.dtype, "y")
+    assert_close(host(rs)[sample], rr, "f32", "rstd")
+    del wg, wu, wd
+    torch.cuda.empty_cache()
+
+
 # --------------------------------------------- grouped-limited sigmoid routing --
 # (E, groups, selected_groups, top_k, group_top_two)
 GROUPED_CASES = [(256, 8, 4, 8, True), (256, 8, 4, 8, False), (64, 8, 3, 6, True),
