@@ -93,6 +93,8 @@ def main():
     ap.add_argument("--special", action="store_true",
                     help="E/32 zero, E/32 copy and E/32 constant experts after the E experts and a "
                          "per-token activity mask (7/8 of the tokens active) in the combine")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the extra timing of the same step replayed from a HIP graph")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 5 times (the "
                          "reference kernel for scaling HBM byte counters), then exit")
@@ -382,6 +384,34 @@ def main():
         cpu = {"value": round(n_cpu / c_el, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
                "sample": f"first {n_cpu} of {T} tokens of {args.workload}; {what}; {c_el:.1f}s wall"}
 
+    # ---- the same step replayed from a HIP graph (launch gaps removed) -----
+    # Reported beside the eager figures (which stay `value`): one step
+    # captured once, then replayed K times.
+    graph = None
+    if not args.no_graph:
+        try:
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                step()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step()
+            for _ in range(3):
+                g.replay()
+            torch.cuda.synchronize()
+            g0 = time.perf_counter()
+            for _ in range(args.steps):
+                g.replay()
+            torch.cuda.synchronize()
+            g_el = time.perf_counter() - g0
+            graph = {"ms_per_step": round(g_el / args.steps * 1e3, 4),
+                     "tokens_per_s": round(T * args.steps / g_el, 1)}
+        except RuntimeError as ex:  # capture not available: report the eager figures only
+            log(f"graph replay skipped: {ex}")
+
     res = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
@@ -391,6 +421,7 @@ def main():
                    "renormalize": w.renormalize, "logits_dtype": "f32"},
         "roofline": roofline, "cpu_baseline": cpu,
     }
+    res["graph_replay"] = graph
     if grouped:
         res["config"]["router"] = dict(GROUPED, kind="sigmoid_grouped", bias="N(0, 0.05^2)")
         res["metric"] = METRIC + "; grouped-limited sigmoid router"
