@@ -2,15 +2,19 @@
 
 One step = one moe_forward call through the C ABI (route -> dispatch maps
 -> gate/up GEMM with fused SiLU*up -> down GEMM -> combine) on the current
-stream over one batch of synthetic input, inputs resident in HBM. Default workload: the Mixtral-shaped bf16 batch (T=4096, H=4096,
-I=14336, E=8, top_k=2, renormalize). Prints one JSON line.
+stream over one batch of synthetic input, inputs resident in HBM. Default
+workload: the Mixtral-shaped bf16 batch (T=4096, H=4096, I=14336, E=8,
+top_k=2, renormalize). Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--router grouped | --special | --train | --quant 8|4] [--no-graph]
 
-moe_forward records HIP events on its stream at the stage boundaries of
-every timed step; the gate/up stage (the dominant kernel, plus its one-block
-tile plan) gives the roofline figure. The CPU baseline times the oracle on the first tokens of the
-same workload.
+moe_forward (or, for the epilogue, grouped-router and special-experts lines,
+the same steps as separate calls) records HIP events on its stream at the
+stage boundaries of every timed step; the gate/up stage (the dominant
+kernel, plus its tile plan) gives the roofline figure. The CPU baseline
+times the oracle on the first tokens of the same workload. The forward lines
+also time the step replayed from a HIP graph (`graph_replay`).
 """
 from __future__ import annotations
 

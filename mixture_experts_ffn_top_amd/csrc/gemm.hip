@@ -6,7 +6,7 @@
 // operands are read along K.
 //
 // Schedule. The rows of expert e are offsets[e]..offsets[e+1]-1 (device
-// data). A one-block plan kernel cuts every expert into M-tiles of BM rows
+// data). A plan kernel cuts every expert into M-tiles of BM rows
 // and writes, for every workgroup of the GEMM grid, one 16-byte entry
 // (expert and K-split, first row, end row, N-tile) or "no tile". The grid is
 // sized on the host from the bound ceil(rows/BM) + min(E, rows) on the
