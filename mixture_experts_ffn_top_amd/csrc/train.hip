@@ -39,7 +39,7 @@ constexpr int kTN = 256;           // output tile columns
 constexpr int kTK = 64;            // K per LDS stage
 constexpr int kTWaves = 8;         // 4 (M) x 2 (N); 64 x 128 outputs per wavefront
 constexpr int kTThreads = 64 * kTWaves;
-constexpr int kNGroup = 8;         // N-tiles per group in the M-grouped tile order
+constexpr int kNGroup = 32;        // N-tiles per group in the M-grouped tile order
 constexpr int kRsrcFlags = 0x00020000;  // raw buffer, no format, no swizzle (gfx9 family)
 constexpr uint32_t kOOR = 0x80000000u;  // voffset past every buffer built here: reads zeros
 constexpr int kRecords = 0x7FFFFFF0;    // buffer size in bytes: every real offset is smaller
