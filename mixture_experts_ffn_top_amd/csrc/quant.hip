@@ -22,8 +22,10 @@
 // same order, so the contraction is unchanged. The codes are dequantised in
 // registers as q * s + (o * s) in fp32 and rounded to the model dtype before
 // the MFMA (INT4 as (q + 8) * s + (o - 8) * s, the same value for integer
-// offsets). The next K-iteration's weight, scale and activation loads are
-// issued before the current iteration's MFMAs.
+// offsets). The next K-iteration's weight and activation loads are issued
+// before the current iteration's MFMAs; the scales are loaded once when a
+// wavefront's K range lies in one scale group (per-channel scales, or groups
+// at least that long), else with each iteration's loads.
 #include <type_traits>
 
 #include "common.h"
@@ -34,7 +36,8 @@ namespace {
 
 constexpr int kRsrcFlagsQ = 0x00020000;
 constexpr uint32_t kOutOfRangeQ = 0x80000000u;
-constexpr int kQRows = 64;     // weight rows per workgroup (4 MFMA tiles of 16)
+constexpr int kQTiles = 4;              // MFMA tiles of 16 weight rows per workgroup
+constexpr int kQRows = 16 * kQTiles;    // weight rows per workgroup
 constexpr int kQTokens = 16;
 constexpr int kQWaves = 4;
 
@@ -58,14 +61,19 @@ __device__ __forceinline__ float silu_q(float g) { return g * __builtin_amdgcn_r
 
 // K-iteration geometry: one 16-byte load per lane and tile covers kSpan / 4
 // codes of a row (kSpan across the 4 lanes of the row), i.e. kMf MFMA
-// k-slices of 8; one K-iteration is one such load per tile (kIter = kSpan
-// input channels: 64 for INT8, 128 for INT4; scale groups are multiples of
-// 128 channels, so an iteration never straddles two groups).
+// k-slices of 8; one K-iteration is kLoads such loads per tile, side by side
+// (kIter = kLoads * kSpan input channels). INT8 takes two (128 channels, 128
+// contiguous bytes of each row, 32 KB of weights in flight per wavefront at
+// two workgroups per CU); INT4 one (its dequantisation needs more registers
+// and more wavefronts to hide it: three workgroups per CU). Scale groups are
+// multiples of 128 channels and INT4-only, so an iteration never straddles
+// two groups.
 template <int kBits> struct QGeo {
   static constexpr int kSpan = kBits == 8 ? 64 : 128;
-  static constexpr int kIter = kSpan;
-  static constexpr int kLoads = 1;
+  static constexpr int kLoads = kBits == 8 ? 2 : 1;
+  static constexpr int kIter = kSpan * kLoads;
   static constexpr int kMf = kSpan / 32;
+  static constexpr int kBlocksPerCU = kBits == 8 ? 2 : 3;
 };
 
 typedef float f32x2q __attribute__((ext_vector_type(2)));
@@ -136,9 +144,9 @@ struct QuantArgs {
 };
 
 template <typename T, bool kSwiGlu, int kBits>
-__global__ __launch_bounds__(64 * kQWaves, 3) void skinny_quant_kernel(QuantArgs p) {
+__global__ __launch_bounds__(64 * kQWaves, QGeo<kBits>::kBlocksPerCU) void skinny_quant_kernel(QuantArgs p) {
   typedef typename MfmaQ<T>::Frag Frag;
-  __shared__ f32x4 red[kQWaves - 1][4][64];
+  __shared__ f32x4 red[kQWaves - 1][kQTiles][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int e = blockIdx.x / p.n_blocks;
@@ -168,11 +176,12 @@ __global__ __launch_bounds__(64 * kQWaves, 3) void skinny_quant_kernel(QuantArgs
   // Weight rows of the 4 tiles; rows past N read as zero and get scale 0.
   typedef QGeo<kBits> Geo;
   const int g = lane >> 4;
-  uint32_t vo_w[4];
-  int wrow[4];
+  constexpr int kHalf = kQTiles / 2;
+  uint32_t vo_w[kQTiles];
+  int wrow[kQTiles];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int n = kSwiGlu ? nb * 32 + (t & 1) * 16 + (lane & 15) : nb * kQRows + t * 16 + (lane & 15);
+  for (int t = 0; t < kQTiles; ++t) {
+    const int n = kSwiGlu ? nb * (16 * kHalf) + (t % kHalf) * 16 + (lane & 15) : nb * kQRows + t * 16 + (lane & 15);
     wrow[t] = n;
     vo_w[t] = (uint32_t)n * qrow + (uint32_t)g * 16u;  // this lane's 16 bytes of each span
   }
@@ -192,36 +201,46 @@ __global__ __launch_bounds__(64 * kQWaves, 3) void skinny_quant_kernel(QuantArgs
       const int src = p.a_map ? min(max(p.a_map[xr] / p.a_div, 0), p.a_rows - 1) : xr;
       vo_x = (uint32_t)src * xrow + (uint32_t)(g * (Geo::kSpan / 4)) * (uint32_t)sizeof(T);
     }
-    f32x4 acc[4];
+    f32x4 acc[kQTiles];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < kQTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // Scale and offset*scale of tile t for the group holding the 128
     // input channels of the K-iteration at kb (groups are multiples of 128 long).
     // Every load is issued (row and group clamped into range), then masked,
     // so none waits behind a branch.
-    auto load_sc = [&](int kb, float (&sc)[4], float (&os)[4]) {
-      const int grp = min(kb, K - 1) / gsz;
-      T sv[4], ov[4];
+    typedef float Sc[kQTiles][Geo::kLoads];
+    auto load_sc = [&](int kb, Sc& sc, Sc& os, int n_loads) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const bool up = kSwiGlu && t >= 2;
-        const int64_t at = (int64_t)min(wrow[t], N - 1) * G + grp;
-        sv[t] = (up ? sp1 : sp0)[at];
-        ov[t] = (up ? ob1 : ob0)[at];  // the scales stand in for absent offsets
-      }
-      // Masked by clearing the bits (+0), not by a select the compiler would
-      // turn back into a branch around the load.
+      for (int l = 0; l < Geo::kLoads; ++l) {
+        if (l >= n_loads) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const bool up = kSwiGlu && t >= 2;
-        const bool on = wrow[t] < N && kb < k_hi;
-        const uint16_t ms = on ? 0xFFFFu : 0u;
-        const uint16_t mo = on && (up ? has_o1 : has_o0) ? 0xFFFFu : 0u;
-        const float s = to_f32(__builtin_bit_cast(T, (uint16_t)(__builtin_bit_cast(uint16_t, sv[t]) & ms)));
-        const float o = to_f32(__builtin_bit_cast(T, (uint16_t)(__builtin_bit_cast(uint16_t, ov[t]) & mo)));
-        sc[t] = s;
-        os[t] = (kBits == 8 ? o : o - 8.0f) * s;  // INT4 codes enter as q + 8
+          for (int t = 0; t < kQTiles; ++t) { sc[t][l] = sc[t][0]; os[t][l] = os[t][0]; }
+          continue;
+        }
+        const int kl = kb + l * Geo::kSpan;
+        const int grp = min(kl, K - 1) / gsz;
+        T sv[kQTiles], ov[kQTiles];
+#pragma unroll
+        for (int t = 0; t < kQTiles; ++t) {
+          const bool up = kSwiGlu && t >= kHalf;
+          const int64_t at = (int64_t)min(wrow[t], N - 1) * G + grp;
+          sv[t] = (up ? sp1 : sp0)[at];
+          ov[t] = (up ? ob1 : ob0)[at];  // the scales stand in for absent offsets
+        }
+        // Masked by clearing the bits (+0), not by a select the compiler would
+        // turn back into a branch around the load.
+#pragma unroll
+        for (int t = 0; t < kQTiles; ++t) {
+          const bool up = kSwiGlu && t >= kHalf;
+          const bool on = wrow[t] < N && kl < k_hi;
+          const uint16_t ms = on ? 0xFFFFu : 0u;
+          const uint16_t mo = on && (up ? has_o1 : has_o0) ? 0xFFFFu : 0u;
+          const float s = to_f32(__builtin_bit_cast(T, (uint16_t)(__builtin_bit_cast(uint16_t, sv[t]) & ms)));
+          const float o = to_f32(__builtin_bit_cast(T, (uint16_t)(__builtin_bit_cast(uint16_t, ov[t]) & mo)));
+          sc[t][l] = s;
+          os[t][l] = (kBits == 8 ? o : o - 8.0f) * s;  // INT4 codes enter as q + 8
+        }
       }
     };
     // Per iteration at input channel kb: load w of tile t holds channels
@@ -229,11 +248,10 @@ __global__ __launch_bounds__(64 * kQWaves, 3) void skinny_quant_kernel(QuantArgs
     // load takes its codes 8m .. 8m+7, and activation chunk [w][m] holds the
     // same 8 channels. Codes past K or past this wavefront's K range meet
     // activations masked to zero (8-channel granularity).
-    uint4 wa[4][Geo::kLoads], wb[4][Geo::kLoads];
+    uint4 wa[kQTiles][Geo::kLoads], wb[kQTiles][Geo::kLoads];
     uint4 xa[Geo::kLoads][Geo::kMf], xb[Geo::kLoads][Geo::kMf];
-    float sa_[4], oa[4], sb_[4], ob[4];
-    auto load = [&](int kb, uint4 (&w)[4][Geo::kLoads], uint4 (&x)[Geo::kLoads][Geo::kMf], float (&sc)[4],
-                    float (&os)[4]) {
+    Sc sa_, oa, sb_, ob;
+    auto load = [&](int kb, uint4 (&w)[kQTiles][Geo::kLoads], uint4 (&x)[Geo::kLoads][Geo::kMf]) {
       const uint32_t soff_q = (uint32_t)kb * kBits / 8;
       const uint32_t soff_x = (uint32_t)kb * sizeof(T);
 #pragma unroll
@@ -241,9 +259,9 @@ __global__ __launch_bounds__(64 * kQWaves, 3) void skinny_quant_kernel(QuantArgs
         const int k0 = kb + l * Geo::kSpan + g * (Geo::kSpan / 4);
         const bool okw = k0 < k_hi;
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < kQTiles; ++t)
           w[t][l] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-              (kSwiGlu && t >= 2) ? rw1 : rw0,
+              (kSwiGlu && t >= kHalf) ? rw1 : rw0,
               okw ? vo_w[t] + (uint32_t)(l * Geo::kSpan * kBits / 8) : kOutOfRangeQ, soff_q, 0));
 #pragma unroll
         for (int m = 0; m < Geo::kMf; ++m) {
@@ -252,59 +270,75 @@ __global__ __launch_bounds__(64 * kQWaves, 3) void skinny_quant_kernel(QuantArgs
               rx, okx ? vo_x + (uint32_t)((l * Geo::kSpan + m * 8) * (int)sizeof(T)) : kOutOfRangeQ, soff_x, 0));
         }
       }
-      load_sc(kb, sc, os);
     };
-    auto compute = [&](const uint4 (&w)[4][Geo::kLoads], const uint4 (&x)[Geo::kLoads][Geo::kMf],
-                       const float (&sc)[4], const float (&os)[4]) {
+    auto compute = [&](const uint4 (&w)[kQTiles][Geo::kLoads], const uint4 (&x)[Geo::kLoads][Geo::kMf],
+                       const Sc& sc, const Sc& os) {
 #pragma unroll
       for (int l = 0; l < Geo::kLoads; ++l)
 #pragma unroll
         for (int m = 0; m < Geo::kMf; ++m)
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const Frag f = __builtin_bit_cast(Frag, dequant8<T, kBits>(w[t][l], m, sc[t], os[t], p.nib_mask));
+          for (int t = 0; t < kQTiles; ++t) {
+            const Frag f = __builtin_bit_cast(Frag, dequant8<T, kBits>(w[t][l], m, sc[t][l], os[t][l], p.nib_mask));
             acc[t] = MfmaQ<T>::run(f, __builtin_bit_cast(Frag, x[l][m]), acc[t]);
           }
     };
     const int n_iter = (k_hi - k_lo + Geo::kIter - 1) / Geo::kIter;
-    if (n_iter > 0) {
-      load(k_lo, wa, xa, sa_, oa);
+    // One scale group over this wavefront's whole K range (per-channel
+    // scales, or groups no shorter than the range): the scales are loaded once.
+    const bool one_group = n_iter > 0 && k_lo / gsz == (k_hi - 1) / gsz;
+    if (one_group) {
+      load_sc(k_lo, sa_, oa, 1);
+      load(k_lo, wa, xa);
       int it = 0;
       for (; it + 2 <= n_iter; it += 2) {
-        load(k_lo + (it + 1) * Geo::kIter, wb, xb, sb_, ob);
+        load(k_lo + (it + 1) * Geo::kIter, wb, xb);
         compute(wa, xa, sa_, oa);
-        load(k_lo + (it + 2) * Geo::kIter, wa, xa, sa_, oa);
-        compute(wb, xb, sb_, ob);
+        load(k_lo + (it + 2) * Geo::kIter, wa, xa);
+        compute(wb, xb, sa_, oa);
       }
       if (it < n_iter) compute(wa, xa, sa_, oa);  // odd count: wa holds the last iteration
+    } else if (n_iter > 0) {
+      load(k_lo, wa, xa);
+      load_sc(k_lo, sa_, oa, Geo::kLoads);
+      int it = 0;
+      for (; it + 2 <= n_iter; it += 2) {
+        load(k_lo + (it + 1) * Geo::kIter, wb, xb);
+        load_sc(k_lo + (it + 1) * Geo::kIter, sb_, ob, Geo::kLoads);
+        compute(wa, xa, sa_, oa);
+        load(k_lo + (it + 2) * Geo::kIter, wa, xa);
+        load_sc(k_lo + (it + 2) * Geo::kIter, sa_, oa, Geo::kLoads);
+        compute(wb, xb, sb_, ob);
+      }
+      if (it < n_iter) compute(wa, xa, sa_, oa);
     }
 
     // Partial sums of wavefronts 1..3 meet wavefront 0's in LDS (fixed order).
     if (wave > 0) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) red[wave - 1][t][lane] = acc[t];
+      for (int t = 0; t < kQTiles; ++t) red[wave - 1][t][lane] = acc[t];
     }
     __syncthreads();
     if (wave == 0) {
 #pragma unroll
       for (int w = 0; w < kQWaves - 1; ++w)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) acc[t] += red[w][t][lane];
+        for (int t = 0; t < kQTiles; ++t) acc[t] += red[w][t][lane];
       // D element v of lane l: weight row (l/16)*4 + v of the tile, token l%16.
       const int tok = rg + (lane & 15);
       if (tok < r_end) {
         T* crow = C + (int64_t)tok * N;
         if (kSwiGlu) {
 #pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const int col = nb * 32 + t * 16 + g * 4;
+          for (int t = 0; t < kHalf; ++t) {
+            const int col = nb * (16 * kHalf) + t * 16 + g * 4;
 #pragma unroll
             for (int v = 0; v < 4; ++v)
-              if (col + v < N) crow[col + v] = from_f32<T>(silu_q(acc[t][v]) * acc[t + 2][v]);
+              if (col + v < N) crow[col + v] = from_f32<T>(silu_q(acc[t][v]) * acc[t + kHalf][v]);
           }
         } else {
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
+          for (int t = 0; t < kQTiles; ++t) {
             const int col = nb * kQRows + t * 16 + g * 4;
 #pragma unroll
             for (int v = 0; v < 4; ++v)
@@ -319,7 +353,7 @@ __global__ __launch_bounds__(64 * kQWaves, 3) void skinny_quant_kernel(QuantArgs
 
 template <typename T, int kBits>
 void launch_q(QuantArgs p, bool swiglu, hipStream_t s) {
-  p.n_blocks = swiglu ? (p.N + 31) / 32 : (p.N + kQRows - 1) / kQRows;
+  p.n_blocks = swiglu ? (p.N + kQRows / 2 - 1) / (kQRows / 2) : (p.N + kQRows - 1) / kQRows;
   constexpr int kIter = QGeo<kBits>::kIter;
   const int iters = (p.K + kIter - 1) / kIter;
   p.k_quarter = (iters + kQWaves - 1) / kQWaves * kIter;

@@ -777,18 +777,24 @@ def _qdev(t, dtype):
             None if off is None else dev(off, dtype))
 
 
-@pytest.mark.parametrize("bits,groups,dtype,with_offset,H,I_", [(8, 1, "bf16", True, 512, 384),
-                                                                (4, 1, "f16", False, 512, 384),
-                                                                (4, 4, "bf16", True, 1024, 512),
-                                                                (8, 1, "bf16", False, 136, 264),
-                                                                (8, 1, "f16", True, 264, 136),
-                                                                (4, 2, "f16", True, 256, 768),
-                                                                (4, 1, "bf16", True, 72, 200)])
-def test_quant_experts_dispatched(bits, groups, dtype, with_offset, H, I_):
-    say("quant experts", bits, groups, dtype)
+@pytest.mark.parametrize("bits,groups,dtype,with_offset,H,I_,ETk", [(8, 1, "bf16", True, 512, 384, (16, 12, 4)),
+                                                                    (4, 1, "f16", False, 512, 384, (16, 12, 4)),
+                                                                    (4, 4, "bf16", True, 1024, 512, (16, 12, 4)),
+                                                                    (8, 1, "bf16", False, 136, 264, (16, 12, 4)),
+                                                                    (8, 1, "f16", True, 264, 136, (16, 12, 4)),
+                                                                    (4, 2, "f16", True, 256, 768, (16, 12, 4)),
+                                                                    (4, 1, "bf16", True, 72, 200, (16, 12, 4)),
+                                                                    # every token also routes to expert 0 (40
+                                                                    # rows): several 16-row groups in one expert
+                                                                    (8, 1, "bf16", True, 768, 640, (32, 40, 1)),
+                                                                    (4, 4, "bf16", False, 1024, 512, (32, 40, 1))])
+def test_quant_experts_dispatched(bits, groups, dtype, with_offset, H, I_, ETk):
+    say("quant experts", bits, groups, dtype, H, I_, ETk)
     g = np.random.default_rng(bits * 10 + groups)
-    E, T, k = 16, 12, 4
+    E, T, k = ETk
     idx = np.stack([g.permutation(E)[:k] for _ in range(T)]).astype(np.uint32)
+    if k == 1:  # a second choice, always expert 0
+        idx = np.stack([np.zeros(T, np.uint32), 1 + idx[:, 0] % (E - 1)], axis=1).astype(np.uint32)
     x = _store(g.standard_normal((T, H)), dtype)
     d = O.dispatch(idx, E, x)
     wq = _quant_experts(g, E, H, I_, bits, groups, dtype, with_offset)
