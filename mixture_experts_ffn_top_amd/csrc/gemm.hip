@@ -25,23 +25,29 @@
 // never mixes two experts' weights. (Runs of 8 measured about 1 % faster than
 // one run of 32 covering the same tiles.)
 //
-// bf16/f16 kernel (gfx950 MFMA 32x32x16): workgroup tile 256 x kBNB, K
-// staged 32 at a time; 512 threads = 8 wavefronts as 4 (M) x 2 (N), 64 x
-// kBNB/2 outputs per wavefront. Global tiles go straight into LDS with
-// buffer loads (buffer_load_dwordx4 ... lds): each lane's 16 bytes land at
-// LDS base + 16 * lane, so the swizzle is applied by choosing which global
-// chunk each lane fetches. A load past the buffer's byte count returns
-// zeros, which covers the N tail of the weights, A rows past the expert's
-// last row and (with a deliberately out-of-range offset) the K tail.
-// kStages (4) LDS stages: loads for k-step kt+3 are issued at the top of
-// k-step kt, and a stage is waited for (vmcnt) only just before the barrier
-// that precedes its first read. Fragment registers are double-buffered
-// across the two k16 sub-steps of a stage so LDS reads overlap MFMAs.
+// bf16/f16 kernel (gfx950 MFMA 32x32x16), two tile shapes:
+//  - 256 x kBNB tiles, 512 threads = 8 wavefronts as 4 (M) x 2 (N), 64 x
+//    kBNB/2 outputs per wavefront, two 64 KB LDS stages of K = 64: the loads
+//    of k-step kt+1 are issued at the top of k-step kt;
+//  - weight streaming (at most 128 rows an expert on average, where the
+//    weights are read about once per 128 rows and the stream of weight tiles
+//    sets the time): 128 x kBNB tiles, 8 wavefronts of 32 x kBNB/2 outputs,
+//    three 48 KB stages, the loads of k-step kt+2 issued at the top of kt, so
+//    two k-steps of weights are in flight per CU instead of one.
+// Global tiles go straight into LDS with buffer loads (buffer_load_dwordx4 ...
+// lds): each lane's 16 bytes land at LDS base + 16 * lane, so the swizzle is
+// applied by choosing which global chunk each lane fetches. A load past the
+// buffer's byte count returns zeros, which covers the N tail of the weights,
+// A rows past the expert's last row and (with a deliberately out-of-range
+// offset) the K tail. A stage is waited for (vmcnt) only just before the
+// barrier that precedes its first read. Fragment registers are
+// double-buffered across the k16 sub-steps of a stage so LDS reads overlap
+// MFMAs.
 //
-// LDS rows are 32 elements (four 16-byte chunks). gfx950 serves a 128-bit
-// LDS read 16 lanes per cycle across 64 banks (four rows of 64 bytes), so
-// the 16 rows read together must cover all 16 (row mod 4, chunk) slots:
-// chunk c of row r is stored at c ^ ((r >> 2) & 3).
+// LDS rows are 64 elements (eight 16-byte chunks, 128 bytes). gfx950 serves
+// a 128-bit LDS read 16 lanes per cycle across 64 banks (two 128-byte rows),
+// so the 16 rows read together must cover all 16 (row mod 2, chunk) slots:
+// chunk c of row r is stored at c ^ ((r >> 1) & 7).
 //
 // Split-K (GEMM 2, when the M x N tiles alone cannot fill the chip): k_splits
 // workgroups per output tile each cover one K range and write fp32 partials;
@@ -142,6 +148,7 @@ struct GemmArgs {
   const int32_t* offsets;  // [E+1]
   const int4* sched;       // [grid] entries written by plan_kernel
   int rows, N, K, max_tiles, n_tiles_n, grid;
+  int bm;  // rows per M-tile of the schedule (selects the kernel's tile shape)
   // Split-K (GEMM 2 only): k_splits workgroups share one output tile, each
   // over k_chunk elements of K, writing fp32 partial sums to
   // partial[split][rows][N]; the caller reduces them in split order.
@@ -258,34 +265,37 @@ __device__ __forceinline__ int swizzle(int r) {
 
 // kWaveM: rows per wavefront, 64 (8 wavefronts, 4 x 2) or 128 (4 wavefronts,
 // 2 x 2; 256 accumulators per lane, one wavefront per SIMD).
-template <int kWaveM>
-constexpr int gemm_threads() { return 64 * (kBM / kWaveM) * 2; }
+template <int kWaveM, int kBMt = kBM>
+constexpr int gemm_threads() { return 64 * (kBMt / kWaveM) * 2; }
 
 // Persistent grouped GEMM. The grid holds one workgroup per CU; workgroup b
 // takes schedule entries b, b + G, b + 2G, ... (G = grid size, a multiple of
 // 8, so every entry it takes belongs to its own XCD's slice of the list).
 //
-// K is staged kBKT (64) elements at a time through two LDS stages. A stage
-// row is 128 bytes, and each buffer load instruction fills 8 rows with
-// 128-byte row segments, which move through the load path about twice as
-// fast as 64-byte ones. The loads of k-step kt+1 are issued at the top of
-// k-step kt and waited for just before the barrier that ends it.
+// K is staged kBKT (64) elements at a time through kStg (2 or 3) LDS stages.
+// A stage row is 128 bytes, and each buffer load instruction fills 8 rows
+// with 128-byte row segments, which move through the load path about twice
+// as fast as 64-byte ones. The loads of k-step kt+kStg-1 are issued at the
+// top of k-step kt; the barrier that ends k-step kt waits only for k-step
+// kt+1's.
 //
 // Between tiles: once every wavefront has finished reading LDS, the first
 // stage of the next tile is requested, and only then are the finished
 // tile's results written out, so the store traffic overlaps the next tile's
 // first loads instead of leaving the CU idle.
-template <typename T, bool kSwiGlu, int kBNB, int kBKT, int kWaveM, bool kCache = false>
-__global__ __launch_bounds__(gemm_threads<kWaveM>()) void mfma_gemm_kernel(GemmArgs p) {
+template <typename T, bool kSwiGlu, int kBNB, int kBKT, int kWaveM, bool kCache = false, int kBMt = kBM,
+          int kStg = 2>
+__global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kernel(GemmArgs p) {
   typedef typename Mfma<T>::Frag Frag;
-  constexpr int kWaves = (kBM / kWaveM) * 2;
+  static_assert(kStg == 2 || kStg == 3, "two or three LDS stages");
+  constexpr int kWaves = (kBMt / kWaveM) * 2;
   constexpr int kThreadsK = 64 * kWaves;
   constexpr int kCh = kBKT / 8;                       // 16-byte chunks per LDS row
   constexpr int kRowsPerInst = 64 / kCh;              // rows filled by one load instruction
   constexpr int kSub = kBKT / 16;                     // MFMA k16 sub-steps per stage
   constexpr int kMB = kWaveM / 32;                    // 32-row blocks per wavefront
   constexpr int kNB = kBNB / 64;                      // 32-column blocks per wavefront
-  constexpr int kLoadsA = kBM * kCh / kThreadsK;      // 16-byte chunks per thread per stage
+  constexpr int kLoadsA = kBMt * kCh / kThreadsK;     // 16-byte chunks per thread per stage
   constexpr int kLoadsB = kBNB * kCh / kThreadsK;
   constexpr int kLoads = kLoadsA + kLoadsB;
   static_assert(!kSwiGlu || kBNB == 256, "fused gate/up uses 128 + 128 B rows");
@@ -321,7 +331,7 @@ __global__ __launch_bounds__(gemm_threads<kWaveM>()) void mfma_gemm_kernel(GemmA
   int e, ks, row0, n_t, mrows, k_begin, k_end;
   auto setup = [&](const Tile& t) {
     e = t.e; ks = t.ks; row0 = t.row0; n_t = t.n_t;
-    mrows = min(kBM, t.row_end - row0);
+    mrows = min(kBMt, t.row_end - row0);
     k_begin = ks * p.k_chunk;
     k_end = min(K, k_begin + p.k_chunk);
     const int64_t expert_elems = (int64_t)e * N * K;
@@ -406,12 +416,22 @@ __global__ __launch_bounds__(gemm_threads<kWaveM>()) void mfma_gemm_kernel(GemmA
   auto step = [&](auto stage, auto compute, int kt, int nk_pad) {
     constexpr int S = decltype(stage)::value;
     constexpr bool kCompute = decltype(compute)::value;
-    constexpr int X = S ^ 1;
-    T* ca = stage_buf<T, kBM * kBKT, 0, S>();
+    constexpr int X = (S + 1) % kStg;        // stage read next
+    constexpr int L = (S + kStg - 1) % kStg; // stage refilled now, for k-step kt + kStg - 1
+    T* ca = stage_buf<T, kBMt * kBKT, 0, S>();
     T* cb = stage_buf<T, kBNB * kBKT, 1, S>();
-    if (kt + 1 < nk_pad) issue_loads(kt + 1, stage_buf<T, kBM * kBKT, 0, X>(), stage_buf<T, kBNB * kBKT, 1, X>());
+    const bool refill = kt + kStg - 1 < nk_pad;
+    if (refill) issue_loads(kt + kStg - 1, stage_buf<T, kBMt * kBKT, 0, L>(), stage_buf<T, kBNB * kBKT, 1, L>());
+    // Stage X (k-step kt+1) must have landed by the barrier; with three
+    // stages the loads just issued for kt+2 may stay in flight.
+    auto wait_next = [&]() {
+      if (kStg == 3 && refill)
+        wait_vmem<kStg == 3 ? kLoads : 0>();
+      else
+        wait_vmem<0>();
+    };
     if constexpr (!kCompute) {
-      wait_vmem<0>();
+      wait_next();
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       return;
     }
@@ -432,10 +452,10 @@ __global__ __launch_bounds__(gemm_threads<kWaveM>()) void mfma_gemm_kernel(GemmA
     // MFMAs are not memory operations and would otherwise drift across the
     // barrier, leaving too few of them to cover the next stage's reads.
     __builtin_amdgcn_sched_barrier(0);
-    wait_vmem<0>();
+    wait_next();
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    read_frags(stage_buf<T, kBM * kBKT, 0, X>(), stage_buf<T, kBNB * kBKT, 1, X>(), 0, 0);
+    read_frags(stage_buf<T, kBMt * kBKT, 0, X>(), stage_buf<T, kBNB * kBKT, 1, X>(), 0, 0);
     mfmas(kLast, kMfma / 2, kMfma);
 #pragma unroll
     for (int i = 0; i < kReads; ++i) {
@@ -443,26 +463,32 @@ __global__ __launch_bounds__(gemm_threads<kWaveM>()) void mfma_gemm_kernel(GemmA
       if (i < kMfma / 2) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
   };
-  // Main loop over one tile, unrolled by the two stages so every LDS pointer
-  // is a fixed object. The trip count is padded to an even number: loads
-  // past K are masked to zeros, so a padding step adds nothing.
+  // Main loop over one tile, unrolled by the stages so every LDS pointer is
+  // a fixed object. The trip count is padded to a multiple of the stage
+  // count: loads past K are masked to zeros, so a padding step adds nothing.
   auto main_loop = [&](auto compute, int nk_pad) {
     if constexpr (decltype(compute)::value)
-      read_frags(stage_buf<T, kBM * kBKT, 0, 0>(), stage_buf<T, kBNB * kBKT, 1, 0>(), 0, 0);
-    for (int kt = 0; kt < nk_pad; kt += 2) {
+      read_frags(stage_buf<T, kBMt * kBKT, 0, 0>(), stage_buf<T, kBNB * kBKT, 1, 0>(), 0, 0);
+    for (int kt = 0; kt < nk_pad; kt += kStg) {
       step(std::integral_constant<int, 0>{}, compute, kt, nk_pad);
       step(std::integral_constant<int, 1>{}, compute, kt + 1, nk_pad);
+      if constexpr (kStg == 3) step(std::integral_constant<int, 2>{}, compute, kt + 2, nk_pad);
     }
+  };
+  // The first kStg - 1 k-steps of a tile are requested ahead of its loop.
+  auto issue_first = [&]() {
+    issue_loads(0, stage_buf<T, kBMt * kBKT, 0, 0>(), stage_buf<T, kBNB * kBKT, 1, 0>());
+    if constexpr (kStg == 3) issue_loads(1, stage_buf<T, kBMt * kBKT, 0, 1>(), stage_buf<T, kBNB * kBKT, 1, 1>());
   };
 
   setup(tile);
-  issue_loads(0, stage_buf<T, kBM * kBKT, 0, 0>(), stage_buf<T, kBNB * kBKT, 1, 0>());
+  issue_first();
   T* C = static_cast<T*>(p.c);
   const int row_lane = (lane >> 5) * 4;
   // Epilogue stores per computing wavefront: 4 per 32x32 output block (3
   // blocks, h, g and u, per h block when the training cache is written).
   constexpr int kStores = (kSwiGlu ? kMB * 2 : kMB * kNB) * 4 * (kCache ? 3 : 1);
-  static_assert(kStores < 64, "vmcnt holds 6 bits");
+  static_assert(kStores + kLoads < 64, "vmcnt holds 6 bits");
   int stores_prev = 0;
   for (;;) {
 #pragma unroll
@@ -472,13 +498,14 @@ __global__ __launch_bounds__(gemm_threads<kWaveM>()) void mfma_gemm_kernel(GemmA
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
     const int nk = (k_end - k_begin + kBKT - 1) / kBKT;
-    const int nk_pad = (nk + 1) & ~1;
-    // Stage 0 of this tile has been requested; wait for it (not for the
-    // previous tile's stores, issued after it).
+    const int nk_pad = (nk + kStg - 1) / kStg * kStg;
+    // Stages 0 .. kStg-2 of this tile have been requested; wait for stage 0
+    // (not for the later stages or the previous tile's stores, issued after it).
+    constexpr int kAhead = (kStg - 2) * kLoads;
     if (stores_prev)
-      wait_vmem<kStores>();
+      wait_vmem<kStores + kAhead>();
     else
-      wait_vmem<0>();
+      wait_vmem<kAhead>();
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     const bool has_rows = wm * kWaveM < mrows;
     if (has_rows)
@@ -493,7 +520,7 @@ __global__ __launch_bounds__(gemm_threads<kWaveM>()) void mfma_gemm_kernel(GemmA
     const bool more = tile_of_block(p, v, next);
     if (more) {
       setup(next);
-      issue_loads(0, stage_buf<T, kBM * kBKT, 0, 0>(), stage_buf<T, kBNB * kBKT, 1, 0>());
+      issue_first();
     }
 
     // Epilogue. Accumulator element i of lane l sits at row
@@ -874,6 +901,11 @@ constexpr int kCUs = 256;
 #define MOE_GEMM_WAVE_M 64
 #endif
 constexpr int kWaveMGemm = MOE_GEMM_WAVE_M;
+// Weight-streaming shape (at most kBMStream rows an expert on average): 128-row
+// M-tiles of 8 wavefronts (32 rows each) and three 48 KB LDS stages, so two
+// k-steps of weights are in flight per CU instead of one.
+constexpr int kBMStream = 128;
+constexpr int kWaveMStream = 32;
 
 static size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
@@ -889,7 +921,7 @@ static int64_t tile_n(int64_t N, int dt, bool swiglu) {
 // workgroups is not left mostly empty; each split keeps >= 64 K-steps.
 ExpertsPlan experts_plan(int64_t rows, int64_t E, int64_t H, int64_t I, int dt) {
   ExpertsPlan p;
-  p.bm = dt == kF32 ? kBMSimt : kBM;
+  p.bm = dt == kF32 ? kBMSimt : (rows <= kBMStream * E ? kBMStream : kBM);
   p.max_tiles = (int)((rows + p.bm - 1) / p.bm + (E < rows ? E : rows));
   p.splits = 1;
   p.k_chunk = (int)I;
@@ -964,6 +996,7 @@ __global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restr
 void plan_tiles(GemmArgs& g, const ExpertsPlan& plan, int E, int dt, bool swiglu, void* scratch,
                 hipStream_t s) {
   g.max_tiles = plan.max_tiles;
+  g.bm = plan.bm;
   g.n_tiles_n = (int)tile_n(g.N, dt, swiglu);
   g.grid = (int)grid_tiles(plan.max_tiles, g.n_tiles_n, g.k_splits);
   int4* sched = static_cast<int4*>(scratch);
@@ -999,6 +1032,19 @@ static int persistent_grid(int entries) {
 template <typename T>
 void launch_mfma(const GemmArgs& g, bool swiglu, hipStream_t s) {
   const dim3 grid(persistent_grid(g.grid));
+  if (g.bm == kBMStream) {
+    constexpr int kThreads = gemm_threads<kWaveMStream, kBMStream>();
+    if (swiglu && g.cache)
+      hipLaunchKernelGGL((mfma_gemm_kernel<T, true, 256, kBK, kWaveMStream, true, kBMStream, 3>), grid,
+                         dim3(kThreads), 0, s, g);
+    else if (swiglu)
+      hipLaunchKernelGGL((mfma_gemm_kernel<T, true, 256, kBK, kWaveMStream, false, kBMStream, 3>), grid,
+                         dim3(kThreads), 0, s, g);
+    else
+      hipLaunchKernelGGL((mfma_gemm_kernel<T, false, 256, kBK, kWaveMStream, false, kBMStream, 3>), grid,
+                         dim3(kThreads), 0, s, g);
+    return;
+  }
   if (swiglu && g.cache)
     hipLaunchKernelGGL((mfma_gemm_kernel<T, true, 256, kBK, kWaveMGemm, true>), grid,
                        dim3(gemm_threads<kWaveMGemm>()), 0, s, g);

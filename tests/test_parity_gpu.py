@@ -245,13 +245,16 @@ def test_experts_few_rows_per_expert(T, k, E, H, I_, dtype, one_expert):
     assert_close(host(y2), ref, dtype, f"skinny halves {dtype}")
 
 
-def test_experts_split_k_and_halves():
+@pytest.mark.parametrize("E,H,I_", [(3, 512, 4096),    # 200 rows an expert: 256-row M-tiles
+                                    (8, 256, 8192)])   # 75 rows an expert: 128-row M-tiles
+def test_experts_split_k_and_halves(E, H, I_):
     """Long K with few output tiles: the down GEMM splits K (fp32 partials,
     reduced in order). Checked through forward_dispatched, through the two
     halves (gate/up reading tokens via the dispatch map) and through
     moe_forward (partials reduced inside the combine)."""
+    say("split-K", E, H, I_)
     g = np.random.default_rng(21)
-    T, k, E, H, I_ = 300, 2, 3, 512, 4096
+    T, k = 300, 2
     x = I.store(g.standard_normal((T, H)).astype(np.float32), "bf16")
     z = I.gapped_logits(21, T, E, k)
     wg, wu, wd = _random_experts(g, E, H, I_, "bf16")
