@@ -44,28 +44,33 @@ BOUND = {"tiny_fp32": "alu", "mixtral_8x_bf16": "mfma", "many_expert_zipf_bf16":
          "dsv3_share_rmsnorm_bf16": "hbm", "decode_nan_rows_bf16": "hbm"}
 
 
-def kernel_source_hash() -> str:
-    """sha256/16 over the sources the profiled kernels are compiled from (the
-    GEMM and combine kernels and their device helpers): counters taken on
-    other sources no longer describe the kernels."""
+FORWARD_SOURCES = ("combine.hip", "common.h", "gemm.hip")
+
+
+def kernel_source_hash(sources=FORWARD_SOURCES) -> str:
+    """sha256/16 over the sources the profiled kernels are compiled from (for
+    the forward lines the GEMM and combine kernels and their device helpers):
+    counters taken on other sources no longer describe the kernels."""
     import hashlib
     d = os.path.join(ROOT, "mixture_experts_ffn_top_amd", "csrc")
     h = hashlib.sha256()
-    for n in ("combine.hip", "common.h", "gemm.hip"):
+    for n in sources:
         h.update(n.encode())
         h.update(open(os.path.join(d, n), "rb").read())
     return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str, kernel: str):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE runs (profiles/counters.json, scaled by the copy-kernel
-    calibration), or None when the kernel sources changed after they were taken."""
+    """HBM bytes per launch of `kernel` (for the quantised and training lines:
+    per step of the launches their roofline covers) from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE runs (profiles/counters.json, scaled by
+    the copy-kernel calibration), or None when the kernel sources changed
+    after they were taken."""
     try:
         data = json.load(open(os.path.join(ROOT, "profiles", "counters.json")))[workload]
     except (OSError, KeyError, ValueError):
         return None
-    if kernel_source_hash() != data.get("kernel_source_sha16"):
+    if kernel_source_hash(tuple(data.get("sources", FORWARD_SOURCES))) != data.get("kernel_source_sha16"):
         return None
     return data["traffic_bytes_per_launch"].get(kernel)
 
@@ -499,10 +504,11 @@ def run_quant(args, w, x, z, to_dev):
     bytes_experts = wbytes_gu + wbytes_dn + T * H * 2 + 2 * R * I_ * 2 + R * H * 2
     exp_s = (stage_ms["gate_up"] + stage_ms["down"]) / 1e3
     gbs = bytes_experts / exp_s / 1e9
+    qkernel = f"skinny_quant_kernel<bf16,gate_up|down,INT{bits}> (both launches)"
     roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
-                "kernel": f"skinny_quant_kernel<bf16,gate_up|down,INT{bits}> (both launches)",
-                "algorithmic_per_launch": bytes_experts}
+                "frac": round(gbs / PEAK_HBM_GBS, 4),
+                "traffic": measured_traffic(f"{args.workload}+int{bits}", qkernel),
+                "kernel": qkernel, "algorithmic_per_launch": bytes_experts}
     cpu = None
     if not args.no_cpu_baseline:
         from oracle import moe_oracle as O
@@ -632,10 +638,11 @@ def run_train(args, w, x, z, xd, zd, wt, kept, n_cpu):
     flops_fwd = 6.0 * R * H * I_
     bwd_tf = flops_bwd / (stage_ms["experts_bwd"] / 1e3) / 1e12
     fwd_tf = flops_fwd / (stage_ms["experts_fwd"] / 1e3) / 1e12
+    tkernel = "moe_experts_backward (4 train_gemm_kernel launches + tile prefix)"
     roofline = {"bound": "mfma", "achieved": round(bwd_tf, 1), "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
-                "frac": round(bwd_tf / PEAK_TFLOPS["bf16"], 4), "traffic": None,
-                "kernel": "moe_experts_backward (4 train_gemm_kernel launches + tile prefix)",
-                "algorithmic_per_launch": flops_bwd}
+                "frac": round(bwd_tf / PEAK_TFLOPS["bf16"], 4),
+                "traffic": measured_traffic(f"{args.workload}+train", tkernel),
+                "kernel": tkernel, "algorithmic_per_launch": flops_bwd}
     cpu = None
     if not args.no_cpu_baseline:
         from oracle import moe_oracle as O
