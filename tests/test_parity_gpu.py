@@ -166,6 +166,11 @@ EXPERT_CASES = [
     # several tiles per persistent workgroup, with ragged column and K tails
     (2560, 4, 256, 264, 200, "bf16"),
     (6000, 4, 96, 136, 328, "f16"),
+    # at the kernel-choice thresholds: 4E + 1 rows (just past the decode
+    # kernel), 128E rows (last batch on 128-row tiles), 128E + 4 (256-row tiles)
+    (33, 1, 8, 136, 200, "bf16"),
+    (256, 4, 8, 136, 264, "bf16"),
+    (257, 4, 8, 136, 264, "f16"),
 ]
 
 
