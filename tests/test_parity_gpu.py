@@ -370,11 +370,13 @@ def test_forward_deterministic():
 
 
 @pytest.mark.parametrize("T,k,E,H,I_,dtype", [(300, 2, 4, 256, 384, "bf16"), (2048, 8, 64, 256, 256, "bf16"),
+                                               (200, 4, 16, 256, 256, "bf16"),
                                                (16, 8, 128, 256, 128, "bf16"), (77, 2, 8, 128, 256, "f32")])
 def test_forward_graph_replay(T, k, E, H, I_, dtype):
     """moe_forward captured once into a HIP graph: every replay, with eager
     library calls and a fill of the outputs between replays, reproduces the
-    eager result bit for bit (decode-sized, MFMA and fp32 paths)."""
+    eager result bit for bit (decode-sized, MFMA with 256- and 128-row tiles,
+    and fp32 paths)."""
     say("graph replay", T, k, E, H, I_, dtype)
     g = np.random.default_rng(T + E)
     x = _store(g.standard_normal((T, H)), dtype)
@@ -836,3 +838,39 @@ def test_forward_quant_decode_shape(bits, groups):
     y = O.experts_forward_quant(d["x_disp"], d["offsets"], quant_of, bits, groups, "bf16")
     ref = O.combine(y, d["row_of_slot"], w_r, "f32", w.T, w.top_k, "bf16")
     assert_close(host(out), ref, "bf16", "quantised forward")
+
+
+@pytest.mark.parametrize("bits,groups", [(8, 1), (4, 2)])
+def test_forward_quant_graph_replay(bits, groups):
+    """moe_forward_quant captured into a HIP graph: each replay, with eager
+    calls between replays, reproduces the eager result bit for bit."""
+    say("quant graph replay", bits, groups)
+    g = np.random.default_rng(70 + bits)
+    T, k, E, H, I_ = 16, 4, 32, 256, 256
+    x = dev(_store(g.standard_normal((T, H)), "bf16"), "bf16")
+    z = dev(I.gapped_logits(T + k, T, E, k), "f32")
+    wq = _quant_experts(g, E, H, I_, bits, groups, "bf16", True)
+    gd, ud, dd = (_qdev(t, "bf16") for t in wq)
+    args = (k, True, gd[0], ud[0], dd[0], bits, (gd[1], ud[1], dd[1]), (gd[2], ud[2], dd[2]), groups)
+    ws_size = moe.moe_forward_workspace_size(T, H, I_, E, k, torch.bfloat16, torch.float32)
+    ws_e = torch.empty(ws_size, dtype=torch.uint8, device="cuda")
+    ws_g = torch.empty_like(ws_e)
+    ref = moe.moe_forward_quant(x, z, *args, ws=ws_e).clone()
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        moe.moe_forward_quant(x, z, *args, out=out, ws=ws_g)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        moe.moe_forward_quant(x, z, *args, out=out, ws=ws_g)
+    other = dev(_store(g.standard_normal((T, H)), "bf16"), "bf16")
+    for rep in range(3):
+        out.fill_(0)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"replay {rep}"
+        moe.moe_forward_quant(other, z, *args, ws=ws_e)  # eager work between replays
+        torch.cuda.synchronize()
