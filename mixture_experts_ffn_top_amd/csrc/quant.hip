@@ -63,17 +63,17 @@ __device__ __forceinline__ float silu_q(float g) { return g * __builtin_amdgcn_r
 // codes of a row (kSpan across the 4 lanes of the row), i.e. kMf MFMA
 // k-slices of 8; one K-iteration is kLoads such loads per tile, side by side
 // (kIter = kLoads * kSpan input channels). INT8 takes two (128 channels, 128
-// contiguous bytes of each row, 32 KB of weights in flight per wavefront at
-// two workgroups per CU); INT4 one (its dequantisation needs more registers
-// and more wavefronts to hide it: three workgroups per CU). Scale groups are
-// multiples of 128 channels and INT4-only, so an iteration never straddles
-// two groups.
+// contiguous bytes of each row, up to 16 KB of weights in flight per
+// wavefront at two wavefronts per SIMD, i.e. two workgroups per CU); INT4 one
+// (its dequantisation needs more registers and more wavefronts to hide it:
+// three per SIMD). Scale groups are multiples of 128 channels and INT4-only,
+// so an iteration never straddles two groups.
 template <int kBits> struct QGeo {
   static constexpr int kSpan = kBits == 8 ? 64 : 128;
   static constexpr int kLoads = kBits == 8 ? 2 : 1;
   static constexpr int kIter = kSpan * kLoads;
   static constexpr int kMf = kSpan / 32;
-  static constexpr int kBlocksPerCU = kBits == 8 ? 2 : 3;
+  static constexpr int kWavesPerSimd = kBits == 8 ? 2 : 3;  // occupancy target (launch bounds)
 };
 
 typedef float f32x2q __attribute__((ext_vector_type(2)));
@@ -144,7 +144,7 @@ struct QuantArgs {
 };
 
 template <typename T, bool kSwiGlu, int kBits>
-__global__ __launch_bounds__(64 * kQWaves, QGeo<kBits>::kBlocksPerCU) void skinny_quant_kernel(QuantArgs p) {
+__global__ __launch_bounds__(64 * kQWaves, QGeo<kBits>::kWavesPerSimd) void skinny_quant_kernel(QuantArgs p) {
   typedef typename MfmaQ<T>::Frag Frag;
   __shared__ f32x4 red[kQWaves - 1][kQTiles][64];
   const int lane = threadIdx.x & 63;
