@@ -253,7 +253,7 @@ def route_sigmoid_grouped_margins(logits, logits_dtype, bias, top_k, groups, sel
 def dispatch(indices: np.ndarray, E: int, x: np.ndarray | None = None, active=None):
     """Compact grouping of the T*k (token, slot) pairs by expert, no capacity
     drop. Within an expert, pairs keep (token, slot) order (the pages leave
-    this order free; this build fixes it). Returns
+    this order free; it is fixed here so results repeat). Returns
       offsets     int32 [E+1]  rows of expert e are offsets[e]:offsets[e+1]
       slot_of_row int32 [R]    flat slot t*k+j held by dispatched row r
       row_of_slot int32 [T*k]  inverse map; -1 for an out-of-range expert id
