@@ -215,14 +215,24 @@ def route_sigmoid_grouped(logits, logits_dtype, bias, top_k, groups, selected_gr
     ids = np.broadcast_to(np.arange(E), (T, E))
     order = np.lexsort((ids, -masked), axis=-1)
     order[bad] = np.arange(E)
-    idx = order[:, :top_k]
-    w = np.take_along_axis(s, idx, axis=1).astype(np.float64)
-    if renormalize:
-        with np.errstate(invalid="ignore"):  # NaN rows, overwritten below
-            w = w / w.sum(axis=1, keepdims=True)
-    w = w * float(scale)
+    idx = order[:, :top_k].astype(np.uint32)
+    w = grouped_selection_weights(logits, logits_dtype, idx, renormalize, scale)
     w[bad] = np.nan
-    return idx.astype(np.uint32), round_to(w, logits_dtype)
+    return idx, w
+
+
+def grouped_selection_weights(logits, logits_dtype, indices, renormalize, scale):
+    """Step 5 of route_sigmoid_grouped for a given selection: the raw fp32
+    sigmoid scores s of the selected experts (the correction bias steers the
+    choice only), divided by their sum when renormalize is set, then times
+    scale, cast to the logits dtype. Any valid selection of a row (one that
+    the grouped rule could have produced) gets its weights from here."""
+    s = sigmoid_fp32(logits, logits_dtype)
+    w = np.take_along_axis(s, np.asarray(indices).astype(np.int64), axis=1).astype(np.float64)
+    if renormalize:
+        with np.errstate(invalid="ignore"):  # NaN rows stay NaN
+            w = w / w.sum(axis=1, keepdims=True)
+    return round_to(w * float(scale), logits_dtype)
 
 
 def route_sigmoid_grouped_margins(logits, logits_dtype, bias, top_k, groups, selected_groups,
@@ -328,15 +338,21 @@ def unpack_int4(packed: np.ndarray) -> np.ndarray:
     return np.where(out >= 8, out - 16, out)
 
 
-def dequant_weight(q, bits, scale, offset, groups, dtype):
-    """One expert's weight matrix [N, K] in the model dtype, returned as the
-    fp64 values of its stored elements:
-    w[n, k] = dtype((q[n, k] + offset[n, j]) * scale[n, j]), j = k // (K / groups).
-    The pseudo-quantisation formula brackets the dequantised weight as a
-    tensor of its own and gives scale and offset the activation dtype; it
-    does not say in what precision that tensor is held. Reading taken: it is
-    held in the activation dtype, as the weights of the unquantised path are,
-    so (q + offset) * scale is formed exactly and rounded once to dtype.
+def dequant_weight(q, bits, scale, offset, groups, dtype, round_weights=True):
+    """One expert's dequantised weight matrix [N, K] as fp64 values:
+        w[n, k] = (q[n, k] + offset[n, j]) * scale[n, j],  j = k // (K / groups)
+    (the pseudo-quantization formula of aclnnFFN, per channel or per group).
+    round_weights=True (the reading used for parity): w is a tensor in the
+    activation dtype, so the exact value is rounded once to dtype. The
+    formula puts the bracketed dequantised weight in the place that W holds
+    in the unquantised formula, where x and W are both activation-dtype
+    tensors, and the page's constraints give antiquantScale and
+    antiquantOffset the activation dtype (FLOAT16 with FLOAT16 x; BFLOAT16
+    with BFLOAT16 x). With integer offsets, q + offset is exact in the
+    activation dtype, so rounding the sum and then the product gives this
+    same single rounding.
+    round_weights=False: the exact fp64 value, not rounded (the plain
+    mathematical definition, for comparison).
     q: int8 [N, K] (bits 8) or packed int4 bytes [N, K/2] (bits 4); scale,
     offset: [N, groups] stored in dtype (offset None = 0)."""
     qi = unpack_int4(q) if bits == 4 else np.asarray(q).view(np.int8).astype(np.int16)
@@ -344,15 +360,18 @@ def dequant_weight(q, bits, scale, offset, groups, dtype):
     gs = K // groups
     sc = np.repeat(decode(scale, dtype).reshape(N, groups), gs, axis=1)
     off = 0.0 if offset is None else np.repeat(decode(offset, dtype).reshape(N, groups), gs, axis=1)
-    return decode(round_to((qi.astype(np.float64) + off) * sc, dtype), dtype)
+    w = (qi.astype(np.float64) + off) * sc
+    return decode(round_to(w, dtype), dtype) if round_weights else w
 
 
-def experts_forward_quant(x_disp, offsets, quant_of, bits, groups, dtype):
-    """Expert outputs for every dispatched row with quantised weights.
+def experts_forward_quant(x_disp, offsets, quant_of, bits, groups, dtype, round_weights=True):
+    """Expert outputs for every dispatched row with quantised weights: the
+    SwiGLU expert of swiglu_expert_f64 on the dequantised weights of
+    dequant_weight (round_weights as there).
     quant_of(e) -> ((q_gate, s_gate, o_gate), (q_up, s_up, o_up),
     (q_down, s_down, o_down)) for expert e."""
     def weights_f64(e):
-        return [dequant_weight(q, bits, sc, off, groups, dtype) for q, sc, off in quant_of(e)]
+        return [dequant_weight(q, bits, sc, off, groups, dtype, round_weights) for q, sc, off in quant_of(e)]
     R = int(offsets[-1])
     out = None
     for e in range(len(offsets) - 1):

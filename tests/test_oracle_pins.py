@@ -700,3 +700,141 @@ def test_quant_expert_reduces_to_plain_expert():
     y8 = O.swiglu_expert_f64(x, *[O.dequant_weight(q.view(np.uint8), 8, o, None, 1, "bf16")
                                   for q, o in zip(qs, ones)], "bf16")
     np.testing.assert_array_equal(y8, ref)
+
+
+# --------------------------------------------------------------------------
+# pins added for the grouped router's decision margins, the grouped forward
+# and the quantised experts as whole functions
+# --------------------------------------------------------------------------
+# All logits 0 give s = sigmoid(0) = 1/2 exactly, so with dyadic biases every
+# corrected score c = 1/2 + bias and every group score is exact in fp32:
+# c = [0.75, 0.625, 0.5625, 1.0, 0.25, 0.375, 0.875, 0.5] (groups of two:
+# {0,1} {2,3} {4,5} {6,7}); top-two group scores 1.375, 1.5625, 0.625, 1.375;
+# largest-score group scores 0.75, 1.0, 0.375, 0.875.
+_DYADIC_BIAS = np.array([0.25, 0.125, 0.0625, 0.5, -0.25, -0.125, 0.375, 0.0], np.float32)
+
+
+@pytest.mark.parametrize("k,SG,two,margin", [
+    (1, 1, True, 0.1875),   # groups: 1.5625 - 1.375; experts of group 1: 1.0 - 0.5625 = 0.4375
+    (2, 1, True, 0.1875),   # k + 1 = 3 exceeds the two kept experts: only their gap counts
+    (2, 2, True, 0.0),      # groups 0 and 3 tie (1.375) for the second kept place
+    (3, 3, True, 0.125),    # groups: 1.375 - 0.625 = 0.75; experts 1.0 .875 .75 .625: 0.125
+    (4, 4, True, 0.0625),   # every group kept (no group gap); top five c: ... .625 .5625
+    (1, 1, False, 0.125),   # largest-score groups: 1.0 - 0.875
+])
+def test_grouped_margins_closed_form(k, SG, two, margin):
+    z = np.zeros((1, 8), np.float32)
+    got = O.route_sigmoid_grouped_margins(z, "f32", _DYADIC_BIAS, k, 4, SG, two)
+    assert got.tolist() == [margin]
+
+
+def test_grouped_margins_scale_with_a_gap_planted_in_the_logits():
+    """Planting a logit gap d between the k-th and (k+1)-th expert of a row
+    (all in one group, no bias) gives a margin of at most s(a) - s(a - d),
+    which shrinks with d; the row without a planted gap keeps the larger
+    margin of its own spacing (also the margin of the d = 0.5 row, whose
+    planted gap is not its smallest)."""
+    E, k = 8, 3
+    base = np.array([3.0, 2.0, 1.0, 0.0, -1.0, -2.0, -3.0, -4.0], np.float32)
+    z = np.tile(base, (4, 1))
+    for r, d in enumerate((0.5, 0.05, 0.005)):
+        z[r, 3] = np.float32(1.0 - d)  # the 4th best now sits d below the 3rd
+    got = O.route_sigmoid_grouped_margins(z, "f32", None, k, 1, 1, False)
+    s = torch.sigmoid(torch.tensor(z, dtype=torch.float64)).float().double().numpy()
+    for r in range(4):
+        top = np.sort(s[r])[::-1][:k + 1]
+        assert got[r] == pytest.approx(np.diff(-top).min(), rel=0, abs=0)
+    assert got[2] < got[1] < got[0] == got[3]
+
+
+def test_grouped_forward_matches_weighted_dense_mixture():
+    """forward_sigmoid_grouped against a dense reference built without the
+    oracle's router or dispatch: with one group the choice is torch.topk of
+    sigmoid + bias, the weights the selected sigmoid scores normalised and
+    scaled, and the output the weighted sum of every selected expert's dense
+    SwiGLU (fp32 model dtype: only the rounding of h and of the output to
+    fp32 separate the two)."""
+    g = rng(61)
+    T, H, I, E, k, scale = 19, 8, 12, 6, 3, 2.5
+    x = g.standard_normal((T, H)).astype(np.float32)
+    z = g.standard_normal((T, E)).astype(np.float32)
+    bias = (g.standard_normal(E) * 0.5).astype(np.float32)
+    wg, wu, wd = _weights(g, E, H, I)
+    idx, w, d, y, out = O.forward_sigmoid_grouped(x, z, "f32", bias, k, 1, 1, False, True, scale,
+                                                  lambda e: (wg[e], wu[e], wd[e]), E, "f32")
+    s = torch.sigmoid(torch.from_numpy(z).double())
+    _, top = torch.topk(s.float() + torch.from_numpy(bias), k, dim=1)
+    np.testing.assert_array_equal(idx, top.numpy())
+    dense = np.stack([_torch_swiglu(x, wg[e], wu[e], wd[e]).numpy() for e in range(E)], 1)  # [T, E, H]
+    gate = np.zeros((T, E))
+    for t in range(T):
+        sel = top[t].numpy()
+        gate[t, sel] = s[t, sel].numpy() / s[t, sel].numpy().sum() * scale
+    ref = np.einsum("te,teh->th", gate, dense)
+    assert np.allclose(out, ref, rtol=1e-5, atol=1e-6)
+    # with three groups of two, keeping one: every token's experts share one group
+    idx3, _, _, _, _ = O.forward_sigmoid_grouped(x, z, "f32", bias, 2, 3, 1, True, True, 1.0,
+                                                 lambda e: (wg[e], wu[e], wd[e]), E, "f32")
+    assert (idx3[:, 0] // 2 == idx3[:, 1] // 2).all()
+
+
+def _quant_case(g, E, H, I_, bits, groups):
+    """Integer codes (as the kernel stores them) and power-of-two scales, so
+    that every dequantised weight is exact in bf16."""
+    def one(N, K):
+        v = g.integers(-8, 8, size=(E, N, K)).astype(np.int16)
+        if bits == 8:
+            q = v.astype(np.int8).view(np.uint8)
+        else:
+            q = ((v[..., 0::2] & 0xF) | ((v[..., 1::2] & 0xF) << 4)).astype(np.uint8)
+        sc = 2.0 ** g.integers(-6, -2, size=(E, N, groups))
+        off = g.integers(-2, 3, size=(E, N, groups)).astype(np.float64)
+        w = (v + np.repeat(off, K // groups, axis=2)) * np.repeat(sc, K // groups, axis=2)
+        return (q, _bf16(sc), _bf16(off)), _bf16(w)
+    return [one(I_, H), one(I_, H), one(H, I_)]
+
+
+@pytest.mark.parametrize("bits,groups", [(8, 1), (4, 1), (4, 2)])
+def test_experts_forward_quant_equals_plain_experts_on_exact_weights(bits, groups):
+    """experts_forward_quant on several experts, with the dispatch's offsets
+    (empty experts included), equals experts_forward_dispatched on the bf16
+    weights holding (q + offset) * scale, which are exact here: the codes,
+    offsets and scales must meet in the right expert, channel and group
+    (per-group scales differ between the two halves of K)."""
+    g = rng(62 + bits + groups)
+    E, H, I_, T, k = 5, 32, 48, 11, 2
+    case = _quant_case(g, E, H, I_, bits, groups)
+    x = _bf16(g.standard_normal((T, H)))
+    idx = np.stack([g.choice([0, 2, 3, 4], 2, replace=False) for _ in range(T)]).astype(np.uint32)
+    d = O.dispatch(idx, E, x)
+    assert d["offsets"][2] == d["offsets"][1]  # expert 1 gets no rows
+    quant_of = lambda e: tuple((c[0][0][e], c[0][1][e], c[0][2][e]) for c in case)  # noqa: E731
+    plain = lambda e: tuple(c[1][e] for c in case)  # noqa: E731
+    ref = O.experts_forward_dispatched(d["x_disp"], d["offsets"], plain, "bf16")
+    for rw in (True, False):
+        got = O.experts_forward_quant(d["x_disp"], d["offsets"], quant_of, bits, groups, "bf16", rw)
+        np.testing.assert_array_equal(got, ref)
+
+
+def test_experts_forward_quant_exact_variant_keeps_unrounded_weights():
+    """With scales that make (q + offset) * scale inexact in bf16, the exact
+    variant equals the SwiGLU expert on the fp64 dequantised weights, and the
+    rounded variant the same expert on those weights rounded to bf16."""
+    g = rng(66)
+    E, H, I_, T = 2, 16, 24, 6
+    qs = [g.integers(-127, 128, size=s).astype(np.int8) for s in ((E, I_, H), (E, I_, H), (E, H, I_))]
+    scs = [_bf16(1.0 + np.abs(g.standard_normal((E, q.shape[1], 1))) / 7) for q in qs]
+    offs = [_bf16(g.standard_normal((E, q.shape[1], 1))) for q in qs]  # not integers
+    x = _bf16(g.standard_normal((T, H)))
+    d = O.dispatch(np.array([[0], [1]] * (T // 2), np.uint32), E, x)
+    quant_of = lambda e: tuple((q[e].view(np.uint8), s[e], o[e]) for q, s, o in zip(qs, scs, offs))  # noqa: E731
+    exact = O.experts_forward_quant(d["x_disp"], d["offsets"], quant_of, 8, 1, "bf16", False)
+    rounded = O.experts_forward_quant(d["x_disp"], d["offsets"], quant_of, 8, 1, "bf16", True)
+    for e in range(E):
+        lo, hi = int(d["offsets"][e]), int(d["offsets"][e + 1])
+        wf = [(q[e].astype(np.float64) + O.decode(o[e], "bf16")) * O.decode(s[e], "bf16")
+              for q, s, o in zip(qs, scs, offs)]
+        np.testing.assert_array_equal(exact[lo:hi], O.swiglu_expert_f64(x[e::2], *wf, "bf16"))
+        wr = [O.decode(_bf16(a), "bf16") for a in wf]
+        np.testing.assert_array_equal(rounded[lo:hi], O.swiglu_expert_f64(x[e::2], *wr, "bf16"))
+    assert not np.array_equal(exact, rounded)  # the weights' rounding is visible here
