@@ -30,6 +30,14 @@
  *  - Sizes are int64_t; T*top_k must fit in int32; E <= 1024.
  *  - Row lengths H and I must be multiples of 8 elements (16 bytes of
  *    bf16/f16; fp32 tensors are also read in 8-element steps).
+ *  - bf16 / f16 expert GEMMs (every call that runs them: the experts calls,
+ *    the forward calls and the experts' training forward) address their
+ *    operands with 32-bit byte offsets. They return UNSUPPORTED, before
+ *    enqueueing anything, unless each of these is below 2^31 bytes: the
+ *    token rows the gate/up GEMM reads (x_disp, or x when read through a
+ *    map: a_rows * H * b), h (rows * I * b), one expert's weight matrix
+ *    (I * H * b), and 256 * max(H, 2 * I) * 4. (b = 2; fp32 experts use
+ *    64-bit addressing and have no such limit.)
  */
 #ifndef MOE_FFN_H
 #define MOE_FFN_H
@@ -58,7 +66,8 @@ typedef enum moe_status {
   MOE_ERROR_DEVICE = 5,       /* a pointer is not device memory of the stream's device */
   MOE_ERROR_WORKSPACE = 6,    /* workspace NULL, misaligned or too small */
   MOE_ERROR_UNSUPPORTED = 7,  /* E > 1024, T*top_k > INT32_MAX, H or I not a multiple of 8,
-                                 a row of H elements longer than INT32_MAX bytes */
+                                 a row of H elements longer than INT32_MAX bytes, or a bf16 /
+                                 f16 expert GEMM operand of 2^31 bytes or more (see below) */
   MOE_ERROR_HIP = 8           /* a HIP launch or query failed */
 } moe_status;
 
@@ -206,6 +215,9 @@ moe_status moe_combine(const void* expert_out, const int32_t* row_of_slot, const
  *   moe_experts_forward_dispatched; out [T, H] dt (written).
  *   indices_out [T, top_k] uint32 and weights_out [T, top_k] logits_dt are
  *   optional copies of the routing plan (NULL to skip).
+ *   offsets_out [E+1] int32, optional (NULL to skip): the per-expert row
+ *   offsets of the dispatch (expert_offsets of moe_dispatch), so a caller can
+ *   read the expert loads without a second dispatch.
  *   ws / ws_bytes scratch, at least moe_forward_workspace_size(...).
  *   stage_events: NULL, or 6 caller-created HIP events recorded on `stream`
  *   before route, after route, after dispatch, after the gate/up GEMM, after
@@ -215,7 +227,8 @@ moe_status moe_forward(const void* x, const void* logits, moe_dtype logits_dt, i
                        int64_t H, int64_t I, int64_t E, int64_t top_k, int renormalize,
                        const void* w_gate, const void* w_up, const void* w_down, moe_dtype dt,
                        void* out, uint32_t* indices_out, void* weights_out,
-                       void* ws, size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream);
+                       int32_t* offsets_out, void* ws, size_t ws_bytes,
+                       hipEvent_t* stage_events, hipStream_t stream);
 size_t moe_forward_workspace_size(int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k,
                                   moe_dtype dt, moe_dtype logits_dt);
 
@@ -265,8 +278,8 @@ moe_status moe_forward_sigmoid_grouped(const void* x, const void* logits, moe_dt
                                        int renormalize, float scale, const void* w_gate,
                                        const void* w_up, const void* w_down, moe_dtype dt,
                                        void* out, uint32_t* indices_out, void* weights_out,
-                                       void* ws, size_t ws_bytes, hipEvent_t* stage_events,
-                                       hipStream_t stream);
+                                       int32_t* offsets_out, void* ws, size_t ws_bytes,
+                                       hipEvent_t* stage_events, hipStream_t stream);
 
 /*
  * moe_combine_add_rmsnorm - combine fused with the shared-expert term, the
@@ -398,8 +411,9 @@ moe_status moe_forward_quant(const void* x, const void* logits, moe_dtype logits
                              int64_t groups, const void* scale_gate, const void* scale_up,
                              const void* scale_down, const void* offset_gate,
                              const void* offset_up, const void* offset_down, moe_dtype dt,
-                             void* out, uint32_t* indices_out, void* weights_out, void* ws,
-                             size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream);
+                             void* out, uint32_t* indices_out, void* weights_out,
+                             int32_t* offsets_out, void* ws, size_t ws_bytes,
+                             hipEvent_t* stage_events, hipStream_t stream);
 
 /* ===================== first-order training ===================== */
 /*

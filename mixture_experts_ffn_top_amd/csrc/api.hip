@@ -84,6 +84,26 @@ bool row_len_ok(int64_t n) { return n > 0 && n % 8 == 0; }
 // 32-bit range is the row's byte length.
 bool row_bytes_ok(int64_t H, moe_dtype dt) { return H * (int64_t)dtype_size(dt) <= INT32_MAX; }
 
+// n * m * ds < 2^31 without overflowing (n, m >= 0, m * ds <= 2^33).
+bool below_2g(int64_t n, int64_t m, int64_t ds) {
+  return n == 0 || m == 0 || (m <= INT32_MAX && n <= INT32_MAX / (m * ds));
+}
+
+// The bf16 / f16 expert GEMMs (the tiled matrix-core kernel and the decode
+// kernel) address every operand through a buffer resource with a 32-bit byte
+// range, and mask a load or store by giving it the offset 2^31, which must
+// lie outside every range. So the token rows they read (a_rows x H), h
+// (rows x I), one expert's weight matrix (I x H), and one 256-row output tile
+// of up to 2I fp32 columns (the training cache stores g and u side by side)
+// must each stay below 2^31 bytes. The fp32 path uses 64-bit pointers and is
+// not limited.
+bool gemm_bytes_ok(int64_t a_rows, int64_t rows, int64_t H, int64_t I, moe_dtype dt) {
+  if (dt == MOE_F32) return true;
+  const int64_t ds = (int64_t)dtype_size(dt);
+  return below_2g(a_rows, H, ds) && below_2g(rows, I, ds) && below_2g(I, H, ds) &&
+         below_2g(256, std::max(H, 2 * I), 4);
+}
+
 // Options of the grouped-limited sigmoid router (ruDNN user guide, "10.
 // Grouped-limited sigmoid MoE routing"), validated after check_route_args.
 moe_status check_grouped_args(int64_t E, int64_t top_k, int64_t groups, int64_t selected_groups,
@@ -276,7 +296,8 @@ moe_status moe_experts_forward_dispatched(const void* x_disp, const int32_t* exp
                                           void* ws, size_t ws_bytes, hipStream_t stream) {
   if (rows < 0 || E < 1 || H < 1 || I < 1) return MOE_ERROR_SHAPE;
   if (!valid_dt(dt)) return MOE_ERROR_DTYPE;
-  if (E > kMaxE || rows > INT32_MAX || !row_len_ok(H) || !row_len_ok(I))
+  if (E > kMaxE || rows > INT32_MAX || !row_len_ok(H) || !row_len_ok(I) ||
+      !gemm_bytes_ok(rows, rows, H, I, dt))
     return MOE_ERROR_UNSUPPORTED;
   if (rows == 0) return MOE_SUCCESS;
   if (!x_disp || !expert_offsets || !w_gate || !w_up || !w_down || !expert_out)
@@ -310,7 +331,8 @@ moe_status moe_experts_gate_up(const void* x, const int32_t* row_map, int64_t ma
   if (rows < 0 || E < 1 || H < 1 || I < 1) return MOE_ERROR_SHAPE;
   if (!valid_dt(dt)) return MOE_ERROR_DTYPE;
   if (row_map && (map_div < 1 || map_div > rows)) return MOE_ERROR_ARGUMENT;
-  if (E > kMaxE || rows > INT32_MAX || !row_len_ok(H) || !row_len_ok(I))
+  if (E > kMaxE || rows > INT32_MAX || !row_len_ok(H) || !row_len_ok(I) ||
+      !gemm_bytes_ok(row_map ? (rows + map_div - 1) / map_div : rows, rows, H, I, dt))
     return MOE_ERROR_UNSUPPORTED;
   if (rows == 0) return MOE_SUCCESS;
   if (!x || !expert_offsets || !w_gate || !w_up || !h) return MOE_ERROR_NULL_POINTER;
@@ -334,7 +356,8 @@ moe_status moe_experts_down(const void* h, const int32_t* expert_offsets, int64_
                             void* expert_out, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (rows < 0 || E < 1 || H < 1 || I < 1) return MOE_ERROR_SHAPE;
   if (!valid_dt(dt)) return MOE_ERROR_DTYPE;
-  if (E > kMaxE || rows > INT32_MAX || !row_len_ok(H) || !row_len_ok(I))
+  if (E > kMaxE || rows > INT32_MAX || !row_len_ok(H) || !row_len_ok(I) ||
+      !gemm_bytes_ok(rows, rows, H, I, dt))
     return MOE_ERROR_UNSUPPORTED;
   if (rows == 0) return MOE_SUCCESS;
   if (!h || !expert_offsets || !w_down || !expert_out) return MOE_ERROR_NULL_POINTER;
@@ -413,13 +436,15 @@ namespace {
 moe_status forward_impl(const void* x, const void* logits, moe_dtype logits_dt, int64_t T,
                         int64_t H, int64_t I, int64_t E, int64_t top_k, const Router& router,
                         const void* w_gate, const void* w_up, const void* w_down, moe_dtype dt,
-                        void* out, uint32_t* indices_out, void* weights_out, void* ws,
-                        size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream,
+                        void* out, uint32_t* indices_out, void* weights_out,
+                        int32_t* offsets_out, void* ws, size_t ws_bytes,
+                        hipEvent_t* stage_events, hipStream_t stream,
                         const QuantWeights* quant = nullptr) {
   if (H < 1 || I < 1) return MOE_ERROR_SHAPE;
   moe_status st = MOE_SUCCESS;
   if (!valid_dt(dt)) return MOE_ERROR_DTYPE;
   if (!row_len_ok(H) || !row_len_ok(I) || !row_bytes_ok(H, dt)) return MOE_ERROR_UNSUPPORTED;
+  if (!quant && !gemm_bytes_ok(T, T * top_k, H, I, dt)) return MOE_ERROR_UNSUPPORTED;
   if (T == 0) return MOE_SUCCESS;
   if (!x || !logits || !w_gate || !w_up || !w_down || !out) return MOE_ERROR_NULL_POINTER;
   const ForwardLayout L = forward_layout(T, H, I, E, top_k, dt, logits_dt);
@@ -427,18 +452,20 @@ moe_status forward_impl(const void* x, const void* logits, moe_dtype logits_dt, 
   const size_t ds = dtype_size(dt), ls = dtype_size(logits_dt), slots = (size_t)(T * top_k);
   const size_t wbytes = quant ? quant_bytes(E, I, H, quant->bits) : (size_t)E * (size_t)I * (size_t)H * ds;
   const Span outs[] = {{out, (size_t)T * (size_t)H * ds}, {indices_out, indices_out ? slots * 4 : 0},
-                       {weights_out, weights_out ? slots * ls : 0}, {ws, L.total}};
+                       {weights_out, weights_out ? slots * ls : 0},
+                       {offsets_out, offsets_out ? (size_t)(E + 1) * 4 : 0}, {ws, L.total}};
   const Span ins[] = {{x, (size_t)T * (size_t)H * ds}, {logits, (size_t)(T * E) * ls},
                       {w_gate, wbytes}, {w_up, wbytes}, {w_down, wbytes}};
   const Span bias_in[] = {{router.bias, router.bias ? (size_t)E * 4 : 0}};
-  if (any_overlap(outs, 4, ins, 5) || any_overlap(outs, 4, bias_in, 1)) return MOE_ERROR_ARGUMENT;
-  const void* ptrs[] = {x, logits, w_gate, w_up, w_down, out, indices_out, weights_out, ws, router.bias};
-  if ((st = check_device(ptrs, 10, stream)) != MOE_SUCCESS) return st;
+  if (any_overlap(outs, 5, ins, 5) || any_overlap(outs, 5, bias_in, 1)) return MOE_ERROR_ARGUMENT;
+  const void* ptrs[] = {x,           logits,      w_gate,      w_up, w_down,     out,
+                        indices_out, weights_out, offsets_out, ws,   router.bias};
+  if ((st = check_device(ptrs, 11, stream)) != MOE_SUCCESS) return st;
 
   char* base = static_cast<char*>(ws);
   uint32_t* idx = indices_out ? indices_out : reinterpret_cast<uint32_t*>(base + L.indices);
   void* w = weights_out ? weights_out : static_cast<void*>(base + L.weights);
-  int32_t* offsets = reinterpret_cast<int32_t*>(base + L.offsets);
+  int32_t* offsets = offsets_out ? offsets_out : reinterpret_cast<int32_t*>(base + L.offsets);
   int32_t* sor = reinterpret_cast<int32_t*>(base + L.slot_of_row);
   int32_t* ros = reinterpret_cast<int32_t*>(base + L.row_of_slot);
   void* y = base + L.expert_out;
@@ -500,15 +527,16 @@ extern "C" {
 moe_status moe_forward(const void* x, const void* logits, moe_dtype logits_dt, int64_t T,
                        int64_t H, int64_t I, int64_t E, int64_t top_k, int renormalize,
                        const void* w_gate, const void* w_up, const void* w_down, moe_dtype dt,
-                       void* out, uint32_t* indices_out, void* weights_out, void* ws,
-                       size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream) {
+                       void* out, uint32_t* indices_out, void* weights_out,
+                       int32_t* offsets_out, void* ws, size_t ws_bytes,
+                       hipEvent_t* stage_events, hipStream_t stream) {
   if (H < 1 || I < 1) return MOE_ERROR_SHAPE;
   const moe_status st = check_route_args(T, E, top_k, logits_dt);
   if (st != MOE_SUCCESS) return st;
   Router r;
   r.renormalize = renormalize ? 1 : 0;
   return forward_impl(x, logits, logits_dt, T, H, I, E, top_k, r, w_gate, w_up, w_down, dt, out,
-                      indices_out, weights_out, ws, ws_bytes, stage_events, stream);
+                      indices_out, weights_out, offsets_out, ws, ws_bytes, stage_events, stream);
 }
 
 moe_status moe_route_sigmoid_grouped(const void* logits, moe_dtype logits_dt, int64_t T, int64_t E,
@@ -540,8 +568,8 @@ moe_status moe_forward_sigmoid_grouped(const void* x, const void* logits, moe_dt
                                        int renormalize, float scale, const void* w_gate,
                                        const void* w_up, const void* w_down, moe_dtype dt,
                                        void* out, uint32_t* indices_out, void* weights_out,
-                                       void* ws, size_t ws_bytes, hipEvent_t* stage_events,
-                                       hipStream_t stream) {
+                                       int32_t* offsets_out, void* ws, size_t ws_bytes,
+                                       hipEvent_t* stage_events, hipStream_t stream) {
   if (H < 1 || I < 1) return MOE_ERROR_SHAPE;
   moe_status st = check_route_args(T, E, top_k, logits_dt);
   if (st != MOE_SUCCESS) return st;
@@ -556,7 +584,7 @@ moe_status moe_forward_sigmoid_grouped(const void* x, const void* logits, moe_dt
   r.group_top_two = group_top_two ? 1 : 0;
   r.scale = scale;
   return forward_impl(x, logits, logits_dt, T, H, I, E, top_k, r, w_gate, w_up, w_down, dt, out,
-                      indices_out, weights_out, ws, ws_bytes, stage_events, stream);
+                      indices_out, weights_out, offsets_out, ws, ws_bytes, stage_events, stream);
 }
 
 }  // extern "C"
@@ -699,8 +727,9 @@ moe_status moe_forward_quant(const void* x, const void* logits, moe_dtype logits
                              int64_t groups, const void* scale_gate, const void* scale_up,
                              const void* scale_down, const void* offset_gate,
                              const void* offset_up, const void* offset_down, moe_dtype dt,
-                             void* out, uint32_t* indices_out, void* weights_out, void* ws,
-                             size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream) {
+                             void* out, uint32_t* indices_out, void* weights_out,
+                             int32_t* offsets_out, void* ws, size_t ws_bytes,
+                             hipEvent_t* stage_events, hipStream_t stream) {
   if (H < 1 || I < 1) return MOE_ERROR_SHAPE;
   moe_status st = check_route_args(T, E, top_k, logits_dt);
   if (st != MOE_SUCCESS) return st;
@@ -723,7 +752,7 @@ moe_status moe_forward_quant(const void* x, const void* logits, moe_dtype logits
   qw.s_gate = scale_gate; qw.s_up = scale_up; qw.s_down = scale_down;
   qw.o_gate = offset_gate; qw.o_up = offset_up; qw.o_down = offset_down;
   return forward_impl(x, logits, logits_dt, T, H, I, E, top_k, r, w_gate, w_up, w_down, dt, out,
-                      indices_out, weights_out, ws, ws_bytes, stage_events, stream, &qw);
+                      indices_out, weights_out, offsets_out, ws, ws_bytes, stage_events, stream, &qw);
 }
 
 // ---- first-order training (ruDNN user guide, "12. MoE first-order training") ----
@@ -828,6 +857,8 @@ static moe_status check_train_args(int64_t rows, int64_t E, int64_t H, int64_t I
   if (dt == MOE_F32) return MOE_ERROR_UNSUPPORTED;  // the matrix-core path is bf16 / f16
   if (E > kMaxE || rows > INT32_MAX || !row_len_ok(H) || !row_len_ok(I)) return MOE_ERROR_UNSUPPORTED;
   if ((int64_t)E * I * H > INT64_MAX / 8 || 2 * I > INT32_MAX) return MOE_ERROR_UNSUPPORTED;
+  // the training forward runs the inference gate/up and down GEMMs
+  if (!gemm_bytes_ok(rows, rows, H, I, dt)) return MOE_ERROR_UNSUPPORTED;
   // the training GEMM keeps a lane's offset inside a 256-row tile in 32 bits
   // (leading dimensions up to 2^22 elements) and numbers its tiles in int
   if (H > (1 << 22) || 2 * I > (1 << 22)) return MOE_ERROR_UNSUPPORTED;

@@ -45,7 +45,7 @@ _SIGS = {
     "moe_experts_down": ([P, P, I64, I64, I64, I64, P, I32, P, P, SZ, P], I32),
     "moe_experts_gemm_workspace_size": ([I64, I64, I64, I64, I32], SZ),
     "moe_combine": ([P, P, P, I32, I64, I64, I64, I32, P, P], I32),
-    "moe_forward": ([P, P, I32, I64, I64, I64, I64, I64, I32, P, P, P, I32, P, P, P, P, SZ, P, P], I32),
+    "moe_forward": ([P, P, I32, I64, I64, I64, I64, I64, I32, P, P, P, I32, P, P, P, P, P, SZ, P, P], I32),
     "moe_forward_workspace_size": ([I64, I64, I64, I64, I64, I32, I32], SZ),
     "moe_dispatch_masked": ([P, P, I32, I64, I64, I64, P, I32, I64, P, P, P, P, P, SZ, P], I32),
     "moe_combine_special": ([P, P, P, P, I32, I64, I64, I64, I32, I64, I64, I64, I64, P, P, P, P, P, I32,
@@ -56,11 +56,11 @@ _SIGS = {
                                               I32, P, P, SZ, P], I32),
     "moe_experts_quant_workspace_size": ([I64, I64, I64, I64, I32], SZ),
     "moe_forward_quant": ([P, P, I32, I64, I64, I64, I64, I64, I32, P, P, P, I32, I64, P, P, P, P, P, P, I32,
-                           P, P, P, P, SZ, P, P], I32),
+                           P, P, P, P, P, SZ, P, P], I32),
     "moe_route_sigmoid_grouped": ([P, I32, I64, I64, P, I64, I64, I64, I32, I32, ctypes.c_float, P, P, P],
                                   I32),
     "moe_forward_sigmoid_grouped": ([P, P, I32, I64, I64, I64, I64, P, I64, I64, I64, I32, I32,
-                                     ctypes.c_float, P, P, P, I32, P, P, P, P, SZ, P, P], I32),
+                                     ctypes.c_float, P, P, P, I32, P, P, P, P, P, SZ, P, P], I32),
     "moe_combine_add_rmsnorm": ([P, P, P, I32, P, P, P, ctypes.c_float, I64, I64, I64, I32, P, P,
                                  P, P], I32),
     "moe_router_weights": ([P, I32, P, I32, I64, I64, I64, I32, I32, ctypes.c_float, P, P], I32),
@@ -150,14 +150,15 @@ def moe_dispatch(indices, E: int, x=None, with_x_disp: bool = True, ws=None, off
 
 
 def moe_dispatch_masked(indices, E: int, active=None, x=None, with_x_disp: bool = True, ws=None,
-                        offsets=None, slot_of_row=None, row_of_slot=None):
+                        offsets=None, slot_of_row=None, row_of_slot=None, x_disp=None):
     """moe_dispatch with an activity mask: active None, uint8/bool [T] (per token)
     or [T, k] (per slot). Returns the same dict as moe_dispatch."""
     T, k = indices.shape
     dev = indices.device
     H = x.shape[1] if x is not None else 0
     dt = dtype_code(x.dtype) if x is not None else BF16
-    x_disp = torch.empty((T * k, H), dtype=x.dtype, device=dev) if (x is not None and with_x_disp) else None
+    if x_disp is None and x is not None and with_x_disp:
+        x_disp = torch.empty((T * k, H), dtype=x.dtype, device=dev)
     offsets = torch.empty(E + 1, dtype=torch.int32, device=dev) if offsets is None else offsets
     sor = torch.empty(T * k, dtype=torch.int32, device=dev) if slot_of_row is None else slot_of_row
     ros = torch.empty(T * k, dtype=torch.int32, device=dev) if row_of_slot is None else row_of_slot
@@ -276,9 +277,10 @@ def moe_forward_workspace_size(T, H, I, E, top_k, dt, logits_dt) -> int:
 
 
 def moe_forward(x, logits, top_k: int, renormalize: bool, w_gate, w_up, w_down, out=None,
-                indices_out=None, weights_out=None, ws=None, stage_events=None):
+                indices_out=None, weights_out=None, ws=None, stage_events=None, offsets_out=None):
     """stage_events: optional list of 6 torch.cuda.Event (recorded at the stage
-    boundaries on the current stream, for per-stage timing)."""
+    boundaries on the current stream, for per-stage timing). offsets_out:
+    optional int32 [E+1] tensor receiving the dispatch's per-expert offsets."""
     T, H = x.shape
     E = logits.shape[1]
     I = w_gate.shape[1]
@@ -294,7 +296,7 @@ def moe_forward(x, logits, top_k: int, renormalize: bool, w_gate, w_up, w_down, 
     _check(lib().moe_forward(_ptr(x), _ptr(logits), dtype_code(logits.dtype), T, H, I, E, top_k,
                              int(renormalize), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
                              dtype_code(x.dtype), _ptr(out), _ptr(indices_out), _ptr(weights_out),
-                             _ptr(ws), ws.numel(), ev, _stream()), "moe_forward")
+                             _ptr(offsets_out), _ptr(ws), ws.numel(), ev, _stream()), "moe_forward")
     return out
 
 
@@ -318,7 +320,7 @@ def moe_route_sigmoid_grouped(logits, top_k: int, groups: int, selected_groups: 
 def moe_forward_sigmoid_grouped(x, logits, top_k: int, groups: int, selected_groups: int,
                                 group_top_two: bool, renormalize: bool, scale: float, w_gate, w_up,
                                 w_down, bias=None, out=None, indices_out=None, weights_out=None,
-                                ws=None, stage_events=None):
+                                ws=None, stage_events=None, offsets_out=None):
     """moe_forward with the grouped-limited sigmoid router."""
     T, H = x.shape
     E = logits.shape[1]
@@ -336,7 +338,8 @@ def moe_forward_sigmoid_grouped(x, logits, top_k: int, groups: int, selected_gro
         _ptr(x), _ptr(logits), dtype_code(logits.dtype), T, H, I, E, _ptr(bias), top_k, groups,
         selected_groups, int(group_top_two), int(renormalize), float(scale), _ptr(w_gate),
         _ptr(w_up), _ptr(w_down), dtype_code(x.dtype), _ptr(out), _ptr(indices_out),
-        _ptr(weights_out), _ptr(ws), ws.numel(), ev, _stream()), "moe_forward_sigmoid_grouped")
+        _ptr(weights_out), _ptr(offsets_out), _ptr(ws), ws.numel(), ev, _stream()),
+        "moe_forward_sigmoid_grouped")
     return out
 
 
@@ -362,7 +365,7 @@ def moe_experts_forward_dispatched_quant(x_disp, expert_offsets, w_gate, w_up, w
 
 def moe_forward_quant(x, logits, top_k: int, renormalize: bool, w_gate, w_up, w_down, bits: int, scales,
                       offsets=(None, None, None), groups: int = 1, out=None, indices_out=None,
-                      weights_out=None, ws=None, stage_events=None):
+                      weights_out=None, ws=None, stage_events=None, offsets_out=None):
     """moe_forward with weight-only quantised experts (see the dispatched variant)."""
     T, H = x.shape
     E = logits.shape[1]
@@ -379,8 +382,8 @@ def moe_forward_quant(x, logits, top_k: int, renormalize: bool, w_gate, w_up, w_
     _check(lib().moe_forward_quant(
         _ptr(x), _ptr(logits), dtype_code(logits.dtype), T, H, I, E, top_k, int(renormalize), _ptr(w_gate),
         _ptr(w_up), _ptr(w_down), bits, groups, *[_ptr(t) for t in scales], *[_ptr(t) for t in offsets],
-        dtype_code(x.dtype), _ptr(out), _ptr(indices_out), _ptr(weights_out), _ptr(ws), ws.numel(), ev,
-        _stream()), "moe_forward_quant")
+        dtype_code(x.dtype), _ptr(out), _ptr(indices_out), _ptr(weights_out), _ptr(offsets_out), _ptr(ws),
+        ws.numel(), ev, _stream()), "moe_forward_quant")
     return out
 
 

@@ -137,8 +137,10 @@ def test_forward_validation_and_workspace_query():
     assert need >= 4096 * 2 * (14336 + 4096) * 2
     assert q(4, 128, 256, 8, 9, 2, 0) == 0
     f = lib.moe_forward
+    # x, logits, logits_dt, T, H, I, E, k, renorm, wg, wu, wd, dt, out, indices_out, weights_out,
+    # offsets_out, ws, ws_bytes, stage_events, stream
     base = [FAKE, FAKE + 2**20, 0, 64, 128, 256, 8, 2, 1, FAKE + 2**21, FAKE + 2**22, FAKE + 2**23,
-            0, FAKE + 2**24, None, None, FAKE + 2**26, q(64, 128, 256, 8, 2, 0, 0), None, None]
+            0, FAKE + 2**24, None, None, None, FAKE + 2**26, q(64, 128, 256, 8, 2, 0, 0), None, None]
 
     def call(i=None, v=None):
         a = list(base)
@@ -149,10 +151,12 @@ def test_forward_validation_and_workspace_query():
     assert call(7, 9) == S["MOE_ERROR_ARGUMENT"]
     assert call(12, 4) == S["MOE_ERROR_DTYPE"]
     assert call(5, 250) == S["MOE_ERROR_UNSUPPORTED"]
-    assert call(17, 10) == S["MOE_ERROR_WORKSPACE"]
+    assert call(18, 10) == S["MOE_ERROR_WORKSPACE"]
     assert call(0, None) == S["MOE_ERROR_NULL_POINTER"]
     assert call(3, 0) == S["MOE_SUCCESS"]
     assert call(13, FAKE + 64) == S["MOE_ERROR_ARGUMENT"]  # out overlaps x
+    assert call(16, FAKE + 2**24 + 64) == S["MOE_ERROR_ARGUMENT"]  # offsets_out overlaps out
+    assert call(16, FAKE + 2**26 + 256) == S["MOE_ERROR_ARGUMENT"]  # offsets_out inside the workspace
 
 
 def test_grouped_route_validation():
@@ -185,7 +189,7 @@ def test_grouped_route_validation():
     g = moe.lib().moe_forward_sigmoid_grouped
     q = moe.lib().moe_forward_workspace_size(64, 128, 256, 16, 4, 2, 0)
     fb = [FAKE, FAKE + 2**20, 0, 64, 128, 256, 16, None, 4, 4, 2, 1, 1, 1.0, FAKE + 2**21,
-          FAKE + 2**22, FAKE + 2**23, 2, FAKE + 2**24, None, None, FAKE + 2**26, q, None, None]
+          FAKE + 2**22, FAKE + 2**23, 2, FAKE + 2**24, None, None, None, FAKE + 2**26, q, None, None]
     a = list(fb)
     a[9] = 5  # groups must divide E = 16
     assert g(*a) == S["MOE_ERROR_ARGUMENT"]
@@ -308,3 +312,73 @@ def test_training_validation():
     assert call(bw, okw, 14, None) == S["MOE_ERROR_NULL_POINTER"]
     assert call(bw, okw, 17, need_b - 1) == S["MOE_ERROR_WORKSPACE"]
     assert call(bw, okw, 14, FAKE + 2**31 + 4) == S["MOE_ERROR_ARGUMENT"]  # dup overlaps dgate
+
+
+def test_gemm_operands_of_2_gib_are_unsupported():
+    """The bf16 / f16 expert GEMMs address operands with 32-bit byte offsets:
+    every entry point that reaches them rejects, before any device query, an
+    operand of 2^31 bytes or more, and accepts the same shape one size step
+    below (the call then fails later, on the fake pointers, with another
+    status). fp32 experts use 64-bit addressing and are not limited."""
+    lib = moe.lib()
+    U = S["MOE_ERROR_UNSUPPORTED"]
+    ws = FAKE + 2**40
+
+    def experts(rows, H, I_, dt=2):
+        return lib.moe_experts_forward_dispatched(FAKE, FAKE + 2**38, rows, 8, H, I_, FAKE + 2**39,
+                                                  FAKE + 2**41, FAKE + 2**42, dt, FAKE + 2**43, ws,
+                                                  2**44, None)
+
+    # h [rows, I]: 131072 rows of the Mixtral expert width (3.76 GB) against 65536 (1.88 GB)
+    assert experts(131072, 4096, 14336) == U
+    assert experts(65536, 4096, 14336) != U
+    assert experts(131072, 4096, 14336, dt=1) == U    # f16 too
+    assert experts(131072, 4096, 14336, dt=0) != U    # fp32: 64-bit pointers
+    # x_disp [rows, H]: 16384 rows of 65536 elements is exactly 2^31 bytes
+    assert experts(16384, 65536, 8) == U
+    assert experts(16383, 65536, 8) != U
+    # one expert's weight matrix [I, H]: 32768 x 32768 bf16 is 2^31 bytes
+    assert experts(8, 32768, 32768) == U
+    assert experts(8, 32768, 32760) != U
+    # a 256-row fp32 output tile of H = 2^21 columns
+    assert experts(1, 2**21, 8) == U
+    assert experts(1, 2**21 - 8, 8) != U
+
+    def gate_up(rows, div, H, I_):
+        return lib.moe_experts_gate_up(FAKE, FAKE + 2**38, div, FAKE + 2**37, rows, 8, H, I_, FAKE + 2**39,
+                                       FAKE + 2**41, 2, FAKE + 2**43, ws, 2**44, None)
+
+    # token rows read through the map: ceil(rows / div) rows of x
+    assert gate_up(131072, 8, 65536, 8) == U
+    assert gate_up(131072, 9, 65536, 8) != U
+
+    def down(rows, H, I_):
+        return lib.moe_experts_down(FAKE, FAKE + 2**38, rows, 8, H, I_, FAKE + 2**39, 2, FAKE + 2**43, ws,
+                                    2**44, None)
+
+    assert down(131072, 4096, 14336) == U
+    assert down(65536, 4096, 14336) != U
+
+    def forward(T, k, H, I_, grouped=False):
+        if grouped:
+            return lib.moe_forward_sigmoid_grouped(FAKE, FAKE + 2**36, 0, T, H, I_, 8, None, k, 1, 1, 0, 1,
+                                                   1.0, FAKE + 2**39, FAKE + 2**41, FAKE + 2**42, 2,
+                                                   FAKE + 2**43, None, None, None, ws, 2**45, None, None)
+        return lib.moe_forward(FAKE, FAKE + 2**36, 0, T, H, I_, 8, k, 1, FAKE + 2**39, FAKE + 2**41,
+                               FAKE + 2**42, 2, FAKE + 2**43, None, None, None, ws, 2**45, None, None)
+
+    assert forward(65536, 2, 4096, 14336) == U          # h = 131072 x 14336 bf16
+    assert forward(32768, 2, 4096, 14336) != U
+    assert forward(65536, 2, 4096, 14336, grouped=True) == U
+    assert forward(32768, 2, 4096, 14336, grouped=True) != U
+    assert forward(16384, 1, 65536, 8) == U             # x [T, H] read by the gate/up GEMM
+    assert forward(16383, 1, 65536, 8) != U
+
+    # the experts' training forward runs the same GEMMs
+    def train(rows, H, I_):
+        return lib.moe_experts_forward_training(FAKE, FAKE + 2**38, rows, 8, H, I_, FAKE + 2**39,
+                                                FAKE + 2**41, FAKE + 2**42, 2, FAKE + 2**43, FAKE + 2**44,
+                                                ws, 2**45, None)
+
+    assert train(131072, 4096, 14336) == U
+    assert train(65536, 4096, 14336) != U
