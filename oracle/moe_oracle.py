@@ -216,9 +216,18 @@ def route_sigmoid_grouped(logits, logits_dtype, bias, top_k, groups, selected_gr
     order = np.lexsort((ids, -masked), axis=-1)
     order[bad] = np.arange(E)
     idx = order[:, :top_k].astype(np.uint32)
-    w = grouped_selection_weights(logits, logits_dtype, idx, renormalize, scale)
+    w = _grouped_weights_f64(logits, logits_dtype, idx, renormalize, scale)
     w[bad] = np.nan
-    return idx, w
+    return idx, round_to(w, logits_dtype)
+
+
+def _grouped_weights_f64(logits, logits_dtype, indices, renormalize, scale):
+    s = sigmoid_fp32(logits, logits_dtype)
+    w = np.take_along_axis(s, np.asarray(indices).astype(np.int64), axis=1).astype(np.float64)
+    if renormalize:
+        with np.errstate(invalid="ignore"):  # NaN rows, marked by the caller
+            w = w / w.sum(axis=1, keepdims=True)
+    return w * float(scale)
 
 
 def grouped_selection_weights(logits, logits_dtype, indices, renormalize, scale):
@@ -226,13 +235,9 @@ def grouped_selection_weights(logits, logits_dtype, indices, renormalize, scale)
     sigmoid scores s of the selected experts (the correction bias steers the
     choice only), divided by their sum when renormalize is set, then times
     scale, cast to the logits dtype. Any valid selection of a row (one that
-    the grouped rule could have produced) gets its weights from here."""
-    s = sigmoid_fp32(logits, logits_dtype)
-    w = np.take_along_axis(s, np.asarray(indices).astype(np.int64), axis=1).astype(np.float64)
-    if renormalize:
-        with np.errstate(invalid="ignore"):  # NaN rows stay NaN
-            w = w / w.sum(axis=1, keepdims=True)
-    return round_to(w * float(scale), logits_dtype)
+    the grouped rule could have produced) gets its weights from here; rows
+    whose scores hold a NaN are route_sigmoid_grouped's to mark."""
+    return round_to(_grouped_weights_f64(logits, logits_dtype, indices, renormalize, scale), logits_dtype)
 
 
 def route_sigmoid_grouped_margins(logits, logits_dtype, bias, top_k, groups, selected_groups,

@@ -525,6 +525,32 @@ def test_grouped_sigmoid_special_values():
     assert idx[2, 0] == 3 and w[2, 0] == 0.5 and w[2, 1] == 0.0
 
 
+@pytest.mark.parametrize("ldt", ["bf16", "f16"])
+def test_grouped_sigmoid_half_logits(ldt):
+    """bf16 / fp16 logits: the choice equals the fp32 router's on the same
+    (exactly widened) values, the weights are the fp32 router's within one
+    rounding to the logits dtype, and a NaN row keeps ids 0..k-1 with NaN
+    weights in the logits dtype."""
+    rng_ = rng(67)
+    z = O.round_to(rng_.standard_normal((40, 32)), ldt)
+    z32 = O.decode(z, ldt).astype(np.float32)
+    if ldt == "bf16":
+        z[5, 20] = 0x7FC0
+    else:
+        z[5, 20] = np.float16(np.nan)
+    z32[5, 20] = np.nan
+    bias = (rng_.standard_normal(32) * 0.05).astype(np.float32)
+    idx, w = O.route_sigmoid_grouped(z, ldt, bias, 4, 4, 2, True, True, 2.5)
+    i32, w32 = O.route_sigmoid_grouped(z32, "f32", bias, 4, 4, 2, True, True, 2.5)
+    np.testing.assert_array_equal(idx, i32)
+    assert idx[5].tolist() == [0, 1, 2, 3]
+    wd = O.decode(w, ldt)
+    assert np.isnan(wd[5]).all() and not np.isnan(np.delete(wd, 5, axis=0)).any()
+    ok = np.arange(40) != 5
+    ulp = 2.0 ** -8 if ldt == "bf16" else 2.0 ** -11
+    np.testing.assert_allclose(wd[ok], w32[ok].astype(np.float64), rtol=ulp, atol=0)
+
+
 def test_grouped_sigmoid_argument_checks():
     z = np.zeros((1, 12), np.float32)
     bad = [dict(groups=5), dict(groups=0), dict(selected_groups=0), dict(selected_groups=5),
