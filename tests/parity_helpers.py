@@ -39,6 +39,15 @@ def decode(a: np.ndarray, dtype: str) -> np.ndarray:
     return np.asarray(a).astype(np.float64)
 
 
+def count_outside(gpu: np.ndarray, ref: np.ndarray, dtype: str, tol=None) -> int:
+    """Elements outside the tolerance, NaN mismatches included."""
+    g, r = decode(gpu, dtype), decode(ref, dtype)
+    gn, rn = np.isnan(g), np.isnan(r)
+    atol, rtol = tol or TOL[dtype]
+    ok = ~rn & ~gn
+    return int((gn != rn).sum() + (np.abs(g[ok] - r[ok]) > atol + rtol * np.abs(r[ok])).sum())
+
+
 def assert_close(gpu: np.ndarray, ref: np.ndarray, dtype: str, what: str = "", tol=None):
     g, r = decode(gpu, dtype), decode(ref, dtype)
     assert g.shape == r.shape, (what, g.shape, r.shape)
@@ -74,3 +83,32 @@ def upload_expert_weights(w: I.Workload, keep=(), device="cuda", chunk: int = 16
             del a
     torch.cuda.synchronize()
     return out["w_gate"], out["w_up"], out["w_down"], {e: tuple(v) for e, v in kept.items()}
+
+
+def grouped_choice_valid(c, gsc, chosen, G, SG, margin):
+    """Whether `chosen` (one row's expert ids, in slot order) is a choice the
+    grouped rule could make, within `margin`, given the oracle's fp32 corrected
+    scores c [E] and group scores gsc [G]: k distinct experts in at most SG
+    groups; some set of SG kept groups containing theirs, no better than any
+    dropped group by more than the margin (the best such set is theirs plus
+    the best groups not excluded below); every unchosen expert that beats the
+    weakest chosen one by more than the margin lies in a dropped group; and
+    the slots run in descending c up to the margin."""
+    E = c.shape[0]
+    gs = E // G
+    chosen = [int(e) for e in chosen]
+    if len(set(chosen)) != len(chosen) or max(chosen) >= E:
+        return False
+    cg = {e // gs for e in chosen}
+    cmin = min(c[e] for e in chosen)
+    must_drop = {e // gs for e in range(E) if e not in chosen and c[e] > cmin + margin}
+    if must_drop & cg or len(cg) > SG:
+        return False
+    rest = sorted((g for g in range(G) if g not in cg and g not in must_drop), key=lambda g: (-gsc[g], g))
+    if len(rest) < SG - len(cg):
+        return False
+    kept = cg | set(rest[:SG - len(cg)])
+    dropped = [gsc[g] for g in range(G) if g not in kept]
+    if dropped and min(gsc[g] for g in kept) < max(dropped) - margin:
+        return False
+    return all(c[a] >= c[b] - margin for a, b in zip(chosen, chosen[1:]))
