@@ -104,6 +104,9 @@ def main():
                          "per-token activity mask (7/8 of the tokens active) in the combine")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the extra timing of the same step replayed from a HIP graph")
+    ap.add_argument("--no-targets", action="store_true",
+                    help="default line only: skip the two HBM measurements reported beside it (the "
+                         "decode weight stream and the DeepSeek-V3-shaped combine + Add + RMSNorm)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 5 times (the "
                          "reference kernel for scaling HBM byte counters), then exit")
@@ -324,7 +327,7 @@ def main():
     roofline = {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4),
                 "traffic": measured_traffic(args.workload, kname),
-                "kernel": kname,
+                "kernel": kname, "covers": "the gate/up launch (both GEMMs: expert_gemm_frac_peak)",
                 "algorithmic_per_launch": flops_gate_up if bound != "hbm" else bytes_gate_up}
     gemm_s = (stage_ms["gate_up"] + stage_ms["down"]) / 1e3
     expert_tflops = (flops_gate_up + flops_down) / gemm_s / 1e12
@@ -356,6 +359,9 @@ def main():
         extra["route_gbs"] = round(route_bytes / (stage_ms["route"] / 1e3) / 1e9, 1)
     if args.special:
         extra["rows_dispatched"] = R_disp
+
+    if args.workload == "mixtral_8x_bf16" and not (grouped or args.special or args.no_targets):
+        extra.update(measure_targets(args, torch, moe, I))
 
     # ---- CPU baseline: the oracle on the first tokens of the workload -----
     cpu = None
@@ -440,6 +446,106 @@ def main():
         res["metric"] = METRIC + "; special experts and activity mask in the combine"
     res.update(extra)
     print(json.dumps(res), flush=True)
+
+
+def _device_weights(w, torch, td):
+    """The workload's expert weights, generated expert by expert on the host
+    and copied to the device."""
+    out = {}
+    for name in ("w_gate", "w_up", "w_down"):
+        shape = (w.E, w.I, w.H) if name != "w_down" else (w.E, w.H, w.I)
+        t = torch.empty(shape, dtype=td, device="cuda")
+        for e0 in range(0, w.E, 16):
+            ex = list(range(e0, min(w.E, e0 + 16)))
+            a = I.expert_weights(w, name, ex)
+            t[ex[0]:ex[-1] + 1].copy_(torch.from_numpy(a.view(np.int16)).view(td))
+        out[name] = t
+    return out
+
+
+def _event_ms(torch, run, steps, warmup):
+    """Mean duration in ms of run() between HIP events on the current stream."""
+    for _ in range(warmup):
+        run()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        run()
+        b.record()
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+
+def measure_targets(args, torch, moe, I):
+    """The two HBM-bound steps measured beside the default line, each on its
+    workload's full shape with inputs resident in HBM, timed with HIP events
+    on the stream the kernels run on:
+      - the decode weight stream: moe_forward on the decode workload (T 16,
+        H 4096, I 1536, E 128, top-8); both expert GEMMs' algorithmic bytes
+        (the touched experts' gate, up and down weights, plus their input and
+        output rows) over the two GEMM stages;
+      - the epilogue: moe_combine_add_rmsnorm on the DeepSeek-V3-shaped batch
+        (T 2048, H 7168, top-8) from seeded expert rows and the routing maps
+        of that workload's logits, with the shared-expert term, residual and
+        gamma; its algorithmic bytes (expert rows, maps, weights, shared,
+        residual and gamma in; y, x_out and rstd out) over its duration."""
+    td = torch.bfloat16
+    res = {}
+    # decode weight stream
+    w = I.workload("decode_nan_rows_bf16")
+    T, H, I_, E, k = w.T, w.H, w.I, w.E, w.top_k
+    wt = _device_weights(w, torch, td)
+    xd = torch.from_numpy(I.tokens_for(w).view(np.int16)).view(td).cuda()
+    zd = torch.from_numpy(I.logits_for(w)).cuda()
+    out = torch.empty((T, H), dtype=td, device="cuda")
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    offs = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(moe.moe_forward_workspace_size(T, H, I_, E, k, td, torch.float32), dtype=torch.uint8,
+                     device="cuda")
+    for _ in range(args.warmup):
+        moe.moe_forward(xd, zd, k, w.renormalize, wt["w_gate"], wt["w_up"], wt["w_down"], out=out, ws=ws,
+                        indices_out=idx, offsets_out=offs)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for ev in evs:
+        moe.moe_forward(xd, zd, k, w.renormalize, wt["w_gate"], wt["w_up"], wt["w_down"], out=out, ws=ws,
+                        indices_out=idx, offsets_out=offs, stage_events=ev)
+    torch.cuda.synchronize()
+    gemm_ms = float(np.mean([ev[2].elapsed_time(ev[4]) for ev in evs]))
+    counts = np.diff(offs.cpu().numpy())
+    touched, rows = int((counts > 0).sum()), int(counts.sum())
+    stream_bytes = touched * 3 * I_ * H * 2 + (T * H + 2 * rows * I_ + rows * H) * 2
+    gbs = stream_bytes / (gemm_ms / 1e3) / 1e9
+    res["hbm_decode_weight_stream_frac"] = round(gbs / PEAK_HBM_GBS, 4)
+    res["hbm_decode_weight_stream"] = {"workload": w.name, "experts_touched": touched,
+                                       "bytes": stream_bytes, "ms": round(gemm_ms, 4), "gbs": round(gbs, 1)}
+    del wt
+    torch.cuda.empty_cache()
+    # combine + shared + residual Add + RMSNorm at the DeepSeek-V3-shaped batch
+    w = I.workload("dsv3_share_rmsnorm_bf16")
+    T, H, E, k = w.T, w.H, w.E, w.top_k
+    R = T * k
+    zd = torch.from_numpy(I.logits_for(w)).cuda()
+    idx, wts = moe.moe_route(zd, k, w.renormalize)
+    d = moe.moe_dispatch(idx, E)
+    y = torch.from_numpy(I.store(I.normal(w.seed, "expert_out", (R, H)), "bf16").view(np.int16)).view(td).cuda()
+    sh, rs, gam = I.epilogue_inputs(w)
+    shd, rsd = (torch.from_numpy(a.view(np.int16)).view(td).cuda() for a in (sh, rs))
+    gamd = torch.from_numpy(gam).cuda()
+    yo, xo = torch.empty((T, H), dtype=td, device="cuda"), torch.empty((T, H), dtype=td, device="cuda")
+    rstd = torch.empty(T, dtype=torch.float32, device="cuda")
+    ms = _event_ms(torch, lambda: moe.moe_combine_add_rmsnorm(y, d["row_of_slot"], wts, rsd, gamd, w.eps,
+                                                              shared=shd, y=yo, x_out=xo, rstd=rstd),
+                   args.steps, args.warmup)
+    ep_bytes = R * H * 2 + R * 4 + R * 4 + 4 * T * H * 2 + 4 * H + 4 * T
+    gbs = ep_bytes / (ms / 1e3) / 1e9
+    res["hbm_epilogue_frac"] = round(gbs / PEAK_HBM_GBS, 4)
+    res["hbm_epilogue"] = {"workload": w.name, "kernel": "combine_norm_kernel", "bytes": ep_bytes,
+                           "ms": round(ms, 4), "gbs": round(gbs, 1)}
+    log(f"targets: decode weight stream {res['hbm_decode_weight_stream_frac']:.3f} of HBM, "
+        f"epilogue {res['hbm_epilogue_frac']:.3f}")
+    return res
 
 
 def run_quant(args, w, x, z, to_dev):
