@@ -448,7 +448,7 @@ def main():
     print(json.dumps(res), flush=True)
 
 
-def _device_weights(w, torch, td):
+def _device_weights(w, torch, td, I):
     """The workload's expert weights, generated expert by expert on the host
     and copied to the device."""
     out = {}
@@ -495,7 +495,7 @@ def measure_targets(args, torch, moe, I):
     # decode weight stream
     w = I.workload("decode_nan_rows_bf16")
     T, H, I_, E, k = w.T, w.H, w.I, w.E, w.top_k
-    wt = _device_weights(w, torch, td)
+    wt = _device_weights(w, torch, td, I)
     xd = torch.from_numpy(I.tokens_for(w).view(np.int16)).view(td).cuda()
     zd = torch.from_numpy(I.logits_for(w)).cuda()
     out = torch.empty((T, H), dtype=td, device="cuda")
