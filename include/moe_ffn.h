@@ -233,6 +233,30 @@ size_t moe_forward_workspace_size(int64_t T, int64_t H, int64_t I, int64_t E, in
                                   moe_dtype dt, moe_dtype logits_dt);
 
 /*
+ * moe_forward_noalloc - moe_forward for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): no workspace argument; the call uses a scratch array the
+ * library holds in its own device memory, MOE_NOALLOC_SCRATCH_BYTES (64 MiB)
+ * on every device it runs on, kept until the process ends. It calls no
+ * allocating routine.
+ *   Arguments, results and errors as moe_forward (outputs stay caller-owned),
+ *   plus WORKSPACE when moe_forward_workspace_size(T, H, I, E, top_k, dt,
+ *   logits_dt) exceeds MOE_NOALLOC_SCRATCH_BYTES (nothing is enqueued); that
+ *   holds decode and serving batches (e.g. 16 tokens of E 128, top-8, H 4096,
+ *   I 1536 need about 2 MB), not the large prefill batches.
+ *   Every call on one device shares that device's array: calls on one stream
+ *   are ordered, but calls that may run at the same time on one device (other
+ *   streams, other host threads) race on it. The array keeps the last call's
+ *   contents; nothing in it needs to start at zero.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status moe_forward_noalloc(const void* x, const void* logits, moe_dtype logits_dt, int64_t T,
+                               int64_t H, int64_t I, int64_t E, int64_t top_k, int renormalize,
+                               const void* w_gate, const void* w_up, const void* w_down,
+                               moe_dtype dt, void* out, uint32_t* indices_out, void* weights_out,
+                               int32_t* offsets_out, hipEvent_t* stage_events, hipStream_t stream);
+
+/*
  * moe_route_sigmoid_grouped - grouped-limited sigmoid routing with an
  * optional correction bias.
  * Passage: ruDNN user guide, "10. Grouped-limited sigmoid MoE routing"

@@ -3,6 +3,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 #include <stdint.h>
 
 #include "kernels.h"
@@ -439,7 +440,7 @@ moe_status forward_impl(const void* x, const void* logits, moe_dtype logits_dt, 
                         void* out, uint32_t* indices_out, void* weights_out,
                         int32_t* offsets_out, void* ws, size_t ws_bytes,
                         hipEvent_t* stage_events, hipStream_t stream,
-                        const QuantWeights* quant = nullptr) {
+                        const QuantWeights* quant = nullptr, bool ws_is_library_scratch = false) {
   if (H < 1 || I < 1) return MOE_ERROR_SHAPE;
   moe_status st = MOE_SUCCESS;
   if (!valid_dt(dt)) return MOE_ERROR_DTYPE;
@@ -458,8 +459,10 @@ moe_status forward_impl(const void* x, const void* logits, moe_dtype logits_dt, 
                       {w_gate, wbytes}, {w_up, wbytes}, {w_down, wbytes}};
   const Span bias_in[] = {{router.bias, router.bias ? (size_t)E * 4 : 0}};
   if (any_overlap(outs, 5, ins, 5) || any_overlap(outs, 5, bias_in, 1)) return MOE_ERROR_ARGUMENT;
-  const void* ptrs[] = {x,           logits,      w_gate,      w_up, w_down,     out,
-                        indices_out, weights_out, offsets_out, ws,   router.bias};
+  // the library's own scratch array is device memory of the stream's device by construction
+  const void* ptrs[] = {x,           logits,      w_gate,      w_up,
+                        w_down,      out,         indices_out, weights_out,
+                        offsets_out, ws_is_library_scratch ? nullptr : ws, router.bias};
   if ((st = check_device(ptrs, 11, stream)) != MOE_SUCCESS) return st;
 
   char* base = static_cast<char*>(ws);
@@ -537,6 +540,75 @@ moe_status moe_forward(const void* x, const void* logits, moe_dtype logits_dt, i
   r.renormalize = renormalize ? 1 : 0;
   return forward_impl(x, logits, logits_dt, T, H, I, E, top_k, r, w_gate, w_up, w_down, dt, out,
                       indices_out, weights_out, offsets_out, ws, ws_bytes, stage_events, stream);
+}
+
+}  // extern "C"
+
+// ---- moe_forward_noalloc: moe_forward on the library's own scratch array ----
+// For callers that cannot allocate. One array per device, shared by every
+// call on that device and kept until the process ends; calls that overlap on
+// one device race on it. Host code never names the array itself (that name is
+// a host-side stand-in): it uses the device address looked up once per device.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch array's address on `dev`, looked up (with `dev` current) the
+// first time a call runs there.
+moe_status scratch_on_device(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERROR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int prev = -1;
+    if (hipGetDevice(&prev) != hipSuccess) {
+      (void)hipGetLastError();
+      return MOE_ERROR_HIP;
+    }
+    if (prev != dev && hipSetDevice(dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return MOE_ERROR_HIP;
+    }
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (prev != dev) (void)hipSetDevice(prev);
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return MOE_ERROR_HIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_forward_noalloc(const void* x, const void* logits, moe_dtype logits_dt, int64_t T,
+                               int64_t H, int64_t I, int64_t E, int64_t top_k, int renormalize,
+                               const void* w_gate, const void* w_up, const void* w_down,
+                               moe_dtype dt, void* out, uint32_t* indices_out, void* weights_out,
+                               int32_t* offsets_out, hipEvent_t* stage_events,
+                               hipStream_t stream) {
+  if (H < 1 || I < 1) return MOE_ERROR_SHAPE;
+  moe_status st = check_route_args(T, E, top_k, logits_dt);
+  if (st != MOE_SUCCESS) return st;
+  if (T == 0) return MOE_SUCCESS;
+  int dev = 0;
+  if ((st = stream_device(stream, &dev)) != MOE_SUCCESS) return st;
+  void* ws = nullptr;
+  if ((st = scratch_on_device(dev, &ws)) != MOE_SUCCESS) return st;
+  Router r;
+  r.renormalize = renormalize ? 1 : 0;
+  // too large a batch: the scratch is smaller than the workspace it needs (WORKSPACE)
+  return forward_impl(x, logits, logits_dt, T, H, I, E, top_k, r, w_gate, w_up, w_down, dt, out,
+                      indices_out, weights_out, offsets_out, ws, MOE_NOALLOC_SCRATCH_BYTES,
+                      stage_events, stream, nullptr, true);
 }
 
 moe_status moe_route_sigmoid_grouped(const void* logits, moe_dtype logits_dt, int64_t T, int64_t E,

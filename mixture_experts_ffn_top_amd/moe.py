@@ -47,6 +47,7 @@ _SIGS = {
     "moe_combine": ([P, P, P, I32, I64, I64, I64, I32, P, P], I32),
     "moe_forward": ([P, P, I32, I64, I64, I64, I64, I64, I32, P, P, P, I32, P, P, P, P, P, SZ, P, P], I32),
     "moe_forward_workspace_size": ([I64, I64, I64, I64, I64, I32, I32], SZ),
+    "moe_forward_noalloc": ([P, P, I32, I64, I64, I64, I64, I64, I32, P, P, P, I32, P, P, P, P, P, P], I32),
     "moe_dispatch_masked": ([P, P, I32, I64, I64, I64, P, I32, I64, P, P, P, P, P, SZ, P], I32),
     "moe_combine_special": ([P, P, P, P, I32, I64, I64, I64, I32, I64, I64, I64, I64, P, P, P, P, P, I32,
                              P, P, P], I32),
@@ -297,6 +298,30 @@ def moe_forward(x, logits, top_k: int, renormalize: bool, w_gate, w_up, w_down, 
                              int(renormalize), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
                              dtype_code(x.dtype), _ptr(out), _ptr(indices_out), _ptr(weights_out),
                              _ptr(offsets_out), _ptr(ws), ws.numel(), ev, _stream()), "moe_forward")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES
+
+
+def moe_forward_noalloc(x, logits, top_k: int, renormalize: bool, w_gate, w_up, w_down, out=None,
+                        indices_out=None, weights_out=None, offsets_out=None, stage_events=None):
+    """moe_forward on the library's own scratch array (no workspace argument;
+    the C call allocates nothing). Pass `out` to allocate nothing here either."""
+    T, H = x.shape
+    E = logits.shape[1]
+    I = w_gate.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=x.dtype, device=x.device)
+    ev = None
+    if stage_events is not None:
+        if len(stage_events) != 6:
+            raise ValueError("stage_events needs 6 events")
+        ev = (ctypes.c_void_p * 6)(*[_event_handle(e) for e in stage_events])
+    _check(lib().moe_forward_noalloc(_ptr(x), _ptr(logits), dtype_code(logits.dtype), T, H, I, E, top_k,
+                                     int(renormalize), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+                                     dtype_code(x.dtype), _ptr(out), _ptr(indices_out), _ptr(weights_out),
+                                     _ptr(offsets_out), ev, _stream()), "moe_forward_noalloc")
     return out
 
 

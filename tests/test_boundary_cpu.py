@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 30, names
+    assert len(names) == 31, names
     lib = moe.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -382,3 +382,23 @@ def test_gemm_operands_of_2_gib_are_unsupported():
 
     assert train(131072, 4096, 14336) == U
     assert train(65536, 4096, 14336) != U
+
+
+def test_forward_noalloc_validation():
+    """moe_forward_noalloc checks its arguments like moe_forward, before it
+    looks up the device or its scratch array."""
+    f = moe.lib().moe_forward_noalloc
+    # x, logits, logits_dt, T, H, I, E, k, renorm, wg, wu, wd, dt, out, idx, w, offs, events, stream
+    base = [FAKE, FAKE + 2**20, 0, 64, 128, 256, 8, 2, 1, FAKE + 2**21, FAKE + 2**22, FAKE + 2**23,
+            2, FAKE + 2**24, None, None, None, None, None]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return f(*a)
+
+    assert call(7, 9) == S["MOE_ERROR_ARGUMENT"]     # top_k > E
+    assert call(4, 0) == S["MOE_ERROR_SHAPE"]
+    assert call(2, 7) == S["MOE_ERROR_DTYPE"]        # logits dtype
+    assert call(6, 2000) == S["MOE_ERROR_UNSUPPORTED"]
+    assert call(3, 0) == S["MOE_SUCCESS"]            # no tokens: nothing to do
