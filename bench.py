@@ -463,20 +463,6 @@ def _device_weights(w, torch, td, I):
     return out
 
 
-def _event_ms(torch, run, steps, warmup):
-    """Mean duration in ms of run() between HIP events on the current stream."""
-    for _ in range(warmup):
-        run()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-    torch.cuda.synchronize()
-    for a, b in ev:
-        a.record()
-        run()
-        b.record()
-    torch.cuda.synchronize()
-    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
-
-
 def measure_targets(args, torch, moe, I):
     """The two HBM-bound steps measured beside the default line, each on its
     workload's full shape with inputs resident in HBM, timed with HIP events
@@ -489,7 +475,11 @@ def measure_targets(args, torch, moe, I):
         (T 2048, H 7168, top-8) from seeded expert rows and the routing maps
         of that workload's logits, with the shared-expert term, residual and
         gamma; its algorithmic bytes (expert rows, maps, weights, shared,
-        residual and gamma in; y, x_out and rstd out) over its duration."""
+        residual and gamma in; y, x_out and rstd out) over its duration. Its
+        352.5 MB would partly stay in the 256 MB MALL between back-to-back
+        calls on the same buffers, so three input sets (1.06 GB) rotate: each
+        call reads buffers last touched two calls earlier. The K calls run
+        back to back between two events (the launch gaps amortised)."""
     td = torch.bfloat16
     res = {}
     # decode weight stream
@@ -533,16 +523,35 @@ def measure_targets(args, torch, moe, I):
     sh, rs, gam = I.epilogue_inputs(w)
     shd, rsd = (torch.from_numpy(a.view(np.int16)).view(td).cuda() for a in (sh, rs))
     gamd = torch.from_numpy(gam).cuda()
-    yo, xo = torch.empty((T, H), dtype=td, device="cuda"), torch.empty((T, H), dtype=td, device="cuda")
-    rstd = torch.empty(T, dtype=torch.float32, device="cuda")
-    ms = _event_ms(torch, lambda: moe.moe_combine_add_rmsnorm(y, d["row_of_slot"], wts, rsd, gamd, w.eps,
-                                                              shared=shd, y=yo, x_out=xo, rstd=rstd),
-                   args.steps, args.warmup)
+    sets = []
+    for i in range(3):  # the same values in three places
+        sets.append(dict(y=y if i == 0 else y.clone(), sh=shd if i == 0 else shd.clone(),
+                         rs=rsd if i == 0 else rsd.clone(), ros=d["row_of_slot"].clone(), w=wts.clone(),
+                         yo=torch.empty((T, H), dtype=td, device="cuda"),
+                         xo=torch.empty((T, H), dtype=td, device="cuda"),
+                         rstd=torch.empty(T, dtype=torch.float32, device="cuda")))
+
+    def epilogue(i):
+        b = sets[i % 3]
+        moe.moe_combine_add_rmsnorm(b["y"], b["ros"], b["w"], b["rs"], gamd, w.eps, shared=b["sh"], y=b["yo"],
+                                    x_out=b["xo"], rstd=b["rstd"])
+
+    for i in range(max(args.warmup, 3)):
+        epilogue(i)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for i in range(args.steps):
+        epilogue(i)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
     ep_bytes = R * H * 2 + R * 4 + R * 4 + 4 * T * H * 2 + 4 * H + 4 * T
     gbs = ep_bytes / (ms / 1e3) / 1e9
     res["hbm_epilogue_frac"] = round(gbs / PEAK_HBM_GBS, 4)
     res["hbm_epilogue"] = {"workload": w.name, "kernel": "combine_norm_kernel", "bytes": ep_bytes,
-                           "ms": round(ms, 4), "gbs": round(gbs, 1)}
+                           "ms": round(ms, 4), "gbs": round(gbs, 1),
+                           "inputs": "three rotating sets, each last touched two calls earlier"}
     log(f"targets: decode weight stream {res['hbm_decode_weight_stream_frac']:.3f} of HBM, "
         f"epilogue {res['hbm_epilogue_frac']:.3f}")
     return res

@@ -173,9 +173,10 @@ __global__ __launch_bounds__(256) void combine_partials_kernel(
   o.store(out + (int64_t)t * H + v * 8);
 }
 
-// One workgroup per token, up to 1024 threads; thread owns VPT groups of 8
-// columns strided by the workgroup and keeps x in registers between the sum
-// of squares and the scaling.
+// One workgroup per token, one thread per VPT groups of 8 columns (strided
+// by the workgroup); x stays in registers between the sum of squares and the
+// scaling. The expert rows' loads are issued first, at most 16 16-byte
+// pieces a thread at a time; the residual and shared rows follow.
 template <typename T, typename WT, int VPT>
 __global__ __launch_bounds__(1024) void combine_norm_kernel(
     const T* __restrict__ y, const int32_t* __restrict__ row_of_slot, const WT* __restrict__ w,
@@ -192,40 +193,24 @@ __global__ __launch_bounds__(1024) void combine_norm_kernel(
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[q][i] = 0.f;
 
-  // The residual and shared rows do not depend on the routing: when the
-  // registers allow, their loads go out first, ahead of the map reads the
-  // expert rows wait on.
-  constexpr bool kEarly = VPT * Vec8<T>::kChunks <= 2;
-  Vec8<T> rs[VPT], sh[VPT];
-  auto load_rs = [&](int q) {
-    const int v = threadIdx.x + q * nthreads;
-    if (v < nvec) {
-      LOAD(rs[q], residual + (int64_t)t * H + v * 8);
-      if (shared) LOAD(sh[q], shared + (int64_t)t * H + v * 8);
-    }
-  };
-  if (kEarly) {
-#pragma unroll
-    for (int q = 0; q < VPT; ++q) load_rs(q);
-  }
-
   float wsum = 0.f;
   bool lost = false;
-  add_token_slots<VPT, kEarly ? 16 : 8>(y, row_of_slot, w, t, k, H, threadIdx.x, nthreads, x, wsum,
-                                        lost);
+  add_token_slots<VPT, 16>(y, row_of_slot, w, t, k, H, threadIdx.x, nthreads, x, wsum, lost);
   float ss = 0.f;
 #pragma unroll
   for (int q = 0; q < VPT; ++q) {
     const int v = threadIdx.x + q * nthreads;
     if (v < nvec) {
-      if (!kEarly) load_rs(q);
+      Vec8<T> rs, sh;
+      LOAD(rs, residual + (int64_t)t * H + v * 8);
+      if (shared) LOAD(sh, shared + (int64_t)t * H + v * 8);
       Vec8<T> xo;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         // sum_j w_j * (y_j + s) = sum_j w_j y_j + (sum_j w_j) s
         float xv = x[q][i];
-        if (shared) xv = fmaf(wsum, sh[q].get(i), xv);
-        xv = lost ? NAN : xv + rs[q].get(i);
+        if (shared) xv = fmaf(wsum, sh.get(i), xv);
+        xv = lost ? NAN : xv + rs.get(i);
         x[q][i] = xv;
         ss = fmaf(xv, xv, ss);
         xo.set(i, xv);
@@ -290,21 +275,15 @@ hipError_t norm_launch(const void* y, const int32_t* ros, const void* w, const v
   return hipGetLastError();
 }
 
-// Groups of 8 columns per thread: at least two (measured best on the
-// DeepSeek-V3-shaped epilogue), more once H/8 exceeds 1024 threads.
-#ifndef MOE_NORM_MIN_VPT
-#define MOE_NORM_MIN_VPT 2
-#endif
+// Four groups of 8 columns per thread (H <= 32768: at most 1024 threads).
+// On the DeepSeek-V3-shaped epilogue (H 7168) four measured faster than one
+// or two per thread, with every token's workgroup resident at once.
+constexpr int kNormVpt = 4;
 template <typename T, typename WT>
 hipError_t norm_vpt(const void* y, const int32_t* ros, const void* w, const void* sh,
                     const void* res, const float* gamma, float eps, int T_, int k, int H,
                     void* yo, void* xo, float* rstd, hipStream_t s) {
-  int per = (H / 8 + 1023) / 1024;
-  if (per < MOE_NORM_MIN_VPT) per = MOE_NORM_MIN_VPT;
-  if (per <= 1) return norm_launch<T, WT, 1>(y, ros, w, sh, res, gamma, eps, T_, k, H, yo, xo, rstd, s);
-  if (per <= 2) return norm_launch<T, WT, 2>(y, ros, w, sh, res, gamma, eps, T_, k, H, yo, xo, rstd, s);
-  if (per <= 4) return norm_launch<T, WT, 4>(y, ros, w, sh, res, gamma, eps, T_, k, H, yo, xo, rstd, s);
-  return norm_launch<T, WT, 8>(y, ros, w, sh, res, gamma, eps, T_, k, H, yo, xo, rstd, s);
+  return norm_launch<T, WT, kNormVpt>(y, ros, w, sh, res, gamma, eps, T_, k, H, yo, xo, rstd, s);
 }
 
 template <typename T>

@@ -636,10 +636,10 @@ __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kern
   }
 }
 
-// Skinny grouped GEMM for a few rows per expert (decode): weight-bandwidth
-// bound, so weights stream from HBM straight into registers (no reuse to
-// stage through LDS) and the MFMA work is sized to the rows that exist.
-// One workgroup of 4 wavefronts per (expert, block of 64 weight rows); the
+// Decode gate/up GEMM for a few rows per expert: weight-bandwidth bound, so
+// weights stream from HBM straight into registers (no reuse to stage through
+// LDS) and the MFMA work is sized to the rows that exist. One workgroup of 4
+// wavefronts per (expert, block of 32 gate rows and the same 32 up rows); the
 // wavefronts split K four ways and their partial sums meet in LDS, so the
 // grid has enough independent streams to keep every CU busy. Rows of A
 // (tokens) are taken 16 at a time. MFMA 16x16x32 with A = 16 weight rows and
@@ -648,8 +648,6 @@ __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kern
 // k = kb + 32c + 8g, the MFMA's own operand layout, so the four lanes of a
 // row read 64 contiguous bytes per load. All loads of the next iteration are
 // issued before the current one's MFMAs.
-// GEMM 1 blocks hold 32 gate rows and the same 32 up rows.
-constexpr int kSkinnyWaveRows = 64;  // weight rows per workgroup (4 MFMA tiles)
 constexpr int kSkinnyTokens = 16;
 constexpr int kSkinnyKIter = 128;
 constexpr int kSkinnyWaves = 4;
@@ -671,12 +669,12 @@ template <> struct Mfma16<f16> {
 struct SkinnyArgs {
   GemmArgs g;
   int E;
-  int n_blocks;  // weight-row blocks per expert
-  int k_quarter; // K elements per wavefront (multiple of kSkinnyKIter)
+  int n_blocks;   // weight-row blocks per expert (one workgroup each)
+  int k_quarter;  // K elements per wavefront (multiple of kSkinnyKIter)
 };
 
-template <typename T, bool kSwiGlu>
-__global__ __launch_bounds__(64 * kSkinnyWaves) void skinny_gemm_kernel(SkinnyArgs sa) {
+template <typename T>
+__global__ __launch_bounds__(64 * kSkinnyWaves) void skinny_gate_up_kernel(SkinnyArgs sa) {
   typedef typename Mfma16<T>::Frag Frag;
   __shared__ f32x4 red[kSkinnyWaves - 1][4][64];
   const GemmArgs& p = sa.g;
@@ -697,21 +695,21 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void skinny_gemm_kernel(SkinnyAr
   const int b_bytes = (int)((uint32_t)N * row_bytes);
   const __amdgpu_buffer_rsrc_t rw0 = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<T*>(static_cast<const T*>(p.b0) + expert_elems), (short)0, b_bytes, kRsrcFlags);
-  const __amdgpu_buffer_rsrc_t rw1 = kSwiGlu
-      ? __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(static_cast<const T*>(p.b1) + expert_elems),
-                                          (short)0, b_bytes, kRsrcFlags)
-      : rw0;
+  const __amdgpu_buffer_rsrc_t rw1 = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T*>(static_cast<const T*>(p.b1) + expert_elems), (short)0, b_bytes, kRsrcFlags);
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<void*>(p.a), (short)0, (int)((uint32_t)p.a_rows * row_bytes), kRsrcFlags);
 
-  // Weight rows of the 4 tiles (rows past N read as zero).
+  // Weight rows of the 4 tiles: gate rows nb*32 .. +31 (tiles 0, 1), the
+  // same up rows (tiles 2, 3); rows past N read as zero.
   const int g = lane >> 4;
   uint32_t vo_w[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const int n = kSwiGlu ? nb * 32 + (t & 1) * 16 + (lane & 15) : nb * kSkinnyWaveRows + t * 16 + (lane & 15);
+    const int n = nb * 32 + (t & 1) * 16 + (lane & 15);
     vo_w[t] = (uint32_t)n * row_bytes + (uint32_t)g * 16u;
   }
+  const int n_it = max((k_hi - k_lo + kSkinnyKIter - 1) / kSkinnyKIter, 0);  // this wavefront's K-iterations
 
   T* C = static_cast<T*>(p.c);
   for (int rg = r_begin; rg < r_end; rg += kSkinnyTokens) {
@@ -726,17 +724,18 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void skinny_gemm_kernel(SkinnyAr
     for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // Two register buffers, named (not indexed) so they stay in registers;
-    // loads past this wavefront's K range read as zero.
+    // loads past this wavefront's K range or its last iteration read as zero.
     uint4 wa[4][4], xa[4], wb[4][4], xb[4];
-    auto load = [&](int kb, uint4 (&w)[4][4], uint4 (&x)[4]) {
+    auto load = [&](int it, uint4 (&w)[4][4], uint4 (&x)[4]) {
+      const int kb = k_lo + it * kSkinnyKIter;
       const uint32_t soff = (uint32_t)kb * sizeof(T);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const bool ok = kb + c * 32 + g * 8 < k_hi;
+        const bool ok = it < n_it && kb + c * 32 + g * 8 < k_hi;
 #pragma unroll
         for (int t = 0; t < 4; ++t)
           w[t][c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-              (kSwiGlu && t >= 2) ? rw1 : rw0, ok ? vo_w[t] + c * 64u : kOutOfRange, soff, 0));
+              t >= 2 ? rw1 : rw0, ok ? vo_w[t] + c * 64u : kOutOfRange, soff, 0));
         x[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
             rx, ok ? vo_x + c * 64u : kOutOfRange, soff, 0));
       }
@@ -749,41 +748,24 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void skinny_gemm_kernel(SkinnyAr
           acc[t] = Mfma16<T>::run(__builtin_bit_cast(Frag, w[t][c]), __builtin_bit_cast(Frag, x[c]),
                                   acc[t]);
     };
-    const int n_iter = (k_hi - k_lo + kSkinnyKIter - 1) / kSkinnyKIter;
-    if (n_iter > 0) {
-      load(k_lo, wa, xa);
-      // keep every load of the next iteration ahead of this one's MFMAs
-      constexpr int kLoadsPerIter = 4 * 4 + 4;
-      int it = 0;
-      for (; it + 2 <= n_iter; it += 2) {
-        load(k_lo + (it + 1) * kSkinnyKIter, wb, xb);
-        compute(wa, xa);
-        __builtin_amdgcn_sched_group_barrier(0x020, kLoadsPerIter, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
-        load(k_lo + (it + 2) * kSkinnyKIter, wa, xa);
-        compute(wb, xb);
-        __builtin_amdgcn_sched_group_barrier(0x020, kLoadsPerIter, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+    // Partial sums of wavefronts 1..3 meet wavefront 0's in LDS (fixed
+    // order), wavefront 0 stores. Every wavefront calls this once per token
+    // group (the same barriers, whatever its K range).
+    auto finish = [&]() {
+      if (wave > 0) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) red[wave - 1][t][lane] = acc[t];
       }
-      if (it < n_iter) compute(wa, xa);  // odd count: wa holds the last iteration
-    }
-
-    // Partial sums of wavefronts 1..3 meet wavefront 0's in LDS (fixed order).
-    if (wave > 0) {
+      __syncthreads();
+      if (wave == 0) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) red[wave - 1][t][lane] = acc[t];
-    }
-    __syncthreads();
-    if (wave == 0) {
+        for (int w = 0; w < kSkinnyWaves - 1; ++w)
 #pragma unroll
-      for (int w = 0; w < kSkinnyWaves - 1; ++w)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) acc[t] += red[w][t][lane];
-      // D element v of lane l: weight row (l/16)*4 + v of the tile, token l%16.
-      const int tok = rg + (lane & 15);
-      if (tok < r_end) {
-        T* crow = C + (int64_t)tok * N;
-        if (kSwiGlu) {
+          for (int t = 0; t < 4; ++t) acc[t] += red[w][t][lane];
+        // D element v of lane l: weight row (l/16)*4 + v of the tile, token l%16.
+        const int tok = rg + (lane & 15);
+        if (tok < r_end) {
+          T* crow = C + (int64_t)tok * N;
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
             const int col = nb * 32 + t * 16 + g * 4;
@@ -791,18 +773,127 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void skinny_gemm_kernel(SkinnyAr
             for (int v = 0; v < 4; ++v)
               if (col + v < N) crow[col + v] = from_f32<T>(silu(acc[t][v]) * acc[t + 2][v]);
           }
-        } else {
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const int col = nb * kSkinnyWaveRows + t * 16 + g * 4;
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-              if (col + v < N) crow[col + v] = from_f32<T>(acc[t][v]);
-          }
         }
       }
+      __syncthreads();  // red[] is reused by the next token group
+    };
+
+    if (n_it > 0) {
+      // keep every load of the next iteration ahead of this one's MFMAs
+      constexpr int kLoadsPerIter = 4 * 4 + 4;
+      load(0, wa, xa);
+      int it = 0;
+      for (; it + 2 <= n_it; it += 2) {
+        load(it + 1, wb, xb);
+        compute(wa, xa);
+        __builtin_amdgcn_sched_group_barrier(0x020, kLoadsPerIter, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+        load(it + 2, wa, xa);
+        compute(wb, xb);
+        __builtin_amdgcn_sched_group_barrier(0x020, kLoadsPerIter, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+      }
+      if (it < n_it) compute(wa, xa);  // odd count: wa holds the last iteration
     }
-    __syncthreads();  // red[] is reused by the next row group
+    finish();
+  }
+}
+
+// Decode down GEMM, one wavefront per 16 output columns over the whole of K:
+// the wavefront streams its 16 weight rows from HBM straight into MFMA
+// operands, kDepth K-iterations of loads in flight, no K split and no LDS
+// (each wavefront reads whole rows: a K split made the short K = I rows of
+// the down projection into pieces of a few hundred bytes per wavefront). MFMA 16x16x32, A = 16 weight rows, B = 16
+// token rows, D[weight row][token]; load c of a K-iteration of 128 gives lane
+// group g = lane/16 the 8 elements at k = kb + 32c + 8g, so the four lanes of
+// a row read 64 contiguous bytes per load.
+constexpr int kRowsWaves = 4;  // wavefronts per workgroup
+constexpr int kRowsDepth = 2;  // K-iterations of loads in flight per wavefront
+
+template <typename T, int kDepth>
+__global__ __launch_bounds__(64 * kRowsWaves) void skinny_down_kernel(SkinnyArgs sa) {
+  typedef typename Mfma16<T>::Frag Frag;
+  constexpr int kT = 1;  // weight tiles per wavefront
+  const GemmArgs& p = sa.g;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int e = blockIdx.x / sa.n_blocks;
+  const int nb = blockIdx.x - e * sa.n_blocks;
+  if (e >= sa.E) return;
+  const int r_begin = max(__builtin_amdgcn_readfirstlane(p.offsets[e]), 0);
+  const int r_end = min(__builtin_amdgcn_readfirstlane(p.offsets[e + 1]), p.rows);
+  const int K = p.K, N = p.N;
+  const int col0 = (nb * kRowsWaves + wave) * 16;  // this wavefront's output columns
+  if (r_end <= r_begin || col0 >= N) return;        // no barriers in this kernel
+
+  const uint32_t row_bytes = (uint32_t)K * sizeof(T);
+  const int64_t expert_elems = (int64_t)e * N * K;
+  const int b_bytes = (int)((uint32_t)N * row_bytes);
+  const __amdgpu_buffer_rsrc_t rw0 = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T*>(static_cast<const T*>(p.b0) + expert_elems), (short)0, b_bytes, kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(p.a), (short)0, (int)((uint32_t)p.a_rows * row_bytes), kRsrcFlags);
+  const int g = lane >> 4;
+  // weight row col0 + lane % 16 (rows past N read as zero)
+  const uint32_t vo_w = (uint32_t)(col0 + (lane & 15)) * row_bytes + (uint32_t)g * 16u;
+  const int n_it = (K + kSkinnyKIter - 1) / kSkinnyKIter;
+
+  T* C = static_cast<T*>(p.c);
+  for (int rg = r_begin; rg < r_end; rg += kSkinnyTokens) {
+    const int xr = rg + (lane & 15);
+    uint32_t vo_x = kOutOfRange;
+    if (xr < r_end) {
+      const int src = p.a_map ? min(max(p.a_map[xr] / p.a_div, 0), p.a_rows - 1) : xr;
+      vo_x = (uint32_t)src * row_bytes + (uint32_t)g * 16u;
+    }
+    f32x4 acc[kT];
+#pragma unroll
+    for (int t = 0; t < kT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // kDepth register buffers, indexed only by unrolled constants so they
+    // stay in registers; K-iterations past the end read as zero.
+    uint4 w[kDepth][kT][4], x[kDepth][4];
+    auto load = [&](int it, uint4 (&wd)[kT][4], uint4 (&xd)[4]) {
+      const int kb = it * kSkinnyKIter;
+      const uint32_t soff = (uint32_t)kb * sizeof(T);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const bool ok = it < n_it && kb + c * 32 + g * 8 < K;
+#pragma unroll
+        for (int t = 0; t < kT; ++t)
+          wd[t][c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+              rw0, ok ? vo_w + c * 64u : kOutOfRange, soff, 0));
+        xd[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+            rx, ok ? vo_x + c * 64u : kOutOfRange, soff, 0));
+      }
+    };
+    constexpr int kLoadsPerIter = kT * 4 + 4;
+#pragma unroll
+    for (int d = 0; d + 1 < kDepth; ++d) load(d, w[d], x[d]);
+    for (int it0 = 0; it0 < n_it; it0 += kDepth) {
+#pragma unroll
+      for (int d = 0; d < kDepth; ++d) {
+        // keep the loads kDepth - 1 iterations ahead of this one's MFMAs
+        load(it0 + d + kDepth - 1, w[(d + kDepth - 1) % kDepth], x[(d + kDepth - 1) % kDepth]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int t = 0; t < kT; ++t)
+            acc[t] = Mfma16<T>::run(__builtin_bit_cast(Frag, w[d][t][c]), __builtin_bit_cast(Frag, x[d][c]),
+                                    acc[t]);
+        __builtin_amdgcn_sched_group_barrier(0x020, kLoadsPerIter, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4 * kT, 0);
+      }
+    }
+    // D element v of lane l: weight row (l/16)*4 + v of the tile, token l%16.
+    const int tok = rg + (lane & 15);
+    if (tok < r_end) {
+      T* crow = C + (int64_t)tok * N;
+      const int col = col0 + g * 4;
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        if (col + v < N)
+          crow[col + v] = from_f32<T>(acc[0][v]);
+    }
   }
 }
 
@@ -1088,21 +1179,33 @@ void setup_down(GemmArgs& g, const ExpertsPlan& plan, void* scratch, const void*
 // Few rows per expert (decode-shaped batches): weight streaming dominates.
 bool use_skinny(int rows, int E, int dt) { return dt != kF32 && rows <= 4 * E; }
 
+// Decode-sized batches: the gate/up GEMM (K = H) on skinny_gate_up_kernel
+// (4 wavefronts split K), the down GEMM (K = I, usually short) on
+// skinny_down_kernel (each wavefront streams whole weight rows); on the
+// decode workload each measured faster than the other kernel's scheme.
+template <typename T>
+void launch_rows(const SkinnyArgs& sa, hipStream_t s) {
+  const dim3 grid((unsigned)((int64_t)sa.E * sa.n_blocks));
+  hipLaunchKernelGGL((skinny_down_kernel<T, kRowsDepth>), grid, dim3(64 * kRowsWaves), 0, s, sa);
+}
+
 void launch_skinny(const GemmArgs& g, int E, int dt, bool swiglu, hipStream_t s) {
   SkinnyArgs sa;
   sa.g = g;
   sa.E = E;
-  sa.n_blocks = swiglu ? (g.N + 31) / 32 : (g.N + kSkinnyWaveRows - 1) / kSkinnyWaveRows;
+  if (!swiglu) {
+    sa.n_blocks = (g.N + 16 * kRowsWaves - 1) / (16 * kRowsWaves);
+    sa.k_quarter = 0;
+    if (dt == kF16) launch_rows<f16>(sa, s);
+    else launch_rows<bf16>(sa, s);
+    return;
+  }
+  sa.n_blocks = (g.N + 31) / 32;
   const int iters = (g.K + kSkinnyKIter - 1) / kSkinnyKIter;
   sa.k_quarter = (iters + kSkinnyWaves - 1) / kSkinnyWaves * kSkinnyKIter;
   const dim3 grid((unsigned)((int64_t)E * sa.n_blocks));
-  if (dt == kF16) {
-    if (swiglu) hipLaunchKernelGGL((skinny_gemm_kernel<f16, true>), grid, dim3(64 * kSkinnyWaves), 0, s, sa);
-    else hipLaunchKernelGGL((skinny_gemm_kernel<f16, false>), grid, dim3(64 * kSkinnyWaves), 0, s, sa);
-  } else {
-    if (swiglu) hipLaunchKernelGGL((skinny_gemm_kernel<bf16, true>), grid, dim3(64 * kSkinnyWaves), 0, s, sa);
-    else hipLaunchKernelGGL((skinny_gemm_kernel<bf16, false>), grid, dim3(64 * kSkinnyWaves), 0, s, sa);
-  }
+  if (dt == kF16) hipLaunchKernelGGL((skinny_gate_up_kernel<f16>), grid, dim3(64 * kSkinnyWaves), 0, s, sa);
+  else hipLaunchKernelGGL((skinny_gate_up_kernel<bf16>), grid, dim3(64 * kSkinnyWaves), 0, s, sa);
 }
 
 hipError_t reduce_splits(const ExpertsPlan& plan, void* scratch, const int32_t* offsets, int rows,
