@@ -321,7 +321,7 @@ def main():
     if w.dtype == "f32":
         kname = "simt_gemm_kernel<gate_up>"
     elif R <= 4 * E:  # the library's weight-streaming path for decode-sized batches
-        kname = "skinny_gemm_kernel<bf16,gate_up>"
+        kname = "skinny_gate_up_kernel<bf16>"
     else:
         kname = "mfma_gemm_kernel<bf16,gate_up>"
     roofline = {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
