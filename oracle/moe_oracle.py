@@ -343,21 +343,17 @@ def unpack_int4(packed: np.ndarray) -> np.ndarray:
     return np.where(out >= 8, out - 16, out)
 
 
-def dequant_weight(q, bits, scale, offset, groups, dtype, round_weights=True):
+def dequant_weight(q, bits, scale, offset, groups, dtype, round_weights=False):
     """One expert's dequantised weight matrix [N, K] as fp64 values:
         w[n, k] = (q[n, k] + offset[n, j]) * scale[n, j],  j = k // (K / groups)
     (the pseudo-quantization formula of aclnnFFN, per channel or per group).
-    round_weights=True (the reading used for parity): w is a tensor in the
-    activation dtype, so the exact value is rounded once to dtype. The
-    formula puts the bracketed dequantised weight in the place that W holds
-    in the unquantised formula, where x and W are both activation-dtype
-    tensors, and the page's constraints give antiquantScale and
-    antiquantOffset the activation dtype (FLOAT16 with FLOAT16 x; BFLOAT16
-    with BFLOAT16 x). With integer offsets, q + offset is exact in the
-    activation dtype, so rounding the sum and then the product gives this
-    same single rounding.
-    round_weights=False: the exact fp64 value, not rounded (the plain
-    mathematical definition, for comparison).
+    round_weights=False (the reading used for parity): the formula in exact
+    arithmetic. The page states the formula and the storage dtypes of the
+    codes, antiquantScale and antiquantOffset (the activation dtype), not a
+    rounding of the bracketed product, so w is the exact value and only the
+    GEMMs' results are rounded, as in the unquantised path.
+    round_weights=True (an alternative reading, for comparison): w held as a
+    tensor of the activation dtype, the exact value rounded once.
     q: int8 [N, K] (bits 8) or packed int4 bytes [N, K/2] (bits 4); scale,
     offset: [N, groups] stored in dtype (offset None = 0)."""
     qi = unpack_int4(q) if bits == 4 else np.asarray(q).view(np.int8).astype(np.int16)
@@ -369,7 +365,7 @@ def dequant_weight(q, bits, scale, offset, groups, dtype, round_weights=True):
     return decode(round_to(w, dtype), dtype) if round_weights else w
 
 
-def experts_forward_quant(x_disp, offsets, quant_of, bits, groups, dtype, round_weights=True):
+def experts_forward_quant(x_disp, offsets, quant_of, bits, groups, dtype, round_weights=False):
     """Expert outputs for every dispatched row with quantised weights: the
     SwiGLU expert of swiglu_expert_f64 on the dequantised weights of
     dequant_weight (round_weights as there).

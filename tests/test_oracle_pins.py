@@ -691,7 +691,8 @@ def test_dequant_closed_forms():
 
 
 def test_dequant_rounds_once_to_model_dtype():
-    """Scale 1 + 2^-7 (exact in bf16). bf16 spacing is 2^-6 in [2, 4), 2^-5
+    """The rounded reading (round_weights=True, kept for comparison).
+    Scale 1 + 2^-7 (exact in bf16). bf16 spacing is 2^-6 in [2, 4), 2^-5
     in [4, 8) and 2^-1 in [64, 128):
     127 * s = 127.9921875 -> 128;  2 * s = 2.015625 exact;
     -5 * s = -5.0390625 (-161.25 steps of 2^-5) -> -5.03125;
@@ -702,12 +703,17 @@ def test_dequant_rounds_once_to_model_dtype():
     127 * s still rounds to 128 (spacing 2^-4 in [64, 128))."""
     q = np.array([[127, 2, -5, 3]], np.int8)
     sc = _bf16([[1.0 + 2.0 ** -7]])
-    w = O.dequant_weight(q.view(np.uint8), 8, sc, None, 1, "bf16")
+    w = O.dequant_weight(q.view(np.uint8), 8, sc, None, 1, "bf16", round_weights=True)
     np.testing.assert_array_equal(w, [[128.0, 2.015625, -5.03125, 3.03125]])
-    w = O.dequant_weight(q.view(np.uint8), 8, sc, _bf16([[0.5]]), 1, "bf16")
+    w = O.dequant_weight(q.view(np.uint8), 8, sc, _bf16([[0.5]]), 1, "bf16", round_weights=True)
     np.testing.assert_array_equal(w, [[128.0, 2.515625, -4.53125, 3.53125]])
-    w = O.dequant_weight(q.view(np.uint8), 8, np.array([[1.0 + 2.0 ** -7]], np.float16), None, 1, "f16")
+    w = O.dequant_weight(q.view(np.uint8), 8, np.array([[1.0 + 2.0 ** -7]], np.float16), None, 1, "f16",
+                         round_weights=True)
     np.testing.assert_array_equal(w[0, [0, 3]], [128.0, 3.0234375])
+    # the parity reading keeps the exact products: 127 * (1 + 2^-7) = 127.9921875, 3.5 * s = 3.52734375
+    w = O.dequant_weight(q.view(np.uint8), 8, sc, _bf16([[0.5]]), 1, "bf16")
+    np.testing.assert_array_equal(w, [[127.5 * (1 + 2.0 ** -7), 2.5 * (1 + 2.0 ** -7), -4.5 * (1 + 2.0 ** -7),
+                                       3.5 * (1 + 2.0 ** -7)]])
 
 
 def test_quant_expert_reduces_to_plain_expert():
