@@ -9,23 +9,32 @@
 //   low nibble first, two's complement (-8..7);
 //   scale, offset [E, N, G] in the model dtype, G groups of K/G consecutive
 //   input channels (G = 1: per channel; K/G a multiple of 128, so a
-//   K-iteration (64 or 128 channels) never straddles two groups); offset may be
+//   K-iteration (128 channels) never straddles two groups); offset may be
 //   absent (0).
 //
-// Same structure as the bf16 weight-streaming kernel: one workgroup of 4
-// wavefronts per (expert, block of 64 weight rows), K split four ways and
-// reduced in LDS, MFMA 16x16x32 with A = 16 weight rows and B = 16 token
-// rows. Every weight load is 16 bytes per lane, four lanes side by side on a
-// row (64 contiguous bytes per row and instruction): 16 INT8 or 32 INT4
-// codes, i.e. 2 or 4 MFMA k-slices of 8. The k order inside a lane's span
-// differs from the MFMA's native one, and the activations are loaded in the
-// same order, so the contraction is unchanged. The codes are dequantised in
-// registers as q * s + (o * s) in fp32 and rounded to the model dtype before
-// the MFMA (INT4 as (q + 8) * s + (o - 8) * s, the same value for integer
-// offsets). The next K-iteration's weight and activation loads are issued
-// before the current iteration's MFMAs; the scales are loaded once when a
-// wavefront's K range lies in one scale group (per-channel scales, or groups
-// at least that long), else with each iteration's loads.
+// The formula is computed as written, without rounding the dequantised
+// weights: for output channel n and group g,
+//   sum_k x_k (q_k + o) s = s (sum_k x_k c_k) + s (o - C) (sum_k x_k)
+// where c_k = q_k + C is the code shifted by a constant C so that it is an
+// exact small integer in the model dtype that a few bit operations build
+// (INT4: 128 + the unsigned nibble; INT8: the unsigned byte, converted).
+// The MFMA contracts the activations with the codes (exact products, fp32
+// accumulation), a second MFMA against ones gives sum_k x_k, and the scale
+// and offset are applied to those fp32 sums once per group.
+//
+// One workgroup of 4 wavefronts per (expert, block of 64 weight rows), K
+// split four ways and reduced in LDS, MFMA 16x16x32 with A = 16 token rows
+// and B = 16 weight rows, D[token][weight row]: a lane's outputs share one
+// weight row, so it needs one scale and offset per tile. Every weight load
+// is 16 bytes per lane, four lanes side by side on a row (64 contiguous
+// bytes per row and instruction): 16 INT8 or 32 INT4 codes, i.e. 2 or 4 MFMA
+// k-slices of 8. The k order inside a lane's span differs from the MFMA's
+// native one, and the activations are loaded in the same order, so the
+// contraction is unchanged. The next K-iteration's weight and activation
+// loads are issued before the current iteration's MFMAs; the scales are
+// loaded once when a wavefront's K range lies in one scale group
+// (per-channel scales, or groups at least that long), else with each
+// iteration's loads.
 #include <type_traits>
 
 #include "common.h"
@@ -93,38 +102,49 @@ __device__ __forceinline__ uint32_t word_of(const uint4& q, int i) {
   return i < 2 ? (i == 0 ? q.x : q.y) : (i == 2 ? q.z : q.w);
 }
 
-// The 8 dequantised weights of MFMA slice m of a lane's 16 bytes, as an MFMA
-// operand: w = fma(c, s, os) in fp32, rounded to T.
-//  INT8: codes 8m .. 8m+7 are the signed bytes of words 2m, 2m+1; c = q,
-//        os = o s.
-//  INT4: codes 8m .. 8m+7 are the nibbles of word m, low nibble first. With
-//        each nibble's top bit flipped, u = q + 8 is the unsigned nibble; the
-//        nibbles are split into the bytes of two words (even codes, odd
-//        codes) and converted with byte conversions; c = u, os = (o - 8) s.
+// The shift C of the codes: c = q + C is what enters the MFMA.
+//  INT8: c = q + 128, the unsigned byte (0..255, exact in bf16 and fp16).
+//  INT4: c = 128 + u with u = q + 8 the unsigned nibble (bf16: exponent of
+//        128, u in the low mantissa bits); fp16: c = 1024 + u.
 template <typename T, int kBits>
-__device__ __forceinline__ uint4 dequant8(const uint4& q, int m, float sc, float os, uint32_t nib_mask) {
-  float f[8];
+__device__ __forceinline__ constexpr float code_shift() {
+  return kBits == 8 ? 128.0f : (std::is_same<T, bf16>::value ? 136.0f : 1032.0f);
+}
+
+// The 8 codes of MFMA slice m of a lane's 16 bytes, as an MFMA operand of T.
+//  INT8: codes 8m .. 8m+7 are the bytes of words 2m, 2m+1; with the sign bit
+//        flipped each byte is q + 128, converted exactly.
+//  INT4: codes 8m .. 8m+7 are the nibbles of word m, low nibble first; with
+//        each nibble's top bit flipped it is u = q + 8, and the pair of codes
+//        2d, 2d+1 (byte d of the word) becomes one dword of two T values by
+//        placing u in the mantissa field of 128 (bf16) or 1024 (fp16).
+template <typename T, int kBits>
+__device__ __forceinline__ uint4 codes8(const uint4& q, int m, uint32_t nib_mask) {
   if constexpr (kBits == 8) {
+    float f[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) f[i] = (float)(int)(int8_t)(word_of(q, 2 * m + (i >> 2)) >> (8 * (i & 3)));
+    for (int i = 0; i < 8; ++i) f[i] = (float)((word_of(q, 2 * m + (i >> 2)) ^ 0x80808080u) >> (8 * (i & 3)) & 0xFFu);
+    uint4 r;
+    r.x = pack2<T>(f[0], f[1]);
+    r.y = pack2<T>(f[2], f[3]);
+    r.z = pack2<T>(f[4], f[5]);
+    r.w = pack2<T>(f[6], f[7]);
+    return r;
   } else {
     const uint32_t x = word_of(q, m) ^ 0x88888888u;
-    // nib_mask (0x0F0F0F0F) comes from the kernel arguments: a compile-time
-    // mask lets the compiler fold it into one bit-field extract per code
-    // instead of one byte-select conversion
+    // nib_mask (0x0F0F0F0F) comes from the kernel arguments (a compile-time
+    // mask would let the compiler split the byte moves into bit-field ops)
     const uint32_t lo = x & nib_mask, hi = (x >> 4) & nib_mask;
+    constexpr uint32_t kBase = std::is_same<T, bf16>::value ? 0x43004300u : 0x64006400u;
+    // byte permute: selectors 0-3 take the bytes of the second source (lo),
+    // 4-7 those of the first (hi), 12 gives a zero byte; dword b holds byte
+    // b of lo in its low half and byte b of hi in its high half
+    uint32_t d[4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      f[2 * b] = (float)((lo >> (8 * b)) & 0xFFu);
-      f[2 * b + 1] = (float)((hi >> (8 * b)) & 0xFFu);
-    }
+    for (int b = 0; b < 4; ++b)
+      d[b] = __builtin_amdgcn_perm(hi, lo, 0x0C000C00u | ((uint32_t)(4 + b) << 16) | (uint32_t)b) | kBase;
+    return uint4{d[0], d[1], d[2], d[3]};
   }
-  uint4 r;
-  r.x = pack2<T>(fmaf(f[0], sc, os), fmaf(f[1], sc, os));
-  r.y = pack2<T>(fmaf(f[2], sc, os), fmaf(f[3], sc, os));
-  r.z = pack2<T>(fmaf(f[4], sc, os), fmaf(f[5], sc, os));
-  r.w = pack2<T>(fmaf(f[6], sc, os), fmaf(f[7], sc, os));
-  return r;
 }
 
 struct QuantArgs {
@@ -143,22 +163,29 @@ struct QuantArgs {
   uint32_t nib_mask;      // 0x0F0F0F0F
 };
 
-template <typename T, bool kSwiGlu, int kBits>
+// The 4 wavefronts of a workgroup form 4 / kSplitK groups; each group owns a
+// block of kQRows weight rows (or kQRows / 2 gate and as many up rows) and
+// its kSplitK wavefronts split K, their partial sums meeting in LDS.
+template <typename T, bool kSwiGlu, int kBits, int kSplitK>
 __global__ __launch_bounds__(64 * kQWaves, QGeo<kBits>::kWavesPerSimd) void skinny_quant_kernel(QuantArgs p) {
   typedef typename MfmaQ<T>::Frag Frag;
-  __shared__ f32x4 red[kQWaves - 1][kQTiles][64];
+  static_assert(kQWaves % kSplitK == 0, "whole groups of wavefronts");
+  constexpr int kGroups = kQWaves / kSplitK;
+  __shared__ f32x4 red[kGroups][kSplitK > 1 ? kSplitK - 1 : 1][kQTiles][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wk = wave % kSplitK, wn = wave / kSplitK;  // K slice, row block of the workgroup
   const int e = blockIdx.x / p.n_blocks;
-  const int nb = blockIdx.x - e * p.n_blocks;
+  const int nb = (blockIdx.x - e * p.n_blocks) * kGroups + wn;
   if (e >= p.E) return;
   const int r_begin = max(__builtin_amdgcn_readfirstlane(p.offsets[e]), 0);
   const int r_end = min(__builtin_amdgcn_readfirstlane(p.offsets[e + 1]), p.rows);
   if (r_end <= r_begin) return;
+  if (kSplitK == 1 && nb * (kSwiGlu ? kQRows / 2 : kQRows) >= p.N) return;  // no barriers without a K split
 
   const int K = p.K, N = p.N, G = p.G;
   const int gsz = K / G;  // input channels per group (multiple of 8)
-  const int k_lo = wave * p.k_quarter;
+  const int k_lo = wk * p.k_quarter;
   const int k_hi = min(K, k_lo + p.k_quarter);
   const uint32_t qrow = (uint32_t)K * kBits / 8;  // bytes per quantised row
   const int64_t expert_rows = (int64_t)e * N;
@@ -239,7 +266,7 @@ __global__ __launch_bounds__(64 * kQWaves, QGeo<kBits>::kWavesPerSimd) void skin
           const float s = to_f32(__builtin_bit_cast(T, (uint16_t)(__builtin_bit_cast(uint16_t, sv[t]) & ms)));
           const float o = to_f32(__builtin_bit_cast(T, (uint16_t)(__builtin_bit_cast(uint16_t, ov[t]) & mo)));
           sc[t][l] = s;
-          os[t][l] = (kBits == 8 ? o : o - 8.0f) * s;  // INT4 codes enter as q + 8
+          os[t][l] = (o - code_shift<T, kBits>()) * s;  // the codes enter as q + C
         }
       }
     };
@@ -271,17 +298,37 @@ __global__ __launch_bounds__(64 * kQWaves, QGeo<kBits>::kWavesPerSimd) void skin
         }
       }
     };
-    auto compute = [&](const uint4 (&w)[kQTiles][Geo::kLoads], const uint4 (&x)[Geo::kLoads][Geo::kMf],
-                       const Sc& sc, const Sc& os) {
+    // Codes against activations (cacc, per tile) and ones against
+    // activations (xsum: every column the sum of the token's activations),
+    // both in fp32; finish() applies the group's scale and offset.
+    f32x4 cacc[kQTiles], xsum = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < kQTiles; ++t) cacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const Frag ones = __builtin_bit_cast(
+        Frag, std::is_same<T, bf16>::value ? uint4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u}
+                                           : uint4{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u});
+    auto compute = [&](const uint4 (&w)[kQTiles][Geo::kLoads], const uint4 (&x)[Geo::kLoads][Geo::kMf]) {
 #pragma unroll
       for (int l = 0; l < Geo::kLoads; ++l)
 #pragma unroll
-        for (int m = 0; m < Geo::kMf; ++m)
+        for (int m = 0; m < Geo::kMf; ++m) {
+          const Frag xf = __builtin_bit_cast(Frag, x[l][m]);
 #pragma unroll
-          for (int t = 0; t < kQTiles; ++t) {
-            const Frag f = __builtin_bit_cast(Frag, dequant8<T, kBits>(w[t][l], m, sc[t][l], os[t][l], p.nib_mask));
-            acc[t] = MfmaQ<T>::run(f, __builtin_bit_cast(Frag, x[l][m]), acc[t]);
-          }
+          for (int t = 0; t < kQTiles; ++t)
+            cacc[t] = MfmaQ<T>::run(xf, __builtin_bit_cast(Frag, codes8<T, kBits>(w[t][l], m, p.nib_mask)), cacc[t]);
+          xsum = MfmaQ<T>::run(xf, ones, xsum);
+        }
+    };
+    // acc += s * cacc + s (o - C) * xsum for the group just finished (all of
+    // an iteration's loads lie in one group: index 0 of sc, os).
+    auto finish = [&](const Sc& sc, const Sc& os) {
+#pragma unroll
+      for (int t = 0; t < kQTiles; ++t) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[t][v] += sc[t][0] * cacc[t][v] + os[t][0] * xsum[v];
+        cacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      xsum = f32x4{0.f, 0.f, 0.f, 0.f};
     };
     const int n_iter = (k_hi - k_lo + Geo::kIter - 1) / Geo::kIter;
     // One scale group over this wavefront's whole K range (per-channel
@@ -293,75 +340,104 @@ __global__ __launch_bounds__(64 * kQWaves, QGeo<kBits>::kWavesPerSimd) void skin
       int it = 0;
       for (; it + 2 <= n_iter; it += 2) {
         load(k_lo + (it + 1) * Geo::kIter, wb, xb);
-        compute(wa, xa, sa_, oa);
+        compute(wa, xa);
         load(k_lo + (it + 2) * Geo::kIter, wa, xa);
-        compute(wb, xb, sa_, oa);
+        compute(wb, xb);
       }
-      if (it < n_iter) compute(wa, xa, sa_, oa);  // odd count: wa holds the last iteration
+      if (it < n_iter) compute(wa, xa);  // odd count: wa holds the last iteration
+      finish(sa_, oa);
     } else if (n_iter > 0) {
+      // the group ends after iteration it when the next one starts a new group
+      auto group_ends = [&](int it) {
+        const int kn = k_lo + (it + 1) * Geo::kIter;
+        return it + 1 == n_iter || kn % gsz == 0;
+      };
       load(k_lo, wa, xa);
       load_sc(k_lo, sa_, oa, Geo::kLoads);
       int it = 0;
       for (; it + 2 <= n_iter; it += 2) {
         load(k_lo + (it + 1) * Geo::kIter, wb, xb);
         load_sc(k_lo + (it + 1) * Geo::kIter, sb_, ob, Geo::kLoads);
-        compute(wa, xa, sa_, oa);
+        compute(wa, xa);
+        if (group_ends(it)) finish(sa_, oa);
         load(k_lo + (it + 2) * Geo::kIter, wa, xa);
         load_sc(k_lo + (it + 2) * Geo::kIter, sa_, oa, Geo::kLoads);
-        compute(wb, xb, sb_, ob);
+        compute(wb, xb);
+        if (group_ends(it + 1)) finish(sb_, ob);
       }
-      if (it < n_iter) compute(wa, xa, sa_, oa);
+      if (it < n_iter) {
+        compute(wa, xa);
+        finish(sa_, oa);
+      }
     }
 
-    // Partial sums of wavefronts 1..3 meet wavefront 0's in LDS (fixed order).
-    if (wave > 0) {
+    // Partial sums of a group's wavefronts 1.. meet its wavefront 0's in LDS
+    // (fixed order).
+    if (kSplitK > 1) {
+      if (wk > 0) {
 #pragma unroll
-      for (int t = 0; t < kQTiles; ++t) red[wave - 1][t][lane] = acc[t];
+        for (int t = 0; t < kQTiles; ++t) red[wn][wk - 1][t][lane] = acc[t];
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    if (wave == 0) {
+    if (wk == 0) {
 #pragma unroll
-      for (int w = 0; w < kQWaves - 1; ++w)
+      for (int w = 0; w < kSplitK - 1; ++w)
 #pragma unroll
-        for (int t = 0; t < kQTiles; ++t) acc[t] += red[w][t][lane];
-      // D element v of lane l: weight row (l/16)*4 + v of the tile, token l%16.
-      const int tok = rg + (lane & 15);
-      if (tok < r_end) {
+        for (int t = 0; t < kQTiles; ++t) acc[t] += red[wn][w][t][lane];
+      // D element v of lane l: token (l/16)*4 + v, weight row l%16 of the tile.
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int tok = rg + g * 4 + v;
+        if (tok >= r_end) continue;
         T* crow = C + (int64_t)tok * N;
         if (kSwiGlu) {
 #pragma unroll
           for (int t = 0; t < kHalf; ++t) {
-            const int col = nb * (16 * kHalf) + t * 16 + g * 4;
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-              if (col + v < N) crow[col + v] = from_f32<T>(silu_q(acc[t][v]) * acc[t + kHalf][v]);
+            const int col = nb * (16 * kHalf) + t * 16 + (lane & 15);
+            if (col < N) crow[col] = from_f32<T>(silu_q(acc[t][v]) * acc[t + kHalf][v]);
           }
         } else {
 #pragma unroll
           for (int t = 0; t < kQTiles; ++t) {
-            const int col = nb * kQRows + t * 16 + g * 4;
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-              if (col + v < N) crow[col + v] = from_f32<T>(acc[t][v]);
+            const int col = nb * kQRows + t * 16 + (lane & 15);
+            if (col < N) crow[col] = from_f32<T>(acc[t][v]);
           }
         }
       }
     }
-    __syncthreads();  // red[] is reused by the next row group
+    if (kSplitK > 1) __syncthreads();  // red[] is reused by the next row group
   }
+}
+
+#ifndef MOE_Q_SPLIT_GU8
+#define MOE_Q_SPLIT_GU8 4
+#endif
+#ifndef MOE_Q_SPLIT_DN8
+#define MOE_Q_SPLIT_DN8 2
+#endif
+#ifndef MOE_Q_SPLIT_GU4
+#define MOE_Q_SPLIT_GU4 4
+#endif
+#ifndef MOE_Q_SPLIT_DN4
+#define MOE_Q_SPLIT_DN4 4
+#endif
+template <typename T, int kBits, bool kSwiGlu, int kSplitK>
+void launch_q_split(QuantArgs p, hipStream_t s) {
+  const int rows_per_wave = kSwiGlu ? kQRows / 2 : kQRows;  // output columns of one row block
+  const int rows_per_group = rows_per_wave * (kQWaves / kSplitK);
+  p.n_blocks = (p.N + rows_per_group - 1) / rows_per_group;
+  constexpr int kIter = QGeo<kBits>::kIter;
+  const int iters = (p.K + kIter - 1) / kIter;
+  p.k_quarter = (iters + kSplitK - 1) / kSplitK * kIter;
+  const dim3 grid((unsigned)((int64_t)p.E * p.n_blocks));
+  hipLaunchKernelGGL((skinny_quant_kernel<T, kSwiGlu, kBits, kSplitK>), grid, dim3(64 * kQWaves), 0, s, p);
 }
 
 template <typename T, int kBits>
 void launch_q(QuantArgs p, bool swiglu, hipStream_t s) {
-  p.n_blocks = swiglu ? (p.N + kQRows / 2 - 1) / (kQRows / 2) : (p.N + kQRows - 1) / kQRows;
-  constexpr int kIter = QGeo<kBits>::kIter;
-  const int iters = (p.K + kIter - 1) / kIter;
-  p.k_quarter = (iters + kQWaves - 1) / kQWaves * kIter;
-  const dim3 grid((unsigned)((int64_t)p.E * p.n_blocks));
-  if (swiglu)
-    hipLaunchKernelGGL((skinny_quant_kernel<T, true, kBits>), grid, dim3(64 * kQWaves), 0, s, p);
-  else
-    hipLaunchKernelGGL((skinny_quant_kernel<T, false, kBits>), grid, dim3(64 * kQWaves), 0, s, p);
+  if (swiglu) launch_q_split<T, kBits, true, kBits == 8 ? MOE_Q_SPLIT_GU8 : MOE_Q_SPLIT_GU4>(p, s);
+  else launch_q_split<T, kBits, false, kBits == 8 ? MOE_Q_SPLIT_DN8 : MOE_Q_SPLIT_DN4>(p, s);
 }
 
 template <typename T>

@@ -840,21 +840,21 @@ def test_quant_experts_dispatched(bits, groups, dtype, with_offset, H, I_, ETk):
     quant_of = lambda e: tuple((t[0][e], t[1][e], None if t[2] is None else t[2][e]) for t in wq)  # noqa: E731
     ref = O.experts_forward_quant(d["x_disp"], d["offsets"], quant_of, bits, groups, dtype)
     assert_close(host(y), ref, dtype, "quantised experts")
-    _report_unrounded(host(y), d["x_disp"], d["offsets"], quant_of, bits, groups, dtype)
+    _report_rounded_reading(host(y), d["x_disp"], d["offsets"], quant_of, bits, groups, dtype)
 
 
-def _report_unrounded(y, x_disp, offsets, quant_of, bits, groups, dtype):
-    """The comparison above follows the reading that the dequantised weight is
-    a tensor in the activation dtype (rounded once). Against the plain
-    definition with unrounded weights, report how many outputs fall outside
-    the same tolerance; by the bf16 / fp16 rounding of each weight (half an
-    ulp, 2^-9 / 2^-12 relative) only a few cancelling sums may, so more than
-    0.5 % would point at something else."""
-    exact = O.experts_forward_quant(x_disp, offsets, quant_of, bits, groups, dtype, round_weights=False)
-    n = count_outside(y, exact, dtype)
-    say(f"quantised experts, INT{bits} G={groups} {dtype}: {n} of {exact.size} outputs outside the "
-        "tolerance against the unrounded dequantised weights")
-    assert n <= 0.005 * exact.size
+def _report_rounded_reading(y, x_disp, offsets, quant_of, bits, groups, dtype):
+    """The comparison above follows the formula in exact arithmetic. Against
+    the alternative reading that rounds each dequantised weight to the
+    activation dtype, report how many outputs fall outside the same
+    tolerance; by that rounding (half an ulp of a weight, 2^-9 / 2^-12
+    relative) only a few cancelling sums may, so more than 0.5 % would point
+    at something else."""
+    rounded = O.experts_forward_quant(x_disp, offsets, quant_of, bits, groups, dtype, round_weights=True)
+    n = count_outside(y, rounded, dtype)
+    say(f"quantised experts, INT{bits} G={groups} {dtype}: {n} of {rounded.size} outputs outside the "
+        "tolerance against the dequantised weights rounded to the activation dtype")
+    assert n <= 0.005 * rounded.size
 
 
 @pytest.mark.parametrize("bits,groups", [(8, 1), (4, 4)])
@@ -878,12 +878,12 @@ def test_forward_quant_decode_shape(bits, groups):
     y = O.experts_forward_quant(d["x_disp"], d["offsets"], quant_of, bits, groups, "bf16")
     ref = O.combine(y, d["row_of_slot"], w_r, "f32", w.T, w.top_k, "bf16")
     assert_close(host(out), ref, "bf16", "quantised forward")
-    y_exact = O.experts_forward_quant(d["x_disp"], d["offsets"], quant_of, bits, groups, "bf16", False)
-    ref_exact = O.combine(y_exact, d["row_of_slot"], w_r, "f32", w.T, w.top_k, "bf16")
-    n = count_outside(host(out), ref_exact, "bf16")
-    say(f"quantised forward INT{bits}: {n} of {ref_exact.size} outputs outside the tolerance against the "
-        "unrounded dequantised weights")
-    assert n <= 0.005 * ref_exact.size
+    y_rounded = O.experts_forward_quant(d["x_disp"], d["offsets"], quant_of, bits, groups, "bf16", True)
+    ref_rounded = O.combine(y_rounded, d["row_of_slot"], w_r, "f32", w.T, w.top_k, "bf16")
+    n = count_outside(host(out), ref_rounded, "bf16")
+    say(f"quantised forward INT{bits}: {n} of {ref_rounded.size} outputs outside the tolerance against the "
+        "dequantised weights rounded to the activation dtype")
+    assert n <= 0.005 * ref_rounded.size
 
 
 @pytest.mark.parametrize("bits,groups", [(8, 1), (4, 2)])
