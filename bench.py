@@ -434,7 +434,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "T": T, "H": H, "I": I_, "E": E, "top_k": k,
                    "renormalize": w.renormalize, "logits_dtype": "f32"},
-        "roofline": roofline, "cpu_baseline": cpu,
+        "roofline": roofline, "cpu_baseline": cpu, "device": device_info(torch),
     }
     res["graph_replay"] = graph
     if grouped:
@@ -446,6 +446,42 @@ def main():
         res["metric"] = METRIC + "; special experts and activity mask in the combine"
     res.update(extra)
     print(json.dumps(res), flush=True)
+
+
+def device_info(torch):
+    """The device the line was measured on: name, compute units, memory, the
+    highest shader clock level the driver lists (sysfs, null where it cannot
+    be read), the peaks the fractions use and a measured 1 GiB device copy
+    (read + written bytes over its median time of 5)."""
+    p = torch.cuda.get_device_properties(0)
+    info = {"name": p.name, "arch": p.gcnArchName.split(":")[0], "compute_units": p.multi_processor_count,
+            "memory_gib": round(p.total_memory / 2**30, 1), "peak_bf16_tflops": PEAK_TFLOPS["bf16"],
+            "peak_hbm_gbs": PEAK_HBM_GBS, "max_sclk_mhz": None}
+    bus = f"{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}.0"
+    try:
+        with open(f"/sys/bus/pci/devices/{bus}/pp_dpm_sclk") as f:
+            mhz = [int(tok.lower().replace("mhz", "")) for line in f for tok in line.split()[1:2]
+                   if tok.lower().endswith("mhz")]
+        info["max_sclk_mhz"] = max(mhz) if mhz else None
+    except (OSError, ValueError):
+        pass
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    b.copy_(a)
+    times = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    del a, b
+    torch.cuda.empty_cache()
+    info["copy_1gib_gbs"] = round(2 * n / (float(np.median(times)) / 1e3) / 1e9, 1)
+    return info
 
 
 def _device_weights(w, torch, td, I):
@@ -647,7 +683,7 @@ def run_quant(args, w, x, z, to_dev):
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{args.workload}+int{bits}", "T": T, "H": H, "I": I_, "E": E, "top_k": k,
                    "bits": bits, "groups": groups},
-        "roofline": roofline, "cpu_baseline": cpu,
+        "roofline": roofline, "cpu_baseline": cpu, "device": device_info(torch),
         "stages_ms": {k_: round(v, 4) for k_, v in stage_ms.items()},
         "weight_stream_gbs": round((wbytes_gu + wbytes_dn) / exp_s / 1e9, 1),
         "experts_touched": touched,
@@ -793,7 +829,7 @@ def run_train(args, w, x, z, xd, zd, wt, kept, n_cpu):
         "data": "synthetic",
         "config": {"workload": args.workload + "+train", "T": T, "H": H, "I": I_, "E": E, "top_k": k,
                    "scoring": "softmax", "normalize": w.renormalize},
-        "roofline": roofline, "cpu_baseline": cpu,
+        "roofline": roofline, "cpu_baseline": cpu, "device": device_info(torch),
         "stages_ms": {k_: round(v, 4) for k_, v in stage_ms.items()},
         "experts_fwd_tflops": round(fwd_tf, 1), "experts_bwd_tflops": round(bwd_tf, 1),
     }
