@@ -506,7 +506,7 @@ def measure_targets(args, torch, moe, I):
       - the decode weight stream: moe_forward on the decode workload (T 16,
         H 4096, I 1536, E 128, top-8); both expert GEMMs' algorithmic bytes
         (the touched experts' gate, up and down weights, plus their input and
-        output rows) over the two GEMM stages;
+        output rows) over the median duration of the two GEMM stages;
       - the epilogue: moe_combine_add_rmsnorm on the DeepSeek-V3-shaped batch
         (T 2048, H 7168, top-8) from seeded expert rows and the routing maps
         of that workload's logits, with the shared-expert term, residual and
@@ -538,14 +538,18 @@ def measure_targets(args, torch, moe, I):
         moe.moe_forward(xd, zd, k, w.renormalize, wt["w_gate"], wt["w_up"], wt["w_down"], out=out, ws=ws,
                         indices_out=idx, offsets_out=offs, stage_events=ev)
     torch.cuda.synchronize()
-    gemm_ms = float(np.mean([ev[2].elapsed_time(ev[4]) for ev in evs]))
+    # the median over the timed calls (one late call does not move it); the
+    # mean is reported beside it
+    gemm_all = [ev[2].elapsed_time(ev[4]) for ev in evs]
+    gemm_ms, gemm_mean = float(np.median(gemm_all)), float(np.mean(gemm_all))
     counts = np.diff(offs.cpu().numpy())
     touched, rows = int((counts > 0).sum()), int(counts.sum())
     stream_bytes = touched * 3 * I_ * H * 2 + (T * H + 2 * rows * I_ + rows * H) * 2
     gbs = stream_bytes / (gemm_ms / 1e3) / 1e9
     res["hbm_decode_weight_stream_frac"] = round(gbs / PEAK_HBM_GBS, 4)
     res["hbm_decode_weight_stream"] = {"workload": w.name, "experts_touched": touched,
-                                       "bytes": stream_bytes, "ms": round(gemm_ms, 4), "gbs": round(gbs, 1)}
+                                       "bytes": stream_bytes, "ms": round(gemm_ms, 4), "ms_mean": round(gemm_mean, 4),
+                                       "gbs": round(gbs, 1), "stat": f"median of {len(gemm_all)} calls"}
     del wt
     torch.cuda.empty_cache()
     # combine + shared + residual Add + RMSNorm at the DeepSeek-V3-shaped batch
