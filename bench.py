@@ -44,7 +44,7 @@ BOUND = {"tiny_fp32": "alu", "mixtral_8x_bf16": "mfma", "many_expert_zipf_bf16":
          "dsv3_share_rmsnorm_bf16": "hbm", "decode_nan_rows_bf16": "hbm"}
 
 
-FORWARD_SOURCES = ("combine.hip", "common.h", "gemm.hip")
+FORWARD_SOURCES = ("combine.hip", "common.h", "gemm.hip", "schedule.h")
 
 
 def kernel_source_hash(sources=FORWARD_SOURCES) -> str:

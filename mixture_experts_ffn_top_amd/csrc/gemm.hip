@@ -13,17 +13,18 @@
 // M-tile count; workgroups without a tile exit at once. Expert counts never
 // travel to the host.
 //
-// Order of the schedule. The hardware deals workgroups round-robin to the 8
-// XCDs (each with its own L2), so workgroup b runs on XCD b % 8, and each XCD
-// starts its workgroups in the order b / 8. The plan gives XCD x a contiguous
-// slice of the tile list, so the ~32 workgroups resident on one XCD at a time
-// are neighbours in the list. Inside an expert the list takes groups of up to
-// 8 M-tiles, and inside such a group runs of N-tiles wide enough that one run
-// covers about 8 tiles (4 M-tiles x 2 N-tiles, 8 x 1, 1 x 8 ...), N first
-// inside a run: the ~32 tiles resident together (four consecutive runs) share
-// their weight tiles and activation tiles through that XCD's L2, and a run
-// never mixes two experts' weights. (Runs of 8 measured about 1 % faster than
-// one run of 32 covering the same tiles.)
+// Order of the schedule (schedule.h). The hardware deals workgroups
+// round-robin to the 8 XCDs (each with its own L2), so workgroup b runs on
+// XCD b % 8, and each XCD starts its workgroups in the order b / 8. The plan
+// gives XCD x a contiguous slice of the tile list, so the ~32 workgroups
+// resident on one XCD at a time are neighbours in the list. Inside an expert
+// the list takes groups of up to 8 M-tiles, and inside such a group runs of
+// N-tiles wide enough that one run covers about 8 tiles (4 M-tiles x 2
+// N-tiles, 8 x 1, 1 x 8 ...), N first inside a run: the ~32 tiles resident
+// together (four consecutive runs) share their weight tiles and activation
+// tiles through that XCD's L2, and a run never mixes two experts' weights.
+// (Runs of 8 measured about 1 % faster than one run of 32 covering the same
+// tiles.)
 //
 // bf16/f16 kernel (gfx950 MFMA 32x32x16), two tile shapes:
 //  - 256 x kBNB tiles, 512 threads = 8 wavefronts as 4 (M) x 2 (N), 64 x
@@ -62,6 +63,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "schedule.h"
 
 
 namespace moe {
@@ -70,15 +72,14 @@ namespace {
 constexpr int kBM = 256;      // rows per M-tile (MFMA path)
 constexpr int kBK = 64;       // K per LDS stage
 constexpr int kBMSimt = 64;   // rows per M-tile (fp32 path)
-constexpr int kXcds = 8;
-constexpr int kRunTiles = 8;   // tiles per run of the schedule order
-constexpr int kGroupM = 8;     // M-tiles per schedule group
+constexpr int kXcds = sched::kXcds;
 // Third dword of a raw buffer resource on gfx9-family parts (no format, no swizzle).
 constexpr int kRsrcFlags = 0x00020000;
 constexpr uint32_t kOutOfRange = 0x80000000u;  // voffset past any buffer we build (< 2^31 bytes)
 
 // One schedule entry per workgroup: x = expert | (K-split << 16), y = first
-// row, z = end row (exclusive), w = N-tile; x < 0: no tile.
+// row, z = end row (exclusive), w = N-tile; x < 0: no tile. The list and its
+// split into XCD slices are those of schedule.h.
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ offsets, int E,
                                                      int rows, int bm, int max_tiles,
                                                      int n_tiles_n, int k_splits, int grid,
@@ -100,40 +101,26 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   }
   if (e == 0) s_first[E] = total;
   __syncthreads();
-  const int per_split = min(total, max_tiles) * n_tiles_n;
-  const int n_real = per_split * k_splits;
-  const int chunk = (n_real + kXcds - 1) / kXcds;
+  sched::Table t;
+  t.first = s_first;
+  t.lo = s_lo;
+  t.hi = s_hi;
+  t.E = E;
+  t.bm = bm;
+  t.n_tiles_n = n_tiles_n;
+  t.k_splits = k_splits;
+  t.per_split = min(total, max_tiles) * n_tiles_n;
+  t.n_real = t.per_split * k_splits;
   for (int b = blockIdx.x * blockDim.x + threadIdx.x; b < grid; b += gridDim.x * blockDim.x) {
-    const int slot = b / kXcds;
-    const int L = (b % kXcds) * chunk + slot;
-    int4 t = make_int4(-1, 0, 0, 0);
-    if (slot < chunk && L < n_real) {
-      const int ks = L / per_split;
-      const int idx = L - ks * per_split;
-      // expert: the last e with s_first[e] * n_tiles_n <= idx
-      int lo_e = 0, hi_e = E - 1;
-      while (lo_e < hi_e) {
-        const int mid = (lo_e + hi_e + 1) / 2;
-        if (s_first[mid] * n_tiles_n <= idx) lo_e = mid;
-        else hi_e = mid - 1;
-      }
-      const int ex = lo_e;
-      const int local = idx - s_first[ex] * n_tiles_n;
-      const int me = s_first[ex + 1] - s_first[ex];
-      const int mg = min(me, kGroupM);
-      const int ng = max(1, kRunTiles / mg);
-      const int mgi = local / (mg * n_tiles_n);
-      const int mgw = min(mg, me - mgi * mg);
-      const int j = local - mgi * mg * n_tiles_n;
-      const int ngi = j / (mgw * ng);
-      const int w = min(ng, n_tiles_n - ngi * ng);
-      const int r = j - ngi * mgw * ng;
-      t.x = ex | (ks << 16);
-      t.y = s_lo[ex] + (mgi * mg + r / w) * bm;
-      t.z = s_hi[ex];
-      t.w = ngi * ng + r % w;
+    int begin, end;
+    sched::xcd_range(t, b % sched::kXcds, &begin, &end);
+    const int L = begin + b / sched::kXcds;
+    int4 v = make_int4(-1, 0, 0, 0);
+    if (L < end) {
+      const sched::Entry en = sched::entry_at(t, L);
+      v = make_int4(en.ex | (en.ks << 16), en.row0, en.row_end, en.n_t);
     }
-    sched[b] = t;
+    sched[b] = v;
   }
 }
 
