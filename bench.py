@@ -450,9 +450,9 @@ def main():
 
 def device_info(torch):
     """The device the line was measured on: name, compute units, memory, the
-    highest shader clock level the driver lists (sysfs, null where it cannot
-    be read), the peaks the fractions use and a measured 1 GiB device copy
-    (read + written bytes over its median time of 5)."""
+    highest shader clock level the amdgpu kernel driver lists (sysfs; null
+    where it cannot be read), the peaks the fractions use and a measured
+    1 GiB device copy (read + written bytes over its median time of 5)."""
     p = torch.cuda.get_device_properties(0)
     info = {"name": p.name, "arch": p.gcnArchName.split(":")[0], "compute_units": p.multi_processor_count,
             "memory_gib": round(p.total_memory / 2**30, 1), "peak_bf16_tflops": PEAK_TFLOPS["bf16"],
