@@ -400,11 +400,11 @@ moe_status moe_combine_add_rmsnorm_special(
  *     scale_gate, scale_up [E, I, groups], scale_down [E, H, groups] in dt,
  *     offset_*: same shapes, or NULL for 0;
  *   group j of a row covers input channels j*K/groups .. (j+1)*K/groups - 1
- *   (groups = 1: one scale per output channel). The dequantised weight is
- *   a value of dt: (q + offset) * scale is formed in fp32 and rounded once
- *   to dt before it enters the product (exact before that rounding for
- *   integer offsets), so the result equals moe_experts_forward_dispatched
- *   given those dt weights.
+ *   (groups = 1: one scale per output channel). Each weight is taken as
+ *   the exact (q + offset) * scale, not rounded to dt: per group the
+ *   kernels accumulate sum(x * (q + C)) and sum(x) in fp32 for a constant
+ *   code shift C and add scale * sum(x * (q + C)) + (offset - C) * scale *
+ *   sum(x); only the two GEMMs' results are rounded to dt.
  *   Other arguments as moe_experts_forward_dispatched; workspace:
  *   moe_experts_quant_workspace_size(rows, E, H, I, dt) (holds h).
  * Errors: ARGUMENT if bits is not 8 or 4, groups < 1 or does not divide H
