@@ -410,6 +410,10 @@ __global__ __launch_bounds__(64 * kQWaves, QGeo<kBits>::kWavesPerSimd) void skin
   }
 }
 
+// Wavefronts per K range (kSplitK) of each GEMM and bit width, measured on
+// the decode shape: 4 everywhere except the INT8 down GEMM (K = I, short
+// rows), where two row blocks of two K halves each ran faster than one row
+// block of four K quarters; the INT4 GEMMs were slower with 2 or 1.
 #ifndef MOE_Q_SPLIT_GU8
 #define MOE_Q_SPLIT_GU8 4
 #endif
