@@ -288,6 +288,15 @@ __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kern
   static_assert(!kSwiGlu || kBNB == 256, "fused gate/up uses 128 + 128 B rows");
   static_assert(kSub >= 2, "at least two k16 sub-steps per stage");
   static_assert((kBNB / 2) % (kWaves * kRowsPerInst) == 0, "gate/up split between instructions");
+  // 256 x 256 tiles with two stages and no training cache: the MFMAs take
+  // the weight fragment as their row operand, so that each lane's 16
+  // accumulators of a 32 x 32 block hold one output row (token) and four
+  // runs of four consecutive output columns; the epilogue stages the block
+  // through the LDS stage that holds no k-step between two tiles and stores
+  // 16-byte row chunks (split-K partials go out directly, four fp32 at a
+  // time). The other shapes keep the token fragment as row operand and
+  // transpose in registers.
+  constexpr bool kLdsEpi = kStg == 2 && !kCache && kBMt == 256 && kWaveM == 64 && kBNB == 256;
 
   int v = blockIdx.x;
   Tile tile;
@@ -316,7 +325,19 @@ __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kern
   __amdgpu_buffer_rsrc_t rsrc_b0, rsrc_b1;
   uint32_t vo_a[kLoadsA], vo_b[kLoadsB];
   int e, ks, row0, n_t, mrows, k_begin, k_end;
-  auto setup = [&](const Tile& t) {
+  // Source rows of this lane's A chunks (through the row map when there is
+  // one). Fetched for the next tile at the start of the current one, so the
+  // map's latency is hidden behind its k-steps.
+  auto a_src = [&](const Tile& t, int (&src)[kLoadsA]) {
+    const int mr = min(kBMt, t.row_end - t.row0);
+#pragma unroll
+    for (int j = 0; j < kLoadsA; ++j) {
+      const int r = (j * kWaves + wave) * kRowsPerInst + lane / kCh;
+      const int grow = t.row0 + min(r, mr - 1);
+      src[j] = p.a_map ? min(max(p.a_map[grow] / p.a_div, 0), p.a_rows - 1) : grow;
+    }
+  };
+  auto setup = [&](const Tile& t, const int (&src)[kLoadsA]) {
     e = t.e; ks = t.ks; row0 = t.row0; n_t = t.n_t;
     mrows = min(kBMt, t.row_end - row0);
     k_begin = ks * p.k_chunk;
@@ -331,10 +352,8 @@ __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kern
 #pragma unroll
     for (int j = 0; j < kLoadsA; ++j) {
       const int r = (j * kWaves + wave) * kRowsPerInst + lane / kCh;
-      const int grow = row0 + min(r, mrows - 1);
-      const int src = p.a_map ? min(max(p.a_map[grow] / p.a_div, 0), p.a_rows - 1) : grow;
       // rows past the expert's last row are not fetched (they read as zero)
-      vo_a[j] = r < mrows ? (uint32_t)src * row_bytes + (uint32_t)c_lane * 16u : kOutOfRange;
+      vo_a[j] = r < mrows ? (uint32_t)src[j] * row_bytes + (uint32_t)c_lane * 16u : kOutOfRange;
     }
 #pragma unroll
     for (int j = 0; j < kLoadsB; ++j) {
@@ -385,8 +404,12 @@ __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kern
   };
   auto mfmas = [&](int slot, int from, int to) {
 #pragma unroll
-    for (int i = from; i < to; ++i)
-      acc[i / kNB][i % kNB] = Mfma<T>::run(fa[slot][i / kNB], fb[slot][i % kNB], acc[i / kNB][i % kNB]);
+    for (int i = from; i < to; ++i) {
+      if constexpr (kLdsEpi)
+        acc[i / kNB][i % kNB] = Mfma<T>::run(fb[slot][i % kNB], fa[slot][i / kNB], acc[i / kNB][i % kNB]);
+      else
+        acc[i / kNB][i % kNB] = Mfma<T>::run(fa[slot][i / kNB], fb[slot][i % kNB], acc[i / kNB][i % kNB]);
+    }
   };
   constexpr int kMfma = kMB * kNB;   // MFMAs per k16 sub-step
   constexpr int kReads = kMB + kNB;  // fragment reads per sub-step
@@ -468,7 +491,11 @@ __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kern
     if constexpr (kStg == 3) issue_loads(1, stage_buf<T, kBMt * kBKT, 0, 1>(), stage_buf<T, kBNB * kBKT, 1, 1>());
   };
 
-  setup(tile);
+  {
+    int src[kLoadsA];
+    a_src(tile, src);
+    setup(tile, src);
+  }
   issue_first();
   T* C = static_cast<T*>(p.c);
   const int row_lane = (lane >> 5) * 4;
@@ -476,6 +503,12 @@ __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kern
   // blocks, h, g and u, per h block when the training cache is written).
   constexpr int kStores = (kSwiGlu ? kMB * 2 : kMB * kNB) * 4 * (kCache ? 3 : 1);
   static_assert(kStores + kLoads < 64, "vmcnt holds 6 bits");
+  // Stores of the LDS epilogue: 64 rows x 64 columns (one pass) per gate/up
+  // wavefront, 64 x 128 (two passes) per down wavefront, 8 per pass.
+  constexpr int kStoresLds = kSwiGlu ? 8 : 16;
+  // The next tile waits for its first stage with vmcnt(this): never more
+  // than the stores any wavefront issued after those loads.
+  constexpr int kStoresWait = kLdsEpi ? kStoresLds : kStores;
   int stores_prev = 0;
   for (;;) {
 #pragma unroll
@@ -490,11 +523,17 @@ __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kern
     // (not for the later stages or the previous tile's stores, issued after it).
     constexpr int kAhead = (kStg - 2) * kLoads;
     if (stores_prev)
-      wait_vmem<kStores + kAhead>();
+      wait_vmem<kStoresWait + kAhead>();
     else
       wait_vmem<kAhead>();
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     const bool has_rows = wm * kWaveM < mrows;
+    // The next tile's schedule entry and A-row sources, requested now and
+    // used after the main loop.
+    Tile next;
+    const bool more = tile_of_block(p, v + gridDim.x, next);
+    int nsrc[kLoadsA];
+    if (more) a_src(next, nsrc);
     if (has_rows)
       main_loop(std::true_type{}, nk_pad);
     else
@@ -503,10 +542,8 @@ __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kern
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     const int t_row0 = row0, t_mrows = mrows, t_nt = n_t, t_ks = ks;
     v += gridDim.x;
-    Tile next;
-    const bool more = tile_of_block(p, v, next);
     if (more) {
-      setup(next);
+      setup(next, nsrc);
       issue_first();
     }
 
@@ -522,8 +559,108 @@ __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kern
     // after the next tile's first loads, and the next tile waits for its
     // loads with vmcnt(kStores) without draining the stores.
     int stores_out = 0;
-    if (has_rows) {
-      const bool part = !kSwiGlu && p.partial != nullptr;
+    const bool part = !kSwiGlu && p.partial != nullptr;
+    if (kLdsEpi && has_rows) {
+      // Lane l holds, for accumulator i of block (mb, nb), output row
+      // mb*32 + l%32 of the wavefront and column nb*32 + (i/4)*8 + 4*(l/32)
+      // + i%4: four consecutive columns per group of four accumulators.
+      const int m32 = lane & 31, h4 = (lane >> 5) * 4;
+      if (part) {
+        // fp32 split-K partials: 16 bytes per lane and group, straight out
+        const __amdgpu_buffer_rsrc_t rsrc_p = __builtin_amdgcn_make_buffer_rsrc(
+            reinterpret_cast<char*>(p.partial + (int64_t)t_ks * p.rows * N + (int64_t)t_row0 * N), (short)0,
+            t_mrows * N * 4, kRsrcFlags);
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int row = wm * kWaveM + mb * 32 + m32;
+              const int col = t_nt * kBNB + wn * (kBNB / 2) + nb * 32 + g * 8 + h4;
+              // copied out first: a bit cast of a vector element reads the
+              // vector's first element
+              const float x0 = acc[mb][nb][4 * g], x1 = acc[mb][nb][4 * g + 1];
+              const float x2 = acc[mb][nb][4 * g + 2], x3 = acc[mb][nb][4 * g + 3];
+              const i32x4 d = {__builtin_bit_cast(int, x0), __builtin_bit_cast(int, x1),
+                               __builtin_bit_cast(int, x2), __builtin_bit_cast(int, x3)};
+              const uint32_t vo = col < N ? (uint32_t)(row * N + col) * 4u : kOutOfRange;
+              __builtin_amdgcn_raw_buffer_store_b128(d, rsrc_p, vo, 0, 0);
+            }
+      } else {
+        // Wavefront w's block goes to its own 8 KB of stage 1 (waves 0-3 in
+        // the A half, 4-7 in the B half): 64 rows of 64 elements, 16-byte
+        // chunk c of row r at slot c ^ ((r >> 1) & 7), so that the 32 rows
+        // of an 8-byte write instruction and the 8 rows of a 16-byte read
+        // spread over all banks.
+        T* const blk = wave < 4 ? stage_buf<T, kBMt * kBKT, 0, 1>() + wave * 4096
+                                : stage_buf<T, kBNB * kBKT, 1, 1>() + (wave - 4) * 4096;
+        const __amdgpu_buffer_rsrc_t rsrc_c = __builtin_amdgcn_make_buffer_rsrc(
+            reinterpret_cast<char*>(C + (int64_t)t_row0 * N), (short)0, t_mrows * N * (int)sizeof(T), kRsrcFlags);
+        // four values at row mb*32 + m32, columns nbx*32 + g*8 + h4 .. +3
+        const int wrow = m32 * 64 + h4;
+        const int wsw = (m32 >> 1) & 7;
+        typedef float f32x4v __attribute__((ext_vector_type(4)));
+        typedef T tx4 __attribute__((ext_vector_type(4)));
+        auto put4 = [&](float x0, float x1, float x2, float x3, int mb, int nbx, int g) {
+          const f32x4v xv = {x0, x1, x2, x3};
+          *reinterpret_cast<tx4*>(blk + mb * 2048 + wrow + (((nbx * 4 + g) ^ wsw) << 3)) =
+              __builtin_convertvector(xv, tx4);
+        };
+        // 64 rows x 64 columns from output column col_base: lane l reads
+        // chunk l%8 of rows l/8 + 8j; rows past the tile fall beyond the
+        // buffer's byte count, a chunk past N gets an out-of-range offset
+        // (N is a multiple of 8)
+        const int rr = lane >> 3, ch = lane & 7;
+        const T* const rd0 = blk + rr * 64 + ((ch ^ (rr >> 1)) << 3);
+        const T* const rd1 = blk + rr * 64 + ((ch ^ (rr >> 1) ^ 4) << 3);
+        auto drain = [&](int col_base) {
+          const int col = col_base + ch * 8;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const i32x4 d = *reinterpret_cast<const i32x4*>((j & 1 ? rd1 : rd0) + j * 512);
+            const int row = wm * kWaveM + rr + 8 * j;
+            const uint32_t vo = col < N ? (uint32_t)(row * N + col) * (uint32_t)sizeof(T) : kOutOfRange;
+            __builtin_amdgcn_raw_buffer_store_b128(d, rsrc_c, vo, 0, 0);
+          }
+        };
+        if constexpr (kSwiGlu) {
+#pragma unroll
+          for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+              for (int g = 0; g < 4; ++g) {
+                float hv[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                  // the product is rounded to fp32 before the conversion, as
+                  // on the register path: the empty asm keeps the compiler
+                  // from fusing multiply and conversion into one rounding
+                  hv[q] = silu(acc[mb][nb][4 * g + q]) * acc[mb][nb + 2][4 * g + q];
+                  asm("" : "+v"(hv[q]));
+                }
+                put4(hv[0], hv[1], hv[2], hv[3], mb, nb, g);
+              }
+          drain(t_nt * (kBNB / 2) + wn * 64);
+        } else {
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+            for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+              for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                  const f32x16& a = acc[mb][2 * hf + nb];
+                  put4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3], mb, nb, g);
+                }
+            drain(t_nt * kBNB + wn * (kBNB / 2) + hf * 64);
+          }
+        }
+      }
+      stores_out = 1;
+    } else if (has_rows) {
       const int esz = part ? 4 : (int)sizeof(T);
       char* base = part ? reinterpret_cast<char*>(p.partial + (int64_t)t_ks * p.rows * N + (int64_t)t_row0 * N)
                         : reinterpret_cast<char*>(C + (int64_t)t_row0 * N);
