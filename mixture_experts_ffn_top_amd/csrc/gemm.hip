@@ -28,8 +28,9 @@
 //
 // bf16/f16 kernel (gfx950 MFMA 32x32x16), two tile shapes:
 //  - 256 x kBNB tiles, 512 threads = 8 wavefronts as 4 (M) x 2 (N), 64 x
-//    kBNB/2 outputs per wavefront, two 64 KB LDS stages of K = 64: the loads
-//    of k-step kt+1 are issued at the top of k-step kt;
+//    kBNB/2 outputs per wavefront, K = 64 a stage, two 32 KB stages of the
+//    activation tile and three of the weight tile (160 KB): k-step kt
+//    requests the activations of kt+1 and the weights of kt+2;
 //  - weight streaming (at most 128 rows an expert on average, where the
 //    weights are read about once per 128 rows and the stream of weight tiles
 //    sets the time): 128 x kBNB tiles, 8 wavefronts of 32 x kBNB/2 outputs,
@@ -259,12 +260,13 @@ constexpr int gemm_threads() { return 64 * (kBMt / kWaveM) * 2; }
 // takes schedule entries b, b + G, b + 2G, ... (G = grid size, a multiple of
 // 8, so every entry it takes belongs to its own XCD's slice of the list).
 //
-// K is staged kBKT (64) elements at a time through kStg (2 or 3) LDS stages.
-// A stage row is 128 bytes, and each buffer load instruction fills 8 rows
-// with 128-byte row segments, which move through the load path about twice
-// as fast as 64-byte ones. The loads of k-step kt+kStg-1 are issued at the
-// top of k-step kt; the barrier that ends k-step kt waits only for k-step
-// kt+1's.
+// K is staged kBKT (64) elements at a time through LDS stages. A stage row
+// is 128 bytes, and each buffer load instruction fills 8 rows with 128-byte
+// row segments, which move through the load path about twice as fast as
+// 64-byte ones. 256-row tiles: two A stages and three B stages; k-step kt
+// requests A(kt+1) and B(kt+2) at its top, and the barrier that ends it
+// waits for A(kt+1) and B(kt+1) only. 128-row tiles: three stages of both;
+// the loads of k-step kt+2 are issued at the top of k-step kt.
 //
 // Between tiles: once every wavefront has finished reading LDS, the first
 // stage of the next tile is requested, and only then are the finished
@@ -297,6 +299,10 @@ __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kern
   // time). The other shapes keep the token fragment as row operand and
   // transpose in registers.
   constexpr bool kLdsEpi = kStg == 2 && !kCache && kBMt == 256 && kWaveM == 64 && kBNB == 256;
+  // 256-row tiles: two A stages and three B stages (160 KB of LDS), so that
+  // weight tiles, which mostly come from HBM, are requested two k-steps
+  // ahead and activation tiles, which mostly hit the caches, one.
+  constexpr bool kB3 = kStg == 2 && kBMt == 256;
 
   int v = blockIdx.x;
   Tile tile;
@@ -322,7 +328,10 @@ __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kern
   const int kc = c_lane * 8;  // element offset of this lane's chunk within a stage
 
   // Per-tile load state.
-  __amdgpu_buffer_rsrc_t rsrc_b0, rsrc_b1;
+  // the expert's weight bases (the buffer resources are rebuilt at each
+  // use from these scalars)
+  const T* wb0;
+  const T* wb1;
   uint32_t vo_a[kLoadsA], vo_b[kLoadsB];
   int e, ks, row0, n_t, mrows, k_begin, k_end;
   // Source rows of this lane's A chunks (through the row map when there is
@@ -343,12 +352,8 @@ __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kern
     k_begin = ks * p.k_chunk;
     k_end = min(K, k_begin + p.k_chunk);
     const int64_t expert_elems = (int64_t)e * N * K;
-    rsrc_b0 = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<T*>(static_cast<const T*>(p.b0) + expert_elems), (short)0, b_bytes, kRsrcFlags);
-    rsrc_b1 = kSwiGlu
-        ? __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(static_cast<const T*>(p.b1) + expert_elems),
-                                            (short)0, b_bytes, kRsrcFlags)
-        : rsrc_b0;
+    wb0 = static_cast<const T*>(p.b0) + expert_elems;
+    wb1 = kSwiGlu ? static_cast<const T*>(p.b1) + expert_elems : wb0;
 #pragma unroll
     for (int j = 0; j < kLoadsA; ++j) {
       const int r = (j * kWaves + wave) * kRowsPerInst + lane / kCh;
@@ -364,6 +369,25 @@ __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kern
     }
   };
 
+  auto issue_a = [&](int kt, T* la) __attribute__((always_inline)) {
+    const int k0 = k_begin + kt * kBKT;
+    const uint32_t soff = (uint32_t)k0 * sizeof(T);
+    const bool in_k = k0 + kc < k_end;
+#pragma unroll
+    for (int j = 0; j < kLoadsA; ++j)
+      load_lds16(rsrc_a, la + (j * kWaves + wave) * 64 * 8, in_k ? vo_a[j] : kOutOfRange, soff);
+  };
+  auto issue_b = [&](int kt, T* lb) __attribute__((always_inline)) {
+    const int k0 = k_begin + kt * kBKT;
+    const uint32_t soff = (uint32_t)k0 * sizeof(T);
+    const bool in_k = k0 + kc < k_end;
+#pragma unroll
+    for (int j = 0; j < kLoadsB; ++j)
+      load_lds16(__builtin_amdgcn_make_buffer_rsrc(
+                     const_cast<T*>(kSwiGlu && j * kWaves * kRowsPerInst >= kBNB / 2 ? wb1 : wb0), (short)0,
+                     b_bytes, kRsrcFlags),
+                 lb + (j * kWaves + wave) * 64 * 8, in_k ? vo_b[j] : kOutOfRange, soff);
+  };
   auto issue_loads = [&](int kt, T* la, T* lb) {
     const int k0 = k_begin + kt * kBKT;
     const uint32_t soff = (uint32_t)k0 * sizeof(T);
@@ -375,7 +399,9 @@ __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kern
     for (int j = 0; j < kLoadsB; ++j)
       // fused gate/up: B rows 0..127 come from gate, 128..255 from up; the
       // split falls between instructions
-      load_lds16(kSwiGlu && j * kWaves * kRowsPerInst >= kBNB / 2 ? rsrc_b1 : rsrc_b0,
+      load_lds16(__builtin_amdgcn_make_buffer_rsrc(
+                     const_cast<T*>(kSwiGlu && j * kWaves * kRowsPerInst >= kBNB / 2 ? wb1 : wb0), (short)0,
+                     b_bytes, kRsrcFlags),
                  lb + (j * kWaves + wave) * 64 * 8, in_k ? vo_b[j] : kOutOfRange, soff);
   };
 
@@ -395,14 +421,14 @@ __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kern
 
   f32x16 acc[kMB][kNB];
   Frag fa[2][kMB], fb[2][kNB];
-  auto read_frags = [&](const T* la, const T* lb, int s, int slot) {
+  auto read_frags = [&](const T* la, const T* lb, int s, int slot) __attribute__((always_inline)) {
     const int c = ((2 * s + (lane >> 5)) ^ sw) * 8;
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb) fa[slot][mb] = *reinterpret_cast<const Frag*>(la + a_row[mb] + c);
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) fb[slot][nb] = *reinterpret_cast<const Frag*>(lb + b_row[nb] + c);
   };
-  auto mfmas = [&](int slot, int from, int to) {
+  auto mfmas = [&](int slot, int from, int to) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = from; i < to; ++i) {
       if constexpr (kLdsEpi)
@@ -423,7 +449,7 @@ __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kern
   // sub-step 0 fragment reads overlapping the other half of the last
   // sub-step]. A wavefront whose rows all lie past the expert's last row
   // (short M-tiles) runs the same loads and barriers without reads or MFMAs.
-  auto step = [&](auto stage, auto compute, int kt, int nk_pad) {
+  auto step = [&](auto stage, auto compute, int kt, int nk_pad) __attribute__((always_inline)) {
     constexpr int S = decltype(stage)::value;
     constexpr bool kCompute = decltype(compute)::value;
     constexpr int X = (S + 1) % kStg;        // stage read next
@@ -473,10 +499,81 @@ __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kern
       if (i < kMfma / 2) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
   };
+  // Three B stages: k-step kt reads A slot kt % 2 and B slot kt % 3,
+  // requests A(kt+1) and B(kt+2) at its top (their slots were last read in
+  // k-step kt-1), and before its barrier waits for A(kt+1) and B(kt+1)
+  // (issued a k-step earlier), leaving B(kt+2) in flight.
+  auto step3 = [&](auto jc, auto compute, int kt, int nk) __attribute__((always_inline)) {
+    constexpr int J = decltype(jc)::value;
+    constexpr bool kCompute = decltype(compute)::value;
+    T* ca = stage_buf<T, kBMt * kBKT, 0, J % 2>();
+    T* cb = stage_buf<T, kBNB * kBKT, 1, J % 3>();
+    const bool more_a = kt + 1 < nk, more_b = kt + 2 < nk;
+    if (more_a) issue_a(kt + 1, stage_buf<T, kBMt * kBKT, 0, (J + 1) % 2>());
+    if (more_b) issue_b(kt + 2, stage_buf<T, kBNB * kBKT, 1, (J + 2) % 3>());
+    auto wait_next = [&]() __attribute__((always_inline)) {
+      if (more_b)
+        wait_vmem<kLoadsB>();
+      else
+        wait_vmem<0>();
+    };
+    if constexpr (!kCompute) {
+      wait_next();
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      return;
+    }
+#pragma unroll
+    for (int sub = 0; sub + 1 < kSub; ++sub) {
+      read_frags(ca, cb, sub + 1, (sub + 1) & 1);
+      mfmas(sub & 1, 0, kMfma);
+#pragma unroll
+      for (int i = 0; i < kMfma; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (sub == 0 && i < kLoads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        if (i < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+    constexpr int kLast = (kSub - 1) & 1;
+    mfmas(kLast, 0, kMfma / 2);
+    __builtin_amdgcn_sched_group_barrier(0x008, kMfma / 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_next();
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(stage_buf<T, kBMt * kBKT, 0, (J + 1) % 2>(), stage_buf<T, kBNB * kBKT, 1, (J + 1) % 3>(), 0, 0);
+    mfmas(kLast, kMfma / 2, kMfma);
+#pragma unroll
+    for (int i = 0; i < kReads; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (i < kMfma / 2) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+  };
+  // Unrolled by 6 (the slot periods 2 and 3), leaving after the tile's last
+  // k-step wherever it falls.
+  auto main_loop3 = [&](auto compute, int nk) __attribute__((always_inline)) {
+    if constexpr (decltype(compute)::value)
+      read_frags(stage_buf<T, kBMt * kBKT, 0, 0>(), stage_buf<T, kBNB * kBKT, 1, 0>(), 0, 0);
+    const int nk6 = nk / 6 * 6;
+    for (int kt = 0; kt < nk6; kt += 6) {
+      step3(std::integral_constant<int, 0>{}, compute, kt, nk);
+      step3(std::integral_constant<int, 1>{}, compute, kt + 1, nk);
+      step3(std::integral_constant<int, 2>{}, compute, kt + 2, nk);
+      step3(std::integral_constant<int, 3>{}, compute, kt + 3, nk);
+      step3(std::integral_constant<int, 4>{}, compute, kt + 4, nk);
+      step3(std::integral_constant<int, 5>{}, compute, kt + 5, nk);
+    }
+    // the last nk % 6 k-steps (slots continue from 0)
+    const int r = nk - nk6;
+    if (r > 0) step3(std::integral_constant<int, 0>{}, compute, nk6, nk);
+    if (r > 1) step3(std::integral_constant<int, 1>{}, compute, nk6 + 1, nk);
+    if (r > 2) step3(std::integral_constant<int, 2>{}, compute, nk6 + 2, nk);
+    if (r > 3) step3(std::integral_constant<int, 3>{}, compute, nk6 + 3, nk);
+    if (r > 4) step3(std::integral_constant<int, 4>{}, compute, nk6 + 4, nk);
+  };
   // Main loop over one tile, unrolled by the stages so every LDS pointer is
   // a fixed object. The trip count is padded to a multiple of the stage
   // count: loads past K are masked to zeros, so a padding step adds nothing.
-  auto main_loop = [&](auto compute, int nk_pad) {
+  auto main_loop = [&](auto compute, int nk_pad) __attribute__((always_inline)) {
     if constexpr (decltype(compute)::value)
       read_frags(stage_buf<T, kBMt * kBKT, 0, 0>(), stage_buf<T, kBNB * kBKT, 1, 0>(), 0, 0);
     for (int kt = 0; kt < nk_pad; kt += kStg) {
@@ -487,6 +584,13 @@ __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kern
   };
   // The first kStg - 1 k-steps of a tile are requested ahead of its loop.
   auto issue_first = [&]() {
+    if constexpr (kB3) {
+      // A(0), B(0), then B(1) (which may stay in flight when the tile starts)
+      issue_a(0, stage_buf<T, kBMt * kBKT, 0, 0>());
+      issue_b(0, stage_buf<T, kBNB * kBKT, 1, 0>());
+      issue_b(1, stage_buf<T, kBNB * kBKT, 1, 1>());
+      return;
+    }
     issue_loads(0, stage_buf<T, kBMt * kBKT, 0, 0>(), stage_buf<T, kBNB * kBKT, 1, 0>());
     if constexpr (kStg == 3) issue_loads(1, stage_buf<T, kBMt * kBKT, 0, 1>(), stage_buf<T, kBNB * kBKT, 1, 1>());
   };
@@ -521,7 +625,7 @@ __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kern
     const int nk_pad = (nk + kStg - 1) / kStg * kStg;
     // Stages 0 .. kStg-2 of this tile have been requested; wait for stage 0
     // (not for the later stages or the previous tile's stores, issued after it).
-    constexpr int kAhead = (kStg - 2) * kLoads;
+    constexpr int kAhead = kB3 ? kLoadsB : (kStg - 2) * kLoads;
     if (stores_prev)
       wait_vmem<kStoresWait + kAhead>();
     else
@@ -534,10 +638,17 @@ __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kern
     const bool more = tile_of_block(p, v + gridDim.x, next);
     int nsrc[kLoadsA];
     if (more) a_src(next, nsrc);
-    if (has_rows)
-      main_loop(std::true_type{}, nk_pad);
-    else
-      main_loop(std::false_type{}, nk_pad);
+    if constexpr (kB3) {
+      if (has_rows)
+        main_loop3(std::true_type{}, nk);
+      else
+        main_loop3(std::false_type{}, nk);
+    } else {
+      if (has_rows)
+        main_loop(std::true_type{}, nk_pad);
+      else
+        main_loop(std::false_type{}, nk_pad);
+    }
     // Every wavefront is done with LDS before the next tile's loads land.
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     const int t_row0 = row0, t_mrows = mrows, t_nt = n_t, t_ks = ks;
@@ -594,7 +705,7 @@ __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kern
         // of an 8-byte write instruction and the 8 rows of a 16-byte read
         // spread over all banks.
         T* const blk = wave < 4 ? stage_buf<T, kBMt * kBKT, 0, 1>() + wave * 4096
-                                : stage_buf<T, kBNB * kBKT, 1, 1>() + (wave - 4) * 4096;
+                                : stage_buf<T, kBNB * kBKT, 1, kB3 ? 2 : 1>() + (wave - 4) * 4096;
         const __amdgpu_buffer_rsrc_t rsrc_c = __builtin_amdgcn_make_buffer_rsrc(
             reinterpret_cast<char*>(C + (int64_t)t_row0 * N), (short)0, t_mrows * N * (int)sizeof(T), kRsrcFlags);
         // four values at row mb*32 + m32, columns nbx*32 + g*8 + h4 .. +3
@@ -1229,7 +1340,7 @@ float* partial_buffer(const ExpertsPlan& plan, void* scratch) {
                          : nullptr;
 }
 
-// Workgroups of the persistent MFMA GEMM: one per CU (its 128 KB of LDS
+// Workgroups of the persistent MFMA GEMM: one per CU (its 144-160 KB of LDS
 // stages leave room for no second one), at most one per schedule entry; a
 // multiple of 8 so each workgroup stays on the XCD its entries belong to.
 static int persistent_grid(int entries) {
