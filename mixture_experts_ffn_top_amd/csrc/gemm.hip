@@ -534,19 +534,25 @@ __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kern
       }
     }
     constexpr int kLast = (kSub - 1) & 1;
-    mfmas(kLast, 0, kMfma / 2);
-    __builtin_amdgcn_sched_group_barrier(0x008, kMfma / 2, 0);
+    // MFMAs of the last sub-step left for after the barrier, where they
+    // cover the next stage's first fragment reads: 6 of 8 in gate/up, half
+    // in the down GEMM (measured: 6 or 8 helped gate/up by 1-3 %, 8 slowed
+    // the down GEMM by 2 %)
+    constexpr int kDefer = kSwiGlu ? 6 : kMfma / 2;
+    mfmas(kLast, 0, kMfma - kDefer);
+    __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kDefer, 0);
     __builtin_amdgcn_sched_barrier(0);
     wait_next();
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
     read_frags(stage_buf<T, kBMt * kBKT, 0, (J + 1) % 2>(), stage_buf<T, kBNB * kBKT, 1, (J + 1) % 3>(), 0, 0);
-    mfmas(kLast, kMfma / 2, kMfma);
+    mfmas(kLast, kMfma - kDefer, kMfma);
 #pragma unroll
     for (int i = 0; i < kReads; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (i < kMfma / 2) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < kDefer) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
+    static_assert(kDefer <= kReads, "deferred MFMAs pair with the next stage's reads");
   };
   // Unrolled by 6 (the slot periods 2 and 3), leaving after the tile's last
   // k-step wherever it falls.
