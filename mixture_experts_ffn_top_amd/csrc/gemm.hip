@@ -276,7 +276,8 @@ template <typename T, bool kSwiGlu, int kBNB, int kBKT, int kWaveM, bool kCache 
           int kStg = 2>
 __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kernel(GemmArgs p) {
   typedef typename Mfma<T>::Frag Frag;
-  static_assert(kStg == 2 || kStg == 3, "two or three LDS stages");
+  static_assert((kStg == 2 && kBMt == 256) || (kStg == 3 && kBMt == 128),
+                "256-row tiles (2 activation + 3 weight stages) or 128-row tiles (3 + 3)");
   constexpr int kWaves = (kBMt / kWaveM) * 2;
   constexpr int kThreadsK = 64 * kWaves;
   constexpr int kCh = kBKT / 8;                       // 16-byte chunks per LDS row
@@ -301,8 +302,9 @@ __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kern
   constexpr bool kLdsEpi = kStg == 2 && !kCache && kBMt == 256 && kWaveM == 64 && kBNB == 256;
   // 256-row tiles: two A stages and three B stages (160 KB of LDS), so that
   // weight tiles, which mostly come from HBM, are requested two k-steps
-  // ahead and activation tiles, which mostly hit the caches, one.
-  constexpr bool kB3 = kStg == 2 && kBMt == 256;
+  // ahead and activation tiles, which mostly hit the caches, one. 128-row
+  // tiles: three stages of both (step / main_loop below).
+  constexpr bool kB3 = kStg == 2;
 
   int v = blockIdx.x;
   Tile tile;
@@ -440,10 +442,10 @@ __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kern
   constexpr int kMfma = kMB * kNB;   // MFMAs per k16 sub-step
   constexpr int kReads = kMB + kNB;  // fragment reads per sub-step
 
-  // One K-stage: compute from stage S while the other stage is refilled for
-  // k-step kt+1 (none after the tile's last padded step). The barrier is a
-  // plain s_barrier (a scheduling boundary): a fenced __syncthreads would
-  // make the compiler drain every LDS-DMA load in flight.
+  // 128-row tiles, one K-stage: compute from stage S while stage L is
+  // refilled for k-step kt+2 (none in the tile's last two padded steps). The
+  // barrier is a plain s_barrier (a scheduling boundary): a fenced
+  // __syncthreads would make the compiler drain every LDS-DMA load in flight.
   // Order: [loads, sub-step s MFMAs interleaved with sub-step s+1 fragment
   // reads ..., half of the last sub-step] wait + barrier [next stage's
   // sub-step 0 fragment reads overlapping the other half of the last
@@ -458,11 +460,11 @@ __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kern
     T* cb = stage_buf<T, kBNB * kBKT, 1, S>();
     const bool refill = kt + kStg - 1 < nk_pad;
     if (refill) issue_loads(kt + kStg - 1, stage_buf<T, kBMt * kBKT, 0, L>(), stage_buf<T, kBNB * kBKT, 1, L>());
-    // Stage X (k-step kt+1) must have landed by the barrier; with three
-    // stages the loads just issued for kt+2 may stay in flight.
+    // Stage X (k-step kt+1) must have landed by the barrier; the loads just
+    // issued for kt+2 may stay in flight.
     auto wait_next = [&]() {
-      if (kStg == 3 && refill)
-        wait_vmem<kStg == 3 ? kLoads : 0>();
+      if (refill)
+        wait_vmem<kLoads>();
       else
         wait_vmem<0>();
     };
@@ -585,10 +587,10 @@ __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kern
     for (int kt = 0; kt < nk_pad; kt += kStg) {
       step(std::integral_constant<int, 0>{}, compute, kt, nk_pad);
       step(std::integral_constant<int, 1>{}, compute, kt + 1, nk_pad);
-      if constexpr (kStg == 3) step(std::integral_constant<int, 2>{}, compute, kt + 2, nk_pad);
+      step(std::integral_constant<int, 2>{}, compute, kt + 2, nk_pad);
     }
   };
-  // The first kStg - 1 k-steps of a tile are requested ahead of its loop.
+  // The first loads of a tile, requested ahead of its loop.
   auto issue_first = [&]() {
     if constexpr (kB3) {
       // A(0), B(0), then B(1) (which may stay in flight when the tile starts)
@@ -598,7 +600,7 @@ __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kern
       return;
     }
     issue_loads(0, stage_buf<T, kBMt * kBKT, 0, 0>(), stage_buf<T, kBNB * kBKT, 1, 0>());
-    if constexpr (kStg == 3) issue_loads(1, stage_buf<T, kBMt * kBKT, 0, 1>(), stage_buf<T, kBNB * kBKT, 1, 1>());
+    issue_loads(1, stage_buf<T, kBMt * kBKT, 0, 1>(), stage_buf<T, kBNB * kBKT, 1, 1>());
   };
 
   {
@@ -629,9 +631,10 @@ __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kern
         for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
     const int nk = (k_end - k_begin + kBKT - 1) / kBKT;
     const int nk_pad = (nk + kStg - 1) / kStg * kStg;
-    // Stages 0 .. kStg-2 of this tile have been requested; wait for stage 0
-    // (not for the later stages or the previous tile's stores, issued after it).
-    constexpr int kAhead = kB3 ? kLoadsB : (kStg - 2) * kLoads;
+    // This tile's first loads have been requested; wait for k-step 0's (not
+    // for the weights of k-step 1, or the loads of k-step 1 with 128-row
+    // tiles, or the previous tile's stores, all issued after them).
+    constexpr int kAhead = kB3 ? kLoadsB : kLoads;
     if (stores_prev)
       wait_vmem<kStoresWait + kAhead>();
     else
@@ -711,7 +714,7 @@ __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kern
         // of an 8-byte write instruction and the 8 rows of a 16-byte read
         // spread over all banks.
         T* const blk = wave < 4 ? stage_buf<T, kBMt * kBKT, 0, 1>() + wave * 4096
-                                : stage_buf<T, kBNB * kBKT, 1, kB3 ? 2 : 1>() + (wave - 4) * 4096;
+                                : stage_buf<T, kBNB * kBKT, 1, 2>() + (wave - 4) * 4096;
         const __amdgpu_buffer_rsrc_t rsrc_c = __builtin_amdgcn_make_buffer_rsrc(
             reinterpret_cast<char*>(C + (int64_t)t_row0 * N), (short)0, t_mrows * N * (int)sizeof(T), kRsrcFlags);
         // four values at row mb*32 + m32, columns nbx*32 + g*8 + h4 .. +3
