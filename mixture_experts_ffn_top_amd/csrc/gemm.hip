@@ -1111,22 +1111,36 @@ __global__ __launch_bounds__(64 * kRowsWaves) void skinny_down_kernel(SkinnyArgs
       }
     };
     constexpr int kLoadsPerIter = kT * 4 + 4;
+    auto mfma = [&](const uint4 (&wd)[kT][4], const uint4 (&xd)[4]) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int t = 0; t < kT; ++t)
+          acc[t] = Mfma16<T>::run(__builtin_bit_cast(Frag, wd[t][c]), __builtin_bit_cast(Frag, xd[c]), acc[t]);
+    };
 #pragma unroll
     for (int d = 0; d + 1 < kDepth; ++d) load(d, w[d], x[d]);
-    for (int it0 = 0; it0 < n_it; it0 += kDepth) {
+    // Loads run kDepth - 1 iterations ahead of the MFMAs. Full blocks of
+    // kDepth iterations whose loads all lie before the last iteration run
+    // without branches; the rest (fewer than 2 kDepth - 1 iterations) issues
+    // no load past the last iteration (such loads, all out of range, had
+    // cost 3 % of the launch's time on the decode shape).
+    int it0 = 0;
+    for (; it0 + 2 * kDepth - 2 < n_it; it0 += kDepth) {
 #pragma unroll
       for (int d = 0; d < kDepth; ++d) {
-        // keep the loads kDepth - 1 iterations ahead of this one's MFMAs
         load(it0 + d + kDepth - 1, w[(d + kDepth - 1) % kDepth], x[(d + kDepth - 1) % kDepth]);
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-          for (int t = 0; t < kT; ++t)
-            acc[t] = Mfma16<T>::run(__builtin_bit_cast(Frag, w[d][t][c]), __builtin_bit_cast(Frag, x[d][c]),
-                                    acc[t]);
+        mfma(w[d], x[d]);
         __builtin_amdgcn_sched_group_barrier(0x020, kLoadsPerIter, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 4 * kT, 0);
       }
+    }
+#pragma unroll
+    for (int d = 0; d < 2 * kDepth - 2; ++d) {
+      if (it0 + d >= n_it) break;
+      if (it0 + d + kDepth - 1 < n_it)
+        load(it0 + d + kDepth - 1, w[(d + kDepth - 1) % kDepth], x[(d + kDepth - 1) % kDepth]);
+      mfma(w[d % kDepth], x[d % kDepth]);
     }
     // D element v of lane l: weight row (l/16)*4 + v of the tile, token l%16.
     const int tok = rg + (lane & 15);
