@@ -507,18 +507,12 @@ moe_status forward_impl(const void* x, const void* logits, moe_dtype logits_dt, 
     e = launch_gate_up(x, sor, (int)top_k, offsets, (int)slots, (int)E, (int)H, (int)I, w_gate,
                        w_up, dt, h, base + L.experts, stream);
   if (e == hipSuccess) e = mark(3);
-  // When the down GEMM splits K, its fp32 partial sums go straight to the
-  // combine, which rounds each expert row exactly as expert_out would be.
-  DownPartials part;
   if (e == hipSuccess)
     e = launch_down(h, offsets, (int)slots, (int)E, (int)H, (int)I, w_down, dt, y,
-                    base + L.experts, stream, &part);
+                    base + L.experts, stream);
   if (e == hipSuccess) e = mark(4);
   if (e == hipSuccess)
-    e = part.splits > 1
-            ? launch_combine_partials(part, ros, w, logits_dt, (int)T, (int)top_k, (int)H, dt, out,
-                                      stream)
-            : launch_combine(y, ros, w, logits_dt, (int)T, (int)top_k, (int)H, dt, out, stream);
+    e = launch_combine(y, ros, w, logits_dt, (int)T, (int)top_k, (int)H, dt, out, stream);
   if (e == hipSuccess) e = mark(5);
   return from_hip(e);
 }

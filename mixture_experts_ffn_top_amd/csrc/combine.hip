@@ -114,65 +114,6 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y,
   o.store(out + (int64_t)t * H + v * 8);
 }
 
-// As combine_kernel, but expert rows are split-K partial sums: each row is
-// summed over the splits in order and rounded to T before it is weighted.
-template <typename T, typename WT>
-__global__ __launch_bounds__(256) void combine_partials_kernel(
-    const float* __restrict__ partial, int splits, int64_t split_stride,
-    const int32_t* __restrict__ row_of_slot, const WT* __restrict__ w, int k, int H,
-    int blocks_per_token, T* __restrict__ out) {
-  const int t = blockIdx.x / blocks_per_token;
-  const int v = (blockIdx.x % blocks_per_token) * blockDim.x + threadIdx.x;
-  if (v * 8 >= H) return;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  bool lost = false;
-  constexpr int kC = 4;
-  for (int j0 = 0; j0 < k; j0 += kC) {
-    float4 a0[kC], a1[kC];
-    float wj[kC];
-    const float* src[kC];
-#pragma unroll
-    for (int j = 0; j < kC; ++j) {
-      wj[j] = 0.f;
-      src[j] = nullptr;
-      if (j0 + j < k) {
-        const int r = row_of_slot[(int64_t)t * k + j0 + j];
-        wj[j] = to_f32(w[(int64_t)t * k + j0 + j]);
-        if (r < 0) {
-          lost = true;
-        } else {
-          src[j] = partial + (int64_t)r * H + v * 8;
-          a0[j] = *reinterpret_cast<const float4*>(src[j]);
-          a1[j] = *reinterpret_cast<const float4*>(src[j] + 4);
-        }
-      }
-    }
-    for (int sp = 1; sp < splits; ++sp) {
-#pragma unroll
-      for (int j = 0; j < kC; ++j) {
-        if (src[j]) {
-          const float4 b0 = *reinterpret_cast<const float4*>(src[j] + sp * split_stride);
-          const float4 b1 = *reinterpret_cast<const float4*>(src[j] + sp * split_stride + 4);
-          a0[j].x += b0.x; a0[j].y += b0.y; a0[j].z += b0.z; a0[j].w += b0.w;
-          a1[j].x += b1.x; a1[j].y += b1.y; a1[j].z += b1.z; a1[j].w += b1.w;
-        }
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < kC; ++j) {
-      if (src[j]) {
-        const float y[8] = {a0[j].x, a0[j].y, a0[j].z, a0[j].w, a1[j].x, a1[j].y, a1[j].z, a1[j].w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj[j], to_f32(from_f32<T>(y[i])), acc[i]);
-      }
-    }
-  }
-  Vec8<T> o;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) o.set(i, lost ? NAN : acc[i]);
-  o.store(out + (int64_t)t * H + v * 8);
-}
-
 // One workgroup per token, one thread per VPT groups of 8 columns (strided
 // by the workgroup); x stays in registers between the sum of squares and the
 // scaling. The expert rows' loads are issued first, at most 16 16-byte
@@ -297,34 +238,7 @@ hipError_t norm_w(const void* y, const int32_t* ros, const void* w, int w_dt, co
   }
 }
 
-template <typename T, typename WT>
-hipError_t combine_partials_t(const DownPartials& part, const int32_t* ros, const void* w, int T_,
-                              int k, int H, void* out, hipStream_t s) {
-  const int bpt = (H / 8 + 255) / 256;
-  hipLaunchKernelGGL((combine_partials_kernel<T, WT>), dim3((int64_t)T_ * bpt), dim3(256), 0, s,
-                     part.partial, part.splits, part.split_stride, ros, static_cast<const WT*>(w),
-                     k, H, bpt, static_cast<T*>(out));
-  return hipGetLastError();
-}
-
-template <typename T>
-hipError_t combine_partials_w(const DownPartials& part, const int32_t* ros, const void* w,
-                              int w_dt, int T_, int k, int H, void* out, hipStream_t s) {
-  switch (w_dt) {
-    case kF32: return combine_partials_t<T, float>(part, ros, w, T_, k, H, out, s);
-    case kF16: return combine_partials_t<T, f16>(part, ros, w, T_, k, H, out, s);
-    default: return combine_partials_t<T, bf16>(part, ros, w, T_, k, H, out, s);
-  }
-}
-
 }  // namespace
-
-hipError_t launch_combine_partials(const DownPartials& part, const int32_t* row_of_slot,
-                                   const void* weights, int w_dt, int T, int k, int H, int dt,
-                                   void* out, hipStream_t s) {
-  if (dt == kF16) return combine_partials_w<f16>(part, row_of_slot, weights, w_dt, T, k, H, out, s);
-  return combine_partials_w<bf16>(part, row_of_slot, weights, w_dt, T, k, H, out, s);
-}
 
 hipError_t launch_combine(const void* expert_out, const int32_t* row_of_slot, const void* weights,
                           int w_dt, int T, int k, int H, int dt, void* out, hipStream_t s) {

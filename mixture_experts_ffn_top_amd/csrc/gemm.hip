@@ -51,10 +51,11 @@
 // so the 16 rows read together must cover all 16 (row mod 2, chunk) slots:
 // chunk c of row r is stored at c ^ ((r >> 1) & 7).
 //
-// Split-K (GEMM 2, when the M x N tiles alone cannot fill the chip): k_splits
-// workgroups per output tile each cover one K range and write fp32 partials;
-// a separate pass (or the combine) sums them in split order, so results do
-// not depend on scheduling.
+// Split-K of the last round (GEMM 2): the tiles left over after the full
+// rounds of workgroups are split along K, each K range written as fp32
+// partial sums to a block of its own; a separate pass adds them in K-range
+// order, so results do not depend on scheduling. Every other tile covers all
+// of K and stores its output directly.
 //
 // In GEMM 1 the B tile holds 128 gate rows and the same 128 up rows, and
 // every wavefront owns matching gate and up accumulators, so SiLU(g) * u is
@@ -78,13 +79,17 @@ constexpr int kXcds = sched::kXcds;
 constexpr int kRsrcFlags = 0x00020000;
 constexpr uint32_t kOutOfRange = 0x80000000u;  // voffset past any buffer we build (< 2^31 bytes)
 
-// One schedule entry per workgroup: x = expert | (K-split << 16), y = first
-// row, z = end row (exclusive), w = N-tile; x < 0: no tile. The list and its
-// split into XCD slices are those of schedule.h.
+// One schedule entry per slot: x = expert | (K-range << 16) | (K-ranges of
+// the tile << 20), y = first row, z = end row (exclusive), w = N-tile | (index
+// of a split tile among the last round's << 16); x < 0: no tile. The list,
+// its XCD slices and the split of the last round are those of schedule.h.
+// With a split last round, split[0] = (r, s) and split[1 + u] = (expert,
+// first row, end row, N-tile) of split tile u, for the reduction of its
+// partial sums; split[0].y = 1 otherwise.
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ offsets, int E,
                                                      int rows, int bm, int max_tiles,
-                                                     int n_tiles_n, int k_splits, int grid,
-                                                     int4* __restrict__ sched) {
+                                                     int n_tiles_n, int cap, int wgs, int grid,
+                                                     int4* __restrict__ sched, int4* __restrict__ split) {
   __shared__ int s_first[kMaxExperts + 1], s_lo[kMaxExperts], s_hi[kMaxExperts];
   const int e = threadIdx.x;
   int lo = 0, hi = 0, n = 0;
@@ -109,19 +114,22 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   t.E = E;
   t.bm = bm;
   t.n_tiles_n = n_tiles_n;
-  t.k_splits = k_splits;
-  t.per_split = min(total, max_tiles) * n_tiles_n;
-  t.n_real = t.per_split * k_splits;
+  t.tiles = min(total, max_tiles) * n_tiles_n;
+  const sched::Rounds d = sched::rounds_of(t, wgs, cap);
   for (int b = blockIdx.x * blockDim.x + threadIdx.x; b < grid; b += gridDim.x * blockDim.x) {
-    int begin, end;
-    sched::xcd_range(t, b % sched::kXcds, &begin, &end);
-    const int L = begin + b / sched::kXcds;
+    sched::Entry en;
     int4 v = make_int4(-1, 0, 0, 0);
-    if (L < end) {
-      const sched::Entry en = sched::entry_at(t, L);
-      v = make_int4(en.ex | (en.ks << 16), en.row0, en.row_end, en.n_t);
-    }
+    if (sched::slot_entry(t, d, b, &en))
+      v = make_int4(en.ex | (en.ks << 16) | (en.s << 20), en.row0, en.row_end, en.n_t | (en.u << 16));
     sched[b] = v;
+  }
+  if (split != nullptr && blockIdx.x == 0) {
+    if (threadIdx.x == 0) split[0] = make_int4(d.r, d.s, 0, 0);
+    if (d.s > 1)
+      for (int u = threadIdx.x; u < d.r; u += blockDim.x) {
+        const sched::Entry en = sched::entry_at(t, d.q * d.W + u);
+        split[1 + u] = make_int4(en.ex, en.row0, en.row_end, en.n_t);
+      }
   }
 }
 
@@ -136,11 +144,12 @@ struct GemmArgs {
   const int32_t* offsets;  // [E+1]
   const int4* sched;       // [grid] entries written by plan_kernel
   int rows, N, K, max_tiles, n_tiles_n, grid;
-  int bm;  // rows per M-tile of the schedule (selects the kernel's tile shape)
-  // Split-K (GEMM 2 only): k_splits workgroups share one output tile, each
-  // over k_chunk elements of K, writing fp32 partial sums to
-  // partial[split][rows][N]; the caller reduces them in split order.
-  int k_splits, k_chunk;
+  int wgs;  // workgroups of the persistent MFMA kernel (a multiple of 8)
+  int bm;   // rows per M-tile of the schedule (selects the kernel's tile shape)
+  // GEMM 2 only: a tile of the last round whose K is split s ways writes the
+  // fp32 partial sums of K-range ks to partial + (u * s + ks) * bm * 256, a
+  // bm x 256 block (u: its index among the split tiles); they are added in
+  // K-range order afterwards.
   float* partial;
   // GEMM 1 of the experts' training forward: also store g and u, rounded to
   // T, into cache[rows, 2N] = (g | u), and form h from those rounded values.
@@ -164,12 +173,12 @@ template <> struct Mfma<f16> {
 // SiLU with the hardware reciprocal (1 ulp) in place of a full division.
 __device__ __forceinline__ float silu(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
-inline int64_t grid_tiles(int64_t max_tiles, int64_t n_tiles_n, int64_t k_splits) {
-  return (max_tiles * n_tiles_n * k_splits + kXcds - 1) / kXcds * kXcds;
+inline int64_t grid_tiles(int64_t max_tiles, int64_t n_tiles_n) {
+  return (max_tiles * n_tiles_n + kXcds - 1) / kXcds * kXcds;
 }
 
 struct Tile {
-  int e, ks, row0, row_end, n_t;
+  int e, ks, s, u, row0, row_end, n_t;
 };
 
 // Schedule entry v (wave-uniform); false past the grid or if it holds no tile.
@@ -179,10 +188,13 @@ __device__ __forceinline__ bool tile_of_block(const GemmArgs& p, int v, Tile& t)
   const int x = __builtin_amdgcn_readfirstlane(e.x);
   if (x < 0) return false;
   t.e = x & 0xFFFF;
-  t.ks = x >> 16;
+  t.ks = (x >> 16) & 0xF;
+  t.s = x >> 20;
   t.row0 = __builtin_amdgcn_readfirstlane(e.y);
   t.row_end = __builtin_amdgcn_readfirstlane(e.z);
-  t.n_t = __builtin_amdgcn_readfirstlane(e.w);
+  const int w = __builtin_amdgcn_readfirstlane(e.w);
+  t.n_t = w & 0xFFFF;
+  t.u = w >> 16;
   return t.row0 < t.row_end;
 }
 
@@ -335,7 +347,7 @@ __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kern
   const T* wb0;
   const T* wb1;
   uint32_t vo_a[kLoadsA], vo_b[kLoadsB];
-  int e, ks, row0, n_t, mrows, k_begin, k_end;
+  int e, ks, ts, tu, row0, n_t, mrows, k_begin, k_end;
   // Source rows of this lane's A chunks (through the row map when there is
   // one). Fetched for the next tile at the start of the current one, so the
   // map's latency is hidden behind its k-steps.
@@ -349,10 +361,9 @@ __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kern
     }
   };
   auto setup = [&](const Tile& t, const int (&src)[kLoadsA]) {
-    e = t.e; ks = t.ks; row0 = t.row0; n_t = t.n_t;
+    e = t.e; ks = t.ks; ts = t.s; tu = t.u; row0 = t.row0; n_t = t.n_t;
     mrows = min(kBMt, t.row_end - row0);
-    k_begin = ks * p.k_chunk;
-    k_end = min(K, k_begin + p.k_chunk);
+    sched::k_range(K, kBKT, ks, ts, &k_begin, &k_end);
     const int64_t expert_elems = (int64_t)e * N * K;
     wb0 = static_cast<const T*>(p.b0) + expert_elems;
     wb1 = kSwiGlu ? static_cast<const T*>(p.b1) + expert_elems : wb0;
@@ -660,7 +671,8 @@ __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kern
     }
     // Every wavefront is done with LDS before the next tile's loads land.
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    const int t_row0 = row0, t_mrows = mrows, t_nt = n_t, t_ks = ks;
+    const int t_row0 = row0, t_mrows = mrows, t_nt = n_t, t_slot = tu * ts + ks;
+    const bool part = !kSwiGlu && ts > 1;
     v += gridDim.x;
     if (more) {
       setup(next, nsrc);
@@ -679,7 +691,6 @@ __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kern
     // after the next tile's first loads, and the next tile waits for its
     // loads with vmcnt(kStores) without draining the stores.
     int stores_out = 0;
-    const bool part = !kSwiGlu && p.partial != nullptr;
     if (kLdsEpi && has_rows) {
       // Lane l holds, for accumulator i of block (mb, nb), output row
       // mb*32 + l%32 of the wavefront and column nb*32 + (i/4)*8 + 4*(l/32)
@@ -687,25 +698,27 @@ __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kern
       const int m32 = lane & 31, h4 = (lane >> 5) * 4;
       if (part) {
         // fp32 split-K partials: 16 bytes per lane and group, straight out
+        // to the tile's own kBMt x kBNB block; its rows past the expert fall
+        // beyond the byte count, its columns past N are stored and never
+        // read, so every offset is this lane's base plus a constant
         const __amdgpu_buffer_rsrc_t rsrc_p = __builtin_amdgcn_make_buffer_rsrc(
-            reinterpret_cast<char*>(p.partial + (int64_t)t_ks * p.rows * N + (int64_t)t_row0 * N), (short)0,
-            t_mrows * N * 4, kRsrcFlags);
+            reinterpret_cast<char*>(p.partial + (int64_t)t_slot * kBMt * kBNB), (short)0,
+            t_mrows * kBNB * 4, kRsrcFlags);
+        const uint32_t vb = (uint32_t)((wm * kWaveM + m32) * kBNB + wn * (kBNB / 2) + h4) * 4u;
 #pragma unroll
         for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
           for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-              const int row = wm * kWaveM + mb * 32 + m32;
-              const int col = t_nt * kBNB + wn * (kBNB / 2) + nb * 32 + g * 8 + h4;
               // copied out first: a bit cast of a vector element reads the
               // vector's first element
               const float x0 = acc[mb][nb][4 * g], x1 = acc[mb][nb][4 * g + 1];
               const float x2 = acc[mb][nb][4 * g + 2], x3 = acc[mb][nb][4 * g + 3];
               const i32x4 d = {__builtin_bit_cast(int, x0), __builtin_bit_cast(int, x1),
                                __builtin_bit_cast(int, x2), __builtin_bit_cast(int, x3)};
-              const uint32_t vo = col < N ? (uint32_t)(row * N + col) * 4u : kOutOfRange;
-              __builtin_amdgcn_raw_buffer_store_b128(d, rsrc_p, vo, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b128(
+                  d, rsrc_p, vb + (uint32_t)((mb * 32 * kBNB + nb * 32 + g * 8) * 4), 0, 0);
             }
       } else {
         // Wavefront w's block goes to its own 8 KB of stage 1 (waves 0-3 in
@@ -781,11 +794,15 @@ __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kern
       }
       stores_out = 1;
     } else if (has_rows) {
+      // split-K partials go to the tile's own kBMt x kBNB block (row
+      // stride kBNB, columns from the tile's first), outputs to C
       const int esz = part ? 4 : (int)sizeof(T);
-      char* base = part ? reinterpret_cast<char*>(p.partial + (int64_t)t_ks * p.rows * N + (int64_t)t_row0 * N)
+      const int ld = part ? kBNB : N;
+      const int col_off = part ? t_nt * kBNB : 0;
+      char* base = part ? reinterpret_cast<char*>(p.partial + (int64_t)t_slot * kBMt * kBNB)
                         : reinterpret_cast<char*>(C + (int64_t)t_row0 * N);
       const __amdgpu_buffer_rsrc_t rsrc_c =
-          __builtin_amdgcn_make_buffer_rsrc(base, (short)0, t_mrows * N * esz, kRsrcFlags);
+          __builtin_amdgcn_make_buffer_rsrc(base, (short)0, t_mrows * ld * esz, kRsrcFlags);
       const int col4 = (lane & 31) & ~3;
       auto store_block = [&](float (&val)[16], int row_base, int col_base) {
 #pragma unroll
@@ -794,7 +811,7 @@ __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kern
           transpose4(x, lane);
           const int lrow = row_base + g * 8 + row_lane + (lane & 3);
           const int col = col_base + col4;
-          const uint32_t vo = (lrow < t_mrows && col < N) ? (uint32_t)(lrow * N + col) * (uint32_t)esz
+          const uint32_t vo = (lrow < t_mrows && col < N) ? (uint32_t)(lrow * ld + col - col_off) * (uint32_t)esz
                                                           : kOutOfRange;
           if (part) {
             const i32x4 d = {__builtin_bit_cast(int, x[0]), __builtin_bit_cast(int, x[1]),
@@ -1265,40 +1282,45 @@ static int64_t tile_n(int64_t N, int dt, bool swiglu) {
   return (N + w - 1) / w;
 }
 
-// Split-K of the down GEMM: when its output tiles would give the 256 CUs
-// fewer than four workgroups each, K is split so the last round of
-// workgroups is not left mostly empty; each split keeps >= 64 K-steps.
+// Split-K of the down GEMM's last round: at most kSplitCap K-ranges a tile,
+// each at least kSplitMinSteps K-steps long (64 elements a step), on at most
+// kCUs workgroups (so at most kCUs split entries).
+constexpr int kSplitCap = 8;
+constexpr int kSplitMinSteps = 32;
+
 ExpertsPlan experts_plan(int64_t rows, int64_t E, int64_t H, int64_t I, int dt) {
   ExpertsPlan p;
   p.bm = dt == kF32 ? kBMSimt : (rows <= kBMStream * E ? kBMStream : kBM);
   p.max_tiles = (int)((rows + p.bm - 1) / p.bm + (E < rows ? E : rows));
-  p.splits = 1;
-  p.k_chunk = (int)I;
-  if (dt != kF32) {
-    const int64_t tiles = (int64_t)p.max_tiles * ((H + 255) / 256);
-    const int64_t ksteps = (I + kBK - 1) / kBK;
-    if (tiles < 4 * kCUs) {
-      int64_t sp = (4 * kCUs + tiles - 1) / tiles;
-      sp = std::min<int64_t>(sp, std::max<int64_t>(1, ksteps / 64));
-      p.splits = (int)std::min<int64_t>(sp, 8);
-    }
-    p.k_chunk = (int)((ksteps + p.splits - 1) / p.splits * kBK);
-  }
+  p.split_cap = 1;
+  p.split_slots = 0;
   const int64_t n_gate_up = tile_n(I, dt, true), n_down = tile_n(H, dt, false);
-  p.sched_entries = std::max(grid_tiles(p.max_tiles, n_gate_up, 1),
-                             grid_tiles(p.max_tiles, n_down, p.splits));
+  int64_t entries_down = grid_tiles(p.max_tiles, n_down);
+  if (dt != kF32) {
+    const int64_t ksteps = (I + kBK - 1) / kBK;
+    p.split_cap = (int)std::max<int64_t>(1, std::min<int64_t>(kSplitCap, ksteps / kSplitMinSteps));
+    if (p.split_cap > 1) {
+      p.split_slots = (int)std::min<int64_t>(kCUs, entries_down * p.split_cap);
+      entries_down += p.split_slots;
+    }
+  }
+  p.sched_entries = std::max(grid_tiles(p.max_tiles, n_gate_up), entries_down);
   return p;
 }
 
+// Scratch of one GEMM call: the schedule, the split tiles' table (a header
+// and up to kCUs entries) and their fp32 partial-sum blocks.
 static size_t tile_list_bytes(const ExpertsPlan& p) {
   return align256((size_t)p.sched_entries * sizeof(int4));
+}
+static size_t split_table_bytes() { return align256((size_t)(1 + kCUs) * sizeof(int4)); }
+static size_t partial_bytes(const ExpertsPlan& p) {
+  return align256((size_t)p.split_slots * (size_t)p.bm * 256 * sizeof(float));
 }
 
 size_t gemm_scratch_bytes(int64_t rows, int64_t E, int64_t H, int64_t I, int dt) {
   const ExpertsPlan p = experts_plan(rows, E, H, I, dt);
-  size_t b = tile_list_bytes(p);
-  if (p.splits > 1) b += align256((size_t)p.splits * (size_t)rows * (size_t)H * sizeof(float));
-  return b;
+  return tile_list_bytes(p) + split_table_bytes() + partial_bytes(p);
 }
 
 size_t experts_scratch_bytes(int64_t rows, int64_t E, int64_t H, int64_t I, int dt) {
@@ -1307,66 +1329,50 @@ size_t experts_scratch_bytes(int64_t rows, int64_t E, int64_t H, int64_t I, int 
 
 namespace {
 
-// out[r] = sum over splits (in split order) of partial[s][r], for rows below
-// the device row count; N is a multiple of 8.
+// The split tiles of the down GEMM's last round: block u adds the s fp32
+// partial blocks of split tile u (split[1 + u]) in K-range order and stores
+// the tile's rows of out; nothing when the last round was not split
+// (split[0] = (r, s)). Eight columns a thread, 32 threads a row.
 template <typename T>
-__global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restrict__ partial,
-                                                             int splits, int rows, int N,
-                                                             const int32_t* __restrict__ offsets_end,
-                                                             T* __restrict__ out) {
-  const int vec = N / 8;
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t row = i / vec;
-  const int v = (int)(i % vec);
-  if (row >= min(*offsets_end, rows)) return;
-  const int64_t at = row * N + v * 8;
-  const int64_t stride = (int64_t)rows * N;
-  float acc[8];
-  {
-    const float4 a0 = *reinterpret_cast<const float4*>(partial + at);
-    const float4 a1 = *reinterpret_cast<const float4*>(partial + at + 4);
-    acc[0] = a0.x; acc[1] = a0.y; acc[2] = a0.z; acc[3] = a0.w;
-    acc[4] = a1.x; acc[5] = a1.y; acc[6] = a1.z; acc[7] = a1.w;
-  }
-  for (int s = 1; s < splits; ++s) {
-    const float4 a0 = *reinterpret_cast<const float4*>(partial + s * stride + at);
-    const float4 a1 = *reinterpret_cast<const float4*>(partial + s * stride + at + 4);
-    acc[0] += a0.x; acc[1] += a0.y; acc[2] += a0.z; acc[3] += a0.w;
-    acc[4] += a1.x; acc[5] += a1.y; acc[6] += a1.z; acc[7] += a1.w;
-  }
-  Vec8<T> o;
+__global__ __launch_bounds__(256) void reduce_split_tiles_kernel(const float* __restrict__ partial,
+                                                                 const int4* __restrict__ split, int bm,
+                                                                 int N, T* __restrict__ out) {
+  const int4 hd = split[0];
+  const int r = hd.x, s = hd.y, u = blockIdx.x;
+  if (s <= 1 || u >= r) return;
+  const int4 d = split[1 + u];
+  const int mrows = min(bm, d.z - d.y);
+  const int c = (threadIdx.x & 31) * 8;
+  const int col = d.w * 256 + c;
+  if (col >= N) return;  // N is a multiple of 8
+  const float* blk = partial + (int64_t)u * s * bm * 256;
+  const int64_t stride = (int64_t)bm * 256;
+  for (int lr = threadIdx.x >> 5; lr < mrows; lr += 8) {
+    const float* src = blk + lr * 256 + c;
+    float acc[8];
+    {
+      const float4 a0 = *reinterpret_cast<const float4*>(src);
+      const float4 a1 = *reinterpret_cast<const float4*>(src + 4);
+      acc[0] = a0.x; acc[1] = a0.y; acc[2] = a0.z; acc[3] = a0.w;
+      acc[4] = a1.x; acc[5] = a1.y; acc[6] = a1.z; acc[7] = a1.w;
+    }
+    for (int k = 1; k < s; ++k) {
+      const float4 a0 = *reinterpret_cast<const float4*>(src + k * stride);
+      const float4 a1 = *reinterpret_cast<const float4*>(src + k * stride + 4);
+      acc[0] += a0.x; acc[1] += a0.y; acc[2] += a0.z; acc[3] += a0.w;
+      acc[4] += a1.x; acc[5] += a1.y; acc[6] += a1.z; acc[7] += a1.w;
+    }
+    Vec8<T> o;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) o.set(j, acc[j]);
-  o.store(out + at);
-}
-
-// Carves the schedule out of `scratch` and enqueues the plan kernel for the
-// GEMM described by g (N, k_splits already set).
-void plan_tiles(GemmArgs& g, const ExpertsPlan& plan, int E, int dt, bool swiglu, void* scratch,
-                hipStream_t s) {
-  g.max_tiles = plan.max_tiles;
-  g.bm = plan.bm;
-  g.n_tiles_n = (int)tile_n(g.N, dt, swiglu);
-  g.grid = (int)grid_tiles(plan.max_tiles, g.n_tiles_n, g.k_splits);
-  int4* sched = static_cast<int4*>(scratch);
-  // Each workgroup repeats the expert scan and fills 1024 entries: the entry
-  // arithmetic (a binary search and several divisions) dominates, and one
-  // workgroup on one CU would take it in series.
-  const int blocks = std::max(1, std::min((g.grid + 1023) / 1024, 64));
-  hipLaunchKernelGGL(plan_kernel, dim3(blocks), dim3(1024), 0, s, g.offsets, E, g.rows, plan.bm,
-                     plan.max_tiles, g.n_tiles_n, g.k_splits, g.grid, sched);
-  g.sched = sched;
-}
-
-float* partial_buffer(const ExpertsPlan& plan, void* scratch) {
-  return plan.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(scratch) + tile_list_bytes(plan))
-                         : nullptr;
+    for (int j = 0; j < 8; ++j) o.set(j, acc[j]);
+    o.store(out + (int64_t)(d.y + lr) * N + col);
+  }
 }
 
 // Workgroups of the persistent MFMA GEMM: one per CU (its 144-160 KB of LDS
 // stages leave room for no second one), at most one per schedule entry; a
 // multiple of 8 so each workgroup stays on the XCD its entries belong to.
-static int persistent_grid(int entries) {
+static int persistent_grid(int64_t entries) {
   static int cus[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
@@ -1375,12 +1381,53 @@ static int persistent_grid(int entries) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8) n = kCUs;
     cus[dev] = n / 8 * 8;
   }
-  return std::min(entries, cus[dev]);
+  return (int)std::min<int64_t>(entries, cus[dev]);
+}
+
+int4* split_table(const ExpertsPlan& plan, void* scratch) {
+  return reinterpret_cast<int4*>(static_cast<char*>(scratch) + tile_list_bytes(plan));
+}
+
+float* partial_buffer(const ExpertsPlan& plan, void* scratch) {
+  return plan.split_slots > 0
+             ? reinterpret_cast<float*>(static_cast<char*>(scratch) + tile_list_bytes(plan) + split_table_bytes())
+             : nullptr;
+}
+
+// Carves the schedule out of `scratch` and enqueues the plan kernel for the
+// GEMM described by g (N set; the down GEMM with split = true may split its
+// last round's K).
+void plan_tiles(GemmArgs& g, const ExpertsPlan& plan, int E, int dt, bool swiglu, bool split, void* scratch,
+                hipStream_t s) {
+  g.max_tiles = plan.max_tiles;
+  g.bm = plan.bm;
+  g.n_tiles_n = (int)tile_n(g.N, dt, swiglu);
+  const int64_t tiles = grid_tiles(plan.max_tiles, g.n_tiles_n);
+  const int cap = split && plan.split_slots > 0 ? plan.split_cap : 1;
+  if (cap > 1) {
+    // workgroups: enough for every split entry, at most kCUs (the split
+    // entries' partial blocks are sized for kCUs)
+    g.wgs = std::min(persistent_grid(tiles * cap), plan.split_slots);
+    g.grid = (int)(tiles + g.wgs);
+  } else {
+    g.wgs = persistent_grid(tiles);
+    g.grid = (int)tiles;
+  }
+  g.partial = cap > 1 ? partial_buffer(plan, scratch) : nullptr;
+  int4* sched = static_cast<int4*>(scratch);
+  // Each workgroup repeats the expert scan and fills 1024 entries: the entry
+  // arithmetic (a binary search and several divisions) dominates, and one
+  // workgroup on one CU would take it in series.
+  const int blocks = std::max(1, std::min((g.grid + 1023) / 1024, 64));
+  hipLaunchKernelGGL(plan_kernel, dim3(blocks), dim3(1024), 0, s, g.offsets, E, g.rows, plan.bm,
+                     plan.max_tiles, g.n_tiles_n, cap, g.wgs, g.grid, sched,
+                     cap > 1 ? split_table(plan, scratch) : nullptr);
+  g.sched = sched;
 }
 
 template <typename T>
 void launch_mfma(const GemmArgs& g, bool swiglu, hipStream_t s) {
-  const dim3 grid(persistent_grid(g.grid));
+  const dim3 grid(g.wgs);
   if (g.bm == kBMStream) {
     constexpr int kThreads = gemm_threads<kWaveMStream, kBMStream>();
     if (swiglu && g.cache)
@@ -1422,16 +1469,14 @@ void setup_gate_up(GemmArgs& g, const void* a, const int32_t* a_map, int a_div, 
   g.a_rows = a_map ? (g.rows + g.a_div - 1) / g.a_div : g.rows;
   g.b0 = w_gate; g.b1 = w_up; g.c = h;
   g.N = I; g.K = H;
-  g.k_splits = 1; g.k_chunk = H; g.partial = nullptr;
+  g.partial = nullptr;
 }
 
-void setup_down(GemmArgs& g, const ExpertsPlan& plan, void* scratch, const void* h, int H, int I,
-                const void* w_down, void* expert_out) {
+void setup_down(GemmArgs& g, const void* h, int H, int I, const void* w_down, void* expert_out) {
   g.a = h; g.a_map = nullptr; g.a_div = 1; g.a_rows = g.rows;
   g.b0 = w_down; g.b1 = nullptr; g.c = expert_out;
   g.N = H; g.K = I;
-  g.k_splits = plan.splits; g.k_chunk = plan.k_chunk;
-  g.partial = partial_buffer(plan, scratch);
+  g.partial = nullptr;
 }
 
 // Few rows per expert (decode-shaped batches): weight streaming dominates.
@@ -1466,17 +1511,17 @@ void launch_skinny(const GemmArgs& g, int E, int dt, bool swiglu, hipStream_t s)
   else hipLaunchKernelGGL((skinny_gate_up_kernel<bf16>), grid, dim3(64 * kSkinnyWaves), 0, s, sa);
 }
 
-hipError_t reduce_splits(const ExpertsPlan& plan, void* scratch, const int32_t* offsets, int rows,
-                         int E, int H, int dt, void* expert_out, hipStream_t s) {
-  const int64_t n = (int64_t)rows * (H / 8);
-  const float* part = partial_buffer(plan, scratch);
-  const int blocks = (int)((n + 255) / 256);
+// Adds the down GEMM's split last-round tiles into expert_out (one block a
+// possible split tile; those past the plan kernel's count return at once).
+hipError_t reduce_split_tiles(const GemmArgs& g, const ExpertsPlan& plan, void* scratch, int dt,
+                              void* expert_out, hipStream_t s) {
+  const int4* table = split_table(plan, scratch);
   if (dt == kF16)
-    hipLaunchKernelGGL(reduce_splits_kernel<f16>, dim3(blocks), dim3(256), 0, s, part, plan.splits,
-                       rows, H, offsets + E, static_cast<f16*>(expert_out));
+    hipLaunchKernelGGL(reduce_split_tiles_kernel<f16>, dim3(g.wgs), dim3(256), 0, s, g.partial, table, plan.bm,
+                       g.N, static_cast<f16*>(expert_out));
   else
-    hipLaunchKernelGGL(reduce_splits_kernel<bf16>, dim3(blocks), dim3(256), 0, s, part,
-                       plan.splits, rows, H, offsets + E, static_cast<bf16*>(expert_out));
+    hipLaunchKernelGGL(reduce_split_tiles_kernel<bf16>, dim3(g.wgs), dim3(256), 0, s, g.partial, table, plan.bm,
+                       g.N, static_cast<bf16*>(expert_out));
   return hipGetLastError();
 }
 
@@ -1503,37 +1548,31 @@ hipError_t launch_gate_up(const void* a, const int32_t* a_map, int a_div, const 
   g.offsets = offsets; g.rows = rows;
   setup_gate_up(g, a, a_map, a_div, H, I, w_gate, w_up, h);
   g.cache = cache;
-  plan_tiles(g, plan, E, dt, true, scratch, s);
+  plan_tiles(g, plan, E, dt, true, false, scratch, s);
   launch_gemm<true>(g, dt, s);
   return hipGetLastError();
 }
 
 hipError_t launch_down(const void* h, const int32_t* offsets, int rows, int E, int H, int I,
-                       const void* w_down, int dt, void* expert_out, void* scratch,
-                       hipStream_t s, DownPartials* keep) {
+                       const void* w_down, int dt, void* expert_out, void* scratch, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   if (use_skinny(rows, E, dt)) {
     GemmArgs g = {};
     g.offsets = offsets; g.rows = rows;
-    setup_down(g, ExpertsPlan{kBM, 0, 1, I, 0}, nullptr, h, H, I, w_down, expert_out);
-    g.partial = nullptr;
+    setup_down(g, h, H, I, w_down, expert_out);
     launch_skinny(g, E, dt, false, s);
     return hipGetLastError();
   }
   const ExpertsPlan plan = experts_plan(rows, E, H, I, dt);
   GemmArgs g = {};
   g.offsets = offsets; g.rows = rows;
-  setup_down(g, plan, scratch, h, H, I, w_down, expert_out);
-  plan_tiles(g, plan, E, dt, false, scratch, s);
+  setup_down(g, h, H, I, w_down, expert_out);
+  plan_tiles(g, plan, E, dt, false, true, scratch, s);
   launch_gemm<false>(g, dt, s);
-  if (plan.splits > 1) {
-    if (keep) {
-      keep->partial = g.partial;
-      keep->splits = plan.splits;
-      keep->split_stride = (int64_t)rows * H;
-      return hipGetLastError();
-    }
-    return reduce_splits(plan, scratch, offsets, rows, E, H, dt, expert_out, s);
+  if (g.partial != nullptr) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return reduce_split_tiles(g, plan, scratch, dt, expert_out, s);
   }
   return hipGetLastError();
 }
@@ -1541,13 +1580,13 @@ hipError_t launch_down(const void* h, const int32_t* offsets, int rows, int E, i
 hipError_t launch_experts(const void* a, const int32_t* a_map, int a_div,
                           const int32_t* offsets, int rows, int E, int H, int I,
                           const void* w_gate, const void* w_up, const void* w_down, int dt,
-                          void* expert_out, void* scratch, hipStream_t s, DownPartials* keep) {
+                          void* expert_out, void* scratch, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   void* h = static_cast<char*>(scratch) + gemm_scratch_bytes(rows, E, H, I, dt);
   hipError_t e = launch_gate_up(a, a_map, a_div, offsets, rows, E, H, I, w_gate, w_up, dt, h,
                                 scratch, s);
   if (e != hipSuccess) return e;
-  return launch_down(h, offsets, rows, E, H, I, w_down, dt, expert_out, scratch, s, keep);
+  return launch_down(h, offsets, rows, E, H, I, w_down, dt, expert_out, scratch, s);
 }
 
 }  // namespace moe

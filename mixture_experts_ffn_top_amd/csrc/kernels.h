@@ -40,29 +40,21 @@ hipError_t launch_gather_rows(const void* x, int dt, int H, int k, const int32_t
                               hipStream_t s);
 
 // ---- experts (grouped GEMMs) ---------------------------------------------------
-// The M-tile list: for each tile, (expert, first row). Built on the device
-// from the expert offsets; its length is stored at tile_count. The down GEMM
-// may split K (fp32 partial sums, reduced in split order).
+// The schedule of the MFMA path is built on the device from the expert
+// offsets (plan kernel). The down GEMM may split the K of its last round's
+// tiles (fp32 partial sums, added in K-range order into expert_out).
 struct ExpertsPlan {
-  int bm;         // rows per M-tile
-  int max_tiles;  // host upper bound of the tile count
-  int splits;     // K splits of the down GEMM
-  int k_chunk;    // K elements per split
-  int64_t sched_entries;  // workgroup schedule entries, the larger GEMM grid
+  int bm;           // rows per M-tile
+  int max_tiles;    // host upper bound of the M-tile count
+  int split_cap;    // most K-ranges a tile of the down GEMM's last round may take (1: none)
+  int split_slots;  // partial-sum blocks reserved for split tiles (0: none)
+  int64_t sched_entries;  // schedule slots, the larger of the two GEMMs'
 };
 ExpertsPlan experts_plan(int64_t rows, int64_t E, int64_t H, int64_t I, int dt);
-// Scratch of one GEMM call (workgroup schedule + split-K partials).
+// Scratch of one GEMM call (schedule, split-tile table and partial sums).
 size_t gemm_scratch_bytes(int64_t rows, int64_t E, int64_t H, int64_t I, int dt);
 // Scratch of both GEMMs (the above + h).
 size_t experts_scratch_bytes(int64_t rows, int64_t E, int64_t H, int64_t I, int dt);
-
-// Split-K partial sums left for the caller (moe_forward reduces them inside
-// the combine): partial[s * split_stride + r * H + c].
-struct DownPartials {
-  const float* partial = nullptr;
-  int splits = 1;
-  int64_t split_stride = 0;
-};
 
 // a_map: optional; when given, A row r is row a_map[r] / a_div of `a`
 // (gathering tokens straight from x instead of a materialised x_disp).
@@ -73,25 +65,16 @@ hipError_t launch_gate_up(const void* a, const int32_t* a_map, int a_div, const 
                           int rows, int E, int H, int I, const void* w_gate, const void* w_up,
                           int dt, void* h, void* scratch, hipStream_t s, void* cache = nullptr);
 bool gate_up_can_cache(int64_t rows, int64_t E, int dt);
-// With keep != NULL and a split K, the partial sums stay in scratch and are
-// described in *keep instead of being reduced into expert_out.
 hipError_t launch_down(const void* h, const int32_t* offsets, int rows, int E, int H, int I,
-                       const void* w_down, int dt, void* expert_out, void* scratch,
-                       hipStream_t s, DownPartials* keep = nullptr);
+                       const void* w_down, int dt, void* expert_out, void* scratch, hipStream_t s);
 hipError_t launch_experts(const void* a, const int32_t* a_map, int a_div,
                           const int32_t* offsets, int rows, int E, int H, int I,
                           const void* w_gate, const void* w_up, const void* w_down, int dt,
-                          void* expert_out, void* scratch, hipStream_t s,
-                          DownPartials* keep = nullptr);
+                          void* expert_out, void* scratch, hipStream_t s);
 
 // ---- combine ------------------------------------------------------------------
 hipError_t launch_combine(const void* expert_out, const int32_t* row_of_slot, const void* weights,
                           int w_dt, int T, int k, int H, int dt, void* out, hipStream_t s);
-// Combine from split-K partial sums: each expert row is first summed over
-// the splits and rounded to the model dtype, exactly as expert_out would be.
-hipError_t launch_combine_partials(const DownPartials& part, const int32_t* row_of_slot,
-                                   const void* weights, int w_dt, int T, int k, int H, int dt,
-                                   void* out, hipStream_t s);
 hipError_t launch_combine_add_rmsnorm(const void* expert_out, const int32_t* row_of_slot,
                                       const void* weights, int w_dt, const void* shared,
                                       const void* residual, const float* gamma, float eps, int T,

@@ -1,22 +1,34 @@
-// Tile list of the grouped expert GEMMs: which (K-split, expert, M-tile,
-// N-tile) each schedule entry computes. Plain arithmetic over the expert table
-// the plan kernel builds (gemm.hip), usable on the host as well, so that the
-// mapping can be checked exhaustively on a CPU.
+// Tile list of the grouped expert GEMMs: which (expert, M-tile, N-tile, and
+// K-range) each schedule entry computes. Plain arithmetic over the expert
+// table the plan kernel builds (gemm.hip), usable on the host as well, so
+// that the mapping can be checked exhaustively on a CPU.
 //
-// The list. Per K-split, experts in id order; inside an expert, groups of up
-// to kGroupM M-tiles, and inside a group runs of N-tiles wide enough that one
-// run covers about kRunTiles tiles (4 M-tiles x 2 N-tiles, 8 x 1, 1 x 8 ...),
-// N first inside a run. Consecutive entries thus share weight tiles and
-// activation tiles, and a run never mixes two experts' weights.
+// The list. Experts in id order; inside an expert, groups of up to kGroupM
+// M-tiles, and inside a group runs of N-tiles wide enough that one run covers
+// about kRunTiles tiles (4 M-tiles x 2 N-tiles, 8 x 1, 1 x 8 ...), N first
+// inside a run. Consecutive entries thus share weight tiles and activation
+// tiles, and a run never mixes two experts' weights.
 //
-// Slices. Entry b belongs to XCD b % kXcds (the hardware deals workgroups to
-// the XCDs round-robin, and the persistent kernel's workgroup b only takes
-// entries b + i * grid, with grid a multiple of kXcds), slot b / kXcds, and
-// XCD x computes the list positions [x * chunk, (x + 1) * chunk) in slot
-// order, chunk = ceil(entries / kXcds). (Cutting the slices at equal
-// estimated cost instead, with an expert's short last M-tile counted cheaper,
-// measured no faster on the Mixtral-shaped GEMM and slower where the weight
-// stream sets the time: there every tile streams the same weight bytes.)
+// Slots. Slot b belongs to XCD b % kXcds (the hardware deals workgroups to
+// the XCDs round-robin, and the persistent kernel's workgroup v takes the
+// slots v + i * W, W workgroups, a multiple of kXcds) and is that XCD's slot
+// j = b / kXcds. XCD x computes the list positions [x * chunk, (x + 1) *
+// chunk) in slot order, chunk = ceil(tiles / kXcds). (Cutting the slices at
+// equal estimated cost instead, with an expert's short last M-tile counted
+// cheaper, measured no faster on the Mixtral-shaped GEMM and slower where the
+// weight stream sets the time: there every tile streams the same weight
+// bytes.)
+//
+// The last round. When K may be split (the down GEMM), T tiles on W
+// workgroups make q = T / W full rounds and a last round of r = T % W tiles
+// that would leave W - r workgroups idle for a whole tile's time. Those r
+// tiles are instead split s = min(cap, W / r) ways along K: the last round
+// has r * s entries of 1/s of a tile each (K-range ks of tile u, ordered
+// K-range first, so that entries reading the same weight K-range are
+// neighbours), their fp32 partial sums are added afterwards, and every other
+// tile computes all of K and stores its output directly. Each XCD then takes
+// q full rounds' positions [x * q * W/8, (x + 1) * q * W/8) and the
+// last-round entries [x * W/8, (x + 1) * W/8).
 #pragma once
 
 #include <stdint.h>
@@ -43,12 +55,11 @@ struct Table {
   const int* first;
   const int* lo;
   const int* hi;
-  int E, bm, n_tiles_n, k_splits;
-  int per_split;  // entries of one K-split's list
-  int n_real;     // per_split * k_splits
+  int E, bm, n_tiles_n;
+  int tiles;  // entries of the list: min(first[E], the host's M-tile bound) * n_tiles_n
 };
 
-// The expert holding split-local entry idx: the last e with
+// The expert holding list position idx: the last e with
 // first[e] * n_tiles_n <= idx.
 MOE_SCHED_FN int expert_of(const Table& t, int idx) {
   int lo_e = 0, hi_e = t.E - 1;
@@ -74,30 +85,90 @@ MOE_SCHED_FN void local_tile(int me, int n_tiles_n, int j, int* m, int* n) {
   *n = ngi * ng + r % w;
 }
 
-// Entry of the list at position L: expert, K-split, first row and N-tile.
+// A schedule entry: expert, first row and end row of the expert, N-tile;
+// K-range ks of s (s = 1: all of K) and, when split, the tile's index u
+// among the last round's tiles.
 struct Entry {
-  int ex, ks, row0, row_end, n_t;
+  int ex, row0, row_end, n_t, ks, s, u;
 };
 
+// Entry of the list at position L (all of K).
 MOE_SCHED_FN Entry entry_at(const Table& t, int L) {
   Entry e;
-  e.ks = L / t.per_split;
-  const int idx = L - e.ks * t.per_split;
-  e.ex = expert_of(t, idx);
+  e.ex = expert_of(t, L);
   const int me = t.first[e.ex + 1] - t.first[e.ex];
   int m, n;
-  local_tile(me, t.n_tiles_n, idx - t.first[e.ex] * t.n_tiles_n, &m, &n);
+  local_tile(me, t.n_tiles_n, L - t.first[e.ex] * t.n_tiles_n, &m, &n);
   e.row0 = t.lo[e.ex] + m * t.bm;
   e.row_end = t.hi[e.ex];
   e.n_t = n;
+  e.ks = 0;
+  e.s = 1;
+  e.u = 0;
   return e;
 }
 
-// List range [*begin, *end) of XCD x.
+// List range [*begin, *end) of XCD x when the last round is not split.
 MOE_SCHED_FN void xcd_range(const Table& t, int x, int* begin, int* end) {
-  const int chunk = (t.n_real + kXcds - 1) / kXcds;
-  *begin = imin(x * chunk, t.n_real);
-  *end = imin((x + 1) * chunk, t.n_real);
+  const int chunk = (t.tiles + kXcds - 1) / kXcds;
+  *begin = imin(x * chunk, t.tiles);
+  *end = imin((x + 1) * chunk, t.tiles);
+}
+
+// Rounds of a schedule on W workgroups: q full rounds, r tiles left, split s
+// ways (s = 1: the last round is not split). cap = 1: K is never split.
+struct Rounds {
+  int W, q, r, s;
+};
+
+MOE_SCHED_FN Rounds rounds_of(const Table& t, int W, int cap) {
+  Rounds d;
+  d.W = W;
+  d.q = t.tiles / W;
+  d.r = t.tiles - d.q * W;
+  d.s = d.r > 0 && cap > 1 ? imax(1, imin(cap, W / d.r)) : 1;
+  return d;
+}
+
+// Entry of slot b; false if the slot holds none. Each XCD's entries fill a
+// prefix of its slots, so a workgroup stops at its first empty slot.
+MOE_SCHED_FN bool slot_entry(const Table& t, const Rounds& d, int b, Entry* en) {
+  const int x = b % kXcds, j = b / kXcds;
+  if (d.s == 1) {
+    int begin, end;
+    xcd_range(t, x, &begin, &end);
+    if (begin + j >= end) return false;
+    *en = entry_at(t, begin + j);
+    return true;
+  }
+  const int w8 = d.W / kXcds;
+  const int full = d.q * w8;  // full-round slots of each XCD
+  if (j < full) {
+    *en = entry_at(t, x * full + j);
+    return true;
+  }
+  const int v = x * w8 + (j - full);  // last-round entry
+  if (j - full >= w8 || v >= d.r * d.s) return false;
+  const int u = v % d.r;
+  *en = entry_at(t, d.q * d.W + u);
+  en->ks = v / d.r;
+  en->s = d.s;
+  en->u = u;
+  return true;
+}
+
+// First slot past every entry: q full rounds and the last one.
+MOE_SCHED_FN int slots_used(const Rounds& d) {
+  return d.s == 1 ? (d.q * d.W + d.r + kXcds - 1) / kXcds * kXcds : (d.q + 1) * d.W;
+}
+
+// K-range [*k0, *k1) of range ks of s over K elements in steps of bk: whole
+// steps, ceil(steps / s) per range.
+MOE_SCHED_FN void k_range(int K, int bk, int ks, int s, int* k0, int* k1) {
+  const int steps = (K + bk - 1) / bk;
+  const int per = (steps + s - 1) / s * bk;
+  *k0 = ks * per;
+  *k1 = imin(K, *k0 + per);
 }
 
 }  // namespace sched
