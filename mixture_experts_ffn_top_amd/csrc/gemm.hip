@@ -672,7 +672,7 @@ __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kern
     // Every wavefront is done with LDS before the next tile's loads land.
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     const int t_row0 = row0, t_mrows = mrows, t_nt = n_t, t_slot = tu * ts + ks;
-    const bool part = !kSwiGlu && ts > 1;
+    const bool part = !kSwiGlu && ts > 1;  // a split tile of the down GEMM
     v += gridDim.x;
     if (more) {
       setup(next, nsrc);
@@ -811,8 +811,10 @@ __global__ __launch_bounds__((gemm_threads<kWaveM, kBMt>())) void mfma_gemm_kern
           transpose4(x, lane);
           const int lrow = row_base + g * 8 + row_lane + (lane & 3);
           const int col = col_base + col4;
-          const uint32_t vo = (lrow < t_mrows && col < N) ? (uint32_t)(lrow * ld + col - col_off) * (uint32_t)esz
-                                                          : kOutOfRange;
+          // (a partial block's columns past N are stored and never read)
+          const uint32_t vo = (lrow < t_mrows && (part || col < N))
+                                  ? (uint32_t)(lrow * ld + col - col_off) * (uint32_t)esz
+                                  : kOutOfRange;
           if (part) {
             const i32x4 d = {__builtin_bit_cast(int, x[0]), __builtin_bit_cast(int, x[1]),
                              __builtin_bit_cast(int, x[2]), __builtin_bit_cast(int, x[3])};
@@ -1284,7 +1286,9 @@ static int64_t tile_n(int64_t N, int dt, bool swiglu) {
 
 // Split-K of the down GEMM's last round: at most kSplitCap K-ranges a tile,
 // each at least kSplitMinSteps K-steps long (64 elements a step), on at most
-// kCUs workgroups (so at most kCUs split entries).
+// kCUs workgroups (so at most kCUs split entries). (The gate/up GEMM's last
+// round split the same way, its reduction forming SiLU(g) * u, measured no
+// faster on the many-expert shape, the one whose last round is short.)
 constexpr int kSplitCap = 8;
 constexpr int kSplitMinSteps = 32;
 
@@ -1292,19 +1296,13 @@ ExpertsPlan experts_plan(int64_t rows, int64_t E, int64_t H, int64_t I, int dt) 
   ExpertsPlan p;
   p.bm = dt == kF32 ? kBMSimt : (rows <= kBMStream * E ? kBMStream : kBM);
   p.max_tiles = (int)((rows + p.bm - 1) / p.bm + (E < rows ? E : rows));
-  p.split_cap = 1;
-  p.split_slots = 0;
+  p.split_cap = dt == kF32 ? 1
+                            : (int)std::max<int64_t>(
+                                  1, std::min<int64_t>(kSplitCap, (I + kBK - 1) / kBK / kSplitMinSteps));
   const int64_t n_gate_up = tile_n(I, dt, true), n_down = tile_n(H, dt, false);
-  int64_t entries_down = grid_tiles(p.max_tiles, n_down);
-  if (dt != kF32) {
-    const int64_t ksteps = (I + kBK - 1) / kBK;
-    p.split_cap = (int)std::max<int64_t>(1, std::min<int64_t>(kSplitCap, ksteps / kSplitMinSteps));
-    if (p.split_cap > 1) {
-      p.split_slots = (int)std::min<int64_t>(kCUs, entries_down * p.split_cap);
-      entries_down += p.split_slots;
-    }
-  }
-  p.sched_entries = std::max(grid_tiles(p.max_tiles, n_gate_up), entries_down);
+  const int64_t tiles_gu = grid_tiles(p.max_tiles, n_gate_up), tiles_dn = grid_tiles(p.max_tiles, n_down);
+  p.split_slots = p.split_cap > 1 ? (int)std::min<int64_t>(kCUs, tiles_dn * p.split_cap) : 0;
+  p.sched_entries = std::max(tiles_gu, tiles_dn + p.split_slots);
   return p;
 }
 
@@ -1329,26 +1327,28 @@ size_t experts_scratch_bytes(int64_t rows, int64_t E, int64_t H, int64_t I, int 
 
 namespace {
 
-// The split tiles of the down GEMM's last round: block u adds the s fp32
-// partial blocks of split tile u (split[1 + u]) in K-range order and stores
-// the tile's rows of out; nothing when the last round was not split
-// (split[0] = (r, s)). Eight columns a thread, 32 threads a row.
+// The split tiles of the down GEMM's last round: for each split tile u
+// (split[1 + u]), its s fp32 partial blocks are added in K-range order and
+// the tile's rows of out stored; nothing when the last round was not split
+// (split[0] = (r, s)). Eight columns a thread, 32 threads a row; workgroups
+// take 8-row pieces of the split tiles in turn.
 template <typename T>
 __global__ __launch_bounds__(256) void reduce_split_tiles_kernel(const float* __restrict__ partial,
                                                                  const int4* __restrict__ split, int bm,
                                                                  int N, T* __restrict__ out) {
   const int4 hd = split[0];
-  const int r = hd.x, s = hd.y, u = blockIdx.x;
-  if (s <= 1 || u >= r) return;
-  const int4 d = split[1 + u];
-  const int mrows = min(bm, d.z - d.y);
+  const int r = hd.x, s = hd.y;
+  if (s <= 1) return;
+  const int pieces = bm / 8;  // pieces of a tile
   const int c = (threadIdx.x & 31) * 8;
-  const int col = d.w * 256 + c;
-  if (col >= N) return;  // N is a multiple of 8
-  const float* blk = partial + (int64_t)u * s * bm * 256;
   const int64_t stride = (int64_t)bm * 256;
-  for (int lr = threadIdx.x >> 5; lr < mrows; lr += 8) {
-    const float* src = blk + lr * 256 + c;
+  for (int pc = blockIdx.x; pc < r * pieces; pc += gridDim.x) {
+    const int u = pc / pieces;
+    const int lr = (pc - u * pieces) * 8 + (threadIdx.x >> 5);
+    const int4 d = split[1 + u];
+    const int col = d.w * 256 + c;
+    if (lr >= min(bm, d.z - d.y) || col >= N) continue;  // N is a multiple of 8
+    const float* src = partial + (int64_t)u * s * stride + lr * 256 + c;
     float acc[8];
     {
       const float4 a0 = *reinterpret_cast<const float4*>(src);
@@ -1511,17 +1511,18 @@ void launch_skinny(const GemmArgs& g, int E, int dt, bool swiglu, hipStream_t s)
   else hipLaunchKernelGGL((skinny_gate_up_kernel<bf16>), grid, dim3(64 * kSkinnyWaves), 0, s, sa);
 }
 
-// Adds the down GEMM's split last-round tiles into expert_out (one block a
-// possible split tile; those past the plan kernel's count return at once).
-hipError_t reduce_split_tiles(const GemmArgs& g, const ExpertsPlan& plan, void* scratch, int dt,
-                              void* expert_out, hipStream_t s) {
+// Adds the down GEMM's split last-round tiles into expert_out: 8-row pieces
+// of up to g.wgs split tiles.
+hipError_t reduce_split_tiles(const GemmArgs& g, const ExpertsPlan& plan, void* scratch, int dt, void* out,
+                              hipStream_t s) {
   const int4* table = split_table(plan, scratch);
+  const dim3 grid(std::min(2048, g.wgs * (plan.bm / 8))), block(256);
   if (dt == kF16)
-    hipLaunchKernelGGL(reduce_split_tiles_kernel<f16>, dim3(g.wgs), dim3(256), 0, s, g.partial, table, plan.bm,
-                       g.N, static_cast<f16*>(expert_out));
+    hipLaunchKernelGGL(reduce_split_tiles_kernel<f16>, grid, block, 0, s, g.partial, table, plan.bm, g.N,
+                       static_cast<f16*>(out));
   else
-    hipLaunchKernelGGL(reduce_split_tiles_kernel<bf16>, dim3(g.wgs), dim3(256), 0, s, g.partial, table, plan.bm,
-                       g.N, static_cast<bf16*>(expert_out));
+    hipLaunchKernelGGL(reduce_split_tiles_kernel<bf16>, grid, block, 0, s, g.partial, table, plan.bm, g.N,
+                       static_cast<bf16*>(out));
   return hipGetLastError();
 }
 
