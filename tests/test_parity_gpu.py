@@ -255,10 +255,12 @@ def test_experts_few_rows_per_expert(T, k, E, H, I_, dtype, one_expert):
 @pytest.mark.parametrize("E,H,I_", [(3, 512, 4096),    # 200 rows an expert: 256-row M-tiles
                                     (8, 256, 8192)])   # 75 rows an expert: 128-row M-tiles
 def test_experts_split_k_and_halves(E, H, I_):
-    """Long K with few output tiles: the down GEMM splits K (fp32 partials,
-    reduced in order). Checked through forward_dispatched, through the two
-    halves (gate/up reading tokens via the dispatch map) and through
-    moe_forward (partials reduced inside the combine)."""
+    """Long K with fewer output tiles than workgroups: every tile falls in the
+    down GEMM's last round and is split along K (fp32 partial blocks added in
+    K-range order by the reduction kernel): 6 tiles split 2 ways on 256-row
+    M-tiles, 8 tiles split 4 ways on 128-row M-tiles. Checked through
+    forward_dispatched, through the two halves (gate/up reading tokens via
+    the dispatch map) and through moe_forward."""
     say("split-K", E, H, I_)
     g = np.random.default_rng(21)
     T, k = 300, 2
