@@ -88,9 +88,9 @@ constexpr uint32_t kOutOfRange = 0x80000000u;  // voffset past any buffer we bui
 // partial sums; split[0].y = 1 otherwise.
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ offsets, int E,
                                                      int rows, int bm, int max_tiles,
-                                                     int n_tiles_n, int cap, int wgs, int grid,
+                                                     int n_tiles_n, int cap, int costed, int wgs, int grid,
                                                      int4* __restrict__ sched, int4* __restrict__ split) {
-  __shared__ int s_first[kMaxExperts + 1], s_lo[kMaxExperts], s_hi[kMaxExperts];
+  __shared__ int s_first[kMaxExperts + 1], s_cfirst[kMaxExperts + 1], s_lo[kMaxExperts], s_hi[kMaxExperts];
   const int e = threadIdx.x;
   int lo = 0, hi = 0, n = 0;
   if (e < E) {
@@ -98,24 +98,31 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
     hi = min(offsets[e + 1], rows);
     n = hi > lo ? (hi - lo + bm - 1) / bm : 0;
   }
-  int total = 0;
+  int total = 0, ctotal = 0;
   const int first = block_exclusive_scan(n, &total);
+  const int cfirst = block_exclusive_scan(costed ? sched::expert_cost(hi - lo, bm, n_tiles_n) : 0, &ctotal);
   if (e < E) {
     s_first[e] = first;
+    s_cfirst[e] = cfirst;
     s_lo[e] = lo;
     s_hi[e] = hi;
   }
-  if (e == 0) s_first[E] = total;
+  if (e == 0) {
+    s_first[E] = total;
+    s_cfirst[E] = ctotal;
+  }
   __syncthreads();
   sched::Table t;
   t.first = s_first;
   t.lo = s_lo;
   t.hi = s_hi;
+  t.cfirst = nullptr;
   t.E = E;
   t.bm = bm;
   t.n_tiles_n = n_tiles_n;
   t.tiles = min(total, max_tiles) * n_tiles_n;
   const sched::Rounds d = sched::rounds_of(t, wgs, cap);
+  if (costed && d.s == 1) t.cfirst = s_cfirst;  // slices of equal cost
   for (int b = blockIdx.x * blockDim.x + threadIdx.x; b < grid; b += gridDim.x * blockDim.x) {
     sched::Entry en;
     int4 v = make_int4(-1, 0, 0, 0);
@@ -1302,7 +1309,9 @@ ExpertsPlan experts_plan(int64_t rows, int64_t E, int64_t H, int64_t I, int dt) 
   const int64_t n_gate_up = tile_n(I, dt, true), n_down = tile_n(H, dt, false);
   const int64_t tiles_gu = grid_tiles(p.max_tiles, n_gate_up), tiles_dn = grid_tiles(p.max_tiles, n_down);
   p.split_slots = p.split_cap > 1 ? (int)std::min<int64_t>(kCUs, tiles_dn * p.split_cap) : 0;
-  p.sched_entries = std::max(tiles_gu, tiles_dn + p.split_slots);
+  // slots of the schedule (cost slices or a split last round) on at most
+  // kCUs workgroups
+  p.sched_entries = std::max(sched::slots_bound((int)tiles_gu, kCUs), sched::slots_bound((int)tiles_dn, kCUs));
   return p;
 }
 
@@ -1404,15 +1413,19 @@ void plan_tiles(GemmArgs& g, const ExpertsPlan& plan, int E, int dt, bool swiglu
   g.n_tiles_n = (int)tile_n(g.N, dt, swiglu);
   const int64_t tiles = grid_tiles(plan.max_tiles, g.n_tiles_n);
   const int cap = split && plan.split_slots > 0 ? plan.split_cap : 1;
-  if (cap > 1) {
-    // workgroups: enough for every split entry, at most kCUs (the split
-    // entries' partial blocks are sized for kCUs)
+  // workgroups, at most kCUs (the schedule and the split entries' partial
+  // blocks are sized for kCUs): with a possible split, enough for every split
+  // entry
+  if (cap > 1)
     g.wgs = std::min(persistent_grid(tiles * cap), plan.split_slots);
-    g.grid = (int)(tiles + g.wgs);
-  } else {
-    g.wgs = persistent_grid(tiles);
-    g.grid = (int)tiles;
-  }
+  else
+    g.wgs = std::min(persistent_grid(tiles), kCUs);
+  // slices of equal estimated cost for the gate/up GEMM on the 256-row tile
+  // (many-expert shape: 0.46 -> 0.43 ms); equal count for the down GEMM
+  // (its 12-k-step tiles measured 1-3 % slower with cost slices) and on the
+  // fp32 path, which launches one workgroup per slot
+  const bool costed = dt != kF32 && plan.bm == kBM && swiglu;
+  g.grid = dt != kF32 ? sched::slots_bound((int)tiles, g.wgs) : (int)tiles;
   g.partial = cap > 1 ? partial_buffer(plan, scratch) : nullptr;
   int4* sched = static_cast<int4*>(scratch);
   // Each workgroup repeats the expert scan and fills 1024 entries: the entry
@@ -1420,7 +1433,7 @@ void plan_tiles(GemmArgs& g, const ExpertsPlan& plan, int E, int dt, bool swiglu
   // workgroup on one CU would take it in series.
   const int blocks = std::max(1, std::min((g.grid + 1023) / 1024, 64));
   hipLaunchKernelGGL(plan_kernel, dim3(blocks), dim3(1024), 0, s, g.offsets, E, g.rows, plan.bm,
-                     plan.max_tiles, g.n_tiles_n, cap, g.wgs, g.grid, sched,
+                     plan.max_tiles, g.n_tiles_n, cap, costed ? 1 : 0, g.wgs, g.grid, sched,
                      cap > 1 ? split_table(plan, scratch) : nullptr);
   g.sched = sched;
 }

@@ -12,12 +12,19 @@
 // Slots. Slot b belongs to XCD b % kXcds (the hardware deals workgroups to
 // the XCDs round-robin, and the persistent kernel's workgroup v takes the
 // slots v + i * W, W workgroups, a multiple of kXcds) and is that XCD's slot
-// j = b / kXcds. XCD x computes the list positions [x * chunk, (x + 1) *
-// chunk) in slot order, chunk = ceil(tiles / kXcds). (Cutting the slices at
-// equal estimated cost instead, with an expert's short last M-tile counted
-// cheaper, measured no faster on the Mixtral-shaped GEMM and slower where the
-// weight stream sets the time: there every tile streams the same weight
-// bytes.)
+// j = b / kXcds. XCD x computes the list positions [cut(x), cut(x + 1)) in
+// slot order. The cuts split the list into eighths of equal count, or (the
+// gate/up GEMM on the 256-row tile) of equal estimated cost: an
+// M-tile whose rows fill at most half of it has one wavefront with rows per
+// SIMD and costs about 0.78 of a full one (per-tile timestamps of the
+// many-expert GEMMs: 0.74-0.80 for up to 128 rows, 1.0 beyond), and inside
+// an expert the cost is spread evenly over its positions. On the many-expert
+// shape the experts with one short M-tile come last in id order; counted
+// equal they filled the last XCD's slice while the first workgroups of every
+// other XCD ran one full tile more than the rest. (Counted equal, the tiles
+// of the weight-streaming 128-row tile each stream the same weight bytes;
+// cost cuts measured no faster on the Mixtral-shaped GEMM, whose short last
+// M-tiles interleave with full ones.)
 //
 // The last round. When K may be split (the down GEMM), T tiles on W
 // workgroups make q = T / W full rounds and a last round of r = T % W tiles
@@ -55,9 +62,22 @@ struct Table {
   const int* first;
   const int* lo;
   const int* hi;
+  const int* cfirst;  // estimated cost before expert e (cfirst[E]: all); null: slices of equal count
   int E, bm, n_tiles_n;
   int tiles;  // entries of the list: min(first[E], the host's M-tile bound) * n_tiles_n
 };
+
+// Estimated cost of an expert's tiles: kCostFull a tile, kCostShort for
+// those of an M-tile at most half full.
+constexpr int kCostFull = 100;
+constexpr int kCostShort = 78;
+
+MOE_SCHED_FN int expert_cost(int rows, int bm, int n_tiles_n) {
+  if (rows <= 0) return 0;
+  const int me = (rows + bm - 1) / bm;
+  const int last = rows - (me - 1) * bm;
+  return n_tiles_n * ((me - 1) * kCostFull + (2 * last <= bm ? kCostShort : kCostFull));
+}
 
 // The expert holding list position idx: the last e with
 // first[e] * n_tiles_n <= idx.
@@ -108,11 +128,29 @@ MOE_SCHED_FN Entry entry_at(const Table& t, int L) {
   return e;
 }
 
+// First list position of XCD x's slice (x = kXcds: the list's end).
+MOE_SCHED_FN int xcd_cut(const Table& t, int x) {
+  if (x >= kXcds) return t.tiles;
+  if (t.cfirst == nullptr) return imin(x * ((t.tiles + kXcds - 1) / kXcds), t.tiles);
+  // the expert holding cost x / kXcds of the total, and the position inside
+  // it in proportion
+  const int th = (int)(((long long)t.cfirst[t.E] * x + kXcds - 1) / kXcds);
+  int lo_e = 0, hi_e = t.E - 1;
+  while (lo_e < hi_e) {
+    const int mid = (lo_e + hi_e + 1) / 2;
+    if (t.cfirst[mid] <= th) lo_e = mid;
+    else hi_e = mid - 1;
+  }
+  const int ce = t.cfirst[lo_e + 1] - t.cfirst[lo_e];
+  const int te = (t.first[lo_e + 1] - t.first[lo_e]) * t.n_tiles_n;
+  const int in = ce > 0 ? (int)(((long long)(th - t.cfirst[lo_e]) * te + ce - 1) / ce) : 0;
+  return imin(t.first[lo_e] * t.n_tiles_n + imin(in, te), t.tiles);
+}
+
 // List range [*begin, *end) of XCD x when the last round is not split.
 MOE_SCHED_FN void xcd_range(const Table& t, int x, int* begin, int* end) {
-  const int chunk = (t.tiles + kXcds - 1) / kXcds;
-  *begin = imin(x * chunk, t.tiles);
-  *end = imin((x + 1) * chunk, t.tiles);
+  *begin = xcd_cut(t, x);
+  *end = xcd_cut(t, x + 1);
 }
 
 // Rounds of a schedule on W workgroups: q full rounds, r tiles left, split s
@@ -157,10 +195,10 @@ MOE_SCHED_FN bool slot_entry(const Table& t, const Rounds& d, int b, Entry* en) 
   return true;
 }
 
-// First slot past every entry: q full rounds and the last one.
-MOE_SCHED_FN int slots_used(const Rounds& d) {
-  return d.s == 1 ? (d.q * d.W + d.r + kXcds - 1) / kXcds * kXcds : (d.q + 1) * d.W;
-}
+// Slots that can hold an entry for T tiles on W workgroups: a cost slice
+// holds at most kCostFull / kCostShort (< 4/3) of an eighth of the tiles and
+// one more (or q full rounds and a split last one: at most T + W).
+MOE_SCHED_FN int slots_bound(int T, int W) { return ((4 * T + 2) / 3 + 3 * kXcds - 1) / kXcds * kXcds + W; }
 
 // K-range [*k0, *k1) of range ks of s over K elements in steps of bk: whole
 // steps, ceil(steps / s) per range.

@@ -3,9 +3,11 @@
 // the slots 0 .. grid-1 that the plan kernel fills must hold every (expert,
 // M-tile, N-tile) exactly once, or, for a tile of a split last round, each of
 // its K-ranges exactly once; each XCD's entries must be a prefix of its slots
-// (the persistent workgroups stop at the first empty one); the split round
-// must fit on the workgroups, and the K-ranges must partition K. Prints
-// "ok <cases>" or the first failure.
+// (the persistent workgroups stop at the first empty one); the XCD slices,
+// of equal count or of equal estimated cost, must tile the list in order;
+// the split round must fit on the workgroups, and the K-ranges must
+// partition K. Prints "ok <cases> <split cases> <cost-sliced cases>" or the
+// first failure.
 #include <algorithm>
 #include <cstdint>
 #include <cstdio>
@@ -25,7 +27,7 @@ static int fail(const char* what, int c) {
 
 int main() {
   std::mt19937_64 rng(20251202);
-  int cases = 0, split_cases = 0;
+  int cases = 0, split_cases = 0, cost_cases = 0;
   // K-ranges: whole 64-element steps, ceil(steps / s) a range, covering [0, K)
   for (int K = 1; K <= 4096; K += 37)
     for (int sp = 1; sp <= 8; ++sp) {
@@ -68,27 +70,44 @@ int main() {
     // when the schedule has fewer entries
     const int64_t want = cap > 1 ? tiles64 * cap : tiles64;
     const int W = (int)std::min<int64_t>(want, 8 * (1 + (int)(rng() % 32)));
-    const int grid = (int)(cap > 1 ? tiles64 + W : tiles64);
+    const bool costed = rng() % 3 != 0;  // slices of equal estimated cost (without a split)
+    const int grid = slots_bound((int)tiles64, W);
     // the expert table, as the plan kernel builds it
-    std::vector<int> first(E + 1, 0), lo(E), hi(E);
+    std::vector<int> first(E + 1, 0), cfirst(E + 1, 0), lo(E), hi(E);
     for (int e = 0; e < E; ++e) {
       lo[e] = offsets[e];
       hi[e] = offsets[e + 1];
       first[e + 1] = first[e] + (hi[e] > lo[e] ? (hi[e] - lo[e] + bm - 1) / bm : 0);
+      cfirst[e + 1] = cfirst[e] + expert_cost(hi[e] - lo[e], bm, n_tiles_n);
     }
     Table t;
     t.first = first.data();
     t.lo = lo.data();
     t.hi = hi.data();
+    t.cfirst = nullptr;
     t.E = E;
     t.bm = bm;
     t.n_tiles_n = n_tiles_n;
     t.tiles = std::min(first[E], max_tiles) * n_tiles_n;
     if (first[E] > max_tiles) return fail("M-tile bound", c);
     const Rounds d = rounds_of(t, W, cap);
+    if (costed && d.s == 1) t.cfirst = cfirst.data();
     if (d.s < 1 || d.s > cap) return fail("split count out of range", c);
     if (d.s > 1 && (d.r * d.s > W || d.r == 0)) return fail("split round does not fit the workgroups", c);
-    if (slots_used(d) > grid) return fail("slots past the grid", c);
+    for (int b = grid; b < grid + W; ++b) {  // nothing past the grid
+      Entry en;
+      if (slot_entry(t, d, b, &en)) return fail("entry past the grid", c);
+    }
+    if (d.s == 1) {  // the slices tile the list in order
+      int covered = 0;
+      for (int x = 0; x < kXcds; ++x) {
+        int begin, end;
+        xcd_range(t, x, &begin, &end);
+        if (begin != covered || end < begin) return fail("slices not contiguous", c);
+        covered = end;
+      }
+      if (covered != t.tiles) return fail("slices do not cover the list", c);
+    }
     // every slot, as the plan kernel fills them
     std::map<std::tuple<int, int, int>, std::vector<int>> seen;  // tile -> K-ranges seen
     std::map<std::tuple<int, int, int>, int> split_u;
@@ -149,9 +168,11 @@ int main() {
     }
     if (d.s > 1 && (worst_whole > d.q || worst_split > 1)) return fail("split round not balanced", c);
     split_cases += d.s > 1;
+    cost_cases += t.cfirst != nullptr;
     ++cases;
   }
   if (split_cases < 50) return fail("too few split cases", split_cases);
-  std::printf("ok %d %d\n", cases, split_cases);
+  if (cost_cases < 50) return fail("too few cost-sliced cases", cost_cases);
+  std::printf("ok %d %d %d\n", cases, split_cases, cost_cases);
   return 0;
 }

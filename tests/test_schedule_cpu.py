@@ -24,4 +24,4 @@ def test_schedule_covers_every_tile_once(tmp_path):
                     os.path.join(ROOT, "tests", "schedule", "check_schedule.cpp"), "-o", str(exe)], check=True)
     out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=300).stdout.strip()
     assert out.startswith("ok "), out
-    assert int(out.split()[1]) > 300 and int(out.split()[2]) >= 50, out
+    assert int(out.split()[1]) > 300 and int(out.split()[2]) >= 50 and int(out.split()[3]) >= 50, out
