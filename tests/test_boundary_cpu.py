@@ -402,3 +402,15 @@ def test_forward_noalloc_validation():
     assert call(2, 7) == S["MOE_ERROR_DTYPE"]        # logits dtype
     assert call(6, 2000) == S["MOE_ERROR_UNSUPPORTED"]
     assert call(3, 0) == S["MOE_SUCCESS"]            # no tokens: nothing to do
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU's share; asked for several it exits with status 2 and says so,
+    before importing torch or touching a device."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout == ""
